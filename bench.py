@@ -1,0 +1,186 @@
+"""Benchmark of the blocked GEMM C = A·B on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+A step is one call of the library's ``gemm`` (host-side plan plus the kernel)
+on the workload's synthetic, seeded inputs, already resident in HBM.  Prints
+one JSON line: whole-job TFLOP/s over K timed steps, the dominant kernel's
+achieved TFLOP/s against the dense MFMA peak (HIP events on the stream the
+kernel runs on), and the CPU oracle timed on a bounded sample of the same
+workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s and % of MFMA peak at fp16/bf16 4096³ and 8192³ on 1 MI355X"
+# MI355X dense MFMA peaks (TFLOP/s): 256 CUs x 2.4 GHz x FLOP/clk/CU
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
+HOST_THREADS_CAP = 16  # the host-core share of one GPU on the GPU machines
+KERNEL_SOURCES = ["dense_tiled_matrix_amd/csrc/gemm_mfma16.hip",
+                  "dense_tiled_matrix_amd/csrc/device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    w = rec.get("workloads", {}).get(workload)
+    if not w or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return w.get("hbm_bytes_per_launch")
+
+
+def to_device(op, torch_dtype, torch):
+    import numpy as np
+
+    store = torch.from_numpy(op.bits.view(np.int32 if op.dtype == "f32" else np.int16))
+    t = store.to("cuda:0").view(torch_dtype)
+    return t.as_strided((op.rows, op.cols), (op.stride_r, op.stride_c), op.offset)
+
+
+def time_gemm(dtm, torch, a, b, c, steps, warmup):
+    """(wall ms per step, kernel ms per launch from HIP events) over `steps`."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        dtm.gemm(a, b, out=c, stream=stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        dtm.gemm(a, b, out=c, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return wall_ms, start.elapsed_time(end) / steps
+
+
+def cpu_baseline(p, target_s: float):
+    """The oracle (untuned, fp64, OpenMP over rows) on the first R rows of the
+    workload, R sized so the timed run takes about `target_s` seconds."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    threads = max(1, min(HOST_THREADS_CAP, len(os.sched_getaffinity(0))))
+    A2 = p.A.bits.reshape(p.M, p.K)
+
+    def run_rows(R):
+        sub = W.Problem(R, p.N, p.K, W.dense(np.ascontiguousarray(A2[:R]), p.in_dtype), p.B,
+                        p.in_dtype, p.out_dtype)
+        t0 = time.perf_counter()
+        oracle.gemm_problem(sub, threads=threads)
+        return time.perf_counter() - t0
+
+    # two calibration points separate the fixed cost (decoding B) from the
+    # per-row cost
+    t1 = run_rows(threads)
+    t4 = run_rows(4 * threads)
+    per_row = max((t4 - t1) / (3 * threads), 1e-6)
+    R = int((target_s - t1) / per_row) + threads
+    R = int(min(p.M, max(threads, threads * (R // threads))))
+    t = run_rows(R)
+    flops = 2.0 * R * p.N * p.K
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {R} of {p.M} rows of A times all of B ({p.K}x{p.N}), "
+                      f"{t:.1f} s wall incl. decoding the operands to fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="bf16_8192_bf16out")
+    ap.add_argument("--secondary", default="f16_4096_f32out",
+                    help="comma-separated workloads also timed (not the headline)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this GEMM library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dense_tiled_matrix_amd as dtm
+    import workloads as W
+
+    TD = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+    def measure(name):
+        p = W.workload(name)
+        a = to_device(p.A, TD[p.in_dtype], torch)
+        b = to_device(p.B, TD[p.in_dtype], torch)
+        c = torch.empty(p.M, p.N, dtype=TD[p.out_dtype], device="cuda:0")
+        plan = dtm.gemm_plan(a, b, out=c)
+        wall_ms, kern_ms = time_gemm(dtm, torch, a, b, c, args.steps, args.warmup)
+        flops = 2.0 * p.M * p.N * p.K
+        return p, plan, wall_ms, kern_ms, flops
+
+    p, plan, wall_ms, kern_ms, flops = measure(args.workload)
+    peak = PEAK_TFLOPS[p.in_dtype]
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(flops / (wall_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.in_dtype,
+        "data": "synthetic",
+        "config": {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "in_dtype": p.in_dtype,
+                   "out_dtype": p.out_dtype, "kernel": plan["kernel_name"],
+                   "tile": [plan["block_m"], plan["block_n"], plan["block_k"]],
+                   "grid": [plan["grid_m"], plan["grid_n"]]},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(p.name)},
+    }
+    secondary = []
+    for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
+        q, qplan, qwall, qkern, qflops = measure(name)
+        qa = qflops / (qkern * 1e-3) / 1e12
+        secondary.append({"workload": q.name, "tflops_wall": round(qflops / (qwall * 1e-3) / 1e12, 2),
+                          "tflops_kernel": round(qa, 2), "frac": round(qa / PEAK_TFLOPS[q.in_dtype], 4),
+                          "kernel_ms": round(qkern, 4),
+                          "tile": [qplan["block_m"], qplan["block_n"], qplan["block_k"]]})
+    if secondary:
+        line["secondary"] = secondary
+    line["cpu_baseline"] = None if args.no_cpu else cpu_baseline(p, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

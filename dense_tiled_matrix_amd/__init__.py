@@ -1,0 +1,237 @@
+"""Python binding of libdtm_gemm.so, the MI355X (gfx950) blocked GEMM C = A·B.
+
+The C ABI is declared in ``include/dtm_gemm.h``; the functions here have the
+same names and only marshal arguments (sizes, device pointers, element
+strides, dtype codes and the current HIP stream) into it.  Every step of the
+computation runs in the library's HIP kernels.  PyTorch provides device memory
+and streams.
+
+There is no fallback: if the shared library is missing or fails to load, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdtm_gemm.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "dtm_gemm.h")
+
+# dtm_dtype
+DTM_F32, DTM_F16, DTM_BF16 = 0, 1, 2
+# dtm_status
+STATUS = {
+    0: "DTM_OK", 1: "DTM_ERR_INVALID_DIM", 2: "DTM_ERR_NULL_POINTER", 3: "DTM_ERR_DTYPE",
+    4: "DTM_ERR_STRIDE", 5: "DTM_ERR_ALIAS", 6: "DTM_ERR_CONFIG", 7: "DTM_ERR_WORKSPACE",
+    8: "DTM_ERR_DEVICE", 9: "DTM_ERR_LAUNCH",
+}
+globals().update({v: k for k, v in STATUS.items()})
+# dtm_kernel
+KERNELS = {0: "none", 1: "zero_fill", 2: "generic", 3: "mfma_f16", 4: "mfma_f32"}
+DTM_KERNEL_NONE, DTM_KERNEL_ZERO_FILL, DTM_KERNEL_GENERIC = 0, 1, 2
+DTM_KERNEL_MFMA_F16, DTM_KERNEL_MFMA_F32 = 3, 4
+
+
+class TileConfig(ctypes.Structure):
+    """dtm_tile_config: zero fields mean "the selector chooses"."""
+
+    _fields_ = [("kernel", ctypes.c_int32), ("block_m", ctypes.c_int32),
+                ("block_n", ctypes.c_int32), ("block_k", ctypes.c_int32),
+                ("split_k", ctypes.c_int32)]
+
+
+class Plan(ctypes.Structure):
+    """dtm_plan."""
+
+    _fields_ = [("kernel", ctypes.c_int32), ("block_m", ctypes.c_int32),
+                ("block_n", ctypes.c_int32), ("block_k", ctypes.c_int32),
+                ("grid_m", ctypes.c_int64), ("grid_n", ctypes.c_int64),
+                ("k_iters", ctypes.c_int64), ("split_k", ctypes.c_int32),
+                ("threads", ctypes.c_int32), ("fast_path", ctypes.c_int32),
+                ("ragged", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64)]
+
+    def as_dict(self):
+        d = {f: getattr(self, f) for f, _ in self._fields_}
+        d["kernel_name"] = KERNELS.get(self.kernel, "unknown")
+        return d
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, where: str = "gemm"):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {gemm_status_string(status)}")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libdtm_gemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, i32, u64 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64
+        ops = [i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, i32, i32]
+        L.gemm.argtypes = ops + [vp]
+        L.gemm.restype = i32
+        L.gemm_plan.argtypes = ops + [ctypes.POINTER(TileConfig), ctypes.POINTER(Plan)]
+        L.gemm_plan.restype = i32
+        L.gemm_ex.argtypes = ops + [ctypes.POINTER(TileConfig), vp, u64, vp]
+        L.gemm_ex.restype = i32
+        L.gemm_status_string.argtypes = [i32]
+        L.gemm_status_string.restype = ctypes.c_char_p
+        L.gemm_kernel_name.argtypes = [i32]
+        L.gemm_kernel_name.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def header_functions():
+    """Names of the functions include/dtm_gemm.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def gemm_status_string(status: int) -> str:
+    return lib().gemm_status_string(int(status)).decode()
+
+
+def gemm_kernel_name(kernel: int) -> str:
+    return lib().gemm_kernel_name(int(kernel)).decode()
+
+
+# ---------------------------------------------------------------- tensors
+
+
+def _dtype_code(dt) -> int:
+    import torch
+
+    codes = {torch.float32: DTM_F32, torch.float16: DTM_F16, torch.bfloat16: DTM_BF16}
+    if dt not in codes:
+        raise TypeError(f"unsupported dtype {dt}; expected float32, float16 or bfloat16")
+    return codes[dt]
+
+
+def _torch_dtype(code_or_dtype):
+    import torch
+
+    if code_or_dtype is None or isinstance(code_or_dtype, torch.dtype):
+        return code_or_dtype
+    return {DTM_F32: torch.float32, DTM_F16: torch.float16, DTM_BF16: torch.bfloat16}[code_or_dtype]
+
+
+def _operands(a, b, out, out_dtype):
+    import torch
+
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D")
+    if a.dtype != b.dtype:
+        raise TypeError(f"a and b must share a dtype ({a.dtype} vs {b.dtype})")
+    M, K = a.shape
+    K2, N = b.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: a is {tuple(a.shape)}, b is {tuple(b.shape)}")
+    if out is None:
+        odt = _torch_dtype(out_dtype) or torch.float32
+        out = torch.empty((M, N), dtype=odt, device=a.device)
+    elif tuple(out.shape) != (M, N):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
+    return M, N, K, out
+
+
+def _args(a, b, out, M, N, K):
+    return (M, N, K, a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(), b.stride(0),
+            b.stride(1), out.data_ptr(), out.stride(0), out.stride(1), _dtype_code(a.dtype),
+            _dtype_code(out.dtype))
+
+
+def _stream(device, stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _config(config):
+    if config is None:
+        return None
+    if isinstance(config, TileConfig):
+        return ctypes.byref(config)
+    c = TileConfig(**config)
+    return ctypes.byref(c)
+
+
+def gemm(a, b, out=None, out_dtype=None, stream=None):
+    """C = a @ b on the GPU through the C ``gemm``; returns ``out``.
+
+    ``a`` (M x K) and ``b`` (K x N) are device tensors of one dtype (float32,
+    float16 or bfloat16) with any strides; ``out`` (M x N) may be given, else
+    it is allocated with ``out_dtype`` (default float32).  The call is
+    asynchronous on ``stream`` (default: torch's current stream).
+    """
+    M, N, K, out = _operands(a, b, out, out_dtype)
+    st = lib().gemm(*_args(a, b, out, M, N, K), _stream(a.device, stream))
+    if st != DTM_OK:
+        raise GemmError(st, "gemm")
+    return out
+
+
+def gemm_ex(a, b, out=None, out_dtype=None, config=None, workspace=None, stream=None):
+    """``gemm`` with a forced tile configuration (a dict of dtm_tile_config
+    fields or a TileConfig) and an optional workspace tensor."""
+    M, N, K, out = _operands(a, b, out, out_dtype)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().gemm_ex(*_args(a, b, out, M, N, K), _config(config), ws_ptr, ws_bytes,
+                       _stream(a.device, stream))
+    if st != DTM_OK:
+        raise GemmError(st, "gemm_ex")
+    return out
+
+
+def gemm_plan(a, b, out=None, out_dtype=None, config=None) -> dict:
+    """The plan ``gemm``/``gemm_ex`` would launch (host only, no GPU needed).
+
+    Tensors may live on any device: only shapes, strides, dtypes and pointer
+    values are read.
+    """
+    M, N, K, out = _operands(a, b, out, out_dtype)
+    p = Plan()
+    st = lib().gemm_plan(*_args(a, b, out, M, N, K), _config(config), ctypes.byref(p))
+    if st != DTM_OK:
+        raise GemmError(st, "gemm_plan")
+    return p.as_dict()
+
+
+def gemm_plan_raw(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C, stride_cm,
+                  stride_cn, in_dtype, out_dtype, config=None):
+    """``gemm_plan`` on raw integers; returns ``(status, plan_dict)``."""
+    p = Plan()
+    st = lib().gemm_plan(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C, stride_cm,
+                         stride_cn, in_dtype, out_dtype, _config(config), ctypes.byref(p))
+    return st, p.as_dict()
+
+
+def gemm_raw(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C, stride_cm, stride_cn,
+             in_dtype, out_dtype, stream=None):
+    """``gemm`` on raw integers (device pointers); returns the status."""
+    s = ctypes.c_void_p(0 if stream is None else int(stream))
+    return lib().gemm(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C, stride_cm,
+                      stride_cn, in_dtype, out_dtype, s)
+
+
+def gemm_ex_raw(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C, stride_cm,
+                stride_cn, in_dtype, out_dtype, config=None, workspace=0, workspace_bytes=0,
+                stream=None):
+    """``gemm_ex`` on raw integers (device pointers); returns the status."""
+    s = ctypes.c_void_p(0 if stream is None else int(stream))
+    return lib().gemm_ex(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C, stride_cm,
+                         stride_cn, in_dtype, out_dtype, _config(config), workspace or None,
+                         workspace_bytes, s)

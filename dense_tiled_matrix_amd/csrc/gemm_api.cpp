@@ -1,0 +1,345 @@
+// gemm_api.cpp -- the C ABI declared in dtm_gemm.h: argument checks, the
+// tile-config selector, and kernel dispatch on the caller's stream.
+//
+// The host side of "Chapter 13: The Blocked Matmul Kernel" section 13.1's
+// wrapper: check the shapes, size the launch grid as
+// (cdiv(M, BLOCK_M), cdiv(N, BLOCK_N)) with cdiv(K, BLOCK_K) K-iterations per
+// tile, and pass the six element strides through.  Unlike the pages' wrapper
+// the output is caller-owned and every check runs before anything is
+// launched ("Triton matmul" notes: a failure before the GPU is reached is the
+// one to want).
+#include <atomic>
+#include <cstring>
+#include <mutex>
+
+#include "dtm_gemm.h"
+#include "launch.h"
+
+namespace {
+
+using dtm::cdiv;
+using dtm::GemmArgs;
+
+struct Call {
+    int64_t M, N, K;
+    const void *A;
+    int64_t sam, sak;
+    const void *B;
+    int64_t sbk, sbn;
+    const void *C;
+    int64_t scm, scn;
+    int in, out;
+};
+
+bool valid_dtype(int d) { return d == DTM_F32 || d == DTM_F16 || d == DTM_BF16; }
+int64_t item_size(int d) { return d == DTM_F32 ? 4 : 2; }
+
+// Byte range [lo, hi) spanned by a rows x cols view; false on overflow.
+bool view_range(const void *base, int64_t rows, int64_t cols, int64_t sr, int64_t sc,
+                int64_t item, uintptr_t &lo, uintptr_t &hi)
+{
+    int64_t er, ec;
+    if (__builtin_mul_overflow(rows - 1, sr, &er) || __builtin_mul_overflow(cols - 1, sc, &ec))
+        return false;
+    const int64_t mn = (er < 0 ? er : 0) + (ec < 0 ? ec : 0);
+    const int64_t mx = (er > 0 ? er : 0) + (ec > 0 ? ec : 0);
+    int64_t blo, bhi;
+    if (__builtin_mul_overflow(mn, item, &blo) || __builtin_mul_overflow(mx + 1, item, &bhi))
+        return false;
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base);
+    lo = b + static_cast<uintptr_t>(blo);  // wraps correctly for negative offsets
+    hi = b + static_cast<uintptr_t>(bhi);
+    if (blo < 0 && static_cast<uintptr_t>(-blo) > b)
+        return false;
+    if (hi < b)
+        return false;
+    return true;
+}
+
+// Distinct (i, j) of an M x N view with these strides never share an element.
+bool c_strides_ok(int64_t M, int64_t N, int64_t scm, int64_t scn)
+{
+    if (scm < 0 || scn < 0)
+        return false;
+    if (M > 1 && scm == 0)
+        return false;
+    if (N > 1 && scn == 0)
+        return false;
+    if (M <= 1 || N <= 1)
+        return true;
+    // the smaller stride's axis must fit entirely inside one step of the larger
+    int64_t s_small = scm, n_small = M, s_big = scn;
+    if (scn < scm) {
+        s_small = scn;
+        n_small = N;
+        s_big = scm;
+    }
+    int64_t span;
+    if (__builtin_mul_overflow(s_small, n_small, &span))
+        return false;
+    return s_big >= span;
+}
+
+int validate(const Call &c)
+{
+    constexpr int64_t kMaxDim = 0x7fffffffLL;
+    if (c.M < 0 || c.N < 0 || c.K < 0 || c.M > kMaxDim || c.N > kMaxDim || c.K > kMaxDim)
+        return DTM_ERR_INVALID_DIM;
+    if (!valid_dtype(c.in) || !valid_dtype(c.out))
+        return DTM_ERR_DTYPE;
+    if (c.M == 0 || c.N == 0)
+        return DTM_OK;
+    if (!c.C)
+        return DTM_ERR_NULL_POINTER;
+    if (c.K > 0 && (!c.A || !c.B))
+        return DTM_ERR_NULL_POINTER;
+    if (!c_strides_ok(c.M, c.N, c.scm, c.scn))
+        return DTM_ERR_STRIDE;
+    uintptr_t clo, chi;
+    if (!view_range(c.C, c.M, c.N, c.scm, c.scn, item_size(c.out), clo, chi))
+        return DTM_ERR_STRIDE;
+    if (c.K > 0) {
+        uintptr_t alo, ahi, blo, bhi;
+        if (!view_range(c.A, c.M, c.K, c.sam, c.sak, item_size(c.in), alo, ahi) ||
+            !view_range(c.B, c.K, c.N, c.sbk, c.sbn, item_size(c.in), blo, bhi))
+            return DTM_ERR_STRIDE;
+        if ((clo < ahi && alo < chi) || (clo < bhi && blo < chi))
+            return DTM_ERR_ALIAS;
+    }
+    return DTM_OK;
+}
+
+// The MFMA fp16/bf16 kernel reads 16-byte chunks along K of A and along N of
+// B: both must be unit-stride, and every chunk start 16-byte aligned.
+bool mfma16_layout_ok(const Call &c)
+{
+    if (c.in != DTM_F16 && c.in != DTM_BF16)
+        return false;
+    if (c.sak != 1 || c.sbn != 1)
+        return false;
+    if ((reinterpret_cast<uintptr_t>(c.A) & 15) || (reinterpret_cast<uintptr_t>(c.B) & 15))
+        return false;
+    if ((c.sam % 8) != 0 || (c.sbk % 8) != 0)
+        return false;
+    return true;
+}
+
+void fill_grid(const Call &c, dtm_plan &p)
+{
+    p.grid_m = cdiv(c.M, p.block_m);
+    p.grid_n = cdiv(c.N, p.block_n);
+    const int64_t k_slice = cdiv(c.K, p.split_k > 0 ? p.split_k : 1);
+    p.k_iters = cdiv(k_slice, p.block_k);
+    p.ragged = (c.M % p.block_m) || (c.N % p.block_n) || (c.K % p.block_k) ? 1 : 0;
+}
+
+// Generic tile for a problem: the largest tile that still gives the chip a
+// few hundred workgroups, down to 16 x 16.
+void pick_generic(const Call &c, dtm_plan &p)
+{
+    struct T {
+        int bm, bn, bk;
+    };
+    static const T order[] = {{64, 64, 16}, {32, 32, 16}, {16, 16, 16}};
+    const T *pick = &order[2];
+    for (const T &t : order) {
+        if (cdiv(c.M, t.bm) * cdiv(c.N, t.bn) >= 512) {
+            pick = &t;
+            break;
+        }
+    }
+    p.block_m = pick->bm;
+    p.block_n = pick->bn;
+    p.block_k = pick->bk;
+}
+
+int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
+{
+    if (!out)
+        return DTM_ERR_NULL_POINTER;
+    std::memset(out, 0, sizeof(*out));
+    const int st = validate(c);
+    if (st != DTM_OK)
+        return st;
+    dtm_plan p;
+    std::memset(&p, 0, sizeof(p));
+    p.split_k = 1;
+    if (c.M == 0 || c.N == 0) {
+        p.kernel = DTM_KERNEL_NONE;
+        *out = p;
+        return DTM_OK;
+    }
+    const bool fast16 = mfma16_layout_ok(c);
+    p.fast_path = fast16 ? 1 : 0;
+    if (c.K == 0) {
+        p.kernel = DTM_KERNEL_ZERO_FILL;
+        p.block_m = p.block_n = p.block_k = 1;
+        p.threads = 256;
+        p.grid_m = c.M;
+        p.grid_n = c.N;
+        *out = p;
+        return DTM_OK;
+    }
+
+    const bool forced_dims = force && (force->block_m || force->block_n || force->block_k);
+    if (force && force->split_k > 1)
+        return DTM_ERR_CONFIG;  // no split-K kernel yet
+    int kernel = force && force->kernel ? force->kernel : (fast16 ? DTM_KERNEL_MFMA_F16
+                                                                  : DTM_KERNEL_GENERIC);
+    if (kernel == DTM_KERNEL_MFMA_F16) {
+        if (!fast16)
+            return DTM_ERR_CONFIG;
+        if (forced_dims) {
+            if (!dtm::mfma16_has_config(force->block_m, force->block_n, force->block_k))
+                return DTM_ERR_CONFIG;
+            p.block_m = force->block_m;
+            p.block_n = force->block_n;
+            p.block_k = force->block_k;
+        } else {
+            const bool big = cdiv(c.M, 256) * cdiv(c.N, 256) >= 256;
+            p.block_m = p.block_n = big ? 256 : 128;
+            p.block_k = 64;
+        }
+        p.threads = 256;
+    } else if (kernel == DTM_KERNEL_GENERIC) {
+        if (forced_dims) {
+            if (!dtm::generic_has_config(force->block_m, force->block_n, force->block_k))
+                return DTM_ERR_CONFIG;
+            p.block_m = force->block_m;
+            p.block_n = force->block_n;
+            p.block_k = force->block_k;
+        } else {
+            pick_generic(c, p);
+        }
+        p.threads = dtm::generic_threads(p.block_m, p.block_n, p.block_k);
+    } else {
+        return DTM_ERR_CONFIG;
+    }
+    p.kernel = kernel;
+    fill_grid(c, p);
+    if (p.grid_m * p.grid_n > 0x7fffffffLL)
+        return DTM_ERR_CONFIG;
+    *out = p;
+    return DTM_OK;
+}
+
+// ---- device check ---------------------------------------------------------
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return DTM_ERR_DEVICE;
+    if (dev < kMaxDevices) {
+        const int known = g_device_ok[dev].load(std::memory_order_acquire);
+        if (known == 1)
+            return DTM_OK;
+        if (known == 2)
+            return DTM_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return DTM_ERR_DEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices)
+        g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_release);
+    return ok ? DTM_OK : DTM_ERR_DEVICE;
+}
+
+int run(const Call &c, const dtm_tile_config *force, void * /*workspace*/,
+        uint64_t /*workspace_bytes*/, void *stream)
+{
+    dtm_plan p;
+    int st = make_plan(c, force, &p);
+    if (st != DTM_OK)
+        return st;
+    if (p.kernel == DTM_KERNEL_NONE)
+        return DTM_OK;
+    st = check_device();
+    if (st != DTM_OK)
+        return st;
+    GemmArgs a{c.M, c.N, c.K, c.A, c.sam, c.sak, c.B, c.sbk, c.sbn, const_cast<void *>(c.C),
+               c.scm, c.scn};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    switch (p.kernel) {
+    case DTM_KERNEL_ZERO_FILL: e = dtm::launch_zero_fill(a, c.out, s); break;
+    case DTM_KERNEL_GENERIC:
+        e = dtm::launch_generic(a, c.in, c.out, p.block_m, p.block_n, p.block_k, s);
+        break;
+    case DTM_KERNEL_MFMA_F16:
+        e = dtm::launch_mfma16(a, c.in, c.out, p.block_m, p.block_n, p.block_k, p.ragged != 0, s);
+        break;
+    default: return DTM_ERR_CONFIG;
+    }
+    return e == hipSuccess ? DTM_OK : DTM_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm(int64_t M, int64_t N, int64_t K, const void *A, int64_t stride_am, int64_t stride_ak,
+         const void *B, int64_t stride_bk, int64_t stride_bn, void *C, int64_t stride_cm,
+         int64_t stride_cn, int in_dtype, int out_dtype, void *stream)
+{
+    const Call c{M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C, stride_cm,
+                 stride_cn, in_dtype, out_dtype};
+    return run(c, nullptr, nullptr, 0, stream);
+}
+
+int gemm_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t stride_am,
+              int64_t stride_ak, const void *B, int64_t stride_bk, int64_t stride_bn,
+              const void *C, int64_t stride_cm, int64_t stride_cn, int in_dtype, int out_dtype,
+              const dtm_tile_config *force, dtm_plan *out)
+{
+    const Call c{M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C, stride_cm,
+                 stride_cn, in_dtype, out_dtype};
+    return make_plan(c, force, out);
+}
+
+int gemm_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t stride_am, int64_t stride_ak,
+            const void *B, int64_t stride_bk, int64_t stride_bn, void *C, int64_t stride_cm,
+            int64_t stride_cn, int in_dtype, int out_dtype, const dtm_tile_config *force,
+            void *workspace, uint64_t workspace_bytes, void *stream)
+{
+    const Call c{M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C, stride_cm,
+                 stride_cn, in_dtype, out_dtype};
+    return run(c, force, workspace, workspace_bytes, stream);
+}
+
+const char *gemm_status_string(int status)
+{
+    switch (status) {
+    case DTM_OK: return "ok";
+    case DTM_ERR_INVALID_DIM: return "invalid dimension: M, N and K must be in [0, 2^31)";
+    case DTM_ERR_NULL_POINTER: return "null pointer for an operand or out-parameter that is needed";
+    case DTM_ERR_DTYPE: return "unknown dtype code (expected DTM_F32, DTM_F16 or DTM_BF16)";
+    case DTM_ERR_STRIDE:
+        return "bad C strides (negative, or two elements of C overlap) or a view whose address "
+               "range overflows";
+    case DTM_ERR_ALIAS: return "C overlaps A or B";
+    case DTM_ERR_CONFIG: return "forced tile configuration is not available for this problem";
+    case DTM_ERR_WORKSPACE: return "workspace too small or its allocation failed";
+    case DTM_ERR_DEVICE: return "current HIP device is not gfx950 or could not be queried";
+    case DTM_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+const char *gemm_kernel_name(int kernel)
+{
+    switch (kernel) {
+    case DTM_KERNEL_NONE: return "none";
+    case DTM_KERNEL_ZERO_FILL: return "zero_fill";
+    case DTM_KERNEL_GENERIC: return "generic";
+    case DTM_KERNEL_MFMA_F16: return "mfma_f16";
+    case DTM_KERNEL_MFMA_F32: return "mfma_f32";
+    }
+    return "unknown";
+}
+
+}  // extern "C"

@@ -1,0 +1,25 @@
+// launch.h -- host-side launchers of the gfx950 kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "device.h"
+
+namespace dtm {
+
+// Generic strided kernel: any strides, any dtype pair, tiles from the fixed
+// list below.  Returns false when (bm, bn, bk) is not one of them.
+bool generic_has_config(int bm, int bn, int bk);
+int generic_threads(int bm, int bn, int bk);
+hipError_t launch_generic(const GemmArgs &a, int in_dtype, int out_dtype, int bm, int bn, int bk,
+                          hipStream_t s);
+
+// MFMA kernel for fp16/bf16 inputs with K-contiguous A and N-contiguous B.
+bool mfma16_has_config(int bm, int bn, int bk);
+hipError_t launch_mfma16(const GemmArgs &a, int in_dtype, int out_dtype, int bm, int bn, int bk,
+                         bool ragged, hipStream_t s);
+
+// Writes zeros to the M x N view of C (the K == 0 product).
+hipError_t launch_zero_fill(const GemmArgs &a, int out_dtype, hipStream_t s);
+
+}  // namespace dtm

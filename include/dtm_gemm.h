@@ -1,0 +1,170 @@
+/*
+ * dtm_gemm.h -- C ABI of libdtm_gemm.so, a blocked GEMM C = A.B for AMD
+ * MI355X (gfx950).
+ *
+ * The operation.  "Chapter 13: The Blocked Matmul Kernel" (Triton from first
+ * principles), section 13.1: a 2-D grid of BLOCK_M x BLOCK_N output tiles;
+ * each tile walks the shared dimension K in BLOCK_K chunks and adds every
+ * chunk's tile product into one fp32 accumulator that is initialised once,
+ * before the loop.  Section 13.2: rows >= M, columns >= N and k >= K are
+ * masked so that they contribute exact zeros.  Section 13.3: the accumulator
+ * stays fp32 whatever the input dtype and is converted to the output dtype
+ * once, at the store.  Operands are strided row/column views as in the
+ * section 13.1 kernel signature (stride_am, stride_ak, stride_bk, stride_bn,
+ * stride_cm, stride_cn), with strides counted in elements, not bytes
+ * ("Triton from zero, Lesson 4: Block Pointers", section 2).  The result is
+ *
+ *     C[i][j] = sum over k in [0, K) of A[i][k] * B[k][j],  0 <= i < M, 0 <= j < N,
+ *
+ * with fp32 products and sums and one round-to-nearest-even conversion of
+ * the fp32 accumulator to out_dtype.
+ *
+ * Conventions shared by every entry point below.
+ *   - Element (i,k) of A is at A + i*stride_am + k*stride_ak, element (k,j)
+ *     of B at B + k*stride_bk + j*stride_bn, element (i,j) of C at
+ *     C + i*stride_cm + j*stride_cn (all in elements of the operand's dtype).
+ *   - A and B share in_dtype.  C has out_dtype.  The accumulator is fp32.
+ *   - C is overwritten (no alpha/beta, no accumulate-into-C).  Nothing of C's
+ *     allocation outside the M x N view is written.
+ *   - All pointers are device memory on the current HIP device, owned by the
+ *     caller.  The library keeps no pointer after a call returns.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
+ *     and the call returns without waiting; the result is visible once the
+ *     caller synchronises that stream.  Calls are thread-safe.
+ *   - Every argument check runs on the host before anything is launched; on
+ *     a non-zero status nothing was launched and C is untouched.
+ *   - A and B may have any strides, including zero (broadcast), negative and
+ *     transposed views.  Layouts the MFMA kernels do not cover run on the
+ *     generic strided kernel instead of being rejected.  The library cannot
+ *     check that pointers and strides stay inside the caller's allocations.
+ *   - M == 0 or N == 0 is a successful no-op.  K == 0 writes zeros (the empty
+ *     sum) to the M x N view of C.
+ */
+#ifndef DTM_GEMM_H
+#define DTM_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+typedef enum {
+    DTM_F32 = 0,  /* IEEE binary32 */
+    DTM_F16 = 1,  /* IEEE binary16 */
+    DTM_BF16 = 2  /* bfloat16: the upper 16 bits of a binary32 */
+} dtm_dtype;
+
+/* Status codes returned by every entry point. */
+typedef enum {
+    DTM_OK = 0,
+    DTM_ERR_INVALID_DIM = 1,  /* M, N or K negative or above 2^31-1 */
+    DTM_ERR_NULL_POINTER = 2, /* a needed pointer (A, B, C or an out-parameter) is NULL */
+    DTM_ERR_DTYPE = 3,        /* in_dtype or out_dtype is not a dtm_dtype */
+    DTM_ERR_STRIDE = 4,       /* C strides negative or making two (i,j) share an element,
+                                 or a view whose address range overflows 64 bits */
+    DTM_ERR_ALIAS = 5,        /* C's address range intersects A's or B's */
+    DTM_ERR_CONFIG = 6,       /* a forced tile configuration that does not exist or
+                                 cannot serve this problem */
+    DTM_ERR_WORKSPACE = 7,    /* workspace smaller than the plan needs, or its allocation
+                                 failed */
+    DTM_ERR_DEVICE = 8,       /* the current device is not gfx950 or cannot be queried */
+    DTM_ERR_LAUNCH = 9        /* the HIP runtime reported an error when launching */
+} dtm_status;
+
+/* Kernels a plan can name. */
+typedef enum {
+    DTM_KERNEL_NONE = 0,      /* nothing to launch (M == 0 or N == 0) */
+    DTM_KERNEL_ZERO_FILL = 1, /* K == 0: write zeros to C */
+    DTM_KERNEL_GENERIC = 2,   /* any strides and dtypes; fp32 FMA on LDS tiles */
+    DTM_KERNEL_MFMA_F16 = 3,  /* fp16/bf16 inputs, K-contiguous A, N-contiguous B; MFMA */
+    DTM_KERNEL_MFMA_F32 = 4   /* fp32 inputs on fp32 MFMA */
+} dtm_kernel;
+
+/* A tile configuration.  Zero fields mean "the selector chooses". */
+typedef struct {
+    int32_t kernel;  /* dtm_kernel, or 0 */
+    int32_t block_m; /* BLOCK_M x BLOCK_N output tile, BLOCK_K chunk of K */
+    int32_t block_n;
+    int32_t block_k;
+    int32_t split_k; /* number of K slices summed by a second pass; 0 or 1 = none */
+} dtm_tile_config;
+
+/* What gemm() would launch for a problem.  Produced on the host only. */
+typedef struct {
+    int32_t kernel;           /* dtm_kernel */
+    int32_t block_m, block_n, block_k;
+    int64_t grid_m;           /* cdiv(M, block_m) output tiles along M */
+    int64_t grid_n;           /* cdiv(N, block_n) output tiles along N */
+    int64_t k_iters;          /* K-loop trip count of one tile: cdiv(K_slice, block_k) */
+    int32_t split_k;          /* K slices (1 = the whole K in one accumulator) */
+    int32_t threads;          /* threads per workgroup */
+    int32_t fast_path;        /* 1 when the MFMA layout and alignment predicate holds */
+    int32_t ragged;           /* 1 when M, N or K is not a multiple of its block */
+    uint64_t workspace_bytes; /* device scratch the plan needs (split-K partials) */
+} dtm_plan;
+
+/*
+ * gemm -- C = A.B (the computation stated at the top of this header).
+ * M, N, K: logical sizes (K is the logical shared dimension, independent of
+ *   the storage A and B are views into).  in_dtype: dtype of A and B;
+ *   out_dtype: dtype of C.  stream: hipStream_t or NULL.
+ * The library picks the kernel and tile with its selector.  When the chosen
+ * plan splits K it uses a per-device workspace owned by the library, grown on
+ * demand (a device allocation the first time a larger one is needed; the
+ * allocation synchronises the device).
+ * Returns a dtm_status.
+ */
+int gemm(int64_t M, int64_t N, int64_t K,
+         const void *A, int64_t stride_am, int64_t stride_ak,
+         const void *B, int64_t stride_bk, int64_t stride_bn,
+         void *C, int64_t stride_cm, int64_t stride_cn,
+         int in_dtype, int out_dtype, void *stream);
+
+/*
+ * gemm_plan -- validate the arguments of gemm() and report the plan it would
+ * launch, on the host, without touching a GPU.  `force` may be NULL (the
+ * selector decides) or a configuration as for gemm_ex().  Writes *out.
+ * Returns the same status gemm()/gemm_ex() would return before launching.
+ */
+int gemm_plan(int64_t M, int64_t N, int64_t K,
+              const void *A, int64_t stride_am, int64_t stride_ak,
+              const void *B, int64_t stride_bk, int64_t stride_bn,
+              const void *C, int64_t stride_cm, int64_t stride_cn,
+              int in_dtype, int out_dtype,
+              const dtm_tile_config *force, dtm_plan *out);
+
+/*
+ * gemm_ex -- gemm() with a forced tile configuration and an optional
+ * caller-owned workspace.
+ * force: NULL or a dtm_tile_config whose non-zero fields override the
+ *   selector (for example {DTM_KERNEL_GENERIC, 4, 4, 4, 0} runs 4x4x4 tiles).
+ *   A configuration the library does not have, or an MFMA kernel for a
+ *   layout it cannot serve, gives DTM_ERR_CONFIG.
+ * workspace, workspace_bytes: device memory of at least plan.workspace_bytes
+ *   bytes, used when the plan splits K; NULL means the library's own
+ *   per-device workspace.  The workspace must not be in use by other work
+ *   that can run concurrently on the device.
+ * Returns a dtm_status.
+ */
+int gemm_ex(int64_t M, int64_t N, int64_t K,
+            const void *A, int64_t stride_am, int64_t stride_ak,
+            const void *B, int64_t stride_bk, int64_t stride_bn,
+            void *C, int64_t stride_cm, int64_t stride_cn,
+            int in_dtype, int out_dtype,
+            const dtm_tile_config *force, void *workspace, uint64_t workspace_bytes,
+            void *stream);
+
+/* gemm_status_string -- a static, NUL-terminated description of a status. */
+const char *gemm_status_string(int status);
+
+/* gemm_kernel_name -- a static name for a dtm_kernel value. */
+const char *gemm_kernel_name(int kernel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DTM_GEMM_H */

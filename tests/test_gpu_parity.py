@@ -1,0 +1,362 @@
+"""GPU parity: the HIP kernels through the C ABI against the CPU oracle.
+
+Bar: value-exact for integer-valued inputs (every partial sum is an integer
+below 2^24, so fp32 accumulation is exact in any order and only the final
+round-to-nearest-even conversion remains); otherwise per element
+|C - C64| <= 1e-5*K*max|a|*max|b| (fp32 inputs) or 4e-3*sqrt(K)*max|a|*max|b|
+(fp16/bf16 inputs), plus half an output ulp for fp16/bf16 outputs, with C64
+the oracle's fp64 result on the same rounded inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dense_tiled_matrix_amd as dtm
+import oracle
+import workloads as W
+from gpu_util import CBuf, compare, dev_storage, note, run
+
+pytestmark = pytest.mark.gpu
+
+GEN = dtm.DTM_KERNEL_GENERIC
+MF16 = dtm.DTM_KERNEL_MFMA_F16
+T444 = dict(kernel=GEN, block_m=4, block_n=4, block_k=4)
+
+
+def int_problem(M, N, K, ind, outd, R, seed, la="N", lb="N"):
+    return W.random_problem(M, N, K, ind, outd, ("int", -R, R), seed, la, lb,
+                            name=f"int{M}x{N}x{K}")
+
+
+def padded_int_problem(M, N, K, ind, outd, R, seed, extra=0):
+    """Integer-valued row-major operands whose leading dimensions are rounded
+    up to a multiple of 8 elements (16 bytes), plus ``extra``; the padding
+    holds NaN, which must never be read."""
+    rng = np.random.default_rng(seed)
+    lda = -(-K // 8) * 8 + extra
+    ldb = -(-N // 8) * 8 + extra
+    abuf = np.full((M, lda), np.nan)
+    abuf[:, :K] = rng.integers(-R, R + 1, size=(M, K))
+    bbuf = np.full((K, ldb), np.nan)
+    bbuf[:, :N] = rng.integers(-R, R + 1, size=(K, N))
+    A = W.Operand(W.to_bits(abuf, ind).reshape(-1), ind, M, K, 0, lda, 1)
+    B = W.Operand(W.to_bits(bbuf, ind).reshape(-1), ind, K, N, 0, ldb, 1)
+    return W.Problem(M, N, K, A, B, ind, outd, name=f"pad{M}x{N}x{K}")
+
+
+# ----------------------------------------------------------- the pages' cases
+
+
+def test_worked_2x2_forced_4x4x4():
+    """The 2x2 single-tile product through one ragged 4x4x4 tile."""
+    p = W.worked_2x2()
+    c, untouched = run(p, config=T444)
+    assert oracle.decode(c, "f32").tolist() == [[19.0, 22.0], [43.0, 50.0]]
+    assert untouched
+
+
+def test_int8x8x8_forced_4x4x4_grid_2x2():
+    """Integer-valued fp32 8x8x8 with 4x4x4 tiles: a (2, 2) grid and two
+    K-iterations per tile (Worked Example 13.1.1's launch); exact."""
+    p = W.workload("int8x8x8_f32")
+    a = torch.empty(8, 8, device="cuda:0")
+    assert dtm.gemm_plan(a, a, config=T444)["k_iters"] == 2
+    c, untouched = run(p, config=T444)
+    compare(p, c, exact=True, label="int8x8x8")
+    assert untouched
+
+
+@pytest.mark.parametrize("M,K,N", [(8, 8, 8), (5, 7, 6)])
+def test_pages_arange_cases(M, K, N):
+    """Worked Examples 13.1.1 and 13.2.1 (0.1*arange inputs, fp32, 4x4x4)."""
+    p = W.arange_problem(M, K, N, scale=0.1)
+    c, _ = run(p, config=T444)
+    compare(p, c, label=f"arange{M}x{K}x{N}")
+    c, _ = run(p)  # the selector's own choice
+    compare(p, c, label=f"arange{M}x{K}x{N} default")
+
+
+@pytest.mark.parametrize("sentinel", [999.0, float("nan"), float("inf")])
+@pytest.mark.parametrize("config", [T444, None])
+def test_sentinel_views(sentinel, config):
+    """Worked Example 13.2.2: A and B are views into buffers whose other slots
+    hold a sentinel.  The result must equal the K-masked table; C sits inside
+    a NaN-filled buffer whose other slots must stay untouched."""
+    p = W.sentinel_problem(sentinel)
+    c, untouched = run(p, config=config, c_pad=3)
+    want = oracle.gemm_problem(W.sentinel_problem(999.0))
+    compare(p, c, c64=want[0], cout=want[1], label=f"sentinel {sentinel}")
+    assert untouched
+
+
+@pytest.mark.parametrize("ind", ["f16", "bf16"])
+@pytest.mark.parametrize("sentinel", [999.0, float("nan")])
+def test_sentinel_views_mfma(ind, sentinel):
+    """The sentinel construction on the MFMA kernel: A is the first K columns
+    of a wider buffer, B the first K rows and N columns of a larger one, both
+    with 16-byte-aligned leading dimensions; every other slot is a sentinel."""
+    M, K, N, ldA, ldB = 40, 37, 50, 64, 72
+    rng = np.random.default_rng(1)
+    abuf = np.full((M, ldA), sentinel)
+    abuf[:, :K] = rng.integers(-8, 9, size=(M, K))
+    bbuf = np.full((K + 9, ldB), sentinel)
+    bbuf[:K, :N] = rng.integers(-8, 9, size=(K, N))
+    A = W.Operand(W.to_bits(abuf, ind).reshape(-1), ind, M, K, 0, ldA, 1)
+    B = W.Operand(W.to_bits(bbuf, ind).reshape(-1), ind, K, N, 0, ldB, 1)
+    p = W.Problem(M, N, K, A, B, ind, "f32")
+    cfg = dict(kernel=MF16, block_m=128, block_n=128, block_k=64)
+    c, untouched = run(p, config=cfg, c_pad=5)
+    compare(p, c, exact=True, label=f"sentinel mfma {ind} {sentinel}")
+    assert untouched
+
+
+def test_seed0_accumulation_fp16_out():
+    """Section 13.3's inputs (4x1024x4 fp16, fp16 output): the fp32
+    accumulator keeps the result at one final rounding of the exact sum, so
+    its max error against the fp64 truth matches the printed fp32-accumulator
+    figure, far below the fp16-accumulator one."""
+    p = W.seed0_fp16_problem()
+    c64, c16 = oracle.gemm_problem(p)
+    fp16acc = oracle.decode(oracle.gemm_fp16acc_problem(p, 8), "f16")
+    for config in [dict(kernel=GEN, block_m=4, block_n=4, block_k=4), None]:
+        c, _ = run(p, config=config)
+        got = oracle.decode(c, "f16")
+        err = float(np.abs(got - c64).max())
+        note(f"fp32-acc err {err!r} vs fp16-acc err {float(np.abs(fp16acc - c64).max())!r}")
+        # equal to rne16(C64) except where the fp32 sum falls on the other side
+        # of an fp16 rounding boundary
+        assert (got != oracle.decode(c16, "f16")).sum() <= 2
+        assert err <= 9.737179152580211e-05 * 1.01
+        assert err * 10 < float(np.abs(fp16acc - c64).max())
+
+
+# ------------------------------------------------------ the measured workloads
+
+
+def test_ragged_f32_transposed_a():
+    """257x129x193 fp32, A a transposed view (strides (1, 257)), N(0,1)."""
+    p = W.workload("ragged257x129x193_f32_At")
+    assert (p.A.stride_r, p.A.stride_c) == (1, 257)
+    c, untouched = run(p)
+    err, tol = compare(p, c, label="ragged257")
+    note(f"ragged257x129x193 f32: max err {err:.3e} tol {tol:.3e}")
+    assert untouched
+
+
+def _sample_rows_cols(M, N, tile, per_tile=1, seed=0):
+    """At least one row per tile-row and one column per tile-column."""
+    rng = np.random.default_rng(seed)
+    rows = sorted({int(t * tile + rng.integers(0, tile)) for t in range(M // tile)
+                   for _ in range(per_tile)} | {0, M - 1})
+    cols = sorted({int(t * tile + rng.integers(0, tile)) for t in range(N // tile)
+                   for _ in range(per_tile)} | {0, N - 1})
+    return rows, cols
+
+
+def _big_check(p, tile):
+    """Full-size run in the launch configuration the bench times, checked on
+    sampled rows and columns covering every output tile, plus a Freivalds
+    probe of the whole result."""
+    note(f"{p.name}: {p.M}x{p.N}x{p.K} {p.in_dtype}->{p.out_dtype}")
+    sa, sb = dev_storage(p.A.bits, p.in_dtype), dev_storage(p.B.bits, p.in_dtype)
+    TD = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    a = sa.view(TD[p.in_dtype]).view(p.M, p.K)
+    b = sb.view(TD[p.in_dtype]).view(p.K, p.N)
+    plan = dtm.gemm_plan(a, b, out_dtype=TD[p.out_dtype])
+    assert plan["kernel_name"] == "mfma_f16" and plan["block_m"] == tile, plan
+    c = dtm.gemm(a, b, out_dtype=TD[p.out_dtype])
+    torch.cuda.synchronize()
+    cb = c.view(torch.int32 if p.out_dtype == "f32" else torch.int16).cpu().numpy()
+    cb = cb.view(np.uint32 if p.out_dtype == "f32" else np.uint16)
+    rows, cols = _sample_rows_cols(p.M, p.N, tile)
+    A2 = p.A.bits.reshape(p.M, p.K)
+    B2 = p.B.bits.reshape(p.K, p.N)
+    # sampled rows: all of B, the chosen rows of A
+    pr = W.Problem(len(rows), p.N, p.K, W.dense(A2[rows], p.in_dtype), p.B, p.in_dtype,
+                   p.out_dtype)
+    err_r, tol = compare(pr, cb[rows], label=f"{p.name} rows")
+    # sampled columns: all of A, the chosen columns of B
+    pc = W.Problem(p.M, len(cols), p.K, p.A, W.dense(B2[:, cols], p.in_dtype), p.in_dtype,
+                   p.out_dtype)
+    err_c, _ = compare(pc, cb[:, cols], label=f"{p.name} cols")
+    # Freivalds: u^T C v against (u^T A)(B v), bounded by tol * sum|u| * sum|v|
+    rng = np.random.default_rng(5)
+    u = rng.choice([-1.0, 1.0], size=p.M)
+    v = rng.choice([-1.0, 1.0], size=p.N)
+    Ad = oracle.decode(A2, p.in_dtype)
+    Bd = oracle.decode(B2, p.in_dtype)
+    Cd = oracle.decode(cb, p.out_dtype)
+    lhs = u @ (Cd @ v)
+    rhs = (u @ Ad) @ (Bd @ v)
+    assert np.isfinite(Cd).all()
+    bound = (tol + float(np.abs(Cd).max()) * 2.0 ** -8) * p.M * p.N
+    assert abs(lhs - rhs) <= bound
+    note(f"{p.name}: rows/cols max err {max(err_r, err_c):.3e} tol {tol:.3e}; "
+         f"Freivalds |d| {abs(lhs - rhs):.3e}")
+    return max(err_r, err_c), tol
+
+
+def test_f16_4096_f32out():
+    _big_check(W.workload("f16_4096_f32out"), 256)
+
+
+def test_bf16_8192_bf16out():
+    _big_check(W.workload("bf16_8192_bf16out"), 256)
+
+
+def test_f16_skinny_long_k():
+    """512x512x65536 fp16 U[0,1] -> fp32: full comparison, plus the
+    accumulation-error report against section 13.3's fp16 accumulator
+    (emulated by the oracle on a 64x64 corner with the kernel's BLOCK_K)."""
+    p = W.workload("f16_skinny512x512x65536_f32out")
+    note(f"{p.name}: {p.M}x{p.N}x{p.K}")
+    c, untouched = run(p)
+    c64, cout = oracle.gemm_problem(p)
+    err, tol = compare(p, c, c64=c64, cout=cout, label=p.name)
+    plan_bk = 64
+    A2, B2 = p.A.bits.reshape(p.M, p.K), p.B.bits.reshape(p.K, p.N)
+    corner = oracle.gemm_fp16acc(64, 64, p.K, np.ascontiguousarray(A2[:64]), 0, p.K, 1,
+                                 np.ascontiguousarray(B2[:, :64]), 0, 64, 1, "f16", plan_bk)
+    err16 = float(np.abs(oracle.decode(corner, "f16") - c64[:64, :64]).max())
+    gerr = float(np.abs(oracle.decode(c, "f32")[:64, :64] - c64[:64, :64]).max())
+    note(f"long-K: fp32-acc max err {err:.3e} (corner {gerr:.3e}) vs fp16-acc emulation "
+         f"{err16:.3e} (BLOCK_K {plan_bk}); tol {tol:.3e}")
+    assert gerr * 100 < err16
+    assert untouched
+
+
+# ------------------------------------------------------------ ragged sweeps
+
+EDGE = [1, 2, 3, 15, 16, 17, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+def _sweep_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    shapes = [(1, 1, 1), (257, 257, 257), (129, 1, 65), (1, 300, 1), (64, 64, 1)]
+    while len(shapes) < n:
+        shapes.append(tuple(int(x) for x in rng.choice(EDGE, size=3)))
+    return shapes
+
+
+@pytest.mark.parametrize("ind", ["f16", "bf16"])
+@pytest.mark.parametrize("tile", [128, 256])
+def test_mfma_ragged_sweep_exact(ind, tile):
+    """Integer-valued inputs on the MFMA kernel at edge sizes around the
+    tile (both tiles), every output dtype: value-exact."""
+    cfg = dict(kernel=MF16, block_m=tile, block_n=tile, block_k=64)
+    for n, (M, N, K) in enumerate(_sweep_shapes(14, seed=tile + len(ind))):
+        outd = ["f32", "f16", "bf16"][n % 3]
+        p = padded_int_problem(M, N, K, ind, outd, 8, seed=100 + n, extra=8 * (n % 2))
+        c, untouched = run(p, config=cfg, c_pad=2 if n % 2 else 0)
+        compare(p, c, exact=True, label=f"{ind} {tile} {M}x{N}x{K}->{outd}")
+        assert untouched
+
+
+@pytest.mark.parametrize("layout", ["NN", "NT", "TN", "TT"])
+@pytest.mark.parametrize("ind", ["f32", "f16", "bf16"])
+def test_generic_layouts_sweep_exact(layout, ind):
+    """All four transpose combinations on the generic kernel, ragged sizes,
+    each of its tile shapes: value-exact on integer-valued inputs."""
+    cfgs = [dict(kernel=GEN, block_m=b, block_n=b, block_k=k)
+            for b, k in [(4, 4), (16, 16), (32, 16), (64, 16), (128, 8)]]
+    R = 16 if ind == "bf16" else 32
+    for n, (M, N, K) in enumerate(_sweep_shapes(8, seed=len(layout) + len(ind))):
+        outd = ["f32", "f16", "bf16"][n % 3]
+        p = int_problem(M, N, K, ind, outd, R, seed=200 + n, la=layout[0], lb=layout[1])
+        c, untouched = run(p, config=cfgs[n % len(cfgs)], c_layout="T" if n % 2 else "N")
+        compare(p, c, exact=True, label=f"{layout} {ind} {M}x{N}x{K}")
+        assert untouched
+
+
+@pytest.mark.parametrize("ind", ["f32", "f16", "bf16"])
+def test_random_values_default_plan(ind):
+    """N(0,1) inputs at ragged sizes through the selector's own plan."""
+    for n, (M, N, K) in enumerate([(300, 200, 150), (1000, 513, 777), (64, 4097, 33),
+                                   (511, 257, 1025)]):
+        p = W.random_problem(M, N, K, ind, "f32", ("normal", 0.0, 1.0), seed=300 + n)
+        c, _ = run(p)
+        err, tol = compare(p, c, label=f"{ind} {M}x{N}x{K}")
+        note(f"{ind} {M}x{N}x{K}: max err {err:.3e} tol {tol:.3e}")
+
+
+def test_negative_and_zero_strides():
+    """Negative row strides and a broadcast (zero-stride) row on the generic
+    kernel."""
+    rng = np.random.default_rng(9)
+    M, N, K = 33, 21, 17
+    a = rng.integers(-9, 10, size=(M, K)).astype(np.float64)
+    b = rng.integers(-9, 10, size=(K, N)).astype(np.float64)
+    A = W.Operand(W.to_bits(a[::-1].copy(), "f32").reshape(-1), "f32", M, K, (M - 1) * K, -K, 1)
+    B = W.dense(W.to_bits(b, "f32"), "f32")
+    p = W.Problem(M, N, K, A, B, "f32", "f32")
+    assert np.array_equal(A.logical_bits(), W.to_bits(a, "f32"))
+    c, _ = run(p)
+    compare(p, c, exact=True, label="negative stride")
+    row = W.Operand(W.to_bits(a[0], "f32"), "f32", M, K, 0, 0, 1)
+    p2 = W.Problem(M, N, K, row, B, "f32", "f32")
+    c, _ = run(p2)
+    compare(p2, c, exact=True, label="broadcast")
+
+
+# ------------------------------------------------------------ semantics
+
+
+@pytest.mark.parametrize("outd", ["f32", "f16", "bf16"])
+def test_k_zero_writes_zeros(outd):
+    p = W.Problem(37, 19, 0, W.Operand(np.zeros(1, np.uint16), "f16", 37, 0, 0, 0, 1),
+                  W.Operand(np.zeros(1, np.uint16), "f16", 0, 19, 0, 19, 1), "f16", outd)
+    c, untouched = run(p, c_pad=3)
+    assert not oracle.decode(c, outd).any()
+    assert untouched
+
+
+def test_m_or_n_zero_writes_nothing():
+    for (M, N) in [(0, 7), (7, 0)]:
+        buf = torch.full((64,), 12345, dtype=torch.int32, device="cuda:0")
+        a = torch.ones(max(M, 1), 5, device="cuda:0")
+        st = dtm.gemm_raw(M, N, 5, a.data_ptr(), 5, 1, a.data_ptr(), 7, 1, buf.data_ptr(), 7, 1,
+                          dtm.DTM_F32, dtm.DTM_F32)
+        torch.cuda.synchronize()
+        assert st == 0 and bool((buf == 12345).all())
+
+
+def test_deterministic():
+    p = W.random_problem(1024, 768, 2048, "bf16", "f32", ("normal", 0.0, 1.0), seed=17)
+    c1, _ = run(p)
+    c2, _ = run(p)
+    assert np.array_equal(c1, c2)
+    q = W.random_problem(200, 300, 500, "f32", "f32", ("normal", 0.0, 1.0), seed=18,
+                         a_layout="T")
+    assert np.array_equal(run(q)[0], run(q)[0])
+
+
+def test_non_default_stream_ordering():
+    """The work is enqueued on the caller's stream: it sees writes made
+    earlier on that stream and is complete after that stream synchronises."""
+    s = torch.cuda.Stream()
+    M = N = K = 512
+    with torch.cuda.stream(s):
+        a = torch.zeros(M, K, dtype=torch.float16, device="cuda:0")
+        b = torch.zeros(K, N, dtype=torch.float16, device="cuda:0")
+        a.fill_(1.0)  # ordered before the GEMM on s
+        b.fill_(2.0)
+        c = dtm.gemm(a, b, stream=s)
+    s.synchronize()
+    assert bool((c == 2.0 * K).all())
+
+
+def test_tensor_binding_views():
+    """The torch-level binding: strides and storage offsets of views pass
+    through unchanged."""
+    base = torch.randn(300, 400, device="cuda:0")
+    a = base[10:210, 5:105].t()  # 100 x 200, column-major view with offset
+    b = torch.randn(200, 50, device="cuda:0")[:, ::2]  # stride 2 columns
+    out = torch.empty(100, 25, device="cuda:0")
+    dtm.gemm(a, b, out=out)
+    torch.cuda.synchronize()
+    p = W.Problem(100, 25, 200,
+                  W.Operand(a.contiguous().cpu().numpy().view(np.uint32).reshape(-1), "f32", 100,
+                            200, 0, 200, 1),
+                  W.Operand(b.contiguous().cpu().numpy().view(np.uint32).reshape(-1), "f32", 200,
+                            25, 0, 25, 1), "f32", "f32")
+    compare(p, out.cpu().numpy().view(np.uint32), label="torch views")

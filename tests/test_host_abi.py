@@ -1,0 +1,164 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/dtm_gemm.h declares, plans launches ("Chapter 13: The
+Blocked Matmul Kernel", Worked Example 13.1.1: an 8x8x8 product with 4x4x4
+tiles runs a (2, 2) grid with 2 K-iterations per tile) and rejects bad
+arguments before anything is launched."""
+import ctypes
+
+import pytest
+
+import dense_tiled_matrix_amd as dtm
+
+F32, F16, BF16 = dtm.DTM_F32, dtm.DTM_F16, dtm.DTM_BF16
+# fake, 256-byte-aligned, far-apart addresses: gemm_plan only reads pointer values
+PA, PB, PC = 0x10000000, 0x20000000, 0x30000000
+
+
+def plan(M, N, K, A=PA, sam=None, sak=1, B=PB, sbk=None, sbn=1, C=PC, scm=None, scn=1,
+         ind=F16, outd=F32, config=None):
+    sam = K if sam is None else sam
+    sbk = N if sbk is None else sbk
+    scm = N if scm is None else scm
+    return dtm.gemm_plan_raw(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, ind, outd, config)
+
+
+def test_library_exports_every_declared_function():
+    names = dtm.header_functions()
+    assert {"gemm", "gemm_plan", "gemm_ex", "gemm_status_string", "gemm_kernel_name"} <= set(names)
+    L = dtm.lib()
+    for n in names:
+        assert hasattr(L, n), n
+        assert isinstance(getattr(L, n), ctypes._CFuncPtr)
+
+
+def test_status_strings():
+    for code, name in dtm.STATUS.items():
+        s = dtm.gemm_status_string(code)
+        assert s and s != "unknown status", name
+    assert dtm.gemm_status_string(999) == "unknown status"
+    assert dtm.gemm_kernel_name(dtm.DTM_KERNEL_MFMA_F16) == "mfma_f16"
+
+
+def test_plan_worked_example_grid():
+    """8x8x8 with forced 4x4x4 tiles: grid (2, 2), 2 K-iterations."""
+    st, p = plan(8, 8, 8, ind=F32, config=dict(kernel=dtm.DTM_KERNEL_GENERIC, block_m=4, block_n=4,
+                                                 block_k=4))
+    assert st == 0
+    assert (p["grid_m"], p["grid_n"], p["k_iters"]) == (2, 2, 2)
+    assert p["kernel_name"] == "generic" and p["threads"] == 16 and p["ragged"] == 0
+
+
+def test_plan_ragged_awkward_dims():
+    """Worked Example 13.2.1: M, K, N = 5, 7, 6 with 4x4x4 tiles -> grid (2, 2),
+    2 K-iterations, and every dimension ragged."""
+    st, p = plan(5, 6, 7, ind=F32, config=dict(kernel=dtm.DTM_KERNEL_GENERIC, block_m=4, block_n=4,
+                                                 block_k=4))
+    assert st == 0 and (p["grid_m"], p["grid_n"], p["k_iters"]) == (2, 2, 2) and p["ragged"] == 1
+    st, p = plan(2, 2, 2, ind=F32, config=dict(kernel=dtm.DTM_KERNEL_GENERIC, block_m=4, block_n=4,
+                                                 block_k=4))
+    assert st == 0 and (p["grid_m"], p["grid_n"], p["k_iters"]) == (1, 1, 1) and p["ragged"] == 1
+
+
+def test_selector_measured_workloads():
+    st, p = plan(4096, 4096, 4096, ind=F16, outd=F32)
+    assert st == 0 and p["kernel_name"] == "mfma_f16" and p["fast_path"] == 1
+    assert (p["block_m"], p["block_n"], p["block_k"]) == (256, 256, 64)
+    assert (p["grid_m"], p["grid_n"], p["k_iters"], p["ragged"]) == (16, 16, 64, 0)
+    st, p = plan(8192, 8192, 8192, ind=BF16, outd=BF16)
+    assert st == 0 and p["kernel_name"] == "mfma_f16"
+    assert (p["grid_m"], p["grid_n"], p["k_iters"]) == (32, 32, 128)
+    # fp32 with a transposed A view: the generic strided kernel
+    st, p = plan(257, 129, 193, sam=1, sak=257, ind=F32, outd=F32)
+    assert st == 0 and p["kernel_name"] == "generic" and p["fast_path"] == 0 and p["ragged"] == 1
+
+
+@pytest.mark.parametrize("kw,why", [
+    (dict(sak=2), "A not K-contiguous"),
+    (dict(sbn=3), "B not N-contiguous"),
+    (dict(A=PA + 2), "A base not 16-byte aligned"),
+    (dict(B=PB + 8), "B base not 16-byte aligned"),
+    (dict(sam=1001), "A leading dimension not a multiple of 8 elements"),
+    (dict(sbk=999), "B leading dimension not a multiple of 8 elements"),
+    (dict(ind=F32), "fp32 inputs"),
+])
+def test_fast_path_predicate_falls_back_to_generic(kw, why):
+    st, p = plan(1024, 1024, 1000, **kw)
+    assert st == 0, why
+    assert p["fast_path"] == 0 and p["kernel_name"] == "generic", why
+    # forcing the MFMA kernel on such a layout is a configuration error
+    st, _ = plan(1024, 1024, 1000, config=dict(kernel=dtm.DTM_KERNEL_MFMA_F16), **kw)
+    assert st == dtm.DTM_ERR_CONFIG
+
+
+def test_degenerate_shapes():
+    st, p = plan(0, 5, 7)
+    assert st == 0 and p["kernel_name"] == "none"
+    st, p = plan(5, 0, 7, A=0, B=0, C=0)  # nothing to do: pointers are not needed
+    assert st == 0 and p["kernel_name"] == "none"
+    st, p = plan(5, 6, 0, A=0, B=0)  # K == 0: zeros into C, A and B never read
+    assert st == 0 and p["kernel_name"] == "zero_fill"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), "DTM_ERR_INVALID_DIM"),
+    (dict(K=-5), "DTM_ERR_INVALID_DIM"),
+    (dict(N=2 ** 31), "DTM_ERR_INVALID_DIM"),
+    (dict(ind=7), "DTM_ERR_DTYPE"),
+    (dict(outd=-1), "DTM_ERR_DTYPE"),
+    (dict(A=0), "DTM_ERR_NULL_POINTER"),
+    (dict(B=0), "DTM_ERR_NULL_POINTER"),
+    (dict(C=0), "DTM_ERR_NULL_POINTER"),
+    (dict(scm=-64), "DTM_ERR_STRIDE"),
+    (dict(scm=0), "DTM_ERR_STRIDE"),
+    (dict(scm=32), "DTM_ERR_STRIDE"),           # rows overlap: 32 < N = 64
+    (dict(scm=1, scn=32), "DTM_ERR_STRIDE"),    # columns overlap: 32 < M = 48
+    (dict(C=PA + 64), "DTM_ERR_ALIAS"),         # C inside A
+    (dict(C=PB - 100), "DTM_ERR_ALIAS"),        # C runs into B
+    (dict(sam=2 ** 62), "DTM_ERR_STRIDE"),      # A's address range overflows
+])
+def test_validation_errors(kw, status):
+    args = dict(M=48, N=64, K=32)
+    for k in ("M", "N", "K"):
+        if k in kw:
+            args[k] = kw.pop(k)
+    st, p = plan(args["M"], args["N"], args["K"], **kw)
+    assert dtm.STATUS[st] == status
+    assert p["kernel"] == 0
+
+
+def test_c_strides_accepted():
+    # column-major C, padded C, and a single row / column with any stride
+    assert plan(48, 64, 32, scm=1, scn=48)[0] == 0
+    assert plan(48, 64, 32, scm=100, scn=1)[0] == 0
+    assert plan(1, 64, 32, scm=0, scn=1)[0] == 0
+    assert plan(48, 1, 32, scm=1, scn=0)[0] == 0
+
+
+def test_a_and_b_may_alias_each_other_and_broadcast():
+    # A and B may overlap (both are only read) and may have zero strides
+    assert plan(48, 64, 32, B=PA)[0] == 0
+    st, p = plan(48, 64, 32, sam=0, ind=F32)
+    assert st == 0 and p["kernel_name"] == "generic"
+    st, p = plan(48, 64, 32, sam=-32, A=PA + 48 * 32 * 2, ind=F32)
+    assert st == 0
+
+
+def test_forced_configs():
+    gen = dtm.DTM_KERNEL_GENERIC
+    assert plan(64, 64, 64, config=dict(kernel=gen, block_m=4, block_n=4, block_k=4))[0] == 0
+    assert plan(64, 64, 64, config=dict(kernel=gen, block_m=5, block_n=4, block_k=4))[0] == \
+        dtm.DTM_ERR_CONFIG
+    mf = dtm.DTM_KERNEL_MFMA_F16
+    st, p = plan(64, 64, 64, config=dict(kernel=mf, block_m=128, block_n=128, block_k=64))
+    assert st == 0 and p["grid_m"] == 1 and p["ragged"] == 1
+    assert plan(64, 64, 64, config=dict(kernel=mf, block_m=64, block_n=64, block_k=64))[0] == \
+        dtm.DTM_ERR_CONFIG
+    assert plan(64, 64, 64, config=dict(kernel=99))[0] == dtm.DTM_ERR_CONFIG
+
+
+def test_gemm_rejects_before_touching_a_device():
+    """Argument errors come back from gemm() itself without any GPU."""
+    assert dtm.gemm_raw(-1, 4, 4, PA, 4, 1, PB, 4, 1, PC, 4, 1, F32, F32) == \
+        dtm.DTM_ERR_INVALID_DIM
+    assert dtm.gemm_raw(4, 4, 4, PA, 4, 1, PB, 4, 1, PA, 4, 1, F32, F32) == dtm.DTM_ERR_ALIAS
+    assert dtm.gemm_raw(0, 4, 4, 0, 4, 1, 0, 4, 1, 0, 4, 1, F32, F32) == dtm.DTM_OK
