@@ -120,6 +120,9 @@ def main():
                     help="comma-separated workloads also timed (not the headline)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run 3 plain device copies of this many MiB (a known-size "
+                         "reference for hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -133,6 +136,15 @@ def main():
     import workloads as W
 
     TD = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def measure(name):
         p = W.workload(name)

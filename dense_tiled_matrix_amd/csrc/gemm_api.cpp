@@ -189,8 +189,12 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
     if (kernel == DTM_KERNEL_MFMA_F16) {
         if (!fast16)
             return DTM_ERR_CONFIG;
+        const bool dma = dtm::mfma16_dma_fits(c.M, c.N, c.K);
         if (forced_dims) {
-            if (!dtm::mfma16_has_config(force->block_m, force->block_n, force->block_k))
+            const bool dma_cfg = force->block_m == 256 && force->block_n == 256 &&
+                                 force->block_k == 32;
+            if (dma_cfg ? !dma
+                        : !dtm::mfma16_has_config(force->block_m, force->block_n, force->block_k))
                 return DTM_ERR_CONFIG;
             p.block_m = force->block_m;
             p.block_n = force->block_n;
@@ -198,7 +202,7 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
         } else {
             const bool big = cdiv(c.M, 256) * cdiv(c.N, 256) >= 256;
             p.block_m = p.block_n = big ? 256 : 128;
-            p.block_k = 64;
+            p.block_k = big && dma ? 32 : 64;
         }
         p.threads = 256;
     } else if (kernel == DTM_KERNEL_GENERIC) {
@@ -271,7 +275,11 @@ int run(const Call &c, const dtm_tile_config *force, void * /*workspace*/,
         e = dtm::launch_generic(a, c.in, c.out, p.block_m, p.block_n, p.block_k, s);
         break;
     case DTM_KERNEL_MFMA_F16:
-        e = dtm::launch_mfma16(a, c.in, c.out, p.block_m, p.block_n, p.block_k, p.ragged != 0, s);
+        if (p.block_k == 32)
+            e = dtm::launch_mfma16_dma(a, c.in, c.out, s);
+        else
+            e = dtm::launch_mfma16(a, c.in, c.out, p.block_m, p.block_n, p.block_k,
+                                   p.ragged != 0, s);
         break;
     default: return DTM_ERR_CONFIG;
     }

@@ -1,0 +1,325 @@
+// gemm_mfma16_dma.hip -- deep-pipelined MFMA GEMM for fp16/bf16 inputs on
+// gfx950, for problems whose M, N are multiples of 256 and K of 32.
+//
+// The computation is the blocked product of "Chapter 13: The Blocked Matmul
+// Kernel" (section 13.1): one workgroup per 256 x 256 output tile, a K-loop
+// over 32-deep chunks adding each chunk's tile product into an fp32
+// accumulator zeroed once before the loop, and a single conversion to the
+// output dtype at the store (section 13.3).  No edge masking is needed on
+// this path ("Triton from zero, Lesson 4: Block Pointers", homework 3: pay
+// only for the raggedness a problem has); ragged problems use the other MFMA
+// kernel.
+//
+// gfx950 design:
+//  * 4 wave64s (2 x 2), each owning 128 x 128 of C as 4 x 4 tiles of
+//    v_mfma_f32_32x32x16_{f16,bf16}; 256 fp32 accumulators per lane in the
+//    AccVGPR file.
+//  * Operands move global -> LDS with global_load_lds_dwordx4 (each wave
+//    instruction writes 1 KiB of LDS, lane i's 16 bytes at offset 16*i), so
+//    no VGPRs stage them.  Four LDS stages of (16 + 16) KiB: the chunk
+//    loaded at iteration k is consumed at k + 3, which hides about three
+//    chunks of MFMA time of memory latency.  One barrier per chunk, after a
+//    wait for exactly the loads of the chunk about to be read.
+//  * A is stored row-major (64 bytes per row); the 16-byte chunk c of row r
+//    sits at position c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, so the
+//    fragment reads (16 consecutive rows, one chunk each) touch distinct
+//    bank groups.
+//  * B stays N-contiguous (512 bytes per k-row); chunk c of k-row k sits at
+//    c ^ g(k), g = {0, 6, 10, 12}[k % 4].  Fragments are read with
+//    ds_read_b64_tr_b16, which hands lane i of each 16-lane group the
+//    i-th column of a 4 x 16 block whose rows the lanes address, i.e. four
+//    consecutive k of one column -- the MFMA B operand -- with no transpose
+//    anywhere else.
+//  * Workgroup ids are remapped so that each XCD owns a compact group of
+//    tiles (shared A rows and B columns stay in its L2).
+#include "launch.h"
+
+namespace dtm {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
+
+constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4;
+constexpr int A_STAGE_BYTES = BM * BK * 2;  // 16 KiB
+constexpr int B_STAGE_BYTES = BK * BN * 2;  // 16 KiB
+constexpr int STAGE_BYTES = A_STAGE_BYTES + B_STAGE_BYTES;
+constexpr int DMA_PER_WAVE = 4;             // 1 KiB instructions per operand per wave
+constexpr int64_t GROUP_M = 4;
+
+// s_waitcnt immediate (gfx9 layout): vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8],
+// vmcnt[5:4] in bits [15:14].
+constexpr int waitcnt_imm(int vm, int lgkm)
+{
+    return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | (((vm >> 4) & 3) << 14);
+}
+
+__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz_b(int k)
+{
+    // 0, 6, 10, 12 for k % 4 = 0..3
+    return (0xCA60 >> (4 * (k & 3))) & 15;
+}
+
+// 16 bytes per lane from global memory straight into LDS at
+// lds_addr + 16 * lane (global_load_lds_dwordx4; M0 holds the LDS address).
+__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+template <int IN>
+__device__ __forceinline__ floatx16 mfma(const u32x4 &a, const u32x4 &b, const floatx16 &c)
+{
+    if constexpr (IN == DTM_F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
+                                                      __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0,
+                                                       0);
+}
+
+template <int IN, int OUT>
+__global__ __launch_bounds__(256) void gemm_mfma16_dma_kernel(GemmArgs p, int64_t grid_m,
+                                                              int64_t grid_n)
+{
+    __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    int64_t pid_m, pid_n;
+    grouped_tile(xcd_remap(blockIdx.x, grid_m * grid_n), grid_m, grid_n, GROUP_M, pid_m, pid_n);
+    const int64_t m0 = pid_m * BM, n0 = pid_n * BN;
+
+    const uint16_t *A = static_cast<const uint16_t *>(p.A);
+    const uint16_t *B = static_cast<const uint16_t *>(p.B);
+
+    // ---- DMA source addresses of this lane -------------------------------
+    // A instruction j of wave w fills LDS chunks 64*(4w+j) .. +63, i.e. rows
+    // 16*(4w+j) + lane/4, physical chunk lane%4.
+    const uint16_t *a_src[DMA_PER_WAVE];
+#pragma unroll
+    for (int j = 0; j < DMA_PER_WAVE; ++j) {
+        const int r = 16 * (DMA_PER_WAVE * wave + j) + (lane >> 2);
+        const int c = (lane & 3) ^ swz_a(r);
+        a_src[j] = A + (m0 + r) * p.sam + 8 * c;
+    }
+    // B instruction j of wave w fills k-rows 2*(4w+j) + lane/32, physical
+    // chunk lane%32.
+    const uint16_t *b_src[DMA_PER_WAVE];
+#pragma unroll
+    for (int j = 0; j < DMA_PER_WAVE; ++j) {
+        const int k = 2 * (DMA_PER_WAVE * wave + j) + (lane >> 5);
+        const int c = (lane & 31) ^ swz_b(k);
+        b_src[j] = B + (int64_t)k * p.sbk + n0 + 8 * c;
+    }
+    const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, lds)));
+    const uint32_t a_dst0 = lds_base + (DMA_PER_WAVE * wave) * 1024;
+    const uint32_t b_dst0 = lds_base + A_STAGE_BYTES + (DMA_PER_WAVE * wave) * 1024;
+
+    // Chunk kt into LDS stage `stage`.  Issued as inline assembly so that the
+    // compiler neither reorders nor waits on these asynchronous LDS writes;
+    // the loop below waits for them explicitly (vmcnt) before a barrier.
+    auto issue_dma = [&](int64_t kt, int stage) __attribute__((always_inline)) {
+        const int64_t k0 = kt * BK;
+        const uint32_t so = static_cast<uint32_t>(stage) * STAGE_BYTES;
+#pragma unroll
+        for (int j = 0; j < DMA_PER_WAVE; ++j)
+            dma16(a_src[j] + k0, a_dst0 + so + 1024 * j);
+#pragma unroll
+        for (int j = 0; j < DMA_PER_WAVE; ++j)
+            dma16(b_src[j] + k0 * p.sbk, b_dst0 + so + 1024 * j);
+    };
+
+    // ---- fragment read offsets (bytes within a stage) ---------------------
+    // A: lane reads row wm*128 + i*32 + lane%32, logical chunk 2*kk + lane/32.
+    int a_off[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = wm * 128 + i * 32 + (lane & 31);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            a_off[i][kk] = r * 64 + (((2 * kk + (lane >> 5)) ^ swz_a(r)) * 16);
+    }
+    // B (transposing read): within 16-lane group G = lane/16, lane i = lane%16
+    // addresses k-row kk*16 + 8*(G/2) + 4*e + i/4 at column
+    // wn*128 + j*32 + 16*(G%2) + 4*(i%4).
+    const int G = lane >> 4, li = lane & 15;
+    int b_off[4][2][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int k = kk * 16 + 8 * (G >> 1) + 4 * e + (li >> 2);
+                const int n = wn * 128 + j * 32 + 16 * (G & 1) + 4 * (li & 3);
+                b_off[j][kk][e] = A_STAGE_BYTES + k * 512 + (((n >> 3) ^ swz_b(k)) * 16) +
+                                  ((n >> 2) & 1) * 8;
+            }
+
+    // Fragments of one 16-deep k-step: 4 A row blocks, 4 B column blocks.
+    struct Frags {
+        u32x4 a[4], b[4];
+    };
+    auto read_frags = [&](Frags &f, int stage, int kk) __attribute__((always_inline)) {
+        const char *st = lds + stage * STAGE_BYTES;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            f.a[i] = *LDS_PTR(const u32x4, st + a_off[i][kk]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const s16x4 lo =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, st + b_off[j][kk][0]));
+            const s16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, st + b_off[j][kk][1]));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+            const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+            f.b[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
+        }
+    };
+
+    floatx16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = floatx16{0.0f};
+
+    auto mfmas = [&](const Frags &f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = mfma<IN>(f.a[i], f.b[j], acc[i][j]);
+    };
+
+    // Interleave the 12 LDS reads of the next k-step with the 16 MFMAs of
+    // the current one: MFMA, read, MFMA, read, ... so that read latency hides
+    // under matrix work.
+    auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 12; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);  // one DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x0008, 4, 0);
+    };
+
+    // Pipeline.  Chunk kt lives in stage kt % 4; DMA for chunk kt + 3 is
+    // issued in iteration kt right after the barrier that proves every wave
+    // finished reading that stage (it held chunk kt - 1).  Within iteration
+    // kt: MFMAs of k-step 0 while reading k-step 1's fragments; wait for
+    // this wave's loads of chunk kt + 1 and barrier; MFMAs of k-step 1 while
+    // reading chunk kt + 1's first fragments.
+    const int64_t nk = p.K / BK;
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk)
+            issue_dma(s, s);
+    if (nk > 2)
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * 2 * DMA_PER_WAVE, 0));
+    else if (nk > 1)
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * DMA_PER_WAVE, 0));
+    else
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    Frags f0, f1;
+    read_frags(f0, 0, 0);
+    for (int64_t kt = 0; kt + 1 < nk; ++kt) {
+        const int stage = static_cast<int>(kt % STAGES);
+        read_frags(f1, stage, 1);
+        mfmas(f0);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        // chunk kt + 1 must be in LDS (this wave's part) before the barrier
+        if (kt + 2 < nk)
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * DMA_PER_WAVE, 15));
+        else
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kt + STAGES - 1 < nk)
+            issue_dma(kt + STAGES - 1, static_cast<int>((kt + STAGES - 1) % STAGES));
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(f0, (stage + 1) % STAGES, 0);
+        mfmas(f1);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // last chunk
+    read_frags(f1, static_cast<int>((nk - 1) % STAGES), 1);
+    mfmas(f0);
+    mfmas(f1);
+
+    // Epilogue: lane holds column lane%32 and rows 8*(v/4) + 4*(lane/32) + v%4
+    // of each 32x32 tile.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                store_elem<OUT>(p.C, row * p.scm + col * p.scn, acc[i][j][v]);
+            }
+        }
+    }
+}
+
+template <int IN, int OUT>
+hipError_t launch(const GemmArgs &a, hipStream_t s)
+{
+    const int64_t gm = a.M / BM, gn = a.N / BN;
+    hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT>), dim3((unsigned)(gm * gn)), dim3(256), 0,
+                       s, a, gm, gn);
+    return hipGetLastError();
+}
+
+template <int IN>
+hipError_t dispatch_out(const GemmArgs &a, int out, hipStream_t s)
+{
+    switch (out) {
+    case DTM_F32: return launch<IN, DTM_F32>(a, s);
+    case DTM_F16: return launch<IN, DTM_F16>(a, s);
+    case DTM_BF16: return launch<IN, DTM_BF16>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool mfma16_dma_fits(int64_t M, int64_t N, int64_t K)
+{
+    return M > 0 && N > 0 && K > 0 && M % BM == 0 && N % BN == 0 && K % BK == 0 &&
+           (M / BM) * (N / BN) <= 0x7fffffffLL;
+}
+
+hipError_t launch_mfma16_dma(const GemmArgs &a, int in, int out, hipStream_t s)
+{
+    if (!mfma16_dma_fits(a.M, a.N, a.K))
+        return hipErrorInvalidConfiguration;
+    switch (in) {
+    case DTM_F16: return dispatch_out<DTM_F16>(a, out, s);
+    case DTM_BF16: return dispatch_out<DTM_BF16>(a, out, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dtm

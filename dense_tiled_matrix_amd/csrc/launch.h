@@ -19,6 +19,11 @@ bool mfma16_has_config(int bm, int bn, int bk);
 hipError_t launch_mfma16(const GemmArgs &a, int in_dtype, int out_dtype, int bm, int bn, int bk,
                          bool ragged, hipStream_t s);
 
+// Deep-pipelined MFMA kernel (256 x 256 x 32 tiles, global -> LDS DMA) for
+// the same layouts when M and N are multiples of 256 and K of 32.
+bool mfma16_dma_fits(int64_t M, int64_t N, int64_t K);
+hipError_t launch_mfma16_dma(const GemmArgs &a, int in_dtype, int out_dtype, hipStream_t s);
+
 // Writes zeros to the M x N view of C (the K == 0 product).
 hipError_t launch_zero_fill(const GemmArgs &a, int out_dtype, hipStream_t s);
 

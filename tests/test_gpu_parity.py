@@ -252,6 +252,23 @@ def test_mfma_ragged_sweep_exact(ind, tile):
         assert untouched
 
 
+@pytest.mark.parametrize("ind", ["f16", "bf16"])
+def test_mfma_pipelined_exact(ind):
+    """The 256x256x32 pipelined kernel (global->LDS DMA, 4 stages) at every
+    trip count of its pipeline (1, 2, 3, 4 and many K-chunks) and several
+    grid shapes: value-exact on integer-valued inputs, all output dtypes."""
+    cfg = dict(kernel=MF16, block_m=256, block_n=256, block_k=32)
+    shapes = [(256, 256, 32), (256, 256, 64), (512, 256, 96), (256, 512, 128),
+              (768, 512, 160), (512, 1024, 2048), (1280, 256, 4096)]
+    for n, (M, N, K) in enumerate(shapes):
+        outd = ["f32", "f16", "bf16"][n % 3]
+        R = 8 if K <= 256 else 2
+        p = padded_int_problem(M, N, K, ind, outd, R, seed=400 + n, extra=8 * (n % 2))
+        c, untouched = run(p, config=cfg, c_pad=4 if n % 2 else 0)
+        compare(p, c, exact=True, label=f"pipelined {ind} {M}x{N}x{K}->{outd}")
+        assert untouched
+
+
 @pytest.mark.parametrize("layout", ["NN", "NT", "TN", "TT"])
 @pytest.mark.parametrize("ind", ["f32", "f16", "bf16"])
 def test_generic_layouts_sweep_exact(layout, ind):

@@ -62,11 +62,14 @@ def test_plan_ragged_awkward_dims():
 def test_selector_measured_workloads():
     st, p = plan(4096, 4096, 4096, ind=F16, outd=F32)
     assert st == 0 and p["kernel_name"] == "mfma_f16" and p["fast_path"] == 1
-    assert (p["block_m"], p["block_n"], p["block_k"]) == (256, 256, 64)
-    assert (p["grid_m"], p["grid_n"], p["k_iters"], p["ragged"]) == (16, 16, 64, 0)
+    assert (p["block_m"], p["block_n"], p["block_k"]) == (256, 256, 32)
+    assert (p["grid_m"], p["grid_n"], p["k_iters"], p["ragged"]) == (16, 16, 128, 0)
     st, p = plan(8192, 8192, 8192, ind=BF16, outd=BF16)
     assert st == 0 and p["kernel_name"] == "mfma_f16"
-    assert (p["grid_m"], p["grid_n"], p["k_iters"]) == (32, 32, 128)
+    assert (p["grid_m"], p["grid_n"], p["k_iters"]) == (32, 32, 256)
+    # ragged edges keep the 64-deep register-staged kernel
+    st, p = plan(4096, 4096, 4100, sam=4104, ind=F16, outd=F32)
+    assert st == 0 and (p["block_m"], p["block_k"], p["ragged"]) == (256, 64, 1)
     # fp32 with a transposed A view: the generic strided kernel
     st, p = plan(257, 129, 193, sam=1, sak=257, ind=F32, outd=F32)
     assert st == 0 and p["kernel_name"] == "generic" and p["fast_path"] == 0 and p["ragged"] == 1
@@ -153,6 +156,11 @@ def test_forced_configs():
     assert st == 0 and p["grid_m"] == 1 and p["ragged"] == 1
     assert plan(64, 64, 64, config=dict(kernel=mf, block_m=64, block_n=64, block_k=64))[0] == \
         dtm.DTM_ERR_CONFIG
+    # the 32-deep pipelined tile needs M, N multiples of 256 and K of 32
+    dma = dict(kernel=mf, block_m=256, block_n=256, block_k=32)
+    assert plan(512, 256, 96, config=dma)[0] == 0
+    assert plan(512, 256, 100, sam=104, config=dma)[0] == dtm.DTM_ERR_CONFIG
+    assert plan(500, 256, 96, config=dma)[0] == dtm.DTM_ERR_CONFIG
     assert plan(64, 64, 64, config=dict(kernel=99))[0] == dtm.DTM_ERR_CONFIG
 
 
