@@ -21,11 +21,14 @@
 //    chunks of MFMA time of memory latency.  One barrier per chunk, after a
 //    wait for exactly the loads of the chunk about to be read.
 //  * A is stored row-major (64 bytes per row); the 16-byte chunk c of row r
-//    sits at position c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, so the
-//    fragment reads (16 consecutive rows, one chunk each) touch distinct
-//    bank groups.
+//    sits at position c ^ f(r), f(r) = (r >> 2) & 3, so each group of 16
+//    consecutive rows read by a fragment load (one chunk each) covers all 64
+//    banks once.  (Measured on gfx950 with SQ_LDS_BANK_CONFLICT: zero
+//    conflicts for this pattern; other XOR patterns cost 4-12 extra cycles
+//    per ds_read_b128.)
 //  * B stays N-contiguous (512 bytes per k-row); chunk c of k-row k sits at
-//    c ^ g(k), g = {0, 6, 10, 12}[k % 4].  Fragments are read with
+//    c ^ g(k), g = {0, 6, 10, 12}[k % 4] (measured conflict-free for the
+//    transposing reads below; no swizzle costs about 6 extra cycles each).  Fragments are read with
 //    ds_read_b64_tr_b16, which hands lane i of each 16-lane group the
 //    i-th column of a 4 x 16 block whose rows the lanes address, i.e. four
 //    consecutive k of one column -- the MFMA B operand -- with no transpose
@@ -51,7 +54,10 @@ constexpr int A_STAGE_BYTES = BM * BK * 2;  // 16 KiB
 constexpr int B_STAGE_BYTES = BK * BN * 2;  // 16 KiB
 constexpr int STAGE_BYTES = A_STAGE_BYTES + B_STAGE_BYTES;
 constexpr int DMA_PER_WAVE = 4;             // 1 KiB instructions per operand per wave
-constexpr int64_t GROUP_M = 4;
+#ifndef DTM_DMA_GROUP_M
+#define DTM_DMA_GROUP_M 4
+#endif
+constexpr int64_t GROUP_M = DTM_DMA_GROUP_M;  // tile-rows walked together per XCD
 
 // s_waitcnt immediate (gfx9 layout): vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8],
 // vmcnt[5:4] in bits [15:14].
@@ -60,7 +66,7 @@ constexpr int waitcnt_imm(int vm, int lgkm)
     return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | (((vm >> 4) & 3) << 14);
 }
 
-__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz_a(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int swz_b(int k)
 {
     // 0, 6, 10, 12 for k % 4 = 0..3
@@ -207,35 +213,72 @@ __global__ __launch_bounds__(256) void gemm_mfma16_dma_kernel(GemmArgs p, int64_
                 acc[i][j] = mfma<IN>(f.a[i], f.b[j], acc[i][j]);
     };
 
-    // Interleave the 12 LDS reads of the next k-step with the 16 MFMAs of
-    // the current one: MFMA, read, MFMA, read, ... so that read latency hides
-    // under matrix work.
-    auto interleave = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int q = 0; q < 12; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);  // one DS read
+    // One read of the next k-step's fragments (q = 0..11: 4 A blocks, then
+    // the low and high halves of 4 B blocks).
+    auto read_one = [&](Frags &f, const char *st, int kk, int q) __attribute__((always_inline)) {
+        if (q < 4) {
+            f.a[q] = *LDS_PTR(const u32x4, st + a_off[q][kk]);
+        } else {
+            const int j = (q - 4) >> 1, e = (q - 4) & 1;
+            const s16x4 v =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, st + b_off[j][kk][e]));
+            const u32x2 w = __builtin_bit_cast(u32x2, v);
+            if (e == 0) {
+                f.b[j].x = w.x;
+                f.b[j].y = w.y;
+            } else {
+                f.b[j].z = w.x;
+                f.b[j].w = w.y;
+            }
         }
-        __builtin_amdgcn_sched_group_barrier(0x0008, 4, 0);
     };
 
-    // Pipeline.  Chunk kt lives in stage kt % 4; DMA for chunk kt + 3 is
-    // issued in iteration kt right after the barrier that proves every wave
-    // finished reading that stage (it held chunk kt - 1).  Within iteration
-    // kt: MFMAs of k-step 0 while reading k-step 1's fragments; wait for
-    // this wave's loads of chunk kt + 1 and barrier; MFMAs of k-step 1 while
-    // reading chunk kt + 1's first fragments.
+    // The 16 MFMAs of one k-step with the 12 reads of the next k-step's
+    // fragments interleaved one after each of the first 12 MFMAs, and (when
+    // `dma`) the 8 global->LDS loads of chunk `dma_kt` after every second
+    // MFMA.  The DMA statements are inline assembly with a memory clobber,
+    // which pins the order of everything around them.
+    auto half_step = [&](const Frags &cur, Frags &next, const char *next_st, int next_kk,
+                         bool dma, int64_t dma_kt, int dma_stage) __attribute__((always_inline)) {
+        const int64_t k0 = dma_kt * BK;
+        const uint32_t so = static_cast<uint32_t>(dma_stage) * STAGE_BYTES;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int i = q >> 2, j = q & 3;
+            acc[i][j] = mfma<IN>(cur.a[i], cur.b[j], acc[i][j]);
+            if (q < 12)
+                read_one(next, next_st, next_kk, q);
+            if (dma && (q & 1)) {
+                const int d = q >> 1;
+                if (d < DMA_PER_WAVE)
+                    dma16(a_src[d] + k0, a_dst0 + so + 1024 * d);
+                else
+                    dma16(b_src[d - DMA_PER_WAVE] + k0 * p.sbk,
+                          b_dst0 + so + 1024 * (d - DMA_PER_WAVE));
+            }
+            if (dma) {
+                __builtin_amdgcn_sched_barrier(0);  // keep this triple in place
+            } else {
+                __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // the MFMA
+                if (q < 12)
+                    __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);  // the read
+            }
+        }
+    };
+
+    // Pipeline.  Chunk kt lives in stage kt % 4.  Iteration kt: MFMAs of
+    // k-step 0 while reading k-step 1's fragments; wait for this wave's loads
+    // of chunk kt + 1 and barrier (after it every wave has finished reading
+    // stage (kt + 3) % 4, which held chunk kt - 1); MFMAs of k-step 1 while
+    // reading chunk kt + 1's first fragments and loading chunk kt + 3 into
+    // stage (kt + 3) % 4.  Past the end the loads re-read the last chunk into
+    // that (no longer read) stage, which keeps the count of loads in flight
+    // the same every iteration.
     const int64_t nk = p.K / BK;
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nk)
-            issue_dma(s, s);
-    if (nk > 2)
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * 2 * DMA_PER_WAVE, 0));
-    else if (nk > 1)
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * DMA_PER_WAVE, 0));
-    else
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        issue_dma(s < nk ? s : nk - 1, s);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * 2 * DMA_PER_WAVE, 0));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 
@@ -243,29 +286,24 @@ __global__ __launch_bounds__(256) void gemm_mfma16_dma_kernel(GemmArgs p, int64_
     read_frags(f0, 0, 0);
     for (int64_t kt = 0; kt + 1 < nk; ++kt) {
         const int stage = static_cast<int>(kt % STAGES);
-        read_frags(f1, stage, 1);
-        mfmas(f0);
-        interleave();
+        const char *st = lds + stage * STAGE_BYTES;
+        half_step(f0, f1, st, 1, false, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         // chunk kt + 1 must be in LDS (this wave's part) before the barrier
-        if (kt + 2 < nk)
-            __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * DMA_PER_WAVE, 15));
-        else
-            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * DMA_PER_WAVE, 15));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (kt + STAGES - 1 < nk)
-            issue_dma(kt + STAGES - 1, static_cast<int>((kt + STAGES - 1) % STAGES));
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(f0, (stage + 1) % STAGES, 0);
-        mfmas(f1);
-        interleave();
+        const int64_t kl = kt + STAGES - 1 < nk ? kt + STAGES - 1 : nk - 1;
+        half_step(f1, f0, lds + ((stage + 1) % STAGES) * STAGE_BYTES, 0, true, kl,
+                  static_cast<int>((kt + STAGES - 1) % STAGES));
         __builtin_amdgcn_sched_barrier(0);
     }
     // last chunk
     read_frags(f1, static_cast<int>((nk - 1) % STAGES), 1);
     mfmas(f0);
     mfmas(f1);
+    // no load may still be writing LDS when the workgroup ends
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
 
     // Epilogue: lane holds column lane%32 and rows 8*(v/4) + 4*(lane/32) + v%4
     // of each 32x32 tile.
