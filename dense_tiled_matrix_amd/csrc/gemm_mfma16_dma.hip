@@ -16,10 +16,10 @@
 //    AccVGPR file.
 //  * Operands move global -> LDS with global_load_lds_dwordx4 (each wave
 //    instruction writes 1 KiB of LDS, lane i's 16 bytes at offset 16*i), so
-//    no VGPRs stage them.  Four LDS stages of (16 + 16) KiB: the chunk
-//    loaded at iteration k is consumed at k + 3, which hides about three
-//    chunks of MFMA time of memory latency.  One barrier per chunk, after a
-//    wait for exactly the loads of the chunk about to be read.
+//    no VGPRs stage them.  Four LDS stages of (16 + 16) KiB: a chunk is
+//    loaded three to four chunks of MFMA time before it is read.  One
+//    barrier per chunk, after a wait for exactly the loads of the chunk
+//    about to be read; the loads are issued one after every second MFMA.
 //  * A is stored row-major (64 bytes per row); the 16-byte chunk c of row r
 //    sits at position c ^ f(r), f(r) = (r >> 2) & 3, so each group of 16
 //    consecutive rows read by a fragment load (one chunk each) covers all 64
@@ -53,7 +53,6 @@ constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4;
 constexpr int A_STAGE_BYTES = BM * BK * 2;  // 16 KiB
 constexpr int B_STAGE_BYTES = BK * BN * 2;  // 16 KiB
 constexpr int STAGE_BYTES = A_STAGE_BYTES + B_STAGE_BYTES;
-constexpr int DMA_PER_WAVE = 4;             // 1 KiB instructions per operand per wave
 #ifndef DTM_DMA_GROUP_M
 #define DTM_DMA_GROUP_M 4
 #endif
@@ -95,16 +94,27 @@ __device__ __forceinline__ floatx16 mfma(const u32x4 &a, const u32x4 &b, const f
                                                        0);
 }
 
-template <int IN, int OUT>
-__global__ __launch_bounds__(256) void gemm_mfma16_dma_kernel(GemmArgs p, int64_t grid_m,
-                                                              int64_t grid_n)
+template <int IN, int OUT, int NWAVES>
+__global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p, int64_t grid_m,
+                                                                      int64_t grid_n)
 {
+    // Waves form a 2 x (NWAVES/2) grid over the 256 x 256 tile; each owns
+    // 128 rows and 256/(NWAVES/2) columns as MT x NT tiles of 32 x 32.
+    constexpr int WAVES_N = NWAVES / 2;
+    constexpr int WN_COLS = BN / WAVES_N;
+    constexpr int MT = 4, NT = WN_COLS / 32;
+    constexpr int NREAD = MT + 2 * NT;           // LDS reads per k-step
+    constexpr int NMFMA = MT * NT;               // MFMAs per k-step
+    constexpr int DPO = 16 / NWAVES;             // 1 KiB loads per operand per wave per chunk
+    constexpr int DMA_GROUP = 2 * DPO;           // loads per wave per chunk
+    static_assert(NREAD <= NMFMA && DMA_GROUP <= NMFMA / 2, "interleave slots");
+
     __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
     int64_t pid_m, pid_n;
     grouped_tile(xcd_remap(blockIdx.x, grid_m * grid_n), grid_m, grid_n, GROUP_M, pid_m, pid_n);
@@ -113,48 +123,47 @@ __global__ __launch_bounds__(256) void gemm_mfma16_dma_kernel(GemmArgs p, int64_
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
 
-    // ---- DMA source addresses of this lane -------------------------------
-    // A instruction j of wave w fills LDS chunks 64*(4w+j) .. +63, i.e. rows
-    // 16*(4w+j) + lane/4, physical chunk lane%4.
-    const uint16_t *a_src[DMA_PER_WAVE];
+    // ---- load source addresses of this lane ------------------------------
+    // A load j of wave w fills LDS bytes 1024*(DPO*w + j) .. +1023 of the A
+    // stage: rows 16*(DPO*w + j) + lane/4, physical chunk lane%4.
+    const uint16_t *a_src[DPO];
 #pragma unroll
-    for (int j = 0; j < DMA_PER_WAVE; ++j) {
-        const int r = 16 * (DMA_PER_WAVE * wave + j) + (lane >> 2);
+    for (int j = 0; j < DPO; ++j) {
+        const int r = 16 * (DPO * wave + j) + (lane >> 2);
         const int c = (lane & 3) ^ swz_a(r);
         a_src[j] = A + (m0 + r) * p.sam + 8 * c;
     }
-    // B instruction j of wave w fills k-rows 2*(4w+j) + lane/32, physical
+    // B load j of wave w fills k-rows 2*(DPO*w + j) + lane/32, physical
     // chunk lane%32.
-    const uint16_t *b_src[DMA_PER_WAVE];
+    const uint16_t *b_src[DPO];
 #pragma unroll
-    for (int j = 0; j < DMA_PER_WAVE; ++j) {
-        const int k = 2 * (DMA_PER_WAVE * wave + j) + (lane >> 5);
+    for (int j = 0; j < DPO; ++j) {
+        const int k = 2 * (DPO * wave + j) + (lane >> 5);
         const int c = (lane & 31) ^ swz_b(k);
         b_src[j] = B + (int64_t)k * p.sbk + n0 + 8 * c;
     }
     const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, lds)));
-    const uint32_t a_dst0 = lds_base + (DMA_PER_WAVE * wave) * 1024;
-    const uint32_t b_dst0 = lds_base + A_STAGE_BYTES + (DMA_PER_WAVE * wave) * 1024;
+    const uint32_t a_dst0 = lds_base + (DPO * wave) * 1024;
+    const uint32_t b_dst0 = lds_base + A_STAGE_BYTES + (DPO * wave) * 1024;
 
-    // Chunk kt into LDS stage `stage`.  Issued as inline assembly so that the
-    // compiler neither reorders nor waits on these asynchronous LDS writes;
-    // the loop below waits for them explicitly (vmcnt) before a barrier.
-    auto issue_dma = [&](int64_t kt, int stage) __attribute__((always_inline)) {
+    // Load d (0 .. DMA_GROUP-1) of chunk kt into LDS stage `stage`.  Inline
+    // assembly, so the compiler neither reorders nor waits on these
+    // asynchronous LDS writes; the loop waits for them explicitly (vmcnt)
+    // before a barrier.
+    auto dma_one = [&](int64_t kt, int stage, int d) __attribute__((always_inline)) {
         const int64_t k0 = kt * BK;
         const uint32_t so = static_cast<uint32_t>(stage) * STAGE_BYTES;
-#pragma unroll
-        for (int j = 0; j < DMA_PER_WAVE; ++j)
-            dma16(a_src[j] + k0, a_dst0 + so + 1024 * j);
-#pragma unroll
-        for (int j = 0; j < DMA_PER_WAVE; ++j)
-            dma16(b_src[j] + k0 * p.sbk, b_dst0 + so + 1024 * j);
+        if (d < DPO)
+            dma16(a_src[d] + k0, a_dst0 + so + 1024 * d);
+        else
+            dma16(b_src[d - DPO] + k0 * p.sbk, b_dst0 + so + 1024 * (d - DPO));
     };
 
     // ---- fragment read offsets (bytes within a stage) ---------------------
     // A: lane reads row wm*128 + i*32 + lane%32, logical chunk 2*kk + lane/32.
-    int a_off[4][2];
+    int a_off[MT][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MT; ++i) {
         const int r = wm * 128 + i * 32 + (lane & 31);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
@@ -162,64 +171,32 @@ __global__ __launch_bounds__(256) void gemm_mfma16_dma_kernel(GemmArgs p, int64_
     }
     // B (transposing read): within 16-lane group G = lane/16, lane i = lane%16
     // addresses k-row kk*16 + 8*(G/2) + 4*e + i/4 at column
-    // wn*128 + j*32 + 16*(G%2) + 4*(i%4).
+    // wn*WN_COLS + j*32 + 16*(G%2) + 4*(i%4).
     const int G = lane >> 4, li = lane & 15;
-    int b_off[4][2][2];
+    int b_off[NT][2][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int k = kk * 16 + 8 * (G >> 1) + 4 * e + (li >> 2);
-                const int n = wn * 128 + j * 32 + 16 * (G & 1) + 4 * (li & 3);
+                const int n = wn * WN_COLS + j * 32 + 16 * (G & 1) + 4 * (li & 3);
                 b_off[j][kk][e] = A_STAGE_BYTES + k * 512 + (((n >> 3) ^ swz_b(k)) * 16) +
                                   ((n >> 2) & 1) * 8;
             }
 
-    // Fragments of one 16-deep k-step: 4 A row blocks, 4 B column blocks.
+    // Fragments of one 16-deep k-step.
     struct Frags {
-        u32x4 a[4], b[4];
+        u32x4 a[MT], b[NT];
     };
-    auto read_frags = [&](Frags &f, int stage, int kk) __attribute__((always_inline)) {
-        const char *st = lds + stage * STAGE_BYTES;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            f.a[i] = *LDS_PTR(const u32x4, st + a_off[i][kk]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const s16x4 lo =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, st + b_off[j][kk][0]));
-            const s16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, st + b_off[j][kk][1]));
-            const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-            const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-            f.b[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
-        }
-    };
-
-    floatx16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = floatx16{0.0f};
-
-    auto mfmas = [&](const Frags &f) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = mfma<IN>(f.a[i], f.b[j], acc[i][j]);
-    };
-
-    // One read of the next k-step's fragments (q = 0..11: 4 A blocks, then
-    // the low and high halves of 4 B blocks).
+    // Read q of a k-step's fragments: q < MT the A blocks, then the low and
+    // high halves of the NT B blocks.
     auto read_one = [&](Frags &f, const char *st, int kk, int q) __attribute__((always_inline)) {
-        if (q < 4) {
+        if (q < MT) {
             f.a[q] = *LDS_PTR(const u32x4, st + a_off[q][kk]);
         } else {
-            const int j = (q - 4) >> 1, e = (q - 4) & 1;
+            const int j = (q - MT) >> 1, e = (q - MT) & 1;
             const s16x4 v =
                 __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, st + b_off[j][kk][e]));
             const u32x2 w = __builtin_bit_cast(u32x2, v);
@@ -232,53 +209,67 @@ __global__ __launch_bounds__(256) void gemm_mfma16_dma_kernel(GemmArgs p, int64_
             }
         }
     };
+    auto read_frags = [&](Frags &f, int stage, int kk) __attribute__((always_inline)) {
+        const char *st = lds + stage * STAGE_BYTES;
+#pragma unroll
+        for (int q = 0; q < NREAD; ++q)
+            read_one(f, st, kk, q);
+    };
 
-    // The 16 MFMAs of one k-step with the 12 reads of the next k-step's
-    // fragments interleaved one after each of the first 12 MFMAs, and (when
-    // `dma`) the 8 global->LDS loads of chunk `dma_kt` after every second
-    // MFMA.  The DMA statements are inline assembly with a memory clobber,
-    // which pins the order of everything around them.
+    floatx16 acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+            acc[i][j] = floatx16{0.0f};
+
+    auto mfmas = [&](const Frags &f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                acc[i][j] = mfma<IN>(f.a[i], f.b[j], acc[i][j]);
+    };
+
+    // The MFMAs of one k-step with the reads of the next k-step's fragments
+    // interleaved one after each MFMA, and (when `dma`) the loads of chunk
+    // `dma_kt` one after every second MFMA.
     auto half_step = [&](const Frags &cur, Frags &next, const char *next_st, int next_kk,
                          bool dma, int64_t dma_kt, int dma_stage) __attribute__((always_inline)) {
-        const int64_t k0 = dma_kt * BK;
-        const uint32_t so = static_cast<uint32_t>(dma_stage) * STAGE_BYTES;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int i = q >> 2, j = q & 3;
+        for (int q = 0; q < NMFMA; ++q) {
+            const int i = q / NT, j = q % NT;
             acc[i][j] = mfma<IN>(cur.a[i], cur.b[j], acc[i][j]);
-            if (q < 12)
+            if (q < NREAD)
                 read_one(next, next_st, next_kk, q);
-            if (dma && (q & 1)) {
-                const int d = q >> 1;
-                if (d < DMA_PER_WAVE)
-                    dma16(a_src[d] + k0, a_dst0 + so + 1024 * d);
-                else
-                    dma16(b_src[d - DMA_PER_WAVE] + k0 * p.sbk,
-                          b_dst0 + so + 1024 * (d - DMA_PER_WAVE));
-            }
+            if (dma && (q & 1) && (q >> 1) < DMA_GROUP)
+                dma_one(dma_kt, dma_stage, q >> 1);
             if (dma) {
-                __builtin_amdgcn_sched_barrier(0);  // keep this triple in place
+                __builtin_amdgcn_sched_barrier(0);  // keep this group in place
             } else {
                 __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // the MFMA
-                if (q < 12)
+                if (q < NREAD)
                     __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);  // the read
             }
         }
     };
 
     // Pipeline.  Chunk kt lives in stage kt % 4.  Iteration kt: MFMAs of
-    // k-step 0 while reading k-step 1's fragments; wait for this wave's loads
-    // of chunk kt + 1 and barrier (after it every wave has finished reading
-    // stage (kt + 3) % 4, which held chunk kt - 1); MFMAs of k-step 1 while
-    // reading chunk kt + 1's first fragments and loading chunk kt + 3 into
-    // stage (kt + 3) % 4.  Past the end the loads re-read the last chunk into
-    // that (no longer read) stage, which keeps the count of loads in flight
-    // the same every iteration.
+    // k-step 0 while reading k-step 1's fragments; wait until this wave's
+    // loads of chunk kt + 1 have landed and all its LDS reads have returned,
+    // then barrier -- after it every wave is done with stage kt % 4, since
+    // both k-steps of chunk kt were read before it; MFMAs of k-step 1 while
+    // reading chunk kt + 1's first fragments and loading chunk kt + 4 into
+    // stage kt % 4.  Chunks kt + 2 .. kt + 4 are in flight meanwhile.  Past
+    // the end the loads re-read the last chunk into the freed stage, which
+    // keeps the number of loads in flight the same every iteration.
     const int64_t nk = p.K / BK;
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        issue_dma(s < nk ? s : nk - 1, s);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * 2 * DMA_PER_WAVE, 0));
+    for (int s = 0; s < STAGES; ++s)
+#pragma unroll
+        for (int d = 0; d < DMA_GROUP; ++d)
+            dma_one(s < nk ? s : nk - 1, s, d);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * DMA_GROUP, 0));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 
@@ -289,13 +280,11 @@ __global__ __launch_bounds__(256) void gemm_mfma16_dma_kernel(GemmArgs p, int64_
         const char *st = lds + stage * STAGE_BYTES;
         half_step(f0, f1, st, 1, false, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        // chunk kt + 1 must be in LDS (this wave's part) before the barrier
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * DMA_PER_WAVE, 15));
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * DMA_GROUP, 0));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        const int64_t kl = kt + STAGES - 1 < nk ? kt + STAGES - 1 : nk - 1;
-        half_step(f1, f0, lds + ((stage + 1) % STAGES) * STAGE_BYTES, 0, true, kl,
-                  static_cast<int>((kt + STAGES - 1) % STAGES));
+        const int64_t kl = kt + STAGES < nk ? kt + STAGES : nk - 1;
+        half_step(f1, f0, lds + ((stage + 1) % STAGES) * STAGE_BYTES, 0, true, kl, stage);
         __builtin_amdgcn_sched_barrier(0);
     }
     // last chunk
@@ -308,10 +297,10 @@ __global__ __launch_bounds__(256) void gemm_mfma16_dma_kernel(GemmArgs p, int64_
     // Epilogue: lane holds column lane%32 and rows 8*(v/4) + 4*(lane/32) + v%4
     // of each 32x32 tile.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MT; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
+        for (int j = 0; j < NT; ++j) {
+            const int64_t col = n0 + wn * WN_COLS + j * 32 + (lane & 31);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int64_t row = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
@@ -321,12 +310,16 @@ __global__ __launch_bounds__(256) void gemm_mfma16_dma_kernel(GemmArgs p, int64_
     }
 }
 
+#ifndef DTM_DMA_WAVES
+#define DTM_DMA_WAVES 8
+#endif
+
 template <int IN, int OUT>
 hipError_t launch(const GemmArgs &a, hipStream_t s)
 {
     const int64_t gm = a.M / BM, gn = a.N / BN;
-    hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT>), dim3((unsigned)(gm * gn)), dim3(256), 0,
-                       s, a, gm, gn);
+    hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, DTM_DMA_WAVES>), dim3((unsigned)(gm * gn)),
+                       dim3(64 * DTM_DMA_WAVES), 0, s, a, gm, gn);
     return hipGetLastError();
 }
 

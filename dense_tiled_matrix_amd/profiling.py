@@ -1,0 +1,138 @@
+"""Summaries of rocprofv3 CSV output for the GEMM kernels.
+
+    python -m dense_tiled_matrix_amd.profiling stats  <kernel_stats.csv>
+    python -m dense_tiled_matrix_amd.profiling pmc    <counter_collection.csv> [...]
+    python -m dense_tiled_matrix_amd.profiling traffic --fetch F.csv --write W.csv \
+        --copy-mib 512 --workload NAME --kernel-substr S --source-hash H
+
+``stats`` prints the per-kernel table of a ``--kernel-trace --stats`` run;
+``pmc`` prints per-kernel means of the counters of ``--pmc`` runs (with the
+shader clock derived from GRBM_GUI_ACTIVE, which counts shader-clock cycles
+per XCD, over the dispatch's own duration); ``traffic`` turns a FETCH_SIZE
+run and a WRITE_SIZE run into HBM bytes per launch, each scaled by what the
+same counter reads for a plain device copy of known size run in the same
+command.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import json
+import sys
+
+XCDS = 8
+SIMDS = 1024
+
+
+def _short(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "")
+    return name.split("(")[0][:90]
+
+
+def stats(path: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    out = ["| kernel | calls | average (us) | min (us) | max (us) | share |",
+           "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                   f"{float(r['Percentage']):.1f}% |")
+    return "\n".join(out)
+
+
+def _dispatches(paths):
+    d = collections.OrderedDict()
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            key = (path, r["Dispatch_Id"])
+            rec = d.setdefault(key, {"name": r["Kernel_Name"]})
+            rec[r["Counter_Name"]] = float(r["Counter_Value"])
+            rec["dur_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return list(d.values())
+
+
+def pmc(paths) -> str:
+    per = collections.OrderedDict()
+    for rec in _dispatches(paths):
+        per.setdefault(_short(rec["name"]), []).append(rec)
+    out = []
+    for name, recs in per.items():
+        out.append(f"### `{name}` ({len(recs)} dispatch records)")
+        keys = sorted({k for r in recs for k in r if k not in ("name", "dur_ns")})
+        for k in keys:
+            vals = [r[k] for r in recs if k in r]
+            out.append(f"- {k}: mean {sum(vals) / len(vals):.6g} (n={len(vals)})")
+        clk = [r["GRBM_GUI_ACTIVE"] / XCDS / r["dur_ns"] for r in recs if "GRBM_GUI_ACTIVE" in r]
+        if clk:
+            out.append(f"- shader clock from GRBM_GUI_ACTIVE/XCD over duration: "
+                       f"{sum(clk) / len(clk):.3f} GHz")
+        busy = [r["SQ_VALU_MFMA_BUSY_CYCLES"] / (r["GRBM_GUI_ACTIVE"] / XCDS * SIMDS)
+                for r in recs if "SQ_VALU_MFMA_BUSY_CYCLES" in r and "GRBM_GUI_ACTIVE" in r]
+        if busy:
+            out.append(f"- MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x "
+                       f"{SIMDS} SIMDs)): {100 * sum(busy) / len(busy):.1f}%")
+        conf = [r["SQ_LDS_BANK_CONFLICT"] / r["SQ_LDS_IDX_ACTIVE"] for r in recs
+                if r.get("SQ_LDS_IDX_ACTIVE")]
+        if conf:
+            out.append(f"- LDS bank-conflict cycles / LDS active cycles: "
+                       f"{100 * sum(conf) / len(conf):.2f}%")
+    return "\n".join(out)
+
+
+def _mean_kib(path, substr):
+    vals = [rec for rec in _dispatches([path]) if substr in rec["name"]]
+    key = "FETCH_SIZE" if any("FETCH_SIZE" in r for r in vals) else "WRITE_SIZE"
+    xs = [r[key] for r in vals if key in r]
+    return sum(xs) / len(xs), key
+
+
+def traffic(fetch_csv, write_csv, copy_mib, workload, kernel_substr, source_hash):
+    """HBM bytes per launch of the kernel, scaled by the copy calibration."""
+    copy_fetch, _ = _mean_kib(fetch_csv, "copyBuffer")
+    copy_write, _ = _mean_kib(write_csv, "copyBuffer")
+    k_fetch, _ = _mean_kib(fetch_csv, kernel_substr)
+    k_write, _ = _mean_kib(write_csv, kernel_substr)
+    true_kib = copy_mib * 1024.0
+    f_scale = true_kib / copy_fetch
+    w_scale = true_kib / copy_write
+    rec = {
+        "kernel_source_hash": source_hash,
+        "calibration": {"copy_mib": copy_mib, "fetch_size_kib_read": copy_fetch,
+                        "write_size_kib_read": copy_write, "fetch_scale": f_scale,
+                        "write_scale": w_scale},
+        "workloads": {workload: {
+            "kernel": kernel_substr,
+            "fetch_size_kib": k_fetch, "write_size_kib": k_write,
+            "hbm_bytes_per_launch": round((k_fetch * f_scale + k_write * w_scale) * 1024),
+        }},
+    }
+    return rec
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    p = sub.add_parser("pmc")
+    p.add_argument("csv", nargs="+")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-mib", type=float, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--kernel-substr", required=True)
+    t.add_argument("--source-hash", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        print(stats(a.csv))
+    elif a.cmd == "pmc":
+        print(pmc(a.csv))
+    else:
+        print(json.dumps(traffic(a.fetch, a.write, a.copy_mib, a.workload, a.kernel_substr,
+                                 a.source_hash), indent=1))
+
+
+if __name__ == "__main__":
+    sys.exit(main())
