@@ -10,7 +10,9 @@
 // one to want).
 #include <atomic>
 #include <cstring>
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "dtm_gemm.h"
 #include "launch.h"
@@ -153,6 +155,19 @@ void pick_generic(const Call &c, dtm_plan &p)
     p.block_k = pick->bk;
 }
 
+// Split-K for problems with too few 256 x 256 tiles to fill the chip and a
+// long K: the largest power-of-two split that keeps tiles x split within 256
+// workgroups, slices of at least 512 (16 pipelined chunks) and K divisible.
+int64_t pick_split(const Call &c, int64_t tiles)
+{
+    int64_t s = 1;
+    if (tiles >= 128)
+        return 1;
+    while (tiles * s * 2 <= 256 && c.K % (32 * s * 2) == 0 && c.K / (s * 2) >= 512)
+        s *= 2;
+    return s;
+}
+
 int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
 {
     if (!out)
@@ -182,14 +197,13 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
     }
 
     const bool forced_dims = force && (force->block_m || force->block_n || force->block_k);
-    if (force && force->split_k > 1)
-        return DTM_ERR_CONFIG;  // no split-K kernel yet
+    const int64_t forced_split = force && force->split_k > 1 ? force->split_k : 0;
     int kernel = force && force->kernel ? force->kernel : (fast16 ? DTM_KERNEL_MFMA_F16
                                                                   : DTM_KERNEL_GENERIC);
     if (kernel == DTM_KERNEL_MFMA_F16) {
         if (!fast16)
             return DTM_ERR_CONFIG;
-        const bool dma = dtm::mfma16_dma_fits(c.M, c.N, c.K);
+        const bool dma = dtm::mfma16_dma_fits(c.M, c.N, c.K, 1);
         if (forced_dims) {
             const bool dma_cfg = force->block_m == 256 && force->block_n == 256 &&
                                  force->block_k == 32;
@@ -200,9 +214,24 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
             p.block_n = force->block_n;
             p.block_k = force->block_k;
         } else {
-            const bool big = cdiv(c.M, 256) * cdiv(c.N, 256) >= 256;
-            p.block_m = p.block_n = big ? 256 : 128;
-            p.block_k = big && dma ? 32 : 64;
+            const int64_t tiles256 = cdiv(c.M, 256) * cdiv(c.N, 256);
+            const bool big = tiles256 >= 256;
+            const int64_t split = dma ? pick_split(c, tiles256) : 1;
+            if (dma && (big || split > 1)) {
+                p.block_m = p.block_n = 256;
+                p.block_k = 32;
+                p.split_k = static_cast<int32_t>(split);
+            } else {
+                p.block_m = p.block_n = big ? 256 : 128;
+                p.block_k = 64;
+            }
+        }
+        if (forced_split) {
+            // split-K runs on the 256 x 256 x 32 pipelined kernel only
+            if (p.block_m != 256 || p.block_n != 256 || p.block_k != 32 ||
+                !dtm::mfma16_dma_fits(c.M, c.N, c.K, forced_split))
+                return DTM_ERR_CONFIG;
+            p.split_k = static_cast<int32_t>(forced_split);
         }
         p.threads = 256;
     } else if (kernel == DTM_KERNEL_GENERIC) {
@@ -219,8 +248,13 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
     } else {
         return DTM_ERR_CONFIG;
     }
+    if (forced_split && kernel != DTM_KERNEL_MFMA_F16)
+        return DTM_ERR_CONFIG;
     p.kernel = kernel;
     fill_grid(c, p);
+    if (p.split_k > 1)
+        p.workspace_bytes = static_cast<uint64_t>(p.split_k) * static_cast<uint64_t>(c.M) *
+                            static_cast<uint64_t>(c.N) * sizeof(float);
     if (p.grid_m * p.grid_n > 0x7fffffffLL)
         return DTM_ERR_CONFIG;
     *out = p;
@@ -253,8 +287,40 @@ int check_device()
     return ok ? DTM_OK : DTM_ERR_DEVICE;
 }
 
-int run(const Call &c, const dtm_tile_config *force, void * /*workspace*/,
-        uint64_t /*workspace_bytes*/, void *stream)
+// ---- library-owned split-K workspace ---------------------------------------
+// One buffer per (device, stream), grown on demand.  Growing first waits for
+// the stream (earlier work may still read the old buffer), then frees and
+// allocates.  Work on one stream runs in order, so reuse within a stream is
+// safe; different streams never share a buffer.
+std::mutex g_ws_mutex;
+std::map<std::pair<int, void *>, std::pair<void *, uint64_t>> g_ws;
+
+void *library_workspace(void *stream, uint64_t bytes)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    auto &e = g_ws[{dev, stream}];
+    if (e.second >= bytes)
+        return e.first;
+    if (e.first) {
+        if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+            return nullptr;
+        (void)hipFree(e.first);
+        e.first = nullptr;
+        e.second = 0;
+    }
+    void *ptr = nullptr;
+    if (hipMalloc(&ptr, bytes) != hipSuccess)
+        return nullptr;
+    e.first = ptr;
+    e.second = bytes;
+    return ptr;
+}
+
+int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t workspace_bytes,
+        void *stream)
 {
     dtm_plan p;
     int st = make_plan(c, force, &p);
@@ -275,7 +341,20 @@ int run(const Call &c, const dtm_tile_config *force, void * /*workspace*/,
         e = dtm::launch_generic(a, c.in, c.out, p.block_m, p.block_n, p.block_k, s);
         break;
     case DTM_KERNEL_MFMA_F16:
-        if (p.block_k == 32)
+        if (p.split_k > 1) {
+            void *ws = workspace;
+            if (ws) {
+                if (workspace_bytes < p.workspace_bytes || (reinterpret_cast<uintptr_t>(ws) & 15))
+                    return DTM_ERR_WORKSPACE;
+            } else {
+                ws = library_workspace(stream, p.workspace_bytes);
+                if (!ws)
+                    return DTM_ERR_WORKSPACE;
+            }
+            e = dtm::launch_mfma16_dma_partials(a, c.in, p.split_k, static_cast<float *>(ws), s);
+            if (e == hipSuccess)
+                e = dtm::launch_splitk_reduce(a, c.out, p.split_k, static_cast<float *>(ws), s);
+        } else if (p.block_k == 32)
             e = dtm::launch_mfma16_dma(a, c.in, c.out, s);
         else
             e = dtm::launch_mfma16(a, c.in, c.out, p.block_m, p.block_n, p.block_k,

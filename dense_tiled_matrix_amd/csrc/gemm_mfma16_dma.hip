@@ -96,8 +96,14 @@ __device__ __forceinline__ floatx16 mfma(const u32x4 &a, const u32x4 &b, const f
 
 template <int IN, int OUT, int NWAVES>
 __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p, int64_t grid_m,
-                                                                      int64_t grid_n)
+                                                                      int64_t grid_n,
+                                                                      int64_t k_split,
+                                                                      int64_t c_split_stride)
 {
+    // Split-K: workgroup ids beyond one grid of tiles take further slices of
+    // K, k_split elements each, and write their fp32 partial tile to
+    // C + slice * c_split_stride.  Without a split, k_split = K and the
+    // stride is unused.
     // Waves form a 2 x (NWAVES/2) grid over the 256 x 256 tile; each owns
     // 128 rows and 256/(NWAVES/2) columns as MT x NT tiles of 32 x 32.
     constexpr int WAVES_N = NWAVES / 2;
@@ -117,8 +123,14 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
     int64_t pid_m, pid_n;
-    grouped_tile(xcd_remap(blockIdx.x, grid_m * grid_n), grid_m, grid_n, GROUP_M, pid_m, pid_n);
+    const int64_t tiles = grid_m * grid_n;
+    const int64_t splits = p.K / k_split;
+    // consecutive remapped ids (one XCD) share a K slice and differ in tile
+    const int64_t t_id = xcd_remap(blockIdx.x, tiles * splits);
+    const int64_t slice = t_id / tiles;
+    grouped_tile(t_id - slice * tiles, grid_m, grid_n, GROUP_M, pid_m, pid_n);
     const int64_t m0 = pid_m * BM, n0 = pid_n * BN;
+    const int64_t kb = slice * k_split;
 
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
@@ -131,7 +143,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     for (int j = 0; j < DPO; ++j) {
         const int r = 16 * (DPO * wave + j) + (lane >> 2);
         const int c = (lane & 3) ^ swz_a(r);
-        a_src[j] = A + (m0 + r) * p.sam + 8 * c;
+        a_src[j] = A + (m0 + r) * p.sam + kb + 8 * c;
     }
     // B load j of wave w fills k-rows 2*(DPO*w + j) + lane/32, physical
     // chunk lane%32.
@@ -140,7 +152,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     for (int j = 0; j < DPO; ++j) {
         const int k = 2 * (DPO * wave + j) + (lane >> 5);
         const int c = (lane & 31) ^ swz_b(k);
-        b_src[j] = B + (int64_t)k * p.sbk + n0 + 8 * c;
+        b_src[j] = B + (kb + k) * p.sbk + n0 + 8 * c;
     }
     const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, lds)));
     const uint32_t a_dst0 = lds_base + (DPO * wave) * 1024;
@@ -263,7 +275,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     // stage kt % 4.  Chunks kt + 2 .. kt + 4 are in flight meanwhile.  Past
     // the end the loads re-read the last chunk into the freed stage, which
     // keeps the number of loads in flight the same every iteration.
-    const int64_t nk = p.K / BK;
+    const int64_t nk = k_split / BK;
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
 #pragma unroll
@@ -296,6 +308,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
 
     // Epilogue: lane holds column lane%32 and rows 8*(v/4) + 4*(lane/32) + v%4
     // of each 32x32 tile.
+    void *c_out = static_cast<char *>(p.C) + slice * c_split_stride * (OUT == DTM_F32 ? 4 : 2);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -304,7 +317,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int64_t row = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                store_elem<OUT>(p.C, row * p.scm + col * p.scn, acc[i][j][v]);
+                store_elem<OUT>(c_out, row * p.scm + col * p.scn, acc[i][j][v]);
             }
         }
     }
@@ -315,40 +328,57 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
 #endif
 
 template <int IN, int OUT>
-hipError_t launch(const GemmArgs &a, hipStream_t s)
+hipError_t launch(const GemmArgs &a, int64_t splits, hipStream_t s)
 {
     const int64_t gm = a.M / BM, gn = a.N / BN;
-    hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, DTM_DMA_WAVES>), dim3((unsigned)(gm * gn)),
-                       dim3(64 * DTM_DMA_WAVES), 0, s, a, gm, gn);
+    hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, DTM_DMA_WAVES>),
+                       dim3((unsigned)(gm * gn * splits)), dim3(64 * DTM_DMA_WAVES), 0, s, a, gm, gn,
+                       a.K / splits, a.M * a.N);
     return hipGetLastError();
 }
 
 template <int IN>
-hipError_t dispatch_out(const GemmArgs &a, int out, hipStream_t s)
+hipError_t dispatch_out(const GemmArgs &a, int out, int64_t splits, hipStream_t s)
 {
     switch (out) {
-    case DTM_F32: return launch<IN, DTM_F32>(a, s);
-    case DTM_F16: return launch<IN, DTM_F16>(a, s);
-    case DTM_BF16: return launch<IN, DTM_BF16>(a, s);
+    case DTM_F32: return launch<IN, DTM_F32>(a, splits, s);
+    case DTM_F16: return launch<IN, DTM_F16>(a, splits, s);
+    case DTM_BF16: return launch<IN, DTM_BF16>(a, splits, s);
     }
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-bool mfma16_dma_fits(int64_t M, int64_t N, int64_t K)
+bool mfma16_dma_fits(int64_t M, int64_t N, int64_t K, int64_t splits)
 {
-    return M > 0 && N > 0 && K > 0 && M % BM == 0 && N % BN == 0 && K % BK == 0 &&
-           (M / BM) * (N / BN) <= 0x7fffffffLL;
+    return M > 0 && N > 0 && K > 0 && splits > 0 && M % BM == 0 && N % BN == 0 &&
+           K % (BK * splits) == 0 && (M / BM) * (N / BN) * splits <= 0x7fffffffLL;
 }
 
 hipError_t launch_mfma16_dma(const GemmArgs &a, int in, int out, hipStream_t s)
 {
-    if (!mfma16_dma_fits(a.M, a.N, a.K))
+    if (!mfma16_dma_fits(a.M, a.N, a.K, 1))
         return hipErrorInvalidConfiguration;
     switch (in) {
-    case DTM_F16: return dispatch_out<DTM_F16>(a, out, s);
-    case DTM_BF16: return dispatch_out<DTM_BF16>(a, out, s);
+    case DTM_F16: return dispatch_out<DTM_F16>(a, out, 1, s);
+    case DTM_BF16: return dispatch_out<DTM_BF16>(a, out, 1, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_mfma16_dma_partials(const GemmArgs &a, int in, int64_t splits, float *ws,
+                                      hipStream_t s)
+{
+    if (!mfma16_dma_fits(a.M, a.N, a.K, splits))
+        return hipErrorInvalidConfiguration;
+    GemmArgs w = a;
+    w.C = ws;  // dense fp32 [splits][M][N]
+    w.scm = a.N;
+    w.scn = 1;
+    switch (in) {
+    case DTM_F16: return dispatch_out<DTM_F16>(w, DTM_F32, splits, s);
+    case DTM_BF16: return dispatch_out<DTM_BF16>(w, DTM_F32, splits, s);
     }
     return hipErrorInvalidValue;
 }

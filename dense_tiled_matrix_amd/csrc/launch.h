@@ -21,8 +21,15 @@ hipError_t launch_mfma16(const GemmArgs &a, int in_dtype, int out_dtype, int bm,
 
 // Deep-pipelined MFMA kernel (256 x 256 x 32 tiles, global -> LDS DMA) for
 // the same layouts when M and N are multiples of 256 and K of 32.
-bool mfma16_dma_fits(int64_t M, int64_t N, int64_t K);
+bool mfma16_dma_fits(int64_t M, int64_t N, int64_t K, int64_t splits);
 hipError_t launch_mfma16_dma(const GemmArgs &a, int in_dtype, int out_dtype, hipStream_t s);
+// Split-K on the same kernel: K in `splits` equal slices, fp32 partial tiles
+// written densely to ws[splits][M][N] (a.C and its strides are not used).
+hipError_t launch_mfma16_dma_partials(const GemmArgs &a, int in_dtype, int64_t splits, float *ws,
+                                      hipStream_t s);
+// C = sum over s of ws[s] in order s = 0, 1, ..., converted once to out_dtype.
+hipError_t launch_splitk_reduce(const GemmArgs &a, int out_dtype, int64_t splits, const float *ws,
+                                hipStream_t s);
 
 // Writes zeros to the M x N view of C (the K == 0 product).
 hipError_t launch_zero_fill(const GemmArgs &a, int out_dtype, hipStream_t s);

@@ -205,15 +205,20 @@ def test_bf16_8192_bf16out():
 
 
 def test_f16_skinny_long_k():
-    """512x512x65536 fp16 U[0,1] -> fp32: full comparison, plus the
+    """512x512x65536 fp16 U[0,1] -> fp32 through the selector's split-K plan
+    (64 slices of 1024 on the pipelined kernel): full comparison, plus the
     accumulation-error report against section 13.3's fp16 accumulator
     (emulated by the oracle on a 64x64 corner with the kernel's BLOCK_K)."""
     p = W.workload("f16_skinny512x512x65536_f32out")
     note(f"{p.name}: {p.M}x{p.N}x{p.K}")
+    a = torch.empty(p.M, p.K, dtype=torch.float16, device="cuda:0")
+    b = torch.empty(p.K, p.N, dtype=torch.float16, device="cuda:0")
+    plan = dtm.gemm_plan(a, b, out_dtype=torch.float32)
+    assert plan["split_k"] == 64 and plan["block_k"] == 32, plan
     c, untouched = run(p)
     c64, cout = oracle.gemm_problem(p)
     err, tol = compare(p, c, c64=c64, cout=cout, label=p.name)
-    plan_bk = 64
+    plan_bk = 32
     A2, B2 = p.A.bits.reshape(p.M, p.K), p.B.bits.reshape(p.K, p.N)
     corner = oracle.gemm_fp16acc(64, 64, p.K, np.ascontiguousarray(A2[:64]), 0, p.K, 1,
                                  np.ascontiguousarray(B2[:, :64]), 0, 64, 1, "f16", plan_bk)
@@ -267,6 +272,46 @@ def test_mfma_pipelined_exact(ind):
         c, untouched = run(p, config=cfg, c_pad=4 if n % 2 else 0)
         compare(p, c, exact=True, label=f"pipelined {ind} {M}x{N}x{K}->{outd}")
         assert untouched
+
+
+@pytest.mark.parametrize("ind", ["f16", "bf16"])
+def test_split_k_exact(ind):
+    """Split-K on the pipelined kernel (forced splits, fp32 partials summed
+    in slice order by a second pass): value-exact on integer-valued inputs,
+    with the library's workspace."""
+    shapes = [(256, 256, 64, 2), (512, 256, 1024, 4), (256, 768, 4096, 16), (512, 512, 8192, 64)]
+    for n, (M, N, K, S) in enumerate(shapes):
+        outd = ["f32", "bf16", "f16", "f32"][n]
+        cfg = dict(kernel=MF16, block_m=256, block_n=256, block_k=32, split_k=S)
+        p = padded_int_problem(M, N, K, ind, outd, 2, seed=500 + n)
+        c, untouched = run(p, config=cfg, c_pad=3 if n % 2 else 0)
+        compare(p, c, exact=True, label=f"split-K {S} {ind} {M}x{N}x{K}->{outd}")
+        assert untouched
+
+
+def test_split_k_caller_workspace():
+    """gemm_ex with a caller-owned workspace: same result as the library's;
+    a workspace smaller than the plan needs is rejected before any launch."""
+    M, N, K, S = 512, 512, 2048, 8
+    p = padded_int_problem(M, N, K, "f16", "f32", 4, seed=77)
+    cfg = dict(kernel=MF16, block_m=256, block_n=256, block_k=32, split_k=S)
+    ref, _ = run(p, config=cfg)
+    sa, sb = dev_storage(p.A.bits, "f16"), dev_storage(p.B.bits, "f16")
+    c = torch.empty(M, N, dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(S * M * N, dtype=torch.float32, device="cuda:0")
+    st = dtm.gemm_ex_raw(M, N, K, sa.data_ptr(), p.A.stride_r, 1, sb.data_ptr(), p.B.stride_r, 1,
+                         c.data_ptr(), N, 1, dtm.DTM_F16, dtm.DTM_F32, config=cfg,
+                         workspace=ws.data_ptr(), workspace_bytes=ws.numel() * 4)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert np.array_equal(c.cpu().numpy().view(np.uint32), ref)
+    c2 = torch.full((M, N), 7.0, device="cuda:0")
+    st = dtm.gemm_ex_raw(M, N, K, sa.data_ptr(), p.A.stride_r, 1, sb.data_ptr(), p.B.stride_r, 1,
+                         c2.data_ptr(), N, 1, dtm.DTM_F16, dtm.DTM_F32, config=cfg,
+                         workspace=ws.data_ptr(), workspace_bytes=ws.numel() * 4 - 4)
+    torch.cuda.synchronize()
+    assert st == dtm.DTM_ERR_WORKSPACE
+    assert bool((c2 == 7.0).all())
 
 
 @pytest.mark.parametrize("layout", ["NN", "NT", "TN", "TT"])

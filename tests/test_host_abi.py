@@ -70,6 +70,14 @@ def test_selector_measured_workloads():
     # ragged edges keep the 64-deep register-staged kernel
     st, p = plan(4096, 4096, 4100, sam=4104, ind=F16, outd=F32)
     assert st == 0 and (p["block_m"], p["block_k"], p["ragged"]) == (256, 64, 1)
+    # long-K skinny: 4 tiles of 256 x 256 -> split K into 64 slices of 1024
+    st, p = plan(512, 512, 65536, ind=F16, outd=F32)
+    assert st == 0 and p["kernel_name"] == "mfma_f16" and p["split_k"] == 64
+    assert (p["block_m"], p["block_k"], p["k_iters"]) == (256, 32, 32)
+    assert p["workspace_bytes"] == 64 * 512 * 512 * 4
+    # enough tiles: no split
+    st, p = plan(4096, 4096, 65536, A=1 << 40, B=2 << 40, C=3 << 40, ind=F16, outd=F32)
+    assert st == 0 and p["split_k"] == 1 and p["workspace_bytes"] == 0
     # fp32 with a transposed A view: the generic strided kernel
     st, p = plan(257, 129, 193, sam=1, sak=257, ind=F32, outd=F32)
     assert st == 0 and p["kernel_name"] == "generic" and p["fast_path"] == 0 and p["ragged"] == 1
@@ -162,6 +170,15 @@ def test_forced_configs():
     assert plan(512, 256, 100, sam=104, config=dma)[0] == dtm.DTM_ERR_CONFIG
     assert plan(500, 256, 96, config=dma)[0] == dtm.DTM_ERR_CONFIG
     assert plan(64, 64, 64, config=dict(kernel=99))[0] == dtm.DTM_ERR_CONFIG
+    # forced split-K: only on the pipelined tile, K divisible by 32 * split
+    st, p = plan(512, 256, 1024, config=dict(dma, split_k=4))
+    assert st == 0 and p["split_k"] == 4 and p["k_iters"] == 8
+    assert p["workspace_bytes"] == 4 * 512 * 256 * 4
+    assert plan(512, 256, 1000, sam=1000, config=dict(dma, split_k=4))[0] == dtm.DTM_ERR_CONFIG
+    assert plan(512, 256, 1024, config=dict(kernel=mf, block_m=128, block_n=128, block_k=64,
+                                            split_k=2))[0] == dtm.DTM_ERR_CONFIG
+    assert plan(512, 256, 1024, ind=F32, config=dict(kernel=gen, split_k=2))[0] == \
+        dtm.DTM_ERR_CONFIG
 
 
 def test_gemm_rejects_before_touching_a_device():
