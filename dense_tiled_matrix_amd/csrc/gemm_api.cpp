@@ -111,20 +111,27 @@ int validate(const Call &c)
     return DTM_OK;
 }
 
-// The MFMA fp16/bf16 kernel reads 16-byte chunks along K of A and along N of
-// B: both must be unit-stride, and every chunk start 16-byte aligned.
-bool mfma16_layout_ok(const Call &c)
+// The MFMA kernels read 16-byte chunks along K of A and along N of B: both
+// must be unit-stride, and every chunk start 16-byte aligned (the base and
+// the leading dimension in bytes).  The same rule a tensor descriptor
+// imposes ("Triton matmul", "Things that break"), used here to pick a kernel
+// rather than to reject the call.
+bool mfma_layout_ok(const Call &c)
 {
-    if (c.in != DTM_F16 && c.in != DTM_BF16)
-        return false;
     if (c.sak != 1 || c.sbn != 1)
         return false;
     if ((reinterpret_cast<uintptr_t>(c.A) & 15) || (reinterpret_cast<uintptr_t>(c.B) & 15))
         return false;
-    if ((c.sam % 8) != 0 || (c.sbk % 8) != 0)
+    const int64_t per16 = 16 / item_size(c.in);
+    if ((c.sam % per16) != 0 || (c.sbk % per16) != 0)
         return false;
     return true;
 }
+bool mfma16_layout_ok(const Call &c)
+{
+    return (c.in == DTM_F16 || c.in == DTM_BF16) && mfma_layout_ok(c);
+}
+bool mfma32_layout_ok(const Call &c) { return c.in == DTM_F32 && mfma_layout_ok(c); }
 
 void fill_grid(const Call &c, dtm_plan &p)
 {
@@ -185,7 +192,8 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
         return DTM_OK;
     }
     const bool fast16 = mfma16_layout_ok(c);
-    p.fast_path = fast16 ? 1 : 0;
+    const bool fast32 = mfma32_layout_ok(c);
+    p.fast_path = fast16 || fast32 ? 1 : 0;
     if (c.K == 0) {
         p.kernel = DTM_KERNEL_ZERO_FILL;
         p.block_m = p.block_n = p.block_k = 1;
@@ -198,8 +206,10 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
 
     const bool forced_dims = force && (force->block_m || force->block_n || force->block_k);
     const int64_t forced_split = force && force->split_k > 1 ? force->split_k : 0;
-    int kernel = force && force->kernel ? force->kernel : (fast16 ? DTM_KERNEL_MFMA_F16
-                                                                  : DTM_KERNEL_GENERIC);
+    int kernel = force && force->kernel
+                     ? force->kernel
+                     : (fast16 ? DTM_KERNEL_MFMA_F16 : fast32 ? DTM_KERNEL_MFMA_F32
+                                                              : DTM_KERNEL_GENERIC);
     if (kernel == DTM_KERNEL_MFMA_F16) {
         if (!fast16)
             return DTM_ERR_CONFIG;
@@ -233,6 +243,14 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
                 return DTM_ERR_CONFIG;
             p.split_k = static_cast<int32_t>(forced_split);
         }
+        p.threads = 256;
+    } else if (kernel == DTM_KERNEL_MFMA_F32) {
+        if (!fast32)
+            return DTM_ERR_CONFIG;
+        if (forced_dims && !dtm::mfma32_has_config(force->block_m, force->block_n, force->block_k))
+            return DTM_ERR_CONFIG;
+        p.block_m = p.block_n = 128;
+        p.block_k = 16;
         p.threads = 256;
     } else if (kernel == DTM_KERNEL_GENERIC) {
         if (forced_dims) {
@@ -359,6 +377,9 @@ int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t w
         else
             e = dtm::launch_mfma16(a, c.in, c.out, p.block_m, p.block_n, p.block_k,
                                    p.ragged != 0, s);
+        break;
+    case DTM_KERNEL_MFMA_F32:
+        e = dtm::launch_mfma32(a, c.out, p.block_m, p.block_n, p.block_k, p.ragged != 0, s);
         break;
     default: return DTM_ERR_CONFIG;
     }

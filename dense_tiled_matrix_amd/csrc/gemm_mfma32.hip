@@ -1,0 +1,233 @@
+// gemm_mfma32.hip -- fp32 GEMM on the gfx950 matrix cores.
+//
+// The blocked product of "Chapter 13: The Blocked Matmul Kernel" (section
+// 13.1: one workgroup per output tile, a K-loop over chunks into an fp32
+// accumulator zeroed once; section 13.2: exact zeros outside M, N, K) for
+// fp32 operands, with full-precision fp32 products -- no reduced-precision
+// input rounding of the kind "Triton matmul" warns about under "Precision"
+// (gfx950 has no such fp32 matrix mode).
+//
+// gfx950 design:
+//  * 256 threads = 4 wave64s in 2 x 2; each wave owns (BM/2) x (BN/2) of C
+//    as 32 x 32 tiles of v_mfma_f32_32x32x2_f32 (one fp32 of A and one of B
+//    per lane per instruction, 16 fp32 results per lane).
+//  * 16-deep K-chunks, two LDS stages, loaded through registers one chunk
+//    ahead.  A rows (K-contiguous) go to LDS as they are; B arrives
+//    N-contiguous and each thread transposes its 2 x 4 block on the way, so
+//    LDS holds both operands k-contiguous, rows padded to 80 bytes (16
+//    consecutive rows hit distinct bank groups).
+//  * Which k a lane feeds at each MFMA step is a fixed permutation shared by
+//    A and B: lane half h at step s = 4t + e uses k = 8t + 4h + e, so one
+//    16-byte LDS read serves four steps.  The sum over k is unchanged.
+//  * The RAGGED instantiation zero-fills every slot outside the views.
+#include "launch.h"
+
+namespace dtm {
+namespace {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int BK = 16;
+constexpr int ROW_F = BK + 4;  // floats per LDS row (64 data bytes + 16 pad)
+constexpr int64_t GROUP_M = 4;
+
+// 4 consecutive floats at p[0..3]; positions >= valid are zero, valid <= 0
+// reads nothing.
+__device__ __forceinline__ f32x4 load4_masked(const float *p, int64_t valid)
+{
+    if (valid >= 4)
+        return *reinterpret_cast<const f32x4 *>(p);
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (e < valid)
+            v[e] = p[e];
+    return v;
+}
+
+template <int OUT, int BM, int BN, bool RAGGED>
+__global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t grid_m,
+                                                          int64_t grid_n)
+{
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int MI = WM / 32, NI = WN / 32;
+    constexpr int A_F = BM * ROW_F;                 // floats of one A stage
+    constexpr int STAGE_F = (BM + BN) * ROW_F;
+    constexpr int A_LOADS = BM * (BK / 4) / 256;    // 16-byte A chunks per thread
+    constexpr int B_PAIRS = (BK / 2) * (BN / 4) / 256;  // 2x4 B blocks per thread
+    static_assert(A_LOADS * 256 == BM * (BK / 4), "A tile must split evenly");
+    static_assert(B_PAIRS * 256 == (BK / 2) * (BN / 4), "B tile must split evenly");
+
+    __shared__ __attribute__((aligned(16))) float lds[2 * STAGE_F];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    int64_t pid_m, pid_n;
+    grouped_tile(xcd_remap(blockIdx.x, grid_m * grid_n), grid_m, grid_n, GROUP_M, pid_m, pid_n);
+    const int64_t m0 = pid_m * BM, n0 = pid_n * BN;
+    const float *A = static_cast<const float *>(p.A);
+    const float *B = static_cast<const float *>(p.B);
+
+    // A: thread loads chunk t%4 (k 4c..4c+3) of rows t/4 + 64 i.
+    const int a_c = t & 3, a_r = t >> 2;
+    // B: block q of thread t is k-rows 2*(b%8), +1 at columns 4*(b/8) .. +3,
+    // b = t + 256 q (k-pair fastest: conflict-free LDS writes, and each load
+    // instruction reads 8 k-rows x 128 contiguous bytes).
+    f32x4 ra[A_LOADS];
+    f32x4 rb[B_PAIRS][2];
+
+    auto load_tile = [&](int64_t k0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < A_LOADS; ++i) {
+            const int64_t row = m0 + a_r + 64 * i;
+            const float *src = A + row * p.sam + k0 + 4 * a_c;
+            if constexpr (RAGGED)
+                ra[i] = load4_masked(src, row < p.M ? p.K - (k0 + 4 * a_c) : 0);
+            else
+                ra[i] = *reinterpret_cast<const f32x4 *>(src);
+        }
+#pragma unroll
+        for (int q = 0; q < B_PAIRS; ++q) {
+            const int b = t + 256 * q;
+            const int kk = 2 * (b % (BK / 2)), cc = b / (BK / 2);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int64_t k = k0 + kk + e;
+                const float *src = B + k * p.sbk + n0 + 4 * cc;
+                if constexpr (RAGGED)
+                    rb[q][e] = load4_masked(src, k < p.K ? p.N - (n0 + 4 * cc) : 0);
+                else
+                    rb[q][e] = *reinterpret_cast<const f32x4 *>(src);
+            }
+        }
+    };
+
+    auto store_tile = [&](int stage) __attribute__((always_inline)) {
+        float *sa = lds + stage * STAGE_F;
+        float *sb = sa + A_F;
+#pragma unroll
+        for (int i = 0; i < A_LOADS; ++i)
+            *reinterpret_cast<f32x4 *>(sa + (a_r + 64 * i) * ROW_F + 4 * a_c) = ra[i];
+#pragma unroll
+        for (int q = 0; q < B_PAIRS; ++q) {
+            const int b = t + 256 * q;
+            const int kk = 2 * (b % (BK / 2)), cc = b / (BK / 2);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<f32x2 *>(sb + (4 * cc + j) * ROW_F + kk) =
+                    f32x2{rb[q][0][j], rb[q][1][j]};
+        }
+    };
+
+    floatx16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            acc[i][j] = floatx16{0.0f};
+
+    // lane (row/col lane%32, half h = lane/32) reads 16-byte chunk 2u + h of
+    // its row for u = 0, 1: k = 8u + 4h + e feeds MFMA step 4u + e.
+    const int fr = lane & 31, fh = lane >> 5;
+    auto compute_stage = [&](int stage) __attribute__((always_inline)) {
+        const float *sa = lds + stage * STAGE_F + (wm * WM + fr) * ROW_F;
+        const float *sb = lds + stage * STAGE_F + A_F + (wn * WN + fr) * ROW_F;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            f32x4 fa[MI], fb[NI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                fa[i] = *reinterpret_cast<const f32x4 *>(sa + i * 32 * ROW_F + 4 * (2 * u + fh));
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+                fb[j] = *reinterpret_cast<const f32x4 *>(sb + j * 32 * ROW_F + 4 * (2 * u + fh));
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NI; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][e], fb[j][e],
+                                                                        acc[i][j], 0, 0, 0);
+        }
+    };
+
+    const int64_t nk = cdiv(p.K, BK);
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int64_t kt = 0; kt + 1 < nk; ++kt) {
+        const int cur = static_cast<int>(kt & 1);
+        load_tile((kt + 1) * BK);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_stage(cur);
+        __builtin_amdgcn_sched_barrier(0);
+        store_tile(cur ^ 1);
+        __syncthreads();
+    }
+    compute_stage(static_cast<int>((nk - 1) & 1));
+
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int64_t col = n0 + wn * WN + j * 32 + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = m0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (!RAGGED || (row < p.M && col < p.N))
+                    store_elem<OUT>(p.C, row * p.scm + col * p.scn, acc[i][j][v]);
+            }
+        }
+    }
+}
+
+template <int OUT, int BM, int BN>
+hipError_t launch_tile(const GemmArgs &a, bool ragged, hipStream_t s)
+{
+    const int64_t gm = cdiv(a.M, BM), gn = cdiv(a.N, BN);
+    const int64_t tiles = gm * gn;
+    if (tiles > 0x7fffffffLL)
+        return hipErrorInvalidConfiguration;
+    if (ragged)
+        hipLaunchKernelGGL((gemm_mfma32_kernel<OUT, BM, BN, true>), dim3((unsigned)tiles),
+                           dim3(256), 0, s, a, gm, gn);
+    else
+        hipLaunchKernelGGL((gemm_mfma32_kernel<OUT, BM, BN, false>), dim3((unsigned)tiles),
+                           dim3(256), 0, s, a, gm, gn);
+    return hipGetLastError();
+}
+
+template <int OUT>
+hipError_t dispatch_tile(const GemmArgs &a, int bm, int bn, bool ragged, hipStream_t s)
+{
+    if (bm == 128 && bn == 128)
+        return launch_tile<OUT, 128, 128>(a, ragged, s);
+    return hipErrorInvalidConfiguration;
+}
+
+}  // namespace
+
+bool mfma32_has_config(int bm, int bn, int bk)
+{
+    return bk == BK && bm == 128 && bn == 128;
+}
+
+hipError_t launch_mfma32(const GemmArgs &a, int out, int bm, int bn, int bk, bool ragged,
+                         hipStream_t s)
+{
+    if (bk != BK)
+        return hipErrorInvalidConfiguration;
+    switch (out) {
+    case DTM_F32: return dispatch_tile<DTM_F32>(a, bm, bn, ragged, s);
+    case DTM_F16: return dispatch_tile<DTM_F16>(a, bm, bn, ragged, s);
+    case DTM_BF16: return dispatch_tile<DTM_BF16>(a, bm, bn, ragged, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dtm

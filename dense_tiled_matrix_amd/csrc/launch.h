@@ -31,6 +31,12 @@ hipError_t launch_mfma16_dma_partials(const GemmArgs &a, int in_dtype, int64_t s
 hipError_t launch_splitk_reduce(const GemmArgs &a, int out_dtype, int64_t splits, const float *ws,
                                 hipStream_t s);
 
+// MFMA kernel for fp32 inputs with K-contiguous A and N-contiguous B
+// (128 x 128 x 16 tiles).
+bool mfma32_has_config(int bm, int bn, int bk);
+hipError_t launch_mfma32(const GemmArgs &a, int out_dtype, int bm, int bn, int bk, bool ragged,
+                         hipStream_t s);
+
 // Writes zeros to the M x N view of C (the K == 0 product).
 hipError_t launch_zero_fill(const GemmArgs &a, int out_dtype, hipStream_t s);
 

@@ -314,6 +314,33 @@ def test_split_k_caller_workspace():
     assert bool((c2 == 7.0).all())
 
 
+def test_mfma_f32_exact_and_random():
+    """fp32 inputs on the fp32 matrix cores: value-exact on integer-valued
+    inputs at ragged and interior sizes (every output dtype), and within the
+    fp32 tolerance on N(0,1) inputs."""
+    MF32 = dtm.DTM_KERNEL_MFMA_F32
+    for n, (M, N, K) in enumerate([(128, 128, 16), (256, 384, 512), (129, 257, 33), (1, 1, 1),
+                                   (300, 200, 1000), (127, 129, 17)]):
+        outd = ["f32", "f16", "bf16"][n % 3]
+        rng = np.random.default_rng(600 + n)
+        lda, ldb = -(-K // 4) * 4, -(-N // 4) * 4
+        abuf = np.full((M, lda), np.nan)
+        abuf[:, :K] = rng.integers(-16, 17, size=(M, K))
+        bbuf = np.full((K, ldb), np.nan)
+        bbuf[:, :N] = rng.integers(-16, 17, size=(K, N))
+        p = W.Problem(M, N, K, W.Operand(W.to_bits(abuf, "f32").reshape(-1), "f32", M, K, 0, lda, 1),
+                      W.Operand(W.to_bits(bbuf, "f32").reshape(-1), "f32", K, N, 0, ldb, 1),
+                      "f32", outd)
+        c, untouched = run(p, config=dict(kernel=MF32), c_pad=2 if n % 2 else 0)
+        compare(p, c, exact=True, label=f"mfma_f32 {M}x{N}x{K}->{outd}")
+        assert untouched
+    for n, (M, N, K) in enumerate([(1024, 1024, 1024), (1000, 600, 777)]):
+        p = W.random_problem(M, N, K, "f32", "f32", ("normal", 0.0, 1.0), seed=650 + n)
+        c, _ = run(p)
+        err, tol = compare(p, c, label=f"mfma_f32 random {M}x{N}x{K}")
+        note(f"mfma_f32 {M}x{N}x{K}: max err {err:.3e} tol {tol:.3e}")
+
+
 @pytest.mark.parametrize("layout", ["NN", "NT", "TN", "TT"])
 @pytest.mark.parametrize("ind", ["f32", "f16", "bf16"])
 def test_generic_layouts_sweep_exact(layout, ind):

@@ -90,7 +90,6 @@ def test_selector_measured_workloads():
     (dict(B=PB + 8), "B base not 16-byte aligned"),
     (dict(sam=1001), "A leading dimension not a multiple of 8 elements"),
     (dict(sbk=999), "B leading dimension not a multiple of 8 elements"),
-    (dict(ind=F32), "fp32 inputs"),
 ])
 def test_fast_path_predicate_falls_back_to_generic(kw, why):
     st, p = plan(1024, 1024, 1000, **kw)
@@ -98,6 +97,21 @@ def test_fast_path_predicate_falls_back_to_generic(kw, why):
     assert p["fast_path"] == 0 and p["kernel_name"] == "generic", why
     # forcing the MFMA kernel on such a layout is a configuration error
     st, _ = plan(1024, 1024, 1000, config=dict(kernel=dtm.DTM_KERNEL_MFMA_F16), **kw)
+    assert st == dtm.DTM_ERR_CONFIG
+
+
+def test_fp32_selector():
+    """fp32 with K-contiguous A and N-contiguous B on 16-byte boundaries runs
+    on the fp32 matrix cores; other fp32 layouts on the generic kernel."""
+    st, p = plan(1024, 1024, 1000, ind=F32, sam=1000)
+    assert st == 0 and p["kernel_name"] == "mfma_f32" and p["fast_path"] == 1
+    assert (p["block_m"], p["block_n"], p["block_k"], p["ragged"]) == (128, 128, 16, 1)
+    for kw in [dict(sam=1001), dict(sak=2), dict(A=PA + 4), dict(sbk=1002)]:
+        st, p = plan(1024, 1024, 1000, ind=F32, **kw)
+        assert st == 0 and p["kernel_name"] == "generic", kw
+    st, p = plan(1024, 1024, 1000, ind=F32, config=dict(kernel=dtm.DTM_KERNEL_MFMA_F16))
+    assert st == dtm.DTM_ERR_CONFIG
+    st, p = plan(1024, 1024, 1000, ind=F16, config=dict(kernel=dtm.DTM_KERNEL_MFMA_F32))
     assert st == dtm.DTM_ERR_CONFIG
 
 
@@ -149,7 +163,7 @@ def test_a_and_b_may_alias_each_other_and_broadcast():
     # A and B may overlap (both are only read) and may have zero strides
     assert plan(48, 64, 32, B=PA)[0] == 0
     st, p = plan(48, 64, 32, sam=0, ind=F32)
-    assert st == 0 and p["kernel_name"] == "generic"
+    assert st == 0  # a broadcast row is a valid layout for every kernel that reads rows
     st, p = plan(48, 64, 32, sam=-32, A=PA + 48 * 32 * 2, ind=F32)
     assert st == 0
 
