@@ -47,11 +47,11 @@ template <int D> __device__ __forceinline__ float load_elem(const void *p, int64
 // into the exponent and gives infinity.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v)
 {
-    uint32_t u = __float_as_uint(v);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return static_cast<uint16_t>((u >> 16) | 0x0040u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet_nan = (u >> 16) | 0x0040u;
+    // a select, not a branch: the epilogue converts many values per lane
+    return static_cast<uint16_t>(((u & 0x7fffffffu) > 0x7f800000u) ? quiet_nan : rounded);
 }
 
 // fp32 -> fp16 bits, nearest-even (the hardware conversion in the default

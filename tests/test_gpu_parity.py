@@ -289,6 +289,24 @@ def test_split_k_exact(ind):
         assert untouched
 
 
+@pytest.mark.parametrize("ind", ["f16", "bf16"])
+def test_many_tiles_exact(ind):
+    """More 256x256 work units than compute units on the pipelined kernel
+    (several tiles per CU in turn): 1-, 2- and 3-chunk units, and split-K
+    with more (tile, slice) units than CUs.  Value-exact on integer-valued
+    inputs."""
+    cases = [(4352, 4352, 32, 1), (4352, 4352, 64, 1), (4096, 4608, 96, 1),
+             (2560, 2560, 1024, 4)]
+    for n, (M, N, K, S) in enumerate(cases):
+        outd = ["bf16", "f32", "f16", "f32"][n]
+        cfg = dict(kernel=MF16, block_m=256, block_n=256, block_k=32, split_k=S)
+        p = padded_int_problem(M, N, K, ind, outd, 4, seed=700 + n)
+        note(f"many tiles {ind} {M}x{N}x{K} split {S}")
+        c, untouched = run(p, config=cfg)
+        compare(p, c, exact=True, label=f"many tiles {ind} {M}x{N}x{K} split {S}")
+        assert untouched
+
+
 def test_split_k_caller_workspace():
     """gemm_ex with a caller-owned workspace: same result as the library's;
     a workspace smaller than the plan needs is rejected before any launch."""
