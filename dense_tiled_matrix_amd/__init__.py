@@ -32,6 +32,7 @@ globals().update({v: k for k, v in STATUS.items()})
 KERNELS = {0: "none", 1: "zero_fill", 2: "generic", 3: "mfma_f16", 4: "mfma_f32"}
 DTM_KERNEL_NONE, DTM_KERNEL_ZERO_FILL, DTM_KERNEL_GENERIC = 0, 1, 2
 DTM_KERNEL_MFMA_F16, DTM_KERNEL_MFMA_F32 = 3, 4
+DTM_LAYOUT_A_M_CONTIG, DTM_LAYOUT_B_K_CONTIG = 1, 2
 
 
 class TileConfig(ctypes.Structure):
@@ -50,7 +51,8 @@ class Plan(ctypes.Structure):
                 ("grid_m", ctypes.c_int64), ("grid_n", ctypes.c_int64),
                 ("k_iters", ctypes.c_int64), ("split_k", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("fast_path", ctypes.c_int32),
-                ("ragged", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64)]
+                ("ragged", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_uint64)]
 
     def as_dict(self):
         d = {f: getattr(self, f) for f, _ in self._fields_}

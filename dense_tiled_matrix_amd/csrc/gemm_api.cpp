@@ -111,27 +111,33 @@ int validate(const Call &c)
     return DTM_OK;
 }
 
-// The MFMA kernels read 16-byte chunks along K of A and along N of B: both
-// must be unit-stride, and every chunk start 16-byte aligned (the base and
-// the leading dimension in bytes).  The same rule a tensor descriptor
-// imposes ("Triton matmul", "Things that break"), used here to pick a kernel
-// rather than to reject the call.
-bool mfma_layout_ok(const Call &c)
+// The MFMA kernels read 16-byte chunks along the unit-stride axis of each
+// operand: A K- or M-contiguous, B N- or K-contiguous, every chunk start
+// 16-byte aligned (the base and the leading dimension in bytes).  The same
+// rule a tensor descriptor imposes ("Triton matmul", "Things that break"),
+// used here to pick a kernel rather than to reject the call.  Returns the
+// dtm_layout bits, or -1 when no MFMA layout fits.
+int mfma_layout(const Call &c)
 {
-    if (c.sak != 1 || c.sbn != 1)
-        return false;
     if ((reinterpret_cast<uintptr_t>(c.A) & 15) || (reinterpret_cast<uintptr_t>(c.B) & 15))
-        return false;
+        return -1;
     const int64_t per16 = 16 / item_size(c.in);
-    if ((c.sam % per16) != 0 || (c.sbk % per16) != 0)
-        return false;
-    return true;
+    int layout = 0;
+    if (c.sak == 1 && c.sam % per16 == 0)
+        ;
+    else if (c.sam == 1 && c.sak % per16 == 0)
+        layout |= DTM_LAYOUT_A_M_CONTIG;
+    else
+        return -1;
+    if (c.sbn == 1 && c.sbk % per16 == 0)
+        ;
+    else if (c.sbk == 1 && c.sbn % per16 == 0)
+        layout |= DTM_LAYOUT_B_K_CONTIG;
+    else
+        return -1;
+    return layout;
 }
-bool mfma16_layout_ok(const Call &c)
-{
-    return (c.in == DTM_F16 || c.in == DTM_BF16) && mfma_layout_ok(c);
-}
-bool mfma32_layout_ok(const Call &c) { return c.in == DTM_F32 && mfma_layout_ok(c); }
+bool is16(const Call &c) { return c.in == DTM_F16 || c.in == DTM_BF16; }
 
 void fill_grid(const Call &c, dtm_plan &p)
 {
@@ -191,8 +197,12 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
         *out = p;
         return DTM_OK;
     }
-    const bool fast16 = mfma16_layout_ok(c);
-    const bool fast32 = mfma32_layout_ok(c);
+    // The pipelined kernel reads every layout; the register-staged fp16/bf16
+    // kernel and the fp32 kernel read row-major A and B only.
+    const int layout = mfma_layout(c);
+    const bool dma = is16(c) && layout >= 0 && dtm::mfma16_dma_fits(c.M, c.N, c.K, 1);
+    const bool fast16 = is16(c) && (layout == 0 || dma);
+    const bool fast32 = c.in == DTM_F32 && layout == 0;
     p.fast_path = fast16 || fast32 ? 1 : 0;
     if (c.K == 0) {
         p.kernel = DTM_KERNEL_ZERO_FILL;
@@ -213,12 +223,12 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
     if (kernel == DTM_KERNEL_MFMA_F16) {
         if (!fast16)
             return DTM_ERR_CONFIG;
-        const bool dma = dtm::mfma16_dma_fits(c.M, c.N, c.K, 1);
         if (forced_dims) {
             const bool dma_cfg = force->block_m == 256 && force->block_n == 256 &&
                                  force->block_k == 32;
             if (dma_cfg ? !dma
-                        : !dtm::mfma16_has_config(force->block_m, force->block_n, force->block_k))
+                        : layout != 0 || !dtm::mfma16_has_config(force->block_m, force->block_n,
+                                                                 force->block_k))
                 return DTM_ERR_CONFIG;
             p.block_m = force->block_m;
             p.block_n = force->block_n;
@@ -227,7 +237,7 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
             const int64_t tiles256 = cdiv(c.M, 256) * cdiv(c.N, 256);
             const bool big = tiles256 >= 256;
             const int64_t split = dma ? pick_split(c, tiles256) : 1;
-            if (dma && (big || split > 1)) {
+            if (dma && (big || split > 1 || layout != 0)) {
                 p.block_m = p.block_n = 256;
                 p.block_k = 32;
                 p.split_k = static_cast<int32_t>(split);
@@ -243,7 +253,8 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
                 return DTM_ERR_CONFIG;
             p.split_k = static_cast<int32_t>(forced_split);
         }
-        p.threads = 256;
+        p.threads = p.block_k == 32 ? dtm::mfma16_dma_threads() : 256;
+        p.layout = layout;
     } else if (kernel == DTM_KERNEL_MFMA_F32) {
         if (!fast32)
             return DTM_ERR_CONFIG;
@@ -252,6 +263,7 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
         p.block_m = p.block_n = 128;
         p.block_k = 16;
         p.threads = 256;
+        p.layout = layout;
     } else if (kernel == DTM_KERNEL_GENERIC) {
         if (forced_dims) {
             if (!dtm::generic_has_config(force->block_m, force->block_n, force->block_k))
@@ -369,11 +381,12 @@ int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t w
                 if (!ws)
                     return DTM_ERR_WORKSPACE;
             }
-            e = dtm::launch_mfma16_dma_partials(a, c.in, p.split_k, static_cast<float *>(ws), s);
+            e = dtm::launch_mfma16_dma_partials(a, c.in, p.layout, p.split_k,
+                                                 static_cast<float *>(ws), s);
             if (e == hipSuccess)
                 e = dtm::launch_splitk_reduce(a, c.out, p.split_k, static_cast<float *>(ws), s);
         } else if (p.block_k == 32)
-            e = dtm::launch_mfma16_dma(a, c.in, c.out, s);
+            e = dtm::launch_mfma16_dma(a, c.in, c.out, p.layout, s);
         else
             e = dtm::launch_mfma16(a, c.in, c.out, p.block_m, p.block_n, p.block_k,
                                    p.ragged != 0, s);

@@ -1,5 +1,6 @@
 // gemm_mfma16_dma.hip -- deep-pipelined MFMA GEMM for fp16/bf16 inputs on
-// gfx950, for problems whose M, N are multiples of 256 and K of 32.
+// gfx950, for problems whose M, N are multiples of 256 and K of 32, in any
+// of the four operand layouts (A K- or M-contiguous, B N- or K-contiguous).
 //
 // The computation is the blocked product of "Chapter 13: The Blocked Matmul
 // Kernel" (section 13.1): one workgroup per 256 x 256 output tile, a K-loop
@@ -8,11 +9,13 @@
 // output dtype at the store (section 13.3).  No edge masking is needed on
 // this path ("Triton from zero, Lesson 4: Block Pointers", homework 3: pay
 // only for the raggedness a problem has); ragged problems use the other MFMA
-// kernel.
+// kernel.  Transposed views are read at full speed rather than through a
+// slow strided path (the stride-swap lesson of "Triton from zero",
+// Lesson 4: a transpose is only a change of strides).
 //
 // gfx950 design:
-//  * 4 wave64s (2 x 2), each owning 128 x 128 of C as 4 x 4 tiles of
-//    v_mfma_f32_32x32x16_{f16,bf16}; 256 fp32 accumulators per lane in the
+//  * NWAVES wave64s (2 x NWAVES/2), each owning 128 x (512/NWAVES) of C as
+//    tiles of v_mfma_f32_32x32x16_{f16,bf16} with fp32 accumulators in the
 //    AccVGPR file.
 //  * Operands move global -> LDS with global_load_lds_dwordx4 (each wave
 //    instruction writes 1 KiB of LDS, lane i's 16 bytes at offset 16*i), so
@@ -20,19 +23,20 @@
 //    loaded three to four chunks of MFMA time before it is read.  One
 //    barrier per chunk, after a wait for exactly the loads of the chunk
 //    about to be read; the loads are issued one after every second MFMA.
-//  * A is stored row-major (64 bytes per row); the 16-byte chunk c of row r
-//    sits at position c ^ f(r), f(r) = (r >> 2) & 3, so each group of 16
-//    consecutive rows read by a fragment load (one chunk each) covers all 64
-//    banks once.  (Measured on gfx950 with SQ_LDS_BANK_CONFLICT: zero
-//    conflicts for this pattern; other XOR patterns cost 4-12 extra cycles
-//    per ds_read_b128.)
-//  * B stays N-contiguous (512 bytes per k-row); chunk c of k-row k sits at
-//    c ^ g(k), g = {0, 6, 10, 12}[k % 4] (measured conflict-free for the
-//    transposing reads below; no swizzle costs about 6 extra cycles each).  Fragments are read with
-//    ds_read_b64_tr_b16, which hands lane i of each 16-lane group the
-//    i-th column of a 4 x 16 block whose rows the lanes address, i.e. four
-//    consecutive k of one column -- the MFMA B operand -- with no transpose
-//    anywhere else.
+//  * Both MFMA operands want, in lane l, 8 consecutive k of row/column
+//    l % 32.  An operand that is K-contiguous in memory is staged as 256
+//    rows of 64 bytes; the 16-byte chunk c of row r sits at c ^ f(r),
+//    f(r) = (r >> 2) & 3, and a fragment is one ds_read_b128 per lane (each
+//    16 consecutive rows read cover all 64 banks once; measured on gfx950:
+//    zero SQ_LDS_BANK_CONFLICT, other XOR patterns cost 4-12 extra cycles
+//    per read).
+//  * An operand that is M- or N-contiguous stays that way: 32 k-rows of 512
+//    bytes, chunk c of k-row k at c ^ g(k), g = {0, 6, 10, 12}[k % 4]
+//    (measured conflict-free; no swizzle costs about 6 extra cycles per
+//    read).  A fragment is two ds_read_b64_tr_b16, which hand lane i of each
+//    16-lane group the i-th column of a 4 x 16 block whose rows the lanes
+//    address, i.e. four consecutive k of one row/column -- the operand
+//    layout the MFMA wants, with no transpose anywhere else.
 //  * Workgroup ids are remapped so that each XCD owns a compact group of
 //    tiles (shared A rows and B columns stay in its L2).
 #include "launch.h"
@@ -65,8 +69,9 @@ constexpr int waitcnt_imm(int vm, int lgkm)
     return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | (((vm >> 4) & 3) << 14);
 }
 
-__device__ __forceinline__ int swz_a(int r) { return (r >> 2) & 3; }
-__device__ __forceinline__ int swz_b(int k)
+// Swizzles of the two staging forms (see the file comment).
+__device__ __forceinline__ int swz_row(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz_krow(int k)
 {
     // 0, 6, 10, 12 for k % 4 = 0..3
     return (0xCA60 >> (4 * (k & 3))) & 15;
@@ -94,7 +99,66 @@ __device__ __forceinline__ floatx16 mfma(const u32x4 &a, const u32x4 &b, const f
                                                        0);
 }
 
-template <int IN, int OUT, int NWAVES>
+// Global source of this lane for 1 KiB segment `seg` of an operand's stage.
+// X points at element (0, 0) of the operand viewed as [mn][k]; mn0 and kb
+// are the tile's first row/column and the slice's first k.
+//  K-contiguous (KC): rows 16*seg + lane/4, physical chunk lane % 4.
+//  otherwise: k-rows 2*seg + lane/32, physical chunk lane % 32.
+// The logical chunk is the physical one XOR the row's swizzle.  Chunk kt of
+// the K loop is kt * BK elements further along K.
+template <bool KC>
+__device__ __forceinline__ const uint16_t *stage_src(const uint16_t *X, int64_t mn0, int64_t s_mn,
+                                                     int64_t s_k, int64_t kb, int seg, int lane)
+{
+    if constexpr (KC) {
+        const int r = 16 * seg + (lane >> 2);
+        const int c = (lane & 3) ^ swz_row(r);
+        return X + (mn0 + r) * s_mn + kb + 8 * c;
+    } else {
+        const int k = 2 * seg + (lane >> 5);
+        const int c = (lane & 31) ^ swz_krow(k);
+        return X + (kb + k) * s_k + mn0 + 8 * c;
+    }
+}
+
+// Byte offset, within an operand's stage, of this lane's first fragment read
+// for the 32-wide block of rows/columns starting at `base`, k-step 0.
+//  K-contiguous: row base + lane%32, logical chunk lane/32 (one b128 read);
+//    k-step 1 is logical chunk 2 + lane/32, i.e. the offset XOR 32.
+//  otherwise: within 16-lane group G = lane/16, lane i = lane%16 addresses
+//    k-row 8*(G/2) + i/4 at column base + 16*(G%2) + 4*(i%4); the second
+//    read of the pair (k + 4) is 2048 bytes on and k-step 1 (k + 16) is
+//    8192 bytes on, because the swizzle depends on k % 4 only.
+template <bool KC> __device__ __forceinline__ int frag_off(int base, int lane)
+{
+    if constexpr (KC) {
+        const int r = base + (lane & 31);
+        return r * 64 + (((lane >> 5) ^ swz_row(r)) * 16);
+    } else {
+        const int G = lane >> 4, li = lane & 15;
+        const int k = 8 * (G >> 1) + (li >> 2);
+        const int n = base + 16 * (G & 1) + 4 * (li & 3);
+        return k * 512 + (((n >> 3) ^ swz_krow(k)) * 16) + ((n >> 2) & 1) * 8;
+    }
+}
+
+// Half (e = 0: k 0..3, e = 1: k 4..7) of a fragment by a transposing read.
+__device__ __forceinline__ void read_tr_half(u32x4 &f, int e, const char *p)
+{
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p));
+    const u32x2 w = __builtin_bit_cast(u32x2, v);
+    if (e == 0) {
+        f.x = w.x;
+        f.y = w.y;
+    } else {
+        f.z = w.x;
+        f.w = w.y;
+    }
+}
+
+// TA: A is M-contiguous (stride_am == 1); else K-contiguous.
+// TB: B is K-contiguous (stride_bk == 1); else N-contiguous.
+template <int IN, int OUT, int NWAVES, bool TA, bool TB>
 __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p, int64_t grid_m,
                                                                       int64_t grid_n,
                                                                       int64_t k_split,
@@ -106,14 +170,16 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     // stride is unused.
     // Waves form a 2 x (NWAVES/2) grid over the 256 x 256 tile; each owns
     // 128 rows and 256/(NWAVES/2) columns as MT x NT tiles of 32 x 32.
+    constexpr bool A_KC = !TA, B_KC = TB;
     constexpr int WAVES_N = NWAVES / 2;
     constexpr int WN_COLS = BN / WAVES_N;
     constexpr int MT = 4, NT = WN_COLS / 32;
-    constexpr int NREAD = MT + 2 * NT;           // LDS reads per k-step
-    constexpr int NMFMA = MT * NT;               // MFMAs per k-step
-    constexpr int DPO = 16 / NWAVES;             // 1 KiB loads per operand per wave per chunk
-    constexpr int DMA_GROUP = 2 * DPO;           // loads per wave per chunk
-    static_assert(NREAD <= NMFMA && DMA_GROUP <= NMFMA / 2, "interleave slots");
+    constexpr int A_READS = MT * (A_KC ? 1 : 2);   // LDS reads per k-step
+    constexpr int NREAD = A_READS + NT * (B_KC ? 1 : 2);
+    constexpr int NMFMA = MT * NT;                 // MFMAs per k-step
+    constexpr int DPO = 16 / NWAVES;               // 1 KiB loads per operand per wave per chunk
+    constexpr int DMA_GROUP = 2 * DPO;             // loads per wave per chunk
+    static_assert(DMA_GROUP <= NMFMA / 2, "interleave slots");
 
     __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
 
@@ -135,25 +201,16 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
 
-    // ---- load source addresses of this lane ------------------------------
-    // A load j of wave w fills LDS bytes 1024*(DPO*w + j) .. +1023 of the A
-    // stage: rows 16*(DPO*w + j) + lane/4, physical chunk lane%4.
-    const uint16_t *a_src[DPO];
+    // ---- load sources of this lane: segments DPO*wave .. +DPO-1 ----------
+    const uint16_t *a_src[DPO], *b_src[DPO];
 #pragma unroll
     for (int j = 0; j < DPO; ++j) {
-        const int r = 16 * (DPO * wave + j) + (lane >> 2);
-        const int c = (lane & 3) ^ swz_a(r);
-        a_src[j] = A + (m0 + r) * p.sam + kb + 8 * c;
+        a_src[j] = stage_src<A_KC>(A, m0, p.sam, p.sak, kb, DPO * wave + j, lane);
+        b_src[j] = stage_src<B_KC>(B, n0, p.sbn, p.sbk, kb, DPO * wave + j, lane);
     }
-    // B load j of wave w fills k-rows 2*(DPO*w + j) + lane/32, physical
-    // chunk lane%32.
-    const uint16_t *b_src[DPO];
-#pragma unroll
-    for (int j = 0; j < DPO; ++j) {
-        const int k = 2 * (DPO * wave + j) + (lane >> 5);
-        const int c = (lane & 31) ^ swz_b(k);
-        b_src[j] = B + (kb + k) * p.sbk + n0 + 8 * c;
-    }
+    // elements between consecutive chunks
+    const int64_t a_chunk = A_KC ? BK : BK * p.sak;
+    const int64_t b_chunk = B_KC ? BK : BK * p.sbk;
     const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, lds)));
     const uint32_t a_dst0 = lds_base + (DPO * wave) * 1024;
     const uint32_t b_dst0 = lds_base + A_STAGE_BYTES + (DPO * wave) * 1024;
@@ -163,61 +220,49 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     // asynchronous LDS writes; the loop waits for them explicitly (vmcnt)
     // before a barrier.
     auto dma_one = [&](int64_t kt, int stage, int d) __attribute__((always_inline)) {
-        const int64_t k0 = kt * BK;
         const uint32_t so = static_cast<uint32_t>(stage) * STAGE_BYTES;
         if (d < DPO)
-            dma16(a_src[d] + k0, a_dst0 + so + 1024 * d);
+            dma16(a_src[d] + kt * a_chunk, a_dst0 + so + 1024 * d);
         else
-            dma16(b_src[d - DPO] + k0 * p.sbk, b_dst0 + so + 1024 * (d - DPO));
+            dma16(b_src[d - DPO] + kt * b_chunk, b_dst0 + so + 1024 * (d - DPO));
     };
 
     // ---- fragment read offsets (bytes within a stage) ---------------------
-    // A: lane reads row wm*128 + i*32 + lane%32, logical chunk 2*kk + lane/32.
-    int a_off[MT][2];
+    // A block i: rows wm*128 + 32*i; B block j: columns wn*WN_COLS + 32*j.
+    // [0] k-step 0, [1] k-step 1 (used by K-contiguous operands only).
+    int a_off[MT][2], b_off[NT][2];
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-        const int r = wm * 128 + i * 32 + (lane & 31);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            a_off[i][kk] = r * 64 + (((2 * kk + (lane >> 5)) ^ swz_a(r)) * 16);
+        a_off[i][0] = frag_off<A_KC>(wm * 128 + i * 32, lane);
+        a_off[i][1] = a_off[i][0] ^ 32;
     }
-    // B (transposing read): within 16-lane group G = lane/16, lane i = lane%16
-    // addresses k-row kk*16 + 8*(G/2) + 4*e + i/4 at column
-    // wn*WN_COLS + j*32 + 16*(G%2) + 4*(i%4).
-    const int G = lane >> 4, li = lane & 15;
-    int b_off[NT][2][2];
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int k = kk * 16 + 8 * (G >> 1) + 4 * e + (li >> 2);
-                const int n = wn * WN_COLS + j * 32 + 16 * (G & 1) + 4 * (li & 3);
-                b_off[j][kk][e] = A_STAGE_BYTES + k * 512 + (((n >> 3) ^ swz_b(k)) * 16) +
-                                  ((n >> 2) & 1) * 8;
-            }
+    for (int j = 0; j < NT; ++j) {
+        b_off[j][0] = A_STAGE_BYTES + frag_off<B_KC>(wn * WN_COLS + j * 32, lane);
+        b_off[j][1] = b_off[j][0] ^ 32;
+    }
 
     // Fragments of one 16-deep k-step.
     struct Frags {
         u32x4 a[MT], b[NT];
     };
-    // Read q of a k-step's fragments: q < MT the A blocks, then the low and
-    // high halves of the NT B blocks.
+    // Read q of a k-step's fragments: A blocks first (one read each, or two
+    // halves each when A is M-contiguous), then the B blocks likewise.
     auto read_one = [&](Frags &f, const char *st, int kk, int q) __attribute__((always_inline)) {
-        if (q < MT) {
-            f.a[q] = *LDS_PTR(const u32x4, st + a_off[q][kk]);
-        } else {
-            const int j = (q - MT) >> 1, e = (q - MT) & 1;
-            const s16x4 v =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, st + b_off[j][kk][e]));
-            const u32x2 w = __builtin_bit_cast(u32x2, v);
-            if (e == 0) {
-                f.b[j].x = w.x;
-                f.b[j].y = w.y;
+        if (q < A_READS) {
+            if constexpr (A_KC) {
+                f.a[q] = *LDS_PTR(const u32x4, st + a_off[q][kk]);
             } else {
-                f.b[j].z = w.x;
-                f.b[j].w = w.y;
+                const int i = q >> 1, e = q & 1;
+                read_tr_half(f.a[i], e, st + a_off[i][0] + 8192 * kk + 2048 * e);
+            }
+        } else {
+            const int qb = q - A_READS;
+            if constexpr (B_KC) {
+                f.b[qb] = *LDS_PTR(const u32x4, st + b_off[qb][kk]);
+            } else {
+                const int j = qb >> 1, e = qb & 1;
+                read_tr_half(f.b[j], e, st + b_off[j][0] + 8192 * kk + 2048 * e);
             }
         }
     };
@@ -244,7 +289,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     };
 
     // The MFMAs of one k-step with the reads of the next k-step's fragments
-    // interleaved one after each MFMA, and (when `dma`) the loads of chunk
+    // spread evenly between them, and (when `dma`) the loads of chunk
     // `dma_kt` one after every second MFMA.
     auto half_step = [&](const Frags &cur, Frags &next, const char *next_st, int next_kk,
                          bool dma, int64_t dma_kt, int dma_stage) __attribute__((always_inline)) {
@@ -252,16 +297,19 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
         for (int q = 0; q < NMFMA; ++q) {
             const int i = q / NT, j = q % NT;
             acc[i][j] = mfma<IN>(cur.a[i], cur.b[j], acc[i][j]);
-            if (q < NREAD)
-                read_one(next, next_st, next_kk, q);
+            const int r0 = q * NREAD / NMFMA, r1 = (q + 1) * NREAD / NMFMA;
+#pragma unroll
+            for (int r = r0; r < r1; ++r)
+                read_one(next, next_st, next_kk, r);
             if (dma && (q & 1) && (q >> 1) < DMA_GROUP)
                 dma_one(dma_kt, dma_stage, q >> 1);
             if (dma) {
                 __builtin_amdgcn_sched_barrier(0);  // keep this group in place
             } else {
                 __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // the MFMA
-                if (q < NREAD)
-                    __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);  // the read
+#pragma unroll
+                for (int r = r0; r < r1; ++r)
+                    __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);  // its reads
             }
         }
     };
@@ -327,23 +375,36 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
 #define DTM_DMA_WAVES 8
 #endif
 
-template <int IN, int OUT>
+template <int IN, int OUT, bool TA, bool TB>
 hipError_t launch(const GemmArgs &a, int64_t splits, hipStream_t s)
 {
     const int64_t gm = a.M / BM, gn = a.N / BN;
-    hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, DTM_DMA_WAVES>),
+    hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, DTM_DMA_WAVES, TA, TB>),
                        dim3((unsigned)(gm * gn * splits)), dim3(64 * DTM_DMA_WAVES), 0, s, a, gm, gn,
                        a.K / splits, a.M * a.N);
     return hipGetLastError();
 }
 
+template <int IN, int OUT>
+hipError_t dispatch_layout(const GemmArgs &a, int layout, int64_t splits, hipStream_t s)
+{
+    switch (layout) {
+    case 0: return launch<IN, OUT, false, false>(a, splits, s);
+    case DTM_LAYOUT_A_M_CONTIG: return launch<IN, OUT, true, false>(a, splits, s);
+    case DTM_LAYOUT_B_K_CONTIG: return launch<IN, OUT, false, true>(a, splits, s);
+    case DTM_LAYOUT_A_M_CONTIG | DTM_LAYOUT_B_K_CONTIG:
+        return launch<IN, OUT, true, true>(a, splits, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int IN>
-hipError_t dispatch_out(const GemmArgs &a, int out, int64_t splits, hipStream_t s)
+hipError_t dispatch_out(const GemmArgs &a, int layout, int out, int64_t splits, hipStream_t s)
 {
     switch (out) {
-    case DTM_F32: return launch<IN, DTM_F32>(a, splits, s);
-    case DTM_F16: return launch<IN, DTM_F16>(a, splits, s);
-    case DTM_BF16: return launch<IN, DTM_BF16>(a, splits, s);
+    case DTM_F32: return dispatch_layout<IN, DTM_F32>(a, layout, splits, s);
+    case DTM_F16: return dispatch_layout<IN, DTM_F16>(a, layout, splits, s);
+    case DTM_BF16: return dispatch_layout<IN, DTM_BF16>(a, layout, splits, s);
     }
     return hipErrorInvalidValue;
 }
@@ -356,19 +417,21 @@ bool mfma16_dma_fits(int64_t M, int64_t N, int64_t K, int64_t splits)
            K % (BK * splits) == 0 && (M / BM) * (N / BN) * splits <= 0x7fffffffLL;
 }
 
-hipError_t launch_mfma16_dma(const GemmArgs &a, int in, int out, hipStream_t s)
+int mfma16_dma_threads() { return 64 * DTM_DMA_WAVES; }
+
+hipError_t launch_mfma16_dma(const GemmArgs &a, int in, int out, int layout, hipStream_t s)
 {
     if (!mfma16_dma_fits(a.M, a.N, a.K, 1))
         return hipErrorInvalidConfiguration;
     switch (in) {
-    case DTM_F16: return dispatch_out<DTM_F16>(a, out, 1, s);
-    case DTM_BF16: return dispatch_out<DTM_BF16>(a, out, 1, s);
+    case DTM_F16: return dispatch_out<DTM_F16>(a, layout, out, 1, s);
+    case DTM_BF16: return dispatch_out<DTM_BF16>(a, layout, out, 1, s);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_mfma16_dma_partials(const GemmArgs &a, int in, int64_t splits, float *ws,
-                                      hipStream_t s)
+hipError_t launch_mfma16_dma_partials(const GemmArgs &a, int in, int layout, int64_t splits,
+                                      float *ws, hipStream_t s)
 {
     if (!mfma16_dma_fits(a.M, a.N, a.K, splits))
         return hipErrorInvalidConfiguration;
@@ -377,8 +440,8 @@ hipError_t launch_mfma16_dma_partials(const GemmArgs &a, int in, int64_t splits,
     w.scm = a.N;
     w.scn = 1;
     switch (in) {
-    case DTM_F16: return dispatch_out<DTM_F16>(w, DTM_F32, splits, s);
-    case DTM_BF16: return dispatch_out<DTM_BF16>(w, DTM_F32, splits, s);
+    case DTM_F16: return dispatch_out<DTM_F16>(w, layout, DTM_F32, splits, s);
+    case DTM_BF16: return dispatch_out<DTM_BF16>(w, layout, DTM_F32, splits, s);
     }
     return hipErrorInvalidValue;
 }

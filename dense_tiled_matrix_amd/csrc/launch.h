@@ -14,19 +14,23 @@ int generic_threads(int bm, int bn, int bk);
 hipError_t launch_generic(const GemmArgs &a, int in_dtype, int out_dtype, int bm, int bn, int bk,
                           hipStream_t s);
 
-// MFMA kernel for fp16/bf16 inputs with K-contiguous A and N-contiguous B.
+// Register-staged MFMA kernel for fp16/bf16 inputs with K-contiguous A and
+// N-contiguous B; any M, N, K (edge tiles masked).
 bool mfma16_has_config(int bm, int bn, int bk);
 hipError_t launch_mfma16(const GemmArgs &a, int in_dtype, int out_dtype, int bm, int bn, int bk,
                          bool ragged, hipStream_t s);
 
-// Deep-pipelined MFMA kernel (256 x 256 x 32 tiles, global -> LDS DMA) for
-// the same layouts when M and N are multiples of 256 and K of 32.
+// Deep-pipelined MFMA kernel (256 x 256 x 32 tiles, global -> LDS DMA) when
+// M and N are multiples of 256 and K of 32, for every operand layout:
+// `layout` holds dtm_layout bits (A M-contiguous, B K-contiguous).
 bool mfma16_dma_fits(int64_t M, int64_t N, int64_t K, int64_t splits);
-hipError_t launch_mfma16_dma(const GemmArgs &a, int in_dtype, int out_dtype, hipStream_t s);
+int mfma16_dma_threads();
+hipError_t launch_mfma16_dma(const GemmArgs &a, int in_dtype, int out_dtype, int layout,
+                             hipStream_t s);
 // Split-K on the same kernel: K in `splits` equal slices, fp32 partial tiles
 // written densely to ws[splits][M][N] (a.C and its strides are not used).
-hipError_t launch_mfma16_dma_partials(const GemmArgs &a, int in_dtype, int64_t splits, float *ws,
-                                      hipStream_t s);
+hipError_t launch_mfma16_dma_partials(const GemmArgs &a, int in_dtype, int layout, int64_t splits,
+                                      float *ws, hipStream_t s);
 // C = sum over s of ws[s] in order s = 0, 1, ..., converted once to out_dtype.
 hipError_t launch_splitk_reduce(const GemmArgs &a, int out_dtype, int64_t splits, const float *ws,
                                 hipStream_t s);

@@ -79,9 +79,20 @@ typedef enum {
     DTM_KERNEL_NONE = 0,      /* nothing to launch (M == 0 or N == 0) */
     DTM_KERNEL_ZERO_FILL = 1, /* K == 0: write zeros to C */
     DTM_KERNEL_GENERIC = 2,   /* any strides and dtypes; fp32 FMA on LDS tiles */
-    DTM_KERNEL_MFMA_F16 = 3,  /* fp16/bf16 inputs, K-contiguous A, N-contiguous B; MFMA */
+    DTM_KERNEL_MFMA_F16 = 3,  /* fp16/bf16 inputs on MFMA (layouts: dtm_layout) */
     DTM_KERNEL_MFMA_F32 = 4   /* fp32 inputs on fp32 MFMA */
 } dtm_kernel;
+
+/* Operand layouts the MFMA kernels read at full speed (bits of
+ * dtm_plan.layout).  Each operand must have one unit stride; its other
+ * stride (the leading dimension) a multiple of 16 bytes and its base 16-byte
+ * aligned.  With neither bit set, A is K-contiguous (stride_ak == 1) and B is
+ * N-contiguous (stride_bn == 1): both row-major.  A transposed view sets a
+ * bit.  Any other layout runs on the generic kernel. */
+typedef enum {
+    DTM_LAYOUT_A_M_CONTIG = 1, /* A has stride_am == 1 (e.g. the transpose of a K x M array) */
+    DTM_LAYOUT_B_K_CONTIG = 2  /* B has stride_bk == 1 (e.g. the transpose of an N x K array) */
+} dtm_layout;
 
 /* A tile configuration.  Zero fields mean "the selector chooses". */
 typedef struct {
@@ -103,6 +114,7 @@ typedef struct {
     int32_t threads;          /* threads per workgroup */
     int32_t fast_path;        /* 1 when the MFMA layout and alignment predicate holds */
     int32_t ragged;           /* 1 when M, N or K is not a multiple of its block */
+    int32_t layout;           /* dtm_layout bits of the operands (MFMA kernels; 0 otherwise) */
     uint64_t workspace_bytes; /* device scratch the plan needs (split-K partials) */
 } dtm_plan;
 

@@ -62,8 +62,10 @@ class CBuf:
         return host[idx].view(u), untouched
 
 
-def run(p, out_dtype=None, config=None, c_layout="N", c_pad=0, stream=None, expect=0):
-    """GEMM of problem ``p`` on the GPU; returns (C bits M x N, untouched)."""
+def run(p, out_dtype=None, config=None, c_layout="N", c_pad=0, stream=None, expect=0,
+        plan=None):
+    """GEMM of problem ``p`` on the GPU; returns (C bits M x N, untouched).
+    A dict passed as ``plan`` receives the plan of the call."""
     od = out_dtype or p.out_dtype
     sa = dev_storage(p.A.bits, p.in_dtype) if p.A.bits.size else None
     sb = dev_storage(p.B.bits, p.in_dtype) if p.B.bits.size else None
@@ -71,6 +73,11 @@ def run(p, out_dtype=None, config=None, c_layout="N", c_pad=0, stream=None, expe
     b_ptr = sb.data_ptr() + p.B.offset * ITEM[p.in_dtype] if sb is not None else 0
     c = CBuf(p.M, p.N, od, c_layout, pad=c_pad)
     s = torch.cuda.current_stream() if stream is None else stream
+    if plan is not None:
+        pst, pd = dtm.gemm_plan_raw(p.M, p.N, p.K, a_ptr, p.A.stride_r, p.A.stride_c, b_ptr,
+                                    p.B.stride_r, p.B.stride_c, c.ptr, c.scm, c.scn,
+                                    CODE[p.in_dtype], CODE[od], config=config)
+        plan.update(pd, status=pst)
     st = dtm.gemm_ex_raw(p.M, p.N, p.K, a_ptr, p.A.stride_r, p.A.stride_c, b_ptr, p.B.stride_r,
                          p.B.stride_c, c.ptr, c.scm, c.scn, CODE[p.in_dtype], CODE[od],
                          config=config, stream=s.cuda_stream)

@@ -28,20 +28,29 @@ def int_problem(M, N, K, ind, outd, R, seed, la="N", lb="N"):
                             name=f"int{M}x{N}x{K}")
 
 
-def padded_int_problem(M, N, K, ind, outd, R, seed, extra=0):
-    """Integer-valued row-major operands whose leading dimensions are rounded
-    up to a multiple of 8 elements (16 bytes), plus ``extra``; the padding
-    holds NaN, which must never be read."""
+def padded_int_problem(M, N, K, ind, outd, R, seed, extra=0, a_layout="N", b_layout="N"):
+    """Integer-valued operands whose leading dimensions are rounded up to a
+    multiple of 8 elements (16 bytes), plus ``extra``; the padding holds NaN,
+    which must never be read.  Layout "N" stores an operand row-major (A
+    K-contiguous, B N-contiguous); "T" stores its transpose row-major, so the
+    view has stride 1 along M (A) or K (B)."""
     rng = np.random.default_rng(seed)
-    lda = -(-K // 8) * 8 + extra
-    ldb = -(-N // 8) * 8 + extra
-    abuf = np.full((M, lda), np.nan)
-    abuf[:, :K] = rng.integers(-R, R + 1, size=(M, K))
-    bbuf = np.full((K, ldb), np.nan)
-    bbuf[:, :N] = rng.integers(-R, R + 1, size=(K, N))
-    A = W.Operand(W.to_bits(abuf, ind).reshape(-1), ind, M, K, 0, lda, 1)
-    B = W.Operand(W.to_bits(bbuf, ind).reshape(-1), ind, K, N, 0, ldb, 1)
-    return W.Problem(M, N, K, A, B, ind, outd, name=f"pad{M}x{N}x{K}")
+    a = rng.integers(-R, R + 1, size=(M, K))
+    b = rng.integers(-R, R + 1, size=(K, N))
+
+    def store(x, layout, name):
+        rows, cols = x.shape
+        if layout == "T":
+            x = x.T
+        ld = -(-x.shape[1] // 8) * 8 + extra
+        buf = np.full((x.shape[0], ld), np.nan)
+        buf[:, :x.shape[1]] = x
+        strides = (ld, 1) if layout == "N" else (1, ld)
+        return W.Operand(W.to_bits(buf, ind).reshape(-1), ind, rows, cols, 0, *strides)
+
+    A = store(a, a_layout, "A")
+    B = store(b, b_layout, "B")
+    return W.Problem(M, N, K, A, B, ind, outd, name=f"pad{a_layout}{b_layout}{M}x{N}x{K}")
 
 
 # ----------------------------------------------------------- the pages' cases
@@ -271,6 +280,51 @@ def test_mfma_pipelined_exact(ind):
         p = padded_int_problem(M, N, K, ind, outd, R, seed=400 + n, extra=8 * (n % 2))
         c, untouched = run(p, config=cfg, c_pad=4 if n % 2 else 0)
         compare(p, c, exact=True, label=f"pipelined {ind} {M}x{N}x{K}->{outd}")
+        assert untouched
+
+
+LAYOUT_BITS = {"NN": 0, "TN": dtm.DTM_LAYOUT_A_M_CONTIG, "NT": dtm.DTM_LAYOUT_B_K_CONTIG,
+               "TT": dtm.DTM_LAYOUT_A_M_CONTIG | dtm.DTM_LAYOUT_B_K_CONTIG}
+
+
+@pytest.mark.parametrize("layout", ["TN", "NT", "TT"])
+@pytest.mark.parametrize("ind", ["f16", "bf16"])
+def test_pipelined_layouts_exact(ind, layout):
+    """Transposed operands on the pipelined kernel (A M-contiguous and/or B
+    K-contiguous, staged as stored and read with transposing LDS reads):
+    pipeline depths 1, 3, 5 and many chunks, several grids, padded leading
+    dimensions, split-K, forced and selector plans; value-exact on
+    integer-valued inputs."""
+    shapes = [(256, 256, 32, 1), (512, 256, 96, 1), (256, 768, 160, 1), (768, 512, 2048, 1),
+              (512, 512, 4096, 8), (256, 256, 1024, 4)]
+    for n, (M, N, K, S) in enumerate(shapes):
+        outd = ["f32", "f16", "bf16"][n % 3]
+        p = padded_int_problem(M, N, K, ind, outd, 8 if K <= 256 else 2, seed=600 + n,
+                               extra=8 * (n % 2), a_layout=layout[0], b_layout=layout[1])
+        forced = n % 2 == 1 or n == 5
+        cfg = dict(kernel=MF16, block_m=256, block_n=256, block_k=32,
+                   split_k=S) if forced else None
+        plan = {}
+        c, untouched = run(p, config=cfg, c_pad=4 if n % 2 else 0, plan=plan)
+        assert plan["status"] == 0 and plan["block_k"] == 32, plan
+        assert plan["layout"] == LAYOUT_BITS[layout] and plan["split_k"] == S, plan
+        compare(p, c, exact=True, label=f"pipelined {layout} {ind} {M}x{N}x{K} S{S}->{outd}")
+        assert untouched
+
+
+@pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])
+def test_pipelined_layouts_random(layout):
+    """N(0,1) bf16 and U[-1,1] fp16 operands in every layout through the
+    selector's plan, against the oracle within the stated tolerance."""
+    for n, (ind, outd, dist) in enumerate([("bf16", "bf16", ("normal", 0.0, 1.0)),
+                                          ("f16", "f32", ("uniform", -1.0, 1.0))]):
+        p = W.random_problem(1024, 768, 1536, ind, outd, dist, seed=700 + n,
+                             a_layout=layout[0], b_layout=layout[1])
+        plan = {}
+        c, untouched = run(p, plan=plan)
+        assert plan["layout"] == LAYOUT_BITS[layout] and plan["block_k"] == 32, plan
+        err, tol = compare(p, c, label=f"{layout} {ind} 1024x768x1536")
+        note(f"{layout} {ind}->{outd}: max err {err:.3e} tol {tol:.3e}")
         assert untouched
 
 
