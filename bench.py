@@ -25,7 +25,8 @@ METRIC = "GEMM TFLOP/s and % of MFMA peak at fp16/bf16 4096³ and 8192³ on 1 MI
 # MI355X dense MFMA peaks (TFLOP/s): 256 CUs x 2.4 GHz x FLOP/clk/CU
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
 HOST_THREADS_CAP = 16  # the host-core share of one GPU on the GPU machines
-KERNEL_SOURCES = ["dense_tiled_matrix_amd/csrc/gemm_mfma16.hip",
+# sources of the timed kernel (the 256 x 256 x 32 pipelined MFMA kernel)
+KERNEL_SOURCES = ["dense_tiled_matrix_amd/csrc/gemm_mfma16_dma.hip",
                   "dense_tiled_matrix_amd/csrc/device.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 

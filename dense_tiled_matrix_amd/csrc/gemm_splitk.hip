@@ -27,9 +27,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p, int64_t 
         const int64_t i = g / groups_per_row;
         const int64_t j = (g - i * groups_per_row) * 4;
         const int64_t e = i * p.N + j;
-        f32x4 acc = *reinterpret_cast<const f32x4 *>(ws + e);
-        for (int64_t s = 1; s < splits; ++s)
-            acc += *reinterpret_cast<const f32x4 *>(ws + s * MN + e);
+        const float *src = ws + e;
+        f32x4 acc = *reinterpret_cast<const f32x4 *>(src);
+        int64_t s = 1;
+        // Loads of BATCH slices are issued together (memory-level
+        // parallelism), then added one by one in slice order.
+        constexpr int BATCH = 8;
+        for (; s + BATCH <= splits; s += BATCH) {
+            f32x4 v[BATCH];
+#pragma unroll
+            for (int q = 0; q < BATCH; ++q)
+                v[q] = *reinterpret_cast<const f32x4 *>(src + (s + q) * MN);
+#pragma unroll
+            for (int q = 0; q < BATCH; ++q)
+                acc += v[q];
+        }
+        for (; s < splits; ++s)
+            acc += *reinterpret_cast<const f32x4 *>(src + s * MN);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             store_elem<OUT>(p.C, i * p.scm + (j + q) * p.scn, acc[q]);
