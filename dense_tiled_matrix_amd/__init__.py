@@ -29,9 +29,11 @@ STATUS = {
 }
 globals().update({v: k for k, v in STATUS.items()})
 # dtm_kernel
-KERNELS = {0: "none", 1: "zero_fill", 2: "generic", 3: "mfma_f16", 4: "mfma_f32"}
+KERNELS = {0: "none", 1: "zero_fill", 2: "generic", 3: "mfma_f16", 4: "mfma_f32",
+           5: "generic_fp16acc"}
 DTM_KERNEL_NONE, DTM_KERNEL_ZERO_FILL, DTM_KERNEL_GENERIC = 0, 1, 2
 DTM_KERNEL_MFMA_F16, DTM_KERNEL_MFMA_F32 = 3, 4
+DTM_KERNEL_GENERIC_FP16ACC = 5  # negative control: fp16 accumulator, forced only
 DTM_LAYOUT_A_M_CONTIG, DTM_LAYOUT_B_K_CONTIG = 1, 2
 
 

@@ -264,7 +264,9 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
         p.block_k = 16;
         p.threads = 256;
         p.layout = layout;
-    } else if (kernel == DTM_KERNEL_GENERIC) {
+    } else if (kernel == DTM_KERNEL_GENERIC || kernel == DTM_KERNEL_GENERIC_FP16ACC) {
+        if (kernel == DTM_KERNEL_GENERIC_FP16ACC && c.in != DTM_F16)
+            return DTM_ERR_CONFIG;
         if (forced_dims) {
             if (!dtm::generic_has_config(force->block_m, force->block_n, force->block_k))
                 return DTM_ERR_CONFIG;
@@ -370,6 +372,9 @@ int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t w
     case DTM_KERNEL_GENERIC:
         e = dtm::launch_generic(a, c.in, c.out, p.block_m, p.block_n, p.block_k, s);
         break;
+    case DTM_KERNEL_GENERIC_FP16ACC:
+        e = dtm::launch_generic_fp16acc(a, c.out, p.block_m, p.block_n, p.block_k, s);
+        break;
     case DTM_KERNEL_MFMA_F16:
         if (p.split_k > 1) {
             void *ws = workspace;
@@ -459,6 +464,7 @@ const char *gemm_kernel_name(int kernel)
     case DTM_KERNEL_GENERIC: return "generic";
     case DTM_KERNEL_MFMA_F16: return "mfma_f16";
     case DTM_KERNEL_MFMA_F32: return "mfma_f32";
+    case DTM_KERNEL_GENERIC_FP16ACC: return "generic_fp16acc";
     }
     return "unknown";
 }

@@ -12,15 +12,22 @@
 // This path serves every layout the MFMA kernels do not: transposed and
 // broadcast views, leading dimensions that are not 16-byte multiples,
 // unaligned bases, and the small forced tiles (4x4x4) of the worked examples.
+//
+// ACC16 instantiations (fp16 inputs only) reproduce the fp16-accumulator
+// variant of section 13.3 as a negative control: each K-chunk's tile product
+// is formed in fp32 as above, rounded to fp16, and added into an fp16
+// accumulator with an fp16 addition (round to nearest even), so the rounding
+// error grows with the number of chunks.
 #include "launch.h"
 
 namespace dtm {
 namespace {
 
-template <int IN, int OUT, int BM, int BN, int BK, int TM, int TN>
+template <int IN, int OUT, int BM, int BN, int BK, int TM, int TN, bool ACC16>
 __global__ __launch_bounds__((BM / TM) * (BN / TN)) void gemm_generic_kernel(GemmArgs p,
                                                                                int64_t grid_n)
 {
+    static_assert(!ACC16 || IN == DTM_F16, "the fp16 accumulator is for fp16 inputs");
     constexpr int THREADS = (BM / TM) * (BN / TN);
     // k-major tiles: thread (ty, tx) reads TM consecutive A values and TN
     // consecutive B values per k.
@@ -42,11 +49,14 @@ __global__ __launch_bounds__((BM / TM) * (BN / TN)) void gemm_generic_kernel(Gem
                                                            (p.sbk < 0 ? -p.sbk : p.sbk));
 
     float acc[TM][TN];
+    _Float16 acc16[TM][TN];  // ACC16 only
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j) {
             acc[i][j] = 0.0f;
+            acc16[i][j] = static_cast<_Float16>(0.0f);
+        }
 
     for (int64_t k0 = 0; k0 < p.K; k0 += BK) {
         for (int e = t; e < BM * BK; e += THREADS) {
@@ -83,7 +93,24 @@ __global__ __launch_bounds__((BM / TM) * (BN / TN)) void gemm_generic_kernel(Gem
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
         }
+        if constexpr (ACC16) {
+            // the chunk's product, rounded to fp16, then an fp16 addition
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    acc16[i][j] = acc16[i][j] + static_cast<_Float16>(acc[i][j]);
+                    acc[i][j] = 0.0f;
+                }
+        }
         __syncthreads();
+    }
+    if constexpr (ACC16) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = static_cast<float>(acc16[i][j]);  // exact
     }
 
 #pragma unroll
@@ -98,7 +125,7 @@ __global__ __launch_bounds__((BM / TM) * (BN / TN)) void gemm_generic_kernel(Gem
     }
 }
 
-template <int IN, int OUT, int BM, int BN, int BK, int TM, int TN>
+template <int IN, int OUT, int BM, int BN, int BK, int TM, int TN, bool ACC16>
 hipError_t launch_cfg(const GemmArgs &a, hipStream_t s)
 {
     const int64_t gm = cdiv(a.M, BM), gn = cdiv(a.N, BN);
@@ -106,7 +133,7 @@ hipError_t launch_cfg(const GemmArgs &a, hipStream_t s)
     if (tiles > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     constexpr int THREADS = (BM / TM) * (BN / TN);
-    hipLaunchKernelGGL((gemm_generic_kernel<IN, OUT, BM, BN, BK, TM, TN>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((gemm_generic_kernel<IN, OUT, BM, BN, BK, TM, TN, ACC16>), dim3((unsigned)tiles),
                        dim3(THREADS), 0, s, a, gn);
     return hipGetLastError();
 }
@@ -119,29 +146,29 @@ constexpr Cfg kConfigs[] = {
     {4, 4, 4, 1, 1}, {16, 16, 16, 1, 1}, {32, 32, 16, 2, 2}, {64, 64, 16, 4, 4}, {128, 128, 8, 8, 8},
 };
 
-template <int IN, int OUT>
+template <int IN, int OUT, bool ACC16>
 hipError_t dispatch_tile(const GemmArgs &a, int bm, int bn, int bk, hipStream_t s)
 {
     if (bm == 4 && bn == 4 && bk == 4)
-        return launch_cfg<IN, OUT, 4, 4, 4, 1, 1>(a, s);
+        return launch_cfg<IN, OUT, 4, 4, 4, 1, 1, ACC16>(a, s);
     if (bm == 16 && bn == 16 && bk == 16)
-        return launch_cfg<IN, OUT, 16, 16, 16, 1, 1>(a, s);
+        return launch_cfg<IN, OUT, 16, 16, 16, 1, 1, ACC16>(a, s);
     if (bm == 32 && bn == 32 && bk == 16)
-        return launch_cfg<IN, OUT, 32, 32, 16, 2, 2>(a, s);
+        return launch_cfg<IN, OUT, 32, 32, 16, 2, 2, ACC16>(a, s);
     if (bm == 64 && bn == 64 && bk == 16)
-        return launch_cfg<IN, OUT, 64, 64, 16, 4, 4>(a, s);
+        return launch_cfg<IN, OUT, 64, 64, 16, 4, 4, ACC16>(a, s);
     if (bm == 128 && bn == 128 && bk == 8)
-        return launch_cfg<IN, OUT, 128, 128, 8, 8, 8>(a, s);
+        return launch_cfg<IN, OUT, 128, 128, 8, 8, 8, ACC16>(a, s);
     return hipErrorInvalidConfiguration;
 }
 
-template <int IN>
+template <int IN, bool ACC16>
 hipError_t dispatch_out(const GemmArgs &a, int out, int bm, int bn, int bk, hipStream_t s)
 {
     switch (out) {
-    case DTM_F32: return dispatch_tile<IN, DTM_F32>(a, bm, bn, bk, s);
-    case DTM_F16: return dispatch_tile<IN, DTM_F16>(a, bm, bn, bk, s);
-    case DTM_BF16: return dispatch_tile<IN, DTM_BF16>(a, bm, bn, bk, s);
+    case DTM_F32: return dispatch_tile<IN, DTM_F32, ACC16>(a, bm, bn, bk, s);
+    case DTM_F16: return dispatch_tile<IN, DTM_F16, ACC16>(a, bm, bn, bk, s);
+    case DTM_BF16: return dispatch_tile<IN, DTM_BF16, ACC16>(a, bm, bn, bk, s);
     }
     return hipErrorInvalidValue;
 }
@@ -168,11 +195,17 @@ hipError_t launch_generic(const GemmArgs &a, int in, int out, int bm, int bn, in
                           hipStream_t s)
 {
     switch (in) {
-    case DTM_F32: return dispatch_out<DTM_F32>(a, out, bm, bn, bk, s);
-    case DTM_F16: return dispatch_out<DTM_F16>(a, out, bm, bn, bk, s);
-    case DTM_BF16: return dispatch_out<DTM_BF16>(a, out, bm, bn, bk, s);
+    case DTM_F32: return dispatch_out<DTM_F32, false>(a, out, bm, bn, bk, s);
+    case DTM_F16: return dispatch_out<DTM_F16, false>(a, out, bm, bn, bk, s);
+    case DTM_BF16: return dispatch_out<DTM_BF16, false>(a, out, bm, bn, bk, s);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_generic_fp16acc(const GemmArgs &a, int out, int bm, int bn, int bk,
+                                  hipStream_t s)
+{
+    return dispatch_out<DTM_F16, true>(a, out, bm, bn, bk, s);
 }
 
 // ---- K == 0: the empty sum -------------------------------------------------

@@ -13,6 +13,10 @@ bool generic_has_config(int bm, int bn, int bk);
 int generic_threads(int bm, int bn, int bk);
 hipError_t launch_generic(const GemmArgs &a, int in_dtype, int out_dtype, int bm, int bn, int bk,
                           hipStream_t s);
+// The same kernel with the fp16 accumulator of the negative control (fp16
+// inputs): every K-chunk product rounded to fp16 and added in fp16.
+hipError_t launch_generic_fp16acc(const GemmArgs &a, int out_dtype, int bm, int bn, int bk,
+                                  hipStream_t s);
 
 // Register-staged MFMA kernel for fp16/bf16 inputs with K-contiguous A and
 // N-contiguous B; any M, N, K (edge tiles masked).

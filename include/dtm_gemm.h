@@ -80,7 +80,14 @@ typedef enum {
     DTM_KERNEL_ZERO_FILL = 1, /* K == 0: write zeros to C */
     DTM_KERNEL_GENERIC = 2,   /* any strides and dtypes; fp32 FMA on LDS tiles */
     DTM_KERNEL_MFMA_F16 = 3,  /* fp16/bf16 inputs on MFMA (layouts: dtm_layout) */
-    DTM_KERNEL_MFMA_F32 = 4   /* fp32 inputs on fp32 MFMA */
+    DTM_KERNEL_MFMA_F32 = 4,  /* fp32 inputs on fp32 MFMA */
+    DTM_KERNEL_GENERIC_FP16ACC = 5 /* negative control, only when forced through gemm_ex and
+                                      gemm_plan: fp16 inputs, the generic kernel with the
+                                      fp16 accumulator of "Chapter 13: The Blocked Matmul
+                                      Kernel", section 13.3 -- each BLOCK_K chunk's tile
+                                      product (fp32) is rounded to fp16 and added into an
+                                      fp16 accumulator; not a correct GEMM, it shows the
+                                      accumulation error the fp32 accumulator avoids */
 } dtm_kernel;
 
 /* Operand layouts the MFMA kernels read at full speed (bits of

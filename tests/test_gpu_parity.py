@@ -14,12 +14,14 @@ import torch
 import dense_tiled_matrix_amd as dtm
 import oracle
 import workloads as W
+from conftest import read_golden
 from gpu_util import CBuf, compare, dev_storage, note, run
 
 pytestmark = pytest.mark.gpu
 
 GEN = dtm.DTM_KERNEL_GENERIC
 MF16 = dtm.DTM_KERNEL_MFMA_F16
+ACC16 = dtm.DTM_KERNEL_GENERIC_FP16ACC
 T444 = dict(kernel=GEN, block_m=4, block_n=4, block_k=4)
 
 
@@ -137,6 +139,75 @@ def test_seed0_accumulation_fp16_out():
         assert (got != oracle.decode(c16, "f16")).sum() <= 2
         assert err <= 9.737179152580211e-05 * 1.01
         assert err * 10 < float(np.abs(fp16acc - c64).max())
+
+
+# --------------------------------------- the fp16-accumulator negative control
+
+
+def _fp16acc_against_emulation(p, cfg, label):
+    """The on-device fp16-accumulator kernel against the oracle's emulation
+    of section 13.3 with the same BLOCK_K.  The two differ only in how a
+    chunk's tile product is formed before its rounding to fp16: an fp32 FMA
+    chain on the device, the exact sum in the oracle.  They round to
+    different fp16 values only when the exact sum lies within the fp32
+    chain's error (about sqrt(BLOCK_K) * 2^-24 relative) of an fp16 rounding
+    boundary, an event of probability ~2^-12 per chunk; each such event moves
+    the fp16 accumulator by about one fp16 ulp, and fp16 additions of the
+    same later chunk values keep that offset.  Bound: a few ulps at the
+    result's magnitude, on a small fraction of the outputs."""
+    c, untouched = run(p, out_dtype="f16", config=cfg)
+    emu = oracle.gemm_fp16acc_problem(p, cfg["block_k"])
+    got, want = oracle.decode(c, "f16"), oracle.decode(emu, "f16")
+    top = max(float(np.abs(want).max()), 2.0 ** -14)
+    ulp = 2.0 ** (np.floor(np.log2(top)) - 10)
+    ndiff = int((c != emu).sum())
+    maxd = float(np.abs(got - want).max())
+    note(f"{label}: {ndiff} of {c.size} outputs differ from the emulation, max {maxd:.3e} "
+         f"(fp16 ulp at |C| {ulp:.3e})")
+    assert untouched
+    assert maxd <= 4 * ulp
+    assert ndiff <= max(2, c.size // 20)
+    return got
+
+
+@pytest.mark.parametrize("bk", [8, 4])
+def test_fp16acc_control_seed0(bk):
+    """Worked Example 13.3.1 on the device with the fp16 accumulator: the
+    max error against the fp64 truth is the printed fp16-accumulator figure
+    (up to the fp32-versus-exact chunk product), more than 10x the fp32
+    accumulator's printed figure."""
+    g = {t[0]: t[1] for t in read_golden("accumulation_seed0.txt")["_"]}
+    p = W.seed0_fp16_problem()
+    cfg = dict(kernel=ACC16, block_m=128, block_n=128, block_k=8) if bk == 8 else \
+        dict(kernel=ACC16, block_m=4, block_n=4, block_k=4)
+    got = _fp16acc_against_emulation(p, cfg, f"seed0 BLOCK_K {bk}")
+    c64, _ = oracle.gemm_problem(p)
+    err = float(np.abs(got - c64).max())
+    note(f"seed0 BLOCK_K {bk}: fp16-acc max error {err!r} (printed for BLOCK_K 8: "
+         f"{g['fp16acc_max_abs_diff']!r})")
+    assert err > 10 * float(g["fp32acc_max_abs_diff"])
+    if bk == 8:
+        assert abs(err - float(g["fp16acc_max_abs_diff"])) <= 2 * 2.0 ** -16
+
+
+def test_fp16acc_control_long_k():
+    """The long-K workload's 64 x 64 corner (fp16 U[0,1], K = 65536) with the
+    fp16 accumulator on the device: it follows the emulation, and its error
+    against the fp64 truth is over 100x that of the fp32-accumulating
+    split-K path on the same corner."""
+    w = W.workload("f16_skinny512x512x65536_f32out")
+    A2, B2 = w.A.bits.reshape(w.M, w.K), w.B.bits.reshape(w.K, w.N)
+    p = W.Problem(64, 64, w.K, W.dense(np.ascontiguousarray(A2[:64]), "f16"),
+                  W.dense(np.ascontiguousarray(B2[:, :64]), "f16"), "f16", "f32",
+                  name="skinny corner")
+    got = _fp16acc_against_emulation(p, dict(kernel=ACC16, block_m=64, block_n=64, block_k=16),
+                                     "long-K corner BLOCK_K 16")
+    c64, _ = oracle.gemm_problem(p)
+    c32, _ = run(p, out_dtype="f32")
+    err16 = float(np.abs(got - c64).max())
+    err32 = float(np.abs(oracle.decode(c32, "f32") - c64).max())
+    note(f"long-K corner: fp16-acc max error {err16:.4g}, fp32-acc {err32:.3e}")
+    assert err16 > 100 * err32
 
 
 # ------------------------------------------------------ the measured workloads

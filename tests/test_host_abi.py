@@ -154,6 +154,31 @@ def test_fp32_selector():
     assert st == dtm.DTM_ERR_CONFIG
 
 
+def test_fp16acc_control_is_forced_only():
+    """The fp16-accumulator negative control runs only when forced, on fp16
+    inputs, on the generic kernel's tiles, without split-K."""
+    ACC = dtm.DTM_KERNEL_GENERIC_FP16ACC
+    for M, N, K, kw in [(4, 4, 1024, dict(ind=F16, outd=F16)),
+                        (1024, 1024, 1024, dict(ind=F16, outd=F32))]:
+        st, p = plan(M, N, K, **kw)
+        assert st == 0 and p["kernel"] != ACC
+    st, p = plan(4, 4, 1024, ind=F16, outd=F16,
+                 config=dict(kernel=ACC, block_m=128, block_n=128, block_k=8))
+    assert st == 0 and p["kernel"] == ACC and p["kernel_name"] == "generic_fp16acc"
+    assert (p["block_k"], p["k_iters"], p["threads"]) == (8, 128, 256)
+    assert dtm.gemm_kernel_name(ACC) == "generic_fp16acc"
+    st, p = plan(300, 200, 150, ind=F16, outd=F32, config=dict(kernel=ACC))
+    assert st == 0 and p["kernel"] == ACC
+    for kw in [dict(ind=BF16), dict(ind=F32, sam=1024)]:
+        st, _ = plan(256, 256, 1024, config=dict(kernel=ACC), **kw)
+        assert st == dtm.DTM_ERR_CONFIG, kw
+    st, _ = plan(256, 256, 1024, ind=F16, config=dict(kernel=ACC, block_m=256, block_n=256,
+                                                      block_k=32))
+    assert st == dtm.DTM_ERR_CONFIG
+    st, _ = plan(256, 256, 1024, ind=F16, config=dict(kernel=ACC, split_k=4))
+    assert st == dtm.DTM_ERR_CONFIG
+
+
 def test_degenerate_shapes():
     st, p = plan(0, 5, 7)
     assert st == 0 and p["kernel_name"] == "none"
