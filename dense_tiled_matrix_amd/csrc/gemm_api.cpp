@@ -197,12 +197,11 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
         *out = p;
         return DTM_OK;
     }
-    // The pipelined kernel reads every layout; the register-staged fp16/bf16
-    // kernel and the fp32 kernel read row-major A and B only.
+    // Every MFMA kernel reads all four operand layouts.
     const int layout = mfma_layout(c);
     const bool dma = is16(c) && layout >= 0 && dtm::mfma16_dma_fits(c.M, c.N, c.K, 1);
-    const bool fast16 = is16(c) && (layout == 0 || dma);
-    const bool fast32 = c.in == DTM_F32 && layout == 0;
+    const bool fast16 = is16(c) && layout >= 0;
+    const bool fast32 = c.in == DTM_F32 && layout >= 0;
     p.fast_path = fast16 || fast32 ? 1 : 0;
     if (c.K == 0) {
         p.kernel = DTM_KERNEL_ZERO_FILL;
@@ -227,8 +226,7 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
             const bool dma_cfg = force->block_m == 256 && force->block_n == 256 &&
                                  force->block_k == 32;
             if (dma_cfg ? !dma
-                        : layout != 0 || !dtm::mfma16_has_config(force->block_m, force->block_n,
-                                                                 force->block_k))
+                        : !dtm::mfma16_has_config(force->block_m, force->block_n, force->block_k))
                 return DTM_ERR_CONFIG;
             p.block_m = force->block_m;
             p.block_n = force->block_n;
@@ -237,7 +235,7 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
             const int64_t tiles256 = cdiv(c.M, 256) * cdiv(c.N, 256);
             const bool big = tiles256 >= 256;
             const int64_t split = dma ? pick_split(c, tiles256) : 1;
-            if (dma && (big || split > 1 || layout != 0)) {
+            if (dma && (big || split > 1)) {
                 p.block_m = p.block_n = 256;
                 p.block_k = 32;
                 p.split_k = static_cast<int32_t>(split);
@@ -393,11 +391,12 @@ int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t w
         } else if (p.block_k == 32)
             e = dtm::launch_mfma16_dma(a, c.in, c.out, p.layout, s);
         else
-            e = dtm::launch_mfma16(a, c.in, c.out, p.block_m, p.block_n, p.block_k,
+            e = dtm::launch_mfma16(a, c.in, c.out, p.block_m, p.block_n, p.block_k, p.layout,
                                    p.ragged != 0, s);
         break;
     case DTM_KERNEL_MFMA_F32:
-        e = dtm::launch_mfma32(a, c.out, p.block_m, p.block_n, p.block_k, p.ragged != 0, s);
+        e = dtm::launch_mfma32(a, c.out, p.block_m, p.block_n, p.block_k, p.layout,
+                               p.ragged != 0, s);
         break;
     default: return DTM_ERR_CONFIG;
     }

@@ -16,14 +16,15 @@
 //    (v_mfma_f32_32x32x16_{f16,bf16}: A fragment = 8 k-values of one row per
 //    lane, B fragment = 8 k-values of one column per lane, 16 fp32 results
 //    per lane).  The accumulators live in the AccVGPR file.
-//  * A (K-contiguous) and B (N-contiguous) tiles are read from global memory
-//    with 16-byte loads, coalesced along each operand's contiguous axis.
+//  * Each operand tile is read from global memory with 16-byte loads along
+//    its contiguous axis: K for a K-contiguous operand (A row-major, or B
+//    given as the transpose of an N x K array), M or N otherwise.
 //  * In LDS both tiles are stored "row x k" with k contiguous, so both
-//    fragment reads are single ds_read_b128.  B arrives N-contiguous; each
-//    thread loads a KB x 8 (k x n) block and transposes it in registers
-//    before writing it.  Rows are padded by one 16-byte unit (stride 144 B),
-//    which spreads 16 consecutive rows over distinct bank groups for the
-//    fragment reads.
+//    fragment reads are single ds_read_b128.  An M- or N-contiguous operand
+//    is transposed in registers on the way: each thread loads a KB x 8
+//    (k x row) block and writes its columns as k-contiguous runs.  Rows are
+//    padded by one 16-byte unit (stride 144 B), which spreads 16 consecutive
+//    rows over distinct bank groups for the fragment reads.
 //  * Two LDS stages: the global loads for chunk k+1 are issued before the
 //    MFMAs of chunk k and written to the other stage after them, with one
 //    barrier per chunk.
@@ -76,7 +77,86 @@ __device__ __forceinline__ uint32_t half_of(const u32x4 &v, int j)
     return (j & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-template <int IN, int OUT, int BM, int BN, bool RAGGED>
+// Global -> registers for the R x BK tile of one operand starting at row
+// (or column) mn0 and k0; X addresses element (mn, k) at mn*s_mn + k*s_k and
+// the operand has ext rows.  Each of the 256 threads holds R/32 16-byte
+// units:
+//  K-contiguous (KC): unit i is chunk t%8 (k 8c .. 8c+7) of row t/8 + 32 i;
+//  otherwise: unit i is k-row KB*g + i (KB = R/32, g = t % (BK/KB)) at rows
+//  8c .. 8c+7, c = t / (BK/KB).
+// RAGGED: slots outside the view are exact zeros and are never read.
+template <int R, bool KC, bool RAGGED>
+__device__ __forceinline__ void load_operand(u32x4 (&r)[R / 32], const uint16_t *X, int64_t mn0,
+                                             int64_t s_mn, int64_t s_k, int64_t ext,
+                                             int64_t K, int64_t k0, int t)
+{
+    constexpr int UNITS = R / 32;
+    if constexpr (KC) {
+        const int c = t & 7, row = t >> 3;
+#pragma unroll
+        for (int i = 0; i < UNITS; ++i) {
+            const int64_t mn = mn0 + row + 32 * i;
+            const uint16_t *src = X + mn * s_mn + k0 + 8 * c;
+            if constexpr (RAGGED)
+                r[i] = load8_masked(src, mn < ext ? K - (k0 + 8 * c) : 0);
+            else
+                r[i] = *reinterpret_cast<const u32x4 *>(src);
+        }
+    } else {
+        constexpr int KB = UNITS, KG = BK / KB;
+        const int g = t % KG, c = t / KG;
+#pragma unroll
+        for (int i = 0; i < KB; ++i) {
+            const int64_t k = k0 + KB * g + i;
+            const uint16_t *src = X + k * s_k + mn0 + 8 * c;
+            if constexpr (RAGGED)
+                r[i] = load8_masked(src, k < K ? ext - (mn0 + 8 * c) : 0);
+            else
+                r[i] = *reinterpret_cast<const u32x4 *>(src);
+        }
+    }
+}
+
+// Registers -> the operand's part of an LDS stage (rows of ROW_UNITS
+// 16-byte units, k contiguous).  An M/N-contiguous KB x 8 block is
+// transposed on the way, so that its column j becomes a k-contiguous run in
+// LDS row 8c + j.
+template <int R, bool KC>
+__device__ __forceinline__ void store_operand(const u32x4 (&r)[R / 32], u32x4 *s, int t)
+{
+    constexpr int UNITS = R / 32;
+    if constexpr (KC) {
+        const int c = t & 7, row = t >> 3;
+#pragma unroll
+        for (int i = 0; i < UNITS; ++i)
+            s[(row + 32 * i) * ROW_UNITS + c] = r[i];
+    } else {
+        constexpr int KB = UNITS, KG = BK / KB;
+        static_assert(KB == 8 || KB == 4, "the transposed block is 8x8 or 4x8");
+        const int g = t % KG, c = t / KG;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int n = 8 * c + j;
+            if constexpr (KB == 8) {
+                u32x4 v;
+                v.x = half_of(r[0], j) | (half_of(r[1], j) << 16);
+                v.y = half_of(r[2], j) | (half_of(r[3], j) << 16);
+                v.z = half_of(r[4], j) | (half_of(r[5], j) << 16);
+                v.w = half_of(r[6], j) | (half_of(r[7], j) << 16);
+                s[n * ROW_UNITS + g] = v;
+            } else {
+                u32x2 v;
+                v.x = half_of(r[0], j) | (half_of(r[1], j) << 16);
+                v.y = half_of(r[2], j) | (half_of(r[3], j) << 16);
+                reinterpret_cast<u32x2 *>(s)[n * (2 * ROW_UNITS) + g] = v;
+            }
+        }
+    }
+}
+
+// TA: A is M-contiguous (stride_am == 1), else K-contiguous.
+// TB: B is K-contiguous (stride_bk == 1), else N-contiguous.
+template <int IN, int OUT, int BM, int BN, bool RAGGED, bool TA, bool TB>
 __global__ __launch_bounds__(256) void gemm_mfma16_kernel(GemmArgs p, int64_t grid_m,
                                                           int64_t grid_n)
 {
@@ -84,11 +164,6 @@ __global__ __launch_bounds__(256) void gemm_mfma16_kernel(GemmArgs p, int64_t gr
     constexpr int MI = WM / 32, NI = WN / 32;     // 32x32 MFMA tiles per wave
     constexpr int A_UNITS = BM * ROW_UNITS;
     constexpr int STAGE_UNITS = (BM + BN) * ROW_UNITS;
-    constexpr int A_LOADS = BM * (BK / 8) / 256;  // 16-byte A chunks per thread
-    constexpr int KB = BN / 32;                   // k-rows of the thread's B block
-    constexpr int KG = BK / KB;                   // B k-groups
-    static_assert(A_LOADS * 256 == BM * (BK / 8), "A tile must split evenly");
-    static_assert(KB == 8 || KB == 4, "B block is 8x8 or 4x8");
 
     __shared__ u32x4 lds[2 * STAGE_UNITS];
 
@@ -103,65 +178,17 @@ __global__ __launch_bounds__(256) void gemm_mfma16_kernel(GemmArgs p, int64_t gr
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
 
-    // A: thread loads chunk (t % 8) of rows (t / 8) + 32 i.
-    const int a_chunk = t & 7, a_row = t >> 3;
-    const uint16_t *a_base = A + (m0 + a_row) * p.sam + 8 * a_chunk;
-    // B: thread loads rows KB*g .. KB*g+KB-1, columns 8c .. 8c+7.
-    const int b_g = t % KG, b_c = t / KG;
-    const uint16_t *b_base = B + (int64_t)(KB * b_g) * p.sbk + n0 + 8 * b_c;
+    u32x4 ra[BM / 32];
+    u32x4 rb[BN / 32];
 
-    u32x4 ra[A_LOADS];
-    u32x4 rb[KB];
-
-    // Global -> registers for the K-chunk starting at k0.
     auto load_tile = [&](int64_t k0) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < A_LOADS; ++i) {
-            const uint16_t *src = a_base + (int64_t)(32 * i) * p.sam + k0;
-            if constexpr (RAGGED) {
-                const bool row_ok = (m0 + a_row + 32 * i) < p.M;
-                ra[i] = load8_masked(src, row_ok ? p.K - (k0 + 8 * a_chunk) : 0);
-            } else {
-                ra[i] = *reinterpret_cast<const u32x4 *>(src);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < KB; ++i) {
-            const uint16_t *src = b_base + (k0 + i) * p.sbk;
-            if constexpr (RAGGED) {
-                const bool k_ok = (k0 + KB * b_g + i) < p.K;
-                rb[i] = load8_masked(src, k_ok ? p.N - (n0 + 8 * b_c) : 0);
-            } else {
-                rb[i] = *reinterpret_cast<const u32x4 *>(src);
-            }
-        }
+        load_operand<BM, !TA, RAGGED>(ra, A, m0, p.sam, p.sak, p.M, p.K, k0, t);
+        load_operand<BN, TB, RAGGED>(rb, B, n0, p.sbn, p.sbk, p.N, p.K, k0, t);
     };
-
-    // Registers -> LDS stage; B's KB x 8 block is transposed on the way so
-    // that column j becomes a k-contiguous run in LDS row n = 8c + j.
     auto store_tile = [&](int stage) __attribute__((always_inline)) {
         u32x4 *sa = lds + stage * STAGE_UNITS;
-        u32x4 *sb = sa + A_UNITS;
-#pragma unroll
-        for (int i = 0; i < A_LOADS; ++i)
-            sa[(a_row + 32 * i) * ROW_UNITS + a_chunk] = ra[i];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int n = 8 * b_c + j;
-            if constexpr (KB == 8) {
-                u32x4 v;
-                v.x = half_of(rb[0], j) | (half_of(rb[1], j) << 16);
-                v.y = half_of(rb[2], j) | (half_of(rb[3], j) << 16);
-                v.z = half_of(rb[4], j) | (half_of(rb[5], j) << 16);
-                v.w = half_of(rb[6], j) | (half_of(rb[7], j) << 16);
-                sb[n * ROW_UNITS + b_g] = v;
-            } else {
-                u32x2 v;
-                v.x = half_of(rb[0], j) | (half_of(rb[1], j) << 16);
-                v.y = half_of(rb[2], j) | (half_of(rb[3], j) << 16);
-                reinterpret_cast<u32x2 *>(sb)[n * (2 * ROW_UNITS) + b_g] = v;
-            }
-        }
+        store_operand<BM, !TA>(ra, sa, t);
+        store_operand<BN, TB>(rb, sa + A_UNITS, t);
     };
 
     floatx16 acc[MI][NI];
@@ -242,7 +269,7 @@ __global__ __launch_bounds__(256) void gemm_mfma16_kernel(GemmArgs p, int64_t gr
     }
 }
 
-template <int IN, int OUT, int BM, int BN>
+template <int IN, int OUT, int BM, int BN, bool TA, bool TB>
 hipError_t launch_tile(const GemmArgs &a, bool ragged, hipStream_t s)
 {
     const int64_t gm = cdiv(a.M, BM), gn = cdiv(a.N, BN);
@@ -250,31 +277,46 @@ hipError_t launch_tile(const GemmArgs &a, bool ragged, hipStream_t s)
     if (tiles > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     if (ragged)
-        hipLaunchKernelGGL((gemm_mfma16_kernel<IN, OUT, BM, BN, true>), dim3((unsigned)tiles),
-                           dim3(256), 0, s, a, gm, gn);
+        hipLaunchKernelGGL((gemm_mfma16_kernel<IN, OUT, BM, BN, true, TA, TB>),
+                           dim3((unsigned)tiles), dim3(256), 0, s, a, gm, gn);
     else
-        hipLaunchKernelGGL((gemm_mfma16_kernel<IN, OUT, BM, BN, false>), dim3((unsigned)tiles),
-                           dim3(256), 0, s, a, gm, gn);
+        hipLaunchKernelGGL((gemm_mfma16_kernel<IN, OUT, BM, BN, false, TA, TB>),
+                           dim3((unsigned)tiles), dim3(256), 0, s, a, gm, gn);
     return hipGetLastError();
 }
 
+template <int IN, int OUT, int BM, int BN>
+hipError_t dispatch_layout(const GemmArgs &a, int layout, bool ragged, hipStream_t s)
+{
+    switch (layout) {
+    case 0: return launch_tile<IN, OUT, BM, BN, false, false>(a, ragged, s);
+    case DTM_LAYOUT_A_M_CONTIG: return launch_tile<IN, OUT, BM, BN, true, false>(a, ragged, s);
+    case DTM_LAYOUT_B_K_CONTIG: return launch_tile<IN, OUT, BM, BN, false, true>(a, ragged, s);
+    case DTM_LAYOUT_A_M_CONTIG | DTM_LAYOUT_B_K_CONTIG:
+        return launch_tile<IN, OUT, BM, BN, true, true>(a, ragged, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int IN, int OUT>
-hipError_t dispatch_tile(const GemmArgs &a, int bm, int bn, bool ragged, hipStream_t s)
+hipError_t dispatch_tile(const GemmArgs &a, int bm, int bn, int layout, bool ragged,
+                         hipStream_t s)
 {
     if (bm == 256 && bn == 256)
-        return launch_tile<IN, OUT, 256, 256>(a, ragged, s);
+        return dispatch_layout<IN, OUT, 256, 256>(a, layout, ragged, s);
     if (bm == 128 && bn == 128)
-        return launch_tile<IN, OUT, 128, 128>(a, ragged, s);
+        return dispatch_layout<IN, OUT, 128, 128>(a, layout, ragged, s);
     return hipErrorInvalidConfiguration;
 }
 
 template <int IN>
-hipError_t dispatch_out(const GemmArgs &a, int out, int bm, int bn, bool ragged, hipStream_t s)
+hipError_t dispatch_out(const GemmArgs &a, int out, int bm, int bn, int layout, bool ragged,
+                        hipStream_t s)
 {
     switch (out) {
-    case DTM_F32: return dispatch_tile<IN, DTM_F32>(a, bm, bn, ragged, s);
-    case DTM_F16: return dispatch_tile<IN, DTM_F16>(a, bm, bn, ragged, s);
-    case DTM_BF16: return dispatch_tile<IN, DTM_BF16>(a, bm, bn, ragged, s);
+    case DTM_F32: return dispatch_tile<IN, DTM_F32>(a, bm, bn, layout, ragged, s);
+    case DTM_F16: return dispatch_tile<IN, DTM_F16>(a, bm, bn, layout, ragged, s);
+    case DTM_BF16: return dispatch_tile<IN, DTM_BF16>(a, bm, bn, layout, ragged, s);
     }
     return hipErrorInvalidValue;
 }
@@ -286,14 +328,14 @@ bool mfma16_has_config(int bm, int bn, int bk)
     return bk == BK && ((bm == 256 && bn == 256) || (bm == 128 && bn == 128));
 }
 
-hipError_t launch_mfma16(const GemmArgs &a, int in, int out, int bm, int bn, int bk, bool ragged,
-                         hipStream_t s)
+hipError_t launch_mfma16(const GemmArgs &a, int in, int out, int bm, int bn, int bk, int layout,
+                         bool ragged, hipStream_t s)
 {
     if (bk != BK)
         return hipErrorInvalidConfiguration;
     switch (in) {
-    case DTM_F16: return dispatch_out<DTM_F16>(a, out, bm, bn, ragged, s);
-    case DTM_BF16: return dispatch_out<DTM_BF16>(a, out, bm, bn, ragged, s);
+    case DTM_F16: return dispatch_out<DTM_F16>(a, out, bm, bn, layout, ragged, s);
+    case DTM_BF16: return dispatch_out<DTM_BF16>(a, out, bm, bn, layout, ragged, s);
     }
     return hipErrorInvalidValue;
 }

@@ -12,10 +12,12 @@
 //    as 32 x 32 tiles of v_mfma_f32_32x32x2_f32 (one fp32 of A and one of B
 //    per lane per instruction, 16 fp32 results per lane).
 //  * 16-deep K-chunks, two LDS stages, loaded through registers one chunk
-//    ahead.  A rows (K-contiguous) go to LDS as they are; B arrives
-//    N-contiguous and each thread transposes its 2 x 4 block on the way, so
-//    LDS holds both operands k-contiguous, rows padded to 80 bytes (16
-//    consecutive rows hit distinct bank groups).
+//    ahead.  A K-contiguous operand (A row-major, or B given as the
+//    transpose of an N x K array) goes to LDS as it is; an M- or
+//    N-contiguous one is loaded along its contiguous axis and each thread
+//    transposes its 2 x 4 block on the way, so LDS holds both operands
+//    k-contiguous, rows padded to 80 bytes (16 consecutive rows hit distinct
+//    bank groups).
 //  * Which k a lane feeds at each MFMA step is a fixed permutation shared by
 //    A and B: lane half h at step s = 4t + e uses k = 8t + 4h + e, so one
 //    16-byte LDS read serves four steps.  The sum over k is unchanged.
@@ -47,7 +49,78 @@ __device__ __forceinline__ f32x4 load4_masked(const float *p, int64_t valid)
     return v;
 }
 
-template <int OUT, int BM, int BN, bool RAGGED>
+// Global -> registers for the R x BK tile of one operand starting at row
+// (or column) mn0 and k0; X addresses element (mn, k) at mn*s_mn + k*s_k and
+// the operand has ext rows.  Each of the 256 threads holds R/64 16-byte
+// units:
+//  K-contiguous (KC): unit i is chunk t%4 (k 4c .. 4c+3) of row t/4 + 64 i;
+//  otherwise: units 2q and 2q+1 are k-rows kk and kk+1 of block b = t + 256 q,
+//  kk = 2 (b % (BK/2)), at rows 4 (b / (BK/2)) .. +3 (k-pair fastest:
+//  conflict-free LDS writes, and each load instruction reads 8 k-rows x 128
+//  contiguous bytes).
+// RAGGED: slots outside the view are exact zeros and are never read.
+template <int R, bool KC, bool RAGGED>
+__device__ __forceinline__ void load_operand(f32x4 (&r)[R / 64], const float *X, int64_t mn0,
+                                             int64_t s_mn, int64_t s_k, int64_t ext,
+                                             int64_t K, int64_t k0, int t)
+{
+    constexpr int UNITS = R / 64;
+    if constexpr (KC) {
+        const int c = t & 3, row = t >> 2;
+#pragma unroll
+        for (int i = 0; i < UNITS; ++i) {
+            const int64_t mn = mn0 + row + 64 * i;
+            const float *src = X + mn * s_mn + k0 + 4 * c;
+            if constexpr (RAGGED)
+                r[i] = load4_masked(src, mn < ext ? K - (k0 + 4 * c) : 0);
+            else
+                r[i] = *reinterpret_cast<const f32x4 *>(src);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < UNITS / 2; ++q) {
+            const int b = t + 256 * q;
+            const int kk = 2 * (b % (BK / 2)), cc = b / (BK / 2);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int64_t k = k0 + kk + e;
+                const float *src = X + k * s_k + mn0 + 4 * cc;
+                if constexpr (RAGGED)
+                    r[2 * q + e] = load4_masked(src, k < K ? ext - (mn0 + 4 * cc) : 0);
+                else
+                    r[2 * q + e] = *reinterpret_cast<const f32x4 *>(src);
+            }
+        }
+    }
+}
+
+// Registers -> the operand's part of an LDS stage (rows of ROW_F floats, k
+// contiguous); an M/N-contiguous 2 x 4 block is transposed on the way.
+template <int R, bool KC>
+__device__ __forceinline__ void store_operand(const f32x4 (&r)[R / 64], float *s, int t)
+{
+    constexpr int UNITS = R / 64;
+    if constexpr (KC) {
+        const int c = t & 3, row = t >> 2;
+#pragma unroll
+        for (int i = 0; i < UNITS; ++i)
+            *reinterpret_cast<f32x4 *>(s + (row + 64 * i) * ROW_F + 4 * c) = r[i];
+    } else {
+#pragma unroll
+        for (int q = 0; q < UNITS / 2; ++q) {
+            const int b = t + 256 * q;
+            const int kk = 2 * (b % (BK / 2)), cc = b / (BK / 2);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<f32x2 *>(s + (4 * cc + j) * ROW_F + kk) =
+                    f32x2{r[2 * q][j], r[2 * q + 1][j]};
+        }
+    }
+}
+
+// TA: A is M-contiguous (stride_am == 1), else K-contiguous.
+// TB: B is K-contiguous (stride_bk == 1), else N-contiguous.
+template <int OUT, int BM, int BN, bool RAGGED, bool TA, bool TB>
 __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t grid_m,
                                                           int64_t grid_n)
 {
@@ -55,10 +128,7 @@ __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t gr
     constexpr int MI = WM / 32, NI = WN / 32;
     constexpr int A_F = BM * ROW_F;                 // floats of one A stage
     constexpr int STAGE_F = (BM + BN) * ROW_F;
-    constexpr int A_LOADS = BM * (BK / 4) / 256;    // 16-byte A chunks per thread
-    constexpr int B_PAIRS = (BK / 2) * (BN / 4) / 256;  // 2x4 B blocks per thread
-    static_assert(A_LOADS * 256 == BM * (BK / 4), "A tile must split evenly");
-    static_assert(B_PAIRS * 256 == (BK / 2) * (BN / 4), "B tile must split evenly");
+    static_assert(BM % 128 == 0 && BN % 128 == 0, "operand tiles split over 256 threads");
 
     __shared__ __attribute__((aligned(16))) float lds[2 * STAGE_F];
 
@@ -72,55 +142,17 @@ __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t gr
     const float *A = static_cast<const float *>(p.A);
     const float *B = static_cast<const float *>(p.B);
 
-    // A: thread loads chunk t%4 (k 4c..4c+3) of rows t/4 + 64 i.
-    const int a_c = t & 3, a_r = t >> 2;
-    // B: block q of thread t is k-rows 2*(b%8), +1 at columns 4*(b/8) .. +3,
-    // b = t + 256 q (k-pair fastest: conflict-free LDS writes, and each load
-    // instruction reads 8 k-rows x 128 contiguous bytes).
-    f32x4 ra[A_LOADS];
-    f32x4 rb[B_PAIRS][2];
+    f32x4 ra[BM / 64];
+    f32x4 rb[BN / 64];
 
     auto load_tile = [&](int64_t k0) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < A_LOADS; ++i) {
-            const int64_t row = m0 + a_r + 64 * i;
-            const float *src = A + row * p.sam + k0 + 4 * a_c;
-            if constexpr (RAGGED)
-                ra[i] = load4_masked(src, row < p.M ? p.K - (k0 + 4 * a_c) : 0);
-            else
-                ra[i] = *reinterpret_cast<const f32x4 *>(src);
-        }
-#pragma unroll
-        for (int q = 0; q < B_PAIRS; ++q) {
-            const int b = t + 256 * q;
-            const int kk = 2 * (b % (BK / 2)), cc = b / (BK / 2);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int64_t k = k0 + kk + e;
-                const float *src = B + k * p.sbk + n0 + 4 * cc;
-                if constexpr (RAGGED)
-                    rb[q][e] = load4_masked(src, k < p.K ? p.N - (n0 + 4 * cc) : 0);
-                else
-                    rb[q][e] = *reinterpret_cast<const f32x4 *>(src);
-            }
-        }
+        load_operand<BM, !TA, RAGGED>(ra, A, m0, p.sam, p.sak, p.M, p.K, k0, t);
+        load_operand<BN, TB, RAGGED>(rb, B, n0, p.sbn, p.sbk, p.N, p.K, k0, t);
     };
-
     auto store_tile = [&](int stage) __attribute__((always_inline)) {
         float *sa = lds + stage * STAGE_F;
-        float *sb = sa + A_F;
-#pragma unroll
-        for (int i = 0; i < A_LOADS; ++i)
-            *reinterpret_cast<f32x4 *>(sa + (a_r + 64 * i) * ROW_F + 4 * a_c) = ra[i];
-#pragma unroll
-        for (int q = 0; q < B_PAIRS; ++q) {
-            const int b = t + 256 * q;
-            const int kk = 2 * (b % (BK / 2)), cc = b / (BK / 2);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<f32x2 *>(sb + (4 * cc + j) * ROW_F + kk) =
-                    f32x2{rb[q][0][j], rb[q][1][j]};
-        }
+        store_operand<BM, !TA>(ra, sa, t);
+        store_operand<BN, TB>(rb, sa + A_F, t);
     };
 
     floatx16 acc[MI][NI];
@@ -186,7 +218,7 @@ __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t gr
     }
 }
 
-template <int OUT, int BM, int BN>
+template <int OUT, int BM, int BN, bool TA, bool TB>
 hipError_t launch_tile(const GemmArgs &a, bool ragged, hipStream_t s)
 {
     const int64_t gm = cdiv(a.M, BM), gn = cdiv(a.N, BN);
@@ -194,20 +226,25 @@ hipError_t launch_tile(const GemmArgs &a, bool ragged, hipStream_t s)
     if (tiles > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     if (ragged)
-        hipLaunchKernelGGL((gemm_mfma32_kernel<OUT, BM, BN, true>), dim3((unsigned)tiles),
+        hipLaunchKernelGGL((gemm_mfma32_kernel<OUT, BM, BN, true, TA, TB>), dim3((unsigned)tiles),
                            dim3(256), 0, s, a, gm, gn);
     else
-        hipLaunchKernelGGL((gemm_mfma32_kernel<OUT, BM, BN, false>), dim3((unsigned)tiles),
+        hipLaunchKernelGGL((gemm_mfma32_kernel<OUT, BM, BN, false, TA, TB>), dim3((unsigned)tiles),
                            dim3(256), 0, s, a, gm, gn);
     return hipGetLastError();
 }
 
 template <int OUT>
-hipError_t dispatch_tile(const GemmArgs &a, int bm, int bn, bool ragged, hipStream_t s)
+hipError_t dispatch_layout(const GemmArgs &a, int layout, bool ragged, hipStream_t s)
 {
-    if (bm == 128 && bn == 128)
-        return launch_tile<OUT, 128, 128>(a, ragged, s);
-    return hipErrorInvalidConfiguration;
+    switch (layout) {
+    case 0: return launch_tile<OUT, 128, 128, false, false>(a, ragged, s);
+    case DTM_LAYOUT_A_M_CONTIG: return launch_tile<OUT, 128, 128, true, false>(a, ragged, s);
+    case DTM_LAYOUT_B_K_CONTIG: return launch_tile<OUT, 128, 128, false, true>(a, ragged, s);
+    case DTM_LAYOUT_A_M_CONTIG | DTM_LAYOUT_B_K_CONTIG:
+        return launch_tile<OUT, 128, 128, true, true>(a, ragged, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -217,15 +254,15 @@ bool mfma32_has_config(int bm, int bn, int bk)
     return bk == BK && bm == 128 && bn == 128;
 }
 
-hipError_t launch_mfma32(const GemmArgs &a, int out, int bm, int bn, int bk, bool ragged,
-                         hipStream_t s)
+hipError_t launch_mfma32(const GemmArgs &a, int out, int bm, int bn, int bk, int layout,
+                         bool ragged, hipStream_t s)
 {
-    if (bk != BK)
+    if (bk != BK || bm != 128 || bn != 128)
         return hipErrorInvalidConfiguration;
     switch (out) {
-    case DTM_F32: return dispatch_tile<DTM_F32>(a, bm, bn, ragged, s);
-    case DTM_F16: return dispatch_tile<DTM_F16>(a, bm, bn, ragged, s);
-    case DTM_BF16: return dispatch_tile<DTM_BF16>(a, bm, bn, ragged, s);
+    case DTM_F32: return dispatch_layout<DTM_F32>(a, layout, ragged, s);
+    case DTM_F16: return dispatch_layout<DTM_F16>(a, layout, ragged, s);
+    case DTM_BF16: return dispatch_layout<DTM_BF16>(a, layout, ragged, s);
     }
     return hipErrorInvalidValue;
 }

@@ -18,11 +18,11 @@ hipError_t launch_generic(const GemmArgs &a, int in_dtype, int out_dtype, int bm
 hipError_t launch_generic_fp16acc(const GemmArgs &a, int out_dtype, int bm, int bn, int bk,
                                   hipStream_t s);
 
-// Register-staged MFMA kernel for fp16/bf16 inputs with K-contiguous A and
-// N-contiguous B; any M, N, K (edge tiles masked).
+// Register-staged MFMA kernel for fp16/bf16 inputs in every operand layout
+// (`layout`: dtm_layout bits); any M, N, K (edge tiles masked).
 bool mfma16_has_config(int bm, int bn, int bk);
 hipError_t launch_mfma16(const GemmArgs &a, int in_dtype, int out_dtype, int bm, int bn, int bk,
-                         bool ragged, hipStream_t s);
+                         int layout, bool ragged, hipStream_t s);
 
 // Deep-pipelined MFMA kernel (256 x 256 x 32 tiles, global -> LDS DMA) when
 // M and N are multiples of 256 and K of 32, for every operand layout:
@@ -39,11 +39,10 @@ hipError_t launch_mfma16_dma_partials(const GemmArgs &a, int in_dtype, int layou
 hipError_t launch_splitk_reduce(const GemmArgs &a, int out_dtype, int64_t splits, const float *ws,
                                 hipStream_t s);
 
-// MFMA kernel for fp32 inputs with K-contiguous A and N-contiguous B
-// (128 x 128 x 16 tiles).
+// MFMA kernel for fp32 inputs in every operand layout (128 x 128 x 16 tiles).
 bool mfma32_has_config(int bm, int bn, int bk);
-hipError_t launch_mfma32(const GemmArgs &a, int out_dtype, int bm, int bn, int bk, bool ragged,
-                         hipStream_t s);
+hipError_t launch_mfma32(const GemmArgs &a, int out_dtype, int bm, int bn, int bk, int layout,
+                         bool ragged, hipStream_t s);
 
 // Writes zeros to the M x N view of C (the K == 0 product).
 hipError_t launch_zero_fill(const GemmArgs &a, int out_dtype, hipStream_t s);

@@ -23,6 +23,8 @@ GEN = dtm.DTM_KERNEL_GENERIC
 MF16 = dtm.DTM_KERNEL_MFMA_F16
 ACC16 = dtm.DTM_KERNEL_GENERIC_FP16ACC
 T444 = dict(kernel=GEN, block_m=4, block_n=4, block_k=4)
+LAYOUT_BITS = {"NN": 0, "TN": dtm.DTM_LAYOUT_A_M_CONTIG, "NT": dtm.DTM_LAYOUT_B_K_CONTIG,
+               "TT": dtm.DTM_LAYOUT_A_M_CONTIG | dtm.DTM_LAYOUT_B_K_CONTIG}
 
 
 def int_problem(M, N, K, ind, outd, R, seed, la="N", lb="N"):
@@ -323,17 +325,24 @@ def _sweep_shapes(n, seed):
     return shapes
 
 
+@pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])
 @pytest.mark.parametrize("ind", ["f16", "bf16"])
 @pytest.mark.parametrize("tile", [128, 256])
-def test_mfma_ragged_sweep_exact(ind, tile):
-    """Integer-valued inputs on the MFMA kernel at edge sizes around the
-    tile (both tiles), every output dtype: value-exact."""
+def test_mfma_ragged_sweep_exact(ind, tile, layout):
+    """Integer-valued inputs on the register-staged MFMA kernel at edge sizes
+    around the tile (both tiles), every output dtype, in each operand layout
+    (a transposed operand is loaded along its contiguous axis and transposed
+    in registers): value-exact."""
     cfg = dict(kernel=MF16, block_m=tile, block_n=tile, block_k=64)
-    for n, (M, N, K) in enumerate(_sweep_shapes(14, seed=tile + len(ind))):
+    shapes = _sweep_shapes(14 if layout == "NN" else 8, seed=tile + len(ind) + 7 * len(layout))
+    for n, (M, N, K) in enumerate(shapes):
         outd = ["f32", "f16", "bf16"][n % 3]
-        p = padded_int_problem(M, N, K, ind, outd, 8, seed=100 + n, extra=8 * (n % 2))
-        c, untouched = run(p, config=cfg, c_pad=2 if n % 2 else 0)
-        compare(p, c, exact=True, label=f"{ind} {tile} {M}x{N}x{K}->{outd}")
+        p = padded_int_problem(M, N, K, ind, outd, 8, seed=100 + n, extra=8 * (n % 2),
+                               a_layout=layout[0], b_layout=layout[1])
+        plan = {}
+        c, untouched = run(p, config=cfg, c_pad=2 if n % 2 else 0, plan=plan)
+        assert plan["layout"] == LAYOUT_BITS[layout], plan
+        compare(p, c, exact=True, label=f"{layout} {ind} {tile} {M}x{N}x{K}->{outd}")
         assert untouched
 
 
@@ -354,27 +363,20 @@ def test_mfma_pipelined_exact(ind):
         assert untouched
 
 
-LAYOUT_BITS = {"NN": 0, "TN": dtm.DTM_LAYOUT_A_M_CONTIG, "NT": dtm.DTM_LAYOUT_B_K_CONTIG,
-               "TT": dtm.DTM_LAYOUT_A_M_CONTIG | dtm.DTM_LAYOUT_B_K_CONTIG}
-
-
 @pytest.mark.parametrize("layout", ["TN", "NT", "TT"])
 @pytest.mark.parametrize("ind", ["f16", "bf16"])
 def test_pipelined_layouts_exact(ind, layout):
     """Transposed operands on the pipelined kernel (A M-contiguous and/or B
     K-contiguous, staged as stored and read with transposing LDS reads):
     pipeline depths 1, 3, 5 and many chunks, several grids, padded leading
-    dimensions, split-K, forced and selector plans; value-exact on
-    integer-valued inputs."""
+    dimensions, split-K; value-exact on integer-valued inputs."""
     shapes = [(256, 256, 32, 1), (512, 256, 96, 1), (256, 768, 160, 1), (768, 512, 2048, 1),
               (512, 512, 4096, 8), (256, 256, 1024, 4)]
     for n, (M, N, K, S) in enumerate(shapes):
         outd = ["f32", "f16", "bf16"][n % 3]
         p = padded_int_problem(M, N, K, ind, outd, 8 if K <= 256 else 2, seed=600 + n,
                                extra=8 * (n % 2), a_layout=layout[0], b_layout=layout[1])
-        forced = n % 2 == 1 or n == 5
-        cfg = dict(kernel=MF16, block_m=256, block_n=256, block_k=32,
-                   split_k=S) if forced else None
+        cfg = dict(kernel=MF16, block_m=256, block_n=256, block_k=32, split_k=S)
         plan = {}
         c, untouched = run(p, config=cfg, c_pad=4 if n % 2 else 0, plan=plan)
         assert plan["status"] == 0 and plan["block_k"] == 32, plan
@@ -457,31 +459,67 @@ def test_split_k_caller_workspace():
     assert bool((c2 == 7.0).all())
 
 
-def test_mfma_f32_exact_and_random():
-    """fp32 inputs on the fp32 matrix cores: value-exact on integer-valued
-    inputs at ragged and interior sizes (every output dtype), and within the
-    fp32 tolerance on N(0,1) inputs."""
+def _padded_f32_problem(M, N, K, outd, seed, a_layout, b_layout):
+    """Integer-valued fp32 operands, leading dimensions rounded up to 4
+    elements (16 bytes) with NaN padding; layouts as padded_int_problem."""
+    rng = np.random.default_rng(seed)
+    a = rng.integers(-16, 17, size=(M, K))
+    b = rng.integers(-16, 17, size=(K, N))
+
+    def store(x, layout):
+        rows, cols = x.shape
+        if layout == "T":
+            x = x.T
+        ld = -(-x.shape[1] // 4) * 4
+        buf = np.full((x.shape[0], ld), np.nan)
+        buf[:, :x.shape[1]] = x
+        strides = (ld, 1) if layout == "N" else (1, ld)
+        return W.Operand(W.to_bits(buf, "f32").reshape(-1), "f32", rows, cols, 0, *strides)
+
+    return W.Problem(M, N, K, store(a, a_layout), store(b, b_layout), "f32", outd,
+                     name=f"f32{a_layout}{b_layout}{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])
+def test_mfma_f32_exact_and_random(layout):
+    """fp32 inputs on the fp32 matrix cores in each operand layout:
+    value-exact on integer-valued inputs at ragged and interior sizes (every
+    output dtype), and within the fp32 tolerance on N(0,1) inputs."""
     MF32 = dtm.DTM_KERNEL_MFMA_F32
     for n, (M, N, K) in enumerate([(128, 128, 16), (256, 384, 512), (129, 257, 33), (1, 1, 1),
                                    (300, 200, 1000), (127, 129, 17)]):
         outd = ["f32", "f16", "bf16"][n % 3]
-        rng = np.random.default_rng(600 + n)
-        lda, ldb = -(-K // 4) * 4, -(-N // 4) * 4
-        abuf = np.full((M, lda), np.nan)
-        abuf[:, :K] = rng.integers(-16, 17, size=(M, K))
-        bbuf = np.full((K, ldb), np.nan)
-        bbuf[:, :N] = rng.integers(-16, 17, size=(K, N))
-        p = W.Problem(M, N, K, W.Operand(W.to_bits(abuf, "f32").reshape(-1), "f32", M, K, 0, lda, 1),
-                      W.Operand(W.to_bits(bbuf, "f32").reshape(-1), "f32", K, N, 0, ldb, 1),
-                      "f32", outd)
-        c, untouched = run(p, config=dict(kernel=MF32), c_pad=2 if n % 2 else 0)
-        compare(p, c, exact=True, label=f"mfma_f32 {M}x{N}x{K}->{outd}")
+        p = _padded_f32_problem(M, N, K, outd, 600 + n, layout[0], layout[1])
+        plan = {}
+        c, untouched = run(p, config=dict(kernel=MF32), c_pad=2 if n % 2 else 0, plan=plan)
+        assert plan["layout"] == LAYOUT_BITS[layout], plan
+        compare(p, c, exact=True, label=f"mfma_f32 {layout} {M}x{N}x{K}->{outd}")
         assert untouched
-    for n, (M, N, K) in enumerate([(1024, 1024, 1024), (1000, 600, 777)]):
-        p = W.random_problem(M, N, K, "f32", "f32", ("normal", 0.0, 1.0), seed=650 + n)
-        c, _ = run(p)
-        err, tol = compare(p, c, label=f"mfma_f32 random {M}x{N}x{K}")
-        note(f"mfma_f32 {M}x{N}x{K}: max err {err:.3e} tol {tol:.3e}")
+    for n, (M, N, K) in enumerate([(1024, 1024, 1024), (1000, 600, 776)]):
+        p = W.random_problem(M, N, K, "f32", "f32", ("normal", 0.0, 1.0), seed=650 + n,
+                             a_layout=layout[0], b_layout=layout[1])
+        plan = {}
+        c, _ = run(p, plan=plan)
+        assert plan["kernel_name"] == "mfma_f32" and plan["layout"] == LAYOUT_BITS[layout], plan
+        err, tol = compare(p, c, label=f"mfma_f32 {layout} random {M}x{N}x{K}")
+        note(f"mfma_f32 {layout} {M}x{N}x{K}: max err {err:.3e} tol {tol:.3e}")
+
+
+@pytest.mark.parametrize("layout", ["TN", "NT", "TT"])
+@pytest.mark.parametrize("ind", ["f16", "bf16"])
+def test_register_kernel_layouts_random(ind, layout):
+    """Random values, sizes ragged against the tiles (multiples of 8, so
+    every leading dimension is a 16-byte multiple), transposed operands
+    through the selector's plan: the register-staged MFMA kernel within
+    tolerance."""
+    for n, (M, N, K) in enumerate([(296, 200, 152), (1000, 520, 776), (504, 264, 1032)]):
+        p = W.random_problem(M, N, K, ind, "f32", ("normal", 0.0, 1.0), seed=680 + n,
+                             a_layout=layout[0], b_layout=layout[1])
+        plan = {}
+        c, _ = run(p, plan=plan)
+        assert plan["kernel_name"] == "mfma_f16" and plan["layout"] == LAYOUT_BITS[layout], plan
+        err, tol = compare(p, c, label=f"{layout} {ind} {M}x{N}x{K}")
+        note(f"{layout} {ind} {M}x{N}x{K}: max err {err:.3e} tol {tol:.3e}")
 
 
 @pytest.mark.parametrize("layout", ["NN", "NT", "TN", "TT"])

@@ -101,9 +101,11 @@ def test_fast_path_predicate_falls_back_to_generic(kw, why):
 
 
 def test_selector_transposed_layouts():
-    """A M-contiguous and/or B K-contiguous views run on the pipelined MFMA
-    kernel when its tile divides the problem, with the layout bits in the
-    plan; other transposed problems run on the generic kernel."""
+    """A M-contiguous and/or B K-contiguous views run on the MFMA kernels with
+    the layout bits in the plan: the pipelined kernel when its tile divides
+    the problem, the register-staged one for ragged shapes, the fp32 one for
+    fp32; views whose other stride is not a 16-byte multiple run on the
+    generic kernel."""
     LA, LB = dtm.DTM_LAYOUT_A_M_CONTIG, dtm.DTM_LAYOUT_B_K_CONTIG
     big = dict(A=1 << 40, B=2 << 40, C=3 << 40)
     cases = {0: dict(), LA: dict(sam=1, sak=4096), LB: dict(sbk=1, sbn=4096),
@@ -113,30 +115,37 @@ def test_selector_transposed_layouts():
         assert st == 0 and p["kernel_name"] == "mfma_f16" and p["fast_path"] == 1, kw
         assert (p["block_m"], p["block_k"], p["layout"], p["split_k"]) == (256, 32, bits, 1), kw
         assert p["threads"] == 512
-    # few tiles and a transposed operand: still the pipelined kernel (split K)
+        # ragged: the register-staged kernel, same layout bits
+        rk = {0: dict(sam=4104, sbk=4104), LA: dict(sam=1, sak=4104, sbk=4104),
+              LB: dict(sam=4104, sbk=1, sbn=4104), LA | LB: dict(sam=1, sak=4104, sbk=1,
+                                                                 sbn=4104)}[bits]
+        st, p = plan(4095, 4097, 4100, ind=F16, outd=F32, **big, **rk)
+        assert st == 0 and p["kernel_name"] == "mfma_f16" and p["layout"] == bits, kw
+        assert (p["block_m"], p["block_k"], p["ragged"], p["threads"]) == (256, 64, 1, 256), kw
+        # fp32
+        st, p = plan(1000, 1000, 1000, ind=F32, outd=F32, **big,
+                     **{k: (1000 if v == 4096 else v) for k, v in kw.items()})
+        assert st == 0 and p["kernel_name"] == "mfma_f32" and p["layout"] == bits, kw
+    # few tiles and a transposed operand: the pipelined kernel with split K
     st, p = plan(512, 512, 65536, sam=1, sak=512, ind=F16, outd=F32)
     assert st == 0 and p["layout"] == LA and p["split_k"] == 64 and p["block_k"] == 32
+    # a small transposed problem: the register-staged kernel
     st, p = plan(256, 256, 64, sbk=1, sbn=64, ind=F16, outd=F32)
-    assert st == 0 and p["layout"] == LB and p["block_k"] == 32 and p["split_k"] == 1
-    # ragged or misaligned transposed views: the generic kernel
-    for M, N, K, kw in [(4095, 4096, 4096, dict(sam=1, sak=4096)),
-                        (4096, 4096, 4080, dict(sbk=1, sbn=4088)),
-                        (4096, 4096, 4096, dict(sam=1, sak=4100)),
-                        (4096, 4096, 4096, dict(sbk=1, sbn=4092))]:
-        st, p = plan(M, N, K, ind=F16, **big, **kw)
+    assert st == 0 and p["layout"] == LB and p["block_k"] == 64 and p["block_m"] == 128
+    # other stride not a 16-byte multiple: the generic kernel
+    for M, N, K, kw, ind in [(4096, 4096, 4096, dict(sam=1, sak=4100), F16),
+                             (4096, 4096, 4096, dict(sbk=1, sbn=4092), BF16),
+                             (257, 129, 193, dict(sam=1, sak=257), F32),
+                             (1024, 1024, 1024, dict(sbk=1, sbn=1026), F32)]:
+        st, p = plan(M, N, K, ind=ind, **big, **kw)
         assert st == 0 and p["kernel_name"] == "generic" and p["layout"] == 0, (M, N, K, kw)
-    # the register-staged tile reads row-major operands only
-    st, _ = plan(4096, 4096, 4096, sam=1, sak=4096, ind=F16, **big,
-                 config=dict(kernel=dtm.DTM_KERNEL_MFMA_F16, block_m=256, block_n=256,
-                             block_k=64))
-    assert st == dtm.DTM_ERR_CONFIG
-    st, p = plan(4096, 4096, 4096, sam=1, sak=4096, ind=F16, **big,
-                 config=dict(kernel=dtm.DTM_KERNEL_MFMA_F16, block_m=256, block_n=256,
-                             block_k=32, split_k=4))
-    assert st == 0 and p["split_k"] == 4 and p["layout"] == LA
-    # fp32 transposed views: generic
-    st, p = plan(1024, 1024, 1024, sam=1, sak=1024, ind=F32, outd=F32)
-    assert st == 0 and p["kernel_name"] == "generic"
+    # forced tiles accept every layout
+    for cfg in [dict(block_m=256, block_n=256, block_k=64), dict(block_m=128, block_n=128,
+                                                                 block_k=64),
+                dict(block_m=256, block_n=256, block_k=32, split_k=4)]:
+        st, p = plan(4096, 4096, 4096, sam=1, sak=4096, ind=F16, **big,
+                     config=dict(kernel=dtm.DTM_KERNEL_MFMA_F16, **cfg))
+        assert st == 0 and p["layout"] == LA and p["block_k"] == cfg["block_k"], cfg
 
 
 def test_fp32_selector():
