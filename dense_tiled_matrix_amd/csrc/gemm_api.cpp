@@ -139,6 +139,21 @@ int mfma_layout(const Call &c)
 }
 bool is16(const Call &c) { return c.in == DTM_F16 || c.in == DTM_BF16; }
 
+// Byte extent of a view with non-negative strides (one past its last
+// element, from its origin); UINT64_MAX when a stride is negative or the
+// extent overflows.
+uint64_t view_bytes(int64_t rows, int64_t cols, int64_t sr, int64_t sc, int64_t item)
+{
+    if (sr < 0 || sc < 0 || rows <= 0 || cols <= 0)
+        return UINT64_MAX;
+    const unsigned __int128 last = (unsigned __int128)(rows - 1) * (uint64_t)sr +
+                                   (unsigned __int128)(cols - 1) * (uint64_t)sc + 1;
+    const unsigned __int128 bytes = last * (uint64_t)item;
+    return bytes > UINT64_MAX ? UINT64_MAX : (uint64_t)bytes;
+}
+uint64_t a_view_bytes(const Call &c) { return view_bytes(c.M, c.K, c.sam, c.sak, item_size(c.in)); }
+uint64_t b_view_bytes(const Call &c) { return view_bytes(c.K, c.N, c.sbk, c.sbn, item_size(c.in)); }
+
 void fill_grid(const Call &c, dtm_plan &p)
 {
     p.grid_m = cdiv(c.M, p.block_m);
@@ -168,15 +183,33 @@ void pick_generic(const Call &c, dtm_plan &p)
     p.block_k = pick->bk;
 }
 
+// Whether the 256 x 256 x 32 pipelined kernel can run a problem with K in
+// `splits` slices: its interior form (M, N multiples of 256, K of 32 *
+// splits) or its range-checked form.
+bool dma_interior(const Call &c, int layout, int64_t splits)
+{
+    return is16(c) && layout >= 0 && dtm::mfma16_dma_fits(c.M, c.N, c.K, splits);
+}
+bool dma_ranged(const Call &c, int layout, int64_t splits)
+{
+    return is16(c) && layout >= 0 &&
+           dtm::mfma16_dma_ragged_fits(c.M, c.N, c.K, layout, a_view_bytes(c), b_view_bytes(c),
+                                       splits);
+}
+bool dma_any(const Call &c, int layout, int64_t splits)
+{
+    return dma_interior(c, layout, splits) || dma_ranged(c, layout, splits);
+}
+
 // Split-K for problems with too few 256 x 256 tiles to fill the chip and a
 // long K: the largest power-of-two split that keeps tiles x split within 256
-// workgroups, slices of at least 512 (16 pipelined chunks) and K divisible.
-int64_t pick_split(const Call &c, int64_t tiles)
+// workgroups and slices of at least 512 (16 pipelined chunks).
+int64_t pick_split(const Call &c, int layout, int64_t tiles)
 {
     int64_t s = 1;
     if (tiles >= 128)
         return 1;
-    while (tiles * s * 2 <= 256 && c.K % (32 * s * 2) == 0 && c.K / (s * 2) >= 512)
+    while (tiles * s * 2 <= 256 && c.K / (s * 2) >= 512 && dma_any(c, layout, s * 2))
         s *= 2;
     return s;
 }
@@ -199,7 +232,7 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
     }
     // Every MFMA kernel reads all four operand layouts.
     const int layout = mfma_layout(c);
-    const bool dma = is16(c) && layout >= 0 && dtm::mfma16_dma_fits(c.M, c.N, c.K, 1);
+    const bool dma = c.K > 0 && dma_any(c, layout, 1);  // the pipelined kernel, either form
     const bool fast16 = is16(c) && layout >= 0;
     const bool fast32 = c.in == DTM_F32 && layout >= 0;
     p.fast_path = fast16 || fast32 ? 1 : 0;
@@ -232,22 +265,24 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
             p.block_n = force->block_n;
             p.block_k = force->block_k;
         } else {
+            // The pipelined kernel whenever it can run the problem (measured
+            // ahead of the register-staged kernel at every tile count), with
+            // split-K when there are few tiles and K is long; otherwise the
+            // register-staged kernel.
             const int64_t tiles256 = cdiv(c.M, 256) * cdiv(c.N, 256);
-            const bool big = tiles256 >= 256;
-            const int64_t split = dma ? pick_split(c, tiles256) : 1;
-            if (dma && (big || split > 1)) {
+            if (dma) {
                 p.block_m = p.block_n = 256;
                 p.block_k = 32;
-                p.split_k = static_cast<int32_t>(split);
+                p.split_k = static_cast<int32_t>(pick_split(c, layout, tiles256));
             } else {
-                p.block_m = p.block_n = big ? 256 : 128;
+                p.block_m = p.block_n = tiles256 >= 256 ? 256 : 128;
                 p.block_k = 64;
             }
         }
         if (forced_split) {
             // split-K runs on the 256 x 256 x 32 pipelined kernel only
             if (p.block_m != 256 || p.block_n != 256 || p.block_k != 32 ||
-                !dtm::mfma16_dma_fits(c.M, c.N, c.K, forced_split))
+                !dma_any(c, layout, forced_split))
                 return DTM_ERR_CONFIG;
             p.split_k = static_cast<int32_t>(forced_split);
         }
@@ -282,6 +317,8 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
         return DTM_ERR_CONFIG;
     p.kernel = kernel;
     fill_grid(c, p);
+    if (kernel == DTM_KERNEL_MFMA_F16 && p.block_k == 32)  // which form of the pipelined kernel
+        p.ragged = dma_interior(c, layout, p.split_k) ? 0 : 1;
     if (p.split_k > 1)
         p.workspace_bytes = static_cast<uint64_t>(p.split_k) * static_cast<uint64_t>(c.M) *
                             static_cast<uint64_t>(c.N) * sizeof(float);
@@ -384,11 +421,15 @@ int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t w
                 if (!ws)
                     return DTM_ERR_WORKSPACE;
             }
-            e = dtm::launch_mfma16_dma_partials(a, c.in, p.layout, p.split_k,
+            e = dtm::launch_mfma16_dma_partials(a, c.in, p.layout, p.split_k, p.ragged != 0,
+                                                 a_view_bytes(c), b_view_bytes(c),
                                                  static_cast<float *>(ws), s);
             if (e == hipSuccess)
                 e = dtm::launch_splitk_reduce(a, c.out, p.split_k, static_cast<float *>(ws), s);
-        } else if (p.block_k == 32)
+        } else if (p.block_k == 32 && p.ragged)
+            e = dtm::launch_mfma16_dma_ragged(a, c.in, c.out, p.layout, a_view_bytes(c),
+                                              b_view_bytes(c), s);
+        else if (p.block_k == 32)
             e = dtm::launch_mfma16_dma(a, c.in, c.out, p.layout, s);
         else
             e = dtm::launch_mfma16(a, c.in, c.out, p.block_m, p.block_n, p.block_k, p.layout,

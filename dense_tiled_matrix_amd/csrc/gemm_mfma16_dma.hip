@@ -6,10 +6,15 @@
 // Kernel" (section 13.1): one workgroup per 256 x 256 output tile, a K-loop
 // over 32-deep chunks adding each chunk's tile product into an fp32
 // accumulator zeroed once before the loop, and a single conversion to the
-// output dtype at the store (section 13.3).  No edge masking is needed on
-// this path ("Triton from zero, Lesson 4: Block Pointers", homework 3: pay
-// only for the raggedness a problem has); ragged problems use the other MFMA
-// kernel.  Transposed views are read at full speed rather than through a
+// output dtype at the store (section 13.3).  The interior instantiation
+// does no edge masking ("Triton from zero, Lesson 4: Block Pointers",
+// homework 3: pay only for the raggedness a problem has).  The RAGGED one
+// serves M and N of any size and K a multiple of 8 (section 13.2's masks):
+// its loads are range-checked buffer loads, and every 16-byte chunk outside
+// the view (rows past M or N, k past K) is read as exact zeros -- the
+// hardware returns zeros for an offset past the buffer's size, and such
+// lanes are given one -- so nothing outside the views is ever read; the
+// store is masked.  Transposed views are read at full speed rather than through a
 // slow strided path (the stride-swap lesson of "Triton from zero",
 // Lesson 4: a transpose is only a change of strides).
 //
@@ -87,6 +92,33 @@ __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_addr)
                  : "memory", "m0");
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (gfx9 layout) over `bytes` bytes at `base`: loads at
+// byte offsets >= bytes return zeros.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
+    r.y = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));  // stride 0
+    r.z = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+    r.w = 0x00020000;  // 32-bit data format, untyped access
+    return r;
+}
+
+// As dma16, from byte offset `voff` of a buffer resource.
+__device__ __forceinline__ void dma16_buf(const i32x4 &rsrc, uint32_t voff, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+// Offset past every buffer this kernel builds (they are at most 2^31 bytes).
+constexpr uint32_t OUTSIDE = 0x80000000u;
+
 template <int IN>
 __device__ __forceinline__ floatx16 mfma(const u32x4 &a, const u32x4 &b, const floatx16 &c)
 {
@@ -119,6 +151,38 @@ __device__ __forceinline__ const uint16_t *stage_src(const uint16_t *X, int64_t 
         const int c = (lane & 31) ^ swz_krow(k);
         return X + (kb + k) * s_k + mn0 + 8 * c;
     }
+}
+
+// RAGGED form of stage_src: the byte offset of chunk 0 from the operand's
+// origin, and a limit such that chunk kt exists in the view iff
+// kt * BK < klim (klim = 0 when the lane's row or columns lie outside the
+// view).  K is a multiple of 8 and, for an M/N-contiguous operand, so is its
+// extent, so each 16-byte chunk is either wholly inside or wholly outside.
+template <bool KC>
+__device__ __forceinline__ void stage_off(int64_t mn0, int64_t s_mn, int64_t s_k, int64_t ext,
+                                          int64_t K, int64_t kb, int seg, int lane,
+                                          uint32_t &off, int &klim)
+{
+    int64_t mn, kf, e;
+    bool ok;
+    if constexpr (KC) {
+        const int r = 16 * seg + (lane >> 2);
+        const int c = (lane & 3) ^ swz_row(r);
+        mn = mn0 + r;
+        kf = kb + 8 * c;
+        e = mn * s_mn + kf;
+        ok = mn < ext;
+    } else {
+        const int k = 2 * seg + (lane >> 5);
+        const int c = (lane & 31) ^ swz_krow(k);
+        mn = mn0 + 8 * c;
+        kf = kb + k;
+        e = kf * s_k + mn;
+        ok = mn < ext;
+    }
+    ok = ok && kf < K;
+    off = ok ? static_cast<uint32_t>(2 * e) : 0u;
+    klim = ok ? static_cast<int>(K - kf) : 0;
 }
 
 // Byte offset, within an operand's stage, of this lane's first fragment read
@@ -158,16 +222,22 @@ __device__ __forceinline__ void read_tr_half(u32x4 &f, int e, const char *p)
 
 // TA: A is M-contiguous (stride_am == 1); else K-contiguous.
 // TB: B is K-contiguous (stride_bk == 1); else N-contiguous.
-template <int IN, int OUT, int NWAVES, bool TA, bool TB>
+template <int IN, int OUT, int NWAVES, bool TA, bool TB, bool RAGGED>
 __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p, int64_t grid_m,
                                                                       int64_t grid_n,
+                                                                      int64_t splits,
                                                                       int64_t k_split,
-                                                                      int64_t c_split_stride)
+                                                                      int64_t c_split_stride,
+                                                                      uint32_t a_bytes,
+                                                                      uint32_t b_bytes)
 {
     // Split-K: workgroup ids beyond one grid of tiles take further slices of
-    // K, k_split elements each, and write their fp32 partial tile to
-    // C + slice * c_split_stride.  Without a split, k_split = K and the
-    // stride is unused.
+    // K, k_split elements each (a multiple of BK; in the RAGGED form the
+    // last slice may end early at K), and write their fp32 partial tile to
+    // C + slice * c_split_stride.  Without a split, splits = 1, k_split = K
+    // and the stride is unused.
+    // RAGGED: a_bytes and b_bytes are the byte extents of the A and B views
+    // (at most 2^31).
     // Waves form a 2 x (NWAVES/2) grid over the 256 x 256 tile; each owns
     // 128 rows and 256/(NWAVES/2) columns as MT x NT tiles of 32 x 32.
     constexpr bool A_KC = !TA, B_KC = TB;
@@ -190,7 +260,6 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
 
     int64_t pid_m, pid_n;
     const int64_t tiles = grid_m * grid_n;
-    const int64_t splits = p.K / k_split;
     // consecutive remapped ids (one XCD) share a K slice and differ in tile
     const int64_t t_id = xcd_remap(blockIdx.x, tiles * splits);
     const int64_t slice = t_id / tiles;
@@ -202,15 +271,29 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
 
     // ---- load sources of this lane: segments DPO*wave .. +DPO-1 ----------
-    const uint16_t *a_src[DPO], *b_src[DPO];
+    const uint16_t *a_src[DPO], *b_src[DPO];   // interior
+    uint32_t a_goff[DPO], b_goff[DPO];         // RAGGED
+    int a_lim[DPO], b_lim[DPO];
 #pragma unroll
     for (int j = 0; j < DPO; ++j) {
-        a_src[j] = stage_src<A_KC>(A, m0, p.sam, p.sak, kb, DPO * wave + j, lane);
-        b_src[j] = stage_src<B_KC>(B, n0, p.sbn, p.sbk, kb, DPO * wave + j, lane);
+        if constexpr (RAGGED) {
+            stage_off<A_KC>(m0, p.sam, p.sak, p.M, p.K, kb, DPO * wave + j, lane, a_goff[j],
+                            a_lim[j]);
+            stage_off<B_KC>(n0, p.sbn, p.sbk, p.N, p.K, kb, DPO * wave + j, lane, b_goff[j],
+                            b_lim[j]);
+        } else {
+            a_src[j] = stage_src<A_KC>(A, m0, p.sam, p.sak, kb, DPO * wave + j, lane);
+            b_src[j] = stage_src<B_KC>(B, n0, p.sbn, p.sbk, kb, DPO * wave + j, lane);
+        }
     }
     // elements between consecutive chunks
     const int64_t a_chunk = A_KC ? BK : BK * p.sak;
     const int64_t b_chunk = B_KC ? BK : BK * p.sbk;
+    i32x4 a_rsrc, b_rsrc;
+    if constexpr (RAGGED) {
+        a_rsrc = buffer_rsrc(A, a_bytes);
+        b_rsrc = buffer_rsrc(B, b_bytes);
+    }
     const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, lds)));
     const uint32_t a_dst0 = lds_base + (DPO * wave) * 1024;
     const uint32_t b_dst0 = lds_base + A_STAGE_BYTES + (DPO * wave) * 1024;
@@ -221,10 +304,25 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     // before a barrier.
     auto dma_one = [&](int64_t kt, int stage, int d) __attribute__((always_inline)) {
         const uint32_t so = static_cast<uint32_t>(stage) * STAGE_BYTES;
-        if (d < DPO)
-            dma16(a_src[d] + kt * a_chunk, a_dst0 + so + 1024 * d);
-        else
-            dma16(b_src[d - DPO] + kt * b_chunk, b_dst0 + so + 1024 * (d - DPO));
+        if constexpr (RAGGED) {
+            const int kk = static_cast<int>(kt) * BK;
+            const uint32_t kt32 = static_cast<uint32_t>(kt);
+            if (d < DPO) {
+                const uint32_t o = kk < a_lim[d] ? a_goff[d] + kt32 * static_cast<uint32_t>(2 * a_chunk)
+                                                 : OUTSIDE;
+                dma16_buf(a_rsrc, o, a_dst0 + so + 1024 * d);
+            } else {
+                const int e = d - DPO;
+                const uint32_t o = kk < b_lim[e] ? b_goff[e] + kt32 * static_cast<uint32_t>(2 * b_chunk)
+                                                 : OUTSIDE;
+                dma16_buf(b_rsrc, o, b_dst0 + so + 1024 * e);
+            }
+        } else {
+            if (d < DPO)
+                dma16(a_src[d] + kt * a_chunk, a_dst0 + so + 1024 * d);
+            else
+                dma16(b_src[d - DPO] + kt * b_chunk, b_dst0 + so + 1024 * (d - DPO));
+        }
     };
 
     // ---- fragment read offsets (bytes within a stage) ---------------------
@@ -323,7 +421,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     // stage kt % 4.  Chunks kt + 2 .. kt + 4 are in flight meanwhile.  Past
     // the end the loads re-read the last chunk into the freed stage, which
     // keeps the number of loads in flight the same every iteration.
-    const int64_t nk = k_split / BK;
+    const int64_t nk = RAGGED ? cdiv(k_split, BK) : k_split / BK;
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
 #pragma unroll
@@ -365,7 +463,8 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int64_t row = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                store_elem<OUT>(c_out, row * p.scm + col * p.scn, acc[i][j][v]);
+                if (!RAGGED || (row < p.M && col < p.N))
+                    store_elem<OUT>(c_out, row * p.scm + col * p.scn, acc[i][j][v]);
             }
         }
     }
@@ -375,36 +474,66 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
 #define DTM_DMA_WAVES 8
 #endif
 
-template <int IN, int OUT, bool TA, bool TB>
-hipError_t launch(const GemmArgs &a, int64_t splits, hipStream_t s)
+struct DmaLaunch {
+    int64_t splits;
+    bool ragged;
+    uint32_t a_bytes, b_bytes;
+};
+
+// K elements per slice: K / splits for the interior form; for the RAGGED
+// form cdiv(K, splits) rounded up to a whole number of chunks.
+int64_t slice_k(int64_t K, int64_t splits, bool ragged)
 {
-    const int64_t gm = a.M / BM, gn = a.N / BN;
-    hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, DTM_DMA_WAVES, TA, TB>),
-                       dim3((unsigned)(gm * gn * splits)), dim3(64 * DTM_DMA_WAVES), 0, s, a, gm, gn,
-                       a.K / splits, a.M * a.N);
+    return ragged ? cdiv(cdiv(K, splits), BK) * BK : K / splits;
+}
+
+template <int IN, int OUT, bool TA, bool TB>
+hipError_t launch(const GemmArgs &a, const DmaLaunch &l, hipStream_t s)
+{
+    const int64_t gm = cdiv(a.M, BM), gn = cdiv(a.N, BN);
+    const dim3 grid((unsigned)(gm * gn * l.splits)), block(64 * DTM_DMA_WAVES);
+    const int64_t ks = slice_k(a.K, l.splits, l.ragged);
+    if (l.ragged)
+        hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, DTM_DMA_WAVES, TA, TB, true>), grid,
+                           block, 0, s, a, gm, gn, l.splits, ks, a.M * a.N, l.a_bytes,
+                           l.b_bytes);
+    else
+        hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, DTM_DMA_WAVES, TA, TB, false>), grid,
+                           block, 0, s, a, gm, gn, l.splits, ks, a.M * a.N, 0u, 0u);
     return hipGetLastError();
 }
 
 template <int IN, int OUT>
-hipError_t dispatch_layout(const GemmArgs &a, int layout, int64_t splits, hipStream_t s)
+hipError_t dispatch_layout(const GemmArgs &a, int layout, const DmaLaunch &l, hipStream_t s)
 {
     switch (layout) {
-    case 0: return launch<IN, OUT, false, false>(a, splits, s);
-    case DTM_LAYOUT_A_M_CONTIG: return launch<IN, OUT, true, false>(a, splits, s);
-    case DTM_LAYOUT_B_K_CONTIG: return launch<IN, OUT, false, true>(a, splits, s);
+    case 0: return launch<IN, OUT, false, false>(a, l, s);
+    case DTM_LAYOUT_A_M_CONTIG: return launch<IN, OUT, true, false>(a, l, s);
+    case DTM_LAYOUT_B_K_CONTIG: return launch<IN, OUT, false, true>(a, l, s);
     case DTM_LAYOUT_A_M_CONTIG | DTM_LAYOUT_B_K_CONTIG:
-        return launch<IN, OUT, true, true>(a, splits, s);
+        return launch<IN, OUT, true, true>(a, l, s);
     }
     return hipErrorInvalidValue;
 }
 
 template <int IN>
-hipError_t dispatch_out(const GemmArgs &a, int layout, int out, int64_t splits, hipStream_t s)
+hipError_t dispatch_out(const GemmArgs &a, int layout, int out, const DmaLaunch &l,
+                        hipStream_t s)
 {
     switch (out) {
-    case DTM_F32: return dispatch_layout<IN, DTM_F32>(a, layout, splits, s);
-    case DTM_F16: return dispatch_layout<IN, DTM_F16>(a, layout, splits, s);
-    case DTM_BF16: return dispatch_layout<IN, DTM_BF16>(a, layout, splits, s);
+    case DTM_F32: return dispatch_layout<IN, DTM_F32>(a, layout, l, s);
+    case DTM_F16: return dispatch_layout<IN, DTM_F16>(a, layout, l, s);
+    case DTM_BF16: return dispatch_layout<IN, DTM_BF16>(a, layout, l, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t dispatch_in(const GemmArgs &a, int in, int layout, int out, const DmaLaunch &l,
+                       hipStream_t s)
+{
+    switch (in) {
+    case DTM_F16: return dispatch_out<DTM_F16>(a, layout, out, l, s);
+    case DTM_BF16: return dispatch_out<DTM_BF16>(a, layout, out, l, s);
     }
     return hipErrorInvalidValue;
 }
@@ -417,33 +546,52 @@ bool mfma16_dma_fits(int64_t M, int64_t N, int64_t K, int64_t splits)
            K % (BK * splits) == 0 && (M / BM) * (N / BN) * splits <= 0x7fffffffLL;
 }
 
+bool mfma16_dma_ragged_fits(int64_t M, int64_t N, int64_t K, int layout, uint64_t a_bytes,
+                            uint64_t b_bytes, int64_t splits)
+{
+    const bool ta = layout & DTM_LAYOUT_A_M_CONTIG, tb = layout & DTM_LAYOUT_B_K_CONTIG;
+    return M > 0 && N > 0 && K > 0 && K % 8 == 0 && (!ta || M % 8 == 0) &&
+           (tb || N % 8 == 0) && a_bytes <= (1ull << 31) && b_bytes <= (1ull << 31) &&
+           splits >= 1 && (splits == 1 || N % 4 == 0) &&
+           (splits - 1) * slice_k(K, splits, true) < K &&
+           cdiv(M, BM) * cdiv(N, BN) * splits <= 0x7fffffffLL;
+}
+
 int mfma16_dma_threads() { return 64 * DTM_DMA_WAVES; }
 
 hipError_t launch_mfma16_dma(const GemmArgs &a, int in, int out, int layout, hipStream_t s)
 {
     if (!mfma16_dma_fits(a.M, a.N, a.K, 1))
         return hipErrorInvalidConfiguration;
-    switch (in) {
-    case DTM_F16: return dispatch_out<DTM_F16>(a, layout, out, 1, s);
-    case DTM_BF16: return dispatch_out<DTM_BF16>(a, layout, out, 1, s);
-    }
-    return hipErrorInvalidValue;
+    return dispatch_in(a, in, layout, out, DmaLaunch{1, false, 0u, 0u}, s);
+}
+
+hipError_t launch_mfma16_dma_ragged(const GemmArgs &a, int in, int out, int layout,
+                                    uint64_t a_bytes, uint64_t b_bytes, hipStream_t s)
+{
+    if (!mfma16_dma_ragged_fits(a.M, a.N, a.K, layout, a_bytes, b_bytes, 1))
+        return hipErrorInvalidConfiguration;
+    return dispatch_in(a, in, layout, out,
+                       DmaLaunch{1, true, static_cast<uint32_t>(a_bytes),
+                                 static_cast<uint32_t>(b_bytes)},
+                       s);
 }
 
 hipError_t launch_mfma16_dma_partials(const GemmArgs &a, int in, int layout, int64_t splits,
+                                      bool ragged, uint64_t a_bytes, uint64_t b_bytes,
                                       float *ws, hipStream_t s)
 {
-    if (!mfma16_dma_fits(a.M, a.N, a.K, splits))
+    if (ragged ? !mfma16_dma_ragged_fits(a.M, a.N, a.K, layout, a_bytes, b_bytes, splits)
+               : !mfma16_dma_fits(a.M, a.N, a.K, splits))
         return hipErrorInvalidConfiguration;
     GemmArgs w = a;
     w.C = ws;  // dense fp32 [splits][M][N]
     w.scm = a.N;
     w.scn = 1;
-    switch (in) {
-    case DTM_F16: return dispatch_out<DTM_F16>(w, layout, DTM_F32, splits, s);
-    case DTM_BF16: return dispatch_out<DTM_BF16>(w, layout, DTM_F32, splits, s);
-    }
-    return hipErrorInvalidValue;
+    return dispatch_in(w, in, layout, DTM_F32,
+                       DmaLaunch{splits, ragged, static_cast<uint32_t>(a_bytes),
+                                 static_cast<uint32_t>(b_bytes)},
+                       s);
 }
 
 }  // namespace dtm

@@ -31,10 +31,21 @@ bool mfma16_dma_fits(int64_t M, int64_t N, int64_t K, int64_t splits);
 int mfma16_dma_threads();
 hipError_t launch_mfma16_dma(const GemmArgs &a, int in_dtype, int out_dtype, int layout,
                              hipStream_t s);
-// Split-K on the same kernel: K in `splits` equal slices, fp32 partial tiles
-// written densely to ws[splits][M][N] (a.C and its strides are not used).
+// The same kernel on ragged shapes (its range-checked form): any M and N,
+// K % 8 == 0, an M-contiguous A needs M % 8 == 0 and an N-contiguous B
+// N % 8 == 0; both views non-negatively strided and at most 2^31 bytes
+// (a_bytes, b_bytes: the byte extents of the views).  With splits > 1 the
+// slices hold cdiv(K, splits) rounded up to 32 (the last may be shorter,
+// none empty) and N % 4 == 0 (the second pass reads 4 columns at a time).
+bool mfma16_dma_ragged_fits(int64_t M, int64_t N, int64_t K, int layout, uint64_t a_bytes,
+                            uint64_t b_bytes, int64_t splits);
+hipError_t launch_mfma16_dma_ragged(const GemmArgs &a, int in_dtype, int out_dtype, int layout,
+                                    uint64_t a_bytes, uint64_t b_bytes, hipStream_t s);
+// Split-K on the same kernel (either form): fp32 partial tiles written
+// densely to ws[splits][M][N] (a.C and its strides are not used).
 hipError_t launch_mfma16_dma_partials(const GemmArgs &a, int in_dtype, int layout, int64_t splits,
-                                      float *ws, hipStream_t s);
+                                      bool ragged, uint64_t a_bytes, uint64_t b_bytes, float *ws,
+                                      hipStream_t s);
 // C = sum over s of ws[s] in order s = 0, 1, ..., converted once to out_dtype.
 hipError_t launch_splitk_reduce(const GemmArgs &a, int out_dtype, int64_t splits, const float *ws,
                                 hipStream_t s);

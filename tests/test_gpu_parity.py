@@ -401,6 +401,86 @@ def test_pipelined_layouts_random(layout):
         assert untouched
 
 
+def _round8(x):
+    return -(-x // 8) * 8
+
+
+@pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])
+@pytest.mark.parametrize("ind", ["f16", "bf16"])
+def test_pipelined_ragged_exact(ind, layout):
+    """The pipelined kernel's range-checked form at shapes its tile does not
+    divide (M, N of any size -- multiples of 8 along a contiguous M or N --
+    and K a multiple of 8, including K < 32 and K not a multiple of 32):
+    chunks outside the views must arrive as exact zeros, the NaN padding
+    beyond each leading dimension must never be read, and C outside M x N
+    must stay untouched.  Value-exact on integer-valued inputs."""
+    cfg = dict(kernel=MF16, block_m=256, block_n=256, block_k=32)
+    shapes = [(300, 264, 104), (256, 520, 8), (513, 777, 1000), (8, 8, 8), (777, 255, 64),
+              (1000, 1001, 2048), (257, 300, 24)]
+    for n, (M, N, K) in enumerate(shapes):
+        if layout[0] == "T":
+            M = _round8(M)
+        if layout[1] == "N":
+            N = _round8(N)
+        outd = ["f32", "f16", "bf16"][n % 3]
+        p = padded_int_problem(M, N, K, ind, outd, 8 if K <= 256 else 2, seed=800 + n,
+                               extra=8 * (n % 2), a_layout=layout[0], b_layout=layout[1])
+        plan = {}
+        c, untouched = run(p, config=cfg, c_pad=3 if n % 2 else 0, plan=plan)
+        assert plan["status"] == 0 and plan["block_k"] == 32, plan
+        assert plan["ragged"] == (1 if (M % 256 or N % 256 or K % 32) else 0), plan
+        compare(p, c, exact=True, label=f"pipelined ragged {layout} {ind} {M}x{N}x{K}->{outd}")
+        assert untouched
+
+
+@pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])
+def test_pipelined_ragged_random_selector(layout):
+    """A large ragged bf16 problem (4000 x 4008 x 520, N(0,1)) through the
+    selector's plan -- the pipelined kernel's range-checked form -- against
+    the oracle within tolerance."""
+    p = W.random_problem(4000, 4008, 520, "bf16", "bf16", ("normal", 0.0, 1.0), seed=820,
+                         a_layout=layout[0], b_layout=layout[1])
+    plan = {}
+    c, untouched = run(p, plan=plan)
+    assert (plan["block_k"], plan["ragged"], plan["layout"]) == (32, 1, LAYOUT_BITS[layout]), plan
+    err, tol = compare(p, c, label=f"ragged {layout} 4000x4008x520")
+    note(f"ragged {layout} 4000x4008x520: max err {err:.3e} tol {tol:.3e}")
+    assert untouched
+
+
+@pytest.mark.parametrize("layout", ["NN", "TT"])
+def test_split_k_ragged_exact(layout):
+    """Split-K on the range-checked pipelined kernel: ragged M and N, slices
+    of cdiv(K, S) rounded up to 32 with a shorter last slice, K a multiple of
+    8 only; value-exact on integer-valued inputs (every partial sum is an
+    integer, so the slice order cannot change the result)."""
+    cases = [(500, 264, 1000, 4), (300, 256, 4104, 8), (264, 520, 2056, 3), (8, 8, 2048, 64)]
+    for n, (M, N, K, S) in enumerate(cases):
+        if layout[0] == "T":
+            M = _round8(M)
+        outd = ["f32", "bf16", "f16", "f32"][n]
+        cfg = dict(kernel=MF16, block_m=256, block_n=256, block_k=32, split_k=S)
+        p = padded_int_problem(M, N, K, "bf16" if n % 2 else "f16", outd, 2, seed=840 + n,
+                               a_layout=layout[0], b_layout=layout[1])
+        plan = {}
+        c, untouched = run(p, config=cfg, c_pad=3 if n % 2 else 0, plan=plan)
+        assert (plan["split_k"], plan["ragged"]) == (S, 1), plan
+        compare(p, c, exact=True, label=f"split-K ragged {layout} S{S} {M}x{N}x{K}->{outd}")
+        assert untouched
+
+
+def test_ragged_selector_split():
+    """bf16 2000^3 (64 tiles of 256): the selector splits K in two on the
+    range-checked pipelined kernel; N(0,1) values within tolerance."""
+    p = W.random_problem(2000, 2000, 2000, "bf16", "f32", ("normal", 0.0, 1.0), seed=860)
+    plan = {}
+    c, untouched = run(p, plan=plan)
+    assert (plan["block_k"], plan["split_k"], plan["ragged"]) == (32, 2, 1), plan
+    err, tol = compare(p, c, label="ragged split 2000^3")
+    note(f"ragged split 2000^3: max err {err:.3e} tol {tol:.3e}")
+    assert untouched
+
+
 @pytest.mark.parametrize("ind", ["f16", "bf16"])
 def test_split_k_exact(ind):
     """Split-K on the pipelined kernel (forced splits, fp32 partials summed
@@ -509,15 +589,16 @@ def test_mfma_f32_exact_and_random(layout):
 @pytest.mark.parametrize("ind", ["f16", "bf16"])
 def test_register_kernel_layouts_random(ind, layout):
     """Random values, sizes ragged against the tiles (multiples of 8, so
-    every leading dimension is a 16-byte multiple), transposed operands
-    through the selector's plan: the register-staged MFMA kernel within
-    tolerance."""
+    every leading dimension is a 16-byte multiple), transposed operands on
+    the register-staged MFMA kernel (both tiles): within tolerance."""
     for n, (M, N, K) in enumerate([(296, 200, 152), (1000, 520, 776), (504, 264, 1032)]):
         p = W.random_problem(M, N, K, ind, "f32", ("normal", 0.0, 1.0), seed=680 + n,
                              a_layout=layout[0], b_layout=layout[1])
+        tile = 128 if n % 2 else 256
         plan = {}
-        c, _ = run(p, plan=plan)
-        assert plan["kernel_name"] == "mfma_f16" and plan["layout"] == LAYOUT_BITS[layout], plan
+        c, _ = run(p, plan=plan, config=dict(kernel=MF16, block_m=tile, block_n=tile,
+                                             block_k=64))
+        assert plan["block_k"] == 64 and plan["layout"] == LAYOUT_BITS[layout], plan
         err, tol = compare(p, c, label=f"{layout} {ind} {M}x{N}x{K}")
         note(f"{layout} {ind} {M}x{N}x{K}: max err {err:.3e} tol {tol:.3e}")
 

@@ -67,7 +67,13 @@ def test_selector_measured_workloads():
     st, p = plan(8192, 8192, 8192, ind=BF16, outd=BF16)
     assert st == 0 and p["kernel_name"] == "mfma_f16"
     assert (p["grid_m"], p["grid_n"], p["k_iters"]) == (32, 32, 256)
-    # ragged edges keep the 64-deep register-staged kernel
+    # large ragged shapes with K % 8 == 0: the pipelined kernel's
+    # range-checked form
+    st, p = plan(4000, 4000, 4000, ind=BF16, outd=BF16)
+    assert st == 0 and (p["block_m"], p["block_k"], p["ragged"], p["threads"]) == \
+        (256, 32, 1, 512)
+    assert (p["grid_m"], p["grid_n"], p["k_iters"]) == (16, 16, 125)
+    # K % 8 != 0: the 64-deep register-staged kernel
     st, p = plan(4096, 4096, 4100, sam=4104, ind=F16, outd=F32)
     assert st == 0 and (p["block_m"], p["block_k"], p["ragged"]) == (256, 64, 1)
     # long-K skinny: 4 tiles of 256 x 256 -> split K into 64 slices of 1024
@@ -129,8 +135,11 @@ def test_selector_transposed_layouts():
     # few tiles and a transposed operand: the pipelined kernel with split K
     st, p = plan(512, 512, 65536, sam=1, sak=512, ind=F16, outd=F32)
     assert st == 0 and p["layout"] == LA and p["split_k"] == 64 and p["block_k"] == 32
-    # a small transposed problem: the register-staged kernel
+    # a small transposed problem: the pipelined kernel as well ...
     st, p = plan(256, 256, 64, sbk=1, sbn=64, ind=F16, outd=F32)
+    assert st == 0 and p["layout"] == LB and p["block_k"] == 32 and p["ragged"] == 0
+    # ... unless K % 8 != 0: then the register-staged kernel
+    st, p = plan(256, 256, 60, sam=64, sbk=1, sbn=64, ind=F16, outd=F32)
     assert st == 0 and p["layout"] == LB and p["block_k"] == 64 and p["block_m"] == 128
     # other stride not a 16-byte multiple: the generic kernel
     for M, N, K, kw, ind in [(4096, 4096, 4096, dict(sam=1, sak=4100), F16),
@@ -251,17 +260,37 @@ def test_forced_configs():
     assert st == 0 and p["grid_m"] == 1 and p["ragged"] == 1
     assert plan(64, 64, 64, config=dict(kernel=mf, block_m=64, block_n=64, block_k=64))[0] == \
         dtm.DTM_ERR_CONFIG
-    # the 32-deep pipelined tile needs M, N multiples of 256 and K of 32
+    # the 32-deep pipelined tile: interior when M, N are multiples of 256
+    # and K of 32; its range-checked form needs K % 8 == 0 and, for an
+    # N-contiguous B, N % 8 == 0 (an M-contiguous A: M % 8 == 0)
     dma = dict(kernel=mf, block_m=256, block_n=256, block_k=32)
-    assert plan(512, 256, 96, config=dma)[0] == 0
+    st, p = plan(512, 256, 96, config=dma)
+    assert st == 0 and p["ragged"] == 0
+    st, p = plan(500, 256, 96, config=dma)
+    assert st == 0 and p["ragged"] == 1 and (p["grid_m"], p["k_iters"]) == (2, 3)
+    st, p = plan(512, 256, 104, sam=104, config=dma)
+    assert st == 0 and p["ragged"] == 1 and p["k_iters"] == 4
     assert plan(512, 256, 100, sam=104, config=dma)[0] == dtm.DTM_ERR_CONFIG
-    assert plan(500, 256, 96, config=dma)[0] == dtm.DTM_ERR_CONFIG
+    assert plan(500, 250, 96, sbk=256, config=dma)[0] == dtm.DTM_ERR_CONFIG
+    assert plan(500, 250, 96, sbk=1, sbn=96, config=dma)[0] == 0  # B K-contiguous
+    assert plan(500, 256, 96, sam=1, sak=504, config=dma)[0] == dtm.DTM_ERR_CONFIG
+    assert plan(504, 256, 96, sam=1, sak=504, config=dma)[0] == 0
+    # negative strides or views over 2^31 bytes: not on the range-checked form
+    assert plan(500, 256, 96, sam=-96, A=PA + 600 * 96 * 2, config=dma)[0] == \
+        dtm.DTM_ERR_CONFIG
+    assert plan(40000, 256, 32768, A=1 << 40, B=2 << 40, C=3 << 40, config=dma)[0] == \
+        dtm.DTM_ERR_CONFIG
     assert plan(64, 64, 64, config=dict(kernel=99))[0] == dtm.DTM_ERR_CONFIG
     # forced split-K: only on the pipelined tile, K divisible by 32 * split
     st, p = plan(512, 256, 1024, config=dict(dma, split_k=4))
     assert st == 0 and p["split_k"] == 4 and p["k_iters"] == 8
     assert p["workspace_bytes"] == 4 * 512 * 256 * 4
-    assert plan(512, 256, 1000, sam=1000, config=dict(dma, split_k=4))[0] == dtm.DTM_ERR_CONFIG
+    # uneven slices (256, 256, 256, 232) on the range-checked form
+    st, p = plan(512, 256, 1000, sam=1000, config=dict(dma, split_k=4))
+    assert st == 0 and p["ragged"] == 1 and p["k_iters"] == 8
+    assert plan(512, 256, 1004, sam=1008, config=dict(dma, split_k=4))[0] == dtm.DTM_ERR_CONFIG
+    # a split that would leave a slice empty
+    assert plan(512, 256, 96, config=dict(dma, split_k=4))[0] == dtm.DTM_ERR_CONFIG
     assert plan(512, 256, 1024, config=dict(kernel=mf, block_m=128, block_n=128, block_k=64,
                                             split_k=2))[0] == dtm.DTM_ERR_CONFIG
     assert plan(512, 256, 1024, ind=F32, config=dict(kernel=gen, split_k=2))[0] == \
