@@ -1,4 +1,5 @@
-"""CPU oracle for the blocked GEMM C = A·B (ctypes wrapper over liboracle.so).
+"""CPU oracle for the blocked GEMM C = A·B and the row softmax (ctypes
+wrapper over liboracle.so).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code
@@ -8,7 +9,8 @@ What it computes follows "Chapter 13: The Blocked Matmul Kernel" (sections
 13.1-13.3): ``C[i][j] = sum_k A[i][k]*B[k][j]`` with k ascending and an fp64
 running sum over the exact decoded inputs, then one round-to-nearest-even
 conversion to the output dtype; plus section 13.3's fp16-accumulator variant
-as an emulation.  See ``oracle_gemm.c`` for the arithmetic.
+as an emulation.  The row softmax follows "Triton from zero, Lesson 4: Block
+Pointers", homework 4, in fp64.  See ``oracle_gemm.c`` for the arithmetic.
 """
 from __future__ import annotations
 
@@ -36,6 +38,8 @@ def load_library(path: str):
     L.oracle_gemm_fp16acc.argtypes = [i64, i64, i64, vp, i64, i64, vp, i64, i64, i32, i64,
                                       vp]
     L.oracle_gemm_fp16acc.restype = i32
+    L.oracle_softmax.argtypes = [i64, i64, vp, i64, i64, i32, i32, vp, vp, i32]
+    L.oracle_softmax.restype = i32
     L.oracle_decode_array.argtypes = [vp, i64, i32, vp]
     L.oracle_decode_array.restype = i32
     L.oracle_encode_array.argtypes = [vp, i64, i32, vp]
@@ -131,3 +135,36 @@ def tolerance(in_dtype: str, K: int, max_abs_a: float, max_abs_b: float) -> floa
     if in_dtype == "f32":
         return 1e-5 * K * max_abs_a * max_abs_b
     return 4e-3 * float(np.sqrt(K)) * max_abs_a * max_abs_b
+
+
+def softmax(M, N, x_bits, x_offset, stride_xm, stride_xn, in_dtype, out_dtype, threads: int = 0):
+    """Row softmax of the M x N view; returns ``(Y64, Yout_bits)``, both dense
+    row-major M x N (fp64 values and their rounding to out_dtype)."""
+    x = np.ascontiguousarray(x_bits, dtype=_BITS[in_dtype]).reshape(-1)
+    y64 = np.zeros((M, N), dtype=np.float64)
+    yout = np.zeros((M, N), dtype=_BITS[out_dtype])
+    rc = lib().oracle_softmax(M, N, _ptr(x, x_offset), stride_xm, stride_xn, _CODE[in_dtype],
+                              _CODE[out_dtype], y64.ctypes.data, _ptr(yout, 0), threads)
+    if rc != 0:
+        raise RuntimeError(f"oracle_softmax failed with {rc}")
+    return y64, yout
+
+
+def softmax_problem(p, out_dtype=None, threads: int = 0):
+    """``softmax`` on a ``workloads.SoftmaxProblem``."""
+    X = p.X
+    return softmax(p.M, p.N, X.bits, X.offset, X.stride_r, X.stride_c, p.in_dtype,
+                   out_dtype or p.out_dtype, threads)
+
+
+def softmax_tolerance(x64_row_minus_max: np.ndarray, y64: np.ndarray, terms: int) -> np.ndarray:
+    """Per-element bound for a row softmax computed in fp32 from the same
+    inputs: the shifted argument d = x - max is rounded once (relative
+    2^-24, i.e. absolute |d| 2^-24 in the exponent), exp adds a few ulps,
+    the sum of the row's exponentials adds at most ``terms`` roundings
+    (the longest chain of fp32 additions any one partial sum passes through)
+    and the division one more; values far below 1 can also lose their last
+    bits to fp32 gradual underflow (2^-149 absolute before the division by a
+    sum >= 1).  Returns |Y - Y64| bounds, elementwise."""
+    rel = (np.abs(np.nan_to_num(x64_row_minus_max, nan=0.0, neginf=0.0)) + terms + 8) * 2.0 ** -24
+    return np.abs(y64) * rel + 2.0 ** -140

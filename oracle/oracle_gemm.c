@@ -1,5 +1,6 @@
 /*
- * oracle_gemm.c -- CPU oracle for the blocked GEMM C = A.B
+ * oracle_gemm.c -- CPU oracle for the blocked GEMM C = A.B and for the row
+ * softmax (the second workload, at the end of this file)
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
  * benchmark's CPU-baseline leg load this library.  It shares no code, header,
@@ -281,6 +282,71 @@ int oracle_gemm_fp16acc(int64_t M, int64_t N, int64_t K,
                 acc = dec_f16((uint16_t)rne(acc + p16, 10, 5));
             }
             Cout16[i * N + j] = (uint16_t)rne(acc, 10, 5);
+        }
+    }
+    return 0;
+}
+
+/* ---- row softmax -------------------------------------------------------- */
+
+/*
+ * oracle_softmax -- the row softmax of "Triton from zero, Lesson 4: Block
+ * Pointers", homework 4: for every row i of the M x N view X,
+ *
+ *     m_i    = max over j < N of X[i][j]
+ *     Y[i][j] = exp(X[i][j] - m_i) / sum over j' < N of exp(X[i][j'] - m_i).
+ *
+ * The homework's kernel loads a row tile, replaces the columns at or beyond
+ * N by -inf (so they can neither win the max nor add to the sum: exp(-inf)
+ * is 0), takes the max, exponentiates the shifted values, sums them and
+ * divides.  Here there is no tile, so no padding: the same three steps over
+ * exactly the N columns, in fp64 over the exact decoded inputs (j
+ * ascending for the sum), then one round-to-nearest-even conversion to the
+ * output dtype.
+ *
+ * Special values follow the formula's own IEEE arithmetic: a NaN element
+ * is ignored by the max but makes the sum, hence the whole row, NaN; a +inf
+ * element makes the row NaN (inf - inf); a row whose elements are all -inf
+ * has m = -inf and is NaN (-inf - -inf); -inf elements of any other row
+ * give exact zeros.
+ *
+ * X is read through element strides (stride_xm, stride_xn), which may be
+ * zero or negative.  Y64 (fp64) and Yout (out_dtype bits) are dense
+ * row-major M x N arrays.
+ */
+int oracle_softmax(int64_t M, int64_t N, const void *X, int64_t sxm, int64_t sxn,
+                   int in_dtype, int out_dtype, double *Y64, void *Yout, int nthreads)
+{
+    if (M < 0 || N < 0 || !valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+        return -1;
+    if (M == 0 || N == 0)
+        return 0;
+    if (!X || !Y64 || !Yout)
+        return -1;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#else
+    (void)nthreads;
+#endif
+    for (int64_t i = 0; i < M; ++i) {
+        double *y = Y64 + i * N;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < N; ++j) {
+            const double x = dec(X, i * sxm + j * sxn, in_dtype);
+            y[j] = x;
+            if (x > m) /* false for NaN: the max ignores it */
+                m = x;
+        }
+        double sum = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            y[j] = exp(y[j] - m);
+            sum += y[j];
+        }
+        for (int64_t j = 0; j < N; ++j) {
+            y[j] = y[j] / sum;
+            store(Yout, i * N + j, out_dtype, y[j]);
         }
     }
     return 0;

@@ -11,6 +11,7 @@ import pytest
 
 import oracle
 import test_oracle_pins as P
+import test_oracle_softmax_pins as S
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle_gemm.c")
 
@@ -42,6 +43,16 @@ MUTANTS = [
      "acc = acc + p16;"),
     ("fp16acc: chunk boundary off", "const int64_t k1 = k0 + BK < K ? k0 + BK : K;",
      "const int64_t k1 = k0 + BK + 1 < K ? k0 + BK + 1 : K;"),
+    ("softmax: max not subtracted", "y[j] = exp(y[j] - m);", "y[j] = exp(y[j]);"),
+    ("softmax: min instead of max", "if (x > m) /* false for NaN: the max ignores it */",
+     "if (m == -INFINITY || x < m)"),
+    ("softmax: last column left out of the sum", "sum += y[j];",
+     "if (j + 1 < N) sum += y[j];"),
+    ("softmax: strides swapped", "const double x = dec(X, i * sxm + j * sxn, in_dtype);",
+     "const double x = dec(X, i * sxn + j * sxm, in_dtype);"),
+    ("softmax: divides by the max term", "y[j] = y[j] / sum;", "y[j] = y[j] / exp(0.0);"),
+    ("softmax: output row index", "store(Yout, i * N + j, out_dtype, y[j]);",
+     "store(Yout, j * M + i < M * N ? j * M + i : 0, out_dtype, y[j]);"),
 ]
 
 PINS = [
@@ -60,6 +71,12 @@ PINS = [
     P.test_decode_bf16_exhaustive,
     P.test_encode_f16_and_f32_vs_numpy,
     P.test_encode_bf16,
+    S.test_closed_forms,
+    S.test_max_is_subtracted,
+    S.test_special_values,
+    S.test_rows_sum_to_one_and_match_scipy,
+    S.test_strided_views,
+    lambda: S.test_output_rounding_matches_numpy("f16"),
 ]
 
 

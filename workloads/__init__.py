@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the blocked GEMM C = A·B.
+"""Seeded synthetic inputs for the blocked GEMM C = A·B and the row softmax.
 
 This module is shared by the HIP path's tests and bench and by the CPU oracle's
 tests.  It holds no part of the GEMM itself: it only draws numbers, rounds them
@@ -198,3 +198,56 @@ def seed0_fp16_problem() -> Problem:
     A = dense(a.view(torch.int16).numpy().view(np.uint16).copy(), "f16")
     B = dense(b.view(torch.int16).numpy().view(np.uint16).copy(), "f16")
     return Problem(4, 4, 1024, A, B, "f16", "f16", name="seed0_4x1024x4")
+
+
+# ----------------------------------------------------------------- row softmax
+
+
+@dataclass
+class SoftmaxProblem:
+    M: int
+    N: int
+    X: Operand
+    in_dtype: str
+    out_dtype: str
+    name: str = ""
+    meta: dict = field(default_factory=dict)
+
+
+def softmax_problem(M, N, in_dtype, out_dtype, dist, seed, layout="N", masked=0.0,
+                    name="") -> SoftmaxProblem:
+    """Rows drawn from ``dist``; a fraction ``masked`` of the entries (chosen
+    with seed+1) set to -inf, as an attention-style mask would.  Layout "N"
+    is a row-major view, "T" a view of a contiguous transpose."""
+    x64 = draw((M, N), dist, seed)
+    if masked > 0.0:
+        rng = np.random.default_rng(seed + 1)
+        x64[rng.random((M, N)) < masked] = -np.inf
+    if layout == "N":
+        X = dense(to_bits(x64, in_dtype).reshape(M, N), in_dtype)
+    else:
+        X = transposed_view(to_bits(x64.T.copy(), in_dtype).reshape(N, M), in_dtype)
+    return SoftmaxProblem(M, N, X, in_dtype, out_dtype, name=name)
+
+
+# Softmax workloads (synthetic; the pages give no sizes).  ``index`` is the
+# seed base, after the GEMM workloads'.
+SOFTMAX_WORKLOADS = {
+    "softmax_f32_4096x4096": dict(index=10, M=4096, N=4096, in_dtype="f32", out_dtype="f32",
+                                  dist=("normal", 0.0, 3.0), masked=0.0),
+    "softmax_bf16_8192x8192_masked": dict(index=11, M=8192, N=8192, in_dtype="bf16",
+                                          out_dtype="bf16", dist=("normal", 0.0, 3.0),
+                                          masked=0.1),
+    "softmax_f16_32768x1024": dict(index=12, M=32768, N=1024, in_dtype="f16", out_dtype="f16",
+                                   dist=("normal", 0.0, 3.0), masked=0.0),
+    "softmax_f32_256x65536": dict(index=13, M=256, N=65536, in_dtype="f32", out_dtype="f32",
+                                  dist=("normal", 0.0, 3.0), masked=0.0),
+}
+
+
+def softmax_workload(name: str) -> SoftmaxProblem:
+    w = SOFTMAX_WORKLOADS[name]
+    p = softmax_problem(w["M"], w["N"], w["in_dtype"], w["out_dtype"], w["dist"],
+                        1000 * w["index"], masked=w["masked"], name=name)
+    p.meta = dict(w)
+    return p
