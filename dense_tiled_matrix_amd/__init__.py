@@ -1,7 +1,8 @@
-"""Python binding of libdtm_gemm.so, the MI355X (gfx950) blocked GEMM C = A·B.
+"""Python binding of libdtm_gemm.so, the MI355X (gfx950) blocked GEMM C = A·B
+and the row softmax.
 
-The C ABI is declared in ``include/dtm_gemm.h``; the functions here have the
-same names and only marshal arguments (sizes, device pointers, element
+The C ABI is declared in ``include/dtm_gemm.h`` and ``include/dtm_softmax.h``;
+the functions here have the same names and only marshal arguments (sizes, device pointers, element
 strides, dtype codes and the current HIP stream) into it.  Every step of the
 computation runs in the library's HIP kernels.  PyTorch provides device memory
 and streams.
@@ -17,7 +18,9 @@ import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdtm_gemm.so")
-HEADER = os.path.join(os.path.dirname(HERE), "include", "dtm_gemm.h")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+HEADER = os.path.join(INCLUDE, "dtm_gemm.h")
+HEADERS = [HEADER, os.path.join(INCLUDE, "dtm_softmax.h")]
 
 # dtm_dtype
 DTM_F32, DTM_F16, DTM_BF16 = 0, 1, 2
@@ -62,6 +65,25 @@ class Plan(ctypes.Structure):
         return d
 
 
+# dtm_softmax_form
+SOFTMAX_FORMS = {0: "none", 1: "wave", 2: "block", 3: "online"}
+
+
+class SoftmaxPlan(ctypes.Structure):
+    """dtm_softmax_plan."""
+
+    _fields_ = [("form", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("rows_per_block", ctypes.c_int32), ("chunks", ctypes.c_int32),
+                ("chunk_elems", ctypes.c_int32), ("vectorized", ctypes.c_int32),
+                ("grid", ctypes.c_int64), ("passes", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+    def as_dict(self):
+        d = {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+        d["form_name"] = SOFTMAX_FORMS.get(self.form, "unknown")
+        return d
+
+
 class GemmError(RuntimeError):
     def __init__(self, status: int, where: str = "gemm"):
         self.status = status
@@ -91,15 +113,23 @@ def lib():
         L.gemm_status_string.restype = ctypes.c_char_p
         L.gemm_kernel_name.argtypes = [i32]
         L.gemm_kernel_name.restype = ctypes.c_char_p
+        sops = [i64, i64, vp, i64, i64, vp, i64, i64, i32, i32]
+        L.row_softmax.argtypes = sops + [vp]
+        L.row_softmax.restype = i32
+        L.row_softmax_plan.argtypes = sops + [ctypes.POINTER(SoftmaxPlan)]
+        L.row_softmax_plan.restype = i32
         _lib = L
     return _lib
 
 
 def header_functions():
-    """Names of the functions include/dtm_gemm.h declares."""
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+    """Names of the functions the headers under include/ declare."""
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def gemm_status_string(status: int) -> str:
@@ -239,3 +269,64 @@ def gemm_ex_raw(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C, st
     return lib().gemm_ex(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C, stride_cm,
                          stride_cn, in_dtype, out_dtype, _config(config), workspace or None,
                          workspace_bytes, s)
+
+
+# ---------------------------------------------------------------- row softmax
+
+
+def _softmax_operands(x, out, out_dtype):
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (rows x columns)")
+    if out is None:
+        import torch
+
+        odt = _torch_dtype(out_dtype) or x.dtype
+        out = torch.empty(x.shape, dtype=odt, device=x.device)
+    elif tuple(out.shape) != tuple(x.shape):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(x.shape)}")
+    return out
+
+
+def _softmax_args(x, out):
+    M, N = x.shape
+    return (M, N, x.data_ptr(), x.stride(0), x.stride(1), out.data_ptr(), out.stride(0),
+            out.stride(1), _dtype_code(x.dtype), _dtype_code(out.dtype))
+
+
+def row_softmax(x, out=None, out_dtype=None, stream=None):
+    """Softmax over the columns of each row of the 2-D device tensor ``x``
+    through the C ``row_softmax``; returns ``out`` (allocated with
+    ``out_dtype``, default x's dtype, when not given; it may be ``x`` itself
+    for an in-place call)."""
+    out = _softmax_operands(x, out, out_dtype)
+    st = lib().row_softmax(*_softmax_args(x, out), _stream(x.device, stream))
+    if st != DTM_OK:
+        raise GemmError(st, "row_softmax")
+    return out
+
+
+def row_softmax_plan(x, out=None, out_dtype=None) -> dict:
+    """The plan ``row_softmax`` would launch (host only)."""
+    out = _softmax_operands(x, out, out_dtype)
+    p = SoftmaxPlan()
+    st = lib().row_softmax_plan(*_softmax_args(x, out), ctypes.byref(p))
+    if st != DTM_OK:
+        raise GemmError(st, "row_softmax_plan")
+    return p.as_dict()
+
+
+def row_softmax_raw(M, N, X, stride_xm, stride_xn, Y, stride_ym, stride_yn, in_dtype,
+                    out_dtype, stream=None):
+    """``row_softmax`` on raw integers (device pointers); returns the status."""
+    s = ctypes.c_void_p(0 if stream is None else int(stream))
+    return lib().row_softmax(M, N, X, stride_xm, stride_xn, Y, stride_ym, stride_yn, in_dtype,
+                             out_dtype, s)
+
+
+def row_softmax_plan_raw(M, N, X, stride_xm, stride_xn, Y, stride_ym, stride_yn, in_dtype,
+                         out_dtype):
+    """``row_softmax_plan`` on raw integers; returns ``(status, plan_dict)``."""
+    p = SoftmaxPlan()
+    st = lib().row_softmax_plan(M, N, X, stride_xm, stride_xn, Y, stride_ym, stride_yn,
+                                in_dtype, out_dtype, ctypes.byref(p))
+    return st, p.as_dict()

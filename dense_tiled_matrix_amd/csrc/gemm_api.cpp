@@ -15,12 +15,49 @@
 #include <utility>
 
 #include "dtm_gemm.h"
+#include "host_util.h"
 #include "launch.h"
+
+namespace dtm {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+}  // namespace
+
+int check_device()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return DTM_ERR_DEVICE;
+    if (dev < kMaxDevices) {
+        const int known = g_device_ok[dev].load(std::memory_order_acquire);
+        if (known == 1)
+            return DTM_OK;
+        if (known == 2)
+            return DTM_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return DTM_ERR_DEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices)
+        g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_release);
+    return ok ? DTM_OK : DTM_ERR_DEVICE;
+}
+
+}  // namespace dtm
 
 namespace {
 
+using dtm::c_strides_ok;
 using dtm::cdiv;
+using dtm::check_device;
 using dtm::GemmArgs;
+using dtm::item_size;
+using dtm::valid_dtype;
+using dtm::view_range;
 
 struct Call {
     int64_t M, N, K;
@@ -32,55 +69,6 @@ struct Call {
     int64_t scm, scn;
     int in, out;
 };
-
-bool valid_dtype(int d) { return d == DTM_F32 || d == DTM_F16 || d == DTM_BF16; }
-int64_t item_size(int d) { return d == DTM_F32 ? 4 : 2; }
-
-// Byte range [lo, hi) spanned by a rows x cols view; false on overflow.
-bool view_range(const void *base, int64_t rows, int64_t cols, int64_t sr, int64_t sc,
-                int64_t item, uintptr_t &lo, uintptr_t &hi)
-{
-    int64_t er, ec;
-    if (__builtin_mul_overflow(rows - 1, sr, &er) || __builtin_mul_overflow(cols - 1, sc, &ec))
-        return false;
-    const int64_t mn = (er < 0 ? er : 0) + (ec < 0 ? ec : 0);
-    const int64_t mx = (er > 0 ? er : 0) + (ec > 0 ? ec : 0);
-    int64_t blo, bhi;
-    if (__builtin_mul_overflow(mn, item, &blo) || __builtin_mul_overflow(mx + 1, item, &bhi))
-        return false;
-    const uintptr_t b = reinterpret_cast<uintptr_t>(base);
-    lo = b + static_cast<uintptr_t>(blo);  // wraps correctly for negative offsets
-    hi = b + static_cast<uintptr_t>(bhi);
-    if (blo < 0 && static_cast<uintptr_t>(-blo) > b)
-        return false;
-    if (hi < b)
-        return false;
-    return true;
-}
-
-// Distinct (i, j) of an M x N view with these strides never share an element.
-bool c_strides_ok(int64_t M, int64_t N, int64_t scm, int64_t scn)
-{
-    if (scm < 0 || scn < 0)
-        return false;
-    if (M > 1 && scm == 0)
-        return false;
-    if (N > 1 && scn == 0)
-        return false;
-    if (M <= 1 || N <= 1)
-        return true;
-    // the smaller stride's axis must fit entirely inside one step of the larger
-    int64_t s_small = scm, n_small = M, s_big = scn;
-    if (scn < scm) {
-        s_small = scn;
-        n_small = N;
-        s_big = scm;
-    }
-    int64_t span;
-    if (__builtin_mul_overflow(s_small, n_small, &span))
-        return false;
-    return s_big >= span;
-}
 
 int validate(const Call &c)
 {
@@ -329,30 +317,6 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
 }
 
 // ---- device check ---------------------------------------------------------
-
-constexpr int kMaxDevices = 64;
-std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
-
-int check_device()
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
-        return DTM_ERR_DEVICE;
-    if (dev < kMaxDevices) {
-        const int known = g_device_ok[dev].load(std::memory_order_acquire);
-        if (known == 1)
-            return DTM_OK;
-        if (known == 2)
-            return DTM_ERR_DEVICE;
-    }
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
-        return DTM_ERR_DEVICE;
-    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-    if (dev < kMaxDevices)
-        g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_release);
-    return ok ? DTM_OK : DTM_ERR_DEVICE;
-}
 
 // ---- library-owned split-K workspace ---------------------------------------
 // One buffer per (device, stream), grown on demand.  Growing first waits for

@@ -1,0 +1,65 @@
+// host_util.h -- host-side argument checks shared by the C-ABI entry points
+// (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dtm_gemm.h"
+
+namespace dtm {
+
+inline bool valid_dtype(int d) { return d == DTM_F32 || d == DTM_F16 || d == DTM_BF16; }
+inline int64_t item_size(int d) { return d == DTM_F32 ? 4 : 2; }
+
+// Byte range [lo, hi) spanned by a rows x cols view; false on overflow.
+inline bool view_range(const void *base, int64_t rows, int64_t cols, int64_t sr, int64_t sc,
+                int64_t item, uintptr_t &lo, uintptr_t &hi)
+{
+    int64_t er, ec;
+    if (__builtin_mul_overflow(rows - 1, sr, &er) || __builtin_mul_overflow(cols - 1, sc, &ec))
+        return false;
+    const int64_t mn = (er < 0 ? er : 0) + (ec < 0 ? ec : 0);
+    const int64_t mx = (er > 0 ? er : 0) + (ec > 0 ? ec : 0);
+    int64_t blo, bhi;
+    if (__builtin_mul_overflow(mn, item, &blo) || __builtin_mul_overflow(mx + 1, item, &bhi))
+        return false;
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base);
+    lo = b + static_cast<uintptr_t>(blo);  // wraps correctly for negative offsets
+    hi = b + static_cast<uintptr_t>(bhi);
+    if (blo < 0 && static_cast<uintptr_t>(-blo) > b)
+        return false;
+    if (hi < b)
+        return false;
+    return true;
+}
+
+// Distinct (i, j) of an M x N view with these strides never share an element.
+inline bool c_strides_ok(int64_t M, int64_t N, int64_t scm, int64_t scn)
+{
+    if (scm < 0 || scn < 0)
+        return false;
+    if (M > 1 && scm == 0)
+        return false;
+    if (N > 1 && scn == 0)
+        return false;
+    if (M <= 1 || N <= 1)
+        return true;
+    // the smaller stride's axis must fit entirely inside one step of the larger
+    int64_t s_small = scm, n_small = M, s_big = scn;
+    if (scn < scm) {
+        s_small = scn;
+        n_small = N;
+        s_big = scm;
+    }
+    int64_t span;
+    if (__builtin_mul_overflow(s_small, n_small, &span))
+        return false;
+    return s_big >= span;
+}
+
+// DTM_OK when the current HIP device is a gfx950, else DTM_ERR_DEVICE
+// (cached per device).
+int check_device();
+
+}  // namespace dtm

@@ -1,0 +1,398 @@
+// softmax.hip -- row softmax on gfx950, the second workload.
+//
+// "Triton from zero, Lesson 4: Block Pointers", homework 4: each row of an
+// M x N view becomes exp(x - max) / sum(exp(x - max)); the columns a tile
+// holds past N are given -inf before the max, so they can neither win it nor
+// add to the sum (zero padding would be wrong for the max, section 3's
+// gotcha).  Here such slots are simply never read and contribute exactly 0
+// to the sum.  Arithmetic is fp32 (inputs are decoded exactly), the
+// exponential is the device library's expf, the division is IEEE-rounded,
+// and the result is converted once to the output dtype.
+//
+// The operation reads and writes each element once: it is bound by HBM
+// bandwidth, not by arithmetic, so there is no matrix-core work here.  What
+// matters is that every row is read once, with 16-byte loads when the rows
+// are unit-stride and aligned, and that the reductions stay on chip:
+//  * WAVE form: one wave64 per row, four rows per workgroup; each lane holds
+//    CH chunks of E elements in registers; max and sum are reduced across
+//    the wave with lane shuffles.
+//  * BLOCK form: one 1024-thread workgroup per row (rows too long for one
+//    wave); wave results are combined through LDS.
+//  * ONLINE form: rows too long for the workgroup's registers.  One pass
+//    keeps, per thread, a running max m and a sum s of exp(x - m), rescaling
+//    s by exp(m_old - m_new) when the max grows; the threads' (m, s) pairs
+//    are combined the same way; a second pass reads the row again and
+//    writes exp(x - m) / s.  Two reads and one write per element.
+// Special values follow the formula's own arithmetic: a NaN element does not
+// change the max (fmaxf) but makes the sum NaN, a +inf element makes the row
+// NaN, a row of -inf has max -inf and is NaN, other -inf elements give 0.
+// In-place use (Y the same view as X) is safe: every thread finishes reading
+// the row, or its element, before any thread writes it.
+#include "softmax_launch.h"
+
+namespace dtm {
+namespace {
+
+constexpr int WAVE = 64;
+constexpr int BLOCK_THREADS = 1024;
+constexpr int BLOCK_WAVES = BLOCK_THREADS / WAVE;
+
+template <int D> struct Bytes;
+template <> struct Bytes<DTM_F32> { static constexpr int value = 4; };
+template <> struct Bytes<DTM_F16> { static constexpr int value = 2; };
+template <> struct Bytes<DTM_BF16> { static constexpr int value = 2; };
+
+// Elements per chunk: one 16-byte load when vectorised, else one element.
+template <int IN, bool VEC> constexpr int chunk_elems() { return VEC ? 16 / Bytes<IN>::value : 1; }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Decodes E elements of chunk starting at column `col` of row `row_ptr`
+// into v[]; columns >= N are not read and marked invalid by the caller.
+template <int IN, bool VEC, int E>
+__device__ __forceinline__ void load_chunk(const SoftmaxArgs &p, int64_t row, int64_t col,
+                                           float (&v)[E])
+{
+    const int64_t base = row * p.sxm;
+    if constexpr (VEC) {
+        if (col + E <= p.N) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(
+                static_cast<const char *>(p.X) + (base + col) * Bytes<IN>::value);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                if constexpr (IN == DTM_F32) {
+                    v[e] = __uint_as_float(w[e]);
+                } else {
+                    const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                    if constexpr (IN == DTM_F16)
+                        v[e] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+                    else
+                        v[e] = __uint_as_float(h << 16);
+                }
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        v[e] = (col + e < p.N) ? load_elem<IN>(p.X, base + (col + e) * p.sxn) : 0.0f;
+}
+
+template <int OUT, bool VEC, int E>
+__device__ __forceinline__ void store_chunk(const SoftmaxArgs &p, int64_t row, int64_t col,
+                                            const float (&y)[E])
+{
+    const int64_t base = row * p.sym;
+    if constexpr (VEC) {
+        if (col + E <= p.N) {
+            char *dst = static_cast<char *>(p.Y) + (base + col) * Bytes<OUT>::value;
+            if constexpr (OUT == DTM_F32) {
+#pragma unroll
+                for (int h = 0; h < E / 4; ++h)
+                    *reinterpret_cast<u32x4 *>(dst + 16 * h) =
+                        u32x4{__float_as_uint(y[4 * h]), __float_as_uint(y[4 * h + 1]),
+                              __float_as_uint(y[4 * h + 2]), __float_as_uint(y[4 * h + 3])};
+            } else {
+                uint32_t w[E / 2];
+#pragma unroll
+                for (int h = 0; h < E / 2; ++h) {
+                    uint32_t lo, hi;
+                    if constexpr (OUT == DTM_F16) {
+                        lo = f32_to_f16_rne(y[2 * h]);
+                        hi = f32_to_f16_rne(y[2 * h + 1]);
+                    } else {
+                        lo = f32_to_bf16_rne(y[2 * h]);
+                        hi = f32_to_bf16_rne(y[2 * h + 1]);
+                    }
+                    w[h] = lo | (hi << 16);
+                }
+                if constexpr (E == 8) {
+                    *reinterpret_cast<u32x4 *>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+                } else {  // E == 4: 8 bytes
+                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                    *reinterpret_cast<u32x2 *>(dst) = u32x2{w[0], w[1]};
+                }
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (col + e < p.N)
+            store_elem<OUT>(p.Y, base + (col + e) * p.syn, y[e]);
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = WAVE / 2; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, WAVE));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = WAVE / 2; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, WAVE);
+    return v;
+}
+
+// Combines two (max, sum of exp(x - max)) pairs.  When both maxima are
+// equal (including both -inf) no rescaling is applied.
+__device__ __forceinline__ void merge_ms(float &m, float &s, float m2, float s2)
+{
+    const float mn = fmaxf(m, m2);
+    const float a = (m == mn) ? s : s * expf(m - mn);
+    const float b = (m2 == mn) ? s2 : s2 * expf(m2 - mn);
+    m = mn;
+    s = a + b;
+}
+
+// ---- WAVE form ---------------------------------------------------------------
+
+template <int IN, int OUT, int CH, bool VEC>
+__global__ __launch_bounds__(4 * WAVE) void softmax_wave_kernel(SoftmaxArgs p)
+{
+    constexpr int E = chunk_elems<IN, VEC>();
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (row >= p.M)
+        return;  // a whole wave leaves together; no barrier follows
+
+    float x[CH][E];
+    float m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+        const int64_t col = (static_cast<int64_t>(q) * WAVE + lane) * E;
+        load_chunk<IN, VEC, E>(p, row, col, x[q]);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (col + e < p.N)
+                m = fmaxf(m, x[q][e]);
+    }
+    m = wave_max(m);
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+        const int64_t col = (static_cast<int64_t>(q) * WAVE + lane) * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            x[q][e] = (col + e < p.N) ? expf(x[q][e] - m) : 0.0f;
+            s += x[q][e];
+        }
+    }
+    s = wave_sum(s);
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+        const int64_t col = (static_cast<int64_t>(q) * WAVE + lane) * E;
+        float y[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            y[e] = x[q][e] / s;
+        store_chunk<OUT, VEC, E>(p, row, col, y);
+    }
+}
+
+// ---- BLOCK and ONLINE forms ---------------------------------------------------
+
+// Reduces one value per wave across the workgroup through LDS; every thread
+// gets the result.  `red` holds BLOCK_WAVES floats; two barriers.
+template <bool MAX>
+__device__ __forceinline__ float block_reduce(float v, float *red)
+{
+    const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x >> 6;
+    v = MAX ? wave_max(v) : wave_sum(v);
+    if (lane == 0)
+        red[wave] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < BLOCK_WAVES; ++w)
+        r = MAX ? fmaxf(r, red[w]) : r + red[w];
+    __syncthreads();  // red may be reused
+    return r;
+}
+
+template <int IN, int OUT, int CH, bool VEC>
+__global__ __launch_bounds__(BLOCK_THREADS) void softmax_block_kernel(SoftmaxArgs p)
+{
+    constexpr int E = chunk_elems<IN, VEC>();
+    __shared__ float red[BLOCK_WAVES];
+    const int64_t row = blockIdx.x;
+    const int t = threadIdx.x;
+
+    float x[CH][E];
+    float m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+        const int64_t col = (static_cast<int64_t>(q) * BLOCK_THREADS + t) * E;
+        load_chunk<IN, VEC, E>(p, row, col, x[q]);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (col + e < p.N)
+                m = fmaxf(m, x[q][e]);
+    }
+    m = block_reduce<true>(m, red);
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+        const int64_t col = (static_cast<int64_t>(q) * BLOCK_THREADS + t) * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            x[q][e] = (col + e < p.N) ? expf(x[q][e] - m) : 0.0f;
+            s += x[q][e];
+        }
+    }
+    s = block_reduce<false>(s, red);
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+        const int64_t col = (static_cast<int64_t>(q) * BLOCK_THREADS + t) * E;
+        float y[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            y[e] = x[q][e] / s;
+        store_chunk<OUT, VEC, E>(p, row, col, y);
+    }
+}
+
+template <int IN, int OUT, bool VEC>
+__global__ __launch_bounds__(BLOCK_THREADS) void softmax_online_kernel(SoftmaxArgs p)
+{
+    constexpr int E = chunk_elems<IN, VEC>();
+    constexpr int CH = 2;  // chunks per thread per tile (loads in flight)
+    constexpr int64_t TILE = static_cast<int64_t>(BLOCK_THREADS) * CH * E;
+    __shared__ float red_m[BLOCK_WAVES], red_s[BLOCK_WAVES];
+    const int64_t row = blockIdx.x;
+    const int t = threadIdx.x;
+    const int lane = t & (WAVE - 1), wave = t >> 6;
+
+    // pass 1: running (max, sum of exp(x - max)) per thread
+    float m = -INFINITY, s = 0.0f;
+    for (int64_t c0 = 0; c0 < p.N; c0 += TILE) {
+        float x[CH][E];
+        float tm = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < CH; ++q) {
+            const int64_t col = c0 + (static_cast<int64_t>(q) * BLOCK_THREADS + t) * E;
+            load_chunk<IN, VEC, E>(p, row, col, x[q]);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (col + e < p.N)
+                    tm = fmaxf(tm, x[q][e]);
+        }
+        float ts = 0.0f;
+#pragma unroll
+        for (int q = 0; q < CH; ++q) {
+            const int64_t col = c0 + (static_cast<int64_t>(q) * BLOCK_THREADS + t) * E;
+            // a -inf element adds exactly 0 (even when the tile's max is
+            // -inf too); a row of -inf still ends NaN in pass 2, where the
+            // row max is -inf
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (col + e < p.N && x[q][e] != -INFINITY)
+                    ts += expf(x[q][e] - tm);
+        }
+        merge_ms(m, s, tm, ts);
+    }
+    // combine the threads' pairs: across the wave, then across waves
+#pragma unroll
+    for (int o = WAVE / 2; o > 0; o >>= 1) {
+        const float m2 = __shfl_xor(m, o, WAVE), s2 = __shfl_xor(s, o, WAVE);
+        merge_ms(m, s, m2, s2);
+    }
+    if (lane == 0) {
+        red_m[wave] = m;
+        red_s[wave] = s;
+    }
+    __syncthreads();
+    m = red_m[0];
+    s = red_s[0];
+#pragma unroll
+    for (int w = 1; w < BLOCK_WAVES; ++w)
+        merge_ms(m, s, red_m[w], red_s[w]);
+
+    // pass 2: write exp(x - m) / s
+    for (int64_t c0 = 0; c0 < p.N; c0 += TILE) {
+#pragma unroll
+        for (int q = 0; q < CH; ++q) {
+            const int64_t col = c0 + (static_cast<int64_t>(q) * BLOCK_THREADS + t) * E;
+            float x[E], y[E];
+            load_chunk<IN, VEC, E>(p, row, col, x);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                y[e] = expf(x[e] - m) / s;
+            store_chunk<OUT, VEC, E>(p, row, col, y);
+        }
+    }
+}
+
+// ---- launchers ------------------------------------------------------------------
+
+template <int IN, int OUT, bool VEC>
+hipError_t launch_form(const SoftmaxArgs &a, int form, int ch, hipStream_t s)
+{
+    if (form == SOFTMAX_WAVE) {
+        const dim3 grid((unsigned)cdiv(a.M, 4)), block(4 * WAVE);
+        switch (ch) {
+        case 1: hipLaunchKernelGGL((softmax_wave_kernel<IN, OUT, 1, VEC>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((softmax_wave_kernel<IN, OUT, 2, VEC>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((softmax_wave_kernel<IN, OUT, 4, VEC>), grid, block, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((softmax_wave_kernel<IN, OUT, 8, VEC>), grid, block, 0, s, a); break;
+        default: return hipErrorInvalidConfiguration;
+        }
+    } else if (form == SOFTMAX_BLOCK) {
+        const dim3 grid((unsigned)a.M), block(BLOCK_THREADS);
+        switch (ch) {
+        case 1: hipLaunchKernelGGL((softmax_block_kernel<IN, OUT, 1, VEC>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((softmax_block_kernel<IN, OUT, 2, VEC>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((softmax_block_kernel<IN, OUT, 4, VEC>), grid, block, 0, s, a); break;
+        default: return hipErrorInvalidConfiguration;
+        }
+    } else if (form == SOFTMAX_ONLINE) {
+        hipLaunchKernelGGL((softmax_online_kernel<IN, OUT, VEC>), dim3((unsigned)a.M),
+                           dim3(BLOCK_THREADS), 0, s, a);
+    } else {
+        return hipErrorInvalidConfiguration;
+    }
+    return hipGetLastError();
+}
+
+template <int IN, int OUT>
+hipError_t dispatch_vec(const SoftmaxArgs &a, int form, int ch, bool vec, hipStream_t s)
+{
+    return vec ? launch_form<IN, OUT, true>(a, form, ch, s)
+               : launch_form<IN, OUT, false>(a, form, ch, s);
+}
+
+template <int IN>
+hipError_t dispatch_out(const SoftmaxArgs &a, int out, int form, int ch, bool vec, hipStream_t s)
+{
+    switch (out) {
+    case DTM_F32: return dispatch_vec<IN, DTM_F32>(a, form, ch, vec, s);
+    case DTM_F16: return dispatch_vec<IN, DTM_F16>(a, form, ch, vec, s);
+    case DTM_BF16: return dispatch_vec<IN, DTM_BF16>(a, form, ch, vec, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int softmax_chunk_elems(int in_dtype, bool vec) { return vec ? (in_dtype == DTM_F32 ? 4 : 8) : 1; }
+int softmax_form_threads(int form) { return form == SOFTMAX_WAVE ? 4 * WAVE : BLOCK_THREADS; }
+int softmax_form_lanes(int form) { return form == SOFTMAX_WAVE ? WAVE : BLOCK_THREADS; }
+
+hipError_t launch_softmax(const SoftmaxArgs &a, int in, int out, int form, int ch, bool vec,
+                          hipStream_t s)
+{
+    if (a.M <= 0 || a.N <= 0 || a.M > 0x7fffffffLL)
+        return hipErrorInvalidConfiguration;
+    switch (in) {
+    case DTM_F32: return dispatch_out<DTM_F32>(a, out, form, ch, vec, s);
+    case DTM_F16: return dispatch_out<DTM_F16>(a, out, form, ch, vec, s);
+    case DTM_BF16: return dispatch_out<DTM_BF16>(a, out, form, ch, vec, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dtm

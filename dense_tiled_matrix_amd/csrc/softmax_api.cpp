@@ -1,0 +1,152 @@
+// softmax_api.cpp -- the C ABI of the row softmax: validation, plan, launch.
+//
+// The operation is the row softmax of "Triton from zero, Lesson 4: Block
+// Pointers", homework 4 (see include/dtm_softmax.h).  Every check runs on
+// the host before any launch; a non-zero status means nothing was launched.
+#include <cstring>
+
+#include "dtm_softmax.h"
+#include "host_util.h"
+#include "softmax_launch.h"
+
+namespace {
+
+struct SCall {
+    int64_t M, N;
+    const void *X;
+    int64_t sxm, sxn;
+    const void *Y;
+    int64_t sym, syn;
+    int in, out;
+};
+
+int validate(const SCall &c)
+{
+    constexpr int64_t kMaxDim = 0x7fffffffLL;
+    if (c.M < 0 || c.N < 0 || c.M > kMaxDim || c.N > kMaxDim)
+        return DTM_ERR_INVALID_DIM;
+    if (!dtm::valid_dtype(c.in) || !dtm::valid_dtype(c.out))
+        return DTM_ERR_DTYPE;
+    if (c.M == 0 || c.N == 0)
+        return DTM_OK;
+    if (!c.X || !c.Y)
+        return DTM_ERR_NULL_POINTER;
+    if (!dtm::c_strides_ok(c.M, c.N, c.sym, c.syn))
+        return DTM_ERR_STRIDE;
+    uintptr_t xlo, xhi, ylo, yhi;
+    if (!dtm::view_range(c.X, c.M, c.N, c.sxm, c.sxn, dtm::item_size(c.in), xlo, xhi) ||
+        !dtm::view_range(c.Y, c.M, c.N, c.sym, c.syn, dtm::item_size(c.out), ylo, yhi))
+        return DTM_ERR_STRIDE;
+    const bool in_place = c.X == c.Y && c.sxm == c.sym && c.sxn == c.syn &&
+                          dtm::item_size(c.in) == dtm::item_size(c.out);
+    if (!in_place && ylo < xhi && xlo < yhi)
+        return DTM_ERR_ALIAS;
+    return DTM_OK;
+}
+
+// 16-byte loads along the rows: unit column strides, 16-byte aligned rows of
+// X, and rows of Y aligned to the size of one chunk's output (at most 16).
+bool vectorizable(const SCall &c)
+{
+    if (c.sxn != 1 || c.syn != 1)
+        return false;
+    const int64_t in_sz = dtm::item_size(c.in), out_sz = dtm::item_size(c.out);
+    const int64_t e = 16 / in_sz;
+    const int64_t yal = e * out_sz < 16 ? e * out_sz : 16;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(c.X), y = reinterpret_cast<uintptr_t>(c.Y);
+    if (x % 16 || y % yal)
+        return false;
+    if (c.M > 1 && ((c.sxm * in_sz) % 16 || (c.sym * out_sz) % yal))
+        return false;
+    return true;
+}
+
+int make_plan(const SCall &c, dtm_softmax_plan *out)
+{
+    if (!out)
+        return DTM_ERR_NULL_POINTER;
+    std::memset(out, 0, sizeof(*out));
+    const int st = validate(c);
+    if (st != DTM_OK)
+        return st;
+    dtm_softmax_plan p;
+    std::memset(&p, 0, sizeof(p));
+    if (c.M == 0 || c.N == 0) {
+        p.form = DTM_SOFTMAX_NONE;
+        *out = p;
+        return DTM_OK;
+    }
+    const bool vec = vectorizable(c);
+    const int64_t e = dtm::softmax_chunk_elems(c.in, vec);
+    const int64_t wave_lanes = dtm::softmax_form_lanes(dtm::SOFTMAX_WAVE);
+    const int64_t block_lanes = dtm::softmax_form_lanes(dtm::SOFTMAX_BLOCK);
+    // A wave per row while a row fits in a wave's registers (8 chunks per
+    // lane) and there are enough rows to fill the chip; a workgroup per row
+    // up to 4 chunks per thread; beyond that the two-pass online form.
+    const bool many_rows = c.M >= 2048;
+    int form, ch = 0;
+    if (c.N <= wave_lanes * e * 8 && (many_rows || c.N <= wave_lanes * e * 2)) {
+        form = dtm::SOFTMAX_WAVE;
+        for (ch = 1; wave_lanes * e * ch < c.N; ch *= 2) {
+        }
+    } else if (c.N <= block_lanes * e * 4) {
+        form = dtm::SOFTMAX_BLOCK;
+        for (ch = 1; block_lanes * e * ch < c.N; ch *= 2) {
+        }
+    } else {
+        form = dtm::SOFTMAX_ONLINE;
+        ch = 2;
+    }
+    p.form = form;
+    p.threads = dtm::softmax_form_threads(form);
+    p.rows_per_block = form == dtm::SOFTMAX_WAVE ? p.threads / static_cast<int>(wave_lanes) : 1;
+    p.chunks = ch;
+    p.chunk_elems = static_cast<int32_t>(e);
+    p.vectorized = vec ? 1 : 0;
+    p.grid = dtm::cdiv(c.M, p.rows_per_block);
+    p.passes = form == dtm::SOFTMAX_ONLINE ? 2 : 1;
+    *out = p;
+    return DTM_OK;
+}
+
+SCall make_call(int64_t M, int64_t N, const void *X, int64_t sxm, int64_t sxn, const void *Y,
+                int64_t sym, int64_t syn, int in, int out)
+{
+    return SCall{M, N, X, sxm, sxn, Y, sym, syn, in, out};
+}
+
+}  // namespace
+
+extern "C" {
+
+int row_softmax(int64_t M, int64_t N, const void *X, int64_t stride_xm, int64_t stride_xn,
+                void *Y, int64_t stride_ym, int64_t stride_yn, int in_dtype, int out_dtype,
+                void *stream)
+{
+    const SCall c = make_call(M, N, X, stride_xm, stride_xn, Y, stride_ym, stride_yn, in_dtype,
+                              out_dtype);
+    dtm_softmax_plan p;
+    int st = make_plan(c, &p);
+    if (st != DTM_OK)
+        return st;
+    if (p.form == DTM_SOFTMAX_NONE)
+        return DTM_OK;
+    st = dtm::check_device();
+    if (st != DTM_OK)
+        return st;
+    const dtm::SoftmaxArgs a{M, N, X, stride_xm, stride_xn, Y, stride_ym, stride_yn};
+    const hipError_t e = dtm::launch_softmax(a, in_dtype, out_dtype, p.form, p.chunks,
+                                             p.vectorized != 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DTM_OK : DTM_ERR_LAUNCH;
+}
+
+int row_softmax_plan(int64_t M, int64_t N, const void *X, int64_t stride_xm, int64_t stride_xn,
+                     const void *Y, int64_t stride_ym, int64_t stride_yn, int in_dtype,
+                     int out_dtype, dtm_softmax_plan *out)
+{
+    return make_plan(make_call(M, N, X, stride_xm, stride_xn, Y, stride_ym, stride_yn, in_dtype,
+                               out_dtype),
+                     out);
+}
+
+}  // extern "C"
