@@ -5,17 +5,22 @@
 // holds past N are given -inf before the max, so they can neither win it nor
 // add to the sum (zero padding would be wrong for the max, section 3's
 // gotcha).  Here such slots are simply never read and contribute exactly 0
-// to the sum.  Arithmetic is fp32 (inputs are decoded exactly), the
-// exponential is the device library's expf, the division is IEEE-rounded,
-// and the result is converted once to the output dtype.
+// to the sum.  Arithmetic is fp32 (inputs are decoded exactly); exp(d) is
+// computed as 2^(d log2 e) on the hardware base-2 exponential (v_exp_f32,
+// about 1 ulp; results below 2^-126 flush to zero), the row sum's
+// reciprocal is taken once (IEEE-rounded) and multiplies every term, and
+// the result is converted once to the output dtype.  (The library's expf
+// and a per-element IEEE division cost ~25 VALU instructions per element,
+// which made the kernel arithmetic-bound on this part.)
 //
 // The operation reads and writes each element once: it is bound by HBM
 // bandwidth, not by arithmetic, so there is no matrix-core work here.  What
 // matters is that every row is read once, with 16-byte loads when the rows
 // are unit-stride and aligned, and that the reductions stay on chip:
 //  * WAVE form: one wave64 per row, four rows per workgroup; each lane holds
-//    CH chunks of E elements in registers; max and sum are reduced across
-//    the wave with lane shuffles.
+//    CH chunks of E elements in registers (16-bit inputs stay packed, and
+//    the exponential is recomputed for the write rather than kept); max and
+//    sum are reduced across the wave with lane shuffles.
 //  * BLOCK form: one 1024-thread workgroup per row (rows too long for one
 //    wave); wave results are combined through LDS.
 //  * ONLINE form: rows too long for the workgroup's registers.  One pass
@@ -47,11 +52,29 @@ template <int IN, bool VEC> constexpr int chunk_elems() { return VEC ? 16 / Byte
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Decodes E elements of chunk starting at column `col` of row `row_ptr`
-// into v[]; columns >= N are not read and marked invalid by the caller.
+// One chunk as loaded: E elements of the input dtype, packed.
+template <int IN, int E> struct Packed {
+    static constexpr int WORDS = (E * Bytes<IN>::value + 3) / 4;
+    uint32_t w[WORDS];
+    __device__ __forceinline__ float get(int e) const
+    {
+        if constexpr (IN == DTM_F32) {
+            return __uint_as_float(w[e]);
+        } else {
+            const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            if constexpr (IN == DTM_F16)
+                return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+            else
+                return __uint_as_float(h << 16);
+        }
+    }
+};
+
+// Loads the E elements of the chunk starting at column `col` of row `row`;
+// columns >= N are not read (their slots are 0 and callers skip them).
 template <int IN, bool VEC, int E>
 __device__ __forceinline__ void load_chunk(const SoftmaxArgs &p, int64_t row, int64_t col,
-                                           float (&v)[E])
+                                           Packed<IN, E> &v)
 {
     const int64_t base = row * p.sxm;
     if constexpr (VEC) {
@@ -59,23 +82,45 @@ __device__ __forceinline__ void load_chunk(const SoftmaxArgs &p, int64_t row, in
             const u32x4 w = *reinterpret_cast<const u32x4 *>(
                 static_cast<const char *>(p.X) + (base + col) * Bytes<IN>::value);
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                if constexpr (IN == DTM_F32) {
-                    v[e] = __uint_as_float(w[e]);
-                } else {
-                    const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                    if constexpr (IN == DTM_F16)
-                        v[e] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
-                    else
-                        v[e] = __uint_as_float(h << 16);
-                }
-            }
+            for (int i = 0; i < 4; ++i)
+                v.w[i] = w[i];
             return;
         }
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-        v[e] = (col + e < p.N) ? load_elem<IN>(p.X, base + (col + e) * p.sxn) : 0.0f;
+    for (int i = 0; i < Packed<IN, E>::WORDS; ++i)
+        v.w[i] = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if (col + e < p.N) {
+            const int64_t idx = base + (col + e) * p.sxn;
+            if constexpr (IN == DTM_F32)
+                v.w[e] = static_cast<const uint32_t *>(p.X)[idx];
+            else
+                v.w[e >> 1] |= static_cast<uint32_t>(static_cast<const uint16_t *>(p.X)[idx])
+                               << (16 * (e & 1));
+        }
+    }
+}
+
+// Tells the compiler the packed words may have changed, so values decoded
+// from them are decoded again after this point instead of being kept in
+// registers (16-bit chunks stay packed: half the registers).  Emits nothing.
+template <int IN, int E, int CH>
+__device__ __forceinline__ void keep_packed(Packed<IN, E> (&x)[CH])
+{
+#pragma unroll
+    for (int q = 0; q < CH; ++q)
+#pragma unroll
+        for (int i = 0; i < Packed<IN, E>::WORDS; ++i)
+            asm volatile("" : "+v"(x[q].w[i]));
+}
+
+// exp(d) for d <= 0 (or NaN): 2^(d log2 e) on the hardware exponential.
+__device__ __forceinline__ float exp_shifted(float d)
+{
+    constexpr float LOG2E = 1.4426950408889634f;
+    return __builtin_amdgcn_exp2f(d * LOG2E);
 }
 
 template <int OUT, bool VEC, int E>
@@ -143,8 +188,8 @@ __device__ __forceinline__ float wave_sum(float v)
 __device__ __forceinline__ void merge_ms(float &m, float &s, float m2, float s2)
 {
     const float mn = fmaxf(m, m2);
-    const float a = (m == mn) ? s : s * expf(m - mn);
-    const float b = (m2 == mn) ? s2 : s2 * expf(m2 - mn);
+    const float a = (m == mn) ? s : s * exp_shifted(m - mn);
+    const float b = (m2 == mn) ? s2 : s2 * exp_shifted(m2 - mn);
     m = mn;
     s = a + b;
 }
@@ -160,7 +205,7 @@ __global__ __launch_bounds__(4 * WAVE) void softmax_wave_kernel(SoftmaxArgs p)
     if (row >= p.M)
         return;  // a whole wave leaves together; no barrier follows
 
-    float x[CH][E];
+    Packed<IN, E> x[CH];
     float m = -INFINITY;
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
@@ -169,27 +214,28 @@ __global__ __launch_bounds__(4 * WAVE) void softmax_wave_kernel(SoftmaxArgs p)
 #pragma unroll
         for (int e = 0; e < E; ++e)
             if (col + e < p.N)
-                m = fmaxf(m, x[q][e]);
+                m = fmaxf(m, x[q].get(e));
     }
     m = wave_max(m);
+    keep_packed(x);
     float s = 0.0f;
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
         const int64_t col = (static_cast<int64_t>(q) * WAVE + lane) * E;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            x[q][e] = (col + e < p.N) ? expf(x[q][e] - m) : 0.0f;
-            s += x[q][e];
-        }
+        for (int e = 0; e < E; ++e)
+            if (col + e < p.N)
+                s += exp_shifted(x[q].get(e) - m);
     }
-    s = wave_sum(s);
+    const float r = 1.0f / wave_sum(s);
+    keep_packed(x);
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
         const int64_t col = (static_cast<int64_t>(q) * WAVE + lane) * E;
         float y[E];
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            y[e] = x[q][e] / s;
+            y[e] = exp_shifted(x[q].get(e) - m) * r;
         store_chunk<OUT, VEC, E>(p, row, col, y);
     }
 }
@@ -222,7 +268,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) void softmax_block_kernel(SoftmaxArg
     const int64_t row = blockIdx.x;
     const int t = threadIdx.x;
 
-    float x[CH][E];
+    Packed<IN, E> x[CH];
     float m = -INFINITY;
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
@@ -231,27 +277,28 @@ __global__ __launch_bounds__(BLOCK_THREADS) void softmax_block_kernel(SoftmaxArg
 #pragma unroll
         for (int e = 0; e < E; ++e)
             if (col + e < p.N)
-                m = fmaxf(m, x[q][e]);
+                m = fmaxf(m, x[q].get(e));
     }
     m = block_reduce<true>(m, red);
+    keep_packed(x);
     float s = 0.0f;
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
         const int64_t col = (static_cast<int64_t>(q) * BLOCK_THREADS + t) * E;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            x[q][e] = (col + e < p.N) ? expf(x[q][e] - m) : 0.0f;
-            s += x[q][e];
-        }
+        for (int e = 0; e < E; ++e)
+            if (col + e < p.N)
+                s += exp_shifted(x[q].get(e) - m);
     }
-    s = block_reduce<false>(s, red);
+    const float r = 1.0f / block_reduce<false>(s, red);
+    keep_packed(x);
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
         const int64_t col = (static_cast<int64_t>(q) * BLOCK_THREADS + t) * E;
         float y[E];
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            y[e] = x[q][e] / s;
+            y[e] = exp_shifted(x[q].get(e) - m) * r;
         store_chunk<OUT, VEC, E>(p, row, col, y);
     }
 }
@@ -270,7 +317,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) void softmax_online_kernel(SoftmaxAr
     // pass 1: running (max, sum of exp(x - max)) per thread
     float m = -INFINITY, s = 0.0f;
     for (int64_t c0 = 0; c0 < p.N; c0 += TILE) {
-        float x[CH][E];
+        Packed<IN, E> x[CH];
         float tm = -INFINITY;
 #pragma unroll
         for (int q = 0; q < CH; ++q) {
@@ -279,7 +326,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) void softmax_online_kernel(SoftmaxAr
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 if (col + e < p.N)
-                    tm = fmaxf(tm, x[q][e]);
+                    tm = fmaxf(tm, x[q].get(e));
         }
         float ts = 0.0f;
 #pragma unroll
@@ -289,9 +336,11 @@ __global__ __launch_bounds__(BLOCK_THREADS) void softmax_online_kernel(SoftmaxAr
             // -inf too); a row of -inf still ends NaN in pass 2, where the
             // row max is -inf
 #pragma unroll
-            for (int e = 0; e < E; ++e)
-                if (col + e < p.N && x[q][e] != -INFINITY)
-                    ts += expf(x[q][e] - tm);
+            for (int e = 0; e < E; ++e) {
+                const float v = x[q].get(e);
+                if (col + e < p.N && v != -INFINITY)
+                    ts += exp_shifted(v - tm);
+            }
         }
         merge_ms(m, s, tm, ts);
     }
@@ -313,15 +362,20 @@ __global__ __launch_bounds__(BLOCK_THREADS) void softmax_online_kernel(SoftmaxAr
         merge_ms(m, s, red_m[w], red_s[w]);
 
     // pass 2: write exp(x - m) / s
+    const float r = 1.0f / s;
     for (int64_t c0 = 0; c0 < p.N; c0 += TILE) {
+        Packed<IN, E> x[CH];
+#pragma unroll
+        for (int q = 0; q < CH; ++q)
+            load_chunk<IN, VEC, E>(p, row, c0 + (static_cast<int64_t>(q) * BLOCK_THREADS + t) * E,
+                                   x[q]);
 #pragma unroll
         for (int q = 0; q < CH; ++q) {
             const int64_t col = c0 + (static_cast<int64_t>(q) * BLOCK_THREADS + t) * E;
-            float x[E], y[E];
-            load_chunk<IN, VEC, E>(p, row, col, x);
+            float y[E];
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                y[e] = expf(x[e] - m) / s;
+                y[e] = exp_shifted(x[q].get(e) - m) * r;
             store_chunk<OUT, VEC, E>(p, row, col, y);
         }
     }
@@ -339,6 +393,7 @@ hipError_t launch_form(const SoftmaxArgs &a, int form, int ch, hipStream_t s)
         case 2: hipLaunchKernelGGL((softmax_wave_kernel<IN, OUT, 2, VEC>), grid, block, 0, s, a); break;
         case 4: hipLaunchKernelGGL((softmax_wave_kernel<IN, OUT, 4, VEC>), grid, block, 0, s, a); break;
         case 8: hipLaunchKernelGGL((softmax_wave_kernel<IN, OUT, 8, VEC>), grid, block, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((softmax_wave_kernel<IN, OUT, 16, VEC>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidConfiguration;
         }
     } else if (form == SOFTMAX_BLOCK) {

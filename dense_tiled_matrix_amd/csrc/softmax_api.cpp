@@ -80,12 +80,12 @@ int make_plan(const SCall &c, dtm_softmax_plan *out)
     const int64_t e = dtm::softmax_chunk_elems(c.in, vec);
     const int64_t wave_lanes = dtm::softmax_form_lanes(dtm::SOFTMAX_WAVE);
     const int64_t block_lanes = dtm::softmax_form_lanes(dtm::SOFTMAX_BLOCK);
-    // A wave per row while a row fits in a wave's registers (8 chunks per
+    // A wave per row while a row fits in a wave's registers (16 chunks per
     // lane) and there are enough rows to fill the chip; a workgroup per row
     // up to 4 chunks per thread; beyond that the two-pass online form.
     const bool many_rows = c.M >= 2048;
     int form, ch = 0;
-    if (c.N <= wave_lanes * e * 8 && (many_rows || c.N <= wave_lanes * e * 2)) {
+    if (c.N <= wave_lanes * e * 16 && (many_rows || c.N <= wave_lanes * e * 2)) {
         form = dtm::SOFTMAX_WAVE;
         for (ch = 1; wave_lanes * e * ch < c.N; ch *= 2) {
         }

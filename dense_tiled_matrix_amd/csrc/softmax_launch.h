@@ -25,7 +25,7 @@ int softmax_chunk_elems(int in_dtype, bool vec);
 // Threads per workgroup and threads per row of a form.
 int softmax_form_threads(int form);
 int softmax_form_lanes(int form);
-// `ch` chunks per thread: WAVE 1, 2, 4, 8; BLOCK 1, 2, 4; ONLINE ignores it.
+// `ch` chunks per thread: WAVE 1, 2, 4, 8, 16; BLOCK 1, 2, 4; ONLINE ignores it.
 hipError_t launch_softmax(const SoftmaxArgs &a, int in_dtype, int out_dtype, int form, int ch,
                           bool vec, hipStream_t s);
 

@@ -159,12 +159,14 @@ def softmax_problem(p, out_dtype=None, threads: int = 0):
 
 def softmax_tolerance(x64_row_minus_max: np.ndarray, y64: np.ndarray, terms: int) -> np.ndarray:
     """Per-element bound for a row softmax computed in fp32 from the same
-    inputs: the shifted argument d = x - max is rounded once (relative
-    2^-24, i.e. absolute |d| 2^-24 in the exponent), exp adds a few ulps,
-    the sum of the row's exponentials adds at most ``terms`` roundings
-    (the longest chain of fp32 additions any one partial sum passes through)
-    and the division one more; values far below 1 can also lose their last
-    bits to fp32 gradual underflow (2^-149 absolute before the division by a
-    sum >= 1).  Returns |Y - Y64| bounds, elementwise."""
-    rel = (np.abs(np.nan_to_num(x64_row_minus_max, nan=0.0, neginf=0.0)) + terms + 8) * 2.0 ** -24
-    return np.abs(y64) * rel + 2.0 ** -140
+    inputs: the shifted argument d = x - max is rounded once and scaled by
+    log2(e) once (together about 2 |d| 2^-24 in the exponent), the base-2
+    exponential adds a few ulps, the sum of the row's exponentials adds at
+    most ``terms`` roundings (the longest chain of fp32 additions any one
+    partial sum passes through), and the reciprocal of the sum and the
+    product with it one each; exponentials below 2^-126 may flush to zero
+    (an absolute 2^-126 before the division by a sum >= 1).  Returns
+    |Y - Y64| bounds, elementwise."""
+    d = np.abs(np.nan_to_num(x64_row_minus_max, nan=0.0, neginf=0.0))
+    rel = (2 * d + terms + 10) * 2.0 ** -24
+    return np.abs(y64) * rel + 2.0 ** -125

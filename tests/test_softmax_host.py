@@ -20,15 +20,16 @@ def test_symbols_exported():
 
 
 def test_forms_by_row_length():
-    """A wave per row while the row fits in a wave's registers and rows are
-    many; a workgroup per row up to 4 chunks per thread; beyond that the
+    """A wave per row while the row fits in a wave's registers (16 chunks per
+    lane) and rows are many; a workgroup per row up to 4 chunks per thread; beyond that the
     two-pass online form.  16-byte chunks: 4 fp32 or 8 fp16/bf16 elements."""
     cases = [
         (32768, 1024, F16, "wave", 2, 8, 1),
         (32768, 4096, F16, "wave", 8, 8, 1),
         (4096, 2048, F32, "wave", 8, 4, 1),
-        (4096, 4096, F32, "block", 1, 4, 1),
-        (8192, 8192, BF16, "block", 1, 8, 1),
+        (4096, 4096, F32, "wave", 16, 4, 1),
+        (8192, 8192, BF16, "wave", 16, 8, 1),
+        (1024, 8192, BF16, "block", 1, 8, 1),   # fewer rows: a workgroup per row
         (256, 16384, F32, "block", 4, 4, 1),
         (256, 65536, F32, "online", 2, 4, 2),
         (64, 2048, F32, "block", 1, 4, 1),   # few rows: a workgroup per row
