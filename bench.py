@@ -7,7 +7,10 @@ on the workload's synthetic, seeded inputs, already resident in HBM.  Prints
 one JSON line: whole-job TFLOP/s over K timed steps, the dominant kernel's
 achieved TFLOP/s against the dense MFMA peak (HIP events on the stream the
 kernel runs on), and the CPU oracle timed on a bounded sample of the same
-workload on this host.
+workload on this host.  The row-softmax workloads (the second, HBM-bound
+operation) are timed the same way and reported under "softmax" in GB/s of
+algorithmic traffic (X read once, Y written once) against the 8 TB/s HBM
+peak.
 """
 from __future__ import annotations
 
@@ -24,6 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GEMM TFLOP/s and % of MFMA peak at fp16/bf16 4096³ and 8192³ on 1 MI355X"
 # MI355X dense MFMA peaks (TFLOP/s): 256 CUs x 2.4 GHz x FLOP/clk/CU
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 HOST_THREADS_CAP = 16  # the host-core share of one GPU on the GPU machines
 # sources of the timed kernel (the 256 x 256 x 32 pipelined MFMA kernel)
 KERNEL_SOURCES = ["dense_tiled_matrix_amd/csrc/gemm_mfma16_dma.hip",
@@ -119,6 +123,10 @@ def main():
     ap.add_argument("--workload", default="bf16_8192_bf16out")
     ap.add_argument("--secondary", default="f16_4096_f32out",
                     help="comma-separated workloads also timed (not the headline)")
+    ap.add_argument("--softmax", default=",".join([
+        "softmax_f32_4096x4096", "softmax_bf16_8192x8192_masked", "softmax_f16_32768x1024",
+        "softmax_f32_256x65536"]),
+        help="comma-separated row-softmax workloads also timed (HBM-bound; 'none' to skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -191,6 +199,34 @@ def main():
                           "tile": [qplan["block_m"], qplan["block_n"], qplan["block_k"]]})
     if secondary:
         line["secondary"] = secondary
+    softmax = []
+    for name in [s for s in args.softmax.split(",") if s and s != "none"]:
+        q = W.softmax_workload(name)
+        x = to_device(q.X, TD[q.in_dtype], torch)
+        y = torch.empty(q.M, q.N, dtype=TD[q.out_dtype], device="cuda:0")
+        splan = dtm.row_softmax_plan(x, out=y)
+        stream = torch.cuda.current_stream()
+        for _ in range(args.warmup):
+            dtm.row_softmax(x, out=y, stream=stream)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            dtm.row_softmax(x, out=y, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        kern_ms = e0.elapsed_time(e1) / args.steps
+        # algorithmic bytes: X read once, Y written once
+        alg = q.M * q.N * (x.element_size() + y.element_size())
+        gbs = alg / (kern_ms * 1e-3) / 1e9
+        softmax.append({"workload": q.name, "form": splan["form_name"],
+                        "chunks": splan["chunks"], "kernel_us": round(kern_ms * 1e3, 2),
+                        "bytes": alg, "gb_s": round(gbs, 1), "peak_gb_s": PEAK_HBM_GBS,
+                        "frac": round(gbs / PEAK_HBM_GBS, 4)})
+        del x, y
+    if softmax:
+        line["softmax"] = softmax
     line["cpu_baseline"] = None if args.no_cpu else cpu_baseline(p, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
