@@ -127,6 +127,10 @@ def main():
         "softmax_f32_4096x4096", "softmax_bf16_8192x8192_masked", "softmax_f16_32768x1024",
         "softmax_f32_256x65536"]),
         help="comma-separated row-softmax workloads also timed (HBM-bound; 'none' to skip)")
+    ap.add_argument("--skinny", default="f16_skinny512x512x65536_f32out",
+                    help="long-K workload timed warm and cold (its inputs fit the 256 MB "
+                         "Infinity Cache, so cold runs overwrite 1 GiB between calls); "
+                         "'none' to skip")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -176,6 +180,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(wall_ms, 4),
+        "host_overhead_us_per_call": round((wall_ms - kern_ms) * 1e3, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -199,6 +204,37 @@ def main():
                           "tile": [qplan["block_m"], qplan["block_n"], qplan["block_k"]]})
     if secondary:
         line["secondary"] = secondary
+    if args.skinny and args.skinny != "none":
+        q = W.workload(args.skinny)
+        a = to_device(q.A, TD[q.in_dtype], torch)
+        b = to_device(q.B, TD[q.in_dtype], torch)
+        c = torch.empty(q.M, q.N, dtype=TD[q.out_dtype], device="cuda:0")
+        qplan = dtm.gemm_plan(a, b, out=c)
+        _, warm_ms = time_gemm(dtm, torch, a, b, c, args.steps, args.warmup)
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
+        stream = torch.cuda.current_stream()
+        cold = []
+        for _ in range(min(args.steps, 20)):
+            flush.fill_(1.0)  # evicts the inputs from the caches, outside the events
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dtm.gemm(a, b, out=c, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        cold_ms = sorted(cold)[len(cold) // 2]
+        # algorithmic bytes: A and B read once, C written once
+        alg = (q.M * q.K + q.K * q.N) * a.element_size() + q.M * q.N * c.element_size()
+        qflops = 2.0 * q.M * q.N * q.K
+        line["skinny"] = {"workload": q.name, "split_k": qplan["split_k"],
+                          "warm_us": round(warm_ms * 1e3, 2), "cold_us": round(cold_ms * 1e3, 2),
+                          "tflops_warm": round(qflops / (warm_ms * 1e-3) / 1e12, 1),
+                          "tflops_cold": round(qflops / (cold_ms * 1e-3) / 1e12, 1),
+                          "bytes": alg, "hbm_roofline_us": round(alg / (PEAK_HBM_GBS * 1e3), 2),
+                          "cold_frac_of_hbm_roofline": round(alg / (PEAK_HBM_GBS * 1e3) /
+                                                             (cold_ms * 1e3), 4)}
+        del a, b, c, flush
     softmax = []
     for name in [s for s in args.softmax.split(",") if s and s != "none"]:
         q = W.softmax_workload(name)

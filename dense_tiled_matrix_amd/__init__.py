@@ -66,7 +66,7 @@ class Plan(ctypes.Structure):
 
 
 # dtm_softmax_form
-SOFTMAX_FORMS = {0: "none", 1: "wave", 2: "block", 3: "online"}
+SOFTMAX_FORMS = {0: "none", 1: "wave", 2: "block", 3: "online", 4: "split"}
 
 
 class SoftmaxPlan(ctypes.Structure):
@@ -76,10 +76,10 @@ class SoftmaxPlan(ctypes.Structure):
                 ("rows_per_block", ctypes.c_int32), ("chunks", ctypes.c_int32),
                 ("chunk_elems", ctypes.c_int32), ("vectorized", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("passes", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("parts", ctypes.c_int32)]
 
     def as_dict(self):
-        d = {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+        d = {f: getattr(self, f) for f, _ in self._fields_}
         d["form_name"] = SOFTMAX_FORMS.get(self.form, "unknown")
         return d
 

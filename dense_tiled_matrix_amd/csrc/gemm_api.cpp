@@ -47,6 +47,40 @@ int check_device()
     return ok ? DTM_OK : DTM_ERR_DEVICE;
 }
 
+// ---- library-owned workspace (split-K partials, split-row softmax statistics) ---------------------------------------
+// One buffer per (device, stream), grown on demand.  Growing first waits for
+// the stream (earlier work may still read the old buffer), then frees and
+// allocates.  Work on one stream runs in order, so reuse within a stream is
+// safe; different streams never share a buffer.
+namespace {
+std::mutex g_ws_mutex;
+std::map<std::pair<int, void *>, std::pair<void *, uint64_t>> g_ws;
+}  // namespace
+
+void *library_workspace(void *stream, uint64_t bytes)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    auto &e = g_ws[{dev, stream}];
+    if (e.second >= bytes)
+        return e.first;
+    if (e.first) {
+        if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+            return nullptr;
+        (void)hipFree(e.first);
+        e.first = nullptr;
+        e.second = 0;
+    }
+    void *ptr = nullptr;
+    if (hipMalloc(&ptr, bytes) != hipSuccess)
+        return nullptr;
+    e.first = ptr;
+    e.second = bytes;
+    return ptr;
+}
+
 }  // namespace dtm
 
 namespace {
@@ -56,6 +90,7 @@ using dtm::cdiv;
 using dtm::check_device;
 using dtm::GemmArgs;
 using dtm::item_size;
+using dtm::library_workspace;
 using dtm::valid_dtype;
 using dtm::view_range;
 
@@ -317,38 +352,6 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
 }
 
 // ---- device check ---------------------------------------------------------
-
-// ---- library-owned split-K workspace ---------------------------------------
-// One buffer per (device, stream), grown on demand.  Growing first waits for
-// the stream (earlier work may still read the old buffer), then frees and
-// allocates.  Work on one stream runs in order, so reuse within a stream is
-// safe; different streams never share a buffer.
-std::mutex g_ws_mutex;
-std::map<std::pair<int, void *>, std::pair<void *, uint64_t>> g_ws;
-
-void *library_workspace(void *stream, uint64_t bytes)
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return nullptr;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    auto &e = g_ws[{dev, stream}];
-    if (e.second >= bytes)
-        return e.first;
-    if (e.first) {
-        if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
-            return nullptr;
-        (void)hipFree(e.first);
-        e.first = nullptr;
-        e.second = 0;
-    }
-    void *ptr = nullptr;
-    if (hipMalloc(&ptr, bytes) != hipSuccess)
-        return nullptr;
-    e.first = ptr;
-    e.second = bytes;
-    return ptr;
-}
 
 int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t workspace_bytes,
         void *stream)

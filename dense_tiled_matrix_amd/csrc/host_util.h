@@ -62,4 +62,11 @@ inline bool c_strides_ok(int64_t M, int64_t N, int64_t scm, int64_t scn)
 // (cached per device).
 int check_device();
 
+// A device buffer of at least `bytes` owned by the library, one per (current
+// device, stream), grown on demand: growing first synchronises the stream
+// (earlier work may still use the old buffer), then frees and allocates.
+// Work on one stream runs in order, so reuse within a stream is safe.
+// nullptr when the allocation fails.
+void *library_workspace(void *stream, uint64_t bytes);
+
 }  // namespace dtm

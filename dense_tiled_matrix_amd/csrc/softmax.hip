@@ -28,6 +28,11 @@
 //    s by exp(m_old - m_new) when the max grows; the threads' (m, s) pairs
 //    are combined the same way; a second pass reads the row again and
 //    writes exp(x - m) / s.  Two reads and one write per element.
+//  * SPLIT form: rows too long for one workgroup per row to fill the chip
+//    (few rows): each row is cut into parts, one workgroup per (row, part);
+//    a first kernel writes each part's (max, sum) pair to a small
+//    workspace, a second merges the row's pairs in a fixed order and writes
+//    its part.  Also two reads and one write per element.
 // Special values follow the formula's own arithmetic: a NaN element does not
 // change the max (fmaxf) but makes the sum NaN, a +inf element makes the row
 // NaN, a row of -inf has max -inf and is NaN, other -inf elements give 0.
@@ -303,20 +308,31 @@ __global__ __launch_bounds__(BLOCK_THREADS) void softmax_block_kernel(SoftmaxArg
     }
 }
 
-template <int IN, int OUT, bool VEC>
-__global__ __launch_bounds__(BLOCK_THREADS) void softmax_online_kernel(SoftmaxArgs p)
+// ONLINE and SPLIT work in tiles of BLOCK_THREADS x ONLINE_CH chunks.
+constexpr int ONLINE_CH = 2;  // chunks per thread per tile (loads in flight)
+template <int IN, bool VEC> constexpr int64_t online_tile()
+{
+    return static_cast<int64_t>(BLOCK_THREADS) * ONLINE_CH * chunk_elems<IN, VEC>();
+}
+
+// The (max, sum of exp(x - max)) pair of columns [cb, ce) of `row`, for the
+// whole workgroup: per thread a running pair over the tiles, rescaled when
+// the max grows, then merged across the wave and across waves.  cb is a
+// multiple of the tile and ce is N or a multiple of the tile, so no chunk
+// straddles ce.  Every thread returns the workgroup's pair.
+template <int IN, bool VEC>
+__device__ __forceinline__ void range_stats(const SoftmaxArgs &p, int64_t row, int64_t cb,
+                                            int64_t ce, float &m, float &s, float *red_m,
+                                            float *red_s)
 {
     constexpr int E = chunk_elems<IN, VEC>();
-    constexpr int CH = 2;  // chunks per thread per tile (loads in flight)
-    constexpr int64_t TILE = static_cast<int64_t>(BLOCK_THREADS) * CH * E;
-    __shared__ float red_m[BLOCK_WAVES], red_s[BLOCK_WAVES];
-    const int64_t row = blockIdx.x;
+    constexpr int CH = ONLINE_CH;
+    constexpr int64_t TILE = online_tile<IN, VEC>();
     const int t = threadIdx.x;
     const int lane = t & (WAVE - 1), wave = t >> 6;
-
-    // pass 1: running (max, sum of exp(x - max)) per thread
-    float m = -INFINITY, s = 0.0f;
-    for (int64_t c0 = 0; c0 < p.N; c0 += TILE) {
+    m = -INFINITY;
+    s = 0.0f;
+    for (int64_t c0 = cb; c0 < ce; c0 += TILE) {
         Packed<IN, E> x[CH];
         float tm = -INFINITY;
 #pragma unroll
@@ -333,8 +349,8 @@ __global__ __launch_bounds__(BLOCK_THREADS) void softmax_online_kernel(SoftmaxAr
         for (int q = 0; q < CH; ++q) {
             const int64_t col = c0 + (static_cast<int64_t>(q) * BLOCK_THREADS + t) * E;
             // a -inf element adds exactly 0 (even when the tile's max is
-            // -inf too); a row of -inf still ends NaN in pass 2, where the
-            // row max is -inf
+            // -inf too); a row of -inf still ends NaN in the write pass,
+            // where the row max is -inf
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const float v = x[q].get(e);
@@ -344,7 +360,6 @@ __global__ __launch_bounds__(BLOCK_THREADS) void softmax_online_kernel(SoftmaxAr
         }
         merge_ms(m, s, tm, ts);
     }
-    // combine the threads' pairs: across the wave, then across waves
 #pragma unroll
     for (int o = WAVE / 2; o > 0; o >>= 1) {
         const float m2 = __shfl_xor(m, o, WAVE), s2 = __shfl_xor(s, o, WAVE);
@@ -360,10 +375,18 @@ __global__ __launch_bounds__(BLOCK_THREADS) void softmax_online_kernel(SoftmaxAr
 #pragma unroll
     for (int w = 1; w < BLOCK_WAVES; ++w)
         merge_ms(m, s, red_m[w], red_s[w]);
+}
 
-    // pass 2: write exp(x - m) / s
-    const float r = 1.0f / s;
-    for (int64_t c0 = 0; c0 < p.N; c0 += TILE) {
+// Writes exp(x - m) * r for columns [cb, ce) of `row` (r = 1 / row sum).
+template <int IN, int OUT, bool VEC>
+__device__ __forceinline__ void range_write(const SoftmaxArgs &p, int64_t row, int64_t cb,
+                                            int64_t ce, float m, float r)
+{
+    constexpr int E = chunk_elems<IN, VEC>();
+    constexpr int CH = ONLINE_CH;
+    constexpr int64_t TILE = online_tile<IN, VEC>();
+    const int t = threadIdx.x;
+    for (int64_t c0 = cb; c0 < ce; c0 += TILE) {
         Packed<IN, E> x[CH];
 #pragma unroll
         for (int q = 0; q < CH; ++q)
@@ -381,10 +404,61 @@ __global__ __launch_bounds__(BLOCK_THREADS) void softmax_online_kernel(SoftmaxAr
     }
 }
 
+template <int IN, int OUT, bool VEC>
+__global__ __launch_bounds__(BLOCK_THREADS) void softmax_online_kernel(SoftmaxArgs p)
+{
+    __shared__ float red_m[BLOCK_WAVES], red_s[BLOCK_WAVES];
+    const int64_t row = blockIdx.x;
+    float m, s;
+    range_stats<IN, VEC>(p, row, 0, p.N, m, s, red_m, red_s);
+    range_write<IN, OUT, VEC>(p, row, 0, p.N, m, 1.0f / s);
+}
+
+// ---- SPLIT form: each row cut into `parts` ranges of `part_len` columns ----
+// (a multiple of the tile), one workgroup per (row, part).  The stats kernel
+// writes each range's (max, sum) pair to ws[2 (row*parts + part) + {0, 1}];
+// the write kernel merges the row's pairs in the fixed order part = 0, 1, ...
+// (so every workgroup of a row gets the same row max and sum, and the result
+// does not depend on scheduling) and writes its range.
+
+template <int IN, bool VEC>
+__global__ __launch_bounds__(BLOCK_THREADS) void softmax_split_stats_kernel(SoftmaxArgs p,
+                                                                            int64_t parts,
+                                                                            int64_t part_len,
+                                                                            float *ws)
+{
+    __shared__ float red_m[BLOCK_WAVES], red_s[BLOCK_WAVES];
+    const int64_t row = blockIdx.x / parts, part = blockIdx.x % parts;
+    const int64_t cb = part * part_len;
+    const int64_t ce = cb + part_len < p.N ? cb + part_len : p.N;
+    float m, s;
+    range_stats<IN, VEC>(p, row, cb, ce, m, s, red_m, red_s);
+    if (threadIdx.x == 0) {
+        ws[2 * blockIdx.x] = m;
+        ws[2 * blockIdx.x + 1] = s;
+    }
+}
+
+template <int IN, int OUT, bool VEC>
+__global__ __launch_bounds__(BLOCK_THREADS) void softmax_split_write_kernel(SoftmaxArgs p,
+                                                                            int64_t parts,
+                                                                            int64_t part_len,
+                                                                            const float *ws)
+{
+    const int64_t row = blockIdx.x / parts, part = blockIdx.x % parts;
+    const int64_t cb = part * part_len;
+    const int64_t ce = cb + part_len < p.N ? cb + part_len : p.N;
+    const float *w = ws + 2 * row * parts;
+    float m = w[0], s = w[1];
+    for (int64_t q = 1; q < parts; ++q)
+        merge_ms(m, s, w[2 * q], w[2 * q + 1]);
+    range_write<IN, OUT, VEC>(p, row, cb, ce, m, 1.0f / s);
+}
+
 // ---- launchers ------------------------------------------------------------------
 
 template <int IN, int OUT, bool VEC>
-hipError_t launch_form(const SoftmaxArgs &a, int form, int ch, hipStream_t s)
+hipError_t launch_form(const SoftmaxArgs &a, int form, int ch, float *ws, hipStream_t s)
 {
     if (form == SOFTMAX_WAVE) {
         const dim3 grid((unsigned)cdiv(a.M, 4)), block(4 * WAVE);
@@ -407,6 +481,19 @@ hipError_t launch_form(const SoftmaxArgs &a, int form, int ch, hipStream_t s)
     } else if (form == SOFTMAX_ONLINE) {
         hipLaunchKernelGGL((softmax_online_kernel<IN, OUT, VEC>), dim3((unsigned)a.M),
                            dim3(BLOCK_THREADS), 0, s, a);
+    } else if (form == SOFTMAX_SPLIT) {
+        const int64_t parts = ch, part_len = cdiv(cdiv(a.N, parts), online_tile<IN, VEC>()) *
+                                             online_tile<IN, VEC>();
+        if (!ws || (parts - 1) * part_len >= a.N)
+            return hipErrorInvalidConfiguration;
+        const dim3 grid((unsigned)(a.M * parts)), block(BLOCK_THREADS);
+        hipLaunchKernelGGL((softmax_split_stats_kernel<IN, VEC>), grid, block, 0, s, a, parts,
+                           part_len, ws);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        hipLaunchKernelGGL((softmax_split_write_kernel<IN, OUT, VEC>), grid, block, 0, s, a,
+                           parts, part_len, static_cast<const float *>(ws));
     } else {
         return hipErrorInvalidConfiguration;
     }
@@ -414,19 +501,21 @@ hipError_t launch_form(const SoftmaxArgs &a, int form, int ch, hipStream_t s)
 }
 
 template <int IN, int OUT>
-hipError_t dispatch_vec(const SoftmaxArgs &a, int form, int ch, bool vec, hipStream_t s)
+hipError_t dispatch_vec(const SoftmaxArgs &a, int form, int ch, bool vec, float *ws,
+                        hipStream_t s)
 {
-    return vec ? launch_form<IN, OUT, true>(a, form, ch, s)
-               : launch_form<IN, OUT, false>(a, form, ch, s);
+    return vec ? launch_form<IN, OUT, true>(a, form, ch, ws, s)
+               : launch_form<IN, OUT, false>(a, form, ch, ws, s);
 }
 
 template <int IN>
-hipError_t dispatch_out(const SoftmaxArgs &a, int out, int form, int ch, bool vec, hipStream_t s)
+hipError_t dispatch_out(const SoftmaxArgs &a, int out, int form, int ch, bool vec, float *ws,
+                        hipStream_t s)
 {
     switch (out) {
-    case DTM_F32: return dispatch_vec<IN, DTM_F32>(a, form, ch, vec, s);
-    case DTM_F16: return dispatch_vec<IN, DTM_F16>(a, form, ch, vec, s);
-    case DTM_BF16: return dispatch_vec<IN, DTM_BF16>(a, form, ch, vec, s);
+    case DTM_F32: return dispatch_vec<IN, DTM_F32>(a, form, ch, vec, ws, s);
+    case DTM_F16: return dispatch_vec<IN, DTM_F16>(a, form, ch, vec, ws, s);
+    case DTM_BF16: return dispatch_vec<IN, DTM_BF16>(a, form, ch, vec, ws, s);
     }
     return hipErrorInvalidValue;
 }
@@ -437,15 +526,20 @@ int softmax_chunk_elems(int in_dtype, bool vec) { return vec ? (in_dtype == DTM_
 int softmax_form_threads(int form) { return form == SOFTMAX_WAVE ? 4 * WAVE : BLOCK_THREADS; }
 int softmax_form_lanes(int form) { return form == SOFTMAX_WAVE ? WAVE : BLOCK_THREADS; }
 
+int64_t softmax_tile(int in_dtype, bool vec)
+{
+    return static_cast<int64_t>(BLOCK_THREADS) * ONLINE_CH * softmax_chunk_elems(in_dtype, vec);
+}
+
 hipError_t launch_softmax(const SoftmaxArgs &a, int in, int out, int form, int ch, bool vec,
-                          hipStream_t s)
+                          float *ws, hipStream_t s)
 {
     if (a.M <= 0 || a.N <= 0 || a.M > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     switch (in) {
-    case DTM_F32: return dispatch_out<DTM_F32>(a, out, form, ch, vec, s);
-    case DTM_F16: return dispatch_out<DTM_F16>(a, out, form, ch, vec, s);
-    case DTM_BF16: return dispatch_out<DTM_BF16>(a, out, form, ch, vec, s);
+    case DTM_F32: return dispatch_out<DTM_F32>(a, out, form, ch, vec, ws, s);
+    case DTM_F16: return dispatch_out<DTM_F16>(a, out, form, ch, vec, ws, s);
+    case DTM_BF16: return dispatch_out<DTM_BF16>(a, out, form, ch, vec, ws, s);
     }
     return hipErrorInvalidValue;
 }

@@ -11,6 +11,15 @@
 
 namespace {
 
+#ifndef DTM_SOFTMAX_SPLIT_MAX_ROWS
+#define DTM_SOFTMAX_SPLIT_MAX_ROWS 128
+#endif
+#ifndef DTM_SOFTMAX_SPLIT_WGS
+#define DTM_SOFTMAX_SPLIT_WGS 256
+#endif
+constexpr int64_t SPLIT_MAX_ROWS = DTM_SOFTMAX_SPLIT_MAX_ROWS;  // rows below which rows split
+constexpr int64_t SPLIT_WGS = DTM_SOFTMAX_SPLIT_WGS;            // workgroups a split aims for
+
 struct SCall {
     int64_t M, N;
     const void *X;
@@ -97,14 +106,34 @@ int make_plan(const SCall &c, dtm_softmax_plan *out)
         form = dtm::SOFTMAX_ONLINE;
         ch = 2;
     }
+    // Few rows that are long: split each row over several workgroups so the
+    // chip fills (about SPLIT_WGS workgroups, parts of at least one tile).
+    int64_t parts = 1;
+    if (form != dtm::SOFTMAX_WAVE && c.M < SPLIT_MAX_ROWS) {
+        const int64_t tile = dtm::softmax_tile(c.in, vec);
+        const int64_t want = dtm::cdiv(SPLIT_WGS, c.M), tiles = dtm::cdiv(c.N, tile);
+        parts = want < tiles ? want : tiles;
+        if (parts >= 2) {
+            // no empty part: part length rounded up to whole tiles
+            const int64_t len = dtm::cdiv(dtm::cdiv(c.N, parts), tile) * tile;
+            parts = dtm::cdiv(c.N, len);
+        }
+        if (parts >= 2) {
+            form = dtm::SOFTMAX_SPLIT;
+            ch = 2;
+        } else {
+            parts = 1;
+        }
+    }
     p.form = form;
     p.threads = dtm::softmax_form_threads(form);
     p.rows_per_block = form == dtm::SOFTMAX_WAVE ? p.threads / static_cast<int>(wave_lanes) : 1;
     p.chunks = ch;
     p.chunk_elems = static_cast<int32_t>(e);
     p.vectorized = vec ? 1 : 0;
-    p.grid = dtm::cdiv(c.M, p.rows_per_block);
-    p.passes = form == dtm::SOFTMAX_ONLINE ? 2 : 1;
+    p.grid = dtm::cdiv(c.M, p.rows_per_block) * parts;
+    p.passes = form == dtm::SOFTMAX_ONLINE || form == dtm::SOFTMAX_SPLIT ? 2 : 1;
+    p.parts = static_cast<int32_t>(parts);
     *out = p;
     return DTM_OK;
 }
@@ -135,8 +164,17 @@ int row_softmax(int64_t M, int64_t N, const void *X, int64_t stride_xm, int64_t 
     if (st != DTM_OK)
         return st;
     const dtm::SoftmaxArgs a{M, N, X, stride_xm, stride_xn, Y, stride_ym, stride_yn};
-    const hipError_t e = dtm::launch_softmax(a, in_dtype, out_dtype, p.form, p.chunks,
-                                             p.vectorized != 0, static_cast<hipStream_t>(stream));
+    float *ws = nullptr;
+    if (p.form == DTM_SOFTMAX_SPLIT) {
+        ws = static_cast<float *>(dtm::library_workspace(
+            stream, static_cast<uint64_t>(2 * sizeof(float)) * static_cast<uint64_t>(M) *
+                        static_cast<uint64_t>(p.parts)));
+        if (!ws)
+            return DTM_ERR_WORKSPACE;
+    }
+    const hipError_t e = dtm::launch_softmax(
+        a, in_dtype, out_dtype, p.form, p.form == DTM_SOFTMAX_SPLIT ? p.parts : p.chunks,
+        p.vectorized != 0, ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? DTM_OK : DTM_ERR_LAUNCH;
 }
 

@@ -18,15 +18,19 @@ struct SoftmaxArgs {
 };
 
 // Launch forms (see softmax.hip).
-enum { SOFTMAX_WAVE = 1, SOFTMAX_BLOCK = 2, SOFTMAX_ONLINE = 3 };
+enum { SOFTMAX_WAVE = 1, SOFTMAX_BLOCK = 2, SOFTMAX_ONLINE = 3, SOFTMAX_SPLIT = 4 };
 
 // Elements one chunk holds: 16 bytes of input when vectorised, else 1.
 int softmax_chunk_elems(int in_dtype, bool vec);
 // Threads per workgroup and threads per row of a form.
 int softmax_form_threads(int form);
 int softmax_form_lanes(int form);
-// `ch` chunks per thread: WAVE 1, 2, 4, 8, 16; BLOCK 1, 2, 4; ONLINE ignores it.
+// Columns one ONLINE/SPLIT tile covers (a SPLIT part is a multiple of it).
+int64_t softmax_tile(int in_dtype, bool vec);
+// `ch` chunks per thread: WAVE 1, 2, 4, 8, 16; BLOCK 1, 2, 4; ONLINE ignores
+// it; SPLIT: the number of parts per row, with `ws` holding 2 * M * parts
+// floats (device memory).
 hipError_t launch_softmax(const SoftmaxArgs &a, int in_dtype, int out_dtype, int form, int ch,
-                          bool vec, hipStream_t s);
+                          bool vec, float *ws, hipStream_t s);
 
 }  // namespace dtm

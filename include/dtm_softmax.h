@@ -31,7 +31,10 @@ typedef enum {
     DTM_SOFTMAX_NONE = 0,   /* nothing to launch (M == 0 or N == 0) */
     DTM_SOFTMAX_WAVE = 1,   /* one wave64 per row, 4 rows per workgroup, row in registers */
     DTM_SOFTMAX_BLOCK = 2,  /* one 1024-thread workgroup per row, row in registers */
-    DTM_SOFTMAX_ONLINE = 3  /* one workgroup per row, running max/sum pass then a write pass */
+    DTM_SOFTMAX_ONLINE = 3, /* one workgroup per row, running max/sum pass then a write pass */
+    DTM_SOFTMAX_SPLIT = 4   /* few long rows: each row cut into `parts` workgroups; a pass
+                               writing each part's max/sum to a small library-owned buffer,
+                               then a pass merging them in a fixed order and writing */
 } dtm_softmax_form;
 
 /* What row_softmax() would launch.  Produced on the host only. */
@@ -43,8 +46,8 @@ typedef struct {
     int32_t chunk_elems;    /* elements per chunk: 16 bytes of input when vectorized, else 1 */
     int32_t vectorized;     /* 1 when rows are unit-stride and 16-byte aligned (16-byte loads) */
     int64_t grid;           /* workgroups */
-    int32_t passes;         /* reads of X per element: 1, or 2 for ONLINE */
-    int32_t reserved;
+    int32_t passes;         /* reads of X per element: 1, or 2 for ONLINE and SPLIT */
+    int32_t parts;          /* SPLIT: workgroups per row (else 1) */
 } dtm_softmax_plan;
 
 /*
@@ -56,6 +59,9 @@ typedef struct {
  * Y may be exactly X (same pointer, strides and element size: in place);
  *   any other overlap of their byte ranges is DTM_ERR_ALIAS.
  * in_dtype, out_dtype: dtm_dtype of X and Y.  stream: hipStream_t or NULL.
+ * The SPLIT form uses 8*M*parts bytes of a per-(device, stream) buffer the
+ * library owns (the one GEMM split-K uses), grown on demand; a failed
+ * allocation returns DTM_ERR_WORKSPACE.
  * Every check runs before any launch; on error nothing is launched.
  * Returns a dtm_status.
  */

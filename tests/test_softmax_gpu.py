@@ -56,9 +56,9 @@ def run_softmax(p, out_dtype=None, layout="N", pad=0, plan=None, in_place=False)
 def _terms(plan, N):
     """Longest chain of fp32 additions/rescalings behind one row sum."""
     per_thread = plan["chunks"] * plan["chunk_elems"]
-    if plan["form_name"] == "online":
+    if plan["form_name"] in ("online", "split"):
         tiles = -(-N // (plan["threads"] * per_thread))
-        return tiles * (per_thread + 4) + 6 * 3 + 16 * 3
+        return tiles * (per_thread + 4) + 6 * 3 + 16 * 3 + 3 * plan.get("parts", 1)
     return per_thread + 6 + (16 if plan["form_name"] == "block" else 0)
 
 
@@ -73,7 +73,7 @@ def check(p, ybits, plan, out_dtype=None, label=""):
     nan = np.isnan(y64)
     assert (np.isnan(got) == nan).all(), f"{label}: NaN pattern differs"
     zero = (y64 == 0.0)
-    extra = 2.0 if plan["form_name"] == "online" else 1.0  # rescaled partial sums
+    extra = 2.0 if plan["form_name"] in ("online", "split") else 1.0  # rescaled partial sums
     tol = extra * oracle.softmax_tolerance(d, y64, _terms(plan, p.N))
     if od != "f32":
         tol = tol + half_ulp(y64, od)
@@ -178,6 +178,28 @@ def test_softmax_special_values():
         check(p, y, plan, label=f"special {N} {plan['form_name']}")
         got = oracle.decode(y, "f32")
         assert np.isnan(got[1:4]).all() and (got[5, :-1] == 0).all() and got[5, -1] == 1.0
+        assert untouched
+
+
+def test_softmax_split_form():
+    """Few long rows split over several workgroups: per-part (max, sum) pairs
+    merged in a fixed order, so results match the oracle and repeat bit for
+    bit; parts that are wholly -inf, and a row of -inf, behave as in the
+    other forms."""
+    for n, (M, N, dt) in enumerate([(2, 300001, "f32"), (64, 65536, "bf16"), (9, 131073, "f16")]):
+        p = W.softmax_problem(M, N, dt, dt, ("normal", 0.0, 3.0), seed=1010 + n,
+                              masked=0.02)
+        x = oracle.decode(p.X.logical_bits(), dt)
+        if n == 0:  # a whole part of row 0 masked, and row 1 all -inf
+            x[0, :100000] = -np.inf
+            x[1, :] = -np.inf
+            p = W.SoftmaxProblem(M, N, W.dense(W.to_bits(x, dt).reshape(M, N), dt), dt, dt)
+        plan = {}
+        y1, untouched = run_softmax(p, plan=plan)
+        assert plan["form_name"] == "split" and plan["parts"] > 1, plan
+        check(p, y1, plan, label=f"split {M}x{N} parts {plan['parts']}")
+        y2, _ = run_softmax(p)
+        assert (y1 == y2).all()
         assert untouched
 
 

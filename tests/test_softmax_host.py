@@ -32,7 +32,7 @@ def test_forms_by_row_length():
         (1024, 8192, BF16, "block", 1, 8, 1),   # fewer rows: a workgroup per row
         (256, 16384, F32, "block", 4, 4, 1),
         (256, 65536, F32, "online", 2, 4, 2),
-        (64, 2048, F32, "block", 1, 4, 1),   # few rows: a workgroup per row
+        (128, 2048, F32, "block", 1, 4, 1),  # few rows: a workgroup per row
         (64, 512, F32, "wave", 2, 4, 1),
     ]
     for M, N, ind, form, ch, e, passes in cases:
@@ -40,9 +40,28 @@ def test_forms_by_row_length():
         assert st == 0, (M, N)
         assert (p["form_name"], p["chunks"], p["chunk_elems"], p["passes"]) == \
             (form, ch, e, passes), (M, N, p)
-        assert p["vectorized"] == 1
+        assert p["vectorized"] == 1 and p["parts"] == 1
         assert p["grid"] == (-(-M // 4) if form == "wave" else M)
         assert p["threads"] == (256 if form == "wave" else 1024)
+
+
+def test_split_form_for_few_long_rows():
+    """Fewer than 128 rows that a wave cannot hold: each row is split over
+    about 256 / M workgroups, parts of whole tiles (2048 chunks), none
+    empty."""
+    for M, N, ind, parts in [(64, 262144, BF16, 4), (8, 1048576, F32, 32), (1, 100003, F32, 13),
+                             (100, 65536, F32, 3), (127, 16384, F32, 2), (64, 2048, F32, 1)]:
+        st, p = plan(M, N, ind=ind)
+        assert st == 0
+        e = 4 if ind == F32 else 8
+        tile = 1024 * 2 * e
+        assert p["parts"] == parts, (M, N, p)
+        if parts > 1:
+            assert p["form_name"] == "split" and p["passes"] == 2 and p["grid"] == M * parts
+            length = -(-(-(-N // parts)) // tile) * tile
+            assert (parts - 1) * length < N <= parts * length
+        else:
+            assert p["form_name"] != "split"
 
 
 def test_vectorization_conditions():
