@@ -189,6 +189,7 @@ def main():
         "config": {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "in_dtype": p.in_dtype,
                    "out_dtype": p.out_dtype, "kernel": plan["kernel_name"],
                    "tile": [plan["block_m"], plan["block_n"], plan["block_k"]],
+                   "threads": plan["threads"],
                    "grid": [plan["grid_m"], plan["grid_n"]]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
@@ -201,7 +202,8 @@ def main():
         secondary.append({"workload": q.name, "tflops_wall": round(qflops / (qwall * 1e-3) / 1e12, 2),
                           "tflops_kernel": round(qa, 2), "frac": round(qa / PEAK_TFLOPS[q.in_dtype], 4),
                           "kernel_ms": round(qkern, 4),
-                          "tile": [qplan["block_m"], qplan["block_n"], qplan["block_k"]]})
+                          "tile": [qplan["block_m"], qplan["block_n"], qplan["block_k"]],
+                          "threads": qplan["threads"]})
     if secondary:
         line["secondary"] = secondary
     if args.skinny and args.skinny != "none":

@@ -45,7 +45,7 @@ class TileConfig(ctypes.Structure):
 
     _fields_ = [("kernel", ctypes.c_int32), ("block_m", ctypes.c_int32),
                 ("block_n", ctypes.c_int32), ("block_k", ctypes.c_int32),
-                ("split_k", ctypes.c_int32)]
+                ("split_k", ctypes.c_int32), ("threads", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):

@@ -237,6 +237,16 @@ int64_t pick_split(const Call &c, int layout, int64_t tiles)
     return s;
 }
 
+// The pipelined kernel's interior form runs with 4 waves of 128 x 128 (one
+// per SIMD) when a launch has at least this many workgroups, i.e. at least
+// two per CU: each wave then reads a third less LDS per MFMA, and the chip,
+// which is power-limited on this kernel, clocks about 10% higher for a few
+// percent fewer busy MFMA cycles (bf16 8192^3: +1 to +3% by layout).  With
+// one workgroup per CU or fewer, the 8-wave form, whose two waves per SIMD
+// cover each other's waits, was as fast or faster (by up to 2%), and on the
+// range-checked form 8 waves were faster at every size measured.
+constexpr int64_t FOUR_WAVE_MIN_TILES = 512;
+
 int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
 {
     if (!out)
@@ -309,7 +319,7 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
                 return DTM_ERR_CONFIG;
             p.split_k = static_cast<int32_t>(forced_split);
         }
-        p.threads = p.block_k == 32 ? dtm::mfma16_dma_threads() : 256;
+        p.threads = p.block_k == 32 ? 512 : 256;  // the pipelined kernel's is settled below
         p.layout = layout;
     } else if (kernel == DTM_KERNEL_MFMA_F32) {
         if (!fast32)
@@ -340,8 +350,22 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
         return DTM_ERR_CONFIG;
     p.kernel = kernel;
     fill_grid(c, p);
-    if (kernel == DTM_KERNEL_MFMA_F16 && p.block_k == 32)  // which form of the pipelined kernel
+    const bool dma_tile = kernel == DTM_KERNEL_MFMA_F16 && p.block_k == 32;
+    if (dma_tile) {
+        // which form of the pipelined kernel, and how many waves
         p.ragged = dma_interior(c, layout, p.split_k) ? 0 : 1;
+        const int forced_threads = force ? force->threads : 0;
+        if (forced_threads) {
+            if (forced_threads % 64 || !dtm::mfma16_dma_waves_ok(forced_threads / 64, p.ragged))
+                return DTM_ERR_CONFIG;
+            p.threads = forced_threads;
+        } else {
+            p.threads = !p.ragged && p.grid_m * p.grid_n * p.split_k >= FOUR_WAVE_MIN_TILES ? 256
+                                                                                           : 512;
+        }
+    } else if (force && force->threads) {
+        return DTM_ERR_CONFIG;  // a workgroup size is chosen for the pipelined kernel only
+    }
     if (p.split_k > 1)
         p.workspace_bytes = static_cast<uint64_t>(p.split_k) * static_cast<uint64_t>(c.M) *
                             static_cast<uint64_t>(c.N) * sizeof(float);
@@ -390,14 +414,14 @@ int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t w
             }
             e = dtm::launch_mfma16_dma_partials(a, c.in, p.layout, p.split_k, p.ragged != 0,
                                                  a_view_bytes(c), b_view_bytes(c),
-                                                 static_cast<float *>(ws), s);
+                                                 p.threads / 64, static_cast<float *>(ws), s);
             if (e == hipSuccess)
                 e = dtm::launch_splitk_reduce(a, c.out, p.split_k, static_cast<float *>(ws), s);
         } else if (p.block_k == 32 && p.ragged)
             e = dtm::launch_mfma16_dma_ragged(a, c.in, c.out, p.layout, a_view_bytes(c),
                                               b_view_bytes(c), s);
         else if (p.block_k == 32)
-            e = dtm::launch_mfma16_dma(a, c.in, c.out, p.layout, s);
+            e = dtm::launch_mfma16_dma(a, c.in, c.out, p.layout, p.threads / 64, s);
         else
             e = dtm::launch_mfma16(a, c.in, c.out, p.block_m, p.block_n, p.block_k, p.layout,
                                    p.ragged != 0, s);

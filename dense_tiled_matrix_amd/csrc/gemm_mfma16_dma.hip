@@ -470,14 +470,11 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     }
 }
 
-#ifndef DTM_DMA_WAVES
-#define DTM_DMA_WAVES 8
-#endif
-
 struct DmaLaunch {
     int64_t splits;
     bool ragged;
     uint32_t a_bytes, b_bytes;
+    int waves;  // 8, or 4 for the interior form
 };
 
 // K elements per slice: K / splits for the interior form; for the RAGGED
@@ -491,15 +488,17 @@ template <int IN, int OUT, bool TA, bool TB>
 hipError_t launch(const GemmArgs &a, const DmaLaunch &l, hipStream_t s)
 {
     const int64_t gm = cdiv(a.M, BM), gn = cdiv(a.N, BN);
-    const dim3 grid((unsigned)(gm * gn * l.splits)), block(64 * DTM_DMA_WAVES);
+    const dim3 grid((unsigned)(gm * gn * l.splits)), block(64 * l.waves);
     const int64_t ks = slice_k(a.K, l.splits, l.ragged);
     if (l.ragged)
-        hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, DTM_DMA_WAVES, TA, TB, true>), grid,
-                           block, 0, s, a, gm, gn, l.splits, ks, a.M * a.N, l.a_bytes,
-                           l.b_bytes);
+        hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, 8, TA, TB, true>), grid, block, 0, s,
+                           a, gm, gn, l.splits, ks, a.M * a.N, l.a_bytes, l.b_bytes);
+    else if (l.waves == 4)
+        hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, 4, TA, TB, false>), grid, block, 0, s,
+                           a, gm, gn, l.splits, ks, a.M * a.N, 0u, 0u);
     else
-        hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, DTM_DMA_WAVES, TA, TB, false>), grid,
-                           block, 0, s, a, gm, gn, l.splits, ks, a.M * a.N, 0u, 0u);
+        hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, 8, TA, TB, false>), grid, block, 0, s,
+                           a, gm, gn, l.splits, ks, a.M * a.N, 0u, 0u);
     return hipGetLastError();
 }
 
@@ -557,13 +556,14 @@ bool mfma16_dma_ragged_fits(int64_t M, int64_t N, int64_t K, int layout, uint64_
            cdiv(M, BM) * cdiv(N, BN) * splits <= 0x7fffffffLL;
 }
 
-int mfma16_dma_threads() { return 64 * DTM_DMA_WAVES; }
+bool mfma16_dma_waves_ok(int waves, bool ragged) { return waves == 8 || (waves == 4 && !ragged); }
 
-hipError_t launch_mfma16_dma(const GemmArgs &a, int in, int out, int layout, hipStream_t s)
+hipError_t launch_mfma16_dma(const GemmArgs &a, int in, int out, int layout, int waves,
+                             hipStream_t s)
 {
-    if (!mfma16_dma_fits(a.M, a.N, a.K, 1))
+    if (!mfma16_dma_fits(a.M, a.N, a.K, 1) || !mfma16_dma_waves_ok(waves, false))
         return hipErrorInvalidConfiguration;
-    return dispatch_in(a, in, layout, out, DmaLaunch{1, false, 0u, 0u}, s);
+    return dispatch_in(a, in, layout, out, DmaLaunch{1, false, 0u, 0u, waves}, s);
 }
 
 hipError_t launch_mfma16_dma_ragged(const GemmArgs &a, int in, int out, int layout,
@@ -573,16 +573,18 @@ hipError_t launch_mfma16_dma_ragged(const GemmArgs &a, int in, int out, int layo
         return hipErrorInvalidConfiguration;
     return dispatch_in(a, in, layout, out,
                        DmaLaunch{1, true, static_cast<uint32_t>(a_bytes),
-                                 static_cast<uint32_t>(b_bytes)},
+                                 static_cast<uint32_t>(b_bytes), 8},
                        s);
 }
 
 hipError_t launch_mfma16_dma_partials(const GemmArgs &a, int in, int layout, int64_t splits,
-                                      bool ragged, uint64_t a_bytes, uint64_t b_bytes,
+                                      bool ragged, uint64_t a_bytes, uint64_t b_bytes, int waves,
                                       float *ws, hipStream_t s)
 {
     if (ragged ? !mfma16_dma_ragged_fits(a.M, a.N, a.K, layout, a_bytes, b_bytes, splits)
                : !mfma16_dma_fits(a.M, a.N, a.K, splits))
+        return hipErrorInvalidConfiguration;
+    if (!mfma16_dma_waves_ok(waves, ragged))
         return hipErrorInvalidConfiguration;
     GemmArgs w = a;
     w.C = ws;  // dense fp32 [splits][M][N]
@@ -590,7 +592,7 @@ hipError_t launch_mfma16_dma_partials(const GemmArgs &a, int in, int layout, int
     w.scn = 1;
     return dispatch_in(w, in, layout, DTM_F32,
                        DmaLaunch{splits, ragged, static_cast<uint32_t>(a_bytes),
-                                 static_cast<uint32_t>(b_bytes)},
+                                 static_cast<uint32_t>(b_bytes), waves},
                        s);
 }
 

@@ -108,6 +108,9 @@ typedef struct {
     int32_t block_n;
     int32_t block_k;
     int32_t split_k; /* number of K slices summed by a second pass; 0 or 1 = none */
+    int32_t threads; /* workgroup size of the 256 x 256 x 32 pipelined MFMA tile: 512
+                        (8 waves) or 256 (4 waves, not on its range-checked form); must
+                        be 0 for any other tile */
 } dtm_tile_config;
 
 /* What gemm() would launch for a problem.  Produced on the host only. */
@@ -159,7 +162,7 @@ int gemm_plan(int64_t M, int64_t N, int64_t K,
  * gemm_ex -- gemm() with a forced tile configuration and an optional
  * caller-owned workspace.
  * force: NULL or a dtm_tile_config whose non-zero fields override the
- *   selector (for example {DTM_KERNEL_GENERIC, 4, 4, 4, 0} runs 4x4x4 tiles).
+ *   selector (for example {DTM_KERNEL_GENERIC, 4, 4, 4, 0, 0} runs 4x4x4 tiles).
  *   A configuration the library does not have, or an MFMA kernel for a
  *   layout it cannot serve, gives DTM_ERR_CONFIG.
  * workspace, workspace_bytes: device memory of at least plan.workspace_bytes

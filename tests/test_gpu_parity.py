@@ -235,7 +235,7 @@ def _sample_rows_cols(M, N, tile, per_tile=1, seed=0):
     return rows, cols
 
 
-def _big_check(p, tile):
+def _big_check(p, tile, threads=None):
     """Full-size run in the launch configuration the bench times, checked on
     sampled rows and columns covering every output tile, plus a Freivalds
     probe of the whole result."""
@@ -246,6 +246,7 @@ def _big_check(p, tile):
     b = sb.view(TD[p.in_dtype]).view(p.K, p.N)
     plan = dtm.gemm_plan(a, b, out_dtype=TD[p.out_dtype])
     assert plan["kernel_name"] == "mfma_f16" and plan["block_m"] == tile, plan
+    assert threads is None or plan["threads"] == threads, plan
     c = dtm.gemm(a, b, out_dtype=TD[p.out_dtype])
     torch.cuda.synchronize()
     cb = c.view(torch.int32 if p.out_dtype == "f32" else torch.int16).cpu().numpy()
@@ -279,11 +280,11 @@ def _big_check(p, tile):
 
 
 def test_f16_4096_f32out():
-    _big_check(W.workload("f16_4096_f32out"), 256)
+    _big_check(W.workload("f16_4096_f32out"), 256, threads=512)
 
 
 def test_bf16_8192_bf16out():
-    _big_check(W.workload("bf16_8192_bf16out"), 256)
+    _big_check(W.workload("bf16_8192_bf16out"), 256, threads=256)
 
 
 def test_f16_skinny_long_k():
@@ -363,25 +364,30 @@ def test_mfma_pipelined_exact(ind):
         assert untouched
 
 
-@pytest.mark.parametrize("layout", ["TN", "NT", "TT"])
+@pytest.mark.parametrize("threads", [512, 256])
+@pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])
 @pytest.mark.parametrize("ind", ["f16", "bf16"])
-def test_pipelined_layouts_exact(ind, layout):
-    """Transposed operands on the pipelined kernel (A M-contiguous and/or B
-    K-contiguous, staged as stored and read with transposing LDS reads):
-    pipeline depths 1, 3, 5 and many chunks, several grids, padded leading
-    dimensions, split-K; value-exact on integer-valued inputs."""
+def test_pipelined_layouts_exact(ind, layout, threads):
+    """Every operand layout on the pipelined kernel with 8 and with 4 waves
+    (A M-contiguous and/or B K-contiguous, staged as stored and read with
+    transposing LDS reads): pipeline depths 1, 3, 5 and many chunks, several
+    grids, padded leading dimensions, split-K; value-exact on integer-valued
+    inputs."""
     shapes = [(256, 256, 32, 1), (512, 256, 96, 1), (256, 768, 160, 1), (768, 512, 2048, 1),
               (512, 512, 4096, 8), (256, 256, 1024, 4)]
     for n, (M, N, K, S) in enumerate(shapes):
         outd = ["f32", "f16", "bf16"][n % 3]
         p = padded_int_problem(M, N, K, ind, outd, 8 if K <= 256 else 2, seed=600 + n,
                                extra=8 * (n % 2), a_layout=layout[0], b_layout=layout[1])
-        cfg = dict(kernel=MF16, block_m=256, block_n=256, block_k=32, split_k=S)
+        cfg = dict(kernel=MF16, block_m=256, block_n=256, block_k=32, split_k=S,
+                   threads=threads)
         plan = {}
         c, untouched = run(p, config=cfg, c_pad=4 if n % 2 else 0, plan=plan)
         assert plan["status"] == 0 and plan["block_k"] == 32, plan
         assert plan["layout"] == LAYOUT_BITS[layout] and plan["split_k"] == S, plan
-        compare(p, c, exact=True, label=f"pipelined {layout} {ind} {M}x{N}x{K} S{S}->{outd}")
+        assert plan["threads"] == threads and plan["ragged"] == 0, plan
+        compare(p, c, exact=True,
+                label=f"pipelined x{threads} {layout} {ind} {M}x{N}x{K} S{S}->{outd}")
         assert untouched
 
 
@@ -399,6 +405,22 @@ def test_pipelined_layouts_random(layout):
         err, tol = compare(p, c, label=f"{layout} {ind} 1024x768x1536")
         note(f"{layout} {ind}->{outd}: max err {err:.3e} tol {tol:.3e}")
         assert untouched
+
+
+@pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])
+def test_four_wave_selector_random(layout):
+    """512 output tiles: the selector's 4-wave form of the pipelined kernel,
+    N(0,1) bf16 in every layout, compared in full within the stated
+    tolerance."""
+    p = W.random_problem(4096, 8192, 256, "bf16", "bf16", ("normal", 0.0, 1.0), seed=720,
+                         a_layout=layout[0], b_layout=layout[1])
+    plan = {}
+    c, untouched = run(p, plan=plan)
+    assert (plan["block_k"], plan["threads"], plan["ragged"]) == (32, 256, 0), plan
+    assert plan["layout"] == LAYOUT_BITS[layout], plan
+    err, tol = compare(p, c, label=f"4 waves {layout} 4096x8192x256")
+    note(f"4 waves {layout}: max err {err:.3e} tol {tol:.3e}")
+    assert untouched
 
 
 def _round8(x):

@@ -297,6 +297,42 @@ def test_forced_configs():
         dtm.DTM_ERR_CONFIG
 
 
+def test_pipelined_wave_count():
+    """The pipelined tile runs 4 waves (256 threads) on its interior form
+    when a launch has at least 512 workgroups, else 8 (512 threads); a
+    forced size must be one the form has, and only that tile takes one."""
+    big = dict(A=1 << 40, B=2 << 40, C=3 << 40)
+    for (M, N, K, kw, threads) in [
+            (8192, 8192, 8192, dict(), 256),                       # 1024 tiles
+            (8192, 8192, 8192, dict(sam=1, sak=8192, sbk=1, sbn=8192), 256),
+            (4096, 8192, 64, dict(), 256),                         # 512 tiles
+            (4096, 7936, 64, dict(), 512),                         # 496 tiles
+            (4096, 4096, 4096, dict(), 512),                       # 256 tiles
+            (8000, 8000, 8000, dict(), 512),                       # range-checked form
+            (512, 512, 65536, dict(), 512)]:                       # 4 tiles x 64 slices
+        st, p = plan(M, N, K, ind=BF16, outd=BF16, **big, **kw)
+        assert st == 0 and p["block_k"] == 32 and p["threads"] == threads, (M, N, K, kw, p)
+    dma = dict(kernel=dtm.DTM_KERNEL_MFMA_F16, block_m=256, block_n=256, block_k=32)
+    for t in (256, 512):
+        st, p = plan(512, 256, 96, config=dict(dma, threads=t))
+        assert st == 0 and p["threads"] == t and p["ragged"] == 0
+        st, p = plan(512, 256, 1024, config=dict(dma, threads=t, split_k=4))
+        assert st == 0 and p["threads"] == t and p["split_k"] == 4
+    st, p = plan(500, 256, 96, config=dict(dma, threads=512))
+    assert st == 0 and p["ragged"] == 1
+    # the range-checked form has 8 waves only
+    assert plan(500, 256, 96, config=dict(dma, threads=256))[0] == dtm.DTM_ERR_CONFIG
+    for t in (128, 320, 1024, 100):
+        assert plan(512, 256, 96, config=dict(dma, threads=t))[0] == dtm.DTM_ERR_CONFIG, t
+    assert plan(512, 256, 96, config=dict(kernel=dtm.DTM_KERNEL_MFMA_F16, block_m=256,
+                                          block_n=256, block_k=64, threads=256))[0] == \
+        dtm.DTM_ERR_CONFIG
+    # with the tile left to the selector, the size applies if it picks this tile
+    assert plan(64, 64, 64, config=dict(threads=512))[1]["threads"] == 512
+    assert plan(64, 64, 64, ind=F32, outd=F32, config=dict(threads=512))[0] == \
+        dtm.DTM_ERR_CONFIG
+
+
 def test_gemm_rejects_before_touching_a_device():
     """Argument errors come back from gemm() itself without any GPU."""
     assert dtm.gemm_raw(-1, 4, 4, PA, 4, 1, PB, 4, 1, PC, 4, 1, F32, F32) == \
