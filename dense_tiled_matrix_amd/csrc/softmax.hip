@@ -18,9 +18,11 @@
 // matters is that every row is read once, with 16-byte loads when the rows
 // are unit-stride and aligned, and that the reductions stay on chip:
 //  * WAVE form: one wave64 per row, four rows per workgroup; each lane holds
-//    CH chunks of E elements in registers (16-bit inputs stay packed, and
-//    the exponential is recomputed for the write rather than kept); max and
-//    sum are reduced across the wave with lane shuffles.
+//    CH chunks of E elements in registers (16-bit inputs stay packed; with
+//    up to 4 chunks the exponentials are kept for the write, with more they
+//    are recomputed from the packed input); max and sum are reduced across
+//    the wave with lane shuffles.  16-bit outputs are packed in pairs by the
+//    hardware conversions.
 //  * BLOCK form: one 1024-thread workgroup per row (rows too long for one
 //    wave); wave results are combined through LDS.
 //  * ONLINE form: rows too long for the workgroup's registers.  One pass
@@ -56,6 +58,9 @@ template <> struct Bytes<DTM_BF16> { static constexpr int value = 2; };
 template <int IN, bool VEC> constexpr int chunk_elems() { return VEC ? 16 / Bytes<IN>::value : 1; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // One chunk as loaded: E elements of the input dtype, packed.
 template <int IN, int E> struct Packed {
@@ -143,18 +148,17 @@ __device__ __forceinline__ void store_chunk(const SoftmaxArgs &p, int64_t row, i
                         u32x4{__float_as_uint(y[4 * h]), __float_as_uint(y[4 * h + 1]),
                               __float_as_uint(y[4 * h + 2]), __float_as_uint(y[4 * h + 3])};
             } else {
+                // pairs through the packed hardware conversions
+                // (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32: nearest-even, like
+                // store_elem, one instruction per two elements)
                 uint32_t w[E / 2];
 #pragma unroll
                 for (int h = 0; h < E / 2; ++h) {
-                    uint32_t lo, hi;
-                    if constexpr (OUT == DTM_F16) {
-                        lo = f32_to_f16_rne(y[2 * h]);
-                        hi = f32_to_f16_rne(y[2 * h + 1]);
-                    } else {
-                        lo = f32_to_bf16_rne(y[2 * h]);
-                        hi = f32_to_bf16_rne(y[2 * h + 1]);
-                    }
-                    w[h] = lo | (hi << 16);
+                    const f32x2 pair{y[2 * h], y[2 * h + 1]};
+                    if constexpr (OUT == DTM_F16)
+                        w[h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pair, f16x2));
+                    else
+                        w[h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pair, bf16x2));
                 }
                 if constexpr (E == 8) {
                     *reinterpret_cast<u32x4 *>(dst) = u32x4{w[0], w[1], w[2], w[3]};
@@ -199,6 +203,74 @@ __device__ __forceinline__ void merge_ms(float &m, float &s, float m2, float s2)
     s = a + b;
 }
 
+// The exponential is the costliest step per element (v_exp_f32 issues at a
+// quarter of the VALU rate).  With few chunks per lane the wave form keeps
+// exp(x - m) in registers for the write; with more, the registers that
+// would take cost more in occupancy than the second exponential costs
+// (measured: 16-chunk fp32 and fp16 rows 12-13% slower when kept; 1-chunk
+// bf16 rows 11% faster), so the write recomputes it from the packed input.
+constexpr int KEEP_EXP_MAX_CH = 4;
+
+// exp(x - m) of every element a thread holds, kept for the write, and their
+// sum.  Slots past N get 0.  `col_of(q)`: first column of chunk q.
+template <int IN, int E, int CH, typename ColOf>
+__device__ __forceinline__ float exps_and_sum(const Packed<IN, E> (&x)[CH], float m, int64_t N,
+                                              ColOf col_of, float (&ex)[CH][E])
+{
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+        const int64_t col = col_of(q);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            ex[q][e] = col + e < N ? exp_shifted(x[q].get(e) - m) : 0.0f;
+            s += ex[q][e];
+        }
+    }
+    return s;
+}
+
+// Sum of exp(x - m) over the elements a thread holds (columns < N).
+template <int IN, int E, int CH, typename ColOf>
+__device__ __forceinline__ float exp_sum(const Packed<IN, E> (&x)[CH], float m, int64_t N,
+                                         ColOf col_of)
+{
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+        const int64_t col = col_of(q);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (col + e < N)
+                s += exp_shifted(x[q].get(e) - m);
+    }
+    return s;
+}
+
+// Writes exp(x - m) * r for chunk x (the exponential computed again).
+template <int OUT, bool VEC, int IN, int E>
+__device__ __forceinline__ void store_recomputed(const SoftmaxArgs &p, int64_t row, int64_t col,
+                                                 const Packed<IN, E> &x, float m, float r)
+{
+    float y[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        y[e] = exp_shifted(x.get(e) - m) * r;
+    store_chunk<OUT, VEC, E>(p, row, col, y);
+}
+
+// Writes chunk `ex` times r.
+template <int OUT, bool VEC, int E>
+__device__ __forceinline__ void store_scaled(const SoftmaxArgs &p, int64_t row, int64_t col,
+                                             const float (&ex)[E], float r)
+{
+    float y[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        y[e] = ex[e] * r;
+    store_chunk<OUT, VEC, E>(p, row, col, y);
+}
+
 // ---- WAVE form ---------------------------------------------------------------
 
 template <int IN, int OUT, int CH, bool VEC>
@@ -223,25 +295,19 @@ __global__ __launch_bounds__(4 * WAVE) void softmax_wave_kernel(SoftmaxArgs p)
     }
     m = wave_max(m);
     keep_packed(x);
-    float s = 0.0f;
+    auto col_of = [&](int q) { return (static_cast<int64_t>(q) * WAVE + lane) * E; };
+    if constexpr (CH <= KEEP_EXP_MAX_CH) {
+        float ex[CH][E];
+        const float r = 1.0f / wave_sum(exps_and_sum<IN, E, CH>(x, m, p.N, col_of, ex));
 #pragma unroll
-    for (int q = 0; q < CH; ++q) {
-        const int64_t col = (static_cast<int64_t>(q) * WAVE + lane) * E;
+        for (int q = 0; q < CH; ++q)
+            store_scaled<OUT, VEC, E>(p, row, col_of(q), ex[q], r);
+    } else {
+        const float r = 1.0f / wave_sum(exp_sum<IN, E, CH>(x, m, p.N, col_of));
+        keep_packed(x);
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-            if (col + e < p.N)
-                s += exp_shifted(x[q].get(e) - m);
-    }
-    const float r = 1.0f / wave_sum(s);
-    keep_packed(x);
-#pragma unroll
-    for (int q = 0; q < CH; ++q) {
-        const int64_t col = (static_cast<int64_t>(q) * WAVE + lane) * E;
-        float y[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            y[e] = exp_shifted(x[q].get(e) - m) * r;
-        store_chunk<OUT, VEC, E>(p, row, col, y);
+        for (int q = 0; q < CH; ++q)
+            store_recomputed<OUT, VEC, IN, E>(p, row, col_of(q), x[q], m, r);
     }
 }
 
@@ -286,26 +352,12 @@ __global__ __launch_bounds__(BLOCK_THREADS) void softmax_block_kernel(SoftmaxArg
     }
     m = block_reduce<true>(m, red);
     keep_packed(x);
-    float s = 0.0f;
-#pragma unroll
-    for (int q = 0; q < CH; ++q) {
-        const int64_t col = (static_cast<int64_t>(q) * BLOCK_THREADS + t) * E;
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            if (col + e < p.N)
-                s += exp_shifted(x[q].get(e) - m);
-    }
-    const float r = 1.0f / block_reduce<false>(s, red);
+    auto col_of = [&](int q) { return (static_cast<int64_t>(q) * BLOCK_THREADS + t) * E; };
+    const float r = 1.0f / block_reduce<false>(exp_sum<IN, E, CH>(x, m, p.N, col_of), red);
     keep_packed(x);
 #pragma unroll
-    for (int q = 0; q < CH; ++q) {
-        const int64_t col = (static_cast<int64_t>(q) * BLOCK_THREADS + t) * E;
-        float y[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            y[e] = exp_shifted(x[q].get(e) - m) * r;
-        store_chunk<OUT, VEC, E>(p, row, col, y);
-    }
+    for (int q = 0; q < CH; ++q)
+        store_recomputed<OUT, VEC, IN, E>(p, row, col_of(q), x[q], m, r);
 }
 
 // ONLINE and SPLIT work in tiles of BLOCK_THREADS x ONLINE_CH chunks.
