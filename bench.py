@@ -10,7 +10,8 @@ kernel runs on), and the CPU oracle timed on a bounded sample of the same
 workload on this host.  The row-softmax workloads (the second, HBM-bound
 operation) are timed the same way and reported under "softmax" in GB/s of
 algorithmic traffic (X read once, Y written once) against the 8 TB/s HBM
-peak.
+peak, back to back (operands may partly stay in the 256 MB Infinity Cache)
+and cold (each call after reading 1 GiB of other data).
 """
 from __future__ import annotations
 
@@ -115,6 +116,24 @@ def cpu_baseline(p, target_s: float):
                       f"{t:.1f} s wall incl. decoding the operands to fp64"}
 
 
+def time_cold(torch, fn, n, flush):
+    """Median ms of one call of fn, each after reading `flush` (1 GiB, four
+    times the Infinity Cache), so its operands come from HBM, not from L2 or
+    the Infinity Cache; only the call is inside the events."""
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(n):
+        flush.sum()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return sorted(times)[len(times) // 2]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,7 +148,7 @@ def main():
         help="comma-separated row-softmax workloads also timed (HBM-bound; 'none' to skip)")
     ap.add_argument("--skinny", default="f16_skinny512x512x65536_f32out",
                     help="long-K workload timed warm and cold (its inputs fit the 256 MB "
-                         "Infinity Cache, so cold runs overwrite 1 GiB between calls); "
+                         "Infinity Cache, so cold runs read 1 GiB between calls); "
                          "'none' to skip")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -206,6 +225,8 @@ def main():
                           "threads": qplan["threads"]})
     if secondary:
         line["secondary"] = secondary
+    # read (not written) between cold calls, so the caches hold clean lines
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
     if args.skinny and args.skinny != "none":
         q = W.workload(args.skinny)
         a = to_device(q.A, TD[q.in_dtype], torch)
@@ -213,19 +234,9 @@ def main():
         c = torch.empty(q.M, q.N, dtype=TD[q.out_dtype], device="cuda:0")
         qplan = dtm.gemm_plan(a, b, out=c)
         _, warm_ms = time_gemm(dtm, torch, a, b, c, args.steps, args.warmup)
-        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
         stream = torch.cuda.current_stream()
-        cold = []
-        for _ in range(min(args.steps, 20)):
-            flush.fill_(1.0)  # evicts the inputs from the caches, outside the events
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            dtm.gemm(a, b, out=c, stream=stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            cold.append(e0.elapsed_time(e1))
-        cold_ms = sorted(cold)[len(cold) // 2]
+        cold_ms = time_cold(torch, lambda: dtm.gemm(a, b, out=c, stream=stream),
+                            min(args.steps, 20), flush)
         # algorithmic bytes: A and B read once, C written once
         alg = (q.M * q.K + q.K * q.N) * a.element_size() + q.M * q.N * c.element_size()
         qflops = 2.0 * q.M * q.N * q.K
@@ -236,7 +247,7 @@ def main():
                           "bytes": alg, "hbm_roofline_us": round(alg / (PEAK_HBM_GBS * 1e3), 2),
                           "cold_frac_of_hbm_roofline": round(alg / (PEAK_HBM_GBS * 1e3) /
                                                              (cold_ms * 1e3), 4)}
-        del a, b, c, flush
+        del a, b, c
     softmax = []
     for name in [s for s in args.softmax.split(",") if s and s != "none"]:
         q = W.softmax_workload(name)
@@ -255,14 +266,26 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         kern_ms = e0.elapsed_time(e1) / args.steps
+        cold_ms = time_cold(torch, lambda: dtm.row_softmax(x, out=y, stream=stream),
+                            min(args.steps, 20), flush)
+        # context: a plain device copy of the same bytes (X read, Y written),
+        # cold the same way -- what this traffic pattern reaches on this part
+        ysame = torch.empty_like(x)
+        copy_ms = time_cold(torch, lambda: ysame.copy_(x), min(args.steps, 20), flush)
+        copy_bytes = 2 * q.M * q.N * x.element_size()
         # algorithmic bytes: X read once, Y written once
         alg = q.M * q.N * (x.element_size() + y.element_size())
         gbs = alg / (kern_ms * 1e-3) / 1e9
+        gbs_cold = alg / (cold_ms * 1e-3) / 1e9
         softmax.append({"workload": q.name, "form": splan["form_name"],
                         "chunks": splan["chunks"], "kernel_us": round(kern_ms * 1e3, 2),
                         "bytes": alg, "gb_s": round(gbs, 1), "peak_gb_s": PEAK_HBM_GBS,
-                        "frac": round(gbs / PEAK_HBM_GBS, 4)})
-        del x, y
+                        "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "kernel_us_cold": round(cold_ms * 1e3, 2),
+                        "gb_s_cold": round(gbs_cold, 1),
+                        "frac_cold": round(gbs_cold / PEAK_HBM_GBS, 4),
+                        "copy_gb_s_cold": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1)})
+        del x, y, ysame
     if softmax:
         line["softmax"] = softmax
     line["cpu_baseline"] = None if args.no_cpu else cpu_baseline(p, args.cpu_seconds)

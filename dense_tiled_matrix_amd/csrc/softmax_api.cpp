@@ -11,6 +11,9 @@
 
 namespace {
 
+#ifndef DTM_SOFTMAX_WAVE_MIN_ROWS
+#define DTM_SOFTMAX_WAVE_MIN_ROWS 2048
+#endif
 #ifndef DTM_SOFTMAX_SPLIT_MAX_ROWS
 #define DTM_SOFTMAX_SPLIT_MAX_ROWS 128
 #endif
@@ -92,7 +95,7 @@ int make_plan(const SCall &c, dtm_softmax_plan *out)
     // A wave per row while a row fits in a wave's registers (16 chunks per
     // lane) and there are enough rows to fill the chip; a workgroup per row
     // up to 4 chunks per thread; beyond that the two-pass online form.
-    const bool many_rows = c.M >= 2048;
+    const bool many_rows = c.M >= DTM_SOFTMAX_WAVE_MIN_ROWS;
     int form, ch = 0;
     if (c.N <= wave_lanes * e * 16 && (many_rows || c.N <= wave_lanes * e * 2)) {
         form = dtm::SOFTMAX_WAVE;

@@ -1,11 +1,15 @@
 """Summaries of rocprofv3 CSV output for the GEMM kernels.
 
     python -m dense_tiled_matrix_amd.profiling stats  <kernel_stats.csv>
+    python -m dense_tiled_matrix_amd.profiling trace  <kernel_trace.csv>
     python -m dense_tiled_matrix_amd.profiling pmc    <counter_collection.csv> [...]
     python -m dense_tiled_matrix_amd.profiling traffic --fetch F.csv --write W.csv \
         --copy-mib 512 --workload NAME --kernel-substr S --source-hash H
 
 ``stats`` prints the per-kernel table of a ``--kernel-trace --stats`` run;
+``trace`` prints the same from its kernel_trace.csv per kernel and launch
+shape (grid and workgroup size), splitting a group whose durations fall in
+two clusters (one kernel launched on two workloads of the same shape);
 ``pmc`` prints per-kernel means of the counters of ``--pmc`` runs (with the
 shader clock derived from GRBM_GUI_ACTIVE, which counts shader-clock cycles
 per XCD, over the dispatch's own duration); ``traffic`` turns a FETCH_SIZE
@@ -38,6 +42,34 @@ def stats(path: str) -> str:
         out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                    f"{float(r['Percentage']):.1f}% |")
+    return "\n".join(out)
+
+
+def _clusters(durs):
+    """Sorted durations, split once at the widest ratio gap if it exceeds 1.5x."""
+    d = sorted(durs)
+    if len(d) < 2:
+        return [d]
+    i = max(range(1, len(d)), key=lambda k: d[k] / max(d[k - 1], 1))
+    return [d[:i], d[i:]] if d[i] / max(d[i - 1], 1) > 1.5 else [d]
+
+
+def trace(path: str) -> str:
+    groups = collections.OrderedDict()
+    for r in csv.DictReader(open(path)):
+        key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    total = sum(sum(v) for v in groups.values())
+    rows = []
+    for (name, grid, wg), durs in groups.items():
+        for c in _clusters(durs):
+            rows.append((sum(c), name, grid // wg, wg, c))
+    out = ["| kernel | workgroups x threads | calls | average (us) | median (us) | min (us) | "
+           "max (us) | share |", "|---|---|---|---|---|---|---|---|"]
+    for tot, name, wgs, wg, c in sorted(rows, key=lambda x: -x[0]):
+        out.append(f"| `{name}` | {wgs} x {wg} | {len(c)} | {tot / len(c) / 1e3:.1f} | "
+                   f"{c[len(c) // 2] / 1e3:.1f} | {c[0] / 1e3:.1f} | {c[-1] / 1e3:.1f} | "
+                   f"{100 * tot / total:.1f}% |")
     return "\n".join(out)
 
 
@@ -80,17 +112,22 @@ def pmc(paths) -> str:
     return "\n".join(out)
 
 
-def _mean_kib(path, substr):
+def _mean_kib(path, substr, largest_only=False):
+    """Mean FETCH_SIZE or WRITE_SIZE of the dispatches whose name holds
+    `substr`; with largest_only, of those within half of the largest value
+    (the calibration copies, not smaller copies the same run makes)."""
     vals = [rec for rec in _dispatches([path]) if substr in rec["name"]]
     key = "FETCH_SIZE" if any("FETCH_SIZE" in r for r in vals) else "WRITE_SIZE"
     xs = [r[key] for r in vals if key in r]
+    if largest_only:
+        xs = [x for x in xs if x >= 0.5 * max(xs)]
     return sum(xs) / len(xs), key
 
 
 def traffic(fetch_csv, write_csv, copy_mib, workload, kernel_substr, source_hash):
     """HBM bytes per launch of the kernel, scaled by the copy calibration."""
-    copy_fetch, _ = _mean_kib(fetch_csv, "copyBuffer")
-    copy_write, _ = _mean_kib(write_csv, "copyBuffer")
+    copy_fetch, _ = _mean_kib(fetch_csv, "copyBuffer", largest_only=True)
+    copy_write, _ = _mean_kib(write_csv, "copyBuffer", largest_only=True)
     k_fetch, _ = _mean_kib(fetch_csv, kernel_substr)
     k_write, _ = _mean_kib(write_csv, kernel_substr)
     true_kib = copy_mib * 1024.0
@@ -115,6 +152,8 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("csv")
+    tr = sub.add_parser("trace")
+    tr.add_argument("csv")
     p = sub.add_parser("pmc")
     p.add_argument("csv", nargs="+")
     t = sub.add_parser("traffic")
@@ -127,6 +166,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats(a.csv))
+    elif a.cmd == "trace":
+        print(trace(a.csv))
     elif a.cmd == "pmc":
         print(pmc(a.csv))
     else:
