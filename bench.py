@@ -66,12 +66,25 @@ def to_device(op, torch_dtype, torch):
     return t.as_strided((op.rows, op.cols), (op.stride_r, op.stride_c), op.offset)
 
 
-def time_gemm(dtm, torch, a, b, c, steps, warmup):
+def warm_up(torch, fn, calls, min_seconds=0.0):
+    """`calls` untimed calls of fn, then more until `min_seconds` of wall time
+    have passed (a power-management transient follows a change of load: a
+    sustained bf16 8192^3 run slows by up to 35% over its first few calls and
+    settles after about 50, i.e. ~45 ms)."""
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        fn()
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < min_seconds:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_gemm(dtm, torch, a, b, c, steps, warmup, min_warm_s=0.0):
     """(wall ms per step, kernel ms per launch from HIP events) over `steps`."""
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        dtm.gemm(a, b, out=c, stream=stream)
-    torch.cuda.synchronize()
+    warm_up(torch, lambda: dtm.gemm(a, b, out=c, stream=stream), warmup, min_warm_s)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -82,6 +95,40 @@ def time_gemm(dtm, torch, a, b, c, steps, warmup):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     return wall_ms, start.elapsed_time(end) / steps
+
+
+def time_gemm_per_call(dtm, torch, a, b, c, steps):
+    """(median, min) ms of single calls, each bracketed by its own events."""
+    stream = torch.cuda.current_stream()
+    pairs = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dtm.gemm(a, b, out=c, stream=stream)
+        e1.record(stream)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in pairs)
+    return t[len(t) // 2], t[0]
+
+
+def host_us_per_call(dtm, torch, calls=500):
+    """Host time to validate, plan and enqueue one call through the Python
+    binding (a 256^3 bf16 problem; the calls are queued, not waited for)."""
+    a = torch.zeros(256, 256, dtype=torch.bfloat16, device="cuda:0")
+    b = torch.zeros(256, 256, dtype=torch.bfloat16, device="cuda:0")
+    c = torch.empty(256, 256, dtype=torch.bfloat16, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    for _ in range(20):
+        dtm.gemm(a, b, out=c, stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        dtm.gemm(a, b, out=c, stream=stream)
+    t = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    return t / calls * 1e6
 
 
 def cpu_baseline(p, target_s: float):
@@ -116,6 +163,59 @@ def cpu_baseline(p, target_s: float):
                       f"{t:.1f} s wall incl. decoding the operands to fp64"}
 
 
+def sustained_clocks(torch, fn, seconds=0.8, batch=20):
+    """Runs fn back to back for about `seconds` (batches of `batch` calls),
+    reading the GPU's own metrics table through amdsmi after each batch:
+    shader clock per XCD, memory clock, socket power and activity.  The
+    table refreshes only every few hundred milliseconds, hence a sustained
+    run of its own rather than a reading inside the short timed region.
+    Returns None when amdsmi or the device is unavailable."""
+    try:
+        import amdsmi
+
+        amdsmi.amdsmi_init()
+        prop = torch.cuda.get_device_properties(0)
+        want = (prop.pci_domain_id, prop.pci_bus_id, prop.pci_device_id)
+        handle = None
+        for h in amdsmi.amdsmi_get_processor_handles():
+            dom, bus, rest = amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")  # dddd:bb:dd.f
+            if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                handle = h
+        if handle is None:
+            return None
+    except Exception:
+        return None
+
+    def num(x):
+        return x if isinstance(x, (int, float)) else None
+
+    samples = []
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(batch):
+            fn()
+        torch.cuda.synchronize()
+        try:
+            m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+        except Exception:
+            return None
+        clks = [c for c in (m.get("current_gfxclks") or []) if num(c)]
+        samples.append({"sclk": sum(clks) / len(clks) if clks else None,
+                        "mclk": num(m.get("current_uclk")),
+                        "power": num(m.get("current_socket_power")),
+                        "activity": num(m.get("average_gfx_activity"))})
+    # readings taken under load (the table lags the start of the run)
+    busy = [r for r in samples if (r["activity"] or 0) >= 50] or samples
+
+    def mean(key):
+        xs = [r[key] for r in busy if r[key] is not None]
+        return round(sum(xs) / len(xs), 1) if xs else None
+
+    return {"readings_under_load": len(busy), "readings": len(samples),
+            "sclk_mhz_mean_over_xcds": mean("sclk"), "mclk_mhz": mean("mclk"),
+            "socket_power_w": mean("power"), "gfx_activity_pct": mean("activity")}
+
+
 def time_cold(torch, fn, n, flush):
     """Median ms of one call of fn, each after reading `flush` (1 GiB, four
     times the Infinity Cache), so its operands come from HBM, not from L2 or
@@ -138,9 +238,14 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed calls before each timed run (the chip's power management "
+                         "settles about 50 calls into a sustained bf16 8192^3 run)")
+    ap.add_argument("--extra-warmup-s", type=float, default=0.3,
+                    help="the workloads besides the headline are warmed for at least this "
+                         "many seconds of back-to-back calls as well as --warmup calls")
     ap.add_argument("--workload", default="bf16_8192_bf16out")
-    ap.add_argument("--secondary", default="f16_4096_f32out",
+    ap.add_argument("--secondary", default="f16_4096_f32out,f16_8192_f32out,bf16_4096_bf16out",
                     help="comma-separated workloads also timed (not the headline)")
     ap.add_argument("--softmax", default=",".join([
         "softmax_f32_4096x4096", "softmax_bf16_8192x8192_masked", "softmax_f16_32768x1024",
@@ -178,17 +283,23 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def measure(name):
+    clocks = None
+
+    def measure(name, sustain=False, min_warm_s=0.0):
+        nonlocal clocks
         p = W.workload(name)
         a = to_device(p.A, TD[p.in_dtype], torch)
         b = to_device(p.B, TD[p.in_dtype], torch)
         c = torch.empty(p.M, p.N, dtype=TD[p.out_dtype], device="cuda:0")
         plan = dtm.gemm_plan(a, b, out=c)
-        wall_ms, kern_ms = time_gemm(dtm, torch, a, b, c, args.steps, args.warmup)
+        wall_ms, kern_ms = time_gemm(dtm, torch, a, b, c, args.steps, args.warmup, min_warm_s)
+        med_ms, min_ms = time_gemm_per_call(dtm, torch, a, b, c, args.steps)
+        if sustain:  # after the timed calls: clocks and power under this load
+            clocks = sustained_clocks(torch, lambda: dtm.gemm(a, b, out=c))
         flops = 2.0 * p.M * p.N * p.K
-        return p, plan, wall_ms, kern_ms, flops
+        return p, plan, wall_ms, kern_ms, flops, (med_ms, min_ms)
 
-    p, plan, wall_ms, kern_ms, flops = measure(args.workload)
+    p, plan, wall_ms, kern_ms, flops, (med_ms, min_ms) = measure(args.workload, sustain=True)
     peak = PEAK_TFLOPS[p.in_dtype]
     achieved = flops / (kern_ms * 1e-3) / 1e12
     line = {
@@ -200,6 +311,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(wall_ms, 4),
         "host_overhead_us_per_call": round((wall_ms - kern_ms) * 1e3, 2),
+        "host_us_per_call": round(host_us_per_call(dtm, torch), 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -213,14 +325,16 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(p.name)},
+        "per_call_ms": {"median": round(med_ms, 4), "min": round(min_ms, 4)},
+        "clocks": clocks,
     }
     secondary = []
-    for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
-        q, qplan, qwall, qkern, qflops = measure(name)
+    for name in [s for s in args.secondary.split(",") if s and s not in (args.workload, "none")]:
+        q, qplan, qwall, qkern, qflops, (qmed, qmin) = measure(name, min_warm_s=args.extra_warmup_s)
         qa = qflops / (qkern * 1e-3) / 1e12
         secondary.append({"workload": q.name, "tflops_wall": round(qflops / (qwall * 1e-3) / 1e12, 2),
                           "tflops_kernel": round(qa, 2), "frac": round(qa / PEAK_TFLOPS[q.in_dtype], 4),
-                          "kernel_ms": round(qkern, 4),
+                          "kernel_ms": round(qkern, 4), "kernel_ms_median": round(qmed, 4),
                           "tile": [qplan["block_m"], qplan["block_n"], qplan["block_k"]],
                           "threads": qplan["threads"]})
     if secondary:
@@ -233,7 +347,7 @@ def main():
         b = to_device(q.B, TD[q.in_dtype], torch)
         c = torch.empty(q.M, q.N, dtype=TD[q.out_dtype], device="cuda:0")
         qplan = dtm.gemm_plan(a, b, out=c)
-        _, warm_ms = time_gemm(dtm, torch, a, b, c, args.steps, args.warmup)
+        _, warm_ms = time_gemm(dtm, torch, a, b, c, args.steps, args.warmup, args.extra_warmup_s)
         stream = torch.cuda.current_stream()
         cold_ms = time_cold(torch, lambda: dtm.gemm(a, b, out=c, stream=stream),
                             min(args.steps, 20), flush)
@@ -255,9 +369,8 @@ def main():
         y = torch.empty(q.M, q.N, dtype=TD[q.out_dtype], device="cuda:0")
         splan = dtm.row_softmax_plan(x, out=y)
         stream = torch.cuda.current_stream()
-        for _ in range(args.warmup):
-            dtm.row_softmax(x, out=y, stream=stream)
-        torch.cuda.synchronize()
+        warm_up(torch, lambda: dtm.row_softmax(x, out=y, stream=stream), args.warmup,
+                args.extra_warmup_s)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)

@@ -287,6 +287,16 @@ def test_bf16_8192_bf16out():
     _big_check(W.workload("bf16_8192_bf16out"), 256, threads=256)
 
 
+def test_f16_8192_f32out():
+    """Extra: fp16 8192^3 with fp32 output (the 4-wave form)."""
+    _big_check(W.workload("f16_8192_f32out"), 256, threads=256)
+
+
+def test_bf16_4096_bf16out():
+    """Extra: bf16 4096^3 with bf16 output (one tile per CU, 8 waves)."""
+    _big_check(W.workload("bf16_4096_bf16out"), 256, threads=512)
+
+
 def test_f16_skinny_long_k():
     """512x512x65536 fp16 U[0,1] -> fp32 through the selector's split-K plan
     (64 slices of 1024 on the pipelined kernel): full comparison, plus the

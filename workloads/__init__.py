@@ -128,7 +128,7 @@ def random_problem(M, N, K, in_dtype, out_dtype, dist, seed, a_layout="N", b_lay
     return Problem(M, N, K, A, B, in_dtype, out_dtype, name=name)
 
 
-# The five measured / checked workloads.  ``index`` is the seed base.
+# The measured / checked workloads.  ``index`` is the seed base.
 WORKLOADS = {
     "int8x8x8_f32": dict(index=0, M=8, N=8, K=8, in_dtype="f32", out_dtype="f32",
                          dist=("int", -4, 4), a_layout="N", b_layout="N"),
@@ -144,6 +144,13 @@ WORKLOADS = {
     "f16_skinny512x512x65536_f32out": dict(index=4, M=512, N=512, K=65536, in_dtype="f16",
                                            out_dtype="f32", dist=("uniform", 0.0, 1.0),
                                            a_layout="N", b_layout="N"),
+    # the two other size/dtype pairings of the measured shapes (extras)
+    "f16_8192_f32out": dict(index=5, M=8192, N=8192, K=8192, in_dtype="f16",
+                            out_dtype="f32", dist=("uniform", -1.0, 1.0),
+                            a_layout="N", b_layout="N"),
+    "bf16_4096_bf16out": dict(index=6, M=4096, N=4096, K=4096, in_dtype="bf16",
+                              out_dtype="bf16", dist=("normal", 0.0, 1.0),
+                              a_layout="N", b_layout="N"),
 }
 
 
