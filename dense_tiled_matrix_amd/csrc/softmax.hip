@@ -24,7 +24,8 @@
 //    the wave with lane shuffles.  16-bit outputs are packed in pairs by the
 //    hardware conversions.
 //  * BLOCK form: one 1024-thread workgroup per row (rows too long for one
-//    wave); wave results are combined through LDS.
+//    wave), up to 16 chunks per thread for fp32 rows (64 Ki elements) and 8
+//    for 16-bit ones; wave results are combined through LDS.
 //  * ONLINE form: rows too long for the workgroup's registers.  One pass
 //    keeps, per thread, a running max m and a sum s of exp(x - m), rescaling
 //    s by exp(m_old - m_new) when the max grows; the threads' (m, s) pairs
@@ -528,6 +529,15 @@ hipError_t launch_form(const SoftmaxArgs &a, int form, int ch, float *ws, hipStr
         case 1: hipLaunchKernelGGL((softmax_block_kernel<IN, OUT, 1, VEC>), grid, block, 0, s, a); break;
         case 2: hipLaunchKernelGGL((softmax_block_kernel<IN, OUT, 2, VEC>), grid, block, 0, s, a); break;
         case 4: hipLaunchKernelGGL((softmax_block_kernel<IN, OUT, 4, VEC>), grid, block, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((softmax_block_kernel<IN, OUT, 8, VEC>), grid, block, 0, s, a); break;
+        case 16:
+            // 16 chunks per thread: fp32 rows only (16-bit rows of that many
+            // chunks would not fit the 128 VGPRs a 1024-thread workgroup allows)
+            if constexpr (IN == DTM_F32) {
+                hipLaunchKernelGGL((softmax_block_kernel<IN, OUT, 16, VEC>), grid, block, 0, s, a);
+                break;
+            }
+            return hipErrorInvalidConfiguration;
         default: return hipErrorInvalidConfiguration;
         }
     } else if (form == SOFTMAX_ONLINE) {

@@ -14,12 +14,16 @@ namespace {
 #ifndef DTM_SOFTMAX_WAVE_MIN_ROWS
 #define DTM_SOFTMAX_WAVE_MIN_ROWS 2048
 #endif
+#ifndef DTM_SOFTMAX_BLOCK_MAX_CH
+#define DTM_SOFTMAX_BLOCK_MAX_CH 16
+#endif
 #ifndef DTM_SOFTMAX_SPLIT_MAX_ROWS
 #define DTM_SOFTMAX_SPLIT_MAX_ROWS 128
 #endif
 #ifndef DTM_SOFTMAX_SPLIT_WGS
 #define DTM_SOFTMAX_SPLIT_WGS 256
 #endif
+constexpr int64_t BLOCK_MAX_CH = DTM_SOFTMAX_BLOCK_MAX_CH;      // chunks per thread, fp32 rows
 constexpr int64_t SPLIT_MAX_ROWS = DTM_SOFTMAX_SPLIT_MAX_ROWS;  // rows below which rows split
 constexpr int64_t SPLIT_WGS = DTM_SOFTMAX_SPLIT_WGS;            // workgroups a split aims for
 
@@ -73,6 +77,21 @@ bool vectorizable(const SCall &c)
     return true;
 }
 
+// Past 4 chunks per thread the BLOCK form's workgroup fills a CU's
+// registers; it then pays against the ONLINE form (which reads each row
+// twice) only when the row fills at least 3/4 of the chunks it is given
+// (measured: rows of 40000 fp32, 61% of 16 chunks, 4-8% slower than ONLINE;
+// rows that fill 76-100% of 8 or 16 chunks 2-27% faster).
+bool block_fill_pays(int64_t N, int64_t chunk_row)
+{
+    if (N <= chunk_row * 4)
+        return true;
+    int64_t ch = 1;
+    while (chunk_row * ch < N)
+        ch *= 2;
+    return 4 * N >= 3 * chunk_row * ch;
+}
+
 int make_plan(const SCall &c, dtm_softmax_plan *out)
 {
     if (!out)
@@ -94,14 +113,17 @@ int make_plan(const SCall &c, dtm_softmax_plan *out)
     const int64_t block_lanes = dtm::softmax_form_lanes(dtm::SOFTMAX_BLOCK);
     // A wave per row while a row fits in a wave's registers (16 chunks per
     // lane) and there are enough rows to fill the chip; a workgroup per row
-    // up to 4 chunks per thread; beyond that the two-pass online form.
+    // while it fits in the workgroup's registers (16 chunks per thread for
+    // fp32, 8 for 16-bit inputs, whose 16 would not fit the 128 VGPRs of a
+    // 1024-thread workgroup); beyond that the two-pass online form.
     const bool many_rows = c.M >= DTM_SOFTMAX_WAVE_MIN_ROWS;
+    const int64_t block_max_ch = c.in == DTM_F32 ? BLOCK_MAX_CH : (BLOCK_MAX_CH < 8 ? BLOCK_MAX_CH : 8);
     int form, ch = 0;
     if (c.N <= wave_lanes * e * 16 && (many_rows || c.N <= wave_lanes * e * 2)) {
         form = dtm::SOFTMAX_WAVE;
         for (ch = 1; wave_lanes * e * ch < c.N; ch *= 2) {
         }
-    } else if (c.N <= block_lanes * e * 4) {
+    } else if (c.N <= block_lanes * e * block_max_ch && block_fill_pays(c.N, block_lanes * e)) {
         form = dtm::SOFTMAX_BLOCK;
         for (ch = 1; block_lanes * e * ch < c.N; ch *= 2) {
         }

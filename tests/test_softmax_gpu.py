@@ -122,6 +122,23 @@ def test_softmax_row_length_sweep(ind, outd):
         assert untouched
 
 
+def test_softmax_block_form_many_chunks():
+    """Rows held whole in a 1024-thread workgroup's registers: 8 and 16 chunks
+    per thread (fp32), 8 (16-bit), ragged lengths, -inf masks, an
+    element-wise (transposed) view, in and out of every dtype."""
+    cases = [(256, 65536, "f32", "f32", "N"), (300, 65532, "f32", "bf16", "N"),
+             (257, 30004, "f32", "f32", "N"), (260, 60000, "bf16", "bf16", "N"),
+             (256, 49160, "f16", "f32", "N"), (300, 13000, "f32", "f16", "T")]
+    for n, (M, N, ind, outd, layout) in enumerate(cases):
+        p = W.softmax_problem(M, N, ind, outd, ("normal", 0.0, 3.0), seed=1050 + n,
+                              layout=layout, masked=0.05 if n % 2 else 0.0)
+        plan = {}
+        y, untouched = run_softmax(p, plan=plan)
+        assert plan["form_name"] == "block" and plan["chunks"] in (8, 16), (M, N, plan)
+        check(p, y, plan, label=f"block x{plan['chunks']} {ind}->{outd} {M}x{N}")
+        assert untouched
+
+
 def test_softmax_many_rows_wave_form():
     """Many short rows so the wave form runs with several chunk counts."""
     for n, N in enumerate([100, 512, 1024, 2048, 4096]):

@@ -21,8 +21,10 @@ def test_symbols_exported():
 
 def test_forms_by_row_length():
     """A wave per row while the row fits in a wave's registers (16 chunks per
-    lane) and rows are many; a workgroup per row up to 4 chunks per thread; beyond that the
-    two-pass online form.  16-byte chunks: 4 fp32 or 8 fp16/bf16 elements."""
+    lane) and rows are many; a workgroup per row up to 16 chunks per thread
+    for fp32 rows, 8 for 16-bit ones, past 4 only when the row fills at
+    least 3/4 of its chunks; beyond that the two-pass online form.  16-byte
+    chunks: 4 fp32 or 8 fp16/bf16 elements."""
     cases = [
         (32768, 1024, F16, "wave", 2, 8, 1),
         (32768, 4096, F16, "wave", 8, 8, 1),
@@ -31,7 +33,15 @@ def test_forms_by_row_length():
         (8192, 8192, BF16, "wave", 16, 8, 1),
         (1024, 8192, BF16, "block", 1, 8, 1),   # fewer rows: a workgroup per row
         (256, 16384, F32, "block", 4, 4, 1),
-        (256, 65536, F32, "online", 2, 4, 2),
+        (256, 65536, F32, "block", 16, 4, 1),
+        (256, 49152, F32, "block", 16, 4, 1),  # 75% of 16 chunks
+        (256, 49148, F32, "online", 2, 4, 2),
+        (256, 40000, F32, "online", 2, 4, 2),
+        (300, 60000, BF16, "block", 8, 8, 1),
+        (300, 65544, BF16, "online", 2, 8, 2),  # 16-bit rows: at most 8 chunks
+        (256, 16388, F32, "online", 2, 4, 2),   # 50% of 8 chunks
+        (256, 24576, F32, "block", 8, 4, 1),
+        (256, 65540, F32, "online", 2, 4, 2),
         (128, 2048, F32, "block", 1, 4, 1),  # few rows: a workgroup per row
         (64, 512, F32, "wave", 2, 4, 1),
     ]
