@@ -206,33 +206,43 @@ void pick_generic(const Call &c, dtm_plan &p)
     p.block_k = pick->bk;
 }
 
-// Whether the 256 x 256 x 32 pipelined kernel can run a problem with K in
-// `splits` slices: its interior form (M, N multiples of 256, K of 32 *
-// splits) or its range-checked form.
-bool dma_interior(const Call &c, int layout, int64_t splits)
+// Whether the tile x tile x 32 pipelined kernel (tile 256 or 128) can run a
+// problem with K in `splits` slices: its interior form (M, N multiples of
+// the tile, K of 32 * splits) or its range-checked form.
+bool dma_interior(const Call &c, int layout, int64_t splits, int tile = 256)
 {
-    return is16(c) && layout >= 0 && dtm::mfma16_dma_fits(c.M, c.N, c.K, splits);
+    return is16(c) && layout >= 0 && dtm::mfma16_dma_fits(c.M, c.N, c.K, splits, tile);
 }
-bool dma_ranged(const Call &c, int layout, int64_t splits)
+bool dma_ranged(const Call &c, int layout, int64_t splits, int tile = 256)
 {
     return is16(c) && layout >= 0 &&
            dtm::mfma16_dma_ragged_fits(c.M, c.N, c.K, layout, a_view_bytes(c), b_view_bytes(c),
-                                       splits);
+                                       splits, tile);
 }
-bool dma_any(const Call &c, int layout, int64_t splits)
+bool dma_any(const Call &c, int layout, int64_t splits, int tile = 256)
 {
-    return dma_interior(c, layout, splits) || dma_ranged(c, layout, splits);
+    return dma_interior(c, layout, splits, tile) || dma_ranged(c, layout, splits, tile);
 }
+bool is_dma_tile(int bm, int bn, int bk) { return bm == bn && (bm == 256 || bm == 128) && bk == 32; }
 
-// Split-K for problems with too few 256 x 256 tiles to fill the chip and a
-// long K: the largest power-of-two split that keeps tiles x split within 256
-// workgroups and slices of at least 512 (16 pipelined chunks).
-int64_t pick_split(const Call &c, int layout, int64_t tiles)
+// Tile of the pipelined kernel: 256 x 256 while there are more than
+// SMALL_TILE_MAX such tiles, else 128 x 128 (four times the workgroups).
+// Measured side by side (bf16 unless noted, TFLOP/s, 256 -> 128): 2048^3
+// 419 -> 675 (256 was split 4 ways), 2560^3 668 -> 749, 1024x4096x4096
+// 644 -> 801, 8192x1024x8192 (128 tiles of 256) 897 -> 967; and back the
+// other way at 144 tiles of 256 (3072^3 881 vs 763, ragged 3000^3 780 vs
+// 577) and at 256 (4096x4096x1024 964 vs 771).
+constexpr int64_t SMALL_TILE_MAX = 128;
+
+// Split-K for problems whose 128 x 128 tiles still cannot fill the chip and
+// whose K is long: the largest power-of-two split that keeps tiles x split
+// within 256 workgroups and slices of at least 2048 (64 pipelined chunks).
+// Measured (128 tiles): 1024x1024x8192 S=1 303, S=4 630, S=8 562;
+// 512x512x65536 fp16 S=8 528, S=16 736; 1024^3 S=1 183, S=2 133.
+int64_t pick_split(const Call &c, int layout, int64_t tiles, int tile)
 {
     int64_t s = 1;
-    if (tiles >= 128)
-        return 1;
-    while (tiles * s * 2 <= 256 && c.K / (s * 2) >= 512 && dma_any(c, layout, s * 2))
+    while (tiles * s * 2 <= 256 && c.K / (s * 2) >= 2048 && dma_any(c, layout, s * 2, tile))
         s *= 2;
     return s;
 }
@@ -289,9 +299,8 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
         if (!fast16)
             return DTM_ERR_CONFIG;
         if (forced_dims) {
-            const bool dma_cfg = force->block_m == 256 && force->block_n == 256 &&
-                                 force->block_k == 32;
-            if (dma_cfg ? !dma
+            const bool dma_cfg = is_dma_tile(force->block_m, force->block_n, force->block_k);
+            if (dma_cfg ? !(c.K > 0 && dma_any(c, layout, 1, force->block_m))
                         : !dtm::mfma16_has_config(force->block_m, force->block_n, force->block_k))
                 return DTM_ERR_CONFIG;
             p.block_m = force->block_m;
@@ -299,27 +308,31 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
             p.block_k = force->block_k;
         } else {
             // The pipelined kernel whenever it can run the problem (measured
-            // ahead of the register-staged kernel at every tile count), with
-            // split-K when there are few tiles and K is long; otherwise the
+            // ahead of the register-staged kernel at every tile count): with
+            // 128-wide tiles, and split-K when even those are few and K is
+            // long, when the 256-wide tiles are few; otherwise the
             // register-staged kernel.
             const int64_t tiles256 = cdiv(c.M, 256) * cdiv(c.N, 256);
             if (dma) {
-                p.block_m = p.block_n = 256;
+                const int tile = tiles256 <= SMALL_TILE_MAX && dma_any(c, layout, 1, 128) ? 128 : 256;
+                p.block_m = p.block_n = tile;
                 p.block_k = 32;
-                p.split_k = static_cast<int32_t>(pick_split(c, layout, tiles256));
+                p.split_k = tile == 128 ? static_cast<int32_t>(pick_split(
+                                              c, layout, cdiv(c.M, 128) * cdiv(c.N, 128), 128))
+                                        : 1;
             } else {
                 p.block_m = p.block_n = tiles256 >= 256 ? 256 : 128;
                 p.block_k = 64;
             }
         }
         if (forced_split) {
-            // split-K runs on the 256 x 256 x 32 pipelined kernel only
-            if (p.block_m != 256 || p.block_n != 256 || p.block_k != 32 ||
-                !dma_any(c, layout, forced_split))
+            // split-K runs on the pipelined kernel only
+            if (!is_dma_tile(p.block_m, p.block_n, p.block_k) ||
+                !dma_any(c, layout, forced_split, p.block_m))
                 return DTM_ERR_CONFIG;
             p.split_k = static_cast<int32_t>(forced_split);
         }
-        p.threads = p.block_k == 32 ? 512 : 256;  // the pipelined kernel's is settled below
+        p.threads = 256;  // the pipelined kernel's is settled below
         p.layout = layout;
     } else if (kernel == DTM_KERNEL_MFMA_F32) {
         if (!fast32)
@@ -353,12 +366,15 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
     const bool dma_tile = kernel == DTM_KERNEL_MFMA_F16 && p.block_k == 32;
     if (dma_tile) {
         // which form of the pipelined kernel, and how many waves
-        p.ragged = dma_interior(c, layout, p.split_k) ? 0 : 1;
+        p.ragged = dma_interior(c, layout, p.split_k, p.block_m) ? 0 : 1;
         const int forced_threads = force ? force->threads : 0;
         if (forced_threads) {
-            if (forced_threads % 64 || !dtm::mfma16_dma_waves_ok(forced_threads / 64, p.ragged))
+            if (forced_threads % 64 ||
+                !dtm::mfma16_dma_waves_ok(p.block_m, forced_threads / 64, p.ragged))
                 return DTM_ERR_CONFIG;
             p.threads = forced_threads;
+        } else if (p.block_m == 128) {
+            p.threads = 256;
         } else {
             p.threads = !p.ragged && p.grid_m * p.grid_n * p.split_k >= FOUR_WAVE_MIN_TILES ? 256
                                                                                            : 512;
@@ -413,15 +429,15 @@ int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t w
                     return DTM_ERR_WORKSPACE;
             }
             e = dtm::launch_mfma16_dma_partials(a, c.in, p.layout, p.split_k, p.ragged != 0,
-                                                 a_view_bytes(c), b_view_bytes(c),
+                                                 a_view_bytes(c), b_view_bytes(c), p.block_m,
                                                  p.threads / 64, static_cast<float *>(ws), s);
             if (e == hipSuccess)
                 e = dtm::launch_splitk_reduce(a, c.out, p.split_k, static_cast<float *>(ws), s);
         } else if (p.block_k == 32 && p.ragged)
             e = dtm::launch_mfma16_dma_ragged(a, c.in, c.out, p.layout, a_view_bytes(c),
-                                              b_view_bytes(c), s);
+                                              b_view_bytes(c), p.block_m, p.threads / 64, s);
         else if (p.block_k == 32)
-            e = dtm::launch_mfma16_dma(a, c.in, c.out, p.layout, p.threads / 64, s);
+            e = dtm::launch_mfma16_dma(a, c.in, c.out, p.layout, p.block_m, p.threads / 64, s);
         else
             e = dtm::launch_mfma16(a, c.in, c.out, p.block_m, p.block_n, p.block_k, p.layout,
                                    p.ragged != 0, s);

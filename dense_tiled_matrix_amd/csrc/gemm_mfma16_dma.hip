@@ -58,10 +58,10 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
 
-constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4;
-constexpr int A_STAGE_BYTES = BM * BK * 2;  // 16 KiB
-constexpr int B_STAGE_BYTES = BK * BN * 2;  // 16 KiB
-constexpr int STAGE_BYTES = A_STAGE_BYTES + B_STAGE_BYTES;
+constexpr int BK = 32, STAGES = 4;
+// A TILE x TILE output tile stages TILE x BK of each operand per chunk:
+// 16 KiB each at TILE = 256, 8 KiB at 128.
+template <int TILE> constexpr int operand_stage_bytes() { return TILE * BK * 2; }
 #ifndef DTM_DMA_GROUP_M
 #define DTM_DMA_GROUP_M 4
 #endif
@@ -131,14 +131,19 @@ __device__ __forceinline__ floatx16 mfma(const u32x4 &a, const u32x4 &b, const f
                                                        0);
 }
 
+// An M/N-contiguous operand is staged as BK k-rows of TILE elements: LPR
+// 16-byte chunks per k-row, RPS k-rows per 1 KiB load segment.
+template <int TILE> constexpr int krow_chunks() { return TILE / 8; }
+template <int TILE> constexpr int krows_per_seg() { return 64 / krow_chunks<TILE>(); }
+
 // Global source of this lane for 1 KiB segment `seg` of an operand's stage.
 // X points at element (0, 0) of the operand viewed as [mn][k]; mn0 and kb
 // are the tile's first row/column and the slice's first k.
 //  K-contiguous (KC): rows 16*seg + lane/4, physical chunk lane % 4.
-//  otherwise: k-rows 2*seg + lane/32, physical chunk lane % 32.
+//  otherwise: k-rows RPS*seg + lane/LPR, physical chunk lane % LPR.
 // The logical chunk is the physical one XOR the row's swizzle.  Chunk kt of
 // the K loop is kt * BK elements further along K.
-template <bool KC>
+template <bool KC, int TILE>
 __device__ __forceinline__ const uint16_t *stage_src(const uint16_t *X, int64_t mn0, int64_t s_mn,
                                                      int64_t s_k, int64_t kb, int seg, int lane)
 {
@@ -147,8 +152,9 @@ __device__ __forceinline__ const uint16_t *stage_src(const uint16_t *X, int64_t 
         const int c = (lane & 3) ^ swz_row(r);
         return X + (mn0 + r) * s_mn + kb + 8 * c;
     } else {
-        const int k = 2 * seg + (lane >> 5);
-        const int c = (lane & 31) ^ swz_krow(k);
+        constexpr int LPR = krow_chunks<TILE>(), RPS = krows_per_seg<TILE>();
+        const int k = RPS * seg + lane / LPR;
+        const int c = (lane % LPR) ^ swz_krow(k);
         return X + (kb + k) * s_k + mn0 + 8 * c;
     }
 }
@@ -158,7 +164,7 @@ __device__ __forceinline__ const uint16_t *stage_src(const uint16_t *X, int64_t 
 // kt * BK < klim (klim = 0 when the lane's row or columns lie outside the
 // view).  K is a multiple of 8 and, for an M/N-contiguous operand, so is its
 // extent, so each 16-byte chunk is either wholly inside or wholly outside.
-template <bool KC>
+template <bool KC, int TILE>
 __device__ __forceinline__ void stage_off(int64_t mn0, int64_t s_mn, int64_t s_k, int64_t ext,
                                           int64_t K, int64_t kb, int seg, int lane,
                                           uint32_t &off, int &klim)
@@ -173,8 +179,9 @@ __device__ __forceinline__ void stage_off(int64_t mn0, int64_t s_mn, int64_t s_k
         e = mn * s_mn + kf;
         ok = mn < ext;
     } else {
-        const int k = 2 * seg + (lane >> 5);
-        const int c = (lane & 31) ^ swz_krow(k);
+        constexpr int LPR = krow_chunks<TILE>(), RPS = krows_per_seg<TILE>();
+        const int k = RPS * seg + lane / LPR;
+        const int c = (lane % LPR) ^ swz_krow(k);
         mn = mn0 + 8 * c;
         kf = kb + k;
         e = kf * s_k + mn;
@@ -191,9 +198,9 @@ __device__ __forceinline__ void stage_off(int64_t mn0, int64_t s_mn, int64_t s_k
 //    k-step 1 is logical chunk 2 + lane/32, i.e. the offset XOR 32.
 //  otherwise: within 16-lane group G = lane/16, lane i = lane%16 addresses
 //    k-row 8*(G/2) + i/4 at column base + 16*(G%2) + 4*(i%4); the second
-//    read of the pair (k + 4) is 2048 bytes on and k-step 1 (k + 16) is
-//    8192 bytes on, because the swizzle depends on k % 4 only.
-template <bool KC> __device__ __forceinline__ int frag_off(int base, int lane)
+//    read of the pair (k + 4) is 4 k-rows on and k-step 1 (k + 16) is 16
+//    k-rows on, because the swizzle depends on k % 4 only.
+template <bool KC, int TILE> __device__ __forceinline__ int frag_off(int base, int lane)
 {
     if constexpr (KC) {
         const int r = base + (lane & 31);
@@ -202,7 +209,7 @@ template <bool KC> __device__ __forceinline__ int frag_off(int base, int lane)
         const int G = lane >> 4, li = lane & 15;
         const int k = 8 * (G >> 1) + (li >> 2);
         const int n = base + 16 * (G & 1) + 4 * (li & 3);
-        return k * 512 + (((n >> 3) ^ swz_krow(k)) * 16) + ((n >> 2) & 1) * 8;
+        return k * (TILE * 2) + (((n >> 3) ^ swz_krow(k)) * 16) + ((n >> 2) & 1) * 8;
     }
 }
 
@@ -222,7 +229,7 @@ __device__ __forceinline__ void read_tr_half(u32x4 &f, int e, const char *p)
 
 // TA: A is M-contiguous (stride_am == 1); else K-contiguous.
 // TB: B is K-contiguous (stride_bk == 1); else N-contiguous.
-template <int IN, int OUT, int NWAVES, bool TA, bool TB, bool RAGGED>
+template <int IN, int OUT, int TILE, int NWAVES, bool TA, bool TB, bool RAGGED>
 __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p, int64_t grid_m,
                                                                       int64_t grid_n,
                                                                       int64_t splits,
@@ -238,18 +245,25 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     // and the stride is unused.
     // RAGGED: a_bytes and b_bytes are the byte extents of the A and B views
     // (at most 2^31).
-    // Waves form a 2 x (NWAVES/2) grid over the 256 x 256 tile; each owns
-    // 128 rows and 256/(NWAVES/2) columns as MT x NT tiles of 32 x 32.
+    // Waves form a 2 x (NWAVES/2) grid over the TILE x TILE tile; each owns
+    // TILE/2 rows and TILE/(NWAVES/2) columns as MT x NT tiles of 32 x 32.
+    constexpr int BM = TILE, BN = TILE;
+    constexpr int A_STAGE_BYTES = operand_stage_bytes<TILE>();
+    constexpr int STAGE_BYTES = 2 * A_STAGE_BYTES;
+    constexpr int ROWB = TILE * 2;                 // bytes per staged k-row (M/N-contiguous)
     constexpr bool A_KC = !TA, B_KC = TB;
     constexpr int WAVES_N = NWAVES / 2;
-    constexpr int WN_COLS = BN / WAVES_N;
-    constexpr int MT = 4, NT = WN_COLS / 32;
+    constexpr int WM_ROWS = BM / 2, WN_COLS = BN / WAVES_N;
+    constexpr int MT = WM_ROWS / 32, NT = WN_COLS / 32;
     constexpr int A_READS = MT * (A_KC ? 1 : 2);   // LDS reads per k-step
     constexpr int NREAD = A_READS + NT * (B_KC ? 1 : 2);
     constexpr int NMFMA = MT * NT;                 // MFMAs per k-step
-    constexpr int DPO = 16 / NWAVES;               // 1 KiB loads per operand per wave per chunk
+    constexpr int DPO = TILE / 16 / NWAVES;        // 1 KiB loads per operand per wave per chunk
     constexpr int DMA_GROUP = 2 * DPO;             // loads per wave per chunk
-    static_assert(DMA_GROUP <= NMFMA / 2, "interleave slots");
+    constexpr int DMA_SLOTS = NMFMA / 2;           // one slot after every second MFMA
+    constexpr int DMA_PER_SLOT = (DMA_GROUP + DMA_SLOTS - 1) / DMA_SLOTS;
+    static_assert(DPO >= 1 && MT >= 1 && NT >= 1, "tile and waves");
+    static_assert(3 * DMA_GROUP < 64, "vmcnt counts at most 63 loads");
 
     __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
 
@@ -277,13 +291,13 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
 #pragma unroll
     for (int j = 0; j < DPO; ++j) {
         if constexpr (RAGGED) {
-            stage_off<A_KC>(m0, p.sam, p.sak, p.M, p.K, kb, DPO * wave + j, lane, a_goff[j],
-                            a_lim[j]);
-            stage_off<B_KC>(n0, p.sbn, p.sbk, p.N, p.K, kb, DPO * wave + j, lane, b_goff[j],
-                            b_lim[j]);
+            stage_off<A_KC, TILE>(m0, p.sam, p.sak, p.M, p.K, kb, DPO * wave + j, lane,
+                                  a_goff[j], a_lim[j]);
+            stage_off<B_KC, TILE>(n0, p.sbn, p.sbk, p.N, p.K, kb, DPO * wave + j, lane,
+                                  b_goff[j], b_lim[j]);
         } else {
-            a_src[j] = stage_src<A_KC>(A, m0, p.sam, p.sak, kb, DPO * wave + j, lane);
-            b_src[j] = stage_src<B_KC>(B, n0, p.sbn, p.sbk, kb, DPO * wave + j, lane);
+            a_src[j] = stage_src<A_KC, TILE>(A, m0, p.sam, p.sak, kb, DPO * wave + j, lane);
+            b_src[j] = stage_src<B_KC, TILE>(B, n0, p.sbn, p.sbk, kb, DPO * wave + j, lane);
         }
     }
     // elements between consecutive chunks
@@ -326,17 +340,17 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     };
 
     // ---- fragment read offsets (bytes within a stage) ---------------------
-    // A block i: rows wm*128 + 32*i; B block j: columns wn*WN_COLS + 32*j.
+    // A block i: rows wm*WM_ROWS + 32*i; B block j: columns wn*WN_COLS + 32*j.
     // [0] k-step 0, [1] k-step 1 (used by K-contiguous operands only).
     int a_off[MT][2], b_off[NT][2];
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-        a_off[i][0] = frag_off<A_KC>(wm * 128 + i * 32, lane);
+        a_off[i][0] = frag_off<A_KC, TILE>(wm * WM_ROWS + i * 32, lane);
         a_off[i][1] = a_off[i][0] ^ 32;
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-        b_off[j][0] = A_STAGE_BYTES + frag_off<B_KC>(wn * WN_COLS + j * 32, lane);
+        b_off[j][0] = A_STAGE_BYTES + frag_off<B_KC, TILE>(wn * WN_COLS + j * 32, lane);
         b_off[j][1] = b_off[j][0] ^ 32;
     }
 
@@ -352,7 +366,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
                 f.a[q] = *LDS_PTR(const u32x4, st + a_off[q][kk]);
             } else {
                 const int i = q >> 1, e = q & 1;
-                read_tr_half(f.a[i], e, st + a_off[i][0] + 8192 * kk + 2048 * e);
+                read_tr_half(f.a[i], e, st + a_off[i][0] + 16 * ROWB * kk + 4 * ROWB * e);
             }
         } else {
             const int qb = q - A_READS;
@@ -360,7 +374,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
                 f.b[qb] = *LDS_PTR(const u32x4, st + b_off[qb][kk]);
             } else {
                 const int j = qb >> 1, e = qb & 1;
-                read_tr_half(f.b[j], e, st + b_off[j][0] + 8192 * kk + 2048 * e);
+                read_tr_half(f.b[j], e, st + b_off[j][0] + 16 * ROWB * kk + 4 * ROWB * e);
             }
         }
     };
@@ -388,7 +402,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
 
     // The MFMAs of one k-step with the reads of the next k-step's fragments
     // spread evenly between them, and (when `dma`) the loads of chunk
-    // `dma_kt` one after every second MFMA.
+    // `dma_kt`, DMA_PER_SLOT after every second MFMA.
     auto half_step = [&](const Frags &cur, Frags &next, const char *next_st, int next_kk,
                          bool dma, int64_t dma_kt, int dma_stage) __attribute__((always_inline)) {
 #pragma unroll
@@ -399,8 +413,12 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
 #pragma unroll
             for (int r = r0; r < r1; ++r)
                 read_one(next, next_st, next_kk, r);
-            if (dma && (q & 1) && (q >> 1) < DMA_GROUP)
-                dma_one(dma_kt, dma_stage, q >> 1);
+            if (dma && (q & 1)) {
+#pragma unroll
+                for (int d = (q >> 1) * DMA_PER_SLOT; d < ((q >> 1) + 1) * DMA_PER_SLOT; ++d)
+                    if (d < DMA_GROUP)
+                        dma_one(dma_kt, dma_stage, d);
+            }
             if (dma) {
                 __builtin_amdgcn_sched_barrier(0);  // keep this group in place
             } else {
@@ -462,7 +480,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
             const int64_t col = n0 + wn * WN_COLS + j * 32 + (lane & 31);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int64_t row = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                const int64_t row = m0 + wm * WM_ROWS + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
                 if (!RAGGED || (row < p.M && col < p.N))
                     store_elem<OUT>(c_out, row * p.scm + col * p.scn, acc[i][j][v]);
             }
@@ -474,7 +492,8 @@ struct DmaLaunch {
     int64_t splits;
     bool ragged;
     uint32_t a_bytes, b_bytes;
-    int waves;  // 8, or 4 for the interior form
+    int tile;   // 256 or 128
+    int waves;  // see waves_ok
 };
 
 // K elements per slice: K / splits for the interior form; for the RAGGED
@@ -484,22 +503,36 @@ int64_t slice_k(int64_t K, int64_t splits, bool ragged)
     return ragged ? cdiv(cdiv(K, splits), BK) * BK : K / splits;
 }
 
+template <int IN, int OUT, int TILE, int NWAVES, bool TA, bool TB>
+hipError_t launch_one(const GemmArgs &a, const DmaLaunch &l, hipStream_t s)
+{
+    const int64_t gm = cdiv(a.M, TILE), gn = cdiv(a.N, TILE);
+    const dim3 grid((unsigned)(gm * gn * l.splits)), block(64 * NWAVES);
+    const int64_t ks = slice_k(a.K, l.splits, l.ragged);
+    if (l.ragged)
+        hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, TILE, NWAVES, TA, TB, true>), grid,
+                           block, 0, s, a, gm, gn, l.splits, ks, a.M * a.N, l.a_bytes, l.b_bytes);
+    else
+        hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, TILE, NWAVES, TA, TB, false>), grid,
+                           block, 0, s, a, gm, gn, l.splits, ks, a.M * a.N, 0u, 0u);
+    return hipGetLastError();
+}
+
+// The instantiated (tile, waves, form) combinations: 256 with 8 waves in
+// either form or 4 waves in the interior form, 128 with 4 waves in either.
 template <int IN, int OUT, bool TA, bool TB>
 hipError_t launch(const GemmArgs &a, const DmaLaunch &l, hipStream_t s)
 {
-    const int64_t gm = cdiv(a.M, BM), gn = cdiv(a.N, BN);
-    const dim3 grid((unsigned)(gm * gn * l.splits)), block(64 * l.waves);
-    const int64_t ks = slice_k(a.K, l.splits, l.ragged);
-    if (l.ragged)
-        hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, 8, TA, TB, true>), grid, block, 0, s,
-                           a, gm, gn, l.splits, ks, a.M * a.N, l.a_bytes, l.b_bytes);
-    else if (l.waves == 4)
-        hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, 4, TA, TB, false>), grid, block, 0, s,
-                           a, gm, gn, l.splits, ks, a.M * a.N, 0u, 0u);
-    else
-        hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, 8, TA, TB, false>), grid, block, 0, s,
-                           a, gm, gn, l.splits, ks, a.M * a.N, 0u, 0u);
-    return hipGetLastError();
+    if (l.tile == 128)
+        return launch_one<IN, OUT, 128, 4, TA, TB>(a, l, s);
+    if (l.waves == 4 && !l.ragged) {
+        hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, 256, 4, TA, TB, false>),
+                           dim3((unsigned)(cdiv(a.M, 256) * cdiv(a.N, 256) * l.splits)),
+                           dim3(256), 0, s, a, cdiv(a.M, 256), cdiv(a.N, 256), l.splits,
+                           slice_k(a.K, l.splits, false), a.M * a.N, 0u, 0u);
+        return hipGetLastError();
+    }
+    return launch_one<IN, OUT, 256, 8, TA, TB>(a, l, s);
 }
 
 template <int IN, int OUT>
@@ -539,52 +572,60 @@ hipError_t dispatch_in(const GemmArgs &a, int in, int layout, int out, const Dma
 
 }  // namespace
 
-bool mfma16_dma_fits(int64_t M, int64_t N, int64_t K, int64_t splits)
+bool mfma16_dma_fits(int64_t M, int64_t N, int64_t K, int64_t splits, int tile)
 {
-    return M > 0 && N > 0 && K > 0 && splits > 0 && M % BM == 0 && N % BN == 0 &&
-           K % (BK * splits) == 0 && (M / BM) * (N / BN) * splits <= 0x7fffffffLL;
+    return (tile == 256 || tile == 128) && M > 0 && N > 0 && K > 0 && splits > 0 &&
+           M % tile == 0 && N % tile == 0 && K % (BK * splits) == 0 &&
+           (M / tile) * (N / tile) * splits <= 0x7fffffffLL;
 }
 
 bool mfma16_dma_ragged_fits(int64_t M, int64_t N, int64_t K, int layout, uint64_t a_bytes,
-                            uint64_t b_bytes, int64_t splits)
+                            uint64_t b_bytes, int64_t splits, int tile)
 {
     const bool ta = layout & DTM_LAYOUT_A_M_CONTIG, tb = layout & DTM_LAYOUT_B_K_CONTIG;
-    return M > 0 && N > 0 && K > 0 && K % 8 == 0 && (!ta || M % 8 == 0) &&
-           (tb || N % 8 == 0) && a_bytes <= (1ull << 31) && b_bytes <= (1ull << 31) &&
-           splits >= 1 && (splits == 1 || N % 4 == 0) &&
+    return (tile == 256 || tile == 128) && M > 0 && N > 0 && K > 0 && K % 8 == 0 &&
+           (!ta || M % 8 == 0) && (tb || N % 8 == 0) && a_bytes <= (1ull << 31) &&
+           b_bytes <= (1ull << 31) && splits >= 1 && (splits == 1 || N % 4 == 0) &&
            (splits - 1) * slice_k(K, splits, true) < K &&
-           cdiv(M, BM) * cdiv(N, BN) * splits <= 0x7fffffffLL;
+           cdiv(M, tile) * cdiv(N, tile) * splits <= 0x7fffffffLL;
 }
 
-bool mfma16_dma_waves_ok(int waves, bool ragged) { return waves == 8 || (waves == 4 && !ragged); }
+bool mfma16_dma_waves_ok(int tile, int waves, bool ragged)
+{
+    if (tile == 128)
+        return waves == 4;
+    return tile == 256 && (waves == 8 || (waves == 4 && !ragged));
+}
 
-hipError_t launch_mfma16_dma(const GemmArgs &a, int in, int out, int layout, int waves,
+hipError_t launch_mfma16_dma(const GemmArgs &a, int in, int out, int layout, int tile, int waves,
                              hipStream_t s)
 {
-    if (!mfma16_dma_fits(a.M, a.N, a.K, 1) || !mfma16_dma_waves_ok(waves, false))
+    if (!mfma16_dma_fits(a.M, a.N, a.K, 1, tile) || !mfma16_dma_waves_ok(tile, waves, false))
         return hipErrorInvalidConfiguration;
-    return dispatch_in(a, in, layout, out, DmaLaunch{1, false, 0u, 0u, waves}, s);
+    return dispatch_in(a, in, layout, out, DmaLaunch{1, false, 0u, 0u, tile, waves}, s);
 }
 
 hipError_t launch_mfma16_dma_ragged(const GemmArgs &a, int in, int out, int layout,
-                                    uint64_t a_bytes, uint64_t b_bytes, hipStream_t s)
+                                    uint64_t a_bytes, uint64_t b_bytes, int tile, int waves,
+                                    hipStream_t s)
 {
-    if (!mfma16_dma_ragged_fits(a.M, a.N, a.K, layout, a_bytes, b_bytes, 1))
+    if (!mfma16_dma_ragged_fits(a.M, a.N, a.K, layout, a_bytes, b_bytes, 1, tile) ||
+        !mfma16_dma_waves_ok(tile, waves, true))
         return hipErrorInvalidConfiguration;
     return dispatch_in(a, in, layout, out,
                        DmaLaunch{1, true, static_cast<uint32_t>(a_bytes),
-                                 static_cast<uint32_t>(b_bytes), 8},
+                                 static_cast<uint32_t>(b_bytes), tile, waves},
                        s);
 }
 
 hipError_t launch_mfma16_dma_partials(const GemmArgs &a, int in, int layout, int64_t splits,
-                                      bool ragged, uint64_t a_bytes, uint64_t b_bytes, int waves,
-                                      float *ws, hipStream_t s)
+                                      bool ragged, uint64_t a_bytes, uint64_t b_bytes, int tile,
+                                      int waves, float *ws, hipStream_t s)
 {
-    if (ragged ? !mfma16_dma_ragged_fits(a.M, a.N, a.K, layout, a_bytes, b_bytes, splits)
-               : !mfma16_dma_fits(a.M, a.N, a.K, splits))
+    if (ragged ? !mfma16_dma_ragged_fits(a.M, a.N, a.K, layout, a_bytes, b_bytes, splits, tile)
+               : !mfma16_dma_fits(a.M, a.N, a.K, splits, tile))
         return hipErrorInvalidConfiguration;
-    if (!mfma16_dma_waves_ok(waves, ragged))
+    if (!mfma16_dma_waves_ok(tile, waves, ragged))
         return hipErrorInvalidConfiguration;
     GemmArgs w = a;
     w.C = ws;  // dense fp32 [splits][M][N]
@@ -592,7 +633,7 @@ hipError_t launch_mfma16_dma_partials(const GemmArgs &a, int in, int layout, int
     w.scn = 1;
     return dispatch_in(w, in, layout, DTM_F32,
                        DmaLaunch{splits, ragged, static_cast<uint32_t>(a_bytes),
-                                 static_cast<uint32_t>(b_bytes), waves},
+                                 static_cast<uint32_t>(b_bytes), tile, waves},
                        s);
 }
 

@@ -24,15 +24,16 @@ bool mfma16_has_config(int bm, int bn, int bk);
 hipError_t launch_mfma16(const GemmArgs &a, int in_dtype, int out_dtype, int bm, int bn, int bk,
                          int layout, bool ragged, hipStream_t s);
 
-// Deep-pipelined MFMA kernel (256 x 256 x 32 tiles, global -> LDS DMA) when
-// M and N are multiples of 256 and K of 32, for every operand layout:
-// `layout` holds dtm_layout bits (A M-contiguous, B K-contiguous).  `waves`
-// per workgroup: 8 (each owns 128 x 64 of the tile, two waves per SIMD), or
-// 4 (128 x 128 each, one wave per SIMD: a third fewer LDS reads per MFMA;
-// the interior form only).
-bool mfma16_dma_fits(int64_t M, int64_t N, int64_t K, int64_t splits);
-bool mfma16_dma_waves_ok(int waves, bool ragged);
-hipError_t launch_mfma16_dma(const GemmArgs &a, int in_dtype, int out_dtype, int layout,
+// Deep-pipelined MFMA kernel (tile x tile x 32 tiles, tile 256 or 128,
+// global -> LDS DMA) when M and N are multiples of the tile and K of 32, for
+// every operand layout: `layout` holds dtm_layout bits (A M-contiguous, B
+// K-contiguous).  `waves` per workgroup: at tile 256, 8 (each owns 128 x 64
+// of the tile, two waves per SIMD) or 4 (128 x 128 each, one wave per SIMD:
+// a third fewer LDS reads per MFMA; the interior form only); at tile 128, 4
+// (64 x 64 each; 64 KiB of LDS, so two workgroups share a CU).
+bool mfma16_dma_fits(int64_t M, int64_t N, int64_t K, int64_t splits, int tile);
+bool mfma16_dma_waves_ok(int tile, int waves, bool ragged);
+hipError_t launch_mfma16_dma(const GemmArgs &a, int in_dtype, int out_dtype, int layout, int tile,
                              int waves, hipStream_t s);
 // The same kernel on ragged shapes (its range-checked form): any M and N,
 // K % 8 == 0, an M-contiguous A needs M % 8 == 0 and an N-contiguous B
@@ -41,14 +42,15 @@ hipError_t launch_mfma16_dma(const GemmArgs &a, int in_dtype, int out_dtype, int
 // slices hold cdiv(K, splits) rounded up to 32 (the last may be shorter,
 // none empty) and N % 4 == 0 (the second pass reads 4 columns at a time).
 bool mfma16_dma_ragged_fits(int64_t M, int64_t N, int64_t K, int layout, uint64_t a_bytes,
-                            uint64_t b_bytes, int64_t splits);
+                            uint64_t b_bytes, int64_t splits, int tile);
 hipError_t launch_mfma16_dma_ragged(const GemmArgs &a, int in_dtype, int out_dtype, int layout,
-                                    uint64_t a_bytes, uint64_t b_bytes, hipStream_t s);
+                                    uint64_t a_bytes, uint64_t b_bytes, int tile, int waves,
+                                    hipStream_t s);
 // Split-K on the same kernel (either form): fp32 partial tiles written
 // densely to ws[splits][M][N] (a.C and its strides are not used).
 hipError_t launch_mfma16_dma_partials(const GemmArgs &a, int in_dtype, int layout, int64_t splits,
-                                      bool ragged, uint64_t a_bytes, uint64_t b_bytes, int waves,
-                                      float *ws, hipStream_t s);
+                                      bool ragged, uint64_t a_bytes, uint64_t b_bytes, int tile,
+                                      int waves, float *ws, hipStream_t s);
 // C = sum over s of ws[s] in order s = 0, 1, ..., converted once to out_dtype.
 hipError_t launch_splitk_reduce(const GemmArgs &a, int out_dtype, int64_t splits, const float *ws,
                                 hipStream_t s);

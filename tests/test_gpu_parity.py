@@ -299,7 +299,8 @@ def test_bf16_4096_bf16out():
 
 def test_f16_skinny_long_k():
     """512x512x65536 fp16 U[0,1] -> fp32 through the selector's split-K plan
-    (64 slices of 1024 on the pipelined kernel): full comparison, plus the
+    (16 slices of 4096 on the pipelined kernel's 128-wide tiles): full
+    comparison, plus the
     accumulation-error report against section 13.3's fp16 accumulator
     (emulated by the oracle on a 64x64 corner with the kernel's BLOCK_K)."""
     p = W.workload("f16_skinny512x512x65536_f32out")
@@ -307,7 +308,7 @@ def test_f16_skinny_long_k():
     a = torch.empty(p.M, p.K, dtype=torch.float16, device="cuda:0")
     b = torch.empty(p.K, p.N, dtype=torch.float16, device="cuda:0")
     plan = dtm.gemm_plan(a, b, out_dtype=torch.float32)
-    assert plan["split_k"] == 64 and plan["block_k"] == 32, plan
+    assert (plan["split_k"], plan["block_k"], plan["block_m"]) == (16, 32, 128), plan
     c, untouched = run(p)
     c64, cout = oracle.gemm_problem(p)
     err, tol = compare(p, c, c64=c64, cout=cout, label=p.name)
@@ -374,30 +375,30 @@ def test_mfma_pipelined_exact(ind):
         assert untouched
 
 
-@pytest.mark.parametrize("threads", [512, 256])
+@pytest.mark.parametrize("tile,threads", [(256, 512), (256, 256), (128, 256)])
 @pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])
 @pytest.mark.parametrize("ind", ["f16", "bf16"])
-def test_pipelined_layouts_exact(ind, layout, threads):
-    """Every operand layout on the pipelined kernel with 8 and with 4 waves
-    (A M-contiguous and/or B K-contiguous, staged as stored and read with
-    transposing LDS reads): pipeline depths 1, 3, 5 and many chunks, several
-    grids, padded leading dimensions, split-K; value-exact on integer-valued
-    inputs."""
+def test_pipelined_layouts_exact(ind, layout, tile, threads):
+    """Every operand layout on the pipelined kernel: 256-wide tiles with 8
+    and with 4 waves, 128-wide tiles with 4 (A M-contiguous and/or B
+    K-contiguous, staged as stored and read with transposing LDS reads):
+    pipeline depths 1, 3, 5 and many chunks, several grids, padded leading
+    dimensions, split-K; value-exact on integer-valued inputs."""
     shapes = [(256, 256, 32, 1), (512, 256, 96, 1), (256, 768, 160, 1), (768, 512, 2048, 1),
               (512, 512, 4096, 8), (256, 256, 1024, 4)]
     for n, (M, N, K, S) in enumerate(shapes):
         outd = ["f32", "f16", "bf16"][n % 3]
         p = padded_int_problem(M, N, K, ind, outd, 8 if K <= 256 else 2, seed=600 + n,
                                extra=8 * (n % 2), a_layout=layout[0], b_layout=layout[1])
-        cfg = dict(kernel=MF16, block_m=256, block_n=256, block_k=32, split_k=S,
+        cfg = dict(kernel=MF16, block_m=tile, block_n=tile, block_k=32, split_k=S,
                    threads=threads)
         plan = {}
         c, untouched = run(p, config=cfg, c_pad=4 if n % 2 else 0, plan=plan)
-        assert plan["status"] == 0 and plan["block_k"] == 32, plan
+        assert plan["status"] == 0 and plan["block_k"] == 32 and plan["block_m"] == tile, plan
         assert plan["layout"] == LAYOUT_BITS[layout] and plan["split_k"] == S, plan
         assert plan["threads"] == threads and plan["ragged"] == 0, plan
         compare(p, c, exact=True,
-                label=f"pipelined x{threads} {layout} {ind} {M}x{N}x{K} S{S}->{outd}")
+                label=f"pipelined {tile} x{threads} {layout} {ind} {M}x{N}x{K} S{S}->{outd}")
         assert untouched
 
 
@@ -437,18 +438,19 @@ def _round8(x):
     return -(-x // 8) * 8
 
 
+@pytest.mark.parametrize("tile", [256, 128])
 @pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])
 @pytest.mark.parametrize("ind", ["f16", "bf16"])
-def test_pipelined_ragged_exact(ind, layout):
+def test_pipelined_ragged_exact(ind, layout, tile):
     """The pipelined kernel's range-checked form at shapes its tile does not
     divide (M, N of any size -- multiples of 8 along a contiguous M or N --
     and K a multiple of 8, including K < 32 and K not a multiple of 32):
     chunks outside the views must arrive as exact zeros, the NaN padding
     beyond each leading dimension must never be read, and C outside M x N
     must stay untouched.  Value-exact on integer-valued inputs."""
-    cfg = dict(kernel=MF16, block_m=256, block_n=256, block_k=32)
+    cfg = dict(kernel=MF16, block_m=tile, block_n=tile, block_k=32)
     shapes = [(300, 264, 104), (256, 520, 8), (513, 777, 1000), (8, 8, 8), (777, 255, 64),
-              (1000, 1001, 2048), (257, 300, 24)]
+              (1000, 1001, 2048), (257, 300, 24), (384, 640, 96)]
     for n, (M, N, K) in enumerate(shapes):
         if layout[0] == "T":
             M = _round8(M)
@@ -459,9 +461,10 @@ def test_pipelined_ragged_exact(ind, layout):
                                extra=8 * (n % 2), a_layout=layout[0], b_layout=layout[1])
         plan = {}
         c, untouched = run(p, config=cfg, c_pad=3 if n % 2 else 0, plan=plan)
-        assert plan["status"] == 0 and plan["block_k"] == 32, plan
-        assert plan["ragged"] == (1 if (M % 256 or N % 256 or K % 32) else 0), plan
-        compare(p, c, exact=True, label=f"pipelined ragged {layout} {ind} {M}x{N}x{K}->{outd}")
+        assert plan["status"] == 0 and plan["block_k"] == 32 and plan["block_m"] == tile, plan
+        assert plan["ragged"] == (1 if (M % tile or N % tile or K % 32) else 0), plan
+        compare(p, c, exact=True,
+                label=f"pipelined {tile} ragged {layout} {ind} {M}x{N}x{K}->{outd}")
         assert untouched
 
 
@@ -480,8 +483,9 @@ def test_pipelined_ragged_random_selector(layout):
     assert untouched
 
 
+@pytest.mark.parametrize("tile", [256, 128])
 @pytest.mark.parametrize("layout", ["NN", "TT"])
-def test_split_k_ragged_exact(layout):
+def test_split_k_ragged_exact(layout, tile):
     """Split-K on the range-checked pipelined kernel: ragged M and N, slices
     of cdiv(K, S) rounded up to 32 with a shorter last slice, K a multiple of
     8 only; value-exact on integer-valued inputs (every partial sum is an
@@ -491,7 +495,7 @@ def test_split_k_ragged_exact(layout):
         if layout[0] == "T":
             M = _round8(M)
         outd = ["f32", "bf16", "f16", "f32"][n]
-        cfg = dict(kernel=MF16, block_m=256, block_n=256, block_k=32, split_k=S)
+        cfg = dict(kernel=MF16, block_m=tile, block_n=tile, block_k=32, split_k=S)
         p = padded_int_problem(M, N, K, "bf16" if n % 2 else "f16", outd, 2, seed=840 + n,
                                a_layout=layout[0], b_layout=layout[1])
         plan = {}
@@ -502,15 +506,18 @@ def test_split_k_ragged_exact(layout):
 
 
 def test_ragged_selector_split():
-    """bf16 2000^3 (64 tiles of 256): the selector splits K in two on the
-    range-checked pipelined kernel; N(0,1) values within tolerance."""
-    p = W.random_problem(2000, 2000, 2000, "bf16", "f32", ("normal", 0.0, 1.0), seed=860)
-    plan = {}
-    c, untouched = run(p, plan=plan)
-    assert (plan["block_k"], plan["split_k"], plan["ragged"]) == (32, 2, 1), plan
-    err, tol = compare(p, c, label="ragged split 2000^3")
-    note(f"ragged split 2000^3: max err {err:.3e} tol {tol:.3e}")
-    assert untouched
+    """Few tiles through the selector on the range-checked pipelined kernel:
+    bf16 2000^3 (64 tiles of 256, so 256 of 128) and 1000 x 1000 x 8200
+    (16 of 256: 64 of 128, K split in 4); N(0,1) values within tolerance."""
+    for M, N, K, S, seed in [(2000, 2000, 2000, 1, 860), (1000, 1000, 8200, 4, 861)]:
+        p = W.random_problem(M, N, K, "bf16", "f32", ("normal", 0.0, 1.0), seed=seed)
+        plan = {}
+        c, untouched = run(p, plan=plan)
+        assert (plan["block_m"], plan["block_k"], plan["split_k"], plan["ragged"]) == \
+            (128, 32, S, 1), plan
+        err, tol = compare(p, c, label=f"ragged {M}x{N}x{K}")
+        note(f"ragged {M}x{N}x{K} S{S}: max err {err:.3e} tol {tol:.3e}")
+        assert untouched
 
 
 @pytest.mark.parametrize("ind", ["f16", "bf16"])

@@ -76,11 +76,20 @@ def test_selector_measured_workloads():
     # K % 8 != 0: the 64-deep register-staged kernel
     st, p = plan(4096, 4096, 4100, sam=4104, ind=F16, outd=F32)
     assert st == 0 and (p["block_m"], p["block_k"], p["ragged"]) == (256, 64, 1)
-    # long-K skinny: 4 tiles of 256 x 256 -> split K into 64 slices of 1024
+    # long-K skinny: 4 tiles of 256 x 256 -> 16 of 128 x 128, K split into
+    # 16 slices of 4096
     st, p = plan(512, 512, 65536, ind=F16, outd=F32)
-    assert st == 0 and p["kernel_name"] == "mfma_f16" and p["split_k"] == 64
-    assert (p["block_m"], p["block_k"], p["k_iters"]) == (256, 32, 32)
-    assert p["workspace_bytes"] == 64 * 512 * 512 * 4
+    assert st == 0 and p["kernel_name"] == "mfma_f16" and p["split_k"] == 16
+    assert (p["block_m"], p["block_k"], p["k_iters"], p["threads"]) == (128, 32, 128, 256)
+    assert p["workspace_bytes"] == 16 * 512 * 512 * 4
+    # few 256-wide tiles: 128-wide ones, split only with K long enough
+    for M, N, K, tile, S in [(2048, 2048, 2048, 128, 1), (1024, 1024, 8192, 128, 4),
+                             (1024, 1024, 1024, 128, 1), (8192, 1024, 8192, 128, 1),
+                             (2560, 2560, 2560, 128, 1), (3072, 3072, 3072, 256, 1),
+                             (4096, 4096, 1024, 256, 1), (2000, 2000, 2000, 128, 1)]:
+        st, p = plan(M, N, K, A=1 << 40, B=2 << 40, C=3 << 40, ind=BF16, outd=BF16)
+        assert st == 0 and (p["block_m"], p["block_k"], p["split_k"]) == (tile, 32, S), \
+            (M, N, K, p)
     # enough tiles: no split
     st, p = plan(4096, 4096, 65536, A=1 << 40, B=2 << 40, C=3 << 40, ind=F16, outd=F32)
     assert st == 0 and p["split_k"] == 1 and p["workspace_bytes"] == 0
@@ -134,7 +143,7 @@ def test_selector_transposed_layouts():
         assert st == 0 and p["kernel_name"] == "mfma_f32" and p["layout"] == bits, kw
     # few tiles and a transposed operand: the pipelined kernel with split K
     st, p = plan(512, 512, 65536, sam=1, sak=512, ind=F16, outd=F32)
-    assert st == 0 and p["layout"] == LA and p["split_k"] == 64 and p["block_k"] == 32
+    assert st == 0 and p["layout"] == LA and p["split_k"] == 16 and p["block_k"] == 32
     # a small transposed problem: the pipelined kernel as well ...
     st, p = plan(256, 256, 64, sbk=1, sbn=64, ind=F16, outd=F32)
     assert st == 0 and p["layout"] == LB and p["block_k"] == 32 and p["ragged"] == 0
@@ -309,7 +318,7 @@ def test_pipelined_wave_count():
             (4096, 7936, 64, dict(), 512),                         # 496 tiles
             (4096, 4096, 4096, dict(), 512),                       # 256 tiles
             (8000, 8000, 8000, dict(), 512),                       # range-checked form
-            (512, 512, 65536, dict(), 512)]:                       # 4 tiles x 64 slices
+            (512, 512, 65536, dict(), 256)]:                       # 128-wide tiles
         st, p = plan(M, N, K, ind=BF16, outd=BF16, **big, **kw)
         assert st == 0 and p["block_k"] == 32 and p["threads"] == threads, (M, N, K, kw, p)
     dma = dict(kernel=dtm.DTM_KERNEL_MFMA_F16, block_m=256, block_n=256, block_k=32)
@@ -322,13 +331,29 @@ def test_pipelined_wave_count():
     assert st == 0 and p["ragged"] == 1
     # the range-checked form has 8 waves only
     assert plan(500, 256, 96, config=dict(dma, threads=256))[0] == dtm.DTM_ERR_CONFIG
+    # 128-wide tiles: 4 waves, both forms, split-K too
+    d128 = dict(dma, block_m=128, block_n=128)
+    for M, N, K, ragged in [(512, 256, 96, 0), (500, 256, 96, 1), (384, 640, 104, 1)]:
+        st, p = plan(M, N, K, sam=K + (-K % 8), config=d128)
+        assert st == 0 and (p["block_m"], p["threads"], p["ragged"]) == (128, 256, ragged), p
+        assert (p["grid_m"], p["grid_n"]) == (-(-M // 128), -(-N // 128))
+    st, p = plan(512, 256, 1024, config=dict(d128, split_k=4))
+    assert st == 0 and p["split_k"] == 4 and p["k_iters"] == 8 and p["block_m"] == 128
+    assert plan(512, 256, 96, config=dict(d128, threads=512))[0] == dtm.DTM_ERR_CONFIG
+    assert plan(512, 256, 96, config=dict(dma, block_m=128))[0] == dtm.DTM_ERR_CONFIG
+    assert plan(512, 256, 96, config=dict(dma, block_m=64, block_n=64))[0] == dtm.DTM_ERR_CONFIG
     for t in (128, 320, 1024, 100):
         assert plan(512, 256, 96, config=dict(dma, threads=t))[0] == dtm.DTM_ERR_CONFIG, t
     assert plan(512, 256, 96, config=dict(kernel=dtm.DTM_KERNEL_MFMA_F16, block_m=256,
                                           block_n=256, block_k=64, threads=256))[0] == \
         dtm.DTM_ERR_CONFIG
-    # with the tile left to the selector, the size applies if it picks this tile
-    assert plan(64, 64, 64, config=dict(threads=512))[1]["threads"] == 512
+    # with the tile left to the selector, the size must suit the tile it picks
+    # (128 x 128 here: 4 waves)
+    st, p = plan(64, 64, 64, config=dict(threads=256))
+    assert st == 0 and (p["block_m"], p["threads"]) == (128, 256)
+    assert plan(64, 64, 64, config=dict(threads=512))[0] == dtm.DTM_ERR_CONFIG
+    st, p = plan(8192, 8192, 64, A=1 << 40, B=2 << 40, C=3 << 40, config=dict(threads=512))
+    assert st == 0 and (p["block_m"], p["threads"]) == (256, 512)
     assert plan(64, 64, 64, ind=F32, outd=F32, config=dict(threads=512))[0] == \
         dtm.DTM_ERR_CONFIG
 
