@@ -1,9 +1,10 @@
 // gemm_mfma16_dma.hip -- deep-pipelined MFMA GEMM for fp16/bf16 inputs on
-// gfx950, for problems whose M, N are multiples of 256 and K of 32, in any
-// of the four operand layouts (A K- or M-contiguous, B N- or K-contiguous).
+// gfx950, in any of the four operand layouts (A K- or M-contiguous, B N- or
+// K-contiguous): an interior form for M, N multiples of the tile and K of 32,
+// and a range-checked form for ragged shapes.
 //
 // The computation is the blocked product of "Chapter 13: The Blocked Matmul
-// Kernel" (section 13.1): one workgroup per 256 x 256 output tile, a K-loop
+// Kernel" (section 13.1): one workgroup per output tile, a K-loop
 // over 32-deep chunks adding each chunk's tile product into an fp32
 // accumulator zeroed once before the loop, and a single conversion to the
 // output dtype at the store (section 13.3).  The interior instantiation
@@ -19,29 +20,38 @@
 // Lesson 4: a transpose is only a change of strides).
 //
 // gfx950 design:
-//  * NWAVES wave64s (2 x NWAVES/2), each owning 128 x (512/NWAVES) of C as
-//    tiles of v_mfma_f32_32x32x16_{f16,bf16} with fp32 accumulators in the
-//    AccVGPR file.
+//  * One workgroup per TILE x TILE output tile (TILE 256 or 128).  NWAVES
+//    wave64s (2 x NWAVES/2) each own TILE/2 x TILE/(NWAVES/2) of C as blocks
+//    of v_mfma_f32_16x16x32_{f16,bf16} with fp32 accumulators (in the
+//    AccVGPR file when they do not fit beside the rest).  That instruction
+//    consumes a whole 32-deep chunk: one k-step per chunk.  It moves fewer
+//    accumulator bytes per FLOP than the 32 x 32 x 16 form, and on this
+//    power-limited part that showed as clock: bf16 8192^3 ran at 1.89 GHz
+//    and 68% MFMA-busy against 1.70 GHz and 72% for the 32 x 32 form, 5.6%
+//    faster.
 //  * Operands move global -> LDS with global_load_lds_dwordx4 (each wave
 //    instruction writes 1 KiB of LDS, lane i's 16 bytes at offset 16*i), so
-//    no VGPRs stage them.  Four LDS stages of (16 + 16) KiB: a chunk is
-//    loaded three to four chunks of MFMA time before it is read.  One
-//    barrier per chunk, after a wait for exactly the loads of the chunk
-//    about to be read; the loads are issued one after every second MFMA.
-//  * Both MFMA operands want, in lane l, 8 consecutive k of row/column
-//    l % 32.  An operand that is K-contiguous in memory is staged as 256
-//    rows of 64 bytes; the 16-byte chunk c of row r sits at c ^ f(r),
-//    f(r) = (r >> 2) & 3, and a fragment is one ds_read_b128 per lane (each
-//    16 consecutive rows read cover all 64 banks once; measured on gfx950:
-//    zero SQ_LDS_BANK_CONFLICT, other XOR patterns cost 4-12 extra cycles
-//    per read).
-//  * An operand that is M- or N-contiguous stays that way: 32 k-rows of 512
-//    bytes, chunk c of k-row k at c ^ g(k), g = {0, 6, 10, 12}[k % 4]
+//    no VGPRs stage them.  Four LDS stages: a chunk is loaded three to four
+//    chunks of MFMA time before it is read.  One barrier per chunk, after a
+//    wait for exactly the loads of the chunk about to be read; the loads are
+//    spread evenly between the MFMAs.
+//  * Both MFMA operands want, in lane l, 8 consecutive k (k-group l/16) of
+//    row/column l % 16.  An operand that is K-contiguous in memory is staged
+//    as TILE rows of 64 bytes; the 16-byte chunk c of row r sits at
+//    c ^ f(r), f(r) = (r >> 2) & 3, and a fragment is one ds_read_b128 per
+//    lane (16 consecutive rows of one chunk cover all 64 banks once;
+//    measured on gfx950: zero SQ_LDS_BANK_CONFLICT, other XOR patterns cost
+//    4-12 extra cycles per read).
+//  * An operand that is M- or N-contiguous stays that way: 32 k-rows of
+//    2 * TILE bytes, chunk c of k-row k at c ^ g(k), g = {0, 6, 10, 12}[k % 4]
 //    (measured conflict-free; no swizzle costs about 6 extra cycles per
 //    read).  A fragment is two ds_read_b64_tr_b16, which hand lane i of each
 //    16-lane group the i-th column of a 4 x 16 block whose rows the lanes
 //    address, i.e. four consecutive k of one row/column -- the operand
 //    layout the MFMA wants, with no transpose anywhere else.
+//  * A fragments are single-buffered (row i's fragment of the next chunk is
+//    read once row i's MFMAs have issued), B fragments double-buffered, the
+//    loop unrolled in pairs so the two B buffers swap without copies.
 //  * Workgroup ids are remapped so that each XCD owns a compact group of
 //    tiles (shared A rows and B columns stay in its L2).
 #include "launch.h"
@@ -51,7 +61,7 @@ namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -119,18 +129,6 @@ __device__ __forceinline__ void dma16_buf(const i32x4 &rsrc, uint32_t voff, uint
 // Offset past every buffer this kernel builds (they are at most 2^31 bytes).
 constexpr uint32_t OUTSIDE = 0x80000000u;
 
-template <int IN>
-__device__ __forceinline__ floatx16 mfma(const u32x4 &a, const u32x4 &b, const floatx16 &c)
-{
-    if constexpr (IN == DTM_F16)
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
-                                                      __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0,
-                                                       0);
-}
-
 // An M/N-contiguous operand is staged as BK k-rows of TILE elements: LPR
 // 16-byte chunks per k-row, RPS k-rows per 1 KiB load segment.
 template <int TILE> constexpr int krow_chunks() { return TILE / 8; }
@@ -192,27 +190,6 @@ __device__ __forceinline__ void stage_off(int64_t mn0, int64_t s_mn, int64_t s_k
     klim = ok ? static_cast<int>(K - kf) : 0;
 }
 
-// Byte offset, within an operand's stage, of this lane's first fragment read
-// for the 32-wide block of rows/columns starting at `base`, k-step 0.
-//  K-contiguous: row base + lane%32, logical chunk lane/32 (one b128 read);
-//    k-step 1 is logical chunk 2 + lane/32, i.e. the offset XOR 32.
-//  otherwise: within 16-lane group G = lane/16, lane i = lane%16 addresses
-//    k-row 8*(G/2) + i/4 at column base + 16*(G%2) + 4*(i%4); the second
-//    read of the pair (k + 4) is 4 k-rows on and k-step 1 (k + 16) is 16
-//    k-rows on, because the swizzle depends on k % 4 only.
-template <bool KC, int TILE> __device__ __forceinline__ int frag_off(int base, int lane)
-{
-    if constexpr (KC) {
-        const int r = base + (lane & 31);
-        return r * 64 + (((lane >> 5) ^ swz_row(r)) * 16);
-    } else {
-        const int G = lane >> 4, li = lane & 15;
-        const int k = 8 * (G >> 1) + (li >> 2);
-        const int n = base + 16 * (G & 1) + 4 * (li & 3);
-        return k * (TILE * 2) + (((n >> 3) ^ swz_krow(k)) * 16) + ((n >> 2) & 1) * 8;
-    }
-}
-
 // Half (e = 0: k 0..3, e = 1: k 4..7) of a fragment by a transposing read.
 __device__ __forceinline__ void read_tr_half(u32x4 &f, int e, const char *p)
 {
@@ -227,42 +204,74 @@ __device__ __forceinline__ void read_tr_half(u32x4 &f, int e, const char *p)
     }
 }
 
+template <int IN>
+__device__ __forceinline__ floatx4 mfma(const u32x4 &a, const u32x4 &b, const floatx4 &c)
+{
+    if constexpr (IN == DTM_F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                      __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0,
+                                                       0);
+}
+
+// Byte offset, within an operand's stage, of this lane's fragment read for
+// the 16 rows/columns starting at `base` (one whole 32-deep chunk: lane l
+// holds 8 consecutive k, k-group l/16, of row/column l%16).
+//  K-contiguous: row base + l%16, logical chunk l/16 (one b128 read).
+//  otherwise: within 16-lane group G = l/16, lane i = l%16 addresses k-row
+//    8*G + i/4 at column base + 4*(i%4); the second read (k + 4) is 4
+//    k-rows on.
+template <bool KC, int TILE> __device__ __forceinline__ int frag_off(int base, int lane)
+{
+    const int G = lane >> 4, li = lane & 15;
+    if constexpr (KC) {
+        const int r = base + li;
+        return r * 64 + ((G ^ swz_row(r)) * 16);
+    } else {
+        const int k = 8 * G + (li >> 2);
+        const int n = base + 4 * (li & 3);
+        return k * (TILE * 2) + (((n >> 3) ^ swz_krow(k)) * 16) + ((n >> 2) & 1) * 8;
+    }
+}
+
 // TA: A is M-contiguous (stride_am == 1); else K-contiguous.
 // TB: B is K-contiguous (stride_bk == 1); else N-contiguous.
+// Each wave's tile is MT x NT blocks of 16 x 16.  Iteration c of the K loop:
+// wait until this wave's loads of chunk c + 1 have landed and its reads of
+// chunk c have returned, barrier (every wave is then done with chunk c's
+// stage), then the MFMAs of chunk c with the reads of chunk c + 1 and the
+// loads of chunk c + 4 (into chunk c's stage) spread between them.
+// Split-K: workgroup ids beyond one grid of tiles take further slices of K,
+// k_split elements each (a multiple of BK; in the RAGGED form the last slice
+// may end early at K), and write their fp32 partial tile to
+// C + slice * c_split_stride.  Without a split, splits = 1, k_split = K and
+// the stride is unused.  RAGGED: a_bytes and b_bytes are the byte extents of
+// the A and B views (at most 2^31).
 template <int IN, int OUT, int TILE, int NWAVES, bool TA, bool TB, bool RAGGED>
 __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p, int64_t grid_m,
-                                                                      int64_t grid_n,
-                                                                      int64_t splits,
-                                                                      int64_t k_split,
-                                                                      int64_t c_split_stride,
-                                                                      uint32_t a_bytes,
-                                                                      uint32_t b_bytes)
+                                                                        int64_t grid_n,
+                                                                        int64_t splits,
+                                                                        int64_t k_split,
+                                                                        int64_t c_split_stride,
+                                                                        uint32_t a_bytes,
+                                                                        uint32_t b_bytes)
 {
-    // Split-K: workgroup ids beyond one grid of tiles take further slices of
-    // K, k_split elements each (a multiple of BK; in the RAGGED form the
-    // last slice may end early at K), and write their fp32 partial tile to
-    // C + slice * c_split_stride.  Without a split, splits = 1, k_split = K
-    // and the stride is unused.
-    // RAGGED: a_bytes and b_bytes are the byte extents of the A and B views
-    // (at most 2^31).
-    // Waves form a 2 x (NWAVES/2) grid over the TILE x TILE tile; each owns
-    // TILE/2 rows and TILE/(NWAVES/2) columns as MT x NT tiles of 32 x 32.
     constexpr int BM = TILE, BN = TILE;
     constexpr int A_STAGE_BYTES = operand_stage_bytes<TILE>();
     constexpr int STAGE_BYTES = 2 * A_STAGE_BYTES;
-    constexpr int ROWB = TILE * 2;                 // bytes per staged k-row (M/N-contiguous)
+    constexpr int ROWB = TILE * 2;
     constexpr bool A_KC = !TA, B_KC = TB;
     constexpr int WAVES_N = NWAVES / 2;
     constexpr int WM_ROWS = BM / 2, WN_COLS = BN / WAVES_N;
-    constexpr int MT = WM_ROWS / 32, NT = WN_COLS / 32;
-    constexpr int A_READS = MT * (A_KC ? 1 : 2);   // LDS reads per k-step
+    constexpr int MT = WM_ROWS / 16, NT = WN_COLS / 16;
+    constexpr int A_READS = MT * (A_KC ? 1 : 2);
     constexpr int NREAD = A_READS + NT * (B_KC ? 1 : 2);
-    constexpr int NMFMA = MT * NT;                 // MFMAs per k-step
-    constexpr int DPO = TILE / 16 / NWAVES;        // 1 KiB loads per operand per wave per chunk
-    constexpr int DMA_GROUP = 2 * DPO;             // loads per wave per chunk
-    constexpr int DMA_SLOTS = NMFMA / 2;           // one slot after every second MFMA
-    constexpr int DMA_PER_SLOT = (DMA_GROUP + DMA_SLOTS - 1) / DMA_SLOTS;
-    static_assert(DPO >= 1 && MT >= 1 && NT >= 1, "tile and waves");
+    constexpr int NMFMA = MT * NT;                 // MFMAs per chunk
+    constexpr int DPO = TILE / 16 / NWAVES;
+    constexpr int DMA_GROUP = 2 * DPO;
+    static_assert(DPO >= 1 && NMFMA >= DMA_GROUP, "tile and waves");
     static_assert(3 * DMA_GROUP < 64, "vmcnt counts at most 63 loads");
 
     __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
@@ -274,7 +283,6 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
 
     int64_t pid_m, pid_n;
     const int64_t tiles = grid_m * grid_n;
-    // consecutive remapped ids (one XCD) share a K slice and differ in tile
     const int64_t t_id = xcd_remap(blockIdx.x, tiles * splits);
     const int64_t slice = t_id / tiles;
     grouped_tile(t_id - slice * tiles, grid_m, grid_n, GROUP_M, pid_m, pid_n);
@@ -284,9 +292,8 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
 
-    // ---- load sources of this lane: segments DPO*wave .. +DPO-1 ----------
-    const uint16_t *a_src[DPO], *b_src[DPO];   // interior
-    uint32_t a_goff[DPO], b_goff[DPO];         // RAGGED
+    const uint16_t *a_src[DPO], *b_src[DPO];
+    uint32_t a_goff[DPO], b_goff[DPO];
     int a_lim[DPO], b_lim[DPO];
 #pragma unroll
     for (int j = 0; j < DPO; ++j) {
@@ -300,7 +307,6 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
             b_src[j] = stage_src<B_KC, TILE>(B, n0, p.sbn, p.sbk, kb, DPO * wave + j, lane);
         }
     }
-    // elements between consecutive chunks
     const int64_t a_chunk = A_KC ? BK : BK * p.sak;
     const int64_t b_chunk = B_KC ? BK : BK * p.sbk;
     i32x4 a_rsrc, b_rsrc;
@@ -312,10 +318,6 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     const uint32_t a_dst0 = lds_base + (DPO * wave) * 1024;
     const uint32_t b_dst0 = lds_base + A_STAGE_BYTES + (DPO * wave) * 1024;
 
-    // Load d (0 .. DMA_GROUP-1) of chunk kt into LDS stage `stage`.  Inline
-    // assembly, so the compiler neither reorders nor waits on these
-    // asynchronous LDS writes; the loop waits for them explicitly (vmcnt)
-    // before a barrier.
     auto dma_one = [&](int64_t kt, int stage, int d) __attribute__((always_inline)) {
         const uint32_t so = static_cast<uint32_t>(stage) * STAGE_BYTES;
         if constexpr (RAGGED) {
@@ -339,106 +341,66 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
         }
     };
 
-    // ---- fragment read offsets (bytes within a stage) ---------------------
-    // A block i: rows wm*WM_ROWS + 32*i; B block j: columns wn*WN_COLS + 32*j.
-    // [0] k-step 0, [1] k-step 1 (used by K-contiguous operands only).
-    int a_off[MT][2], b_off[NT][2];
+    int a_off[MT], b_off[NT];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        a_off[i][0] = frag_off<A_KC, TILE>(wm * WM_ROWS + i * 32, lane);
-        a_off[i][1] = a_off[i][0] ^ 32;
-    }
+    for (int i = 0; i < MT; ++i)
+        a_off[i] = frag_off<A_KC, TILE>(wm * WM_ROWS + i * 16, lane);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-        b_off[j][0] = A_STAGE_BYTES + frag_off<B_KC, TILE>(wn * WN_COLS + j * 32, lane);
-        b_off[j][1] = b_off[j][0] ^ 32;
-    }
+    for (int j = 0; j < NT; ++j)
+        b_off[j] = A_STAGE_BYTES + frag_off<B_KC, TILE>(wn * WN_COLS + j * 16, lane);
 
-    // Fragments of one 16-deep k-step.
-    struct Frags {
-        u32x4 a[MT], b[NT];
-    };
-    // Read q of a k-step's fragments: A blocks first (one read each, or two
-    // halves each when A is M-contiguous), then the B blocks likewise.
-    auto read_one = [&](Frags &f, const char *st, int kk, int q) __attribute__((always_inline)) {
-        if (q < A_READS) {
-            if constexpr (A_KC) {
-                f.a[q] = *LDS_PTR(const u32x4, st + a_off[q][kk]);
-            } else {
-                const int i = q >> 1, e = q & 1;
-                read_tr_half(f.a[i], e, st + a_off[i][0] + 16 * ROWB * kk + 4 * ROWB * e);
-            }
+    // A fragments are single-buffered: row i's fragment of the next chunk is
+    // read as soon as row i's MFMAs of this chunk have issued.  B fragments
+    // are double-buffered (every row needs them) and read over the first
+    // rows' MFMAs.  This keeps the 256-wide tiles within their registers.
+    u32x4 fa[MT], fb0[NT], fb1[NT];
+    auto read_a = [&](const char *st, int i) __attribute__((always_inline)) {
+        if constexpr (A_KC) {
+            fa[i] = *LDS_PTR(const u32x4, st + a_off[i]);
         } else {
-            const int qb = q - A_READS;
-            if constexpr (B_KC) {
-                f.b[qb] = *LDS_PTR(const u32x4, st + b_off[qb][kk]);
-            } else {
-                const int j = qb >> 1, e = qb & 1;
-                read_tr_half(f.b[j], e, st + b_off[j][0] + 16 * ROWB * kk + 4 * ROWB * e);
-            }
+            read_tr_half(fa[i], 0, st + a_off[i]);
+            read_tr_half(fa[i], 1, st + a_off[i] + 4 * ROWB);
         }
     };
-    auto read_frags = [&](Frags &f, int stage, int kk) __attribute__((always_inline)) {
-        const char *st = lds + stage * STAGE_BYTES;
-#pragma unroll
-        for (int q = 0; q < NREAD; ++q)
-            read_one(f, st, kk, q);
+    auto read_b = [&](u32x4 (&fb)[NT], const char *st, int q) __attribute__((always_inline)) {
+        if constexpr (B_KC) {
+            fb[q] = *LDS_PTR(const u32x4, st + b_off[q]);
+        } else {
+            read_tr_half(fb[q >> 1], q & 1, st + b_off[q >> 1] + 4 * ROWB * (q & 1));
+        }
     };
+    constexpr int B_READS = NT * (B_KC ? 1 : 2);
 
-    floatx16 acc[MT][NT];
+    floatx4 acc[MT][NT];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < NT; ++j)
-            acc[i][j] = floatx16{0.0f};
+            acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto mfmas = [&](const Frags &f) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int j = 0; j < NT; ++j)
-                acc[i][j] = mfma<IN>(f.a[i], f.b[j], acc[i][j]);
-    };
-
-    // The MFMAs of one k-step with the reads of the next k-step's fragments
-    // spread evenly between them, and (when `dma`) the loads of chunk
-    // `dma_kt`, DMA_PER_SLOT after every second MFMA.
-    auto half_step = [&](const Frags &cur, Frags &next, const char *next_st, int next_kk,
-                         bool dma, int64_t dma_kt, int dma_stage) __attribute__((always_inline)) {
+    // MFMAs of one chunk (A in fa, B in fb) with, when `reads`, the next
+    // chunk's fragments read from next_st (B into fbn), and the loads of
+    // chunk dma_kt into stage dma_stage (when >= 0), one after every
+    // NMFMA / DMA_GROUP MFMAs.
+    auto step = [&](const u32x4 (&fb)[NT], u32x4 (&fbn)[NT], const char *next_st, bool reads,
+                    int64_t dma_kt, int dma_stage) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < NMFMA; ++q) {
             const int i = q / NT, j = q % NT;
-            acc[i][j] = mfma<IN>(cur.a[i], cur.b[j], acc[i][j]);
-            const int r0 = q * NREAD / NMFMA, r1 = (q + 1) * NREAD / NMFMA;
-#pragma unroll
-            for (int r = r0; r < r1; ++r)
-                read_one(next, next_st, next_kk, r);
-            if (dma && (q & 1)) {
-#pragma unroll
-                for (int d = (q >> 1) * DMA_PER_SLOT; d < ((q >> 1) + 1) * DMA_PER_SLOT; ++d)
-                    if (d < DMA_GROUP)
-                        dma_one(dma_kt, dma_stage, d);
+            acc[i][j] = mfma<IN>(fa[i], fb[j], acc[i][j]);
+            if (reads) {
+                if (q < B_READS)
+                    read_b(fbn, next_st, q);
+                if (j == NT - 1)
+                    read_a(next_st, i);
             }
-            if (dma) {
-                __builtin_amdgcn_sched_barrier(0);  // keep this group in place
-            } else {
-                __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // the MFMA
-#pragma unroll
-                for (int r = r0; r < r1; ++r)
-                    __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);  // its reads
-            }
+            if (dma_stage >= 0 && (q + 1) % (NMFMA / DMA_GROUP) == 0 &&
+                (q + 1) / (NMFMA / DMA_GROUP) <= DMA_GROUP)
+                dma_one(dma_kt, dma_stage, (q + 1) / (NMFMA / DMA_GROUP) - 1);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // Pipeline.  Chunk kt lives in stage kt % 4.  Iteration kt: MFMAs of
-    // k-step 0 while reading k-step 1's fragments; wait until this wave's
-    // loads of chunk kt + 1 have landed and all its LDS reads have returned,
-    // then barrier -- after it every wave is done with stage kt % 4, since
-    // both k-steps of chunk kt were read before it; MFMAs of k-step 1 while
-    // reading chunk kt + 1's first fragments and loading chunk kt + 4 into
-    // stage kt % 4.  Chunks kt + 2 .. kt + 4 are in flight meanwhile.  Past
-    // the end the loads re-read the last chunk into the freed stage, which
-    // keeps the number of loads in flight the same every iteration.
     const int64_t nk = RAGGED ? cdiv(k_split, BK) : k_split / BK;
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
@@ -449,38 +411,54 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 
-    Frags f0, f1;
-    read_frags(f0, 0, 0);
-    for (int64_t kt = 0; kt + 1 < nk; ++kt) {
-        const int stage = static_cast<int>(kt % STAGES);
-        const char *st = lds + stage * STAGE_BYTES;
-        half_step(f0, f1, st, 1, false, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+        read_a(lds, i);
+#pragma unroll
+    for (int q = 0; q < B_READS; ++q)
+        read_b(fb0, lds, q);
+
+    // one iteration: chunk c (B in fb), chunk c + 1 read (B into fbn)
+    auto iter = [&](const u32x4 (&fb)[NT], u32x4 (&fbn)[NT], int64_t c)
+                    __attribute__((always_inline)) {
+        const int stage = static_cast<int>(c % STAGES);
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * DMA_GROUP, 0));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        const int64_t kl = kt + STAGES < nk ? kt + STAGES : nk - 1;
-        half_step(f1, f0, lds + ((stage + 1) % STAGES) * STAGE_BYTES, 0, true, kl, stage);
+        const int64_t kl = c + STAGES < nk ? c + STAGES : nk - 1;
+        step(fb, fbn, lds + ((stage + 1) % STAGES) * STAGE_BYTES, true, kl, stage);
         __builtin_amdgcn_sched_barrier(0);
+    };
+    // nk - 1 iterations read a next chunk; an odd one out runs first (its B
+    // fragments then copied back once), the rest in pairs that swap the two
+    // B buffers, so the last chunk's B fragments always end in fb0.
+    int64_t c = 0;
+    if ((nk - 1) & 1) {
+        iter(fb0, fb1, 0);
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+            fb0[j] = fb1[j];
+        c = 1;
     }
-    // last chunk
-    read_frags(f1, static_cast<int>((nk - 1) % STAGES), 1);
-    mfmas(f0);
-    mfmas(f1);
-    // no load may still be writing LDS when the workgroup ends
+    for (; c + 1 < nk; c += 2) {
+        iter(fb0, fb1, c);
+        iter(fb1, fb0, c + 1);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    step(fb0, fb1, lds, false, 0, -1);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
 
-    // Epilogue: lane holds column lane%32 and rows 8*(v/4) + 4*(lane/32) + v%4
-    // of each 32x32 tile.
+    // Epilogue: lane holds column lane%16 and rows 4*(lane/16) + v of each
+    // 16x16 tile.
     void *c_out = static_cast<char *>(p.C) + slice * c_split_stride * (OUT == DTM_F32 ? 4 : 2);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            const int64_t col = n0 + wn * WN_COLS + j * 32 + (lane & 31);
+            const int64_t col = n0 + wn * WN_COLS + j * 16 + (lane & 15);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = m0 + wm * WM_ROWS + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            for (int v = 0; v < 4; ++v) {
+                const int64_t row = m0 + wm * WM_ROWS + i * 16 + 4 * (lane >> 4) + v;
                 if (!RAGGED || (row < p.M && col < p.N))
                     store_elem<OUT>(c_out, row * p.scm + col * p.scn, acc[i][j][v]);
             }
