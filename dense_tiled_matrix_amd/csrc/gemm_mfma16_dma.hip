@@ -349,12 +349,16 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     for (int j = 0; j < NT; ++j)
         b_off[j] = A_STAGE_BYTES + frag_off<B_KC, TILE>(wn * WN_COLS + j * 16, lane);
 
-    // A fragments are single-buffered: row i's fragment of the next chunk is
-    // read as soon as row i's MFMAs of this chunk have issued.  B fragments
-    // are double-buffered (every row needs them) and read over the first
-    // rows' MFMAs.  This keeps the 256-wide tiles within their registers.
-    u32x4 fa[MT], fb0[NT], fb1[NT];
-    auto read_a = [&](const char *st, int i) __attribute__((always_inline)) {
+    // B fragments are double-buffered (every row needs them).  A fragments
+    // are too when the registers allow it (4 waves: one wave per SIMD, 512
+    // registers); with 8 waves they are single-buffered, row i's fragment of
+    // the next chunk read as soon as row i's MFMAs of this chunk have issued.
+#ifndef DTM_DMA_ADB
+#define DTM_DMA_ADB 1
+#endif
+    constexpr bool A_DB = DTM_DMA_ADB && NWAVES == 4;
+    u32x4 fa0[MT], fa1[MT], fb0[NT], fb1[NT];
+    auto read_a = [&](u32x4 (&fa)[MT], const char *st, int i) __attribute__((always_inline)) {
         if constexpr (A_KC) {
             fa[i] = *LDS_PTR(const u32x4, st + a_off[i]);
         } else {
@@ -370,6 +374,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
         }
     };
     constexpr int B_READS = NT * (B_KC ? 1 : 2);
+    constexpr int A_PER = A_KC ? 1 : 2;  // reads per A fragment
 
     floatx4 acc[MT][NT];
 #pragma unroll
@@ -379,20 +384,33 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
             acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
     // MFMAs of one chunk (A in fa, B in fb) with, when `reads`, the next
-    // chunk's fragments read from next_st (B into fbn), and the loads of
-    // chunk dma_kt into stage dma_stage (when >= 0), one after every
-    // NMFMA / DMA_GROUP MFMAs.
-    auto step = [&](const u32x4 (&fb)[NT], u32x4 (&fbn)[NT], const char *next_st, bool reads,
-                    int64_t dma_kt, int dma_stage) __attribute__((always_inline)) {
+    // chunk's fragments read from next_st (into fan, fbn: spread evenly over
+    // the MFMAs when A is double-buffered, else B over the first MFMAs and
+    // A row by row), and the loads of chunk dma_kt into stage dma_stage
+    // (when >= 0), one after every NMFMA / DMA_GROUP MFMAs.
+    auto step = [&](u32x4 (&fa)[MT], u32x4 (&fan)[MT], const u32x4 (&fb)[NT], u32x4 (&fbn)[NT],
+                    const char *next_st, bool reads, int64_t dma_kt, int dma_stage)
+                    __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < NMFMA; ++q) {
             const int i = q / NT, j = q % NT;
             acc[i][j] = mfma<IN>(fa[i], fb[j], acc[i][j]);
             if (reads) {
-                if (q < B_READS)
-                    read_b(fbn, next_st, q);
-                if (j == NT - 1)
-                    read_a(next_st, i);
+                if constexpr (A_DB) {
+                    const int r0 = q * NREAD / NMFMA, r1 = (q + 1) * NREAD / NMFMA;
+#pragma unroll
+                    for (int r = r0; r < r1; ++r) {
+                        if (r < B_READS)
+                            read_b(fbn, next_st, r);
+                        else if ((r - B_READS) % A_PER == 0)
+                            read_a(fan, next_st, (r - B_READS) / A_PER);
+                    }
+                } else {
+                    if (q < B_READS)
+                        read_b(fbn, next_st, q);
+                    if (j == NT - 1)
+                        read_a(fa, next_st, i);
+                }
             }
             if (dma_stage >= 0 && (q + 1) % (NMFMA / DMA_GROUP) == 0 &&
                 (q + 1) / (NMFMA / DMA_GROUP) <= DMA_GROUP)
@@ -413,39 +431,46 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
 
 #pragma unroll
     for (int i = 0; i < MT; ++i)
-        read_a(lds, i);
+        read_a(fa0, lds, i);
 #pragma unroll
     for (int q = 0; q < B_READS; ++q)
         read_b(fb0, lds, q);
 
-    // one iteration: chunk c (B in fb), chunk c + 1 read (B into fbn)
-    auto iter = [&](const u32x4 (&fb)[NT], u32x4 (&fbn)[NT], int64_t c)
-                    __attribute__((always_inline)) {
+    // one iteration: chunk c in (fa, fb), chunk c + 1 read into (fan, fbn)
+    auto iter = [&](u32x4 (&fa)[MT], u32x4 (&fan)[MT], const u32x4 (&fb)[NT], u32x4 (&fbn)[NT],
+                    int64_t c) __attribute__((always_inline)) {
         const int stage = static_cast<int>(c % STAGES);
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * DMA_GROUP, 0));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         const int64_t kl = c + STAGES < nk ? c + STAGES : nk - 1;
-        step(fb, fbn, lds + ((stage + 1) % STAGES) * STAGE_BYTES, true, kl, stage);
+        step(fa, fan, fb, fbn, lds + ((stage + 1) % STAGES) * STAGE_BYTES, true, kl, stage);
         __builtin_amdgcn_sched_barrier(0);
     };
-    // nk - 1 iterations read a next chunk; an odd one out runs first (its B
-    // fragments then copied back once), the rest in pairs that swap the two
-    // B buffers, so the last chunk's B fragments always end in fb0.
+    // Single-buffered A lives in fa0 throughout.
+    auto& fa1r = A_DB ? fa1 : fa0;
+    // nk - 1 iterations read a next chunk; an odd one out runs first (its
+    // fragments then copied back once), the rest in pairs that swap the
+    // buffers, so the last chunk's fragments always end in fa0 / fb0.
     int64_t c = 0;
     if ((nk - 1) & 1) {
-        iter(fb0, fb1, 0);
+        iter(fa0, fa1r, fb0, fb1, 0);
 #pragma unroll
         for (int j = 0; j < NT; ++j)
             fb0[j] = fb1[j];
+        if constexpr (A_DB) {
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+                fa0[i] = fa1[i];
+        }
         c = 1;
     }
     for (; c + 1 < nk; c += 2) {
-        iter(fb0, fb1, c);
-        iter(fb1, fb0, c + 1);
+        iter(fa0, fa1r, fb0, fb1, c);
+        iter(fa1r, fa0, fb1, fb0, c + 1);
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-    step(fb0, fb1, lds, false, 0, -1);
+    step(fa0, fa1r, fb0, fb1, lds, false, 0, -1);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
 
     // Epilogue: lane holds column lane%16 and rows 4*(lane/16) + v of each
