@@ -247,15 +247,16 @@ int64_t pick_split(const Call &c, int layout, int64_t tiles, int tile)
     return s;
 }
 
-// The pipelined kernel's interior form runs with 4 waves of 128 x 128 (one
-// per SIMD) when a launch has at least this many workgroups, i.e. at least
-// two per CU: each wave then reads a third less LDS per MFMA, and the chip,
-// which is power-limited on this kernel, clocks about 10% higher for a few
-// percent fewer busy MFMA cycles (bf16 8192^3: +1 to +3% by layout).  With
-// one workgroup per CU or fewer, the 8-wave form, whose two waves per SIMD
-// cover each other's waits, was as fast or faster (by up to 2%), and on the
-// range-checked form 8 waves were faster at every size measured.
-constexpr int64_t FOUR_WAVE_MIN_TILES = 512;
+// The pipelined kernel's interior form at tile 256 runs with 4 waves of
+// 128 x 128 (one per SIMD) when each tile's K loop is at least this long,
+// else with 8 waves of 128 x 64 (two per SIMD, which cover each other's
+// waits).  A 4-wave wave reads a third less LDS per MFMA, and on this
+// power-limited chip that shows as clock.  Side by side (bf16 unless noted,
+// TFLOP/s, 8 -> 4 waves): K = 4096 and up gained 0.7-3.8% (fp16 4096^3
+// 1160 -> 1204, 8192^3 1347 -> 1364, 6144^3, 5120^3) except 8192 x 4096 x
+// 4096 (1313 -> 1295); K = 1024 lost (4096 x 4096 x 1024 966 -> 948,
+// 16384 x 16384 x 1024 1068 -> 885).  The range-checked form has 8 waves.
+constexpr int64_t FOUR_WAVE_MIN_K = 2048;
 
 int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
 {
@@ -376,8 +377,7 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
         } else if (p.block_m == 128) {
             p.threads = 256;
         } else {
-            p.threads = !p.ragged && p.grid_m * p.grid_n * p.split_k >= FOUR_WAVE_MIN_TILES ? 256
-                                                                                           : 512;
+            p.threads = !p.ragged && p.k_iters * p.block_k >= FOUR_WAVE_MIN_K ? 256 : 512;
         }
     } else if (force && force->threads) {
         return DTM_ERR_CONFIG;  // a workgroup size is chosen for the pipelined kernel only

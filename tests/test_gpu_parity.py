@@ -280,7 +280,7 @@ def _big_check(p, tile, threads=None):
 
 
 def test_f16_4096_f32out():
-    _big_check(W.workload("f16_4096_f32out"), 256, threads=512)
+    _big_check(W.workload("f16_4096_f32out"), 256, threads=256)
 
 
 def test_bf16_8192_bf16out():
@@ -293,8 +293,8 @@ def test_f16_8192_f32out():
 
 
 def test_bf16_4096_bf16out():
-    """Extra: bf16 4096^3 with bf16 output (one tile per CU, 8 waves)."""
-    _big_check(W.workload("bf16_4096_bf16out"), 256, threads=512)
+    """Extra: bf16 4096^3 with bf16 output (one tile per CU, 4 waves)."""
+    _big_check(W.workload("bf16_4096_bf16out"), 256, threads=256)
 
 
 def test_f16_skinny_long_k():
@@ -420,16 +420,17 @@ def test_pipelined_layouts_random(layout):
 
 @pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])
 def test_four_wave_selector_random(layout):
-    """512 output tiles: the selector's 4-wave form of the pipelined kernel,
-    N(0,1) bf16 in every layout, compared in full within the stated
-    tolerance."""
-    p = W.random_problem(4096, 8192, 256, "bf16", "bf16", ("normal", 0.0, 1.0), seed=720,
+    """192 tiles of 256 and a 2048-long K loop: the selector's 4-wave form
+    of the pipelined kernel, N(0,1) bf16 in every layout, compared in full
+    within the stated tolerance."""
+    p = W.random_problem(4096, 3072, 2048, "bf16", "bf16", ("normal", 0.0, 1.0), seed=720,
                          a_layout=layout[0], b_layout=layout[1])
     plan = {}
     c, untouched = run(p, plan=plan)
-    assert (plan["block_k"], plan["threads"], plan["ragged"]) == (32, 256, 0), plan
+    assert (plan["block_m"], plan["block_k"], plan["threads"], plan["ragged"]) == \
+        (256, 32, 256, 0), plan
     assert plan["layout"] == LAYOUT_BITS[layout], plan
-    err, tol = compare(p, c, label=f"4 waves {layout} 4096x8192x256")
+    err, tol = compare(p, c, label=f"4 waves {layout} 4096x3072x2048")
     note(f"4 waves {layout}: max err {err:.3e} tol {tol:.3e}")
     assert untouched
 

@@ -129,7 +129,7 @@ def test_selector_transposed_layouts():
         st, p = plan(4096, 4096, 4096, ind=BF16, outd=BF16, **big, **kw)
         assert st == 0 and p["kernel_name"] == "mfma_f16" and p["fast_path"] == 1, kw
         assert (p["block_m"], p["block_k"], p["layout"], p["split_k"]) == (256, 32, bits, 1), kw
-        assert p["threads"] == 512
+        assert p["threads"] == 256  # 4096-long K loop: 4 waves
         # ragged: the register-staged kernel, same layout bits
         rk = {0: dict(sam=4104, sbk=4104), LA: dict(sam=1, sak=4104, sbk=4104),
               LB: dict(sam=4104, sbk=1, sbn=4104), LA | LB: dict(sam=1, sak=4104, sbk=1,
@@ -307,16 +307,19 @@ def test_forced_configs():
 
 
 def test_pipelined_wave_count():
-    """The pipelined tile runs 4 waves (256 threads) on its interior form
-    when a launch has at least 512 workgroups, else 8 (512 threads); a
-    forced size must be one the form has, and only that tile takes one."""
+    """The 256-wide pipelined tile runs 4 waves (256 threads) on its interior
+    form when each tile's K loop is at least 2048 long, else 8 (512
+    threads); the 128-wide tile runs 4; a forced size must be one the form
+    has, and only that tile takes one."""
     big = dict(A=1 << 40, B=2 << 40, C=3 << 40)
     for (M, N, K, kw, threads) in [
-            (8192, 8192, 8192, dict(), 256),                       # 1024 tiles
+            (8192, 8192, 8192, dict(), 256),
             (8192, 8192, 8192, dict(sam=1, sak=8192, sbk=1, sbn=8192), 256),
-            (4096, 8192, 64, dict(), 256),                         # 512 tiles
-            (4096, 7936, 64, dict(), 512),                         # 496 tiles
-            (4096, 4096, 4096, dict(), 512),                       # 256 tiles
+            (4096, 4096, 4096, dict(), 256),
+            (4096, 4096, 2048, dict(), 256),
+            (4096, 4096, 2016, dict(), 512),                       # K loop under 2048
+            (16384, 16384, 1024, dict(), 512),
+            (4096, 8192, 64, dict(), 512),
             (8000, 8000, 8000, dict(), 512),                       # range-checked form
             (512, 512, 65536, dict(), 256)]:                       # 128-wide tiles
         st, p = plan(M, N, K, ind=BF16, outd=BF16, **big, **kw)
