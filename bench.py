@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,17 +31,26 @@ METRIC = "GEMM TFLOP/s and % of MFMA peak at fp16/bf16 4096³ and 8192³ on 1 MI
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 HOST_THREADS_CAP = 16  # the host-core share of one GPU on the GPU machines
-# sources of the timed kernel (the 256 x 256 x 32 pipelined MFMA kernel)
+# sources of the kernels whose traffic profiles/traffic.json records (the
+# pipelined MFMA GEMM, the split-K reduce, the row softmax)
 KERNEL_SOURCES = ["dense_tiled_matrix_amd/csrc/gemm_mfma16_dma.hip",
+                  "dense_tiled_matrix_amd/csrc/gemm_splitk.hip",
+                  "dense_tiled_matrix_amd/csrc/softmax.hip",
                   "dense_tiled_matrix_amd/csrc/device.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: comments and blank lines are left
+    out, so an edit of the prose alone keeps recorded counters valid."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        for line in text.splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

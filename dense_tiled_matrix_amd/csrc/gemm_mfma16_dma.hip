@@ -49,9 +49,11 @@
 //    16-lane group the i-th column of a 4 x 16 block whose rows the lanes
 //    address, i.e. four consecutive k of one row/column -- the operand
 //    layout the MFMA wants, with no transpose anywhere else.
-//  * A fragments are single-buffered (row i's fragment of the next chunk is
-//    read once row i's MFMAs have issued), B fragments double-buffered, the
-//    loop unrolled in pairs so the two B buffers swap without copies.
+//  * B fragments are double-buffered.  A fragments are too in the 4-wave
+//    form (its reads then spread evenly between the MFMAs); the 8-wave form,
+//    short of registers, keeps one A buffer and reads row i's fragment of
+//    the next chunk once row i's MFMAs have issued.  The loop is unrolled in
+//    pairs so the buffers swap without copies.
 //  * Workgroup ids are remapped so that each XCD owns a compact group of
 //    tiles (shared A rows and B columns stay in its L2).
 #include "launch.h"
