@@ -223,7 +223,10 @@ bool dma_any(const Call &c, int layout, int64_t splits, int tile = 256)
 {
     return dma_interior(c, layout, splits, tile) || dma_ranged(c, layout, splits, tile);
 }
-bool is_dma_tile(int bm, int bn, int bk) { return bm == bn && (bm == 256 || bm == 128) && bk == 32; }
+bool is_dma_tile(int bm, int bn, int bk)
+{
+    return bm == bn && (bm == 256 || bm == 192 || bm == 128) && bk == 32;
+}
 
 // Tile of the pipelined kernel: 256 x 256 while there are more than
 // SMALL_TILE_MAX such tiles, else 128 x 128 (four times the workgroups).
@@ -233,6 +236,34 @@ bool is_dma_tile(int bm, int bn, int bk) { return bm == bn && (bm == 256 || bm =
 // other way at 144 tiles of 256 (3072^3 881 vs 763, ragged 3000^3 780 vs
 // 577) and at 256 (4096x4096x1024 964 vs 771).
 constexpr int64_t SMALL_TILE_MAX = 128;
+
+// Above that, 192 x 192 tiles when they fill the CUs' rounds better, by
+// enough to pay for their lower rate: a 192-wide workgroup (96 x 96 per
+// wave) reads a third more operand bytes per MFMA than a 256-wide one and
+// runs at about 0.82 of its rate (0.72 in the range-checked form, on
+// shapes 192 does not divide), measured at full rounds.  Each form is
+// scored as rate x fill, fill = tiles / (rounds x 256 CUs), one workgroup
+// per CU at either size.  Measured, bf16 TFLOP/s (256 -> 192): 3072^3
+// 879 -> 1127, 6144^3 1130 -> 1232, ragged 3000^3 778 -> 920, 6144^2 x
+// 2048 993 -> 1054, 3072^2 x 1024 707 -> 818; and the other way 3840^3
+// 1254 vs 1020, 4608^3 970 vs 958, 5120^3 1199 vs 1015, 12288^2 x 1024
+// 1087 vs 924.
+constexpr int64_t CUS = 256;
+constexpr double RATE_192 = 0.82, RATE_192_RAGGED = 0.72;
+
+double round_fill(int64_t tiles)
+{
+    return static_cast<double>(tiles) / static_cast<double>(cdiv(tiles, CUS) * CUS);
+}
+
+bool prefer_192(const Call &c, int layout)
+{
+    if (!dma_any(c, layout, 1, 192))
+        return false;
+    const double r = dma_interior(c, layout, 1, 192) ? RATE_192 : RATE_192_RAGGED;
+    return r * round_fill(cdiv(c.M, 192) * cdiv(c.N, 192)) >
+           round_fill(cdiv(c.M, 256) * cdiv(c.N, 256));
+}
 
 // Split-K for problems whose 128 x 128 tiles still cannot fill the chip and
 // whose K is long: the largest power-of-two split that keeps tiles x split
@@ -311,11 +342,13 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
             // The pipelined kernel whenever it can run the problem (measured
             // ahead of the register-staged kernel at every tile count): with
             // 128-wide tiles, and split-K when even those are few and K is
-            // long, when the 256-wide tiles are few; otherwise the
-            // register-staged kernel.
+            // long, when the 256-wide tiles are few; with 192-wide tiles when
+            // they fill the CUs better; otherwise the register-staged kernel.
             const int64_t tiles256 = cdiv(c.M, 256) * cdiv(c.N, 256);
             if (dma) {
-                const int tile = tiles256 <= SMALL_TILE_MAX && dma_any(c, layout, 1, 128) ? 128 : 256;
+                const int tile = tiles256 <= SMALL_TILE_MAX && dma_any(c, layout, 1, 128) ? 128
+                                 : prefer_192(c, layout)                                 ? 192
+                                                                                         : 256;
                 p.block_m = p.block_n = tile;
                 p.block_k = 32;
                 p.split_k = tile == 128 ? static_cast<int32_t>(pick_split(
@@ -374,8 +407,8 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
                 !dtm::mfma16_dma_waves_ok(p.block_m, forced_threads / 64, p.ragged))
                 return DTM_ERR_CONFIG;
             p.threads = forced_threads;
-        } else if (p.block_m == 128) {
-            p.threads = 256;
+        } else if (p.block_m != 256) {
+            p.threads = 256;  // 192 and 128: 4 waves
         } else {
             p.threads = !p.ragged && p.k_iters * p.block_k >= FOUR_WAVE_MIN_K ? 256 : 512;
         }

@@ -20,7 +20,9 @@
 // Lesson 4: a transpose is only a change of strides).
 //
 // gfx950 design:
-//  * One workgroup per TILE x TILE output tile (TILE 256 or 128).  NWAVES
+//  * One workgroup per TILE x TILE output tile (TILE 256, 192 or 128; the
+//    192-wide tile fills the 256 CUs where 256-wide ones leave a round
+//    part-empty, e.g. 3072^3: 256 tiles of 192 against 144 of 256).  NWAVES
 //    wave64s (2 x NWAVES/2) each own TILE/2 x TILE/(NWAVES/2) of C as blocks
 //    of v_mfma_f32_16x16x32_{f16,bf16} with fp32 accumulators (in the
 //    AccVGPR file when they do not fit beside the rest).  That instruction
@@ -39,13 +41,16 @@
 //    row/column l % 16.  An operand that is K-contiguous in memory is staged
 //    as TILE rows of 64 bytes; the 16-byte chunk c of row r sits at
 //    c ^ f(r), f(r) = (r >> 2) & 3, and a fragment is one ds_read_b128 per
-//    lane (16 consecutive rows of one chunk cover all 64 banks once;
-//    measured on gfx950: zero SQ_LDS_BANK_CONFLICT, other XOR patterns cost
-//    4-12 extra cycles per read).
+//    lane (16 consecutive rows of one chunk cover all 64 banks once; a
+//    probe of the 32-row lane order of 32 x 32 MFMAs measured no conflicts,
+//    other XOR patterns 4-12 extra cycles per read; with this kernel's
+//    16-row order the counters still show some).
 //  * An operand that is M- or N-contiguous stays that way: 32 k-rows of
 //    2 * TILE bytes, chunk c of k-row k at c ^ g(k), g = {0, 6, 10, 12}[k % 4]
-//    (measured conflict-free; no swizzle costs about 6 extra cycles per
-//    read).  A fragment is two ds_read_b64_tr_b16, which hand lane i of each
+//    XOR 2 for k % 16 >= 8.  Without the k % 16 term the two 16-lane groups
+//    of a read, on k-rows 8 apart, hit the same banks: SQ_LDS_BANK_CONFLICT
+//    then counted 50% of the kernel's LDS-active cycles, with it 33% (the
+//    rest from the 64-byte-row reads below; the time did not change).  A fragment is two ds_read_b64_tr_b16, which hand lane i of each
 //    16-lane group the i-th column of a 4 x 16 block whose rows the lanes
 //    address, i.e. four consecutive k of one row/column -- the operand
 //    layout the MFMA wants, with no transpose anywhere else.
@@ -72,7 +77,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 32, STAGES = 4;
 // A TILE x TILE output tile stages TILE x BK of each operand per chunk:
-// 16 KiB each at TILE = 256, 8 KiB at 128.
+// 16 KiB each at TILE = 256, 12 KiB at 192, 8 KiB at 128.
 template <int TILE> constexpr int operand_stage_bytes() { return TILE * BK * 2; }
 #ifndef DTM_DMA_GROUP_M
 #define DTM_DMA_GROUP_M 4
@@ -90,8 +95,9 @@ constexpr int waitcnt_imm(int vm, int lgkm)
 __device__ __forceinline__ int swz_row(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int swz_krow(int k)
 {
-    // 0, 6, 10, 12 for k % 4 = 0..3
-    return (0xCA60 >> (4 * (k & 3))) & 15;
+    // 0, 6, 10, 12 for k % 4 = 0..3, XOR 2 when k % 16 >= 8: a fragment read
+    // has 16-lane groups on k-rows 8 apart, which then land on other banks
+    return ((0xCA60 >> (4 * (k & 3))) & 15) ^ ((k & 8) >> 2);
 }
 
 // 16 bytes per lane from global memory straight into LDS at
@@ -131,17 +137,44 @@ __device__ __forceinline__ void dma16_buf(const i32x4 &rsrc, uint32_t voff, uint
 // Offset past every buffer this kernel builds (they are at most 2^31 bytes).
 constexpr uint32_t OUTSIDE = 0x80000000u;
 
-// An M/N-contiguous operand is staged as BK k-rows of TILE elements: LPR
-// 16-byte chunks per k-row, RPS k-rows per 1 KiB load segment.
+// An M/N-contiguous operand is staged as BK k-rows of TILE elements, TILE / 8
+// 16-byte chunks per k-row, filled in order by the 1 KiB load segments.
 template <int TILE> constexpr int krow_chunks() { return TILE / 8; }
-template <int TILE> constexpr int krows_per_seg() { return 64 / krow_chunks<TILE>(); }
+
+// Physical chunk, within k-row k of such a stage, of logical chunk c, and
+// back.  TILE 256 and 128 XOR the chunk index with swz_krow(k).  A 192-wide
+// k-row (24 chunks, 384 bytes) already puts odd k-rows 32 banks on, so
+// there the chunk index is rotated by 2 * ((k >> 1) & 1) + 4 * ((k >> 3) & 1):
+// the eight k-rows a 32-lane half of a fragment read touches (k0..k0+3 and
+// k0+8..k0+11) then cover the 64 banks once (checked on every fragment of
+// the tile against a model of 32 lanes served per cycle).  Both keep k and
+// k + 4 (the two halves of a fragment, k % 8 < 4) on the same permutation.
+template <int TILE> __device__ __forceinline__ int krow_phys(int c, int k)
+{
+    if constexpr (TILE == 192) {
+        const int p = c + (k & 2) + ((k & 8) >> 1);
+        return p >= 24 ? p - 24 : p;
+    } else {
+        return c ^ swz_krow(k);
+    }
+}
+template <int TILE> __device__ __forceinline__ int krow_logical(int p, int k)
+{
+    if constexpr (TILE == 192) {
+        const int c = p - (k & 2) - ((k & 8) >> 1);
+        return c < 0 ? c + 24 : c;
+    } else {
+        return p ^ swz_krow(k);
+    }
+}
 
 // Global source of this lane for 1 KiB segment `seg` of an operand's stage.
 // X points at element (0, 0) of the operand viewed as [mn][k]; mn0 and kb
 // are the tile's first row/column and the slice's first k.
-//  K-contiguous (KC): rows 16*seg + lane/4, physical chunk lane % 4.
-//  otherwise: k-rows RPS*seg + lane/LPR, physical chunk lane % LPR.
-// The logical chunk is the physical one XOR the row's swizzle.  Chunk kt of
+//  K-contiguous (KC): rows 16*seg + lane/4, physical chunk lane % 4; the
+//    logical chunk is the physical one XOR the row's swizzle.
+//  otherwise: g = 64*seg + lane, k-row g / LPR, physical chunk g % LPR (the
+//    logical one from krow_logical).  Chunk kt of
 // the K loop is kt * BK elements further along K.
 template <bool KC, int TILE>
 __device__ __forceinline__ const uint16_t *stage_src(const uint16_t *X, int64_t mn0, int64_t s_mn,
@@ -152,9 +185,9 @@ __device__ __forceinline__ const uint16_t *stage_src(const uint16_t *X, int64_t 
         const int c = (lane & 3) ^ swz_row(r);
         return X + (mn0 + r) * s_mn + kb + 8 * c;
     } else {
-        constexpr int LPR = krow_chunks<TILE>(), RPS = krows_per_seg<TILE>();
-        const int k = RPS * seg + lane / LPR;
-        const int c = (lane % LPR) ^ swz_krow(k);
+        constexpr int LPR = krow_chunks<TILE>();
+        const int g = 64 * seg + lane, k = g / LPR;
+        const int c = krow_logical<TILE>(g % LPR, k);
         return X + (kb + k) * s_k + mn0 + 8 * c;
     }
 }
@@ -179,9 +212,9 @@ __device__ __forceinline__ void stage_off(int64_t mn0, int64_t s_mn, int64_t s_k
         e = mn * s_mn + kf;
         ok = mn < ext;
     } else {
-        constexpr int LPR = krow_chunks<TILE>(), RPS = krows_per_seg<TILE>();
-        const int k = RPS * seg + lane / LPR;
-        const int c = (lane % LPR) ^ swz_krow(k);
+        constexpr int LPR = krow_chunks<TILE>();
+        const int g = 64 * seg + lane, k = g / LPR;
+        const int c = krow_logical<TILE>(g % LPR, k);
         mn = mn0 + 8 * c;
         kf = kb + k;
         e = kf * s_k + mn;
@@ -234,7 +267,7 @@ template <bool KC, int TILE> __device__ __forceinline__ int frag_off(int base, i
     } else {
         const int k = 8 * G + (li >> 2);
         const int n = base + 4 * (li & 3);
-        return k * (TILE * 2) + (((n >> 3) ^ swz_krow(k)) * 16) + ((n >> 2) & 1) * 8;
+        return k * (TILE * 2) + krow_phys<TILE>(n >> 3, k) * 16 + ((n >> 2) & 1) * 8;
     }
 }
 
@@ -497,7 +530,7 @@ struct DmaLaunch {
     int64_t splits;
     bool ragged;
     uint32_t a_bytes, b_bytes;
-    int tile;   // 256 or 128
+    int tile;   // 256, 192 or 128
     int waves;  // see waves_ok
 };
 
@@ -524,12 +557,15 @@ hipError_t launch_one(const GemmArgs &a, const DmaLaunch &l, hipStream_t s)
 }
 
 // The instantiated (tile, waves, form) combinations: 256 with 8 waves in
-// either form or 4 waves in the interior form, 128 with 4 waves in either.
+// either form or 4 waves in the interior form, 192 and 128 with 4 waves in
+// either.
 template <int IN, int OUT, bool TA, bool TB>
 hipError_t launch(const GemmArgs &a, const DmaLaunch &l, hipStream_t s)
 {
     if (l.tile == 128)
         return launch_one<IN, OUT, 128, 4, TA, TB>(a, l, s);
+    if (l.tile == 192)
+        return launch_one<IN, OUT, 192, 4, TA, TB>(a, l, s);
     if (l.waves == 4 && !l.ragged) {
         hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, 256, 4, TA, TB, false>),
                            dim3((unsigned)(cdiv(a.M, 256) * cdiv(a.N, 256) * l.splits)),
@@ -579,7 +615,7 @@ hipError_t dispatch_in(const GemmArgs &a, int in, int layout, int out, const Dma
 
 bool mfma16_dma_fits(int64_t M, int64_t N, int64_t K, int64_t splits, int tile)
 {
-    return (tile == 256 || tile == 128) && M > 0 && N > 0 && K > 0 && splits > 0 &&
+    return (tile == 256 || tile == 192 || tile == 128) && M > 0 && N > 0 && K > 0 && splits > 0 &&
            M % tile == 0 && N % tile == 0 && K % (BK * splits) == 0 &&
            (M / tile) * (N / tile) * splits <= 0x7fffffffLL;
 }
@@ -588,7 +624,7 @@ bool mfma16_dma_ragged_fits(int64_t M, int64_t N, int64_t K, int layout, uint64_
                             uint64_t b_bytes, int64_t splits, int tile)
 {
     const bool ta = layout & DTM_LAYOUT_A_M_CONTIG, tb = layout & DTM_LAYOUT_B_K_CONTIG;
-    return (tile == 256 || tile == 128) && M > 0 && N > 0 && K > 0 && K % 8 == 0 &&
+    return (tile == 256 || tile == 192 || tile == 128) && M > 0 && N > 0 && K > 0 && K % 8 == 0 &&
            (!ta || M % 8 == 0) && (tb || N % 8 == 0) && a_bytes <= (1ull << 31) &&
            b_bytes <= (1ull << 31) && splits >= 1 && (splits == 1 || N % 4 == 0) &&
            (splits - 1) * slice_k(K, splits, true) < K &&
@@ -597,7 +633,7 @@ bool mfma16_dma_ragged_fits(int64_t M, int64_t N, int64_t K, int layout, uint64_
 
 bool mfma16_dma_waves_ok(int tile, int waves, bool ragged)
 {
-    if (tile == 128)
+    if (tile == 128 || tile == 192)
         return waves == 4;
     return tile == 256 && (waves == 8 || (waves == 4 && !ragged));
 }

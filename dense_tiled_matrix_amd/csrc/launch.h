@@ -24,12 +24,13 @@ bool mfma16_has_config(int bm, int bn, int bk);
 hipError_t launch_mfma16(const GemmArgs &a, int in_dtype, int out_dtype, int bm, int bn, int bk,
                          int layout, bool ragged, hipStream_t s);
 
-// Deep-pipelined MFMA kernel (tile x tile x 32 tiles, tile 256 or 128,
+// Deep-pipelined MFMA kernel (tile x tile x 32 tiles, tile 256, 192 or 128,
 // global -> LDS DMA) when M and N are multiples of the tile and K of 32, for
 // every operand layout: `layout` holds dtm_layout bits (A M-contiguous, B
 // K-contiguous).  `waves` per workgroup: at tile 256, 8 (each owns 128 x 64
 // of the tile, two waves per SIMD) or 4 (128 x 128 each, one wave per SIMD:
-// a third fewer LDS reads per MFMA; the interior form only); at tile 128, 4
+// a third fewer LDS reads per MFMA; the interior form only); at tile 192, 4
+// (96 x 96 each; 96 KiB of LDS, one workgroup per CU); at tile 128, 4
 // (64 x 64 each; 64 KiB of LDS, so two workgroups share a CU).
 bool mfma16_dma_fits(int64_t M, int64_t N, int64_t K, int64_t splits, int tile);
 bool mfma16_dma_waves_ok(int tile, int waves, bool ragged);

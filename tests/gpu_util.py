@@ -33,9 +33,11 @@ def sentinel_bits(value: float, dtype: str):
 
 class CBuf:
     """An output view (M x N, strides scm/scn, element offset) inside a
-    device buffer pre-filled with a sentinel."""
+    device buffer pre-filled with a sentinel.  The offset defaults to 3
+    elements when the leading dimension is padded (a misaligned view), else
+    0."""
 
-    def __init__(self, M, N, dtype, layout="N", sentinel=float("nan"), pad=0):
+    def __init__(self, M, N, dtype, layout="N", sentinel=float("nan"), pad=0, offset=None):
         self.M, self.N, self.dtype = M, N, dtype
         if layout == "N":
             self.scm, self.scn = N + pad, 1
@@ -43,7 +45,7 @@ class CBuf:
             self.scm, self.scn = 1, M + pad
         else:
             raise ValueError(layout)
-        self.offset = 3 if pad else 0
+        self.offset = (3 if pad else 0) if offset is None else offset
         size = self.offset + max(M * self.scm, N * self.scn, 1) + pad + 4
         self.sentinel = sentinel_bits(sentinel, dtype)
         self.buf = torch.full((size,), int(self.sentinel), dtype=torch.int32 if dtype == "f32"
@@ -63,7 +65,7 @@ class CBuf:
 
 
 def run(p, out_dtype=None, config=None, c_layout="N", c_pad=0, stream=None, expect=0,
-        plan=None):
+        plan=None, c_offset=None):
     """GEMM of problem ``p`` on the GPU; returns (C bits M x N, untouched).
     A dict passed as ``plan`` receives the plan of the call."""
     od = out_dtype or p.out_dtype
@@ -71,7 +73,7 @@ def run(p, out_dtype=None, config=None, c_layout="N", c_pad=0, stream=None, expe
     sb = dev_storage(p.B.bits, p.in_dtype) if p.B.bits.size else None
     a_ptr = sa.data_ptr() + p.A.offset * ITEM[p.in_dtype] if sa is not None else 0
     b_ptr = sb.data_ptr() + p.B.offset * ITEM[p.in_dtype] if sb is not None else 0
-    c = CBuf(p.M, p.N, od, c_layout, pad=c_pad)
+    c = CBuf(p.M, p.N, od, c_layout, pad=c_pad, offset=c_offset)
     s = torch.cuda.current_stream() if stream is None else stream
     if plan is not None:
         pst, pd = dtm.gemm_plan_raw(p.M, p.N, p.K, a_ptr, p.A.stride_r, p.A.stride_c, b_ptr,

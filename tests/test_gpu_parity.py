@@ -375,17 +375,18 @@ def test_mfma_pipelined_exact(ind):
         assert untouched
 
 
-@pytest.mark.parametrize("tile,threads", [(256, 512), (256, 256), (128, 256)])
+@pytest.mark.parametrize("tile,threads", [(256, 512), (256, 256), (192, 256), (128, 256)])
 @pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])
 @pytest.mark.parametrize("ind", ["f16", "bf16"])
 def test_pipelined_layouts_exact(ind, layout, tile, threads):
     """Every operand layout on the pipelined kernel: 256-wide tiles with 8
-    and with 4 waves, 128-wide tiles with 4 (A M-contiguous and/or B
-    K-contiguous, staged as stored and read with transposing LDS reads):
+    and with 4 waves, 192- and 128-wide tiles with 4 (A M-contiguous and/or
+    B K-contiguous, staged as stored and read with transposing LDS reads):
     pipeline depths 1, 3, 5 and many chunks, several grids, padded leading
     dimensions, split-K; value-exact on integer-valued inputs."""
-    shapes = [(256, 256, 32, 1), (512, 256, 96, 1), (256, 768, 160, 1), (768, 512, 2048, 1),
-              (512, 512, 4096, 8), (256, 256, 1024, 4)]
+    u = 192 if tile == 192 else 256  # shapes in whole tiles of 192, else of 256
+    shapes = [(u, u, 32, 1), (2 * u, u, 96, 1), (u, 3 * u, 160, 1), (3 * u, 2 * u, 2048, 1),
+              (2 * u, 2 * u, 4096, 8), (u, u, 1024, 4)]
     for n, (M, N, K, S) in enumerate(shapes):
         outd = ["f32", "f16", "bf16"][n % 3]
         p = padded_int_problem(M, N, K, ind, outd, 8 if K <= 256 else 2, seed=600 + n,
@@ -435,11 +436,29 @@ def test_four_wave_selector_random(layout):
     assert untouched
 
 
+@pytest.mark.parametrize("layout", ["NN", "TT"])
+def test_192_selector_random(layout):
+    """Shapes whose 256-wide tiles leave a round of the CUs part-empty: the
+    selector's 192-wide tiles, interior (3072 x 3072 x 1024) and
+    range-checked (3000 x 3000 x 1000), N(0,1) bf16 compared in full within
+    the stated tolerance."""
+    for M, N, K, ragged, seed in [(3072, 3072, 1024, 0, 730), (3000, 3000, 1000, 1, 731)]:
+        p = W.random_problem(M, N, K, "bf16", "bf16", ("normal", 0.0, 1.0), seed=seed,
+                             a_layout=layout[0], b_layout=layout[1])
+        plan = {}
+        c, untouched = run(p, plan=plan)
+        assert (plan["block_m"], plan["block_k"], plan["threads"], plan["ragged"]) == \
+            (192, 32, 256, ragged), plan
+        err, tol = compare(p, c, label=f"192 {layout} {M}x{N}x{K}")
+        note(f"192 {layout} {M}x{N}x{K}: max err {err:.3e} tol {tol:.3e}")
+        assert untouched
+
+
 def _round8(x):
     return -(-x // 8) * 8
 
 
-@pytest.mark.parametrize("tile", [256, 128])
+@pytest.mark.parametrize("tile", [256, 192, 128])
 @pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])
 @pytest.mark.parametrize("ind", ["f16", "bf16"])
 def test_pipelined_ragged_exact(ind, layout, tile):
@@ -469,6 +488,29 @@ def test_pipelined_ragged_exact(ind, layout, tile):
         assert untouched
 
 
+@pytest.mark.parametrize("tile", [256, 192, 128])
+def test_pipelined_output_views(tile):
+    """The pipelined kernel's store of C through views of every kind: rows
+    4-element aligned with N not a multiple of 4 (whole 4-column groups
+    written at once, the group across N element by element), a column-major
+    C, and row strides or base addresses that rule out the wide store.
+    Value-exact on integer-valued inputs; C outside the view untouched."""
+    cfg = dict(kernel=MF16, block_m=tile, block_n=tile, block_k=32)
+    # (M, N, K, C layout, pad, offset): B is K-contiguous, so N may be any size
+    cases = [(300, 250, 96, "N", 6, 0), (512, 256, 64, "N", 4, 4), (264, 258, 160, "N", 2, 0),
+             (256, 512, 64, "T", 0, 0), (520, 256, 32, "N", 4, 2), (256, 254, 64, "N", 2, 8)]
+    for n, (M, N, K, cl, pad, off) in enumerate(cases):
+        for outd in ("f32", "f16", "bf16"):
+            p = padded_int_problem(M, N, K, "bf16" if n % 2 else "f16", outd, 4, seed=870 + n,
+                                   b_layout="T")
+            plan = {}
+            c, untouched = run(p, config=cfg, c_layout=cl, c_pad=pad, c_offset=off, plan=plan)
+            assert plan["status"] == 0 and plan["block_m"] == tile, plan
+            label = f"output view {tile} {M}x{N}x{K} C {cl} pad {pad} offset {off} -> {outd}"
+            compare(p, c, exact=True, label=label)
+            assert untouched, label
+
+
 @pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])
 def test_pipelined_ragged_random_selector(layout):
     """A large ragged bf16 problem (4000 x 4008 x 520, N(0,1)) through the
@@ -484,7 +526,7 @@ def test_pipelined_ragged_random_selector(layout):
     assert untouched
 
 
-@pytest.mark.parametrize("tile", [256, 128])
+@pytest.mark.parametrize("tile", [256, 192, 128])
 @pytest.mark.parametrize("layout", ["NN", "TT"])
 def test_split_k_ragged_exact(layout, tile):
     """Split-K on the range-checked pipelined kernel: ragged M and N, slices
@@ -538,19 +580,19 @@ def test_split_k_exact(ind):
 
 @pytest.mark.parametrize("ind", ["f16", "bf16"])
 def test_many_tiles_exact(ind):
-    """More 256x256 work units than compute units on the pipelined kernel
-    (several tiles per CU in turn): 1-, 2- and 3-chunk units, and split-K
-    with more (tile, slice) units than CUs.  Value-exact on integer-valued
-    inputs."""
-    cases = [(4352, 4352, 32, 1), (4352, 4352, 64, 1), (4096, 4608, 96, 1),
-             (2560, 2560, 1024, 4)]
-    for n, (M, N, K, S) in enumerate(cases):
-        outd = ["bf16", "f32", "f16", "f32"][n]
-        cfg = dict(kernel=MF16, block_m=256, block_n=256, block_k=32, split_k=S)
+    """More 256x256 (and 192x192) work units than compute units on the
+    pipelined kernel (several tiles per CU in turn): 1-, 2-, 3- and 5-chunk
+    units, and split-K with more (tile, slice) units than CUs.  Value-exact
+    on integer-valued inputs."""
+    cases = [(4352, 4352, 32, 1, 256), (4352, 4352, 64, 1, 256), (4096, 4608, 96, 1, 256),
+             (2560, 2560, 1024, 4, 256), (4608, 4608, 64, 1, 192), (4032, 4608, 160, 1, 192)]
+    for n, (M, N, K, S, tile) in enumerate(cases):
+        outd = ["bf16", "f32", "f16", "f32", "bf16", "f16"][n]
+        cfg = dict(kernel=MF16, block_m=tile, block_n=tile, block_k=32, split_k=S)
         p = padded_int_problem(M, N, K, ind, outd, 4, seed=700 + n)
-        note(f"many tiles {ind} {M}x{N}x{K} split {S}")
+        note(f"many tiles {ind} {M}x{N}x{K} tile {tile} split {S}")
         c, untouched = run(p, config=cfg)
-        compare(p, c, exact=True, label=f"many tiles {ind} {M}x{N}x{K} split {S}")
+        compare(p, c, exact=True, label=f"many tiles {ind} {M}x{N}x{K} tile {tile} split {S}")
         assert untouched
 
 

@@ -82,14 +82,24 @@ def test_selector_measured_workloads():
     assert st == 0 and p["kernel_name"] == "mfma_f16" and p["split_k"] == 16
     assert (p["block_m"], p["block_k"], p["k_iters"], p["threads"]) == (128, 32, 128, 256)
     assert p["workspace_bytes"] == 16 * 512 * 512 * 4
-    # few 256-wide tiles: 128-wide ones, split only with K long enough
+    # few 256-wide tiles: 128-wide ones, split only with K long enough;
+    # 192-wide ones where they fill the 256 CUs' rounds enough better
     for M, N, K, tile, S in [(2048, 2048, 2048, 128, 1), (1024, 1024, 8192, 128, 4),
                              (1024, 1024, 1024, 128, 1), (8192, 1024, 8192, 128, 1),
-                             (2560, 2560, 2560, 128, 1), (3072, 3072, 3072, 256, 1),
-                             (4096, 4096, 1024, 256, 1), (2000, 2000, 2000, 128, 1)]:
+                             (2560, 2560, 2560, 128, 1), (3072, 3072, 3072, 192, 1),
+                             (4096, 4096, 1024, 256, 1), (2000, 2000, 2000, 128, 1),
+                             (6144, 6144, 6144, 192, 1), (6144, 6144, 2048, 192, 1),
+                             (3072, 3072, 1024, 192, 1), (3000, 3000, 3000, 192, 1),
+                             (4608, 4608, 4608, 256, 1), (3840, 3840, 3840, 256, 1),
+                             (5120, 5120, 5120, 256, 1), (7168, 7168, 7168, 256, 1),
+                             (8192, 8192, 8192, 256, 1), (12288, 12288, 1024, 256, 1),
+                             (4096, 3072, 2048, 256, 1)]:
         st, p = plan(M, N, K, A=1 << 40, B=2 << 40, C=3 << 40, ind=BF16, outd=BF16)
         assert st == 0 and (p["block_m"], p["block_k"], p["split_k"]) == (tile, 32, S), \
             (M, N, K, p)
+        if tile != 256:
+            assert p["threads"] == 256, (M, N, K, p)
+        assert p["ragged"] == (1 if (M % tile or N % tile) else 0), (M, N, K, p)
     # enough tiles: no split
     st, p = plan(4096, 4096, 65536, A=1 << 40, B=2 << 40, C=3 << 40, ind=F16, outd=F32)
     assert st == 0 and p["split_k"] == 1 and p["workspace_bytes"] == 0
@@ -309,8 +319,8 @@ def test_forced_configs():
 def test_pipelined_wave_count():
     """The 256-wide pipelined tile runs 4 waves (256 threads) on its interior
     form when each tile's K loop is at least 2048 long, else 8 (512
-    threads); the 128-wide tile runs 4; a forced size must be one the form
-    has, and only that tile takes one."""
+    threads); the 192- and 128-wide tiles run 4; a forced size must be one
+    the form has, and only that tile takes one."""
     big = dict(A=1 << 40, B=2 << 40, C=3 << 40)
     for (M, N, K, kw, threads) in [
             (8192, 8192, 8192, dict(), 256),
@@ -343,6 +353,16 @@ def test_pipelined_wave_count():
     st, p = plan(512, 256, 1024, config=dict(d128, split_k=4))
     assert st == 0 and p["split_k"] == 4 and p["k_iters"] == 8 and p["block_m"] == 128
     assert plan(512, 256, 96, config=dict(d128, threads=512))[0] == dtm.DTM_ERR_CONFIG
+    # 192-wide tiles: 4 waves, both forms, split-K too
+    d192 = dict(dma, block_m=192, block_n=192)
+    for M, N, K, ragged in [(384, 576, 96, 0), (500, 256, 96, 1), (3072, 3072, 4096, 0)]:
+        st, p = plan(M, N, K, sam=K + (-K % 8), config=d192)
+        assert st == 0 and (p["block_m"], p["threads"], p["ragged"]) == (192, 256, ragged), p
+        assert (p["grid_m"], p["grid_n"]) == (-(-M // 192), -(-N // 192))
+    st, p = plan(384, 384, 1024, config=dict(d192, split_k=4))
+    assert st == 0 and p["split_k"] == 4 and p["k_iters"] == 8 and p["block_m"] == 192
+    assert plan(384, 384, 96, config=dict(d192, threads=512))[0] == dtm.DTM_ERR_CONFIG
+    assert plan(384, 384, 96, config=dict(dma, block_m=192))[0] == dtm.DTM_ERR_CONFIG
     assert plan(512, 256, 96, config=dict(dma, block_m=128))[0] == dtm.DTM_ERR_CONFIG
     assert plan(512, 256, 96, config=dict(dma, block_m=64, block_n=64))[0] == dtm.DTM_ERR_CONFIG
     for t in (128, 320, 1024, 100):
