@@ -40,20 +40,20 @@
 //  * Both MFMA operands want, in lane l, 8 consecutive k (k-group l/16) of
 //    row/column l % 16.  An operand that is K-contiguous in memory is staged
 //    as TILE rows of 64 bytes; the 16-byte chunk c of row r sits at
-//    c ^ f(r), f(r) = (r >> 2) & 3, and a fragment is one ds_read_b128 per
-//    lane (16 consecutive rows of one chunk cover all 64 banks once; a
-//    probe of the 32-row lane order of 32 x 32 MFMAs measured no conflicts,
-//    other XOR patterns 4-12 extra cycles per read; with this kernel's
-//    16-row order the counters still show some).
+//    c ^ f(r), f(r) = (r >> 1) & 3, and a fragment is one ds_read_b128 per
+//    lane.  An in-bounds probe of this read order (lane l: row l % 16, chunk
+//    l / 16) measured SQ_LDS_BANK_CONFLICT at zero with this f and at 1/6 of
+//    the LDS-active cycles with (r >> 2) & 3, r & 3 or no swizzle.
 //  * An operand that is M- or N-contiguous stays that way: 32 k-rows of
 //    2 * TILE bytes, chunk c of k-row k at c ^ g(k), g = {0, 6, 10, 12}[k % 4]
 //    XOR 2 for k % 16 >= 8.  Without the k % 16 term the two 16-lane groups
-//    of a read, on k-rows 8 apart, hit the same banks: SQ_LDS_BANK_CONFLICT
-//    then counted 50% of the kernel's LDS-active cycles, with it 33% (the
-//    rest from the 64-byte-row reads below; the time did not change).  A fragment is two ds_read_b64_tr_b16, which hand lane i of each
-//    16-lane group the i-th column of a 4 x 16 block whose rows the lanes
-//    address, i.e. four consecutive k of one row/column -- the operand
-//    layout the MFMA wants, with no transpose anywhere else.
+//    of a read, on k-rows 8 apart, hit the same banks.  With both swizzles
+//    the kernel's SQ_LDS_BANK_CONFLICT is zero (it was 50% of the
+//    LDS-active cycles before either).  A fragment is two
+//    ds_read_b64_tr_b16, which hand lane i of each 16-lane group the i-th
+//    column of a 4 x 16 block whose rows the lanes address, i.e. four
+//    consecutive k of one row/column -- the operand layout the MFMA wants,
+//    with no transpose anywhere else.
 //  * B fragments are double-buffered.  A fragments are too in the 4-wave
 //    form (its reads then spread evenly between the MFMAs); the 8-wave form,
 //    short of registers, keeps one A buffer and reads row i's fragment of
@@ -92,7 +92,7 @@ constexpr int waitcnt_imm(int vm, int lgkm)
 }
 
 // Swizzles of the two staging forms (see the file comment).
-__device__ __forceinline__ int swz_row(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz_row(int r) { return (r >> 1) & 3; }
 __device__ __forceinline__ int swz_krow(int k)
 {
     // 0, 6, 10, 12 for k % 4 = 0..3, XOR 2 when k % 16 >= 8: a fragment read
