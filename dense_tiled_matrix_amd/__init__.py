@@ -28,7 +28,7 @@ DTM_F32, DTM_F16, DTM_BF16 = 0, 1, 2
 STATUS = {
     0: "DTM_OK", 1: "DTM_ERR_INVALID_DIM", 2: "DTM_ERR_NULL_POINTER", 3: "DTM_ERR_DTYPE",
     4: "DTM_ERR_STRIDE", 5: "DTM_ERR_ALIAS", 6: "DTM_ERR_CONFIG", 7: "DTM_ERR_WORKSPACE",
-    8: "DTM_ERR_DEVICE", 9: "DTM_ERR_LAUNCH",
+    8: "DTM_ERR_DEVICE", 9: "DTM_ERR_LAUNCH", 10: "DTM_ERR_POINTER",
 }
 globals().update({v: k for k, v in STATUS.items()})
 # dtm_kernel
@@ -113,6 +113,8 @@ def lib():
         L.gemm_status_string.restype = ctypes.c_char_p
         L.gemm_kernel_name.argtypes = [i32]
         L.gemm_kernel_name.restype = ctypes.c_char_p
+        L.gemm_set_pointer_checks.argtypes = [i32]
+        L.gemm_set_pointer_checks.restype = i32
         sops = [i64, i64, vp, i64, i64, vp, i64, i64, i32, i32]
         L.row_softmax.argtypes = sops + [vp]
         L.row_softmax.restype = i32
@@ -130,6 +132,12 @@ def header_functions():
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
     return sorted(names)
+
+
+def set_pointer_checks(on: bool) -> bool:
+    """Turn the library's debug pointer checks on or off (gemm_set_pointer_checks);
+    returns the previous setting."""
+    return bool(lib().gemm_set_pointer_checks(1 if on else 0))
 
 
 def gemm_status_string(status: int) -> str:

@@ -9,6 +9,7 @@
 // launched ("Triton matmul" notes: a failure before the GPU is reached is the
 // one to want).
 #include <atomic>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -24,7 +25,38 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
+bool env_pointer_checks()
+{
+    const char *v = std::getenv("DTM_CHECK_POINTERS");
+    return v && *v && std::strcmp(v, "0") != 0;
+}
+std::atomic<bool> g_pointer_checks{env_pointer_checks()};
+
 }  // namespace
+
+bool pointer_checks_on() { return g_pointer_checks.load(std::memory_order_relaxed); }
+
+int check_view_memory(uintptr_t lo, uintptr_t hi)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return DTM_ERR_POINTER;
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, reinterpret_cast<const void *>(lo)) != hipSuccess) {
+        (void)hipGetLastError();  // clear the sticky error the query may leave
+        return DTM_ERR_POINTER;
+    }
+    if (attr.type != hipMemoryTypeDevice || attr.device != dev)
+        return DTM_ERR_POINTER;
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, reinterpret_cast<hipDeviceptr_t>(lo)) != hipSuccess) {
+        (void)hipGetLastError();
+        return DTM_ERR_POINTER;
+    }
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base);
+    return lo >= b && hi >= lo && hi - b <= size ? DTM_OK : DTM_ERR_POINTER;
+}
 
 int check_device()
 {
@@ -426,6 +458,29 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
 
 // ---- device check ---------------------------------------------------------
 
+// With pointer checks on: every view the plan touches (A and B when K > 0,
+// C, a caller's workspace) inside one device allocation of this device.
+int check_pointers(const Call &c, const dtm_plan &p, const void *workspace)
+{
+    auto view = [](const void *base, int64_t rows, int64_t cols, int64_t sr, int64_t sc,
+                   int64_t item) {
+        uintptr_t lo, hi;
+        if (!view_range(base, rows, cols, sr, sc, item, lo, hi))
+            return static_cast<int>(DTM_ERR_POINTER);
+        return dtm::check_view_memory(lo, hi);
+    };
+    int st = view(c.C, c.M, c.N, c.scm, c.scn, item_size(c.out));
+    if (st == DTM_OK && c.K > 0)
+        st = view(c.A, c.M, c.K, c.sam, c.sak, item_size(c.in));
+    if (st == DTM_OK && c.K > 0)
+        st = view(c.B, c.K, c.N, c.sbk, c.sbn, item_size(c.in));
+    if (st == DTM_OK && workspace && p.workspace_bytes > 0) {
+        const uintptr_t w = reinterpret_cast<uintptr_t>(workspace);
+        st = dtm::check_view_memory(w, w + p.workspace_bytes);
+    }
+    return st;
+}
+
 int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t workspace_bytes,
         void *stream)
 {
@@ -438,6 +493,11 @@ int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t w
     st = check_device();
     if (st != DTM_OK)
         return st;
+    if (dtm::pointer_checks_on()) {
+        st = check_pointers(c, p, workspace);
+        if (st != DTM_OK)
+            return st;
+    }
     GemmArgs a{c.M, c.N, c.K, c.A, c.sam, c.sak, c.B, c.sbk, c.sbn, const_cast<void *>(c.C),
                c.scm, c.scn};
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -532,6 +592,8 @@ const char *gemm_status_string(int status)
     case DTM_ERR_WORKSPACE: return "workspace too small or its allocation failed";
     case DTM_ERR_DEVICE: return "current HIP device is not gfx950 or could not be queried";
     case DTM_ERR_LAUNCH: return "kernel launch failed";
+    case DTM_ERR_POINTER:
+        return "pointer check: a view is not inside one device allocation of the current device";
     }
     return "unknown status";
 }
@@ -547,6 +609,11 @@ const char *gemm_kernel_name(int kernel)
     case DTM_KERNEL_GENERIC_FP16ACC: return "generic_fp16acc";
     }
     return "unknown";
+}
+
+int gemm_set_pointer_checks(int on)
+{
+    return dtm::g_pointer_checks.exchange(on != 0) ? 1 : 0;
 }
 
 }  // extern "C"

@@ -58,6 +58,14 @@ inline bool c_strides_ok(int64_t M, int64_t N, int64_t scm, int64_t scn)
     return s_big >= span;
 }
 
+// Whether the optional pointer checks are on (gemm_set_pointer_checks).
+bool pointer_checks_on();
+
+// DTM_OK when the byte range [lo, hi) lies inside one device-memory
+// allocation of the current device (as the HIP runtime reports it), else
+// DTM_ERR_POINTER.  Only called with pointer checks on.
+int check_view_memory(uintptr_t lo, uintptr_t hi);
+
 // DTM_OK when the current HIP device is a gfx950, else DTM_ERR_DEVICE
 // (cached per device).
 int check_device();

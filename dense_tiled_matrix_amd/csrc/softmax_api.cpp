@@ -188,6 +188,19 @@ int row_softmax(int64_t M, int64_t N, const void *X, int64_t stride_xm, int64_t 
     st = dtm::check_device();
     if (st != DTM_OK)
         return st;
+    if (dtm::pointer_checks_on()) {
+        // X and Y inside device allocations of this device (validate has
+        // already shown both ranges are representable)
+        uintptr_t lo, hi;
+        dtm::view_range(X, M, N, stride_xm, stride_xn, dtm::item_size(in_dtype), lo, hi);
+        st = dtm::check_view_memory(lo, hi);
+        if (st != DTM_OK)
+            return st;
+        dtm::view_range(Y, M, N, stride_ym, stride_yn, dtm::item_size(out_dtype), lo, hi);
+        st = dtm::check_view_memory(lo, hi);
+        if (st != DTM_OK)
+            return st;
+    }
     const dtm::SoftmaxArgs a{M, N, X, stride_xm, stride_xn, Y, stride_ym, stride_yn};
     float *ws = nullptr;
     if (p.form == DTM_SOFTMAX_SPLIT) {

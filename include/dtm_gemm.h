@@ -71,7 +71,10 @@ typedef enum {
     DTM_ERR_WORKSPACE = 7,    /* workspace smaller than the plan needs, or its allocation
                                  failed */
     DTM_ERR_DEVICE = 8,       /* the current device is not gfx950 or cannot be queried */
-    DTM_ERR_LAUNCH = 9        /* the HIP runtime reported an error when launching */
+    DTM_ERR_LAUNCH = 9,       /* the HIP runtime reported an error when launching */
+    DTM_ERR_POINTER = 10      /* pointer checks on (gemm_set_pointer_checks): a view's
+                                 byte range is not inside one device-memory allocation of
+                                 the current device */
 } dtm_status;
 
 /* Kernels a plan can name. */
@@ -184,6 +187,20 @@ const char *gemm_status_string(int status);
 
 /* gemm_kernel_name -- a static name for a dtm_kernel value. */
 const char *gemm_kernel_name(int kernel);
+
+/* gemm_set_pointer_checks -- debug checks of the caller's pointers, off by
+ * default (the library cannot otherwise tell a wrong pointer or stride from
+ * a right one: a view that runs past its memory gives wrong results or a
+ * memory fault, not an error).  When on (on != 0), gemm, gemm_ex and
+ * row_softmax first ask the HIP runtime, for every operand view they would
+ * touch, for the allocation holding its lowest byte, and return
+ * DTM_ERR_POINTER -- launching nothing -- unless the view's whole byte range
+ * lies in that one allocation and the allocation is device memory of the
+ * current device.  It costs a few runtime queries per call.  The initial
+ * setting is on when the environment variable DTM_CHECK_POINTERS is set to
+ * a value other than "0" when the library loads.  Process-wide and
+ * thread-safe; returns the previous setting (0 or 1). */
+int gemm_set_pointer_checks(int on);
 
 #ifdef __cplusplus
 }

@@ -62,6 +62,9 @@ typedef struct {
  * The SPLIT form uses 8*M*parts bytes of a per-(device, stream) buffer the
  * library owns (the one GEMM split-K uses), grown on demand; a failed
  * allocation returns DTM_ERR_WORKSPACE.
+ * With pointer checks on (gemm_set_pointer_checks), X's and Y's byte ranges
+ *   must each lie in one device allocation of the current device, else
+ *   DTM_ERR_POINTER.
  * Every check runs before any launch; on error nothing is launched.
  * Returns a dtm_status.
  */

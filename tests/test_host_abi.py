@@ -4,6 +4,7 @@ Blocked Matmul Kernel", Worked Example 13.1.1: an 8x8x8 product with 4x4x4
 tiles runs a (2, 2) grid with 2 K-iterations per tile) and rejects bad
 arguments before anything is launched."""
 import ctypes
+import os
 
 import pytest
 
@@ -387,3 +388,28 @@ def test_gemm_rejects_before_touching_a_device():
         dtm.DTM_ERR_INVALID_DIM
     assert dtm.gemm_raw(4, 4, 4, PA, 4, 1, PB, 4, 1, PA, 4, 1, F32, F32) == dtm.DTM_ERR_ALIAS
     assert dtm.gemm_raw(0, 4, 4, 0, 4, 1, 0, 4, 1, 0, 4, 1, F32, F32) == dtm.DTM_OK
+
+
+def test_pointer_check_switch():
+    """gemm_set_pointer_checks returns the previous setting; the checks are
+    off unless DTM_CHECK_POINTERS (other than "0") is set when the library
+    loads; argument errors still come first with them on."""
+    import subprocess
+    import sys
+    prev = dtm.set_pointer_checks(True)
+    try:
+        assert dtm.set_pointer_checks(True) is True
+        assert dtm.gemm_raw(-1, 4, 4, PA, 4, 1, PB, 4, 1, PC, 4, 1, F32, F32) == \
+            dtm.DTM_ERR_INVALID_DIM
+        assert dtm.set_pointer_checks(False) is True
+        assert dtm.set_pointer_checks(False) is False
+    finally:
+        dtm.set_pointer_checks(prev)
+    probe = "import dense_tiled_matrix_amd as d; print(int(d.set_pointer_checks(False)))"
+    for env, want in [(None, "0"), ("1", "1"), ("0", "0"), ("yes", "1")]:
+        e = {k: v for k, v in os.environ.items() if k != "DTM_CHECK_POINTERS"}
+        if env is not None:
+            e["DTM_CHECK_POINTERS"] = env
+        out = subprocess.run([sys.executable, "-c", probe], env=e, capture_output=True,
+                             text=True, check=True).stdout.strip()
+        assert out == want, (env, out)
