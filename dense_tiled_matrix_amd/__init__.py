@@ -45,7 +45,8 @@ class TileConfig(ctypes.Structure):
 
     _fields_ = [("kernel", ctypes.c_int32), ("block_m", ctypes.c_int32),
                 ("block_n", ctypes.c_int32), ("block_k", ctypes.c_int32),
-                ("split_k", ctypes.c_int32), ("threads", ctypes.c_int32)]
+                ("split_k", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("dp_rows", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -57,7 +58,7 @@ class Plan(ctypes.Structure):
                 ("k_iters", ctypes.c_int64), ("split_k", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("fast_path", ctypes.c_int32),
                 ("ragged", ctypes.c_int32), ("layout", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_uint64)]
+                ("workspace_bytes", ctypes.c_uint64), ("dp_rows", ctypes.c_int64)]
 
     def as_dict(self):
         d = {f: getattr(self, f) for f, _ in self._fields_}

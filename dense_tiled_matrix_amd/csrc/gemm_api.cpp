@@ -9,6 +9,7 @@
 // launched ("Triton matmul" notes: a failure before the GPU is reached is the
 // one to want).
 #include <atomic>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <map>
@@ -297,6 +298,76 @@ bool prefer_192(const Call &c, int layout)
            round_fill(cdiv(c.M, 256) * cdiv(c.N, 256));
 }
 
+// The rows of C at and below `row0` as a problem of their own (A's rows
+// likewise; B whole).
+Call lower_rows(const Call &c, int64_t row0)
+{
+    Call d = c;
+    d.M = c.M - row0;
+    d.A = static_cast<const char *>(c.A) + row0 * c.sam * item_size(c.in);
+    d.C = static_cast<const char *>(c.C) + row0 * c.scm * item_size(c.out);
+    return d;
+}
+Call upper_rows(const Call &c, int64_t rows)
+{
+    Call d = c;
+    d.M = rows;
+    return d;
+}
+
+// Split only the last, part-filled round of 256-wide tiles.  When the tiles
+// do not fill whole rounds of the 256 CUs, the top tile-rows that do run
+// unsplit and the remaining tile-rows, fewer than one round of tiles, run
+// with K in S slices so that tiles x S nearly fills one more round; their
+// fp32 partials are summed by the split-K pass.  Modelled in units of one
+// chunk of K on one tile: unsplit rows ceil(tiles / 256) x chunks, the tail
+// ceil(chunks / S), plus TAIL_PARTIAL_COST per partial tile written and read
+// back (fitted to measurements: 0.22-0.33).  Taken when that beats the
+// plain plan (256 or 192 wide) by 3%.  Measured, bf16 TFLOP/s (plain ->
+// split tail): 4096 x 5120 x 4096 959 -> 1079-1095, 5120 x 4096 x 4096
+// 954 -> 1110, 6000^3 1028 -> 1161, 7000^3 1049 -> 1212, 4096 x 5120 x 8192
+// 1023 -> 1243; 6144^3 on 192-wide tiles 1232 against 1264.
+constexpr double TAIL_PARTIAL_COST = 0.3;
+constexpr int64_t TAIL_MAX_SPLIT = 16, TAIL_MIN_SLICE = 256;
+
+bool pick_tail_split(const Call &c, int layout, int plain_tile, int64_t &dp_rows, int64_t &split)
+{
+    const int64_t gm = cdiv(c.M, 256), gn = cdiv(c.N, 256), tiles = gm * gn;
+    if (tiles <= CUS || tiles % CUS == 0)
+        return false;
+    const int64_t rows_dp = (tiles / CUS) * CUS / gn;  // tile-rows in whole rounds
+    if (rows_dp <= 0 || rows_dp >= gm)
+        return false;
+    const int64_t tail = (gm - rows_dp) * gn;
+    const double nk = static_cast<double>(cdiv(c.K, 32));
+    double plain = static_cast<double>(cdiv(tiles, CUS)) * nk;
+    if (plain_tile == 192) {
+        const double r = dma_interior(c, layout, 1, 192) ? RATE_192 : RATE_192_RAGGED;
+        plain = static_cast<double>(cdiv(cdiv(c.M, 192) * cdiv(c.N, 192), CUS)) * nk *
+                (192.0 * 192.0) / (256.0 * 256.0) / r;
+    }
+    const Call top = upper_rows(c, rows_dp * 256), low = lower_rows(c, rows_dp * 256);
+    if (!dma_any(top, layout, 1, 256))
+        return false;
+    const double dp = static_cast<double>(cdiv(rows_dp * gn, CUS)) * nk;
+    double best = 0.97 * plain;
+    bool found = false;
+    for (int64_t S = 2; S <= TAIL_MAX_SPLIT && tail * S <= CUS; ++S) {
+        if (c.K / S < TAIL_MIN_SLICE || !dma_any(low, layout, S, 256))
+            continue;
+        const double t = dp + std::ceil(nk / static_cast<double>(S)) +
+                         TAIL_PARTIAL_COST * static_cast<double>(S * tail);
+        if (t < best) {
+            best = t;
+            split = S;
+            found = true;
+        }
+    }
+    if (found)
+        dp_rows = rows_dp * 256;
+    return found;
+}
+
 // Split-K for problems whose 128 x 128 tiles still cannot fill the chip and
 // whose K is long: the largest power-of-two split that keeps tiles x split
 // within 256 workgroups and slices of at least 2048 (64 pipelined chunks).
@@ -386,6 +457,12 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
                 p.split_k = tile == 128 ? static_cast<int32_t>(pick_split(
                                               c, layout, cdiv(c.M, 128) * cdiv(c.N, 128), 128))
                                         : 1;
+                int64_t dp_rows = 0, tail_split = 1;
+                if (tile != 128 && pick_tail_split(c, layout, tile, dp_rows, tail_split)) {
+                    p.block_m = p.block_n = 256;
+                    p.split_k = static_cast<int32_t>(tail_split);
+                    p.dp_rows = dp_rows;
+                }
             } else {
                 p.block_m = p.block_n = tiles256 >= 256 ? 256 : 128;
                 p.block_k = 64;
@@ -397,6 +474,16 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
                 !dma_any(c, layout, forced_split, p.block_m))
                 return DTM_ERR_CONFIG;
             p.split_k = static_cast<int32_t>(forced_split);
+            p.dp_rows = 0;
+        }
+        if (force && force->dp_rows) {
+            // unsplit top rows: whole tiles, below M, each part runnable
+            const int64_t r = force->dp_rows;
+            if (!forced_split || r < 0 || r % p.block_m || r >= c.M ||
+                !dma_any(upper_rows(c, r), layout, 1, p.block_m) ||
+                !dma_any(lower_rows(c, r), layout, forced_split, p.block_m))
+                return DTM_ERR_CONFIG;
+            p.dp_rows = r;
         }
         p.threads = 256;  // the pipelined kernel's is settled below
         p.layout = layout;
@@ -425,30 +512,40 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
     } else {
         return DTM_ERR_CONFIG;
     }
-    if (forced_split && kernel != DTM_KERNEL_MFMA_F16)
+    if ((forced_split || (force && force->dp_rows)) && kernel != DTM_KERNEL_MFMA_F16)
         return DTM_ERR_CONFIG;
     p.kernel = kernel;
     fill_grid(c, p);
     const bool dma_tile = kernel == DTM_KERNEL_MFMA_F16 && p.block_k == 32;
     if (dma_tile) {
-        // which form of the pipelined kernel, and how many waves
-        p.ragged = dma_interior(c, layout, p.split_k, p.block_m) ? 0 : 1;
+        // which form of the pipelined kernel, and how many waves (with
+        // unsplit top rows: ragged when either part is; the top part's waves)
+        bool top_ragged = !dma_interior(c, layout, p.split_k, p.block_m);
+        bool low_ragged = top_ragged;
+        if (p.dp_rows > 0) {
+            top_ragged = !dma_interior(upper_rows(c, p.dp_rows), layout, 1, p.block_m);
+            low_ragged = !dma_interior(lower_rows(c, p.dp_rows), layout, p.split_k, p.block_m);
+        }
+        p.ragged = top_ragged || low_ragged ? 1 : 0;
         const int forced_threads = force ? force->threads : 0;
         if (forced_threads) {
             if (forced_threads % 64 ||
-                !dtm::mfma16_dma_waves_ok(p.block_m, forced_threads / 64, p.ragged))
+                !dtm::mfma16_dma_waves_ok(p.block_m, forced_threads / 64, top_ragged) ||
+                !dtm::mfma16_dma_waves_ok(p.block_m, forced_threads / 64, low_ragged))
                 return DTM_ERR_CONFIG;
             p.threads = forced_threads;
         } else if (p.block_m != 256) {
             p.threads = 256;  // 192 and 128: 4 waves
         } else {
-            p.threads = !p.ragged && p.k_iters * p.block_k >= FOUR_WAVE_MIN_K ? 256 : 512;
+            const int64_t kloop = (p.dp_rows > 0 ? cdiv(c.K, p.block_k) : p.k_iters) * p.block_k;
+            p.threads = !top_ragged && kloop >= FOUR_WAVE_MIN_K ? 256 : 512;
         }
     } else if (force && force->threads) {
         return DTM_ERR_CONFIG;  // a workgroup size is chosen for the pipelined kernel only
     }
     if (p.split_k > 1)
-        p.workspace_bytes = static_cast<uint64_t>(p.split_k) * static_cast<uint64_t>(c.M) *
+        p.workspace_bytes = static_cast<uint64_t>(p.split_k) *
+                            static_cast<uint64_t>(c.M - p.dp_rows) *
                             static_cast<uint64_t>(c.N) * sizeof(float);
     if (p.grid_m * p.grid_n > 0x7fffffffLL)
         return DTM_ERR_CONFIG;
@@ -481,26 +578,11 @@ int check_pointers(const Call &c, const dtm_plan &p, const void *workspace)
     return st;
 }
 
-int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t workspace_bytes,
-        void *stream)
+// Launch a validated plan; `ws` is the split-K workspace when split_k > 1.
+int launch_plan(const Call &c, const dtm_plan &p, void *ws, hipStream_t s)
 {
-    dtm_plan p;
-    int st = make_plan(c, force, &p);
-    if (st != DTM_OK)
-        return st;
-    if (p.kernel == DTM_KERNEL_NONE)
-        return DTM_OK;
-    st = check_device();
-    if (st != DTM_OK)
-        return st;
-    if (dtm::pointer_checks_on()) {
-        st = check_pointers(c, p, workspace);
-        if (st != DTM_OK)
-            return st;
-    }
     GemmArgs a{c.M, c.N, c.K, c.A, c.sam, c.sak, c.B, c.sbk, c.sbn, const_cast<void *>(c.C),
                c.scm, c.scn};
-    hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     switch (p.kernel) {
     case DTM_KERNEL_ZERO_FILL: e = dtm::launch_zero_fill(a, c.out, s); break;
@@ -512,15 +594,6 @@ int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t w
         break;
     case DTM_KERNEL_MFMA_F16:
         if (p.split_k > 1) {
-            void *ws = workspace;
-            if (ws) {
-                if (workspace_bytes < p.workspace_bytes || (reinterpret_cast<uintptr_t>(ws) & 15))
-                    return DTM_ERR_WORKSPACE;
-            } else {
-                ws = library_workspace(stream, p.workspace_bytes);
-                if (!ws)
-                    return DTM_ERR_WORKSPACE;
-            }
             e = dtm::launch_mfma16_dma_partials(a, c.in, p.layout, p.split_k, p.ragged != 0,
                                                  a_view_bytes(c), b_view_bytes(c), p.block_m,
                                                  p.threads / 64, static_cast<float *>(ws), s);
@@ -542,6 +615,54 @@ int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t w
     default: return DTM_ERR_CONFIG;
     }
     return e == hipSuccess ? DTM_OK : DTM_ERR_LAUNCH;
+}
+
+int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t workspace_bytes,
+        void *stream)
+{
+    dtm_plan p;
+    int st = make_plan(c, force, &p);
+    if (st != DTM_OK)
+        return st;
+    if (p.kernel == DTM_KERNEL_NONE)
+        return DTM_OK;
+    st = check_device();
+    if (st != DTM_OK)
+        return st;
+    if (dtm::pointer_checks_on()) {
+        st = check_pointers(c, p, workspace);
+        if (st != DTM_OK)
+            return st;
+    }
+    void *ws = nullptr;
+    if (p.split_k > 1) {
+        ws = workspace;
+        if (ws) {
+            if (workspace_bytes < p.workspace_bytes || (reinterpret_cast<uintptr_t>(ws) & 15))
+                return DTM_ERR_WORKSPACE;
+        } else {
+            ws = library_workspace(stream, p.workspace_bytes);
+            if (!ws)
+                return DTM_ERR_WORKSPACE;
+        }
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p.dp_rows == 0)
+        return launch_plan(c, p, ws, s);
+    // Unsplit top rows, then the split rows below them, in stream order.
+    const Call top = upper_rows(c, p.dp_rows), low = lower_rows(c, p.dp_rows);
+    const int32_t threads = force ? force->threads : 0;
+    const dtm_tile_config f_top{DTM_KERNEL_MFMA_F16, p.block_m, p.block_n, p.block_k, 1, threads, 0};
+    const dtm_tile_config f_low{DTM_KERNEL_MFMA_F16, p.block_m, p.block_n, p.block_k, p.split_k,
+                                threads, 0};
+    dtm_plan p_top, p_low;
+    st = make_plan(top, &f_top, &p_top);
+    if (st == DTM_OK)
+        st = make_plan(low, &f_low, &p_low);
+    if (st != DTM_OK)
+        return st;
+    st = launch_plan(top, p_top, nullptr, s);
+    return st == DTM_OK ? launch_plan(low, p_low, ws, s) : st;
 }
 
 }  // namespace

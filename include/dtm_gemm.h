@@ -114,6 +114,9 @@ typedef struct {
     int32_t threads; /* workgroup size of the 256 x 256 x 32 pipelined MFMA tile: 512
                         (8 waves) or 256 (4 waves, not on its range-checked form); must
                         be 0 for any other tile */
+    int32_t dp_rows; /* with split_k > 1 on the pipelined kernel: the first dp_rows rows
+                        of C (a multiple of block_m, below M) run unsplit and only the
+                        rows below them in split_k slices; 0 = every row split */
 } dtm_tile_config;
 
 /* What gemm() would launch for a problem.  Produced on the host only. */
@@ -129,6 +132,9 @@ typedef struct {
     int32_t ragged;           /* 1 when M, N or K is not a multiple of its block */
     int32_t layout;           /* dtm_layout bits of the operands (MFMA kernels; 0 otherwise) */
     uint64_t workspace_bytes; /* device scratch the plan needs (split-K partials) */
+    int64_t dp_rows;          /* with split_k > 1: rows [0, dp_rows) run unsplit in full
+                                 rounds of tiles, rows [dp_rows, M) in split_k slices
+                                 (k_iters counts a slice); 0 = every row split */
 } dtm_plan;
 
 /*

@@ -454,6 +454,44 @@ def test_192_selector_random(layout):
         assert untouched
 
 
+@pytest.mark.parametrize("layout", ["NN", "TT", "NT"])
+def test_unsplit_rows_exact(layout):
+    """Plans whose top rows run unsplit and whose lower rows run with K split
+    (forced): interior and range-checked lower parts, tiles of 256, 192 and
+    128, every output dtype.  Value-exact on integer-valued inputs; C
+    outside the view untouched."""
+    cases = [(768, 512, 2048, 4, 512, 256), (1000, 520, 1000, 3, 512, 256),
+             (960, 576, 2048, 4, 576, 192), (640, 384, 4096, 2, 384, 128),
+             (520, 264, 2056, 8, 256, 256)]
+    for n, (M, N, K, S, dp, tile) in enumerate(cases):
+        if layout[0] == "T":
+            M = _round8(M)
+        if layout[1] == "N":
+            N = _round8(N)
+        outd = ["f32", "bf16", "f16", "f32", "bf16"][n]
+        p = padded_int_problem(M, N, K, "bf16" if n % 2 else "f16", outd, 2, seed=880 + n,
+                               a_layout=layout[0], b_layout=layout[1])
+        cfg = dict(kernel=MF16, block_m=tile, block_n=tile, block_k=32, split_k=S, dp_rows=dp)
+        plan = {}
+        c, untouched = run(p, config=cfg, c_pad=3 if n % 2 else 0, plan=plan)
+        assert plan["status"] == 0 and (plan["split_k"], plan["dp_rows"]) == (S, dp), plan
+        compare(p, c, exact=True, label=f"unsplit rows {layout} {M}x{N}x{K} S{S} dp{dp}->{outd}")
+        assert untouched
+
+
+def test_unsplit_rows_selector_random():
+    """4096 x 5120 x 4096 has 320 tiles of 256 for 256 CUs: the selector runs
+    the top 12 tile-rows unsplit and the 4 below with K in 2 slices; N(0,1)
+    bf16 compared in full within the stated tolerance."""
+    p = W.random_problem(4096, 5120, 4096, "bf16", "bf16", ("normal", 0.0, 1.0), seed=890)
+    plan = {}
+    c, untouched = run(p, plan=plan)
+    assert (plan["block_m"], plan["split_k"], plan["dp_rows"]) == (256, 2, 3072), plan
+    err, tol = compare(p, c, label="unsplit rows 4096x5120x4096")
+    note(f"unsplit rows 4096x5120x4096: max err {err:.3e} tol {tol:.3e}")
+    assert untouched
+
+
 def _round8(x):
     return -(-x // 8) * 8
 

@@ -91,8 +91,8 @@ def test_selector_measured_workloads():
                              (4096, 4096, 1024, 256, 1), (2000, 2000, 2000, 128, 1),
                              (6144, 6144, 6144, 192, 1), (6144, 6144, 2048, 192, 1),
                              (3072, 3072, 1024, 192, 1), (3000, 3000, 3000, 192, 1),
-                             (4608, 4608, 4608, 256, 1), (3840, 3840, 3840, 256, 1),
-                             (5120, 5120, 5120, 256, 1), (7168, 7168, 7168, 256, 1),
+                             (3840, 3840, 3840, 256, 1),
+                             (5120, 5120, 5120, 256, 1),
                              (8192, 8192, 8192, 256, 1), (12288, 12288, 1024, 256, 1),
                              (4096, 3072, 2048, 256, 1)]:
         st, p = plan(M, N, K, A=1 << 40, B=2 << 40, C=3 << 40, ind=BF16, outd=BF16)
@@ -101,6 +101,25 @@ def test_selector_measured_workloads():
         if tile != 256:
             assert p["threads"] == 256, (M, N, K, p)
         assert p["ragged"] == (1 if (M % tile or N % tile) else 0), (M, N, K, p)
+        assert p["dp_rows"] == 0, (M, N, K, p)
+    # 256-wide tiles that leave the last round part-empty: the top tile-rows
+    # in whole rounds unsplit, the rest with K split so that tiles x S nearly
+    # fills one round (partials: S x rows below x N x 4 bytes)
+    for M, N, K, S, dp_rows, ragged in [(4096, 5120, 4096, 2, 3072, 0),
+                                        (5120, 4096, 4096, 3, 4096, 1),
+                                        (4608, 4608, 4608, 3, 3584, 0),
+                                        (6000, 6000, 6000, 3, 5376, 1),
+                                        (7000, 7000, 7000, 5, 6912, 1),
+                                        (4096, 5120, 8192, 3, 3072, 1),
+                                        (7168, 7168, 7168, 5, 6912, 1)]:
+        st, p = plan(M, N, K, A=1 << 40, B=2 << 40, C=3 << 40, ind=BF16, outd=BF16)
+        assert st == 0 and (p["block_m"], p["block_k"], p["split_k"], p["dp_rows"]) == \
+            (256, 32, S, dp_rows), (M, N, K, p)
+        assert p["ragged"] == ragged and p["k_iters"] == -(-(-(-K // S)) // 32), (M, N, K, p)
+        assert p["workspace_bytes"] == S * (M - dp_rows) * N * 4, (M, N, K, p)
+        gm, gn = -(-M // 256), -(-N // 256)
+        assert (dp_rows // 256) * gn <= 256 * (gm * gn // 256) < (dp_rows // 256 + 1) * gn
+        assert (gm - dp_rows // 256) * gn * S <= 256
     # enough tiles: no split
     st, p = plan(4096, 4096, 65536, A=1 << 40, B=2 << 40, C=3 << 40, ind=F16, outd=F32)
     assert st == 0 and p["split_k"] == 1 and p["workspace_bytes"] == 0
@@ -413,3 +432,25 @@ def test_pointer_check_switch():
         out = subprocess.run([sys.executable, "-c", probe], env=e, capture_output=True,
                              text=True, check=True).stdout.strip()
         assert out == want, (env, out)
+
+
+def test_forced_unsplit_rows():
+    """dp_rows in a forced configuration: the top rows run unsplit and only the
+    rows below them in split_k slices; it must be a multiple of the tile,
+    below M, and come with a split on the pipelined kernel."""
+    dma = dict(kernel=dtm.DTM_KERNEL_MFMA_F16, block_m=256, block_n=256, block_k=32)
+    st, p = plan(1024, 512, 4096, config=dict(dma, split_k=4, dp_rows=512))
+    assert st == 0 and (p["split_k"], p["dp_rows"], p["k_iters"], p["ragged"]) == (4, 512, 32, 0)
+    assert p["workspace_bytes"] == 4 * 512 * 512 * 4
+    st, p = plan(1000, 520, 1000, sam=1000, sbk=520, scm=520,
+                 config=dict(dma, split_k=3, dp_rows=512))
+    assert st == 0 and (p["split_k"], p["dp_rows"], p["ragged"]) == (3, 512, 1), p
+    st, p = plan(960, 576, 2048, config=dict(dma, block_m=192, block_n=192, split_k=4,
+                                                dp_rows=576))
+    assert st == 0 and (p["block_m"], p["dp_rows"], p["threads"]) == (192, 576, 256), p
+    for bad in [dict(split_k=4, dp_rows=300), dict(split_k=4, dp_rows=1024),
+                dict(split_k=4, dp_rows=-256), dict(dp_rows=512), dict(split_k=1, dp_rows=512)]:
+        assert plan(1024, 512, 4096, config=dict(dma, **bad))[0] == dtm.DTM_ERR_CONFIG, bad
+    assert plan(1024, 512, 4096, config=dict(kernel=dtm.DTM_KERNEL_GENERIC, block_m=64,
+                                             block_n=64, block_k=16, dp_rows=512))[0] == \
+        dtm.DTM_ERR_CONFIG
