@@ -15,9 +15,9 @@
 // the view (rows past M or N, k past K) is read as exact zeros -- the
 // hardware returns zeros for an offset past the buffer's size, and such
 // lanes are given one -- so nothing outside the views is ever read; the
-// store is masked.  Transposed views are read at full speed rather than through a
-// slow strided path (the stride-swap lesson of "Triton from zero",
-// Lesson 4: a transpose is only a change of strides).
+// store is masked.  Transposed views are read at full speed rather than
+// through a slow strided path (the stride-swap lesson of "Triton from
+// zero", Lesson 4: a transpose is only a change of strides).
 //
 // gfx950 design:
 //  * One workgroup per TILE x TILE output tile (TILE 256, 192 or 128; the
@@ -46,10 +46,11 @@
 //    the LDS-active cycles with (r >> 2) & 3, r & 3 or no swizzle.
 //  * An operand that is M- or N-contiguous stays that way: 32 k-rows of
 //    2 * TILE bytes, chunk c of k-row k at c ^ g(k), g = {0, 6, 10, 12}[k % 4]
-//    XOR 2 for k % 16 >= 8.  Without the k % 16 term the two 16-lane groups
-//    of a read, on k-rows 8 apart, hit the same banks.  With both swizzles
-//    the kernel's SQ_LDS_BANK_CONFLICT is zero (it was 50% of the
-//    LDS-active cycles before either).  A fragment is two
+//    XOR 2 for k % 16 >= 8 (a rotation instead at TILE 192, whose 24-chunk
+//    k-rows an XOR would leave; see krow_phys).  Without the k % 16 term the
+//    two 16-lane groups of a read, on k-rows 8 apart, hit the same banks.
+//    With both swizzles the kernel's SQ_LDS_BANK_CONFLICT is zero (it was
+//    50% of the LDS-active cycles before either).  A fragment is two
 //    ds_read_b64_tr_b16, which hand lane i of each 16-lane group the i-th
 //    column of a 4 x 16 block whose rows the lanes address, i.e. four
 //    consecutive k of one row/column -- the operand layout the MFMA wants,
