@@ -657,6 +657,23 @@ def test_split_k_caller_workspace():
     torch.cuda.synchronize()
     assert st == dtm.DTM_ERR_WORKSPACE
     assert bool((c2 == 7.0).all())
+    # unsplit top rows: the workspace covers only the rows below them
+    M2, dp = 768, 512
+    p = padded_int_problem(M2, N, K, "f16", "f32", 4, seed=78)
+    cfg = dict(kernel=MF16, block_m=256, block_n=256, block_k=32, split_k=S, dp_rows=dp)
+    plan = {}
+    ref, _ = run(p, config=cfg, plan=plan)
+    assert plan["workspace_bytes"] == S * (M2 - dp) * N * 4, plan
+    sa, sb = dev_storage(p.A.bits, "f16"), dev_storage(p.B.bits, "f16")
+    c = torch.empty(M2, N, dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(S * (M2 - dp) * N, dtype=torch.float32, device="cuda:0")
+    for nbytes, want in [(ws.numel() * 4 - 16, dtm.DTM_ERR_WORKSPACE), (ws.numel() * 4, 0)]:
+        st = dtm.gemm_ex_raw(M2, N, K, sa.data_ptr(), p.A.stride_r, 1, sb.data_ptr(),
+                             p.B.stride_r, 1, c.data_ptr(), N, 1, dtm.DTM_F16, dtm.DTM_F32,
+                             config=cfg, workspace=ws.data_ptr(), workspace_bytes=nbytes)
+        torch.cuda.synchronize()
+        assert st == want, (nbytes, st)
+    assert np.array_equal(c.cpu().numpy().view(np.uint32), ref)
 
 
 def _padded_f32_problem(M, N, K, outd, seed, a_layout, b_layout):
