@@ -111,9 +111,10 @@ typedef struct {
     int32_t block_n;
     int32_t block_k;
     int32_t split_k; /* number of K slices summed by a second pass; 0 or 1 = none */
-    int32_t threads; /* workgroup size of the 256 x 256 x 32 pipelined MFMA tile: 512
-                        (8 waves) or 256 (4 waves, not on its range-checked form); must
-                        be 0 for any other tile */
+    int32_t threads; /* workgroup size of the pipelined MFMA kernel (block_k 32): at
+                        256 x 256, 512 (8 waves) or 256 (4 waves, not on its range-checked
+                        form); at 192 x 192 and 128 x 128, 256; must be 0 for any other
+                        kernel or tile */
     int32_t dp_rows; /* with split_k > 1 on the pipelined kernel: the first dp_rows rows
                         of C (a multiple of block_m, below M) run unsplit and only the
                         rows below them in split_k slices; 0 = every row split */
@@ -143,9 +144,11 @@ typedef struct {
  *   the storage A and B are views into).  in_dtype: dtype of A and B;
  *   out_dtype: dtype of C.  stream: hipStream_t or NULL.
  * The library picks the kernel and tile with its selector.  When the chosen
- * plan splits K it uses a per-device workspace owned by the library, grown on
- * demand (a device allocation the first time a larger one is needed; the
- * allocation synchronises the device).
+ * plan splits K it uses a workspace owned by the library, one per (device,
+ * stream), grown on demand (a device allocation the first time a larger one
+ * is needed; growing first waits for the stream's earlier work).  A plan
+ * with dtm_plan.dp_rows > 0 runs as launches in stream order on row ranges of
+ * the same views: the unsplit top rows, then the split rows and their sum.
  * Returns a dtm_status.
  */
 int gemm(int64_t M, int64_t N, int64_t K,
@@ -171,7 +174,7 @@ int gemm_plan(int64_t M, int64_t N, int64_t K,
  * gemm_ex -- gemm() with a forced tile configuration and an optional
  * caller-owned workspace.
  * force: NULL or a dtm_tile_config whose non-zero fields override the
- *   selector (for example {DTM_KERNEL_GENERIC, 4, 4, 4, 0, 0} runs 4x4x4 tiles).
+ *   selector (for example {DTM_KERNEL_GENERIC, 4, 4, 4, 0, 0, 0} runs 4x4x4 tiles).
  *   A configuration the library does not have, or an MFMA kernel for a
  *   layout it cannot serve, gives DTM_ERR_CONFIG.
  * workspace, workspace_bytes: device memory of at least plan.workspace_bytes
