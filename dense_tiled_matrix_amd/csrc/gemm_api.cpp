@@ -369,16 +369,30 @@ bool pick_tail_split(const Call &c, int layout, int plain_tile, int64_t &dp_rows
 }
 
 // Split-K for problems whose 128 x 128 tiles still cannot fill the chip and
-// whose K is long: the largest power-of-two split that keeps tiles x split
-// within 256 workgroups and slices of at least 2048 (64 pipelined chunks).
-// Measured (128 tiles): 1024x1024x8192 S=1 303, S=4 630, S=8 562;
-// 512x512x65536 fp16 S=8 528, S=16 736; 1024^3 S=1 183, S=2 133.
+// whose K is long: up to S_max = min(256 / tiles, K / 2048) slices (slices of
+// at least 2048, 64 pipelined chunks).  The largest power of two within
+// that is taken when it reaches 3/4 of S_max (it usually divides K into
+// whole chunks, the faster interior form), else S_max itself.  Measured
+// (128 tiles; us): 1024x1024x8192 S=1 58, S=4 25, S=8 28; 512x512x65536
+// fp16 S=8 63, S=16 42; 1024^3 S=1 faster than S=2; 768x768x32768 (36
+// tiles) S=4 63, S=7 51; 384x384x65536 (9 tiles) S=16 37, S=28 32;
+// 896x896x16384 (49 tiles) S=4 and S=5 level.
 int64_t pick_split(const Call &c, int layout, int64_t tiles, int tile)
 {
-    int64_t s = 1;
-    while (tiles * s * 2 <= 256 && c.K / (s * 2) >= 2048 && dma_any(c, layout, s * 2, tile))
-        s *= 2;
-    return s;
+    int64_t s_max = CUS / tiles;
+    if (c.K / 2048 < s_max)
+        s_max = c.K / 2048;
+    if (s_max <= 1)
+        return 1;
+    int64_t p2 = 1;
+    while (p2 * 2 <= s_max)
+        p2 *= 2;
+    if (4 * p2 < 3 * s_max && dma_any(c, layout, s_max, tile))
+        return s_max;
+    for (; p2 > 1; p2 /= 2)
+        if (dma_any(c, layout, p2, tile))
+            return p2;
+    return 1;
 }
 
 // The pipelined kernel's interior form at tile 256 runs with 4 waves of

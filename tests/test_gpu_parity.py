@@ -492,6 +492,19 @@ def test_unsplit_rows_selector_random():
     assert untouched
 
 
+def test_uneven_split_selector_random():
+    """36 tiles of 128 and a 32768-long K: the selector splits K seven ways
+    (252 work units, range-checked slices of 4704 and a shorter last one);
+    U[-1,1] fp16 -> fp32 compared in full within the stated tolerance."""
+    p = W.random_problem(768, 768, 32768, "f16", "f32", ("uniform", -1.0, 1.0), seed=895)
+    plan = {}
+    c, untouched = run(p, plan=plan)
+    assert (plan["block_m"], plan["split_k"], plan["ragged"]) == (128, 7, 1), plan
+    err, tol = compare(p, c, label="split 7 768x768x32768")
+    note(f"split 7 768x768x32768: max err {err:.3e} tol {tol:.3e}")
+    assert untouched
+
+
 def _round8(x):
     return -(-x // 8) * 8
 

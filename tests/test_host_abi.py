@@ -120,6 +120,14 @@ def test_selector_measured_workloads():
         gm, gn = -(-M // 256), -(-N // 256)
         assert (dp_rows // 256) * gn <= 256 * (gm * gn // 256) < (dp_rows // 256 + 1) * gn
         assert (gm - dp_rows // 256) * gn * S <= 256
+    # fewer 128-wide tiles than CUs: S up to min(256 / tiles, K / 2048), a
+    # power of two when that reaches 3/4 of it
+    for M, N, K, S, ragged in [(768, 768, 32768, 7, 1), (384, 384, 65536, 28, 1),
+                               (896, 896, 16384, 4, 0), (640, 640, 32768, 8, 0),
+                               (256, 256, 65536, 32, 0), (1024, 1024, 4096, 2, 0)]:
+        st, p = plan(M, N, K, A=1 << 40, B=2 << 40, C=3 << 40, ind=F16, outd=F32)
+        assert st == 0 and (p["block_m"], p["split_k"], p["ragged"]) == (128, S, ragged), \
+            (M, N, K, p)
     # enough tiles: no split
     st, p = plan(4096, 4096, 65536, A=1 << 40, B=2 << 40, C=3 << 40, ind=F16, outd=F32)
     assert st == 0 and p["split_k"] == 1 and p["workspace_bytes"] == 0
