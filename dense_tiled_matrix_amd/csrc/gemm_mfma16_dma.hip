@@ -536,43 +536,47 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
 // cycles for (r >> 1) & 3, (r >> 1) & 6 or no swizzle.
 __device__ __forceinline__ int swz_row128(int r) { return (r >> 1) & 7; }
 
-// The 256 x 256, 4-wave interior kernel with paired stages, for K slices of
-// an even number of chunks.  Two 64-KiB regions each hold two consecutive
+// The 256 x 256 interior kernel (4 or 8 waves, as gemm_mfma16_dma_kernel)
+// with paired stages, for K slices of an even number of chunks.  Two 64-KiB regions each hold two consecutive
 // 32-deep chunks.  A K-contiguous operand is staged as 256 rows of 128
 // bytes (both chunks of a row side by side), so every load instruction
 // reads 8 whole 128-byte lines instead of 16 half lines; an M/N-contiguous
 // operand keeps the layout of one chunk per 16 KiB half.  A region is
 // refilled (both chunks) once per two chunks, during the odd iterations, as
 // soon as both its chunks have been read.  Measured against the one-chunk
-// stages, bf16: 8192^3 NN +1%, NT +3%, 4096^3 NT +5%; fp16 4096^3 +2%.
-template <int IN, int OUT, bool TA, bool TB>
-__global__ __launch_bounds__(256) void gemm_mfma16_pair_kernel(GemmArgs p, int64_t grid_m,
-                                                                 int64_t grid_n, int64_t splits,
-                                                                 int64_t k_split,
-                                                                 int64_t c_split_stride)
+// stages, bf16: 8192^3 NN +3.5%, NT +8%, TT +5%; fp16 4096^3 -> fp32 +3%;
+// with 8 waves (K < 2048) 16384^2 x 1024 NN +2%, NT +5%.
+template <int IN, int OUT, int NWAVES, bool TA, bool TB>
+__global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_pair_kernel(GemmArgs p, int64_t grid_m,
+                                                                         int64_t grid_n,
+                                                                         int64_t splits,
+                                                                         int64_t k_split,
+                                                                         int64_t c_split_stride)
 {
-    constexpr int TILE = 256, NWAVES = 4;
+    constexpr int TILE = 256;
     constexpr int BM = TILE, BN = TILE;
     constexpr int HALF = TILE * BK * 2;              // one chunk of one operand: 16 KiB
     constexpr int OPB = 2 * HALF;                    // an operand's part of a region: 32 KiB
     constexpr int REGION = 2 * OPB;                  // 64 KiB
     constexpr int ROWB = TILE * 2;                   // an M/N-contiguous k-row
     constexpr bool A_KC = !TA, B_KC = TB;
-    constexpr int WM_ROWS = 128, WN_COLS = 128;
-    constexpr int MT = 8, NT = 8;
+    constexpr int WAVES_N = NWAVES / 2;
+    constexpr int WM_ROWS = 128, WN_COLS = TILE / WAVES_N;
+    constexpr int MT = WM_ROWS / 16, NT = WN_COLS / 16;
+    constexpr bool A_DB = NWAVES == 4;  // 8 waves: one A buffer, as in gemm_mfma16_dma_kernel
     constexpr int A_READS = MT * (A_KC ? 1 : 2);
     constexpr int NREAD = A_READS + NT * (B_KC ? 1 : 2);
     constexpr int NMFMA = MT * NT;
     constexpr int SEGS = OPB / 1024 / NWAVES;       // 1 KiB loads per operand per region: 8
     constexpr int GROUP = 2 * SEGS;                  // loads per region refill: 16
-    static_assert(NMFMA % GROUP == 0 && GROUP < 64, "pair schedule");
+    static_assert(NMFMA % GROUP == 0 && 2 * GROUP < 64, "pair schedule");
 
     __shared__ __attribute__((aligned(1024))) char lds[2 * REGION];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
     int64_t pid_m, pid_n;
     const int64_t tiles = grid_m * grid_n;
@@ -617,40 +621,45 @@ __global__ __launch_bounds__(256) void gemm_mfma16_pair_kernel(GemmArgs p, int64
             dma16(b_src[d - SEGS] + j * b_pair, b_dst0 + ro + 1024 * (d - SEGS));
     };
 
-    // fragment offsets within a region, for each 32-k half h
-    auto frag_off2 = [&](bool kc, int base, int h) __attribute__((always_inline)) {
+    // Fragment offsets within a region for the first 32-k half.  The second
+    // half's are derived: a K-contiguous row's unit (4 + G) ^ f sits at
+    // ((G ^ f) ^ 4) * 16, i.e. the offset XOR 64 (rows are 128-byte
+    // aligned); an M/N-contiguous half is HALF bytes further.
+    auto frag_off0 = [&](bool kc, int base) __attribute__((always_inline)) {
         const int G = lane >> 4, li = lane & 15;
         if (kc) {
             const int r = base + li;
-            return r * 128 + (((4 * h + G) ^ swz_row128(r)) * 16);
+            return r * 128 + ((G ^ swz_row128(r)) * 16);
         }
-        return h * HALF + frag_off<false, TILE>(base, lane);
+        return frag_off<false, TILE>(base, lane);
     };
-    int a_off[2][MT], b_off[2][NT];
+    auto half_off = [](bool kc, int off, int h) __attribute__((always_inline)) {
+        return kc ? (h ? off ^ 64 : off) : off + h * HALF;
+    };
+    int a_off[MT], b_off[NT];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int i = 0; i < MT; ++i)
+        a_off[i] = frag_off0(A_KC, wm * WM_ROWS + i * 16);
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
-            a_off[h][i] = frag_off2(A_KC, wm * WM_ROWS + i * 16, h);
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-            b_off[h][j] = OPB + frag_off2(B_KC, wn * WN_COLS + j * 16, h);
-    }
+    for (int j = 0; j < NT; ++j)
+        b_off[j] = OPB + frag_off0(B_KC, wn * WN_COLS + j * 16);
 
     u32x4 fa0[MT], fa1[MT], fb0[NT], fb1[NT];
     auto read_a = [&](u32x4 (&fa)[MT], const char *rg, int h, int i) __attribute__((always_inline)) {
+        const int o = half_off(A_KC, a_off[i], h);
         if constexpr (A_KC) {
-            fa[i] = *LDS_PTR(const u32x4, rg + a_off[h][i]);
+            fa[i] = *LDS_PTR(const u32x4, rg + o);
         } else {
-            read_tr_half(fa[i], 0, rg + a_off[h][i]);
-            read_tr_half(fa[i], 1, rg + a_off[h][i] + 4 * ROWB);
+            read_tr_half(fa[i], 0, rg + o);
+            read_tr_half(fa[i], 1, rg + o + 4 * ROWB);
         }
     };
     auto read_b = [&](u32x4 (&fb)[NT], const char *rg, int h, int q) __attribute__((always_inline)) {
         if constexpr (B_KC) {
-            fb[q] = *LDS_PTR(const u32x4, rg + b_off[h][q]);
+            fb[q] = *LDS_PTR(const u32x4, rg + half_off(true, b_off[q], h));
         } else {
-            read_tr_half(fb[q >> 1], q & 1, rg + b_off[h][q >> 1] + 4 * ROWB * (q & 1));
+            const int o = half_off(false, b_off[q >> 1], h);
+            read_tr_half(fb[q >> 1], q & 1, rg + o + 4 * ROWB * (q & 1));
         }
     };
     constexpr int B_READS = NT * (B_KC ? 1 : 2);
@@ -675,13 +684,20 @@ __global__ __launch_bounds__(256) void gemm_mfma16_pair_kernel(GemmArgs p, int64
             const int i = q / NT, j = q % NT;
             acc[i][j] = mfma<IN>(fa[i], fb[j], acc[i][j]);
             if (reads) {
-                const int r0 = q * NREAD / NMFMA, r1 = (q + 1) * NREAD / NMFMA;
+                if constexpr (A_DB) {
+                    const int r0 = q * NREAD / NMFMA, r1 = (q + 1) * NREAD / NMFMA;
 #pragma unroll
-                for (int r = r0; r < r1; ++r) {
-                    if (r < B_READS)
-                        read_b(fbn, nrg, nh, r);
-                    else if ((r - B_READS) % A_PER == 0)
-                        read_a(fan, nrg, nh, (r - B_READS) / A_PER);
+                    for (int r = r0; r < r1; ++r) {
+                        if (r < B_READS)
+                            read_b(fbn, nrg, nh, r);
+                        else if ((r - B_READS) % A_PER == 0)
+                            read_a(fan, nrg, nh, (r - B_READS) / A_PER);
+                    }
+                } else {
+                    if (q < B_READS)
+                        read_b(fbn, nrg, nh, q);
+                    if (j == NT - 1)
+                        read_a(fa, nrg, nh, i);
                 }
             }
             if (dma_reg >= 0 && (q + 1) % (NMFMA / GROUP) == 0)
@@ -723,31 +739,35 @@ __global__ __launch_bounds__(256) void gemm_mfma16_pair_kernel(GemmArgs p, int64
         asm volatile("" ::: "memory");
         const int64_t n = c + 1;
         const char *nrg = lds + ((n >> 1) & 1) * REGION;
+        // the next chunk's half is known at compile time: c odd -> c + 1 even
+        constexpr int NH = ODD ? 0 : 1;
         if constexpr (ODD) {
             const int64_t jt = (c + 3) / 2 < np ? (c + 3) / 2 : np - 1;
-            step(fa, fan, fb, fbn, nrg, static_cast<int>(n & 1), true, jt,
-                 static_cast<int>(((c - 1) >> 1) & 1));
+            step(fa, fan, fb, fbn, nrg, NH, true, jt, static_cast<int>(((c - 1) >> 1) & 1));
         } else {
-            step(fa, fan, fb, fbn, nrg, static_cast<int>(n & 1), true, 0, -1);
+            step(fa, fan, fb, fbn, nrg, NH, true, 0, -1);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
     // nk is even: chunk 0 runs alone (then its successor's fragments are
     // copied back), chunks 1 .. nk - 2 in (odd, even) pairs, chunk nk - 1
     // last, from fa0 / fb0.
-    iter(fa0, fa1, fb0, fb1, 0, std::false_type{});
+    auto &fa1r = A_DB ? fa1 : fa0;
+    iter(fa0, fa1r, fb0, fb1, 0, std::false_type{});
 #pragma unroll
     for (int j = 0; j < NT; ++j)
         fb0[j] = fb1[j];
+    if constexpr (A_DB) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
-        fa0[i] = fa1[i];
+        for (int i = 0; i < MT; ++i)
+            fa0[i] = fa1[i];
+    }
     for (int64_t c = 1; c + 1 < nk; c += 2) {
-        iter(fa0, fa1, fb0, fb1, c, std::true_type{});
-        iter(fa1, fa0, fb1, fb0, c + 1, std::false_type{});
+        iter(fa0, fa1r, fb0, fb1, c, std::true_type{});
+        iter(fa1r, fa0, fb1, fb0, c + 1, std::false_type{});
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-    step(fa0, fa1, fb0, fb1, lds, 0, false, 0, -1);
+    step(fa0, fa1r, fb0, fb1, lds, 0, false, 0, -1);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
 
     void *c_out = static_cast<char *>(p.C) + slice * c_split_stride * (OUT == DTM_F32 ? 4 : 2);
@@ -813,12 +833,19 @@ hipError_t launch(const GemmArgs &a, const DmaLaunch &l, hipStream_t s)
         const dim3 grid((unsigned)(cdiv(a.M, 256) * cdiv(a.N, 256) * l.splits));
         const int64_t ks = slice_k(a.K, l.splits, false);
         if (DTM_DMA_PAIRS && (ks / BK) % 2 == 0)
-            hipLaunchKernelGGL((gemm_mfma16_pair_kernel<IN, OUT, TA, TB>), grid, dim3(256), 0, s,
-                               a, cdiv(a.M, 256), cdiv(a.N, 256), l.splits, ks, a.M * a.N);
+            hipLaunchKernelGGL((gemm_mfma16_pair_kernel<IN, OUT, 4, TA, TB>), grid, dim3(256), 0,
+                               s, a, cdiv(a.M, 256), cdiv(a.N, 256), l.splits, ks, a.M * a.N);
         else
             hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, 256, 4, TA, TB, false>), grid,
                                dim3(256), 0, s, a, cdiv(a.M, 256), cdiv(a.N, 256), l.splits,
                                ks, a.M * a.N, 0u, 0u);
+        return hipGetLastError();
+    }
+    if (!l.ragged && DTM_DMA_PAIRS && (slice_k(a.K, l.splits, false) / BK) % 2 == 0) {
+        hipLaunchKernelGGL((gemm_mfma16_pair_kernel<IN, OUT, 8, TA, TB>),
+                           dim3((unsigned)(cdiv(a.M, 256) * cdiv(a.N, 256) * l.splits)), dim3(512),
+                           0, s, a, cdiv(a.M, 256), cdiv(a.N, 256), l.splits,
+                           slice_k(a.K, l.splits, false), a.M * a.N);
         return hipGetLastError();
     }
     return launch_one<IN, OUT, 256, 8, TA, TB>(a, l, s);
