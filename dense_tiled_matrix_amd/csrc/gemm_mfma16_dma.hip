@@ -536,32 +536,35 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
 // cycles for (r >> 1) & 3, (r >> 1) & 6 or no swizzle.
 __device__ __forceinline__ int swz_row128(int r) { return (r >> 1) & 7; }
 
-// The 256 x 256 interior kernel (4 or 8 waves, as gemm_mfma16_dma_kernel)
-// with paired stages, for K slices of an even number of chunks.  Two 64-KiB regions each hold two consecutive
-// 32-deep chunks.  A K-contiguous operand is staged as 256 rows of 128
+// The interior kernel (tile 256 with 4 or 8 waves, 192 or 128 with 4, as
+// gemm_mfma16_dma_kernel) with paired stages, for K slices of an even number
+// of chunks.  Two regions (64 KiB at tile 256) each hold two consecutive
+// 32-deep chunks.  A K-contiguous operand is staged as TILE rows of 128
 // bytes (both chunks of a row side by side), so every load instruction
 // reads 8 whole 128-byte lines instead of 16 half lines; an M/N-contiguous
-// operand keeps the layout of one chunk per 16 KiB half.  A region is
+// operand keeps the layout of one chunk per half (16 KiB at tile 256).
+// Tile 192: 3072^3 bf16 +1.7%, 6144^3 +0.6%; tile 128 is correct but not
+// launched (13-20% slower on the small and split-K grids it serves).  A region is
 // refilled (both chunks) once per two chunks, during the odd iterations, as
 // soon as both its chunks have been read.  Measured against the one-chunk
 // stages, bf16: 8192^3 NN +3.5%, NT +8%, TT +5%; fp16 4096^3 -> fp32 +3%;
 // with 8 waves (K < 2048) 16384^2 x 1024 NN +2%, NT +5%.
-template <int IN, int OUT, int NWAVES, bool TA, bool TB>
+template <int IN, int OUT, int TILE, int NWAVES, bool TA, bool TB>
 __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_pair_kernel(GemmArgs p, int64_t grid_m,
                                                                          int64_t grid_n,
                                                                          int64_t splits,
                                                                          int64_t k_split,
                                                                          int64_t c_split_stride)
 {
-    constexpr int TILE = 256;
     constexpr int BM = TILE, BN = TILE;
-    constexpr int HALF = TILE * BK * 2;              // one chunk of one operand: 16 KiB
-    constexpr int OPB = 2 * HALF;                    // an operand's part of a region: 32 KiB
-    constexpr int REGION = 2 * OPB;                  // 64 KiB
+    constexpr int HALF = TILE * BK * 2;              // one chunk of one operand: 16 KiB at 256
+    constexpr int OPB = 2 * HALF;                    // an operand's part of a region
+    constexpr int REGION = 2 * OPB;                  // 64 KiB at 256
+    constexpr int LPR = krow_chunks<TILE>();         // 16-byte chunks per M/N-contiguous k-row
     constexpr int ROWB = TILE * 2;                   // an M/N-contiguous k-row
     constexpr bool A_KC = !TA, B_KC = TB;
     constexpr int WAVES_N = NWAVES / 2;
-    constexpr int WM_ROWS = 128, WN_COLS = TILE / WAVES_N;
+    constexpr int WM_ROWS = TILE / 2, WN_COLS = TILE / WAVES_N;
     constexpr int MT = WM_ROWS / 16, NT = WN_COLS / 16;
     constexpr bool A_DB = NWAVES == 4;  // 8 waves: one A buffer, as in gemm_mfma16_dma_kernel
     constexpr int A_READS = MT * (A_KC ? 1 : 2);
@@ -595,8 +598,8 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_pair_kernel(GemmArgs 
             const int u = (lane & 7) ^ swz_row128(r);
             return X + (mn0 + r) * s_mn + kb + 8 * u;
         }
-        const int g = 64 * seg + lane, kp = g >> 5;
-        const int c = krow_logical<TILE>(g & 31, kp & 31);
+        const int g = 64 * seg + lane, kp = g / LPR;
+        const int c = krow_logical<TILE>(g % LPR, kp % BK);
         return X + (kb + kp) * s_k + mn0 + 8 * c;
     };
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
@@ -810,18 +813,32 @@ hipError_t launch_one(const GemmArgs &a, const DmaLaunch &l, hipStream_t s)
     const int64_t gm = cdiv(a.M, TILE), gn = cdiv(a.N, TILE);
     const dim3 grid((unsigned)(gm * gn * l.splits)), block(64 * NWAVES);
     const int64_t ks = slice_k(a.K, l.splits, l.ragged);
-    if (l.ragged)
-        hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, TILE, NWAVES, TA, TB, true>), grid,
-                           block, 0, s, a, gm, gn, l.splits, ks, a.M * a.N, l.a_bytes, l.b_bytes);
-    else
+    if (l.ragged) {
+        // the 256-wide 4-wave form has no range-checked instantiation
+        if constexpr (TILE == 256 && NWAVES == 4)
+            return hipErrorInvalidConfiguration;
+        else
+            hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, TILE, NWAVES, TA, TB, true>),
+                               grid, block, 0, s, a, gm, gn, l.splits, ks, a.M * a.N,
+                               l.a_bytes, l.b_bytes);
+    } else if (TILE != 128 && DTM_DMA_PAIRS && (ks / BK) % 2 == 0) {
+        // paired stages pay on the 256- and 192-wide tiles (measured: 0.1-2%
+        // faster on square bf16 shapes); on the 128-wide tile, whose grids are
+        // small or split along K, they were 13-20% slower than the 4-stage form
+        if constexpr (TILE != 128)
+            hipLaunchKernelGGL((gemm_mfma16_pair_kernel<IN, OUT, TILE, NWAVES, TA, TB>), grid,
+                               block, 0, s, a, gm, gn, l.splits, ks, a.M * a.N);
+    } else {
         hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, TILE, NWAVES, TA, TB, false>), grid,
                            block, 0, s, a, gm, gn, l.splits, ks, a.M * a.N, 0u, 0u);
+    }
     return hipGetLastError();
 }
 
 // The instantiated (tile, waves, form) combinations: 256 with 8 waves in
 // either form or 4 waves in the interior form, 192 and 128 with 4 waves in
-// either.
+// either; the 256- and 192-wide interior forms with paired stages when each
+// K slice holds an even number of chunks.
 template <int IN, int OUT, bool TA, bool TB>
 hipError_t launch(const GemmArgs &a, const DmaLaunch &l, hipStream_t s)
 {
@@ -829,25 +846,8 @@ hipError_t launch(const GemmArgs &a, const DmaLaunch &l, hipStream_t s)
         return launch_one<IN, OUT, 128, 4, TA, TB>(a, l, s);
     if (l.tile == 192)
         return launch_one<IN, OUT, 192, 4, TA, TB>(a, l, s);
-    if (l.waves == 4 && !l.ragged) {
-        const dim3 grid((unsigned)(cdiv(a.M, 256) * cdiv(a.N, 256) * l.splits));
-        const int64_t ks = slice_k(a.K, l.splits, false);
-        if (DTM_DMA_PAIRS && (ks / BK) % 2 == 0)
-            hipLaunchKernelGGL((gemm_mfma16_pair_kernel<IN, OUT, 4, TA, TB>), grid, dim3(256), 0,
-                               s, a, cdiv(a.M, 256), cdiv(a.N, 256), l.splits, ks, a.M * a.N);
-        else
-            hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, 256, 4, TA, TB, false>), grid,
-                               dim3(256), 0, s, a, cdiv(a.M, 256), cdiv(a.N, 256), l.splits,
-                               ks, a.M * a.N, 0u, 0u);
-        return hipGetLastError();
-    }
-    if (!l.ragged && DTM_DMA_PAIRS && (slice_k(a.K, l.splits, false) / BK) % 2 == 0) {
-        hipLaunchKernelGGL((gemm_mfma16_pair_kernel<IN, OUT, 8, TA, TB>),
-                           dim3((unsigned)(cdiv(a.M, 256) * cdiv(a.N, 256) * l.splits)), dim3(512),
-                           0, s, a, cdiv(a.M, 256), cdiv(a.N, 256), l.splits,
-                           slice_k(a.K, l.splits, false), a.M * a.N);
-        return hipGetLastError();
-    }
+    if (l.waves == 4)
+        return launch_one<IN, OUT, 256, 4, TA, TB>(a, l, s);
     return launch_one<IN, OUT, 256, 8, TA, TB>(a, l, s);
 }
 
