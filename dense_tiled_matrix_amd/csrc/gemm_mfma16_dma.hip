@@ -529,6 +529,16 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
     }
 }
 
+// 1: wait and barrier in every iteration of the paired-stage loop, not
+// only in the odd ones (the loop's comment gives why the even ones are
+// not needed)
+#ifndef DTM_PAIR_EVEN_SYNC
+#define DTM_PAIR_EVEN_SYNC 0
+#endif
+#ifndef DTM_PAIR_DMA_SPAN
+#define DTM_PAIR_DMA_SPAN 8
+#endif
+
 // Swizzle of the 128-byte rows of the paired stages: 16-byte unit u of row r
 // sits at u ^ ((r >> 1) & 7).  Measured with an in-bounds probe of the
 // fragment read order (lane l: row l % 16, unit 4h + l / 16 for either 32-k
@@ -667,6 +677,11 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_pair_kernel(GemmArgs 
     };
     constexpr int B_READS = NT * (B_KC ? 1 : 2);
     constexpr int A_PER = A_KC ? 1 : 2;
+    // a refill's loads over the first DTM_PAIR_DMA_SPAN eighths of a chunk's
+    // MFMAs: all of them (measured: 6/8 0-1.5% slower, 4/8 1-6%, 2/8 5-8%)
+    constexpr int SPAN = DTM_PAIR_DMA_SPAN;
+    constexpr int DMA_EVERY = NMFMA * SPAN / 8 / GROUP > 0 ? NMFMA * SPAN / 8 / GROUP : 1;
+    static_assert(DMA_EVERY * GROUP <= NMFMA, "a refill must fit in one chunk's MFMAs");
 
     floatx4 acc[MT][NT];
 #pragma unroll
@@ -703,8 +718,8 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_pair_kernel(GemmArgs 
                         read_a(fa, nrg, nh, i);
                 }
             }
-            if (dma_reg >= 0 && (q + 1) % (NMFMA / GROUP) == 0)
-                dma_one(dma_j, dma_reg, (q + 1) / (NMFMA / GROUP) - 1);
+            if (dma_reg >= 0 && (q + 1) % DMA_EVERY == 0 && (q + 1) / DMA_EVERY <= GROUP)
+                dma_one(dma_j, dma_reg, (q + 1) / DMA_EVERY - 1);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -732,13 +747,20 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_pair_kernel(GemmArgs 
     // so after the barrier of odd iteration c both chunks c - 1 and c of
     // region ((c - 1) / 2) % 2 have been read, and it takes pair
     // (c + 3) / 2 (the last pair again past the end).  Chunk c + 1 was
-    // loaded by the refill of odd iteration c - 3 (c even) or c - 2 (c odd),
-    // so at most one refill (c even) or none (c odd) is younger.
+    // loaded by the refill of odd iteration c - 3 (c even) or c - 2 (c odd).
+    // An odd iteration waits for every load (none younger than that refill)
+    // and then for all waves.  An even iteration needs neither: its chunk
+    // c + 1 came with chunk c, already waited for and published by the
+    // barrier of iteration c - 1, and no refill of its region starts before
+    // the barrier of iteration c + 1 (measured: 0-0.8% faster than a wait
+    // and barrier in every iteration).
     auto iter = [&](u32x4 (&fa)[MT], u32x4 (&fan)[MT], const u32x4 (&fb)[NT], u32x4 (&fbn)[NT],
                     int64_t c, auto odd_tag) __attribute__((always_inline)) {
         constexpr bool ODD = decltype(odd_tag)::value;
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(ODD ? 0 : GROUP, 0));
-        __builtin_amdgcn_s_barrier();
+        if (ODD || DTM_PAIR_EVEN_SYNC) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(ODD ? 0 : GROUP, 0));
+            __builtin_amdgcn_s_barrier();
+        }
         asm volatile("" ::: "memory");
         const int64_t n = c + 1;
         const char *nrg = lds + ((n >> 1) & 1) * REGION;
