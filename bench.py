@@ -30,7 +30,7 @@ METRIC = "GEMM TFLOP/s and % of MFMA peak at fp16/bf16 4096³ and 8192³ on 1 MI
 # MI355X dense MFMA peaks (TFLOP/s): 256 CUs x 2.4 GHz x FLOP/clk/CU
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
-HOST_THREADS_CAP = 16  # the host-core share of one GPU on the GPU machines
+HOST_THREADS_CAP = 16  # host threads for the CPU baseline: the host-core share of one GPU
 # sources of the kernels whose traffic profiles/traffic.json records (the
 # pipelined MFMA GEMM, the split-K reduce, the row softmax)
 KERNEL_SOURCES = ["dense_tiled_matrix_amd/csrc/gemm_mfma16_dma.hip",
