@@ -1,6 +1,6 @@
 """Build the CPU oracle's shared library (plain C, gcc, no fast-math).
 
-TEST INFRASTRUCTURE ONLY: the oracle is the checker, never the product path.
+TEST INFRASTRUCTURE ONLY: the oracle checks the GPU path and is never part of it.
 """
 from __future__ import annotations
 
