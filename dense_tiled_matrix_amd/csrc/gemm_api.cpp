@@ -403,8 +403,14 @@ int64_t pick_split(const Call &c, int layout, int64_t tiles, int tile)
 // TFLOP/s, 8 -> 4 waves): K = 4096 and up gained 0.7-3.8% (fp16 4096^3
 // 1160 -> 1204, 8192^3 1347 -> 1364, 6144^3, 5120^3) except 8192 x 4096 x
 // 4096 (1313 -> 1295); K = 1024 lost (4096 x 4096 x 1024 966 -> 948,
-// 16384 x 16384 x 1024 1068 -> 885).  The range-checked form has 8 waves.
-constexpr int64_t FOUR_WAVE_MIN_K = 2048;
+// 16384 x 16384 x 1024 1068 -> 885).  With the paired stages, K = 2048 still
+// favours 8 waves (8192^2 x 2048 NN +2.8%, NT +1.2%) and K = 3072 4 waves
+// (fp16 8192^2 x 3072 -> fp32 +4.6%, 6144^2 x 3072 level).  The
+// range-checked form has 8 waves.
+#ifndef DTM_FOUR_WAVE_MIN_K
+#define DTM_FOUR_WAVE_MIN_K 3072
+#endif
+constexpr int64_t FOUR_WAVE_MIN_K = DTM_FOUR_WAVE_MIN_K;
 
 int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
 {

@@ -421,17 +421,17 @@ def test_pipelined_layouts_random(layout):
 
 @pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])
 def test_four_wave_selector_random(layout):
-    """192 tiles of 256 and a 2048-long K loop: the selector's 4-wave form
+    """192 tiles of 256 and a 3072-long K loop: the selector's 4-wave form
     of the pipelined kernel, N(0,1) bf16 in every layout, compared in full
     within the stated tolerance."""
-    p = W.random_problem(4096, 3072, 2048, "bf16", "bf16", ("normal", 0.0, 1.0), seed=720,
+    p = W.random_problem(4096, 3072, 3072, "bf16", "bf16", ("normal", 0.0, 1.0), seed=720,
                          a_layout=layout[0], b_layout=layout[1])
     plan = {}
     c, untouched = run(p, plan=plan)
     assert (plan["block_m"], plan["block_k"], plan["threads"], plan["ragged"]) == \
         (256, 32, 256, 0), plan
     assert plan["layout"] == LAYOUT_BITS[layout], plan
-    err, tol = compare(p, c, label=f"4 waves {layout} 4096x3072x2048")
+    err, tol = compare(p, c, label=f"4 waves {layout} 4096x3072x3072")
     note(f"4 waves {layout}: max err {err:.3e} tol {tol:.3e}")
     assert untouched
 

@@ -346,7 +346,7 @@ def test_forced_configs():
 
 def test_pipelined_wave_count():
     """The 256-wide pipelined tile runs 4 waves (256 threads) on its interior
-    form when each tile's K loop is at least 2048 long, else 8 (512
+    form when each tile's K loop is at least 3072 long, else 8 (512
     threads); the 192- and 128-wide tiles run 4; a forced size must be one
     the form has, and only that tile takes one."""
     big = dict(A=1 << 40, B=2 << 40, C=3 << 40)
@@ -354,8 +354,9 @@ def test_pipelined_wave_count():
             (8192, 8192, 8192, dict(), 256),
             (8192, 8192, 8192, dict(sam=1, sak=8192, sbk=1, sbn=8192), 256),
             (4096, 4096, 4096, dict(), 256),
-            (4096, 4096, 2048, dict(), 256),
-            (4096, 4096, 2016, dict(), 512),                       # K loop under 2048
+            (4096, 4096, 3072, dict(), 256),
+            (4096, 4096, 3040, dict(), 512),                       # K loop under 3072
+            (4096, 4096, 2048, dict(), 512),
             (16384, 16384, 1024, dict(), 512),
             (4096, 8192, 64, dict(), 512),
             (8000, 8000, 8000, dict(), 512),                       # range-checked form
