@@ -46,7 +46,7 @@ class TileConfig(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("block_m", ctypes.c_int32),
                 ("block_n", ctypes.c_int32), ("block_k", ctypes.c_int32),
                 ("split_k", ctypes.c_int32), ("threads", ctypes.c_int32),
-                ("dp_rows", ctypes.c_int32)]
+                ("dp_rows", ctypes.c_int32), ("workspace_limit", ctypes.c_uint64)]
 
 
 class Plan(ctypes.Structure):
@@ -116,6 +116,14 @@ def lib():
         L.gemm_kernel_name.restype = ctypes.c_char_p
         L.gemm_set_pointer_checks.argtypes = [i32]
         L.gemm_set_pointer_checks.restype = i32
+        L.gemm_mfma_probe.argtypes = [i32, i32, i32, vp, vp, vp, vp]
+        L.gemm_mfma_probe.restype = i32
+        L.gemm_workspace_reserve.argtypes = [u64, vp]
+        L.gemm_workspace_reserve.restype = i32
+        L.gemm_workspace_release.argtypes = [vp]
+        L.gemm_workspace_release.restype = i32
+        L.gemm_workspace_reserved.argtypes = [vp]
+        L.gemm_workspace_reserved.restype = u64
         sops = [i64, i64, vp, i64, i64, vp, i64, i64, i32, i32]
         L.row_softmax.argtypes = sops + [vp]
         L.row_softmax.restype = i32
@@ -147,6 +155,64 @@ def gemm_status_string(status: int) -> str:
 
 def gemm_kernel_name(kernel: int) -> str:
     return lib().gemm_kernel_name(int(kernel)).decode()
+
+
+# ---------------------------------------------------------------- workspace
+
+# The selector's split plans keep slices x rows x N x 4 bytes of fp32 partials:
+# 16 MiB for 512 x 512 in 16 slices, up to ~128 MiB for the last tile-rows of a
+# C near 8192 wide in 16 slices.  A smaller reservation only splits less.
+DEFAULT_WORKSPACE_BYTES = 256 << 20
+
+
+def _current_cuda(device):
+    import torch
+
+    return torch.device(device) if device is not None else \
+        torch.device("cuda", torch.cuda.current_device())
+
+
+def reserve_workspace(nbytes: int = DEFAULT_WORKSPACE_BYTES, stream=None, device=None) -> None:
+    """Reserve (at least) ``nbytes`` of library workspace for ``stream``
+    (default: torch's current stream) through ``gemm_workspace_reserve``.
+
+    ``gemm``/``row_softmax`` never allocate: a plan that splits K keeps its
+    fp32 partials in this workspace and splits only as far as they fit, so
+    without a reservation such shapes run unsplit.  This call may allocate
+    and wait for the stream; make it before timing or graph capture."""
+    import torch
+
+    dev = _current_cuda(device)
+    with torch.cuda.device(dev):
+        st = lib().gemm_workspace_reserve(int(nbytes), _stream(dev, stream))
+    if st != DTM_OK:
+        raise GemmError(st, "gemm_workspace_reserve")
+
+
+def release_workspace(stream=None, device=None) -> None:
+    """Free the workspace reserved for ``stream`` (``gemm_workspace_release``)."""
+    import torch
+
+    dev = _current_cuda(device)
+    with torch.cuda.device(dev):
+        st = lib().gemm_workspace_release(_stream(dev, stream))
+    if st != DTM_OK:
+        raise GemmError(st, "gemm_workspace_release")
+
+
+def workspace_reserved(stream=None, device=None) -> int:
+    """Bytes reserved for ``stream`` (``gemm_workspace_reserved``)."""
+    import torch
+
+    dev = _current_cuda(device)
+    with torch.cuda.device(dev):
+        return int(lib().gemm_workspace_reserved(_stream(dev, stream)))
+
+
+def gemm_mfma_probe_raw(in_dtype, layout, paired, A, B, C, stream=None):
+    """``gemm_mfma_probe`` on raw device pointers; returns the status."""
+    s = ctypes.c_void_p(0 if stream is None else int(stream))
+    return lib().gemm_mfma_probe(in_dtype, layout, paired, A, B, C, s)
 
 
 # ---------------------------------------------------------------- tensors
@@ -188,6 +254,28 @@ def _operands(a, b, out, out_dtype):
     return M, N, K, out
 
 
+def _device_of(*tensors):
+    """The one CUDA device all ``tensors`` live on; ValueError otherwise (a
+    host pointer handed to a kernel would fault the GPU, not fail)."""
+    devs = {t.device for t in tensors}
+    if len(devs) != 1:
+        raise ValueError(f"tensors are on different devices: {sorted(map(str, devs))}")
+    dev = devs.pop()
+    if dev.type != "cuda":
+        raise ValueError(f"every tensor must be on a CUDA device, got {dev}")
+    return dev
+
+
+def _on_device(device, call):
+    """Run ``call()`` with ``device`` as the current HIP device."""
+    import torch
+
+    if device.index is None or device.index == torch.cuda.current_device():
+        return call()
+    with torch.cuda.device(device):
+        return call()
+
+
 def _args(a, b, out, M, N, K):
     return (M, N, K, a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(), b.stride(0),
             b.stride(1), out.data_ptr(), out.stride(0), out.stride(1), _dtype_code(a.dtype),
@@ -216,11 +304,14 @@ def gemm(a, b, out=None, out_dtype=None, stream=None):
 
     ``a`` (M x K) and ``b`` (K x N) are device tensors of one dtype (float32,
     float16 or bfloat16) with any strides; ``out`` (M x N) may be given, else
-    it is allocated with ``out_dtype`` (default float32).  The call is
-    asynchronous on ``stream`` (default: torch's current stream).
+    it is allocated with ``out_dtype`` (default float32).  All must live on
+    one CUDA device (ValueError otherwise).  The call is asynchronous on
+    ``stream`` (default: torch's current stream); split-K plans use the
+    workspace reserved for that stream (``reserve_workspace``).
     """
     M, N, K, out = _operands(a, b, out, out_dtype)
-    st = lib().gemm(*_args(a, b, out, M, N, K), _stream(a.device, stream))
+    dev = _device_of(a, b, out)
+    st = _on_device(dev, lambda: lib().gemm(*_args(a, b, out, M, N, K), _stream(dev, stream)))
     if st != DTM_OK:
         raise GemmError(st, "gemm")
     return out
@@ -230,10 +321,11 @@ def gemm_ex(a, b, out=None, out_dtype=None, config=None, workspace=None, stream=
     """``gemm`` with a forced tile configuration (a dict of dtm_tile_config
     fields or a TileConfig) and an optional workspace tensor."""
     M, N, K, out = _operands(a, b, out, out_dtype)
+    dev = _device_of(a, b, out, *([workspace] if workspace is not None else []))
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib().gemm_ex(*_args(a, b, out, M, N, K), _config(config), ws_ptr, ws_bytes,
-                       _stream(a.device, stream))
+    st = _on_device(dev, lambda: lib().gemm_ex(*_args(a, b, out, M, N, K), _config(config),
+                                               ws_ptr, ws_bytes, _stream(dev, stream)))
     if st != DTM_OK:
         raise GemmError(st, "gemm_ex")
     return out
@@ -308,7 +400,8 @@ def row_softmax(x, out=None, out_dtype=None, stream=None):
     ``out_dtype``, default x's dtype, when not given; it may be ``x`` itself
     for an in-place call)."""
     out = _softmax_operands(x, out, out_dtype)
-    st = lib().row_softmax(*_softmax_args(x, out), _stream(x.device, stream))
+    dev = _device_of(x, out)
+    st = _on_device(dev, lambda: lib().row_softmax(*_softmax_args(x, out), _stream(dev, stream)))
     if st != DTM_OK:
         raise GemmError(st, "row_softmax")
     return out

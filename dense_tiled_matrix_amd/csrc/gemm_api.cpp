@@ -12,9 +12,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
-#include <map>
-#include <mutex>
-#include <utility>
+#include <optional>
 
 #include "dtm_gemm.h"
 #include "host_util.h"
@@ -80,40 +78,6 @@ int check_device()
     return ok ? DTM_OK : DTM_ERR_DEVICE;
 }
 
-// ---- library-owned workspace (split-K partials, split-row softmax statistics) ---------------------------------------
-// One buffer per (device, stream), grown on demand.  Growing first waits for
-// the stream (earlier work may still read the old buffer), then frees and
-// allocates.  Work on one stream runs in order, so reuse within a stream is
-// safe; different streams never share a buffer.
-namespace {
-std::mutex g_ws_mutex;
-std::map<std::pair<int, void *>, std::pair<void *, uint64_t>> g_ws;
-}  // namespace
-
-void *library_workspace(void *stream, uint64_t bytes)
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return nullptr;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    auto &e = g_ws[{dev, stream}];
-    if (e.second >= bytes)
-        return e.first;
-    if (e.first) {
-        if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
-            return nullptr;
-        (void)hipFree(e.first);
-        e.first = nullptr;
-        e.second = 0;
-    }
-    void *ptr = nullptr;
-    if (hipMalloc(&ptr, bytes) != hipSuccess)
-        return nullptr;
-    e.first = ptr;
-    e.second = bytes;
-    return ptr;
-}
-
 }  // namespace dtm
 
 namespace {
@@ -123,7 +87,6 @@ using dtm::cdiv;
 using dtm::check_device;
 using dtm::GemmArgs;
 using dtm::item_size;
-using dtm::library_workspace;
 using dtm::valid_dtype;
 using dtm::view_range;
 
@@ -330,7 +293,8 @@ Call upper_rows(const Call &c, int64_t rows)
 constexpr double TAIL_PARTIAL_COST = 0.3;
 constexpr int64_t TAIL_MAX_SPLIT = 16, TAIL_MIN_SLICE = 256;
 
-bool pick_tail_split(const Call &c, int layout, int plain_tile, int64_t &dp_rows, int64_t &split)
+bool pick_tail_split(const Call &c, int layout, int plain_tile, uint64_t ws_budget,
+                     int64_t &dp_rows, int64_t &split)
 {
     const int64_t gm = cdiv(c.M, 256), gn = cdiv(c.N, 256), tiles = gm * gn;
     if (tiles <= CUS || tiles % CUS == 0)
@@ -352,7 +316,11 @@ bool pick_tail_split(const Call &c, int layout, int plain_tile, int64_t &dp_rows
     const double dp = static_cast<double>(cdiv(rows_dp * gn, CUS)) * nk;
     double best = 0.97 * plain;
     bool found = false;
+    // fp32 partials of one slice of the split rows
+    const uint64_t slice_bytes = static_cast<uint64_t>(low.M) * static_cast<uint64_t>(c.N) * 4u;
     for (int64_t S = 2; S <= TAIL_MAX_SPLIT && tail * S <= CUS; ++S) {
+        if (static_cast<uint64_t>(S) > ws_budget / slice_bytes)
+            break;
         if (c.K / S < TAIL_MIN_SLICE || !dma_any(low, layout, S, 256))
             continue;
         const double t = dp + std::ceil(nk / static_cast<double>(S)) +
@@ -377,11 +345,13 @@ bool pick_tail_split(const Call &c, int layout, int plain_tile, int64_t &dp_rows
 // fp16 S=8 63, S=16 42; 1024^3 S=1 faster than S=2; 768x768x32768 (36
 // tiles) S=4 63, S=7 51; 384x384x65536 (9 tiles) S=16 37, S=28 32;
 // 896x896x16384 (49 tiles) S=4 and S=5 level.
-int64_t pick_split(const Call &c, int layout, int64_t tiles, int tile)
+int64_t pick_split(const Call &c, int layout, int64_t tiles, int tile, int64_t cap)
 {
     int64_t s_max = CUS / tiles;
     if (c.K / 2048 < s_max)
         s_max = c.K / 2048;
+    if (cap < s_max)
+        s_max = cap;
     if (s_max <= 1)
         return 1;
     int64_t p2 = 1;
@@ -412,7 +382,10 @@ int64_t pick_split(const Call &c, int layout, int64_t tiles, int tile)
 #endif
 constexpr int64_t FOUR_WAVE_MIN_K = DTM_FOUR_WAVE_MIN_K;
 
-int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
+// The plan for a call.  ws_budget: bytes of workspace the call can use;
+// the selector splits K only as far as its partials fit in it (UINT64_MAX:
+// no limit).  A forced split is not capped; run() then checks the workspace.
+int make_plan(const Call &c, const dtm_tile_config *force, uint64_t ws_budget, dtm_plan *out)
 {
     if (!out)
         return DTM_ERR_NULL_POINTER;
@@ -474,11 +447,16 @@ int make_plan(const Call &c, const dtm_tile_config *force, dtm_plan *out)
                                                                                          : 256;
                 p.block_m = p.block_n = tile;
                 p.block_k = 32;
+                const uint64_t slice_bytes =
+                    static_cast<uint64_t>(c.M) * static_cast<uint64_t>(c.N) * 4u;
+                const uint64_t cap = ws_budget / slice_bytes;
                 p.split_k = tile == 128 ? static_cast<int32_t>(pick_split(
-                                              c, layout, cdiv(c.M, 128) * cdiv(c.N, 128), 128))
+                                              c, layout, cdiv(c.M, 128) * cdiv(c.N, 128), 128,
+                                              cap < CUS ? static_cast<int64_t>(cap) : CUS))
                                         : 1;
                 int64_t dp_rows = 0, tail_split = 1;
-                if (tile != 128 && pick_tail_split(c, layout, tile, dp_rows, tail_split)) {
+                if (tile != 128 &&
+                    pick_tail_split(c, layout, tile, ws_budget, dp_rows, tail_split)) {
                     p.block_m = p.block_n = 256;
                     p.split_k = static_cast<int32_t>(tail_split);
                     p.dp_rows = dp_rows;
@@ -637,11 +615,27 @@ int launch_plan(const Call &c, const dtm_plan &p, void *ws, hipStream_t s)
     return e == hipSuccess ? DTM_OK : DTM_ERR_LAUNCH;
 }
 
+// The workspace a call can use: the caller's (gemm_ex) or what is reserved
+// for the stream, capped by a forced workspace_limit.
+uint64_t call_budget(const dtm_tile_config *force, uint64_t available)
+{
+    const uint64_t limit = force && force->workspace_limit ? force->workspace_limit : UINT64_MAX;
+    return available < limit ? available : limit;
+}
+
 int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t workspace_bytes,
         void *stream)
 {
+    // Without a caller's workspace, the one reserved for this stream (if
+    // any) bounds the plan; the lease is held until every launch of this
+    // call is queued.
+    std::optional<dtm::WorkspaceLease> lease;
+    if (!workspace)
+        lease.emplace(stream);
+    void *ws = workspace ? workspace : lease->ptr();
+    const uint64_t ws_bytes = workspace ? workspace_bytes : lease->bytes();
     dtm_plan p;
-    int st = make_plan(c, force, &p);
+    int st = make_plan(c, force, call_budget(force, ws_bytes), &p);
     if (st != DTM_OK)
         return st;
     if (p.kernel == DTM_KERNEL_NONE)
@@ -654,17 +648,11 @@ int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t w
         if (st != DTM_OK)
             return st;
     }
-    void *ws = nullptr;
     if (p.split_k > 1) {
-        ws = workspace;
-        if (ws) {
-            if (workspace_bytes < p.workspace_bytes || (reinterpret_cast<uintptr_t>(ws) & 15))
-                return DTM_ERR_WORKSPACE;
-        } else {
-            ws = library_workspace(stream, p.workspace_bytes);
-            if (!ws)
-                return DTM_ERR_WORKSPACE;
-        }
+        if (!ws || ws_bytes < p.workspace_bytes || (reinterpret_cast<uintptr_t>(ws) & 15))
+            return DTM_ERR_WORKSPACE;
+    } else {
+        ws = nullptr;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (p.dp_rows == 0)
@@ -672,13 +660,14 @@ int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t w
     // Unsplit top rows, then the split rows below them, in stream order.
     const Call top = upper_rows(c, p.dp_rows), low = lower_rows(c, p.dp_rows);
     const int32_t threads = force ? force->threads : 0;
-    const dtm_tile_config f_top{DTM_KERNEL_MFMA_F16, p.block_m, p.block_n, p.block_k, 1, threads, 0};
+    const dtm_tile_config f_top{DTM_KERNEL_MFMA_F16, p.block_m, p.block_n, p.block_k, 1, threads,
+                                0, 0};
     const dtm_tile_config f_low{DTM_KERNEL_MFMA_F16, p.block_m, p.block_n, p.block_k, p.split_k,
-                                threads, 0};
+                                threads, 0, 0};
     dtm_plan p_top, p_low;
-    st = make_plan(top, &f_top, &p_top);
+    st = make_plan(top, &f_top, UINT64_MAX, &p_top);
     if (st == DTM_OK)
-        st = make_plan(low, &f_low, &p_low);
+        st = make_plan(low, &f_low, UINT64_MAX, &p_low);
     if (st != DTM_OK)
         return st;
     st = launch_plan(top, p_top, nullptr, s);
@@ -705,7 +694,7 @@ int gemm_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t stride_am,
 {
     const Call c{M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C, stride_cm,
                  stride_cn, in_dtype, out_dtype};
-    return make_plan(c, force, out);
+    return make_plan(c, force, call_budget(force, UINT64_MAX), out);
 }
 
 int gemm_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t stride_am, int64_t stride_ak,
@@ -730,7 +719,9 @@ const char *gemm_status_string(int status)
                "range overflows";
     case DTM_ERR_ALIAS: return "C overlaps A or B";
     case DTM_ERR_CONFIG: return "forced tile configuration is not available for this problem";
-    case DTM_ERR_WORKSPACE: return "workspace too small or its allocation failed";
+    case DTM_ERR_WORKSPACE:
+        return "workspace smaller than the plan needs (reserve one with gemm_workspace_reserve "
+               "or pass a larger one), or its reservation failed";
     case DTM_ERR_DEVICE: return "current HIP device is not gfx950 or could not be queried";
     case DTM_ERR_LAUNCH: return "kernel launch failed";
     case DTM_ERR_POINTER:
@@ -750,6 +741,28 @@ const char *gemm_kernel_name(int kernel)
     case DTM_KERNEL_GENERIC_FP16ACC: return "generic_fp16acc";
     }
     return "unknown";
+}
+
+int gemm_mfma_probe(int in_dtype, int layout, int paired, const void *A, const void *B, void *C,
+                    void *stream)
+{
+    if (in_dtype != DTM_F16 && in_dtype != DTM_BF16)
+        return DTM_ERR_DTYPE;
+    if (layout < 0 || layout > (DTM_LAYOUT_A_M_CONTIG | DTM_LAYOUT_B_K_CONTIG) ||
+        (paired != 0 && paired != 1))
+        return DTM_ERR_CONFIG;
+    if (!A || !B || !C)
+        return DTM_ERR_NULL_POINTER;
+    if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B) |
+         reinterpret_cast<uintptr_t>(C)) & 15)
+        return DTM_ERR_STRIDE;
+    const int st = check_device();
+    if (st != DTM_OK)
+        return st;
+    const hipError_t e = dtm::launch_mfma_probe(in_dtype, layout, paired != 0, A, B,
+                                                static_cast<float *>(C),
+                                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DTM_OK : DTM_ERR_LAUNCH;
 }
 
 int gemm_set_pointer_checks(int on)

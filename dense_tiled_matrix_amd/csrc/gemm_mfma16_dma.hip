@@ -546,6 +546,20 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
 // cycles for (r >> 1) & 3, (r >> 1) & 6 or no swizzle.
 __device__ __forceinline__ int swz_row128(int r) { return (r >> 1) & 7; }
 
+// Byte offset, within a paired-stage region's operand part, of this lane's
+// fragment read for the 16 rows/columns starting at `base`, first 32-k half.
+// K-contiguous: row base + l % 16 of 128 bytes, unit l / 16 (swizzled);
+// otherwise the one-chunk layout of frag_off.
+template <bool KC, int TILE> __device__ __forceinline__ int frag_off_pair(int base, int lane)
+{
+    if constexpr (KC) {
+        const int G = lane >> 4, r = base + (lane & 15);
+        return r * 128 + ((G ^ swz_row128(r)) * 16);
+    } else {
+        return frag_off<false, TILE>(base, lane);
+    }
+}
+
 // The interior kernel (tile 256 with 4 or 8 waves, 192 or 128 with 4, as
 // gemm_mfma16_dma_kernel) with paired stages, for K slices of an even number
 // of chunks.  Two regions (64 KiB at tile 256) each hold two consecutive
@@ -638,24 +652,16 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_pair_kernel(GemmArgs 
     // half's are derived: a K-contiguous row's unit (4 + G) ^ f sits at
     // ((G ^ f) ^ 4) * 16, i.e. the offset XOR 64 (rows are 128-byte
     // aligned); an M/N-contiguous half is HALF bytes further.
-    auto frag_off0 = [&](bool kc, int base) __attribute__((always_inline)) {
-        const int G = lane >> 4, li = lane & 15;
-        if (kc) {
-            const int r = base + li;
-            return r * 128 + ((G ^ swz_row128(r)) * 16);
-        }
-        return frag_off<false, TILE>(base, lane);
-    };
     auto half_off = [](bool kc, int off, int h) __attribute__((always_inline)) {
         return kc ? (h ? off ^ 64 : off) : off + h * HALF;
     };
     int a_off[MT], b_off[NT];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
-        a_off[i] = frag_off0(A_KC, wm * WM_ROWS + i * 16);
+        a_off[i] = frag_off_pair<A_KC, TILE>(wm * WM_ROWS + i * 16, lane);
 #pragma unroll
     for (int j = 0; j < NT; ++j)
-        b_off[j] = OPB + frag_off0(B_KC, wn * WN_COLS + j * 16);
+        b_off[j] = OPB + frag_off_pair<B_KC, TILE>(wn * WN_COLS + j * 16, lane);
 
     u32x4 fa0[MT], fa1[MT], fb0[NT], fb1[NT];
     auto read_a = [&](u32x4 (&fa)[MT], const char *rg, int h, int i) __attribute__((always_inline)) {
@@ -908,7 +914,102 @@ hipError_t dispatch_in(const GemmArgs &a, int in, int layout, int out, const Dma
     return hipErrorInvalidValue;
 }
 
+
+// ---- fragment-layout probe --------------------------------------------------
+// One wave, one v_mfma_f32_16x16x32_{f16,bf16} on a 16 x 32 A and a 32 x 16 B.
+// Each operand is staged into LDS in the layout the kernels above give it (a
+// K-contiguous operand as swizzled rows of 64 bytes, or of 128 bytes in the
+// paired stages; an M/N-contiguous one as k-rows of the 256-wide tile), its
+// fragment is read with the same offsets and instructions, and the result is
+// written with the epilogue's lane map.  With integer inputs every sum is
+// exact, so a wrong lane <-> element map for A, B or C shows as wrong values.
+// A: element (i, k) at A[i * 32 + k], or A[k * 16 + i] when TA (M-contiguous);
+// B: element (k, j) at B[k * 16 + j], or B[j * 32 + k] when TB (K-contiguous);
+// C: element (i, j) at C[i * 16 + j].
+template <int IN, bool TA, bool TB, bool PAIR>
+__global__ __launch_bounds__(64) void mfma_probe_kernel(const uint16_t *A, const uint16_t *B,
+                                                        float *C)
+{
+    constexpr int TILE = 256;
+    constexpr int ROWB = TILE * 2;
+    constexpr int OPB = (PAIR ? 2 : 1) * operand_stage_bytes<TILE>();  // one operand's part
+    __shared__ __attribute__((aligned(1024))) char lds[2 * OPB];
+    const int lane = threadIdx.x;
+
+    // 16 bytes per lane: 16 rows x 4 chunks of 8 k, or 32 k-rows x 2 chunks
+    // of 8 columns
+    auto stage = [&](const uint16_t *X, bool kc, char *dst) __attribute__((always_inline)) {
+        if (kc) {
+            const int r = lane >> 2, c = lane & 3;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(X + r * 32 + 8 * c);
+            const int off = PAIR ? r * 128 + ((c ^ swz_row128(r)) * 16)
+                                 : r * 64 + ((c ^ swz_row(r)) * 16);
+            *LDS_PTR(u32x4, dst + off) = v;
+        } else {
+            const int k = lane >> 1, c = lane & 1;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(X + k * 16 + 8 * c);
+            *LDS_PTR(u32x4, dst + k * ROWB + krow_phys<TILE>(c, k) * 16) = v;
+        }
+    };
+    auto fragment = [&](bool kc, const char *src) __attribute__((always_inline)) {
+        u32x4 f;
+        if (kc) {
+            f = *LDS_PTR(const u32x4,
+                         src + (PAIR ? frag_off_pair<true, TILE>(0, lane) : frag_off<true, TILE>(0, lane)));
+        } else {
+            const int o = frag_off<false, TILE>(0, lane);
+            read_tr_half(f, 0, src + o);
+            read_tr_half(f, 1, src + o + 4 * ROWB);
+        }
+        return f;
+    };
+    stage(A, !TA, lds);
+    stage(B, TB, lds + OPB);
+    __syncthreads();
+    const u32x4 fa = fragment(!TA, lds);
+    const u32x4 fb = fragment(TB, lds + OPB);
+    const floatx4 acc = mfma<IN>(fa, fb, floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+        C[(4 * (lane >> 4) + v) * 16 + (lane & 15)] = acc[v];
+}
+
+template <int IN, bool TA, bool TB>
+hipError_t launch_probe(bool pair, const void *A, const void *B, float *C, hipStream_t s)
+{
+    const uint16_t *a = static_cast<const uint16_t *>(A), *b = static_cast<const uint16_t *>(B);
+    if (pair)
+        hipLaunchKernelGGL((mfma_probe_kernel<IN, TA, TB, true>), dim3(1), dim3(64), 0, s, a, b, C);
+    else
+        hipLaunchKernelGGL((mfma_probe_kernel<IN, TA, TB, false>), dim3(1), dim3(64), 0, s, a, b, C);
+    return hipGetLastError();
+}
+
+template <int IN>
+hipError_t probe_layout(int layout, bool pair, const void *A, const void *B, float *C,
+                        hipStream_t s)
+{
+    switch (layout) {
+    case 0: return launch_probe<IN, false, false>(pair, A, B, C, s);
+    case DTM_LAYOUT_A_M_CONTIG: return launch_probe<IN, true, false>(pair, A, B, C, s);
+    case DTM_LAYOUT_B_K_CONTIG: return launch_probe<IN, false, true>(pair, A, B, C, s);
+    case DTM_LAYOUT_A_M_CONTIG | DTM_LAYOUT_B_K_CONTIG:
+        return launch_probe<IN, true, true>(pair, A, B, C, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_probe(int in, int layout, bool pair, const void *A, const void *B, float *C,
+                             hipStream_t s)
+{
+    if (in == DTM_F16)
+        return probe_layout<DTM_F16>(layout, pair, A, B, C, s);
+    if (in == DTM_BF16)
+        return probe_layout<DTM_BF16>(layout, pair, A, B, C, s);
+    return hipErrorInvalidValue;
+}
 
 bool mfma16_dma_fits(int64_t M, int64_t N, int64_t K, int64_t splits, int tile)
 {

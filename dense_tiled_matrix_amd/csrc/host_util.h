@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "dtm_gemm.h"
 
 namespace dtm {
@@ -70,11 +72,30 @@ int check_view_memory(uintptr_t lo, uintptr_t hi);
 // (cached per device).
 int check_device();
 
-// A device buffer of at least `bytes` owned by the library, one per (current
-// device, stream), grown on demand: growing first synchronises the stream
-// (earlier work may still use the old buffer), then frees and allocates.
-// Work on one stream runs in order, so reuse within a stream is safe.
-// nullptr when the allocation fails.
-void *library_workspace(void *stream, uint64_t bytes);
+// The workspace reserved for (current device, stream) by
+// gemm_workspace_reserve, leased for one call: the lease holds that
+// workspace's lock until it is destroyed, so every launch of the call that
+// uses it is queued before another call (or a reservation) can touch it.
+// ptr() == nullptr and bytes() == 0 when nothing is reserved.  Never
+// allocates and never waits for the GPU.
+struct WorkspaceEntry;
+class WorkspaceLease {
+public:
+    explicit WorkspaceLease(void *stream);
+    void *ptr() const { return ptr_; }
+    uint64_t bytes() const { return bytes_; }
+
+private:
+    std::unique_lock<std::mutex> lock_;
+    void *ptr_ = nullptr;
+    uint64_t bytes_ = 0;
+};
+
+// Grow the workspace of (current device, stream) to at least `bytes` (waits
+// for the stream before freeing a smaller one); release frees it (after
+// waiting for the stream).  DTM_OK or DTM_ERR_WORKSPACE.
+int workspace_reserve(void *stream, uint64_t bytes);
+int workspace_release(void *stream);
+uint64_t workspace_reserved(void *stream);
 
 }  // namespace dtm

@@ -61,6 +61,12 @@ bool mfma32_has_config(int bm, int bn, int bk);
 hipError_t launch_mfma32(const GemmArgs &a, int out_dtype, int bm, int bn, int bk, int layout,
                          bool ragged, hipStream_t s);
 
+// One MFMA of the pipelined kernels on a 16 x 32 A and a 32 x 16 B, through
+// their LDS staging, fragment reads and epilogue lane map (layout: dtm_layout
+// bits; pair: the paired-stage row layout).  C: 16 x 16 fp32, row-major.
+hipError_t launch_mfma_probe(int in_dtype, int layout, bool pair, const void *A, const void *B,
+                             float *C, hipStream_t s);
+
 // Writes zeros to the M x N view of C (the K == 0 product).
 hipError_t launch_zero_fill(const GemmArgs &a, int out_dtype, hipStream_t s);
 

@@ -92,7 +92,10 @@ bool block_fill_pays(int64_t N, int64_t chunk_row)
     return 4 * N >= 3 * chunk_row * ch;
 }
 
-int make_plan(const SCall &c, dtm_softmax_plan *out)
+// ws_budget: bytes of workspace the call can use (UINT64_MAX: no limit);
+// the SPLIT form keeps 8 bytes per row and part in it, so its part count is
+// capped to what fits, and without room for two parts the row is not split.
+int make_plan(const SCall &c, uint64_t ws_budget, dtm_softmax_plan *out)
 {
     if (!out)
         return DTM_ERR_NULL_POINTER;
@@ -138,6 +141,9 @@ int make_plan(const SCall &c, dtm_softmax_plan *out)
         const int64_t tile = dtm::softmax_tile(c.in, vec);
         const int64_t want = dtm::cdiv(SPLIT_WGS, c.M), tiles = dtm::cdiv(c.N, tile);
         parts = want < tiles ? want : tiles;
+        const uint64_t fit = ws_budget / (8u * static_cast<uint64_t>(c.M));
+        if (static_cast<uint64_t>(parts) > fit)
+            parts = static_cast<int64_t>(fit);
         if (parts >= 2) {
             // no empty part: part length rounded up to whole tiles
             const int64_t len = dtm::cdiv(dtm::cdiv(c.N, parts), tile) * tile;
@@ -179,8 +185,11 @@ int row_softmax(int64_t M, int64_t N, const void *X, int64_t stride_xm, int64_t 
 {
     const SCall c = make_call(M, N, X, stride_xm, stride_xn, Y, stride_ym, stride_yn, in_dtype,
                               out_dtype);
+    // the split form's workspace: what is reserved for this stream, leased
+    // until the launches are queued (no allocation here)
+    const dtm::WorkspaceLease lease(stream);
     dtm_softmax_plan p;
-    int st = make_plan(c, &p);
+    int st = make_plan(c, lease.bytes(), &p);
     if (st != DTM_OK)
         return st;
     if (p.form == DTM_SOFTMAX_NONE)
@@ -202,14 +211,7 @@ int row_softmax(int64_t M, int64_t N, const void *X, int64_t stride_xm, int64_t 
             return st;
     }
     const dtm::SoftmaxArgs a{M, N, X, stride_xm, stride_xn, Y, stride_ym, stride_yn};
-    float *ws = nullptr;
-    if (p.form == DTM_SOFTMAX_SPLIT) {
-        ws = static_cast<float *>(dtm::library_workspace(
-            stream, static_cast<uint64_t>(2 * sizeof(float)) * static_cast<uint64_t>(M) *
-                        static_cast<uint64_t>(p.parts)));
-        if (!ws)
-            return DTM_ERR_WORKSPACE;
-    }
+    float *ws = p.form == DTM_SOFTMAX_SPLIT ? static_cast<float *>(lease.ptr()) : nullptr;
     const hipError_t e = dtm::launch_softmax(
         a, in_dtype, out_dtype, p.form, p.form == DTM_SOFTMAX_SPLIT ? p.parts : p.chunks,
         p.vectorized != 0, ws, static_cast<hipStream_t>(stream));
@@ -222,7 +224,7 @@ int row_softmax_plan(int64_t M, int64_t N, const void *X, int64_t stride_xm, int
 {
     return make_plan(make_call(M, N, X, stride_xm, stride_xn, Y, stride_ym, stride_yn, in_dtype,
                                out_dtype),
-                     out);
+                     UINT64_MAX, out);
 }
 
 }  // extern "C"

@@ -30,7 +30,13 @@
  *     caller.  The library keeps no pointer after a call returns.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
  *     and the call returns without waiting; the result is visible once the
- *     caller synchronises that stream.  Calls are thread-safe.
+ *     caller synchronises that stream.  gemm, gemm_ex and row_softmax never
+ *     allocate or free device memory and never wait for the GPU: the only
+ *     device memory they use beyond the caller's views is a workspace the
+ *     caller passes (gemm_ex) or reserved beforehand for the stream with
+ *     gemm_workspace_reserve.  Calls are thread-safe: calls on one stream
+ *     that use its reserved workspace queue their launches one call at a
+ *     time.
  *   - Every argument check runs on the host before anything is launched; on
  *     a non-zero status nothing was launched and C is untouched.
  *   - A and B may have any strides, including zero (broadcast), negative and
@@ -68,8 +74,8 @@ typedef enum {
     DTM_ERR_ALIAS = 5,        /* C's address range intersects A's or B's */
     DTM_ERR_CONFIG = 6,       /* a forced tile configuration that does not exist or
                                  cannot serve this problem */
-    DTM_ERR_WORKSPACE = 7,    /* workspace smaller than the plan needs, or its allocation
-                                 failed */
+    DTM_ERR_WORKSPACE = 7,    /* workspace smaller than a forced split needs, or
+                                 gemm_workspace_reserve could not allocate */
     DTM_ERR_DEVICE = 8,       /* the current device is not gfx950 or cannot be queried */
     DTM_ERR_LAUNCH = 9,       /* the HIP runtime reported an error when launching */
     DTM_ERR_POINTER = 10      /* pointer checks on (gemm_set_pointer_checks): a view's
@@ -118,6 +124,9 @@ typedef struct {
     int32_t dp_rows; /* with split_k > 1 on the pipelined kernel: the first dp_rows rows
                         of C (a multiple of block_m, below M) run unsplit and only the
                         rows below them in split_k slices; 0 = every row split */
+    uint64_t workspace_limit; /* bytes of workspace the selector may plan for (it splits K
+                                 only as far as the partials fit); 0 = no limit beyond the
+                                 workspace the call has.  A forced split_k is not capped. */
 } dtm_tile_config;
 
 /* What gemm() would launch for a problem.  Produced on the host only. */
@@ -139,16 +148,20 @@ typedef struct {
 } dtm_plan;
 
 /*
- * gemm -- C = A.B (the computation stated at the top of this header).
- * M, N, K: logical sizes (K is the logical shared dimension, independent of
- *   the storage A and B are views into).  in_dtype: dtype of A and B;
- *   out_dtype: dtype of C.  stream: hipStream_t or NULL.
- * The library picks the kernel and tile with its selector.  When the chosen
- * plan splits K it uses a workspace owned by the library, one per (device,
- * stream), grown on demand (a device allocation the first time a larger one
- * is needed; growing first waits for the stream's earlier work).  A plan
- * with dtm_plan.dp_rows > 0 runs as launches in stream order on row ranges of
- * the same views: the unsplit top rows, then the split rows and their sum.
+ * gemm -- C = A.B (the computation stated at the top of this header), the
+ * host wrapper of "Chapter 13: The Blocked Matmul Kernel", section 13.1: the
+ * caller owns C, K is the logical shared dimension (independent of the
+ * storage A and B are views into, as in section 13.2's sentinel example) and
+ * the output dtype is the caller's choice (section 13.3).
+ * in_dtype: dtype of A and B; out_dtype: dtype of C.  stream: hipStream_t or
+ * NULL.
+ * The library picks the kernel and tile with its selector.  A plan that
+ * splits K keeps fp32 partials in the workspace reserved for (current
+ * device, stream) by gemm_workspace_reserve; the selector splits only as far
+ * as they fit there (with nothing reserved, it does not split).  Allocates
+ * nothing, frees nothing and does not wait for the GPU.  A plan with
+ * dtm_plan.dp_rows > 0 runs as launches in stream order on row ranges of the
+ * same views: the unsplit top rows, then the split rows and their sum.
  * Returns a dtm_status.
  */
 int gemm(int64_t M, int64_t N, int64_t K,
@@ -159,9 +172,17 @@ int gemm(int64_t M, int64_t N, int64_t K,
 
 /*
  * gemm_plan -- validate the arguments of gemm() and report the plan it would
- * launch, on the host, without touching a GPU.  `force` may be NULL (the
- * selector decides) or a configuration as for gemm_ex().  Writes *out.
- * Returns the same status gemm()/gemm_ex() would return before launching.
+ * launch, on the host, without touching a GPU: the launch grid
+ * (cdiv(M, BLOCK_M), cdiv(N, BLOCK_N)) and the K-loop trip count
+ * cdiv(K, BLOCK_K) of "Chapter 13: The Blocked Matmul Kernel", section 13.1
+ * (Worked Example 13.1.1: grid (2, 2) with 2 K-iterations for M = N = K = 8
+ * on 4 x 4 x 4 tiles).  `force` may be NULL (the selector decides) or a
+ * configuration as for gemm_ex().  The plan is the one gemm_ex() runs with a
+ * caller's workspace of at least plan.workspace_bytes, and the one gemm()
+ * runs when the stream's reserved workspace is at least that large; with a
+ * smaller workspace the selector splits K less (force->workspace_limit shows
+ * that plan).  Writes *out.  Returns the status gemm()/gemm_ex() would
+ * return before launching.
  */
 int gemm_plan(int64_t M, int64_t N, int64_t K,
               const void *A, int64_t stride_am, int64_t stride_ak,
@@ -172,16 +193,21 @@ int gemm_plan(int64_t M, int64_t N, int64_t K,
 
 /*
  * gemm_ex -- gemm() with a forced tile configuration and an optional
- * caller-owned workspace.
+ * caller-owned workspace.  The tile sizes are the BLOCK_M, BLOCK_N, BLOCK_K
+ * meta-parameters of "Chapter 13: The Blocked Matmul Kernel", section 13.1,
+ * which that chapter's worked examples set by hand (4 x 4 x 4 in Worked
+ * Example 13.1.1).
  * force: NULL or a dtm_tile_config whose non-zero fields override the
- *   selector (for example {DTM_KERNEL_GENERIC, 4, 4, 4, 0, 0, 0} runs 4x4x4 tiles).
- *   A configuration the library does not have, or an MFMA kernel for a
- *   layout it cannot serve, gives DTM_ERR_CONFIG.
- * workspace, workspace_bytes: device memory of at least plan.workspace_bytes
- *   bytes, used when the plan splits K; NULL means the library's own
- *   per-device workspace.  The workspace must not be in use by other work
- *   that can run concurrently on the device.
- * Returns a dtm_status.
+ *   selector (for example {DTM_KERNEL_GENERIC, 4, 4, 4, 0, 0, 0, 0} runs 4x4x4
+ *   tiles).  A configuration the library does not have, or an MFMA kernel
+ *   for a layout it cannot serve, gives DTM_ERR_CONFIG.
+ * workspace, workspace_bytes: device memory (16-byte aligned) the plan may
+ *   use for split-K partials; the selector splits K only as far as they fit.
+ *   NULL means the workspace reserved for the stream (gemm_workspace_reserve),
+ *   as in gemm().  A forced split_k needing more than the workspace gives
+ *   DTM_ERR_WORKSPACE.  A caller's workspace must not be in use by other
+ *   work that can run concurrently on the device.
+ * Allocates nothing and does not wait for the GPU.  Returns a dtm_status.
  */
 int gemm_ex(int64_t M, int64_t N, int64_t K,
             const void *A, int64_t stride_am, int64_t stride_ak,
@@ -191,7 +217,36 @@ int gemm_ex(int64_t M, int64_t N, int64_t K,
             const dtm_tile_config *force, void *workspace, uint64_t workspace_bytes,
             void *stream);
 
-/* gemm_status_string -- a static, NUL-terminated description of a status. */
+/*
+ * gemm_workspace_reserve -- make sure the library holds at least `bytes` of
+ * device workspace for (current device, stream), for the split-K partials
+ * of gemm()/gemm_ex() and the split-row statistics of row_softmax() on that
+ * stream.  Unlike those calls it may allocate, and when it replaces a
+ * smaller buffer it first waits for the stream's earlier work.  Call it
+ * outside any code that must not allocate (for example before a graph
+ * capture).  Never shrinks.  Returns DTM_OK, or DTM_ERR_WORKSPACE when the
+ * allocation (or the wait) fails, leaving nothing reserved.
+ * (The splitting it serves is not on the pages: "Chapter 13: The Blocked
+ * Matmul Kernel", section 13.1 gives each tile one accumulator over the
+ * whole K; split-K gives each K slice its own fp32 accumulator and sums
+ * them in fp32, section 13.3's accumulation precision.)
+ */
+int gemm_workspace_reserve(uint64_t bytes, void *stream);
+
+/* gemm_workspace_release -- wait for the stream, then free its reserved
+ * workspace (later calls on it plan without one).  Returns DTM_OK or
+ * DTM_ERR_WORKSPACE when the wait fails. */
+int gemm_workspace_release(void *stream);
+
+/* gemm_workspace_reserved -- bytes reserved for (current device, stream);
+ * 0 when none. */
+uint64_t gemm_workspace_reserved(void *stream);
+
+/* gemm_status_string -- a static, NUL-terminated description of a status.
+ * Every check runs before anything is launched, so a bad call fails on the
+ * host with a message rather than on the GPU (the "Triton matmul" notes,
+ * "Things that break": the failure to want is the one raised before the
+ * GPU is reached). */
 const char *gemm_status_string(int status);
 
 /* gemm_kernel_name -- a static name for a dtm_kernel value. */
@@ -210,6 +265,25 @@ const char *gemm_kernel_name(int kernel);
  * a value other than "0" when the library loads.  Process-wide and
  * thread-safe; returns the previous setting (0 or 1). */
 int gemm_set_pointer_checks(int on);
+
+/*
+ * gemm_mfma_probe -- diagnostic: one 16 x 16 x 32 matrix-core product of the
+ * fp16/bf16 kernels, C = A.B for a 16 x 32 A and a 32 x 16 B, with the
+ * operands staged in LDS, their fragments read and the result stored exactly
+ * as those kernels do (the layouts behind the tile product of "Chapter 13:
+ * The Blocked Matmul Kernel", section 13.1, on this hardware).  On
+ * integer-valued inputs the result is exact, so it pins the lane <-> element
+ * maps of both operands and the result.
+ * in_dtype: DTM_F16 or DTM_BF16.  layout: dtm_layout bits.  paired: 1 for
+ * the 128-byte rows of the paired stages, 0 for the 64-byte rows.
+ * A: 512 elements, element (i, k) at A[i*32 + k], or at A[k*16 + i] with
+ * DTM_LAYOUT_A_M_CONTIG.  B: 512 elements, element (k, j) at B[k*16 + j], or
+ * at B[j*32 + k] with DTM_LAYOUT_B_K_CONTIG.  C: 256 fp32, element (i, j) at
+ * C[i*16 + j].  Device memory, 16-byte aligned, owned by the caller.
+ * Enqueued on `stream`.  Returns a dtm_status.
+ */
+int gemm_mfma_probe(int in_dtype, int layout, int paired, const void *A, const void *B, void *C,
+                    void *stream);
 
 #ifdef __cplusplus
 }

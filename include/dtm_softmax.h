@@ -33,8 +33,9 @@ typedef enum {
     DTM_SOFTMAX_BLOCK = 2,  /* one 1024-thread workgroup per row, row in registers */
     DTM_SOFTMAX_ONLINE = 3, /* one workgroup per row, running max/sum pass then a write pass */
     DTM_SOFTMAX_SPLIT = 4   /* few long rows: each row cut into `parts` workgroups; a pass
-                               writing each part's max/sum to a small library-owned buffer,
-                               then a pass merging them in a fixed order and writing */
+                               writing each part's max/sum to the stream's reserved
+                               workspace, then a pass merging them in a fixed order and
+                               writing */
 } dtm_softmax_form;
 
 /* What row_softmax() would launch.  Produced on the host only. */
@@ -59,9 +60,11 @@ typedef struct {
  * Y may be exactly X (same pointer, strides and element size: in place);
  *   any other overlap of their byte ranges is DTM_ERR_ALIAS.
  * in_dtype, out_dtype: dtm_dtype of X and Y.  stream: hipStream_t or NULL.
- * The SPLIT form uses 8*M*parts bytes of a per-(device, stream) buffer the
- * library owns (the one GEMM split-K uses), grown on demand; a failed
- * allocation returns DTM_ERR_WORKSPACE.
+ * The SPLIT form keeps 8*M*parts bytes of statistics in the workspace
+ * reserved for (current device, stream) by gemm_workspace_reserve (the one
+ * split-K uses); it splits a row only into as many parts as fit there, and
+ * with no room for two parts it runs an unsplit form.  Allocates nothing and
+ * does not wait for the GPU.
  * With pointer checks on (gemm_set_pointer_checks), X's and Y's byte ranges
  *   must each lie in one device allocation of the current device, else
  *   DTM_ERR_POINTER.
@@ -74,7 +77,8 @@ int row_softmax(int64_t M, int64_t N, const void *X, int64_t stride_xm, int64_t 
 
 /*
  * row_softmax_plan -- validate the arguments of row_softmax() and report the
- * plan it would launch, on the host, without touching a GPU.  Writes *out.
+ * plan it would launch, on the host, without touching a GPU (the SPLIT form's
+ * part count as with an unbounded workspace).  Writes *out.
  * Returns the status row_softmax() would return before launching.
  */
 int row_softmax_plan(int64_t M, int64_t N, const void *X, int64_t stride_xm, int64_t stride_xn,

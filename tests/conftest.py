@@ -45,3 +45,21 @@ def _isnum(s):
 @pytest.fixture(scope="session")
 def golden():
     return read_golden
+
+
+_reserved = False
+
+
+@pytest.fixture(autouse=True)
+def _gpu_workspace(request):
+    """Before the first GPU test: reserve library workspace for torch's
+    default stream (the library's gemm never allocates; split-K plans keep
+    their partials in a workspace reserved beforehand, and the forced splits
+    of these tests need up to a few hundred MiB)."""
+    global _reserved
+    if not _reserved and request.node.get_closest_marker("gpu") is not None:
+        import dense_tiled_matrix_amd as dtm
+
+        dtm.reserve_workspace(1 << 30)
+        _reserved = True
+    yield

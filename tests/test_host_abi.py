@@ -463,3 +463,66 @@ def test_forced_unsplit_rows():
     assert plan(1024, 512, 4096, config=dict(kernel=dtm.DTM_KERNEL_GENERIC, block_m=64,
                                              block_n=64, block_k=16, dp_rows=512))[0] == \
         dtm.DTM_ERR_CONFIG
+
+
+def test_selector_splits_only_within_the_workspace():
+    """gemm() plans within the workspace reserved for its stream; the
+    workspace_limit field shows that plan on the host.  The long-K skinny
+    case wants 16 slices (16 MiB of fp32 partials); with room for fewer it
+    takes the largest split that fits, and with room for none it runs
+    unsplit (S up to the cap: the selector's rule takes the cap itself when
+    the largest power of two below it is under 3/4 of it).  A forced split
+    is not capped."""
+    big = dict(A=1 << 40, B=2 << 40, C=3 << 40, ind=F16, outd=F32)
+    slice_bytes = 512 * 512 * 4
+    for limit, S in [(0, 16), (16 * slice_bytes, 16), (16 * slice_bytes - 1, 15),
+                     (9 * slice_bytes, 8), (8 * slice_bytes, 8), (3 * slice_bytes, 3),
+                     (2 * slice_bytes, 2), (2 * slice_bytes - 1, 1), (1, 1)]:
+        st, p = plan(512, 512, 65536, config=dict(workspace_limit=limit), **big)
+        assert st == 0 and p["split_k"] == S, (limit, p)
+        assert p["workspace_bytes"] == (S * slice_bytes if S > 1 else 0), (limit, p)
+        assert limit == 0 or p["workspace_bytes"] <= limit
+    # the split of the last tile-rows (S x rows x N x 4 bytes) likewise
+    st, p = plan(7168, 7168, 7168, A=1 << 40, B=2 << 40, C=3 << 40, ind=BF16, outd=BF16)
+    assert (p["split_k"], p["dp_rows"]) == (5, 6912), p
+    row_bytes = (7168 - 6912) * 7168 * 4
+    st, p = plan(7168, 7168, 7168, A=1 << 40, B=2 << 40, C=3 << 40, ind=BF16, outd=BF16,
+                 config=dict(workspace_limit=3 * row_bytes))
+    assert st == 0 and p["split_k"] <= 3 and p["workspace_bytes"] <= 3 * row_bytes, p
+    st, p = plan(7168, 7168, 7168, A=1 << 40, B=2 << 40, C=3 << 40, ind=BF16, outd=BF16,
+                 config=dict(workspace_limit=row_bytes))
+    assert st == 0 and p["split_k"] == 1 and p["dp_rows"] == 0 and p["workspace_bytes"] == 0, p
+    # a forced split reports what it needs, whatever the limit
+    cfg = dict(kernel=dtm.DTM_KERNEL_MFMA_F16, block_m=128, block_n=128, block_k=32, split_k=4,
+               workspace_limit=1)
+    st, p = plan(512, 512, 65536, config=cfg, **big)
+    assert st == 0 and p["split_k"] == 4 and p["workspace_bytes"] == 4 * slice_bytes
+
+
+def test_softmax_plan_split_form_within_budget():
+    """row_softmax_plan reports the split form's part count with room for it;
+    the host logic that caps it to the stream's workspace is what gemm uses
+    (the same lease); here only the unbounded plan is visible."""
+    st, p = dtm.row_softmax_plan_raw(64, 262144, PA, 262144, 1, PC, 262144, 1, BF16, BF16)
+    assert st == 0 and p["form_name"] == "split" and p["parts"] >= 2, p
+
+
+def test_tensor_binding_rejects_host_and_mixed_devices():
+    """dtm.gemm / gemm_ex / row_softmax raise ValueError, before any library
+    call, for host tensors or tensors on different devices: a host pointer
+    handed to a kernel would fault the GPU rather than fail."""
+    import torch
+
+    a = torch.zeros(64, 32, dtype=torch.float16)
+    b = torch.zeros(32, 48, dtype=torch.float16)
+    with pytest.raises(ValueError, match="CUDA"):
+        dtm.gemm(a, b)
+    with pytest.raises(ValueError, match="CUDA"):
+        dtm.gemm_ex(a, b, config=dict(kernel=dtm.DTM_KERNEL_GENERIC))
+    with pytest.raises(ValueError, match="CUDA"):
+        dtm.row_softmax(a)
+    meta_a = torch.empty(64, 32, dtype=torch.float16, device="meta")
+    with pytest.raises(ValueError, match="different devices"):
+        dtm.gemm(meta_a, b, out=torch.empty(64, 48))
+    with pytest.raises(ValueError, match="different devices"):
+        dtm.row_softmax(a, out=torch.empty(64, 32, dtype=torch.float16, device="meta"))
