@@ -132,3 +132,34 @@ def compare(p, cbits, out_dtype=None, exact=False, c64=None, cout=None, label=""
     assert over.size == 0, f"{label}: {len(over)} elements over tolerance; max err {worst} " \
                            f"tol {tol}; first at {over[:3].tolist()}"
     return worst, tol
+
+
+def _abs_operand(op):
+    """The operand with every element's sign bit cleared (|x|, exactly)."""
+    import workloads as W
+
+    mask = 0x7FFFFFFF if op.dtype == "f32" else 0x7FFF
+    bits = (np.asarray(op.bits).astype(np.uint64) & mask).astype(op.bits.dtype)
+    return W.Operand(bits, op.dtype, op.rows, op.cols, op.offset, op.stride_r, op.stride_c)
+
+
+def higham_ratio(p, cbits, c64, out_dtype=None):
+    """max over C of |C - C64| / (gamma_K * (|A||B|)_ij + half an output ulp
+    of C64), gamma_K = K u' / (1 - K u') with u' = 2 * 2^-24: the worst-case
+    error of any order of K fp32 additions of the products (the textbook
+    bound, with twice the fp32 unit roundoff as headroom for the matrix
+    cores' internal adds).  At most 1 for fp32 accumulation; inputs rounded
+    below fp32 precision on the way in would exceed it."""
+    import workloads as W
+
+    od = out_dtype or p.out_dtype
+    absp = W.Problem(p.M, p.N, p.K, _abs_operand(p.A), _abs_operand(p.B), p.in_dtype, od)
+    ab64, _ = oracle.gemm_problem(absp)
+    u = 2.0 * 2.0 ** -24
+    gamma = p.K * u / (1 - p.K * u)
+    bound = gamma * ab64 + (half_ulp(c64, od) if od != "f32" else 0.0)
+    got = oracle.decode(cbits, od)
+    err = np.abs(got - c64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(err == 0, 0.0, err / bound)
+    return float(r.max()) if r.size else 0.0
