@@ -157,16 +157,26 @@ def softmax_problem(p, out_dtype=None, threads: int = 0):
                    out_dtype or p.out_dtype, threads)
 
 
-def softmax_tolerance(x64_row_minus_max: np.ndarray, y64: np.ndarray, terms: int) -> np.ndarray:
-    """Per-element bound for a row softmax computed in fp32 from the same
-    inputs: the shifted argument d = x - max is rounded once and scaled by
-    log2(e) once (together about 2 |d| 2^-24 in the exponent), the base-2
-    exponential adds a few ulps, the sum of the row's exponentials adds at
-    most ``terms`` roundings (the longest chain of fp32 additions any one
-    partial sum passes through), and the reciprocal of the sum and the
-    product with it one each; exponentials below 2^-126 may flush to zero
-    (an absolute 2^-126 before the division by a sum >= 1).  Returns
-    |Y - Y64| bounds, elementwise."""
+def softmax_tolerance(x64_row_minus_max: np.ndarray, y64: np.ndarray, n: int) -> np.ndarray:
+    """Per-element bound on |Y - Y64| for a row softmax of row length ``n``
+    computed in fp32 (unit roundoff u = 2^-24) from the same inputs, fixed
+    in advance from the formula alone, whatever the order of the sum:
+
+    * the shifted argument d = x - max rounded once and scaled by log2(e)
+      once: a relative error of at most 2|d|u in exp(d);
+    * the exponential itself: 4u (a few ulps);
+    * the sum of the row's n exponentials, with any rescaling of partial
+      sums by exp(m_old - m_new) and the argument errors of the other terms:
+      bounded probabilistically (Higham & Mary, "A new approach to
+      probabilistic rounding error analysis", 2019: rounding errors behave
+      as independent, mean-zero, so n of them grow as sqrt(n), not n) by
+      lambda * sqrt(4n) u with lambda = 8 (a failure probability below
+      1e-13 per element under that model);
+    * the reciprocal of the sum and the product with it: 2u;
+    * exponentials below 2^-126 may flush to zero: an absolute 2^-125
+      (the sum is at least 1, the maximum's own term).
+
+    Returns the bounds elementwise: |Y64| * (2|d| + 6 + 16 sqrt(n)) u + 2^-125."""
     d = np.abs(np.nan_to_num(x64_row_minus_max, nan=0.0, neginf=0.0))
-    rel = (2 * d + terms + 10) * 2.0 ** -24
+    rel = (2.0 * d + 6.0 + 16.0 * np.sqrt(float(max(n, 1)))) * 2.0 ** -24
     return np.abs(y64) * rel + 2.0 ** -125
