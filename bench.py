@@ -30,7 +30,9 @@ METRIC = "GEMM TFLOP/s and % of MFMA peak at fp16/bf16 4096³ and 8192³ on 1 MI
 # MI355X dense MFMA peaks (TFLOP/s): 256 CUs x 2.4 GHz x FLOP/clk/CU
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
-HOST_THREADS_CAP = 16  # host threads for the CPU baseline: the host-core share of one GPU
+# host threads for the CPU baseline: the host cores one GPU's job may use on a
+# shared multi-GPU host (more cores are visible than are this job's to take)
+HOST_THREADS_CAP = 16
 # sources of the kernels whose traffic profiles/traffic.json records (the
 # pipelined MFMA GEMM, the split-K reduce, the row softmax)
 KERNEL_SOURCES = ["dense_tiled_matrix_amd/csrc/gemm_mfma16_dma.hip",
@@ -170,7 +172,9 @@ def cpu_baseline(p, target_s: float):
     flops = 2.0 * R * p.N * p.K
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"first {R} of {p.M} rows of A times all of B ({p.K}x{p.N}), "
-                      f"{t:.1f} s wall incl. decoding the operands to fp64"}
+                      f"{t:.1f} s wall incl. decoding the operands to fp64; {threads} threads "
+                      f"(the host-core share of one GPU; "
+                      f"{len(os.sched_getaffinity(0))} visible)"}
 
 
 def sustained_clocks(torch, fn, seconds=0.8, batch=20):
@@ -251,6 +255,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=100,
                     help="untimed calls before each timed run (the chip's power management "
                          "settles about 50 calls into a sustained bf16 8192^3 run)")
+    ap.add_argument("--headline-warmup-s", type=float, default=1.0,
+                    help="the headline workload is warmed for at least this many seconds of "
+                         "back-to-back calls as well as --warmup calls, so that its timed "
+                         "steps run after the power-management transient of a new load")
     ap.add_argument("--extra-warmup-s", type=float, default=0.3,
                     help="the workloads besides the headline are warmed for at least this "
                          "many seconds of back-to-back calls as well as --warmup calls")
@@ -282,6 +290,10 @@ def main():
     import dense_tiled_matrix_amd as dtm
     import workloads as W
 
+    # gemm() never allocates: the split-K plans (the long-K workload) keep
+    # their partials in workspace reserved here, before anything is timed
+    dtm.reserve_workspace()
+
     TD = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
     if args.calibrate_copy_mib:
@@ -309,7 +321,8 @@ def main():
         flops = 2.0 * p.M * p.N * p.K
         return p, plan, wall_ms, kern_ms, flops, (med_ms, min_ms)
 
-    p, plan, wall_ms, kern_ms, flops, (med_ms, min_ms) = measure(args.workload, sustain=True)
+    p, plan, wall_ms, kern_ms, flops, (med_ms, min_ms) = measure(
+        args.workload, sustain=True, min_warm_s=args.headline_warmup_s)
     peak = PEAK_TFLOPS[p.in_dtype]
     achieved = flops / (kern_ms * 1e-3) / 1e12
     line = {
