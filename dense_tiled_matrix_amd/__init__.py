@@ -28,7 +28,7 @@ DTM_F32, DTM_F16, DTM_BF16 = 0, 1, 2
 STATUS = {
     0: "DTM_OK", 1: "DTM_ERR_INVALID_DIM", 2: "DTM_ERR_NULL_POINTER", 3: "DTM_ERR_DTYPE",
     4: "DTM_ERR_STRIDE", 5: "DTM_ERR_ALIAS", 6: "DTM_ERR_CONFIG", 7: "DTM_ERR_WORKSPACE",
-    8: "DTM_ERR_DEVICE", 9: "DTM_ERR_LAUNCH", 10: "DTM_ERR_POINTER",
+    8: "DTM_ERR_DEVICE", 9: "DTM_ERR_LAUNCH", 10: "DTM_ERR_POINTER", 11: "DTM_ERR_SCRATCH",
 }
 globals().update({v: k for k, v in STATUS.items()})
 # dtm_kernel
@@ -116,6 +116,10 @@ def lib():
         L.gemm_kernel_name.restype = ctypes.c_char_p
         L.gemm_set_pointer_checks.argtypes = [i32]
         L.gemm_set_pointer_checks.restype = i32
+        L.gemm_ex_noalloc.argtypes = ops + [ctypes.POINTER(TileConfig), vp]
+        L.gemm_ex_noalloc.restype = i32
+        L.gemm_noalloc_scratch_bytes.argtypes = []
+        L.gemm_noalloc_scratch_bytes.restype = u64
         L.gemm_mfma_probe.argtypes = [i32, i32, i32, vp, vp, vp, vp]
         L.gemm_mfma_probe.restype = i32
         L.gemm_workspace_reserve.argtypes = [u64, vp]
@@ -370,6 +374,32 @@ def gemm_ex_raw(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C, st
     return lib().gemm_ex(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C, stride_cm,
                          stride_cn, in_dtype, out_dtype, _config(config), workspace or None,
                          workspace_bytes, s)
+
+
+def gemm_ex_noalloc(a, b, out=None, out_dtype=None, config=None, stream=None):
+    """``gemm_ex`` without any workspace argument or reservation, through the
+    C ``gemm_ex_noalloc``: split-K partials go to the library's fixed device
+    array (``gemm_noalloc_scratch_bytes()`` bytes).  Calls that overlap on one
+    GPU race on that array."""
+    M, N, K, out = _operands(a, b, out, out_dtype)
+    dev = _device_of(a, b, out)
+    st = _on_device(dev, lambda: lib().gemm_ex_noalloc(*_args(a, b, out, M, N, K),
+                                                       _config(config), _stream(dev, stream)))
+    if st != DTM_OK:
+        raise GemmError(st, "gemm_ex_noalloc")
+    return out
+
+
+def gemm_ex_noalloc_raw(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C, stride_cm,
+                        stride_cn, in_dtype, out_dtype, config=None, stream=None):
+    """``gemm_ex_noalloc`` on raw integers (device pointers); returns the status."""
+    s = ctypes.c_void_p(0 if stream is None else int(stream))
+    return lib().gemm_ex_noalloc(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C,
+                                 stride_cm, stride_cn, in_dtype, out_dtype, _config(config), s)
+
+
+def gemm_noalloc_scratch_bytes() -> int:
+    return int(lib().gemm_noalloc_scratch_bytes())
 
 
 # ---------------------------------------------------------------- row softmax

@@ -623,8 +623,10 @@ uint64_t call_budget(const dtm_tile_config *force, uint64_t available)
     return available < limit ? available : limit;
 }
 
+// library_ws: `workspace` is memory of the library's own (the pointer
+// checks leave it out).
 int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t workspace_bytes,
-        void *stream)
+        void *stream, bool library_ws = false)
 {
     // Without a caller's workspace, the one reserved for this stream (if
     // any) bounds the plan; the lease is held until every launch of this
@@ -644,7 +646,7 @@ int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t w
     if (st != DTM_OK)
         return st;
     if (dtm::pointer_checks_on()) {
-        st = check_pointers(c, p, workspace);
+        st = check_pointers(c, p, library_ws ? nullptr : workspace);
         if (st != DTM_OK)
             return st;
     }
@@ -675,6 +677,19 @@ int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t w
 }
 
 }  // namespace
+
+namespace dtm {
+
+int gemm_ex_library_ws(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam, int64_t sak,
+                       const void *B, int64_t sbk, int64_t sbn, void *C, int64_t scm, int64_t scn,
+                       int in_dtype, int out_dtype, const dtm_tile_config *force, void *ws,
+                       uint64_t ws_bytes, void *stream)
+{
+    const Call c{M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, in_dtype, out_dtype};
+    return run(c, force, ws, ws_bytes, stream, true);
+}
+
+}  // namespace dtm
 
 extern "C" {
 
@@ -726,6 +741,9 @@ const char *gemm_status_string(int status)
     case DTM_ERR_LAUNCH: return "kernel launch failed";
     case DTM_ERR_POINTER:
         return "pointer check: a view is not inside one device allocation of the current device";
+    case DTM_ERR_SCRATCH:
+        return "the plan needs more scratch than gemm_ex_noalloc's fixed device array holds "
+               "(use gemm_ex with a workspace, or a smaller split)";
     }
     return "unknown status";
 }

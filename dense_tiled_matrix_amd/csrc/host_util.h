@@ -98,4 +98,11 @@ int workspace_reserve(void *stream, uint64_t bytes);
 int workspace_release(void *stream);
 uint64_t workspace_reserved(void *stream);
 
+// gemm_ex with `ws` (ws_bytes) as its workspace, memory the library owns
+// (left out of the pointer checks).
+int gemm_ex_library_ws(int64_t M, int64_t N, int64_t K, const void *A, int64_t sam, int64_t sak,
+                       const void *B, int64_t sbk, int64_t sbn, void *C, int64_t scm, int64_t scn,
+                       int in_dtype, int out_dtype, const dtm_tile_config *force, void *ws,
+                       uint64_t ws_bytes, void *stream);
+
 }  // namespace dtm

@@ -78,9 +78,11 @@ typedef enum {
                                  gemm_workspace_reserve could not allocate */
     DTM_ERR_DEVICE = 8,       /* the current device is not gfx950 or cannot be queried */
     DTM_ERR_LAUNCH = 9,       /* the HIP runtime reported an error when launching */
-    DTM_ERR_POINTER = 10      /* pointer checks on (gemm_set_pointer_checks): a view's
+    DTM_ERR_POINTER = 10,     /* pointer checks on (gemm_set_pointer_checks): a view's
                                  byte range is not inside one device-memory allocation of
                                  the current device */
+    DTM_ERR_SCRATCH = 11      /* gemm_ex_noalloc: the plan needs more split-K scratch than
+                                 its fixed array holds (gemm_noalloc_scratch_bytes) */
 } dtm_status;
 
 /* Kernels a plan can name. */
@@ -241,6 +243,33 @@ int gemm_workspace_release(void *stream);
 /* gemm_workspace_reserved -- bytes reserved for (current device, stream);
  * 0 when none. */
 uint64_t gemm_workspace_reserved(void *stream);
+
+/*
+ * gemm_ex_noalloc -- gemm_ex() for callers that cannot allocate device
+ * memory at all, not even once beforehand with gemm_workspace_reserve: code
+ * recorded under stream capture, serving loops and hosts that forbid
+ * allocation.  The same arguments as gemm_ex() without the workspace: a plan
+ * that splits K keeps its fp32 partials in a fixed array of device memory
+ * that is part of the library (gemm_noalloc_scratch_bytes() bytes, 32 MiB;
+ * each GPU the library runs on holds its own copy until the process ends).
+ * The selector splits only as far as the partials fit in it; a forced
+ * split_k that needs more returns DTM_ERR_SCRATCH before anything is
+ * launched.  The first call on a device looks up that device's copy of the
+ * array (no allocation); no call allocates, frees or waits for the GPU.
+ * Every call on a GPU uses that GPU's one array: calls that overlap on one
+ * GPU (other streams, other threads) race on it and must be serialised by
+ * the caller.  Results equal gemm_ex()'s with the same plan.  Returns a
+ * dtm_status.
+ */
+int gemm_ex_noalloc(int64_t M, int64_t N, int64_t K,
+                    const void *A, int64_t stride_am, int64_t stride_ak,
+                    const void *B, int64_t stride_bk, int64_t stride_bn,
+                    void *C, int64_t stride_cm, int64_t stride_cn,
+                    int in_dtype, int out_dtype,
+                    const dtm_tile_config *force, void *stream);
+
+/* gemm_noalloc_scratch_bytes -- the size of gemm_ex_noalloc's fixed array. */
+uint64_t gemm_noalloc_scratch_bytes(void);
 
 /* gemm_status_string -- a static, NUL-terminated description of a status.
  * Every check runs before anything is launched, so a bad call fails on the
