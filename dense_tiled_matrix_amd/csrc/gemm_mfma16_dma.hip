@@ -36,7 +36,8 @@
 //    no VGPRs stage them.  Four LDS stages: a chunk is loaded three to four
 //    chunks of MFMA time before it is read.  One barrier per chunk, after a
 //    wait for exactly the loads of the chunk about to be read; the loads are
-//    spread evenly between the MFMAs.
+//    spread evenly between the MFMAs.  The paired-stage form (below) loads
+//    with buffer_load_dwordx4 ... lds from a scalar base per chunk pair.
 //  * Both MFMA operands want, in lane l, 8 consecutive k (k-group l/16) of
 //    row/column l % 16.  An operand that is K-contiguous in memory is staged
 //    as TILE rows of 64 bytes; the 16-byte chunk c of row r sits at
@@ -539,6 +540,11 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
 #define DTM_PAIR_DMA_SPAN 8
 #endif
 
+// Byte extent of the raw buffer each paired-stage load addresses: one chunk
+// pair of one operand's tile, from the tile's origin (TILE rows of a
+// K-contiguous operand, 64 k-rows of an M/N-contiguous one).
+constexpr uint32_t PAIR_SPAN_MAX = 0x80000000u;
+
 // Swizzle of the 128-byte rows of the paired stages: 16-byte unit u of row r
 // sits at u ^ ((r >> 1) & 7).  Measured with an in-bounds probe of the
 // fragment read order (lane l: row l % 16, unit 4h + l / 16 for either 32-k
@@ -613,39 +619,47 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_pair_kernel(GemmArgs 
     const int64_t m0 = pid_m * BM, n0 = pid_n * BN;
     const int64_t kb = slice * k_split;
 
-    // Sources of this lane's loads for region-pair j = 0 (chunks 0 and 1);
-    // pair j is 64 * j elements further along K.
-    auto pair_src = [&](const uint16_t *X, bool kc, int64_t mn0, int64_t s_mn, int64_t s_k,
-                        int seg) __attribute__((always_inline)) {
+    // Loads are raw-buffer loads into LDS: the resource's base is the tile's
+    // origin in the operand, advanced by one chunk pair per refill on the
+    // scalar unit, and each lane's byte offset within a pair is fixed, so a
+    // load needs no vector address arithmetic (measured against 64-bit
+    // per-lane addresses: bf16 8192^3 NN +2%, NT +2%, fp16 4096^3 +2-4%).
+    // This lane's element offset, from the origin, for load `seg` of a pair:
+    auto pair_elem = [&](bool kc, int64_t s_mn, int64_t s_k, int seg) __attribute__((always_inline)) {
         if (kc) {
             const int r = 8 * seg + (lane >> 3);
             const int u = (lane & 7) ^ swz_row128(r);
-            return X + (mn0 + r) * s_mn + kb + 8 * u;
+            return static_cast<int64_t>(r) * s_mn + 8 * u;
         }
         const int g = 64 * seg + lane, kp = g / LPR;
         const int c = krow_logical<TILE>(g % LPR, kp % BK);
-        return X + (kb + kp) * s_k + mn0 + 8 * c;
+        return static_cast<int64_t>(kp) * s_k + 8 * c;
     };
-    const uint16_t *A = static_cast<const uint16_t *>(p.A);
-    const uint16_t *B = static_cast<const uint16_t *>(p.B);
-    const uint16_t *a_src[SEGS], *b_src[SEGS];
+    const uint16_t *a_org =
+        static_cast<const uint16_t *>(p.A) + (A_KC ? m0 * p.sam + kb : kb * p.sak + m0);
+    const uint16_t *b_org =
+        static_cast<const uint16_t *>(p.B) + (B_KC ? n0 * p.sbn + kb : kb * p.sbk + n0);
+    uint32_t a_voff[SEGS], b_voff[SEGS];
 #pragma unroll
     for (int d = 0; d < SEGS; ++d) {
-        a_src[d] = pair_src(A, A_KC, m0, p.sam, p.sak, SEGS * wave + d);
-        b_src[d] = pair_src(B, B_KC, n0, p.sbn, p.sbk, SEGS * wave + d);
+        a_voff[d] = static_cast<uint32_t>(2 * pair_elem(A_KC, p.sam, p.sak, SEGS * wave + d));
+        b_voff[d] = static_cast<uint32_t>(2 * pair_elem(B_KC, p.sbn, p.sbk, SEGS * wave + d));
     }
     const int64_t a_pair = A_KC ? 2 * BK : 2 * BK * p.sak;
     const int64_t b_pair = B_KC ? 2 * BK : 2 * BK * p.sbk;
     const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, lds)));
     const uint32_t a_dst0 = lds_base + (SEGS * wave) * 1024;
     const uint32_t b_dst0 = lds_base + OPB + (SEGS * wave) * 1024;
-    // load d of the refill of region `reg` with chunk pair j
+    // load d of the refill of region `reg` with chunk pair j (every offset is
+    // below PAIR_SPAN_MAX bytes: mfma16_dma_pair_span_ok)
     auto dma_one = [&](int64_t j, int reg, int d) __attribute__((always_inline)) {
         const uint32_t ro = static_cast<uint32_t>(reg) * REGION;
         if (d < SEGS)
-            dma16(a_src[d] + j * a_pair, a_dst0 + ro + 1024 * d);
+            dma16_buf(buffer_rsrc(a_org + j * a_pair, PAIR_SPAN_MAX), a_voff[d],
+                      a_dst0 + ro + 1024 * d);
         else
-            dma16(b_src[d - SEGS] + j * b_pair, b_dst0 + ro + 1024 * (d - SEGS));
+            dma16_buf(buffer_rsrc(b_org + j * b_pair, PAIR_SPAN_MAX), b_voff[d - SEGS],
+                      b_dst0 + ro + 1024 * (d - SEGS));
     };
 
     // Fragment offsets within a region for the first 32-k half.  The second
@@ -828,6 +842,19 @@ struct DmaLaunch {
     int waves;  // see waves_ok
 };
 
+// Whether every paired-stage load offset, from its tile's origin, stays
+// below PAIR_SPAN_MAX bytes: a K-contiguous operand spans TILE rows of its
+// leading dimension, an M/N-contiguous one 64 k-rows (plus one tile width).
+bool pair_span_ok(const GemmArgs &a, int tile, bool ta, bool tb)
+{
+    const uint64_t lim = PAIR_SPAN_MAX;
+    const uint64_t a_span = !ta ? (uint64_t)tile * (uint64_t)a.sam * 2 + 256
+                                : 64ull * (uint64_t)a.sak * 2 + (uint64_t)tile * 2;
+    const uint64_t b_span = tb ? (uint64_t)tile * (uint64_t)a.sbn * 2 + 256
+                               : 64ull * (uint64_t)a.sbk * 2 + (uint64_t)tile * 2;
+    return a.sam >= 0 && a.sak >= 0 && a.sbk >= 0 && a.sbn >= 0 && a_span < lim && b_span < lim;
+}
+
 // K elements per slice: K / splits for the interior form; for the RAGGED
 // form cdiv(K, splits) rounded up to a whole number of chunks.
 int64_t slice_k(int64_t K, int64_t splits, bool ragged)
@@ -849,7 +876,8 @@ hipError_t launch_one(const GemmArgs &a, const DmaLaunch &l, hipStream_t s)
             hipLaunchKernelGGL((gemm_mfma16_dma_kernel<IN, OUT, TILE, NWAVES, TA, TB, true>),
                                grid, block, 0, s, a, gm, gn, l.splits, ks, a.M * a.N,
                                l.a_bytes, l.b_bytes);
-    } else if (TILE != 128 && DTM_DMA_PAIRS && (ks / BK) % 2 == 0) {
+    } else if (TILE != 128 && DTM_DMA_PAIRS && (ks / BK) % 2 == 0 &&
+               pair_span_ok(a, TILE, TA, TB)) {
         // paired stages pay on the 256- and 192-wide tiles (measured: 0.1-2%
         // faster on square bf16 shapes); on the 128-wide tile, whose grids are
         // small or split along K, they were 13-20% slower than the 4-stage form
