@@ -34,8 +34,9 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 # shared multi-GPU host (more cores are visible than are this job's to take)
 HOST_THREADS_CAP = 16
 # sources of the kernels whose traffic profiles/traffic.json records (the
-# pipelined MFMA GEMM, the split-K reduce, the row softmax)
+# pipelined MFMA GEMM, the fp32 MFMA GEMM, the split-K reduce, the row softmax)
 KERNEL_SOURCES = ["dense_tiled_matrix_amd/csrc/gemm_mfma16_dma.hip",
+                  "dense_tiled_matrix_amd/csrc/gemm_mfma32.hip",
                   "dense_tiled_matrix_amd/csrc/gemm_splitk.hip",
                   "dense_tiled_matrix_amd/csrc/softmax.hip",
                   "dense_tiled_matrix_amd/csrc/device.h"]
@@ -68,6 +69,14 @@ def measured_traffic(workload: str):
     if not w or rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return w.get("hbm_bytes_per_launch")
+
+
+ELEM_BYTES = {"f16": 2, "bf16": 2, "f32": 4}
+
+
+def algorithmic_bytes(p) -> int:
+    """Bytes a GEMM must move at the least: A and B read once, C written once."""
+    return (p.M * p.K + p.K * p.N) * ELEM_BYTES[p.in_dtype] + p.M * p.N * ELEM_BYTES[p.out_dtype]
 
 
 def to_device(op, torch_dtype, torch):
@@ -263,7 +272,8 @@ def main():
                     help="the workloads besides the headline are warmed for at least this "
                          "many seconds of back-to-back calls as well as --warmup calls")
     ap.add_argument("--workload", default="bf16_8192_bf16out")
-    ap.add_argument("--secondary", default="f16_4096_f32out,f16_8192_f32out,bf16_4096_bf16out",
+    ap.add_argument("--secondary",
+                    default="f16_4096_f32out,f16_8192_f32out,bf16_4096_bf16out,f32_4096_f32out",
                     help="comma-separated workloads also timed (not the headline)")
     ap.add_argument("--softmax", default=",".join([
         "softmax_f32_4096x4096", "softmax_bf16_8192x8192_masked", "softmax_f16_32768x1024",
@@ -359,7 +369,8 @@ def main():
                           "tflops_kernel": round(qa, 2), "frac": round(qa / PEAK_TFLOPS[q.in_dtype], 4),
                           "kernel_ms": round(qkern, 4), "kernel_ms_median": round(qmed, 4),
                           "tile": [qplan["block_m"], qplan["block_n"], qplan["block_k"]],
-                          "threads": qplan["threads"]})
+                          "threads": qplan["threads"], "traffic": measured_traffic(q.name),
+                          "algorithmic_bytes": algorithmic_bytes(q)})
     if secondary:
         line["secondary"] = secondary
     # read (not written) between cold calls, so the caches hold clean lines
@@ -374,8 +385,7 @@ def main():
         stream = torch.cuda.current_stream()
         cold_ms = time_cold(torch, lambda: dtm.gemm(a, b, out=c, stream=stream),
                             min(args.steps, 20), flush)
-        # algorithmic bytes: A and B read once, C written once
-        alg = (q.M * q.K + q.K * q.N) * a.element_size() + q.M * q.N * c.element_size()
+        alg = algorithmic_bytes(q)
         qflops = 2.0 * q.M * q.N * q.K
         line["skinny"] = {"workload": q.name, "split_k": qplan["split_k"],
                           "warm_us": round(warm_ms * 1e3, 2), "cold_us": round(cold_ms * 1e3, 2),

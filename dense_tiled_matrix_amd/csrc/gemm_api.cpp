@@ -365,6 +365,22 @@ int64_t pick_split(const Call &c, int layout, int64_t tiles, int tile, int64_t c
     return 1;
 }
 
+// fp32 on the matrix cores: 256 x 256 tiles (one workgroup per CU) when
+// their round fill, times their measured rate against 128 x 128 tiles (three
+// workgroups per CU; 4096^3 134 against 121 TFLOP/s), beats the 128-wide
+// tiles' fill: 4096^3 and 8192^3 take 256, 3000^3 (144 tiles of 256 for 256
+// CUs) stays on 128.
+constexpr double F32_RATE_256 = 1.11;
+
+bool prefer_f32_256(const Call &c)
+{
+    const int64_t t256 = cdiv(c.M, 256) * cdiv(c.N, 256), t128 = cdiv(c.M, 128) * cdiv(c.N, 128);
+    const double fill256 = static_cast<double>(t256) / static_cast<double>(cdiv(t256, CUS) * CUS);
+    const double fill128 =
+        static_cast<double>(t128) / static_cast<double>(cdiv(t128, 3 * CUS) * 3 * CUS);
+    return F32_RATE_256 * fill256 > fill128;
+}
+
 // The pipelined kernel's interior form at tile 256 runs with 4 waves of
 // 128 x 128 (one per SIMD) when each tile's K loop is at least this long,
 // else with 8 waves of 128 x 64 (two per SIMD, which cover each other's
@@ -490,7 +506,7 @@ int make_plan(const Call &c, const dtm_tile_config *force, uint64_t ws_budget, d
             return DTM_ERR_CONFIG;
         if (forced_dims && !dtm::mfma32_has_config(force->block_m, force->block_n, force->block_k))
             return DTM_ERR_CONFIG;
-        p.block_m = p.block_n = 128;
+        p.block_m = p.block_n = forced_dims ? force->block_m : (prefer_f32_256(c) ? 256 : 128);
         p.block_k = 16;
         p.threads = 256;
         p.layout = layout;

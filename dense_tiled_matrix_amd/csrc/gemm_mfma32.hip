@@ -10,7 +10,10 @@
 // gfx950 design:
 //  * 256 threads = 4 wave64s in 2 x 2; each wave owns (BM/2) x (BN/2) of C
 //    as 32 x 32 tiles of v_mfma_f32_32x32x2_f32 (one fp32 of A and one of B
-//    per lane per instruction, 16 fp32 results per lane).
+//    per lane per instruction, 16 fp32 results per lane).  Tiles of 128 x 128
+//    (64 x 64 per wave, three workgroups per CU) or 256 x 256 (128 x 128 per
+//    wave in the accumulation registers, one workgroup per CU, half the LDS
+//    reads per MFMA: 4096^3 121 -> 134 TFLOP/s, 8192^3 126 -> 132).
 //  * 16-deep K-chunks, two LDS stages, loaded through registers one chunk
 //    ahead.  A K-contiguous operand (A row-major, or B given as the
 //    transpose of an N x K array) goes to LDS as it is; an M- or
@@ -234,35 +237,42 @@ hipError_t launch_tile(const GemmArgs &a, bool ragged, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int OUT>
+template <int OUT, int T>
 hipError_t dispatch_layout(const GemmArgs &a, int layout, bool ragged, hipStream_t s)
 {
     switch (layout) {
-    case 0: return launch_tile<OUT, 128, 128, false, false>(a, ragged, s);
-    case DTM_LAYOUT_A_M_CONTIG: return launch_tile<OUT, 128, 128, true, false>(a, ragged, s);
-    case DTM_LAYOUT_B_K_CONTIG: return launch_tile<OUT, 128, 128, false, true>(a, ragged, s);
+    case 0: return launch_tile<OUT, T, T, false, false>(a, ragged, s);
+    case DTM_LAYOUT_A_M_CONTIG: return launch_tile<OUT, T, T, true, false>(a, ragged, s);
+    case DTM_LAYOUT_B_K_CONTIG: return launch_tile<OUT, T, T, false, true>(a, ragged, s);
     case DTM_LAYOUT_A_M_CONTIG | DTM_LAYOUT_B_K_CONTIG:
-        return launch_tile<OUT, 128, 128, true, true>(a, ragged, s);
+        return launch_tile<OUT, T, T, true, true>(a, ragged, s);
     }
     return hipErrorInvalidValue;
+}
+
+template <int OUT>
+hipError_t dispatch_tile(const GemmArgs &a, int tile, int layout, bool ragged, hipStream_t s)
+{
+    return tile == 256 ? dispatch_layout<OUT, 256>(a, layout, ragged, s)
+                       : dispatch_layout<OUT, 128>(a, layout, ragged, s);
 }
 
 }  // namespace
 
 bool mfma32_has_config(int bm, int bn, int bk)
 {
-    return bk == BK && bm == 128 && bn == 128;
+    return bk == BK && bm == bn && (bm == 128 || bm == 256);
 }
 
 hipError_t launch_mfma32(const GemmArgs &a, int out, int bm, int bn, int bk, int layout,
                          bool ragged, hipStream_t s)
 {
-    if (bk != BK || bm != 128 || bn != 128)
+    if (!mfma32_has_config(bm, bn, bk))
         return hipErrorInvalidConfiguration;
     switch (out) {
-    case DTM_F32: return dispatch_layout<DTM_F32>(a, layout, ragged, s);
-    case DTM_F16: return dispatch_layout<DTM_F16>(a, layout, ragged, s);
-    case DTM_BF16: return dispatch_layout<DTM_BF16>(a, layout, ragged, s);
+    case DTM_F32: return dispatch_tile<DTM_F32>(a, bm, layout, ragged, s);
+    case DTM_F16: return dispatch_tile<DTM_F16>(a, bm, layout, ragged, s);
+    case DTM_BF16: return dispatch_tile<DTM_BF16>(a, bm, layout, ragged, s);
     }
     return hipErrorInvalidValue;
 }

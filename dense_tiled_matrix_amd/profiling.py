@@ -5,6 +5,7 @@
     python -m dense_tiled_matrix_amd.profiling pmc    <counter_collection.csv> [...]
     python -m dense_tiled_matrix_amd.profiling traffic --fetch F.csv --write W.csv \
         --copy-mib 512 --workload NAME --kernel-substr S --source-hash H
+    python -m dense_tiled_matrix_amd.profiling resources [--match S] <file.s> [...]
 
 ``stats`` prints the per-kernel table of a ``--kernel-trace --stats`` run;
 ``trace`` prints the same from its kernel_trace.csv per kernel and launch
@@ -15,7 +16,9 @@ shader clock derived from GRBM_GUI_ACTIVE, which counts shader-clock cycles
 per XCD, over the dispatch's own duration); ``traffic`` turns a FETCH_SIZE
 run and a WRITE_SIZE run into HBM bytes per launch, each scaled by what the
 same counter reads for a plain device copy of known size run in the same
-command.
+command; ``resources`` tabulates, from the AMD assembly the compiler writes
+for this library's own sources (``hipcc ... --cuda-device-only -S``), each
+kernel's VGPR, AGPR, SGPR, LDS and scratch (spill) use and occupancy.
 """
 from __future__ import annotations
 
@@ -78,20 +81,22 @@ def _dispatches(paths):
     for path in paths:
         for r in csv.DictReader(open(path)):
             key = (path, r["Dispatch_Id"])
-            rec = d.setdefault(key, {"name": r["Kernel_Name"]})
+            rec = d.setdefault(key, {"name": r["Kernel_Name"], "grid": int(r["Grid_Size"])})
             rec[r["Counter_Name"]] = float(r["Counter_Value"])
             rec["dur_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     return list(d.values())
 
 
 def pmc(paths) -> str:
+    # one kernel instantiation can serve several workloads: the grid size
+    # tells their dispatches apart
     per = collections.OrderedDict()
     for rec in _dispatches(paths):
-        per.setdefault(_short(rec["name"]), []).append(rec)
+        per.setdefault((_short(rec["name"]), rec["grid"]), []).append(rec)
     out = []
-    for name, recs in per.items():
-        out.append(f"### `{name}` ({len(recs)} dispatch records)")
-        keys = sorted({k for r in recs for k in r if k not in ("name", "dur_ns")})
+    for (name, grid), recs in per.items():
+        out.append(f"### `{name}`, grid {grid} threads ({len(recs)} dispatch records)")
+        keys = sorted({k for r in recs for k in r if k not in ("name", "dur_ns", "grid")})
         for k in keys:
             vals = [r[k] for r in recs if k in r]
             out.append(f"- {k}: mean {sum(vals) / len(vals):.6g} (n={len(vals)})")
@@ -109,14 +114,35 @@ def pmc(paths) -> str:
         if conf:
             out.append(f"- LDS bank-conflict cycles / LDS active cycles: "
                        f"{100 * sum(conf) / len(conf):.2f}%")
+        wait = [r["SQ_WAIT_ANY"] / r["SQ_WAVE_CYCLES"] for r in recs if r.get("SQ_WAVE_CYCLES")]
+        if wait:
+            out.append(f"- SQ_WAIT_ANY / SQ_WAVE_CYCLES: {100 * sum(wait) / len(wait):.1f}%")
+        hit = [r["TCC_HIT_sum"] / (r["TCC_HIT_sum"] + r["TCC_MISS_sum"]) for r in recs
+               if r.get("TCC_HIT_sum", 0) + r.get("TCC_MISS_sum", 0) > 0]
+        if hit:
+            out.append(f"- L2 hit rate TCC_HIT / (TCC_HIT + TCC_MISS): "
+                       f"{100 * sum(hit) / len(hit):.1f}%")
+        lat = [r["TCP_TCC_READ_REQ_LATENCY_sum"] / r["TCP_TCC_READ_REQ_sum"] for r in recs
+               if r.get("TCP_TCC_READ_REQ_sum")]
+        if lat:
+            out.append(f"- mean L1-to-L2 read latency TCP_TCC_READ_REQ_LATENCY / "
+                       f"TCP_TCC_READ_REQ: {sum(lat) / len(lat):.0f} cycles")
+        ea = [r["TCC_EA0_RDREQ_LEVEL_sum"] / r["TCC_EA0_RDREQ_sum"] for r in recs
+              if r.get("TCC_EA0_RDREQ_sum")]
+        if ea:
+            out.append(f"- mean L2-to-fabric read latency TCC_EA0_RDREQ_LEVEL / "
+                       f"TCC_EA0_RDREQ: {sum(ea) / len(ea):.0f} cycles")
     return "\n".join(out)
 
 
-def _mean_kib(path, substr, largest_only=False):
+def _mean_kib(path, substr, largest_only=False, grid=None):
     """Mean FETCH_SIZE or WRITE_SIZE of the dispatches whose name holds
-    `substr`; with largest_only, of those within half of the largest value
-    (the calibration copies, not smaller copies the same run makes)."""
-    vals = [rec for rec in _dispatches([path]) if substr in rec["name"]]
+    `substr` (and, given `grid`, whose grid has that many threads: one kernel
+    instantiation can serve several workloads); with largest_only, of those
+    within half of the largest value (the calibration copies, not smaller
+    copies the same run makes)."""
+    vals = [rec for rec in _dispatches([path]) if substr in rec["name"] and
+            (grid is None or rec.get("grid") == grid)]
     key = "FETCH_SIZE" if any("FETCH_SIZE" in r for r in vals) else "WRITE_SIZE"
     xs = [r[key] for r in vals if key in r]
     if largest_only:
@@ -124,12 +150,13 @@ def _mean_kib(path, substr, largest_only=False):
     return sum(xs) / len(xs), key
 
 
-def traffic(fetch_csv, write_csv, copy_mib, workload, kernel_substr, source_hash):
-    """HBM bytes per launch of the kernel, scaled by the copy calibration."""
+def traffic(fetch_csv, write_csv, copy_mib, specs, source_hash):
+    """Memory-fabric bytes per launch for each (workload, kernel name
+    substring, grid threads or None) in `specs`, scaled by the copy
+    calibration.  One kernel instantiation can serve several workloads of a
+    run; the grid tells their dispatches apart."""
     copy_fetch, _ = _mean_kib(fetch_csv, "copyBuffer", largest_only=True)
     copy_write, _ = _mean_kib(write_csv, "copyBuffer", largest_only=True)
-    k_fetch, _ = _mean_kib(fetch_csv, kernel_substr)
-    k_write, _ = _mean_kib(write_csv, kernel_substr)
     true_kib = copy_mib * 1024.0
     f_scale = true_kib / copy_fetch
     w_scale = true_kib / copy_write
@@ -138,13 +165,63 @@ def traffic(fetch_csv, write_csv, copy_mib, workload, kernel_substr, source_hash
         "calibration": {"copy_mib": copy_mib, "fetch_size_kib_read": copy_fetch,
                         "write_size_kib_read": copy_write, "fetch_scale": f_scale,
                         "write_scale": w_scale},
-        "workloads": {workload: {
-            "kernel": kernel_substr,
+        "workloads": {},
+    }
+    for workload, kernel_substr, grid in specs:
+        k_fetch, _ = _mean_kib(fetch_csv, kernel_substr, grid=grid)
+        k_write, _ = _mean_kib(write_csv, kernel_substr, grid=grid)
+        rec["workloads"][workload] = {
+            "kernel": kernel_substr, "grid_threads": grid,
             "fetch_size_kib": k_fetch, "write_size_kib": k_write,
             "hbm_bytes_per_launch": round((k_fetch * f_scale + k_write * w_scale) * 1024),
-        }},
-    }
+        }
     return rec
+
+
+def _spec(text):
+    """workload=kernel-substring[@grid-threads]"""
+    workload, rest = text.split("=", 1)
+    kernel, _, grid = rest.rpartition("@") if "@" in rest else (rest, "", "")
+    return workload, kernel, int(grid) if grid else None
+
+
+def _demangled(sym: str) -> str:
+    try:
+        import subprocess
+        return subprocess.run(["c++filt", sym], capture_output=True, text=True).stdout.strip()
+    except OSError:
+        return sym
+
+
+def resources(paths, match=None) -> str:
+    """One row per kernel of the assembly files: the register, LDS and
+    scratch figures the compiler reports after each kernel body."""
+    import re
+
+    rows = []
+    for path in paths:
+        text = open(path).read()
+        for m in re.finditer(r"\.amdhsa_kernel (\S+)\n(.*?)\.end_amdhsa_kernel(.*?)(?=\.amdhsa_kernel |\Z)",
+                             text, flags=re.S):
+            sym, body, tail = m.group(1), m.group(2), m.group(3)
+
+            def num(pattern, where):
+                mm = re.search(pattern, where)
+                return int(mm.group(1)) if mm else None
+
+            name = _short(_demangled(sym))
+            if match and match not in name:
+                continue
+            rows.append((name, num(r"; NumVgprs: (\d+)", tail), num(r"; NumAgprs: (\d+)", tail),
+                         num(r"; TotalNumVgprs: (\d+)", tail), num(r"; TotalNumSgprs: (\d+)", tail),
+                         num(r"\.amdhsa_group_segment_fixed_size (\d+)", body),
+                         num(r"; ScratchSize: (\d+)", tail), num(r"; Occupancy: (\d+)", tail)))
+    out = ["| kernel | VGPR | AGPR | total VGPR | SGPR | LDS (bytes) | scratch (bytes) | "
+           "waves/SIMD |", "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append("| `" + r[0] + "` | " + " | ".join("-" if v is None else str(v) for v in r[1:]) +
+                   " |")
+    return "\n".join(out)
 
 
 def main(argv=None):
@@ -160,9 +237,12 @@ def main(argv=None):
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
     t.add_argument("--copy-mib", type=float, required=True)
-    t.add_argument("--workload", required=True)
-    t.add_argument("--kernel-substr", required=True)
+    t.add_argument("--spec", type=_spec, action="append", required=True,
+                   help="workload=kernel-name-substring[@grid-threads], repeatable")
     t.add_argument("--source-hash", required=True)
+    rs = sub.add_parser("resources")
+    rs.add_argument("asm", nargs="+")
+    rs.add_argument("--match", default=None)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats(a.csv))
@@ -170,9 +250,10 @@ def main(argv=None):
         print(trace(a.csv))
     elif a.cmd == "pmc":
         print(pmc(a.csv))
+    elif a.cmd == "resources":
+        print(resources(a.asm, a.match))
     else:
-        print(json.dumps(traffic(a.fetch, a.write, a.copy_mib, a.workload, a.kernel_substr,
-                                 a.source_hash), indent=1))
+        print(json.dumps(traffic(a.fetch, a.write, a.copy_mib, a.spec, a.source_hash), indent=1))
 
 
 if __name__ == "__main__":

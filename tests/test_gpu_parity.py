@@ -229,7 +229,7 @@ def test_ragged_f32_transposed_a():
     assert untouched
 
 
-def _big_check(p, tile, threads=None):
+def _big_check(p, tile, threads=None, kernel="mfma_f16"):
     """Full-size run in the launch configuration the bench times, compared
     with the oracle on every element of C (Worked Example 13.3.1's method:
     the fp64 truth from the same rounded inputs), and the Higham ratio of
@@ -240,7 +240,7 @@ def _big_check(p, tile, threads=None):
     a = sa.view(TD[p.in_dtype]).view(p.M, p.K)
     b = sb.view(TD[p.in_dtype]).view(p.K, p.N)
     plan = dtm.gemm_plan(a, b, out_dtype=TD[p.out_dtype])
-    assert plan["kernel_name"] == "mfma_f16" and plan["block_m"] == tile, plan
+    assert plan["kernel_name"] == kernel and plan["block_m"] == tile, plan
     assert threads is None or plan["threads"] == threads, plan
     c = dtm.gemm(a, b, out_dtype=TD[p.out_dtype])
     torch.cuda.synchronize()
@@ -272,6 +272,12 @@ def test_f16_8192_f32out():
 def test_bf16_4096_bf16out():
     """Extra: bf16 4096^3 with bf16 output (one tile per CU, 4 waves)."""
     _big_check(W.workload("bf16_4096_bf16out"), 256, threads=256)
+
+
+def test_f32_4096_f32out():
+    """Extra: fp32 4096^3 on the fp32 matrix cores (256-wide tiles, one per
+    CU), compared on every element, with its Higham ratio."""
+    _big_check(W.workload("f32_4096_f32out"), 256, threads=256, kernel="mfma_f32")
 
 
 def test_f16_skinny_long_k():
@@ -704,6 +710,17 @@ def test_mfma_f32_exact_and_random(layout):
         c, untouched = run(p, config=dict(kernel=MF32), c_pad=2 if n % 2 else 0, plan=plan)
         assert plan["layout"] == LAYOUT_BITS[layout], plan
         compare(p, c, exact=True, label=f"mfma_f32 {layout} {M}x{N}x{K}->{outd}")
+        assert untouched
+    # the 256-wide tile (the selector's choice for large full rounds), forced
+    for n, (M, N, K) in enumerate([(256, 256, 16), (512, 768, 96), (257, 513, 49),
+                                   (300, 260, 1000)]):
+        outd = ["f32", "bf16", "f16"][n % 3]
+        p = _padded_f32_problem(M, N, K, outd, 640 + n, layout[0], layout[1])
+        plan = {}
+        c, untouched = run(p, config=dict(kernel=MF32, block_m=256, block_n=256, block_k=16),
+                           c_pad=2 if n % 2 else 0, plan=plan)
+        assert plan["block_m"] == 256 and plan["layout"] == LAYOUT_BITS[layout], plan
+        compare(p, c, exact=True, label=f"mfma_f32 256 {layout} {M}x{N}x{K}->{outd}")
         assert untouched
     for n, (M, N, K) in enumerate([(1024, 1024, 1024), (1000, 600, 776)]):
         p = W.random_problem(M, N, K, "f32", "f32", ("normal", 0.0, 1.0), seed=650 + n,

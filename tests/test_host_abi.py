@@ -217,6 +217,18 @@ def test_fp32_selector():
     assert st == dtm.DTM_ERR_CONFIG
     st, p = plan(1024, 1024, 1000, ind=F16, config=dict(kernel=dtm.DTM_KERNEL_MFMA_F32))
     assert st == dtm.DTM_ERR_CONFIG
+    # 256-wide tiles (one workgroup per CU) where their round fill, at 1.11x
+    # the rate, beats the 128-wide tiles' (three workgroups per CU)
+    big = dict(A=1 << 40, B=2 << 40, C=3 << 40)
+    for M, N, K, tile in [(4096, 4096, 4096, 256), (8192, 8192, 8192, 256), (3000, 3000, 3000, 128),
+                          (1024, 1024, 1024, 128), (4096, 8192, 2048, 256), (2048, 2048, 8192, 128)]:
+        st, p = plan(M, N, K, ind=F32, outd=F32, **big)
+        assert st == 0 and p["kernel_name"] == "mfma_f32" and p["block_m"] == tile, (M, N, K, p)
+        assert (p["grid_m"], p["grid_n"]) == (-(-M // tile), -(-N // tile))
+    for bm, ok in [(256, True), (128, True), (64, False)]:
+        st, p = plan(1000, 1000, 1000, ind=F32, config=dict(kernel=dtm.DTM_KERNEL_MFMA_F32,
+                                                            block_m=bm, block_n=bm, block_k=16))
+        assert (st == 0) == ok and (not ok or p["block_m"] == bm), (bm, st, p)
 
 
 def test_fp16acc_control_is_forced_only():

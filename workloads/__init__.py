@@ -151,6 +151,10 @@ WORKLOADS = {
     "bf16_4096_bf16out": dict(index=6, M=4096, N=4096, K=4096, in_dtype="bf16",
                               out_dtype="bf16", dist=("normal", 0.0, 1.0),
                               a_layout="N", b_layout="N"),
+    # fp32 inputs on the fp32 matrix cores at a size where they dominate
+    "f32_4096_f32out": dict(index=7, M=4096, N=4096, K=4096, in_dtype="f32",
+                            out_dtype="f32", dist=("normal", 0.0, 1.0),
+                            a_layout="N", b_layout="N"),
 }
 
 
