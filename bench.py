@@ -34,8 +34,11 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 # shared multi-GPU host (more cores are visible than are this job's to take)
 HOST_THREADS_CAP = 16
 # sources of the kernels whose traffic profiles/traffic.json records (the
-# pipelined MFMA GEMM, the fp32 MFMA GEMM, the split-K reduce, the row softmax)
+# pipelined and wave-K MFMA GEMMs, the fp32 MFMA GEMM, the split-K reduce, the
+# row softmax)
 KERNEL_SOURCES = ["dense_tiled_matrix_amd/csrc/gemm_mfma16_dma.hip",
+                  "dense_tiled_matrix_amd/csrc/gemm_mfma16_wavek.hip",
+                  "dense_tiled_matrix_amd/csrc/mfma16_stage.h",
                   "dense_tiled_matrix_amd/csrc/gemm_mfma32.hip",
                   "dense_tiled_matrix_amd/csrc/gemm_splitk.hip",
                   "dense_tiled_matrix_amd/csrc/softmax.hip",

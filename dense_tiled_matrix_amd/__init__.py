@@ -33,10 +33,11 @@ STATUS = {
 globals().update({v: k for k, v in STATUS.items()})
 # dtm_kernel
 KERNELS = {0: "none", 1: "zero_fill", 2: "generic", 3: "mfma_f16", 4: "mfma_f32",
-           5: "generic_fp16acc"}
+           5: "generic_fp16acc", 6: "mfma_f16_wavek"}
 DTM_KERNEL_NONE, DTM_KERNEL_ZERO_FILL, DTM_KERNEL_GENERIC = 0, 1, 2
 DTM_KERNEL_MFMA_F16, DTM_KERNEL_MFMA_F32 = 3, 4
 DTM_KERNEL_GENERIC_FP16ACC = 5  # negative control: fp16 accumulator, forced only
+DTM_KERNEL_MFMA_F16_WAVEK = 6   # 128 x 128 tiles, K loop split across the 4 waves
 DTM_LAYOUT_A_M_CONTIG, DTM_LAYOUT_B_K_CONTIG = 1, 2
 
 

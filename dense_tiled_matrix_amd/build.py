@@ -32,9 +32,11 @@ def sources():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON
+    # the .cpp host sources go through hipcc as HIP too (its default for
+    # them): give every source the gfx950 device pass, not hipcc's default arch
+    cmd = [HIPCC] + COMMON + DEVICE
     if src.endswith(".hip"):
-        cmd += DEVICE + ["-x", "hip"]
+        cmd += ["-x", "hip"]
     cmd += ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)

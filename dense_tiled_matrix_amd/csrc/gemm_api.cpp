@@ -158,6 +158,17 @@ int mfma_layout(const Call &c)
 }
 bool is16(const Call &c) { return c.in == DTM_F16 || c.in == DTM_BF16; }
 
+// Whether the wave-K kernel (128 x 128 tiles, the K loop split across the
+// workgroup's waves) runs the call with `splits` K slices.
+bool wavek_fits(const Call &c, int layout, int64_t splits)
+{
+    if (!is16(c) || layout < 0)
+        return false;
+    const GemmArgs a{c.M, c.N, c.K, c.A, c.sam, c.sak, c.B, c.sbk, c.sbn,
+                     const_cast<void *>(c.C), c.scm, c.scn};
+    return dtm::mfma16_wavek_fits(a, layout, splits);
+}
+
 // Byte extent of a view with non-negative strides (one past its last
 // element, from its origin); UINT64_MAX when a stride is negative or the
 // extent overflows.
@@ -398,6 +409,24 @@ bool prefer_f32_256(const Call &c)
 #endif
 constexpr int64_t FOUR_WAVE_MIN_K = DTM_FOUR_WAVE_MIN_K;
 
+// The wave-K kernel (128 x 128 tiles whose 4 waves split the K loop, each
+// wave holding the whole tile) takes over from the 128-wide pipelined tile
+// when each tile's K loop is long.  Measured side by side (bf16 unless
+// noted, us, wave-K against 4 waves of 64 x 64): 2048^2 x 8192 62.8 / 68.5,
+// 8192 x 1024 x 8192 127.2 / 136.1, fp16 512 x 512 x 65536 split 16 43.3 /
+// 42.8 back to back and 58.2 / 67.3 with inputs from HBM; shorter loops
+// lose: 2048^3 23.8 / 20.4, 1024 x 4096 x 4096 37.0 / 35.3, 1024^2 x 8192
+// split 4 29.3 / 27.5.
+constexpr int64_t WAVEK_MIN_K = 8192;        // unsplit: the whole K loop
+constexpr int64_t WAVEK_MIN_SLICE_K = 4096;  // split: each slice's
+
+bool prefer_wavek(const Call &c, int layout, int64_t splits)
+{
+    const int64_t k_slice = c.K / splits;
+    return wavek_fits(c, layout, splits) &&
+           k_slice >= (splits > 1 ? WAVEK_MIN_SLICE_K : WAVEK_MIN_K);
+}
+
 // The plan for a call.  ws_budget: bytes of workspace the call can use;
 // the selector splits K only as far as its partials fit in it (UINT64_MAX:
 // no limit).  A forced split is not capped; run() then checks the workspace.
@@ -501,6 +530,19 @@ int make_plan(const Call &c, const dtm_tile_config *force, uint64_t ws_budget, d
         }
         p.threads = 256;  // the pipelined kernel's is settled below
         p.layout = layout;
+    } else if (kernel == DTM_KERNEL_MFMA_F16_WAVEK) {
+        // forced only: 128 x 128 x 32 tiles, 4 waves, the forced split or none
+        const int64_t S = forced_split ? forced_split : 1;
+        if (!fast16 || !wavek_fits(c, layout, S) || force->dp_rows ||
+            (forced_dims &&
+             (force->block_m != 128 || force->block_n != 128 || force->block_k != 32)) ||
+            (force->threads && force->threads != 256))
+            return DTM_ERR_CONFIG;
+        p.block_m = p.block_n = 128;
+        p.block_k = 32;
+        p.split_k = static_cast<int32_t>(S);
+        p.threads = 256;
+        p.layout = layout;
     } else if (kernel == DTM_KERNEL_MFMA_F32) {
         if (!fast32)
             return DTM_ERR_CONFIG;
@@ -526,7 +568,14 @@ int make_plan(const Call &c, const dtm_tile_config *force, uint64_t ws_budget, d
     } else {
         return DTM_ERR_CONFIG;
     }
-    if ((forced_split || (force && force->dp_rows)) && kernel != DTM_KERNEL_MFMA_F16)
+    // the selector's own 128-wide plans: the wave-K kernel where it pays
+    if (kernel == DTM_KERNEL_MFMA_F16 && !(force && (force->kernel || force->split_k > 1 ||
+                                                     force->dp_rows || force->threads)) &&
+        !forced_dims && p.block_m == 128 && p.block_k == 32 && p.dp_rows == 0 &&
+        prefer_wavek(c, layout, p.split_k))
+        kernel = DTM_KERNEL_MFMA_F16_WAVEK;
+    if ((forced_split || (force && force->dp_rows)) && kernel != DTM_KERNEL_MFMA_F16 &&
+        kernel != DTM_KERNEL_MFMA_F16_WAVEK)
         return DTM_ERR_CONFIG;
     p.kernel = kernel;
     fill_grid(c, p);
@@ -554,8 +603,8 @@ int make_plan(const Call &c, const dtm_tile_config *force, uint64_t ws_budget, d
             const int64_t kloop = (p.dp_rows > 0 ? cdiv(c.K, p.block_k) : p.k_iters) * p.block_k;
             p.threads = !top_ragged && kloop >= FOUR_WAVE_MIN_K ? 256 : 512;
         }
-    } else if (force && force->threads) {
-        return DTM_ERR_CONFIG;  // a workgroup size is chosen for the pipelined kernel only
+    } else if (force && force->threads && kernel != DTM_KERNEL_MFMA_F16_WAVEK) {
+        return DTM_ERR_CONFIG;  // a workgroup size is chosen for the pipelined kernels only
     }
     if (p.split_k > 1)
         p.workspace_bytes = static_cast<uint64_t>(p.split_k) *
@@ -621,6 +670,16 @@ int launch_plan(const Call &c, const dtm_plan &p, void *ws, hipStream_t s)
         else
             e = dtm::launch_mfma16(a, c.in, c.out, p.block_m, p.block_n, p.block_k, p.layout,
                                    p.ragged != 0, s);
+        break;
+    case DTM_KERNEL_MFMA_F16_WAVEK:
+        if (p.split_k > 1) {
+            e = dtm::launch_mfma16_wavek_partials(a, c.in, p.layout, p.split_k,
+                                                  static_cast<float *>(ws), s);
+            if (e == hipSuccess)
+                e = dtm::launch_splitk_reduce(a, c.out, p.split_k, static_cast<float *>(ws), s);
+        } else {
+            e = dtm::launch_mfma16_wavek(a, c.in, c.out, p.layout, s);
+        }
         break;
     case DTM_KERNEL_MFMA_F32:
         e = dtm::launch_mfma32(a, c.out, p.block_m, p.block_n, p.block_k, p.layout,
@@ -773,6 +832,7 @@ const char *gemm_kernel_name(int kernel)
     case DTM_KERNEL_MFMA_F16: return "mfma_f16";
     case DTM_KERNEL_MFMA_F32: return "mfma_f32";
     case DTM_KERNEL_GENERIC_FP16ACC: return "generic_fp16acc";
+    case DTM_KERNEL_MFMA_F16_WAVEK: return "mfma_f16_wavek";
     }
     return "unknown";
 }

@@ -52,6 +52,14 @@ hipError_t launch_mfma16_dma_ragged(const GemmArgs &a, int in_dtype, int out_dty
 hipError_t launch_mfma16_dma_partials(const GemmArgs &a, int in_dtype, int layout, int64_t splits,
                                       bool ragged, uint64_t a_bytes, uint64_t b_bytes, int tile,
                                       int waves, float *ws, hipStream_t s);
+// 128 x 128 tiles whose 4 waves split the K loop (interior shapes only:
+// M, N multiples of 128, K of 128 * splits; non-negative strides within the
+// buffer-load span).  Direct: C in out_dtype; partials: fp32 ws[splits][M][N].
+bool mfma16_wavek_fits(const GemmArgs &a, int layout, int64_t splits);
+hipError_t launch_mfma16_wavek(const GemmArgs &a, int in_dtype, int out_dtype, int layout,
+                               hipStream_t s);
+hipError_t launch_mfma16_wavek_partials(const GemmArgs &a, int in_dtype, int layout,
+                                        int64_t splits, float *ws, hipStream_t s);
 // C = sum over s of ws[s] in order s = 0, 1, ..., converted once to out_dtype.
 hipError_t launch_splitk_reduce(const GemmArgs &a, int out_dtype, int64_t splits, const float *ws,
                                 hipStream_t s);

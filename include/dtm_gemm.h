@@ -34,9 +34,11 @@
  *     allocate or free device memory and never wait for the GPU: the only
  *     device memory they use beyond the caller's views is a workspace the
  *     caller passes (gemm_ex) or reserved beforehand for the stream with
- *     gemm_workspace_reserve.  Calls are thread-safe: calls on one stream
- *     that use its reserved workspace queue their launches one call at a
- *     time.
+ *     gemm_workspace_reserve.  (The HIP runtime itself loads a kernel's
+ *     code object on that kernel's first launch in the process; code that
+ *     must not see even that, such as a stream capture, runs each plan once
+ *     beforehand.)  Calls are thread-safe: calls on one stream that use its
+ *     reserved workspace queue their launches one call at a time.
  *   - Every argument check runs on the host before anything is launched; on
  *     a non-zero status nothing was launched and C is untouched.
  *   - A and B may have any strides, including zero (broadcast), negative and
@@ -92,13 +94,19 @@ typedef enum {
     DTM_KERNEL_GENERIC = 2,   /* any strides and dtypes; fp32 FMA on LDS tiles */
     DTM_KERNEL_MFMA_F16 = 3,  /* fp16/bf16 inputs on MFMA (layouts: dtm_layout) */
     DTM_KERNEL_MFMA_F32 = 4,  /* fp32 inputs on fp32 MFMA */
-    DTM_KERNEL_GENERIC_FP16ACC = 5 /* negative control, only when forced through gemm_ex and
+    DTM_KERNEL_GENERIC_FP16ACC = 5, /* negative control, only when forced through gemm_ex and
                                       gemm_plan: fp16 inputs, the generic kernel with the
                                       fp16 accumulator of "Chapter 13: The Blocked Matmul
                                       Kernel", section 13.3 -- each BLOCK_K chunk's tile
                                       product (fp32) is rounded to fp16 and added into an
                                       fp16 accumulator; not a correct GEMM, it shows the
                                       accumulation error the fp32 accumulator avoids */
+    DTM_KERNEL_MFMA_F16_WAVEK = 6 /* fp16/bf16 inputs on MFMA, 128 x 128 x 32 tiles whose 4
+                                     waves each accumulate the whole tile over every fourth
+                                     32-deep chunk of the K loop ("Chapter 13", section
+                                     13.1's K loop, split four ways inside the workgroup),
+                                     summed in LDS in a fixed order; M and N multiples of
+                                     128, K of 128 * split_k, no dp_rows */
 } dtm_kernel;
 
 /* Operand layouts the MFMA kernels read at full speed (bits of

@@ -78,9 +78,9 @@ def test_selector_measured_workloads():
     st, p = plan(4096, 4096, 4100, sam=4104, ind=F16, outd=F32)
     assert st == 0 and (p["block_m"], p["block_k"], p["ragged"]) == (256, 64, 1)
     # long-K skinny: 4 tiles of 256 x 256 -> 16 of 128 x 128, K split into
-    # 16 slices of 4096
+    # 16 slices of 4096, each tile's K loop split across its 4 waves
     st, p = plan(512, 512, 65536, ind=F16, outd=F32)
-    assert st == 0 and p["kernel_name"] == "mfma_f16" and p["split_k"] == 16
+    assert st == 0 and p["kernel_name"] == "mfma_f16_wavek" and p["split_k"] == 16
     assert (p["block_m"], p["block_k"], p["k_iters"], p["threads"]) == (128, 32, 128, 256)
     assert p["workspace_bytes"] == 16 * 512 * 512 * 4
     # few 256-wide tiles: 128-wide ones, split only with K long enough;
@@ -102,6 +102,9 @@ def test_selector_measured_workloads():
             assert p["threads"] == 256, (M, N, K, p)
         assert p["ragged"] == (1 if (M % tile or N % tile) else 0), (M, N, K, p)
         assert p["dp_rows"] == 0, (M, N, K, p)
+        # 128-wide interior tiles with a K loop of 8192 or more: wave-K
+        wk = tile == 128 and not p["ragged"] and K // S >= 8192
+        assert p["kernel_name"] == ("mfma_f16_wavek" if wk else "mfma_f16"), (M, N, K, p)
     # 256-wide tiles that leave the last round part-empty: the top tile-rows
     # in whole rounds unsplit, the rest with K split so that tiles x S nearly
     # fills one round (partials: S x rows below x N x 4 bytes)
@@ -128,6 +131,9 @@ def test_selector_measured_workloads():
         st, p = plan(M, N, K, A=1 << 40, B=2 << 40, C=3 << 40, ind=F16, outd=F32)
         assert st == 0 and (p["block_m"], p["split_k"], p["ragged"]) == (128, S, ragged), \
             (M, N, K, p)
+        # split K slices of 4096 or more on interior tiles: wave-K
+        wk = not ragged and K // S >= 4096 and K % (128 * S) == 0
+        assert p["kernel_name"] == ("mfma_f16_wavek" if wk else "mfma_f16"), (M, N, K, p)
     # enough tiles: no split
     st, p = plan(4096, 4096, 65536, A=1 << 40, B=2 << 40, C=3 << 40, ind=F16, outd=F32)
     assert st == 0 and p["split_k"] == 1 and p["workspace_bytes"] == 0
@@ -538,3 +544,37 @@ def test_tensor_binding_rejects_host_and_mixed_devices():
         dtm.gemm(meta_a, b, out=torch.empty(64, 48))
     with pytest.raises(ValueError, match="different devices"):
         dtm.row_softmax(a, out=torch.empty(64, 32, dtype=torch.float16, device="meta"))
+
+
+def test_forced_wave_k_kernel():
+    """The wave-K kernel (128 x 128 x 32 tiles whose 4 waves split the K
+    loop) is planned when forced on an interior shape: M and N multiples of
+    128, K of 128 * split_k, fp16/bf16 inputs; anything else is refused."""
+    wk = dtm.DTM_KERNEL_MFMA_F16_WAVEK
+    assert dtm.gemm_kernel_name(wk) == "mfma_f16_wavek"
+    st, p = plan(512, 384, 1024, config=dict(kernel=wk))
+    assert st == 0 and p["kernel"] == wk and (p["block_m"], p["block_n"], p["block_k"]) == \
+        (128, 128, 32)
+    assert (p["grid_m"], p["grid_n"], p["split_k"], p["threads"], p["k_iters"]) == \
+        (4, 3, 1, 256, 32)
+    assert p["workspace_bytes"] == 0 and p["ragged"] == 0
+    st, p = plan(512, 512, 65536, config=dict(kernel=wk, split_k=16))
+    assert st == 0 and p["split_k"] == 16 and p["workspace_bytes"] == 16 * 512 * 512 * 4
+    assert p["k_iters"] == 128
+    # every layout
+    assert plan(256, 256, 256, sam=1, sak=256, config=dict(kernel=wk))[0] == 0
+    assert plan(256, 256, 256, sbk=1, sbn=256, config=dict(kernel=wk))[0] == 0
+    # explicit tile and workgroup size: only the ones it has
+    assert plan(256, 256, 256, config=dict(kernel=wk, block_m=128, block_n=128, block_k=32,
+                                           threads=256))[0] == 0
+    for bad in (dict(block_m=256, block_n=256, block_k=32), dict(threads=512)):
+        assert plan(256, 256, 256, config=dict(kernel=wk, **bad))[0] == dtm.DTM_ERR_CONFIG
+    # shapes it does not run: ragged M or N, K not a whole number of
+    # 128-deep regions per slice, fp32 inputs, unsplit top rows
+    err = dtm.DTM_ERR_CONFIG
+    assert plan(200, 256, 256, config=dict(kernel=wk))[0] == err
+    assert plan(256, 136, 256, config=dict(kernel=wk))[0] == err
+    assert plan(256, 256, 96, config=dict(kernel=wk))[0] == err
+    assert plan(256, 256, 1024, config=dict(kernel=wk, split_k=16))[0] == err
+    assert plan(256, 256, 256, ind=F32, config=dict(kernel=wk))[0] == err
+    assert plan(512, 256, 1024, config=dict(kernel=wk, split_k=2, dp_rows=256))[0] == err
