@@ -158,6 +158,31 @@ int mfma_layout(const Call &c)
 }
 bool is16(const Call &c) { return c.in == DTM_F16 || c.in == DTM_BF16; }
 
+// The fp32 matrix-core kernel also reads each operand along its unit-stride
+// axis, but its range-checked form takes views off 16-byte boundaries too
+// (element loads), so any fp32 view with a unit stride along one axis of
+// each operand runs there.  *aligned: mfma_layout's 16-byte rule holds as
+// well (the vector-load forms).  Returns the dtm_layout bits, or -1.
+int mfma32_layout(const Call &c, bool *aligned)
+{
+    int layout = 0;
+    if (c.sak == 1)
+        ;
+    else if (c.sam == 1)
+        layout |= DTM_LAYOUT_A_M_CONTIG;
+    else
+        return -1;
+    if (c.sbn == 1)
+        ;
+    else if (c.sbk == 1)
+        layout |= DTM_LAYOUT_B_K_CONTIG;
+    else
+        return -1;
+    if (aligned)
+        *aligned = mfma_layout(c) == layout;
+    return layout;
+}
+
 // Whether the wave-K kernel (128 x 128 tiles, the K loop split across the
 // workgroup's waves) runs the call with `splits` K slices.
 bool wavek_fits(const Call &c, int layout, int64_t splits)
@@ -450,7 +475,8 @@ int make_plan(const Call &c, const dtm_tile_config *force, uint64_t ws_budget, d
     const int layout = mfma_layout(c);
     const bool dma = c.K > 0 && dma_any(c, layout, 1);  // the pipelined kernel, either form
     const bool fast16 = is16(c) && layout >= 0;
-    const bool fast32 = c.in == DTM_F32 && layout >= 0;
+    const int layout32 = c.in == DTM_F32 ? mfma32_layout(c, nullptr) : -1;
+    const bool fast32 = layout32 >= 0;
     p.fast_path = fast16 || fast32 ? 1 : 0;
     if (c.K == 0) {
         p.kernel = DTM_KERNEL_ZERO_FILL;
@@ -551,7 +577,7 @@ int make_plan(const Call &c, const dtm_tile_config *force, uint64_t ws_budget, d
         p.block_m = p.block_n = forced_dims ? force->block_m : (prefer_f32_256(c) ? 256 : 128);
         p.block_k = 16;
         p.threads = 256;
-        p.layout = layout;
+        p.layout = layout32;
     } else if (kernel == DTM_KERNEL_GENERIC || kernel == DTM_KERNEL_GENERIC_FP16ACC) {
         if (kernel == DTM_KERNEL_GENERIC_FP16ACC && c.in != DTM_F16)
             return DTM_ERR_CONFIG;
@@ -681,10 +707,13 @@ int launch_plan(const Call &c, const dtm_plan &p, void *ws, hipStream_t s)
             e = dtm::launch_mfma16_wavek(a, c.in, c.out, p.layout, s);
         }
         break;
-    case DTM_KERNEL_MFMA_F32:
+    case DTM_KERNEL_MFMA_F32: {
+        bool aligned = false;
+        mfma32_layout(c, &aligned);
         e = dtm::launch_mfma32(a, c.out, p.block_m, p.block_n, p.block_k, p.layout,
-                               p.ragged != 0, s);
+                               p.ragged != 0, aligned, s);
         break;
+    }
     default: return DTM_ERR_CONFIG;
     }
     return e == hipSuccess ? DTM_OK : DTM_ERR_LAUNCH;

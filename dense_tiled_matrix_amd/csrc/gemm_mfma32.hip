@@ -24,7 +24,10 @@
 //  * Which k a lane feeds at each MFMA step is a fixed permutation shared by
 //    A and B: lane half h at step s = 4t + e uses k = 8t + 4h + e, so one
 //    16-byte LDS read serves four steps.  The sum over k is unchanged.
-//  * The RAGGED instantiation zero-fills every slot outside the views.
+//  * The RAGGED instantiation zero-fills every slot outside the views.  Its
+//    unaligned twin (AL = false) serves views whose base or leading
+//    dimension is off a 16-byte boundary, with element loads: any fp32 view
+//    with a unit stride along one axis runs on the matrix cores.
 #include "launch.h"
 
 namespace dtm {
@@ -39,10 +42,12 @@ constexpr int ROW_F = BK + 4;  // floats per LDS row (64 data bytes + 16 pad)
 constexpr int64_t GROUP_M = 4;
 
 // 4 consecutive floats at p[0..3]; positions >= valid are zero, valid <= 0
-// reads nothing.
+// reads nothing.  AL: p is 16-byte aligned (one vector load when all four
+// are valid); otherwise element loads.
+template <bool AL = true>
 __device__ __forceinline__ f32x4 load4_masked(const float *p, int64_t valid)
 {
-    if (valid >= 4)
+    if (AL && valid >= 4)
         return *reinterpret_cast<const f32x4 *>(p);
     f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -61,8 +66,10 @@ __device__ __forceinline__ f32x4 load4_masked(const float *p, int64_t valid)
 //  kk = 2 (b % (BK/2)), at rows 4 (b / (BK/2)) .. +3 (k-pair fastest:
 //  conflict-free LDS writes, and each load instruction reads 8 k-rows x 128
 //  contiguous bytes).
-// RAGGED: slots outside the view are exact zeros and are never read.
-template <int R, bool KC, bool RAGGED>
+// RAGGED: slots outside the view are exact zeros and are never read.  AL:
+// every 4-float unit starts on a 16-byte boundary (else element loads; only
+// with RAGGED).
+template <int R, bool KC, bool RAGGED, bool AL>
 __device__ __forceinline__ void load_operand(f32x4 (&r)[R / 64], const float *X, int64_t mn0,
                                              int64_t s_mn, int64_t s_k, int64_t ext,
                                              int64_t K, int64_t k0, int t)
@@ -75,7 +82,7 @@ __device__ __forceinline__ void load_operand(f32x4 (&r)[R / 64], const float *X,
             const int64_t mn = mn0 + row + 64 * i;
             const float *src = X + mn * s_mn + k0 + 4 * c;
             if constexpr (RAGGED)
-                r[i] = load4_masked(src, mn < ext ? K - (k0 + 4 * c) : 0);
+                r[i] = load4_masked<AL>(src, mn < ext ? K - (k0 + 4 * c) : 0);
             else
                 r[i] = *reinterpret_cast<const f32x4 *>(src);
         }
@@ -89,7 +96,7 @@ __device__ __forceinline__ void load_operand(f32x4 (&r)[R / 64], const float *X,
                 const int64_t k = k0 + kk + e;
                 const float *src = X + k * s_k + mn0 + 4 * cc;
                 if constexpr (RAGGED)
-                    r[2 * q + e] = load4_masked(src, k < K ? ext - (mn0 + 4 * cc) : 0);
+                    r[2 * q + e] = load4_masked<AL>(src, k < K ? ext - (mn0 + 4 * cc) : 0);
                 else
                     r[2 * q + e] = *reinterpret_cast<const f32x4 *>(src);
             }
@@ -123,10 +130,11 @@ __device__ __forceinline__ void store_operand(const f32x4 (&r)[R / 64], float *s
 
 // TA: A is M-contiguous (stride_am == 1), else K-contiguous.
 // TB: B is K-contiguous (stride_bk == 1), else N-contiguous.
-template <int OUT, int BM, int BN, bool RAGGED, bool TA, bool TB>
+template <int OUT, int BM, int BN, bool RAGGED, bool TA, bool TB, bool AL = true>
 __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t grid_m,
                                                           int64_t grid_n)
 {
+    static_assert(AL || RAGGED, "unaligned operands take the range-checked form");
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int MI = WM / 32, NI = WN / 32;
     constexpr int A_F = BM * ROW_F;                 // floats of one A stage
@@ -149,8 +157,8 @@ __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t gr
     f32x4 rb[BN / 64];
 
     auto load_tile = [&](int64_t k0) __attribute__((always_inline)) {
-        load_operand<BM, !TA, RAGGED>(ra, A, m0, p.sam, p.sak, p.M, p.K, k0, t);
-        load_operand<BN, TB, RAGGED>(rb, B, n0, p.sbn, p.sbk, p.N, p.K, k0, t);
+        load_operand<BM, !TA, RAGGED, AL>(ra, A, m0, p.sam, p.sak, p.M, p.K, k0, t);
+        load_operand<BN, TB, RAGGED, AL>(rb, B, n0, p.sbn, p.sbk, p.N, p.K, k0, t);
     };
     auto store_tile = [&](int stage) __attribute__((always_inline)) {
         float *sa = lds + stage * STAGE_F;
@@ -222,13 +230,16 @@ __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t gr
 }
 
 template <int OUT, int BM, int BN, bool TA, bool TB>
-hipError_t launch_tile(const GemmArgs &a, bool ragged, hipStream_t s)
+hipError_t launch_tile(const GemmArgs &a, bool ragged, bool aligned, hipStream_t s)
 {
     const int64_t gm = cdiv(a.M, BM), gn = cdiv(a.N, BN);
     const int64_t tiles = gm * gn;
     if (tiles > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
-    if (ragged)
+    if (!aligned)
+        hipLaunchKernelGGL((gemm_mfma32_kernel<OUT, BM, BN, true, TA, TB, false>),
+                           dim3((unsigned)tiles), dim3(256), 0, s, a, gm, gn);
+    else if (ragged)
         hipLaunchKernelGGL((gemm_mfma32_kernel<OUT, BM, BN, true, TA, TB>), dim3((unsigned)tiles),
                            dim3(256), 0, s, a, gm, gn);
     else
@@ -238,23 +249,25 @@ hipError_t launch_tile(const GemmArgs &a, bool ragged, hipStream_t s)
 }
 
 template <int OUT, int T>
-hipError_t dispatch_layout(const GemmArgs &a, int layout, bool ragged, hipStream_t s)
+hipError_t dispatch_layout(const GemmArgs &a, int layout, bool ragged, bool aligned,
+                           hipStream_t s)
 {
     switch (layout) {
-    case 0: return launch_tile<OUT, T, T, false, false>(a, ragged, s);
-    case DTM_LAYOUT_A_M_CONTIG: return launch_tile<OUT, T, T, true, false>(a, ragged, s);
-    case DTM_LAYOUT_B_K_CONTIG: return launch_tile<OUT, T, T, false, true>(a, ragged, s);
+    case 0: return launch_tile<OUT, T, T, false, false>(a, ragged, aligned, s);
+    case DTM_LAYOUT_A_M_CONTIG: return launch_tile<OUT, T, T, true, false>(a, ragged, aligned, s);
+    case DTM_LAYOUT_B_K_CONTIG: return launch_tile<OUT, T, T, false, true>(a, ragged, aligned, s);
     case DTM_LAYOUT_A_M_CONTIG | DTM_LAYOUT_B_K_CONTIG:
-        return launch_tile<OUT, T, T, true, true>(a, ragged, s);
+        return launch_tile<OUT, T, T, true, true>(a, ragged, aligned, s);
     }
     return hipErrorInvalidValue;
 }
 
 template <int OUT>
-hipError_t dispatch_tile(const GemmArgs &a, int tile, int layout, bool ragged, hipStream_t s)
+hipError_t dispatch_tile(const GemmArgs &a, int tile, int layout, bool ragged, bool aligned,
+                         hipStream_t s)
 {
-    return tile == 256 ? dispatch_layout<OUT, 256>(a, layout, ragged, s)
-                       : dispatch_layout<OUT, 128>(a, layout, ragged, s);
+    return tile == 256 ? dispatch_layout<OUT, 256>(a, layout, ragged, aligned, s)
+                       : dispatch_layout<OUT, 128>(a, layout, ragged, aligned, s);
 }
 
 }  // namespace
@@ -265,14 +278,14 @@ bool mfma32_has_config(int bm, int bn, int bk)
 }
 
 hipError_t launch_mfma32(const GemmArgs &a, int out, int bm, int bn, int bk, int layout,
-                         bool ragged, hipStream_t s)
+                         bool ragged, bool aligned, hipStream_t s)
 {
     if (!mfma32_has_config(bm, bn, bk))
         return hipErrorInvalidConfiguration;
     switch (out) {
-    case DTM_F32: return dispatch_tile<DTM_F32>(a, bm, layout, ragged, s);
-    case DTM_F16: return dispatch_tile<DTM_F16>(a, bm, layout, ragged, s);
-    case DTM_BF16: return dispatch_tile<DTM_BF16>(a, bm, layout, ragged, s);
+    case DTM_F32: return dispatch_tile<DTM_F32>(a, bm, layout, ragged, aligned, s);
+    case DTM_F16: return dispatch_tile<DTM_F16>(a, bm, layout, ragged, aligned, s);
+    case DTM_BF16: return dispatch_tile<DTM_BF16>(a, bm, layout, ragged, aligned, s);
     }
     return hipErrorInvalidValue;
 }

@@ -66,8 +66,10 @@ hipError_t launch_splitk_reduce(const GemmArgs &a, int out_dtype, int64_t splits
 
 // MFMA kernel for fp32 inputs in every operand layout (128 x 128 x 16 tiles).
 bool mfma32_has_config(int bm, int bn, int bk);
+// aligned: both operands' bases and leading dimensions on 16-byte
+// boundaries; otherwise the range-checked form with element loads.
 hipError_t launch_mfma32(const GemmArgs &a, int out_dtype, int bm, int bn, int bk, int layout,
-                         bool ragged, hipStream_t s);
+                         bool ragged, bool aligned, hipStream_t s);
 
 // One MFMA of the pipelined kernels on a 16 x 32 A and a 32 x 16 B, through
 // their LDS staging, fragment reads and epilogue lane map (layout: dtm_layout

@@ -93,7 +93,7 @@ typedef enum {
     DTM_KERNEL_ZERO_FILL = 1, /* K == 0: write zeros to C */
     DTM_KERNEL_GENERIC = 2,   /* any strides and dtypes; fp32 FMA on LDS tiles */
     DTM_KERNEL_MFMA_F16 = 3,  /* fp16/bf16 inputs on MFMA (layouts: dtm_layout) */
-    DTM_KERNEL_MFMA_F32 = 4,  /* fp32 inputs on fp32 MFMA */
+    DTM_KERNEL_MFMA_F32 = 4,  /* fp32 inputs on fp32 MFMA (one unit stride per operand) */
     DTM_KERNEL_GENERIC_FP16ACC = 5, /* negative control, only when forced through gemm_ex and
                                       gemm_plan: fp16 inputs, the generic kernel with the
                                       fp16 accumulator of "Chapter 13: The Blocked Matmul
@@ -110,11 +110,13 @@ typedef enum {
 } dtm_kernel;
 
 /* Operand layouts the MFMA kernels read at full speed (bits of
- * dtm_plan.layout).  Each operand must have one unit stride; its other
- * stride (the leading dimension) a multiple of 16 bytes and its base 16-byte
- * aligned.  With neither bit set, A is K-contiguous (stride_ak == 1) and B is
- * N-contiguous (stride_bn == 1): both row-major.  A transposed view sets a
- * bit.  Any other layout runs on the generic kernel. */
+ * dtm_plan.layout).  Each operand must have one unit stride; for fp16/bf16
+ * its other stride (the leading dimension) must be a multiple of 16 bytes and
+ * its base 16-byte aligned (fp32 views off those boundaries run on the fp32
+ * kernel's range-checked form with element loads).  With neither bit set, A
+ * is K-contiguous (stride_ak == 1) and B is N-contiguous (stride_bn == 1):
+ * both row-major.  A transposed view sets a bit.  Any other layout runs on
+ * the generic kernel. */
 typedef enum {
     DTM_LAYOUT_A_M_CONTIG = 1, /* A has stride_am == 1 (e.g. the transpose of a K x M array) */
     DTM_LAYOUT_B_K_CONTIG = 2  /* B has stride_bk == 1 (e.g. the transpose of an N x K array) */
@@ -148,7 +150,10 @@ typedef struct {
     int64_t k_iters;          /* K-loop trip count of one tile: cdiv(K_slice, block_k) */
     int32_t split_k;          /* K slices (1 = the whole K in one accumulator) */
     int32_t threads;          /* threads per workgroup */
-    int32_t fast_path;        /* 1 when the MFMA layout and alignment predicate holds */
+    int32_t fast_path;        /* 1 when a matrix-core kernel's layout predicate holds:
+                                 fp16/bf16 one unit stride per operand on 16-byte
+                                 boundaries (dtm_layout); fp32 one unit stride per
+                                 operand, any alignment */
     int32_t ragged;           /* 1 when M, N or K is not a multiple of its block */
     int32_t layout;           /* dtm_layout bits of the operands (MFMA kernels; 0 otherwise) */
     uint64_t workspace_bytes; /* device scratch the plan needs (split-K partials) */

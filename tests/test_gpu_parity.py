@@ -696,6 +696,52 @@ def _padded_f32_problem(M, N, K, outd, seed, a_layout, b_layout):
                      name=f"f32{a_layout}{b_layout}{M}x{N}x{K}")
 
 
+def _unaligned_f32_problem(M, N, K, outd, seed, a_layout, b_layout, ld_extra, offset):
+    """As _padded_f32_problem, but leading dimensions of cols + ld_extra
+    elements (off 16-byte boundaries for ld_extra % 4 != 0) and each view
+    starting `offset` elements into its NaN-filled buffer."""
+    rng = np.random.default_rng(seed)
+    a = rng.integers(-16, 17, size=(M, K))
+    b = rng.integers(-16, 17, size=(K, N))
+
+    def store(x, layout):
+        rows, cols = x.shape
+        if layout == "T":
+            x = x.T
+        ld = x.shape[1] + ld_extra
+        buf = np.full(offset + x.shape[0] * ld + 8, np.nan)
+        view = buf[offset:offset + x.shape[0] * ld].reshape(x.shape[0], ld)
+        view[:, :x.shape[1]] = x
+        strides = (ld, 1) if layout == "N" else (1, ld)
+        return W.Operand(W.to_bits(buf, "f32"), "f32", rows, cols, offset, *strides)
+
+    return W.Problem(M, N, K, store(a, a_layout), store(b, b_layout), "f32", outd,
+                     name=f"f32u{a_layout}{b_layout}{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])
+def test_mfma_f32_unaligned_exact(layout):
+    """fp32 views off 16-byte boundaries (leading dimensions of cols + 1 or
+    + 3 elements, views starting 1 or 3 elements into their buffers) on the
+    fp32 matrix cores' range-checked form with element loads, both tile
+    sizes: value-exact on integer-valued inputs, nothing outside the views
+    read (NaN padding)."""
+    MF32 = dtm.DTM_KERNEL_MFMA_F32
+    cases = [(128, 128, 16, 1, 0), (257, 129, 193, 1, 1), (300, 260, 1000, 3, 3),
+             (64, 500, 77, 2, 1), (512, 256, 96, 1, 2)]
+    for n, (M, N, K, extra, off) in enumerate(cases):
+        outd = ["f32", "f16", "bf16"][n % 3]
+        p = _unaligned_f32_problem(M, N, K, outd, 660 + n, layout[0], layout[1], extra, off)
+        for tile in (128, 256):
+            plan = {}
+            c, untouched = run(p, config=dict(kernel=MF32, block_m=tile, block_n=tile, block_k=16),
+                               c_pad=2 if n % 2 else 0, plan=plan)
+            assert plan["status"] == 0 and plan["layout"] == LAYOUT_BITS[layout], plan
+            compare(p, c, exact=True,
+                    label=f"mfma_f32 unaligned {tile} {layout} {M}x{N}x{K}+{extra}@{off}->{outd}")
+            assert untouched
+
+
 @pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])
 def test_mfma_f32_exact_and_random(layout):
     """fp32 inputs on the fp32 matrix cores in each operand layout:

@@ -137,9 +137,11 @@ def test_selector_measured_workloads():
     # enough tiles: no split
     st, p = plan(4096, 4096, 65536, A=1 << 40, B=2 << 40, C=3 << 40, ind=F16, outd=F32)
     assert st == 0 and p["split_k"] == 1 and p["workspace_bytes"] == 0
-    # fp32 with a transposed A view: the generic strided kernel
+    # fp32 with a transposed A view whose leading dimension (257 floats) is
+    # off a 16-byte boundary: the fp32 matrix cores' range-checked form
     st, p = plan(257, 129, 193, sam=1, sak=257, ind=F32, outd=F32)
-    assert st == 0 and p["kernel_name"] == "generic" and p["fast_path"] == 0 and p["ragged"] == 1
+    assert st == 0 and p["kernel_name"] == "mfma_f32" and p["fast_path"] == 1 and p["ragged"] == 1
+    assert p["layout"] == dtm.DTM_LAYOUT_A_M_CONTIG
 
 
 @pytest.mark.parametrize("kw,why", [
@@ -194,13 +196,16 @@ def test_selector_transposed_layouts():
     # ... unless K % 8 != 0: then the register-staged kernel
     st, p = plan(256, 256, 60, sam=64, sbk=1, sbn=64, ind=F16, outd=F32)
     assert st == 0 and p["layout"] == LB and p["block_k"] == 64 and p["block_m"] == 128
-    # other stride not a 16-byte multiple: the generic kernel
+    # other stride not a 16-byte multiple: fp16/bf16 on the generic kernel,
+    # fp32 on the fp32 matrix cores' range-checked form (element loads)
     for M, N, K, kw, ind in [(4096, 4096, 4096, dict(sam=1, sak=4100), F16),
-                             (4096, 4096, 4096, dict(sbk=1, sbn=4092), BF16),
-                             (257, 129, 193, dict(sam=1, sak=257), F32),
-                             (1024, 1024, 1024, dict(sbk=1, sbn=1026), F32)]:
+                             (4096, 4096, 4096, dict(sbk=1, sbn=4092), BF16)]:
         st, p = plan(M, N, K, ind=ind, **big, **kw)
         assert st == 0 and p["kernel_name"] == "generic" and p["layout"] == 0, (M, N, K, kw)
+    for M, N, K, kw, bits in [(257, 129, 193, dict(sam=1, sak=257), LA),
+                              (1024, 1024, 1024, dict(sbk=1, sbn=1026), LB)]:
+        st, p = plan(M, N, K, ind=F32, **big, **kw)
+        assert st == 0 and p["kernel_name"] == "mfma_f32" and p["layout"] == bits, (M, N, K, kw)
     # forced tiles accept every layout
     for cfg in [dict(block_m=256, block_n=256, block_k=64), dict(block_m=128, block_n=128,
                                                                  block_k=64),
@@ -211,14 +216,19 @@ def test_selector_transposed_layouts():
 
 
 def test_fp32_selector():
-    """fp32 with K-contiguous A and N-contiguous B on 16-byte boundaries runs
-    on the fp32 matrix cores; other fp32 layouts on the generic kernel."""
+    """fp32 with a unit stride along one axis of each operand runs on the
+    fp32 matrix cores, on or off 16-byte boundaries; views with no unit
+    stride on the generic kernel."""
     st, p = plan(1024, 1024, 1000, ind=F32, sam=1000)
     assert st == 0 and p["kernel_name"] == "mfma_f32" and p["fast_path"] == 1
     assert (p["block_m"], p["block_n"], p["block_k"], p["ragged"]) == (128, 128, 16, 1)
-    for kw in [dict(sam=1001), dict(sak=2), dict(A=PA + 4), dict(sbk=1002)]:
+    for kw in [dict(sam=1001), dict(A=PA + 4), dict(sbk=1002), dict(B=PB + 8),
+               dict(sam=1, sak=1001), dict(sbk=1, sbn=1003)]:
         st, p = plan(1024, 1024, 1000, ind=F32, **kw)
-        assert st == 0 and p["kernel_name"] == "generic", kw
+        assert st == 0 and p["kernel_name"] == "mfma_f32" and p["fast_path"] == 1, kw
+    for kw in [dict(sak=2), dict(sbn=3), dict(sam=2, sak=2048)]:
+        st, p = plan(1024, 1024, 1000, ind=F32, **kw)
+        assert st == 0 and p["kernel_name"] == "generic" and p["fast_path"] == 0, kw
     st, p = plan(1024, 1024, 1000, ind=F32, config=dict(kernel=dtm.DTM_KERNEL_MFMA_F16))
     assert st == dtm.DTM_ERR_CONFIG
     st, p = plan(1024, 1024, 1000, ind=F16, config=dict(kernel=dtm.DTM_KERNEL_MFMA_F32))
