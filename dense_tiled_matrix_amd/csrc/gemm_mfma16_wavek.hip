@@ -36,11 +36,11 @@ namespace {
 // region r + 2 spread over iteration r: long-K 512 x 512 x 65536 5% slower
 // warm, 18% slower cold).  K slices are whole regions (128 k).
 //
-// The sum of the four wave tiles: a reduce-scatter through LDS in a fixed
-// pairing, (w0 + w2) + (w1 + w3) for every element: round 1 pairs waves
-// w and w ^ 2 over halves of the tile's rows, round 2 waves w and w ^ 1 over
-// quarters; each wave stores its quarter.  fp32 addition is commutative, so
-// which wave of a pair adds does not change a bit.
+// The sum of the four wave tiles goes through LDS in two passes of half the
+// tile's rows each: every wave writes its blocks of that half, then the two
+// waves that own a quarter of it read the four contributions back and add
+// them as (w0 + w2) + (w1 + w3), the same order for every element whichever
+// wave adds, and store their quarter.
 template <int IN, int OUT, bool TA, bool TB>
 __global__ __launch_bounds__(256) void gemm_mfma16_wavek_kernel(GemmArgs p, int64_t grid_m,
                                                                 int64_t grid_n, int64_t splits,
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256) void gemm_mfma16_wavek_kernel(GemmArgs p, int6
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
     // The sum of the four wave tiles, through LDS (1 KiB per 16 x 16 block
-    // of one wave: lane l's 4 values at 16 l), in two rounds of half the
+    // of one wave: lane l's 4 values at 16 l), in two passes of half the
     // tile's rows: every wave writes its blocks of half h, then the two
     // waves whose quarters lie in that half (wave w owns blocks i = 2 w,
     // 2 w + 1) read the four contributions back, add them as (w0 + w2) +
