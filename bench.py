@@ -7,7 +7,9 @@ on the workload's synthetic, seeded inputs, already resident in HBM.  Prints
 one JSON line: whole-job TFLOP/s over K timed steps, the dominant kernel's
 achieved TFLOP/s against the dense MFMA peak (HIP events on the stream the
 kernel runs on), and the CPU oracle timed on a bounded sample of the same
-workload on this host.  The row-softmax workloads (the second, HBM-bound
+workload on this host ("cpu_baseline"; "cpu_configs" adds the oracle's wall
+time on every GEMM workload, a row sample of the large ones, including the
+decoding of the operands to fp64, and one-thread figures for scale).  The row-softmax workloads (the second, HBM-bound
 operation) are timed the same way and reported under "softmax" in GB/s of
 algorithmic traffic (X read once, Y written once) against the 8 TB/s HBM
 peak, back to back (operands may partly stay in the 256 MB Infinity Cache)
@@ -155,38 +157,76 @@ def host_us_per_call(dtm, torch, calls=500):
     return t / calls * 1e6
 
 
-def cpu_baseline(p, target_s: float):
-    """The oracle (untuned, fp64, OpenMP over rows) on the first R rows of the
-    workload, R sized so the timed run takes about `target_s` seconds."""
+def _oracle_rows(p, target_s: float, threads: int):
+    """Time the oracle on the first R rows of problem p (all of them when the
+    whole problem fits), R sized so the timed run takes about `target_s`
+    seconds.  Returns (R, seconds)."""
     import numpy as np
 
     import oracle
     import workloads as W
 
-    threads = max(1, min(HOST_THREADS_CAP, len(os.sched_getaffinity(0))))
-    A2 = p.A.bits.reshape(p.M, p.K)
-
     def run_rows(R):
-        sub = W.Problem(R, p.N, p.K, W.dense(np.ascontiguousarray(A2[:R]), p.in_dtype), p.B,
-                        p.in_dtype, p.out_dtype)
+        if R == p.M:
+            sub = p
+        else:
+            rows = W.Operand(p.A.bits, p.A.dtype, R, p.K, p.A.offset, p.A.stride_r,
+                             p.A.stride_c)
+            sub = W.Problem(R, p.N, p.K, W.dense(np.ascontiguousarray(rows.logical_bits()),
+                                                 p.in_dtype),
+                            p.B, p.in_dtype, p.out_dtype)
         t0 = time.perf_counter()
         oracle.gemm_problem(sub, threads=threads)
         return time.perf_counter() - t0
 
     # two calibration points separate the fixed cost (decoding B) from the
     # per-row cost
-    t1 = run_rows(threads)
-    t4 = run_rows(4 * threads)
-    per_row = max((t4 - t1) / (3 * threads), 1e-6)
-    R = int((target_s - t1) / per_row) + threads
-    R = int(min(p.M, max(threads, threads * (R // threads))))
-    t = run_rows(R)
+    r1 = min(p.M, threads)
+    t1 = run_rows(r1)
+    if r1 == p.M or t1 * p.M / r1 < target_s:
+        return p.M, run_rows(p.M)
+    r4 = min(p.M, 4 * threads)
+    t4 = run_rows(r4)
+    per_row = max((t4 - t1) / max(r4 - r1, 1), 1e-7)
+    R = int((target_s - t1) / per_row) + r1
+    R = int(min(p.M, max(r1, threads * (R // threads))))
+    return R, run_rows(R)
+
+
+def host_threads() -> int:
+    return max(1, min(HOST_THREADS_CAP, len(os.sched_getaffinity(0))))
+
+
+def cpu_baseline(p, target_s: float):
+    """The oracle (untuned, fp64, OpenMP over rows) on the first R rows of the
+    workload, R sized so the timed run takes about `target_s` seconds."""
+    threads = host_threads()
+    R, t = _oracle_rows(p, target_s, threads)
     flops = 2.0 * R * p.N * p.K
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"first {R} of {p.M} rows of A times all of B ({p.K}x{p.N}), "
                       f"{t:.1f} s wall incl. decoding the operands to fp64; {threads} threads "
                       f"(the host-core share of one GPU; "
                       f"{len(os.sched_getaffinity(0))} visible)"}
+
+
+def cpu_configs(target_s: float):
+    """The oracle on every GEMM workload once (a row sample where the whole
+    problem would take longer than `target_s`), on the host-core share and,
+    for the 257 x 129 x 193 and 4096^3 workloads, on one thread for scale."""
+    import workloads as W
+
+    out = []
+    threads = host_threads()
+    for name, nthreads in [("int8x8x8_f32", threads), ("ragged257x129x193_f32_At", threads),
+                           ("ragged257x129x193_f32_At", 1), ("f16_4096_f32out", threads),
+                           ("f16_4096_f32out", 1), ("f16_skinny512x512x65536_f32out", threads)]:
+        p = W.workload(name)
+        R, t = _oracle_rows(p, target_s, nthreads)
+        out.append({"workload": name, "threads": nthreads, "rows": R, "of_rows": p.M,
+                    "seconds": round(t, 4),
+                    "gflop_s": round(2.0 * R * p.N * p.K / t / 1e9, 2)})
+    return out
 
 
 def sustained_clocks(torch, fn, seconds=0.8, batch=20):
@@ -288,6 +328,8 @@ def main():
                          "'none' to skip")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-config-seconds", type=float, default=2.0,
+                    help="oracle seconds per workload for the cpu_configs entry (0: skip)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run 3 plain device copies of this many MiB (a known-size "
                          "reference for hardware byte counters)")
@@ -438,6 +480,8 @@ def main():
     if softmax:
         line["softmax"] = softmax
     line["cpu_baseline"] = None if args.no_cpu else cpu_baseline(p, args.cpu_seconds)
+    if not args.no_cpu and args.cpu_config_seconds > 0:
+        line["cpu_configs"] = cpu_configs(args.cpu_config_seconds)
     print(json.dumps(line), flush=True)
 
 
