@@ -824,8 +824,9 @@ def test_random_values_default_plan(ind):
 
 
 def test_negative_and_zero_strides():
-    """Negative row strides and a broadcast (zero-stride) row on the generic
-    kernel."""
+    """Negative row strides and a broadcast (zero-stride) row: through the
+    selector's plan (the fp32 matrix cores' range-checked form, K being the
+    unit-stride axis) and forced onto the generic kernel; exact."""
     rng = np.random.default_rng(9)
     M, N, K = 33, 21, 17
     a = rng.integers(-9, 10, size=(M, K)).astype(np.float64)
@@ -834,12 +835,14 @@ def test_negative_and_zero_strides():
     B = W.dense(W.to_bits(b, "f32"), "f32")
     p = W.Problem(M, N, K, A, B, "f32", "f32")
     assert np.array_equal(A.logical_bits(), W.to_bits(a, "f32"))
-    c, _ = run(p)
-    compare(p, c, exact=True, label="negative stride")
     row = W.Operand(W.to_bits(a[0], "f32"), "f32", M, K, 0, 0, 1)
     p2 = W.Problem(M, N, K, row, B, "f32", "f32")
-    c, _ = run(p2)
-    compare(p2, c, exact=True, label="broadcast")
+    for cfg, kernel in [(None, "mfma_f32"), (dict(kernel=GEN), "generic")]:
+        for prob, label in [(p, "negative stride"), (p2, "broadcast")]:
+            plan = {}
+            c, _ = run(prob, config=cfg, plan=plan)
+            assert plan["kernel_name"] == kernel, plan
+            compare(prob, c, exact=True, label=f"{label} {kernel}")
 
 
 # ------------------------------------------------------------ semantics
