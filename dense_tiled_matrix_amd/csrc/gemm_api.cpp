@@ -436,20 +436,27 @@ constexpr int64_t FOUR_WAVE_MIN_K = DTM_FOUR_WAVE_MIN_K;
 
 // The wave-K kernel (128 x 128 tiles whose 4 waves split the K loop, each
 // wave holding the whole tile) takes over from the 128-wide pipelined tile
-// when each tile's K loop is long.  Measured side by side (bf16 unless
-// noted, us, wave-K against 4 waves of 64 x 64): 2048^2 x 8192 62.8 / 68.5,
-// 8192 x 1024 x 8192 127.2 / 136.1, fp16 512 x 512 x 65536 split 16 43.3 /
-// 42.8 back to back and 58.2 / 67.3 with inputs from HBM; shorter loops
-// lose: 2048^3 23.8 / 20.4, 1024 x 4096 x 4096 37.0 / 35.3, 1024^2 x 8192
-// split 4 29.3 / 27.5.
-constexpr int64_t WAVEK_MIN_K = 8192;        // unsplit: the whole K loop
-constexpr int64_t WAVEK_MIN_SLICE_K = 4096;  // split: each slice's
+// when each tile's K loop is long.  Measured side by side (bf16 / fp16 -> fp32,
+// us, wave-K against 4 waves of 64 x 64): K loops of 8192 or more gain 3-15%
+// (2048^2 x 8192 63.9 / 67.5, 2048^2 x 16384 118.7 / 132.1, 1536^2 x 8192
+// 58.8 / 64.5, 8192 x 1024 x 8192 130.1 / 135.4, 1024^2 x 32768 split 4
+// 67.3 / 71.2, 1024 x 2048 x 16384 split 2 67.7 / 73.3); split slices of
+// 4096 are level back to back when the slices fill the 256 CUs (512^2 x
+// 65536 split 16 42.3 / 42.1, with inputs from HBM 58.2 / 67.3; 1024^2 x
+// 16384 split 4 41.4 / 41.2) and lose when they do not (640^2 x 32768 split
+// 8, 200 workgroups, 42.0 / 37.7); shorter loops lose (1024^2 x 8192 split
+// 4 28.5 / 26.2, 2048^3 23.8 / 20.4).
+constexpr int64_t WAVEK_MIN_K = 8192;        // K loop per tile (per slice when split)
+constexpr int64_t WAVEK_MIN_FULL_SLICE_K = 4096;  // split slices that fill the CUs
 
 bool prefer_wavek(const Call &c, int layout, int64_t splits)
 {
+    if (!wavek_fits(c, layout, splits))
+        return false;
     const int64_t k_slice = c.K / splits;
-    return wavek_fits(c, layout, splits) &&
-           k_slice >= (splits > 1 ? WAVEK_MIN_SLICE_K : WAVEK_MIN_K);
+    const int64_t units = cdiv(c.M, 128) * cdiv(c.N, 128) * splits;
+    return k_slice >= WAVEK_MIN_K ||
+           (splits > 1 && k_slice >= WAVEK_MIN_FULL_SLICE_K && units >= CUS);
 }
 
 // The plan for a call.  ws_budget: bytes of workspace the call can use;
