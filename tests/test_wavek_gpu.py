@@ -69,3 +69,20 @@ def test_wavek_random_bf16(layout):
     err, tol = compare(p, c, label=f"wave-K {layout} bf16 1024x768x4096")
     note(f"wave-K {layout}: max err {err:.3e} tol {tol:.3e}")
     assert untouched
+
+
+def test_wavek_selector_random():
+    """1536 x 1536 x 8192 bf16 N(0,1) -> bf16 through the selector's plan
+    (the wave-K kernel unsplit: 144 tiles of 128 with an 8192-long K loop),
+    compared in full with the oracle within the stated tolerance and the
+    Higham bound."""
+    p = W.random_problem(1536, 1536, 8192, "bf16", "bf16", ("normal", 0.0, 1.0), seed=940)
+    plan = {}
+    c, untouched = run(p, plan=plan)
+    assert plan["kernel"] == WK and plan["split_k"] == 1 and plan["block_m"] == 128, plan
+    c64, cout = oracle.gemm_problem(p)
+    err, tol = compare(p, c, c64=c64, cout=cout, label="wave-K selector 1536x1536x8192")
+    ratio = higham_ratio(p, c, c64)
+    note(f"wave-K selector 1536x1536x8192: err/tol {err / tol:.2e}; Higham ratio {ratio:.3f}")
+    assert ratio <= 1.0
+    assert untouched
