@@ -157,57 +157,139 @@ def host_us_per_call(dtm, torch, calls=500):
     return t / calls * 1e6
 
 
-def _oracle_rows(p, target_s: float, threads: int):
-    """Time the oracle on the first R rows of problem p (all of them when the
-    whole problem fits), R sized so the timed run takes about `target_s`
-    seconds.  Returns (R, seconds)."""
+def _first_rows(p, R, absolute=False):
+    """Problem p cut to the first R rows of A (and C); with `absolute`, both
+    operands replaced by their elementwise magnitudes (sign bits cleared)."""
     import numpy as np
 
-    import oracle
     import workloads as W
 
-    def run_rows(R):
-        if R == p.M:
-            sub = p
-        else:
-            rows = W.Operand(p.A.bits, p.A.dtype, R, p.K, p.A.offset, p.A.stride_r,
-                             p.A.stride_c)
-            sub = W.Problem(R, p.N, p.K, W.dense(np.ascontiguousarray(rows.logical_bits()),
-                                                 p.in_dtype),
-                            p.B, p.in_dtype, p.out_dtype)
+    def mag(bits, dtype):
+        if not absolute:
+            return bits
+        mask = 0x7FFFFFFF if dtype == "f32" else 0x7FFF
+        return (np.asarray(bits).astype(np.uint64) & mask).astype(bits.dtype)
+
+    rows = W.Operand(p.A.bits, p.A.dtype, R, p.K, p.A.offset, p.A.stride_r, p.A.stride_c)
+    a = W.dense(mag(np.ascontiguousarray(rows.logical_bits()), p.in_dtype), p.in_dtype)
+    b = p.B
+    if absolute:
+        b = W.dense(mag(np.ascontiguousarray(p.B.logical_bits()), p.in_dtype), p.in_dtype)
+    return W.Problem(R, p.N, p.K, a, b, p.in_dtype, p.out_dtype)
+
+
+def _oracle_rows(p, target_s: float, threads: int, keep: list | None = None):
+    """Time the oracle on the first R rows of problem p (all of them when the
+    whole problem fits), R sized so the timed run takes about `target_s`
+    seconds.  Returns (R, seconds); with `keep`, appends the timed run's
+    fp64 result (R x N) to it."""
+    import oracle
+
+    def run_rows(R, final=False):
+        sub = p if R == p.M else _first_rows(p, R)
         t0 = time.perf_counter()
-        oracle.gemm_problem(sub, threads=threads)
-        return time.perf_counter() - t0
+        c64, _ = oracle.gemm_problem(sub, threads=threads)
+        t = time.perf_counter() - t0
+        if final and keep is not None:
+            keep.append(c64)
+        return t
 
     # two calibration points separate the fixed cost (decoding B) from the
     # per-row cost
     r1 = min(p.M, threads)
     t1 = run_rows(r1)
     if r1 == p.M or t1 * p.M / r1 < target_s:
-        return p.M, run_rows(p.M)
+        return p.M, run_rows(p.M, final=True)
     r4 = min(p.M, 4 * threads)
     t4 = run_rows(r4)
     per_row = max((t4 - t1) / max(r4 - r1, 1), 1e-7)
     R = int((target_s - t1) / per_row) + r1
     R = int(min(p.M, max(r1, threads * (R // threads))))
-    return R, run_rows(R)
+    return R, run_rows(R, final=True)
 
 
 def host_threads() -> int:
     return max(1, min(HOST_THREADS_CAP, len(os.sched_getaffinity(0))))
 
 
-def cpu_baseline(p, target_s: float):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _half_ulp(x, dtype: str):
+    """Half the spacing of `dtype` at |x|: the most the final rounding of an
+    exact value to that format adds."""
+    import numpy as np
+
+    mant, emin = {"f32": (23, -126), "f16": (10, -14), "bf16": (7, -126)}[dtype]
+    ax = np.abs(x)
+    e = np.maximum(np.floor(np.log2(np.where(ax > 0, ax, 1.0))), emin)
+    return 0.5 * np.exp2(e - mant)
+
+
+HIGHAM_ROWS = 64
+
+
+def result_check(p, c64, c_bits, threads: int):
+    """The GPU result's first R rows (R = rows of c64) against the oracle's
+    fp64 values of the same rows (Chapter 13 section 13.3, Worked Example
+    13.3.1: truth in fp64 from the same rounded inputs): max |error|, the
+    per-element tolerance (fp32 accumulation over K; half an output ulp for a
+    rounded output), how many elements exceed it, and on the first rows the
+    ratio of the error to the textbook bound gamma_K (|A||B|)_ij of K fp32
+    additions (u' = 2^-23 for the matrix cores' internal adds)."""
+    import numpy as np
+
+    import oracle
+
+    R = c64.shape[0]
+    od = p.out_dtype
+    got = oracle.decode(c_bits, od)
+    amax = float(np.abs(oracle.decode(p.A.logical_bits(), p.in_dtype)).max())
+    bmax = float(np.abs(oracle.decode(p.B.logical_bits(), p.in_dtype)).max())
+    tol = oracle.tolerance(p.in_dtype, p.K, amax, bmax)
+    half = _half_ulp(c64, od) if od != "f32" else 0.0
+    err = np.abs(got - c64)
+    over = int(np.count_nonzero(err > tol + half))
+    h = min(R, HIGHAM_ROWS)
+    ab64, _ = oracle.gemm_problem(_first_rows(p, h, absolute=True), threads=threads)
+    u = 2.0 ** -23
+    gamma = p.K * u / (1 - p.K * u)
+    bound = gamma * ab64 + (_half_ulp(c64[:h], od) if od != "f32" else 0.0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        hr = np.where(err[:h] == 0, 0.0, err[:h] / bound)
+    return {"rows": R, "of_rows": p.M, "max_abs_err": float(err.max()), "tol": tol,
+            "max_err_over_tol": round(float(err.max()) / tol, 4) if tol > 0 else None,
+            "elements_over_tol": over, "nan": bool(np.isnan(got).any()),
+            "higham_ratio": round(float(hr.max()), 4), "higham_rows": h,
+            "ok": over == 0 and not np.isnan(got).any()}
+
+
+def cpu_baseline(p, target_s: float, gpu_rows=None):
     """The oracle (untuned, fp64, OpenMP over rows) on the first R rows of the
-    workload, R sized so the timed run takes about `target_s` seconds."""
+    workload, R sized so the timed run takes about `target_s` seconds.  With
+    `gpu_rows` (a function R -> the GPU result's first R rows as output-dtype
+    bits), the oracle's rows also check the GPU result ("check")."""
     threads = host_threads()
-    R, t = _oracle_rows(p, target_s, threads)
+    keep = []
+    R, t = _oracle_rows(p, target_s, threads, keep)
     flops = 2.0 * R * p.N * p.K
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {R} of {p.M} rows of A times all of B ({p.K}x{p.N}), "
-                      f"{t:.1f} s wall incl. decoding the operands to fp64; {threads} threads "
-                      f"(the host-core share of one GPU; "
-                      f"{len(os.sched_getaffinity(0))} visible)"}
+    out = {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"first {R} of {p.M} rows of A times all of B ({p.K}x{p.N}), "
+                     f"{t:.1f} s wall incl. decoding the operands to fp64; {threads} threads "
+                     f"(the host-core share of one GPU; "
+                     f"{len(os.sched_getaffinity(0))} visible)",
+           "cpu_model": cpu_model()}
+    if gpu_rows is not None:
+        out["check"] = result_check(p, keep[0], gpu_rows(R), threads)
+    return out
 
 
 def cpu_configs(target_s: float):
@@ -374,9 +456,9 @@ def main():
         if sustain:  # after the timed calls: clocks and power under this load
             clocks = sustained_clocks(torch, lambda: dtm.gemm(a, b, out=c))
         flops = 2.0 * p.M * p.N * p.K
-        return p, plan, wall_ms, kern_ms, flops, (med_ms, min_ms)
+        return p, plan, wall_ms, kern_ms, flops, (med_ms, min_ms), c
 
-    p, plan, wall_ms, kern_ms, flops, (med_ms, min_ms) = measure(
+    p, plan, wall_ms, kern_ms, flops, (med_ms, min_ms), c_head = measure(
         args.workload, sustain=True, min_warm_s=args.headline_warmup_s)
     peak = PEAK_TFLOPS[p.in_dtype]
     achieved = flops / (kern_ms * 1e-3) / 1e12
@@ -406,9 +488,17 @@ def main():
         "per_call_ms": {"median": round(med_ms, 4), "min": round(min_ms, 4)},
         "clocks": clocks,
     }
+    sclk = (clocks or {}).get("sclk_mhz_mean_over_xcds")
+    if sclk:
+        # the dense peak scaled to the shader clock the part held under this
+        # load (the published peak assumes 2.4 GHz)
+        at_clk = peak * sclk / 2400.0
+        clocks["peak_tflops_at_sclk"] = round(at_clk, 1)
+        clocks["frac_at_sclk"] = round(achieved / at_clk, 4)
     secondary = []
     for name in [s for s in args.secondary.split(",") if s and s not in (args.workload, "none")]:
-        q, qplan, qwall, qkern, qflops, (qmed, qmin) = measure(name, min_warm_s=args.extra_warmup_s)
+        q, qplan, qwall, qkern, qflops, (qmed, qmin), _ = measure(name,
+                                                                min_warm_s=args.extra_warmup_s)
         qa = qflops / (qkern * 1e-3) / 1e12
         secondary.append({"workload": q.name, "tflops_wall": round(qflops / (qwall * 1e-3) / 1e12, 2),
                           "tflops_kernel": round(qa, 2), "frac": round(qa / PEAK_TFLOPS[q.in_dtype], 4),
@@ -479,10 +569,24 @@ def main():
         del x, y, ysame
     if softmax:
         line["softmax"] = softmax
-    line["cpu_baseline"] = None if args.no_cpu else cpu_baseline(p, args.cpu_seconds)
+    def gpu_rows(R):
+        # the headline's output after its last timed call (every call writes
+        # the same values), first R rows as raw output-dtype bits
+        import numpy as np
+
+        ibits = {2: torch.int16, 4: torch.int32}[c_head.element_size()]
+        ubits = {2: np.uint16, 4: np.uint32}[c_head.element_size()]
+        return c_head[:R].contiguous().view(ibits).cpu().numpy().view(ubits)
+
+    line["cpu_baseline"] = None if args.no_cpu else cpu_baseline(p, args.cpu_seconds, gpu_rows)
     if not args.no_cpu and args.cpu_config_seconds > 0:
         line["cpu_configs"] = cpu_configs(args.cpu_config_seconds)
     print(json.dumps(line), flush=True)
+    check = (line["cpu_baseline"] or {}).get("check")
+    if check is not None and not check["ok"]:
+        print(f"bench.py: the headline result is outside the oracle's tolerance: {check}",
+              file=sys.stderr)
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -18,6 +18,7 @@ import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdtm_gemm.so")
+DEBUG_LIB_PATH = os.path.join(HERE, "libdtm_gemm_debug.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HEADER = os.path.join(INCLUDE, "dtm_gemm.h")
 HEADERS = [HEADER, os.path.join(INCLUDE, "dtm_softmax.h")]
@@ -95,6 +96,43 @@ class GemmError(RuntimeError):
 _lib = None
 
 
+def _load(path):
+    """Load a build of the library at `path` and declare its C signatures."""
+    L = ctypes.CDLL(path)
+    i64, vp, i32, u64 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64
+    ops = [i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, i32, i32]
+    L.gemm.argtypes = ops + [vp]
+    L.gemm.restype = i32
+    L.gemm_plan.argtypes = ops + [ctypes.POINTER(TileConfig), ctypes.POINTER(Plan)]
+    L.gemm_plan.restype = i32
+    L.gemm_ex.argtypes = ops + [ctypes.POINTER(TileConfig), vp, u64, vp]
+    L.gemm_ex.restype = i32
+    L.gemm_status_string.argtypes = [i32]
+    L.gemm_status_string.restype = ctypes.c_char_p
+    L.gemm_kernel_name.argtypes = [i32]
+    L.gemm_kernel_name.restype = ctypes.c_char_p
+    L.gemm_set_pointer_checks.argtypes = [i32]
+    L.gemm_set_pointer_checks.restype = i32
+    L.gemm_ex_noalloc.argtypes = ops + [ctypes.POINTER(TileConfig), vp]
+    L.gemm_ex_noalloc.restype = i32
+    L.gemm_noalloc_scratch_bytes.argtypes = []
+    L.gemm_noalloc_scratch_bytes.restype = u64
+    L.gemm_mfma_probe.argtypes = [i32, i32, i32, vp, vp, vp, vp]
+    L.gemm_mfma_probe.restype = i32
+    L.gemm_workspace_reserve.argtypes = [u64, vp]
+    L.gemm_workspace_reserve.restype = i32
+    L.gemm_workspace_release.argtypes = [vp]
+    L.gemm_workspace_release.restype = i32
+    L.gemm_workspace_reserved.argtypes = [vp]
+    L.gemm_workspace_reserved.restype = u64
+    sops = [i64, i64, vp, i64, i64, vp, i64, i64, i32, i32]
+    L.row_softmax.argtypes = sops + [vp]
+    L.row_softmax.restype = i32
+    L.row_softmax_plan.argtypes = sops + [ctypes.POINTER(SoftmaxPlan)]
+    L.row_softmax_plan.restype = i32
+    return L
+
+
 def lib():
     """The loaded libdtm_gemm.so (raises if it has not been built)."""
     global _lib
@@ -102,40 +140,25 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -c 'import __graft_entry__ as g; g.build()'`")
-        L = ctypes.CDLL(LIB_PATH)
-        i64, vp, i32, u64 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64
-        ops = [i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, i32, i32]
-        L.gemm.argtypes = ops + [vp]
-        L.gemm.restype = i32
-        L.gemm_plan.argtypes = ops + [ctypes.POINTER(TileConfig), ctypes.POINTER(Plan)]
-        L.gemm_plan.restype = i32
-        L.gemm_ex.argtypes = ops + [ctypes.POINTER(TileConfig), vp, u64, vp]
-        L.gemm_ex.restype = i32
-        L.gemm_status_string.argtypes = [i32]
-        L.gemm_status_string.restype = ctypes.c_char_p
-        L.gemm_kernel_name.argtypes = [i32]
-        L.gemm_kernel_name.restype = ctypes.c_char_p
-        L.gemm_set_pointer_checks.argtypes = [i32]
-        L.gemm_set_pointer_checks.restype = i32
-        L.gemm_ex_noalloc.argtypes = ops + [ctypes.POINTER(TileConfig), vp]
-        L.gemm_ex_noalloc.restype = i32
-        L.gemm_noalloc_scratch_bytes.argtypes = []
-        L.gemm_noalloc_scratch_bytes.restype = u64
-        L.gemm_mfma_probe.argtypes = [i32, i32, i32, vp, vp, vp, vp]
-        L.gemm_mfma_probe.restype = i32
-        L.gemm_workspace_reserve.argtypes = [u64, vp]
-        L.gemm_workspace_reserve.restype = i32
-        L.gemm_workspace_release.argtypes = [vp]
-        L.gemm_workspace_release.restype = i32
-        L.gemm_workspace_reserved.argtypes = [vp]
-        L.gemm_workspace_reserved.restype = u64
-        sops = [i64, i64, vp, i64, i64, vp, i64, i64, i32, i32]
-        L.row_softmax.argtypes = sops + [vp]
-        L.row_softmax.restype = i32
-        L.row_softmax_plan.argtypes = sops + [ctypes.POINTER(SoftmaxPlan)]
-        L.row_softmax_plan.restype = i32
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+_debug_lib = None
+
+
+def debug_lib():
+    """The extra-barrier debug build, libdtm_gemm_debug.so (same C ABI; every
+    K iteration of the LDS-staged kernels waits for all memory operations and
+    the whole workgroup).  Raises if it has not been built
+    (`python -m dense_tiled_matrix_amd.build --debug-barriers`)."""
+    global _debug_lib
+    if _debug_lib is None:
+        if not os.path.exists(DEBUG_LIB_PATH):
+            raise RuntimeError(f"{DEBUG_LIB_PATH} is missing: build it with "
+                               "`python -m dense_tiled_matrix_amd.build --debug-barriers`")
+        _debug_lib = _load(DEBUG_LIB_PATH)
+    return _debug_lib
 
 
 def header_functions():
@@ -322,15 +345,18 @@ def gemm(a, b, out=None, out_dtype=None, stream=None):
     return out
 
 
-def gemm_ex(a, b, out=None, out_dtype=None, config=None, workspace=None, stream=None):
+def gemm_ex(a, b, out=None, out_dtype=None, config=None, workspace=None, stream=None,
+            library=None):
     """``gemm`` with a forced tile configuration (a dict of dtm_tile_config
-    fields or a TileConfig) and an optional workspace tensor."""
+    fields or a TileConfig) and an optional workspace tensor.  ``library``:
+    another build of the library to call (e.g. ``debug_lib()``)."""
     M, N, K, out = _operands(a, b, out, out_dtype)
     dev = _device_of(a, b, out, *([workspace] if workspace is not None else []))
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = _on_device(dev, lambda: lib().gemm_ex(*_args(a, b, out, M, N, K), _config(config),
-                                               ws_ptr, ws_bytes, _stream(dev, stream)))
+    L = library if library is not None else lib()
+    st = _on_device(dev, lambda: L.gemm_ex(*_args(a, b, out, M, N, K), _config(config),
+                                           ws_ptr, ws_bytes, _stream(dev, stream)))
     if st != DTM_OK:
         raise GemmError(st, "gemm_ex")
     return out

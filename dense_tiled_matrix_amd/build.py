@@ -3,6 +3,15 @@
 Every translation unit is compiled separately (in parallel) and linked into
 one shared library next to this file.  Device code is built for gfx950 only,
 with packed-fp32 instruction selection disabled.
+
+    python -m dense_tiled_matrix_amd.build [-v] [--debug-barriers]
+
+--debug-barriers builds libdtm_gemm_debug.so instead (objects in
+_build_debug/): the same sources with DTM_DEBUG_BARRIERS=1, which waits for
+all outstanding memory operations and adds a workgroup barrier at the top of
+every K iteration of the LDS-staged kernels.  Its results must be
+bit-identical to the normal library's (an A/B check for missing waits or
+barriers); it is slower and meant for tests only.
 """
 from __future__ import annotations
 
@@ -18,6 +27,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdtm_gemm.so")
+DEBUG_BUILD_DIR = os.path.join(HERE, "_build_debug")
+DEBUG_LIB = os.path.join(HERE, "libdtm_gemm_debug.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -30,11 +41,11 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+def _compile(src: str, verbose: bool, debug: bool = False) -> str:
+    obj = os.path.join(DEBUG_BUILD_DIR if debug else BUILD_DIR, os.path.basename(src) + ".o")
     # the .cpp host sources go through hipcc as HIP too (its default for
     # them): give every source the gfx950 device pass, not hipcc's default arch
-    cmd = [HIPCC] + COMMON + DEVICE
+    cmd = [HIPCC] + COMMON + DEVICE + (["-DDTM_DEBUG_BARRIERS=1"] if debug else [])
     if src.endswith(".hip"):
         cmd += ["-x", "hip"]
     cmd += ["-c", src, "-o", obj]
@@ -51,22 +62,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, jobs: int | None = None, debug_barriers: bool = False) -> str:
+    out_dir = DEBUG_BUILD_DIR if debug_barriers else BUILD_DIR
+    lib = DEBUG_LIB if debug_barriers else LIB
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, os.cpu_count() or 1), 16)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, debug_barriers), srcs))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, debug_barriers="--debug-barriers" in sys.argv))

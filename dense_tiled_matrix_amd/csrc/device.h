@@ -13,6 +13,23 @@
 
 namespace dtm {
 
+// A debug build (DTM_DEBUG_BARRIERS=1; `python -m dense_tiled_matrix_amd.build
+// --debug-barriers` makes libdtm_gemm_debug.so) adds, at the top of every K
+// iteration of the LDS-staged GEMM kernels, a wait for every outstanding
+// global load and LDS access and then a workgroup barrier.  The arithmetic
+// and its order are unchanged, so that build's results are bit-identical to
+// the normal build's; a difference exposes a missing wait or barrier.
+#ifndef DTM_DEBUG_BARRIERS
+#define DTM_DEBUG_BARRIERS 0
+#endif
+__device__ __forceinline__ void debug_sync()
+{
+#if DTM_DEBUG_BARRIERS
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt and lgkmcnt all 0
+    __builtin_amdgcn_s_barrier();
+#endif
+}
+
 // Problem description passed by value to every kernel.  Strides are in
 // elements; pointers address element (0,0) of each view.
 struct GemmArgs {

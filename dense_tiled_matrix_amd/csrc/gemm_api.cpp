@@ -31,6 +31,106 @@ bool env_pointer_checks()
 }
 std::atomic<bool> g_pointer_checks{env_pointer_checks()};
 
+// DTM_GEMM_FORCE: a tile configuration for the calls that pass none (gemm(),
+// and gemm_plan() / gemm_ex() / gemm_ex_noalloc() with force == NULL), so a
+// sweep can drive an unmodified caller.  Read once, when the library is
+// loaded; unset or empty means off.  Comma-separated fields, each either
+// "BMxBNxBK" (the tile) or key=value with key kernel (a dtm_kernel number or
+// its gemm_kernel_name), split, threads or dp_rows.  A value that does not
+// parse makes every such call return DTM_ERR_CONFIG.
+struct EnvForce {
+    bool on = false;
+    bool bad = false;
+    dtm_tile_config cfg{};
+};
+
+bool parse_i32(const char *s, const char *e, int32_t *out)
+{
+    if (s == e || e - s > 9)
+        return false;
+    int32_t v = 0;
+    for (const char *q = s; q < e; ++q) {
+        if (*q < '0' || *q > '9')
+            return false;
+        v = 10 * v + (*q - '0');
+    }
+    *out = v;
+    return true;
+}
+
+bool parse_kernel(const char *s, const char *e, int32_t *out)
+{
+    if (parse_i32(s, e, out))
+        return *out >= 0 && *out <= DTM_KERNEL_MFMA_F16_WAVEK;
+    for (int32_t k = 0; k <= DTM_KERNEL_MFMA_F16_WAVEK; ++k) {
+        const char *n = gemm_kernel_name(k);
+        if (std::strlen(n) == static_cast<size_t>(e - s) && std::strncmp(n, s, e - s) == 0) {
+            *out = k;
+            return true;
+        }
+    }
+    return false;
+}
+
+bool parse_field(const char *s, const char *e, dtm_tile_config *c)
+{
+    const char *eq = static_cast<const char *>(std::memchr(s, '=', e - s));
+    if (!eq) {  // BMxBNxBK
+        const char *x1 = static_cast<const char *>(std::memchr(s, 'x', e - s));
+        const char *x2 = x1 ? static_cast<const char *>(std::memchr(x1 + 1, 'x', e - x1 - 1))
+                            : nullptr;
+        return x2 && parse_i32(s, x1, &c->block_m) && parse_i32(x1 + 1, x2, &c->block_n) &&
+               parse_i32(x2 + 1, e, &c->block_k);
+    }
+    const size_t klen = eq - s;
+    auto key = [&](const char *k) { return std::strlen(k) == klen && !std::strncmp(k, s, klen); };
+    if (key("kernel"))
+        return parse_kernel(eq + 1, e, &c->kernel);
+    if (key("split"))
+        return parse_i32(eq + 1, e, &c->split_k);
+    if (key("threads"))
+        return parse_i32(eq + 1, e, &c->threads);
+    if (key("dp_rows"))
+        return parse_i32(eq + 1, e, &c->dp_rows);
+    return false;
+}
+
+EnvForce parse_env_force(const char *v)
+{
+    EnvForce f;
+    if (!v || !*v)
+        return f;
+    f.on = true;
+    const char *s = v;
+    while (true) {
+        const char *e = std::strchr(s, ',');
+        if (!e)
+            e = s + std::strlen(s);
+        if (!parse_field(s, e, &f.cfg)) {
+            f.bad = true;
+            return f;
+        }
+        if (!*e)
+            break;
+        s = e + 1;
+    }
+    return f;
+}
+
+const EnvForce g_env_force = parse_env_force(std::getenv("DTM_GEMM_FORCE"));
+
+// The configuration a call runs with: its own, else the environment's.
+// Returns false when the environment's does not parse.
+bool resolve_force(const dtm_tile_config *&force)
+{
+    if (force || !g_env_force.on)
+        return true;
+    if (g_env_force.bad)
+        return false;
+    force = &g_env_force.cfg;
+    return true;
+}
+
 }  // namespace
 
 bool pointer_checks_on() { return g_pointer_checks.load(std::memory_order_relaxed); }
@@ -742,6 +842,8 @@ int run(const Call &c, const dtm_tile_config *force, void *workspace, uint64_t w
     // Without a caller's workspace, the one reserved for this stream (if
     // any) bounds the plan; the lease is held until every launch of this
     // call is queued.
+    if (!dtm::resolve_force(force))
+        return DTM_ERR_CONFIG;
     std::optional<dtm::WorkspaceLease> lease;
     if (!workspace)
         lease.emplace(stream);
@@ -820,6 +922,8 @@ int gemm_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t stride_am,
 {
     const Call c{M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C, stride_cm,
                  stride_cn, in_dtype, out_dtype};
+    if (!dtm::resolve_force(force))
+        return DTM_ERR_CONFIG;
     return make_plan(c, force, call_budget(force, UINT64_MAX), out);
 }
 

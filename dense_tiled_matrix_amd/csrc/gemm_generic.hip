@@ -59,6 +59,7 @@ __global__ __launch_bounds__((BM / TM) * (BN / TN)) void gemm_generic_kernel(Gem
         }
 
     for (int64_t k0 = 0; k0 < p.K; k0 += BK) {
+        debug_sync();
         for (int e = t; e < BM * BK; e += THREADS) {
             const int r = a_k_fast ? e / BK : e % BM;
             const int c = a_k_fast ? e % BK : e / BM;

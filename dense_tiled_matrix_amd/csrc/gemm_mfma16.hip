@@ -242,6 +242,7 @@ __global__ __launch_bounds__(256) void gemm_mfma16_kernel(GemmArgs p, int64_t gr
     __syncthreads();
     for (int64_t kt = 0; kt + 1 < nk; ++kt) {
         const int cur = static_cast<int>(kt & 1);
+        debug_sync();
         load_tile((kt + 1) * BK);
         // keep the loads issued before the MFMAs so their latency is hidden
         __builtin_amdgcn_sched_barrier(0);

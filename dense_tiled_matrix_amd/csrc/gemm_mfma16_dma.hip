@@ -277,6 +277,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_dma_kernel(GemmArgs p
         const int stage = static_cast<int>(c % STAGES);
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * DMA_GROUP, 0));
         __builtin_amdgcn_s_barrier();
+        debug_sync();
         asm volatile("" ::: "memory");
         const int64_t kl = c + STAGES < nk ? c + STAGES : nk - 1;
         step(fa, fan, fb, fbn, lds + ((stage + 1) % STAGES) * STAGE_BYTES, true, kl, stage);
@@ -552,6 +553,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_mfma16_pair_kernel(GemmArgs 
             __builtin_amdgcn_s_waitcnt(waitcnt_imm(ODD ? 0 : GROUP, 0));
             __builtin_amdgcn_s_barrier();
         }
+        debug_sync();
         asm volatile("" ::: "memory");
         const int64_t n = c + 1;
         const char *nrg = lds + ((n >> 1) & 1) * REGION;

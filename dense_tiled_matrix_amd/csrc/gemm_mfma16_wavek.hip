@@ -234,6 +234,7 @@ __global__ __launch_bounds__(256) void gemm_mfma16_wavek_kernel(GemmArgs p, int6
                     u32x4 (&fbn)[NT], int64_t r) __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(GROUP, 15));
         __builtin_amdgcn_s_barrier();
+        debug_sync();
         asm volatile("" ::: "memory");
         const int slot = static_cast<int>((r + 1) & 1);
         step(fa, fan, fb, fbn, lds + slot * REGION, true, r + 3, r + 3 < nr, slot);

@@ -47,6 +47,14 @@
  *     check that pointers and strides stay inside the caller's allocations.
  *   - M == 0 or N == 0 is a successful no-op.  K == 0 writes zeros (the empty
  *     sum) to the M x N view of C.
+ *   - Sweeps: the environment variable DTM_GEMM_FORCE, read once when the
+ *     library is loaded, gives a tile configuration to every call that passes
+ *     none (gemm(); gemm_plan(), gemm_ex() and gemm_ex_noalloc() with
+ *     force == NULL).  Comma-separated fields: "BMxBNxBK" for the tile, and
+ *     kernel=<dtm_kernel number or gemm_kernel_name>, split=<S>,
+ *     threads=<T>, dp_rows=<R>, with the meaning of dtm_tile_config's fields
+ *     (e.g. DTM_GEMM_FORCE=128x128x32,split=4).  Unset or empty: off.  A value
+ *     that does not parse makes those calls return DTM_ERR_CONFIG.
  */
 #ifndef DTM_GEMM_H
 #define DTM_GEMM_H

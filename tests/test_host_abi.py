@@ -606,3 +606,56 @@ def test_forced_wave_k_kernel():
     assert plan(256, 256, 1024, config=dict(kernel=wk, split_k=16))[0] == err
     assert plan(256, 256, 256, ind=F32, config=dict(kernel=wk))[0] == err
     assert plan(512, 256, 1024, config=dict(kernel=wk, split_k=2, dp_rows=256))[0] == err
+
+
+def _plan_with_env(force_env, code):
+    """Runs `code` (which prints a result) in a fresh interpreter whose
+    DTM_GEMM_FORCE is `force_env` (the library reads it once, at load)."""
+    import subprocess
+    import sys
+
+    env = dict(os.environ)
+    env["DTM_GEMM_FORCE"] = force_env
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    prog = ("import sys; sys.path.insert(0, %r); import dense_tiled_matrix_amd as dtm; "
+            "PA, PB, PC = 0x10000000, 0x20000000, 0x30000000; " % root) + code
+    r = subprocess.run([sys.executable, "-c", prog], env=env, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    return r.stdout.strip()
+
+
+_PLAN_4096 = ("st, p = dtm.gemm_plan_raw(4096, 4096, 4096, PA, 4096, 1, PB, 4096, 1, PC, 4096, 1, "
+              "dtm.DTM_F16, dtm.DTM_F32{cfg}); "
+              "print(st, p['kernel_name'], p['block_m'], p['block_n'], p['block_k'], "
+              "p['split_k'])")
+
+
+def test_env_force_tile_and_split():
+    """DTM_GEMM_FORCE gives calls without a configuration of their own a
+    forced tile (and split), as gemm_ex's force argument would."""
+    out = _plan_with_env("128x128x32,split=4", _PLAN_4096.format(cfg=""))
+    assert out == "0 mfma_f16 128 128 32 4"
+    out = _plan_with_env("kernel=generic,64x64x16", _PLAN_4096.format(cfg=""))
+    assert out == "0 generic 64 64 16 1"
+    out = _plan_with_env("kernel=2,64x64x16", _PLAN_4096.format(cfg=""))
+    assert out == "0 generic 64 64 16 1"
+
+
+def test_env_force_yields_to_an_explicit_config():
+    cfg = ", {'kernel': dtm.DTM_KERNEL_MFMA_F16, 'block_m': 256, 'block_n': 256, 'block_k': 32}"
+    out = _plan_with_env("kernel=generic,64x64x16", _PLAN_4096.format(cfg=cfg))
+    assert out == "0 mfma_f16 256 256 32 1"
+
+
+def test_env_force_unparsable_is_a_config_error():
+    for bad in ("128x128", "tile=3", "kernel=nope", "128x128x32,", "split=-1"):
+        out = _plan_with_env(bad, _PLAN_4096.format(cfg=""))
+        assert out.split()[0] == str(dtm.DTM_ERR_CONFIG), (bad, out)
+
+
+def test_env_force_empty_is_off():
+    out = _plan_with_env("", _PLAN_4096.format(cfg=""))
+    _, p = plan(4096, 4096, 4096)
+    assert out == f"0 {p['kernel_name']} {p['block_m']} {p['block_n']} {p['block_k']} " \
+                  f"{p['split_k']}"
