@@ -4,10 +4,10 @@ Every translation unit is compiled separately (in parallel) and linked into
 one shared library next to this file.  Device code is built for gfx950 only,
 with packed-fp32 instruction selection disabled.
 
-    python -m dense_tiled_matrix_amd.build [-v] [--debug-barriers]
+    python -m dense_tiled_matrix_amd.build [-v] [--debug-barriers | --all]
 
 --debug-barriers builds libdtm_gemm_debug.so instead (objects in
-_build_debug/): the same sources with DTM_DEBUG_BARRIERS=1, which waits for
+_build_debug/), --all both (what __graft_entry__.build() runs): the same sources with DTM_DEBUG_BARRIERS=1, which waits for
 all outstanding memory operations and adds a workgroup barrier at the top of
 every K iteration of the LDS-staged kernels.  Its results must be
 bit-identical to the normal library's (an A/B check for missing waits or
@@ -62,14 +62,7 @@ def _compile(src: str, verbose: bool, debug: bool = False) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int | None = None, debug_barriers: bool = False) -> str:
-    out_dir = DEBUG_BUILD_DIR if debug_barriers else BUILD_DIR
-    lib = DEBUG_LIB if debug_barriers else LIB
-    os.makedirs(out_dir, exist_ok=True)
-    srcs = sources()
-    jobs = jobs or min(len(srcs), max(1, os.cpu_count() or 1), 16)
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, debug_barriers), srcs))
+def _link(objs, lib: str, verbose: bool) -> str:
     tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
@@ -81,5 +74,35 @@ def build(verbose: bool = False, jobs: int | None = None, debug_barriers: bool =
     return lib
 
 
+def build(verbose: bool = False, jobs: int | None = None, debug_barriers: bool = False) -> str:
+    """One of the two libraries: the normal one, or the extra-barrier build."""
+    out_dir = DEBUG_BUILD_DIR if debug_barriers else BUILD_DIR
+    os.makedirs(out_dir, exist_ok=True)
+    srcs = sources()
+    jobs = jobs or min(len(srcs), max(1, os.cpu_count() or 1), 16)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose, debug_barriers), srcs))
+    return _link(objs, DEBUG_LIB if debug_barriers else LIB, verbose)
+
+
+def build_all(verbose: bool = False, jobs: int | None = None) -> tuple[str, str]:
+    """Both libraries from one pool of compile jobs (the normal build's
+    objects first, so its long compiles start early): libdtm_gemm.so and
+    libdtm_gemm_debug.so, kept in step so the debug build always matches the
+    sources of the normal one."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(DEBUG_BUILD_DIR, exist_ok=True)
+    srcs = sources()
+    work = [(s, False) for s in srcs] + [(s, True) for s in srcs]
+    jobs = jobs or min(len(work), max(1, os.cpu_count() or 1), 16)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda w: _compile(w[0], verbose, w[1]), work))
+    n = len(srcs)
+    return _link(objs[:n], LIB, verbose), _link(objs[n:], DEBUG_LIB, verbose)
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv, debug_barriers="--debug-barriers" in sys.argv))
+    if "--all" in sys.argv:
+        print("\n".join(build_all(verbose="-v" in sys.argv)))
+    else:
+        print(build(verbose="-v" in sys.argv, debug_barriers="--debug-barriers" in sys.argv))
