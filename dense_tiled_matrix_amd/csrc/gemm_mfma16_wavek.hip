@@ -24,17 +24,25 @@ namespace {
 // bytes per tile are the same.  Meant for few output tiles and long K (the
 // split-K plans), where the 256-wide tiles would need 4x the partials.
 //
-// LDS: two regions of 64 KiB, each holding 4 consecutive chunks (128 k) of
-// A's 128 rows and B's 128 columns, laid out exactly as a region of the
-// 256-wide paired stages whose "256 rows" are (k half h2, row r) with
-// k = 64 * h2 + ..: chunk c of a region (k 32c ..) sits where the paired
-// layout keeps rows/columns 128 * (c / 2) .. of half c % 2.  Wave w reads
-// chunk w of each region with the paired form's fragment offsets.
-// Region r's fragments sit in registers while regions r + 1 and r + 2 fill
-// the two slots, so a load has more than a whole iteration before it is
-// waited for (against one slot ahead with reads of region r + 1 and loads of
-// region r + 2 spread over iteration r: long-K 512 x 512 x 65536 5% slower
-// warm, 18% slower cold).  K slices are whole regions (128 k).
+// LDS: a region is 4 consecutive chunks (128 k) of A's 128 rows and of B's
+// 128 columns, each operand's part (32 KiB) laid out exactly as one operand
+// of a region of the 256-wide paired stages whose "256 rows" are (k half h2,
+// row r) with k = 64 * h2 + ..: chunk c of a region (k 32c ..) sits where the
+// paired layout keeps rows/columns 128 * (c / 2) .. of half c % 2.  Wave w
+// reads chunk w of each region with the paired form's fragment offsets.
+// Region r's fragments sit in registers while regions r + 1 and r + 2 sit in
+// four of five 32 KiB slots (all 160 KiB of LDS), so a load has more than a
+// whole iteration before it is waited for (against one region ahead: long-K
+// 512 x 512 x 65536 5% slower warm, 18% slower cold).  The fifth slot lets
+// the refill start with the iteration: in its first half a wave reads region
+// r + 1's B fragments and loads A's part of region r + 3 into the free slot;
+// after a barrier it reads region r + 1's A fragments and loads B's part of
+// region r + 3 into the B slot just read, whose A slot then becomes the free
+// one.  Each half then issues 8 of a wave's 16 loads (a region's 64 KiB take
+// the CU's address unit about as long as the iteration's MFMAs; with all 16
+// in the 40 MFMAs after the reads the loop ran 1742 shader cycles an
+// iteration against 1425 now, 1024 being the MFMAs alone).  K slices are
+// whole regions (128 k).
 //
 // The sum of the four wave tiles goes through LDS in two passes of half the
 // tile's rows each: every wave writes its blocks of that half, then the two
@@ -51,21 +59,19 @@ __global__ __launch_bounds__(256) void gemm_mfma16_wavek_kernel(GemmArgs p, int6
     constexpr int RK = 4 * BK;             // k per region
     constexpr int HALF = VT * BK * 2;      // 16 KiB
     constexpr int OPB = 2 * HALF;          // an operand's part of a region: 32 KiB
-    constexpr int REGION = 2 * OPB;        // 64 KiB
     constexpr int LPR = krow_chunks<VT>(); // 16-byte chunks per (virtual) k-row: 32
     constexpr int ROWB = VT * 2;
     constexpr bool A_KC = !TA, B_KC = TB;
     constexpr int MT = 8, NT = 8;
     constexpr int A_READS = MT * (A_KC ? 1 : 2);
     constexpr int B_READS = NT * (B_KC ? 1 : 2);
-    constexpr int NREAD = A_READS + B_READS;
     constexpr int NMFMA = MT * NT;               // 64
     constexpr int SEGS = OPB / 1024 / 4;         // 1 KiB loads per operand per wave: 8
     constexpr int GROUP = 2 * SEGS;              // loads per wave per refill: 16
-    constexpr int DMA_EVERY = NMFMA / GROUP;     // 4
-    static_assert(DMA_EVERY * GROUP == NMFMA, "wave-K schedule");
+    static_assert(NMFMA % 2 == 0 && B_READS <= NMFMA / 2 && A_READS <= NMFMA / 2,
+                  "wave-K schedule");
 
-    __shared__ __attribute__((aligned(1024))) char lds[2 * REGION];
+    __shared__ __attribute__((aligned(1024))) char lds[5 * OPB];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -108,7 +114,7 @@ __global__ __launch_bounds__(256) void gemm_mfma16_wavek_kernel(GemmArgs p, int6
     const int64_t b_reg = B_KC ? RK : RK * p.sbk;
     const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, lds)));
     const uint32_t a_dst0 = lds_base + (SEGS * wave) * 1024;
-    const uint32_t b_dst0 = lds_base + OPB + (SEGS * wave) * 1024;
+    const uint32_t b_dst0 = lds_base + (SEGS * wave) * 1024;
 
     // This wave's chunk of a region: rows/columns 128 (wave / 2) .. of the
     // virtual layout, half wave % 2.
@@ -122,7 +128,7 @@ __global__ __launch_bounds__(256) void gemm_mfma16_wavek_kernel(GemmArgs p, int6
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         const int o = frag_off_pair<B_KC, VT>(vbase + j * 16, lane);
-        b_off[j] = OPB + (B_KC ? (o ^ (64 * hh)) : o + hh * HALF);
+        b_off[j] = B_KC ? (o ^ (64 * hh)) : o + hh * HALF;
     }
 
     u32x4 fa0[MT], fa1[MT], fb0[NT], fb1[NT];
@@ -149,58 +155,65 @@ __global__ __launch_bounds__(256) void gemm_mfma16_wavek_kernel(GemmArgs p, int6
         for (int j = 0; j < NT; ++j)
             acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Pipeline: region r in registers, regions r + 1 and r + 2 in the two
-    // LDS slots (region q in slot q % 2).  Iteration r: wait for region
-    // r + 1's loads (region r + 2's may be in flight) and barrier; read region
-    // r + 1 during the first RD_MFMAS MFMAs of region r; wait for the reads,
-    // barrier (every wave is done with slot (r + 1) % 2), and refill that
-    // slot with region r + 3 during the remaining MFMAs.  A load then has
-    // more than one whole iteration before it is waited for.  Loads past the
-    // slice's end read a zero-sized buffer: no memory traffic, and they only
-    // fill a slot that is not read again.
-    constexpr int RD_MFMAS = 24;  // measured against 16 and 32: within 1-2%
-    constexpr int DMA_SPAN = NMFMA - RD_MFMAS;
-    // load d of the refill of slot `slot` with region j (offsets below
-    // PAIR_SPAN_MAX: wavek_span_ok); a region past the slice's end (!live)
-    // reads a zero-sized buffer
-    auto dma_one = [&](int64_t j, bool live, int slot, int d) __attribute__((always_inline)) {
-        const uint32_t ro = static_cast<uint32_t>(slot) * REGION;
-        const uint32_t span = live ? PAIR_SPAN_MAX : 0u;
-        if (d < SEGS)
-            dma16_buf(buffer_rsrc(a_org + j * a_reg, span), a_voff[d], a_dst0 + ro + 1024 * d);
-        else
-            dma16_buf(buffer_rsrc(b_org + j * b_reg, span), b_voff[d - SEGS],
-                      b_dst0 + ro + 1024 * (d - SEGS));
+    // Pipeline: region r in registers, regions r + 1 and r + 2 in four of
+    // the five slots (slots of operand parts, tracked in sa1/sb1, sa2/sb2,
+    // sf below).  Iteration r: wait for region r + 1's loads (region
+    // r + 2's may be in flight) and for this wave's reads of the last
+    // iteration, and barrier; during MFMAs 0 .. H - 1 of region r read region
+    // r + 1's B fragments and load A's part of region r + 3 into the free
+    // slot; wait for the reads and barrier (every wave is done with region
+    // r + 1's B slot); during MFMAs H .. 63 read region r + 1's A fragments
+    // and load B's part of region r + 3 into that B slot.  Region r + 1's A
+    // slot is the next free one: the next iteration's wait and barrier cover
+    // every wave's reads of it.  Loads past the slice's end read a zero-sized
+    // buffer: no memory traffic, and they only fill a slot that is not read
+    // again.  (H = 24 and 40 measured level with 32.)
+    constexpr int H = NMFMA / 2;
+    constexpr int P2 = NMFMA - H;
+    // load d of A's (dma_a) or B's (dma_b) part of region j into `slot`
+    // (offsets below PAIR_SPAN_MAX: wavek_span_ok); a region past the slice's
+    // end (!live) reads a zero-sized buffer
+    auto dma_a = [&](int64_t j, bool live, int slot, int d) __attribute__((always_inline)) {
+        dma16_buf(buffer_rsrc(a_org + j * a_reg, live ? PAIR_SPAN_MAX : 0u), a_voff[d],
+                  a_dst0 + static_cast<uint32_t>(slot) * OPB + 1024 * d);
+    };
+    auto dma_b = [&](int64_t j, bool live, int slot, int d) __attribute__((always_inline)) {
+        dma16_buf(buffer_rsrc(b_org + j * b_reg, live ? PAIR_SPAN_MAX : 0u), b_voff[d],
+                  b_dst0 + static_cast<uint32_t>(slot) * OPB + 1024 * d);
     };
     auto step = [&](const u32x4 (&fa)[MT], u32x4 (&fan)[MT], const u32x4 (&fb)[NT],
-                    u32x4 (&fbn)[NT], const char *nrg, bool full, int64_t dma_j, bool live,
-                    int dma_slot) __attribute__((always_inline)) {
+                    u32x4 (&fbn)[NT], const char *nra, const char *nrb, bool full, int64_t dma_j,
+                    bool live, int slot_a, int slot_b) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < NMFMA; ++q) {
             const int i = q / NT, j = q % NT;
             acc[i][j] = mfma<IN>(fa[i], fb[j], acc[i][j]);
             if (full) {
-                if (q < RD_MFMAS) {
-                    const int r0 = q * NREAD / RD_MFMAS, r1 = (q + 1) * NREAD / RD_MFMAS;
+                if (q < H) {
+                    const int r0 = q * B_READS / H, r1 = (q + 1) * B_READS / H;
 #pragma unroll
-                    for (int r = r0; r < r1; ++r) {
-                        if (r < B_READS)
-                            read_b(fbn, nrg, r);
-                        else if ((r - B_READS) % A_PER == 0)
-                            read_a(fan, nrg, (r - B_READS) / A_PER);
-                    }
+                    for (int r = r0; r < r1; ++r)
+                        read_b(fbn, nrb, r);
+                    const int d0 = q * SEGS / H, d1 = (q + 1) * SEGS / H;
+#pragma unroll
+                    for (int d = d0; d < d1; ++d)
+                        dma_a(dma_j, live, slot_a, d);
                 }
-                if (q == RD_MFMAS - 1) {
+                if (q == H - 1) {
                     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
                     __builtin_amdgcn_s_barrier();
                     asm volatile("" ::: "memory");
                 }
-                if (q >= RD_MFMAS) {
-                    const int d0 = (q - RD_MFMAS) * GROUP / DMA_SPAN;
-                    const int d1 = (q + 1 - RD_MFMAS) * GROUP / DMA_SPAN;
+                if (q >= H) {
+                    const int r0 = (q - H) * A_READS / P2, r1 = (q + 1 - H) * A_READS / P2;
+#pragma unroll
+                    for (int r = r0; r < r1; ++r)
+                        if (r % A_PER == 0)
+                            read_a(fan, nra, r / A_PER);
+                    const int d0 = (q - H) * SEGS / P2, d1 = (q + 1 - H) * SEGS / P2;
 #pragma unroll
                     for (int d = d0; d < d1; ++d)
-                        dma_one(dma_j, live, dma_slot, d);
+                        dma_b(dma_j, live, slot_b, d);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -208,12 +221,20 @@ __global__ __launch_bounds__(256) void gemm_mfma16_wavek_kernel(GemmArgs p, int6
     };
 
     const int64_t nr = k_split / RK;  // regions in this slice, >= 1
+    // region 0 in slots (0, 1), region 1 in (2, 3); after region 0 is in
+    // registers, region 2 goes to (4, 1) and slot 0 is free
 #pragma unroll
-    for (int d = 0; d < GROUP; ++d)
-        dma_one(0, true, 0, d);
+    for (int d = 0; d < SEGS; ++d)
+        dma_a(0, true, 0, d);
 #pragma unroll
-    for (int d = 0; d < GROUP; ++d)
-        dma_one(1, nr > 1, 1, d);
+    for (int d = 0; d < SEGS; ++d)
+        dma_b(0, true, 1, d);
+#pragma unroll
+    for (int d = 0; d < SEGS; ++d)
+        dma_a(1, nr > 1, 2, d);
+#pragma unroll
+    for (int d = 0; d < SEGS; ++d)
+        dma_b(1, nr > 1, 3, d);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(GROUP, 0));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -222,23 +243,38 @@ __global__ __launch_bounds__(256) void gemm_mfma16_wavek_kernel(GemmArgs p, int6
         read_a(fa0, lds, i);
 #pragma unroll
     for (int q = 0; q < B_READS; ++q)
-        read_b(fb0, lds, q);
+        read_b(fb0, lds + OPB, q);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 #pragma unroll
-    for (int d = 0; d < GROUP; ++d)
-        dma_one(2, nr > 2, 0, d);
+    for (int d = 0; d < SEGS; ++d)
+        dma_a(2, nr > 2, 4, d);
+#pragma unroll
+    for (int d = 0; d < SEGS; ++d)
+        dma_b(2, nr > 2, 1, d);
+    // slots of region r + 1 (sa1, sb1) and r + 2 (sa2, sb2), and the free one
+    int sa1 = 2, sb1 = 3, sa2 = 4, sb2 = 1, sf = 0;
 
     auto iter = [&](const u32x4 (&fa)[MT], u32x4 (&fan)[MT], const u32x4 (&fb)[NT],
                     u32x4 (&fbn)[NT], int64_t r) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(GROUP, 15));
+        // region r + 1 loaded; every wave's reads of the last iteration done
+        // (the free slot was region r's A part)
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(GROUP, 0));
         __builtin_amdgcn_s_barrier();
         debug_sync();
         asm volatile("" ::: "memory");
-        const int slot = static_cast<int>((r + 1) & 1);
-        step(fa, fan, fb, fbn, lds + slot * REGION, true, r + 3, r + 3 < nr, slot);
+        step(fa, fan, fb, fbn, lds + sa1 * OPB, lds + sb1 * OPB, true, r + 3, r + 3 < nr, sf,
+             sb1);
         __builtin_amdgcn_sched_barrier(0);
+        // region r + 3 took (sf, sb1); region r + 1's A slot is free once
+        // every wave's reads of it are done (the next iteration's wait)
+        const int f = sa1, ob1 = sb1;
+        sa1 = sa2;
+        sb1 = sb2;
+        sa2 = sf;
+        sb2 = ob1;
+        sf = f;
     };
     int64_t r = 0;
     if ((nr & 1) == 0) {
@@ -255,7 +291,7 @@ __global__ __launch_bounds__(256) void gemm_mfma16_wavek_kernel(GemmArgs p, int6
         iter(fa0, fa1, fb0, fb1, r);
         iter(fa1, fa0, fb1, fb0, r + 1);
     }
-    step(fa0, fa1, fb0, fb1, lds, false, 0, false, 0);
+    step(fa0, fa1, fb0, fb1, lds, lds, false, 0, false, 0, 0);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
     // The sum of the four wave tiles, through LDS (1 KiB per 16 x 16 block
