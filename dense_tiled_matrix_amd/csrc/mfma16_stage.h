@@ -48,6 +48,17 @@ __device__ __forceinline__ int swz_krow(int k)
 
 // 16 bytes per lane from global memory straight into LDS at
 // lds_addr + 16 * lane (global_load_lds_dwordx4; M0 holds the LDS address).
+//
+// These loads are written in inline asm, each block setting M0 itself, and
+// the kernels wait for them with explicit s_waitcnt.  The compiler's builtins
+// for the same instructions (global_load_lds, raw_ptr_buffer_load_lds) make
+// it treat every load in flight as a possible writer of any later LDS read
+// of the same array, so it puts s_waitcnt vmcnt(0) before the fragment reads
+// (checked in the wave-K kernel's assembly: 30 vmcnt waits against 5), which
+// would serialize the pipelines.  The compiler warns that M0, a register it
+// reserves, is in the clobber list; in these kernels it never uses M0 itself
+// (every M0 reference in their assembly is one of these blocks' writes,
+// each followed by its load), so nothing of its own is overwritten.
 __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_addr)
 {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
