@@ -15,7 +15,7 @@ import dense_tiled_matrix_amd as dtm
 import oracle
 import workloads as W
 from conftest import read_golden
-from gpu_util import CBuf, compare, dev_storage, higham_ratio, note, run
+from gpu_util import compare, dev_storage, higham_ratio, note, run
 
 pytestmark = pytest.mark.gpu
 

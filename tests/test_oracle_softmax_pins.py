@@ -2,7 +2,6 @@
 Pointers", homework 4) to facts that do not come from the oracle itself:
 closed forms, the formula's IEEE special values, invariants, scipy's
 independent implementation, and numpy's rounding to the output dtype."""
-import math
 
 import numpy as np
 import pytest

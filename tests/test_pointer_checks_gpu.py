@@ -4,12 +4,10 @@ right result; a view in pinned host memory is refused with DTM_ERR_POINTER
 and nothing is written.  (A view running past its allocation is refused by
 the same range test; no case here would touch memory outside a mapped
 allocation if a check let it through.)"""
-import numpy as np
 import pytest
 import torch
 
 import dense_tiled_matrix_amd as dtm
-import oracle
 import workloads as W
 from gpu_util import CODE, run, compare
 

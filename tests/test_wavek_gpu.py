@@ -8,7 +8,6 @@ below 2^24); on random inputs within the stated tolerance and the
 Higham-style bound gamma_K (|A| |B|) of the oracle's fp64 product."""
 import numpy as np
 import pytest
-import torch
 
 import dense_tiled_matrix_amd as dtm
 import oracle

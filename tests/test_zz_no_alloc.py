@@ -9,7 +9,6 @@ import pytest
 import torch
 
 import dense_tiled_matrix_amd as dtm
-import oracle
 import workloads as W
 from gpu_util import CODE, compare, dev_storage, note
 
