@@ -69,63 +69,66 @@ __device__ __forceinline__ f32x4 load4_masked(const float *p, int64_t valid)
 // RAGGED: slots outside the view are exact zeros and are never read.  AL:
 // every 4-float unit starts on a 16-byte boundary (else element loads; only
 // with RAGGED).
+// Unit i of the R x BK tile of one operand (layout below).
+template <int R, bool KC, bool RAGGED, bool AL>
+__device__ __forceinline__ void load_unit(f32x4 &r, int i, const float *X, int64_t mn0,
+                                          int64_t s_mn, int64_t s_k, int64_t ext, int64_t K,
+                                          int64_t k0, int t)
+{
+    if constexpr (KC) {
+        const int c = t & 3, row = t >> 2;
+        const int64_t mn = mn0 + row + 64 * i;
+        const float *src = X + mn * s_mn + k0 + 4 * c;
+        if constexpr (RAGGED)
+            r = load4_masked<AL>(src, mn < ext ? K - (k0 + 4 * c) : 0);
+        else
+            r = *reinterpret_cast<const f32x4 *>(src);
+    } else {
+        const int b = t + 256 * (i >> 1), e = i & 1;
+        const int kk = 2 * (b % (BK / 2)), cc = b / (BK / 2);
+        const int64_t k = k0 + kk + e;
+        const float *src = X + k * s_k + mn0 + 4 * cc;
+        if constexpr (RAGGED)
+            r = load4_masked<AL>(src, k < K ? ext - (mn0 + 4 * cc) : 0);
+        else
+            r = *reinterpret_cast<const f32x4 *>(src);
+    }
+}
+
+// Registers -> the operand's part of an LDS stage (rows of ROW_F floats, k
+// contiguous), unit i; an M/N-contiguous operand's units go in pairs, as a
+// transposed 2 x 4 block, at the even index.
+template <int R, bool KC>
+__device__ __forceinline__ void store_unit(const f32x4 (&r)[R / 64], int i, float *s, int t)
+{
+    if constexpr (KC) {
+        const int c = t & 3, row = t >> 2;
+        *reinterpret_cast<f32x4 *>(s + (row + 64 * i) * ROW_F + 4 * c) = r[i];
+    } else if ((i & 1) == 0) {
+        const int b = t + 256 * (i >> 1);
+        const int kk = 2 * (b % (BK / 2)), cc = b / (BK / 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<f32x2 *>(s + (4 * cc + j) * ROW_F + kk) = f32x2{r[i][j], r[i + 1][j]};
+    }
+}
+
 template <int R, bool KC, bool RAGGED, bool AL>
 __device__ __forceinline__ void load_operand(f32x4 (&r)[R / 64], const float *X, int64_t mn0,
                                              int64_t s_mn, int64_t s_k, int64_t ext,
                                              int64_t K, int64_t k0, int t)
 {
-    constexpr int UNITS = R / 64;
-    if constexpr (KC) {
-        const int c = t & 3, row = t >> 2;
 #pragma unroll
-        for (int i = 0; i < UNITS; ++i) {
-            const int64_t mn = mn0 + row + 64 * i;
-            const float *src = X + mn * s_mn + k0 + 4 * c;
-            if constexpr (RAGGED)
-                r[i] = load4_masked<AL>(src, mn < ext ? K - (k0 + 4 * c) : 0);
-            else
-                r[i] = *reinterpret_cast<const f32x4 *>(src);
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < UNITS / 2; ++q) {
-            const int b = t + 256 * q;
-            const int kk = 2 * (b % (BK / 2)), cc = b / (BK / 2);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int64_t k = k0 + kk + e;
-                const float *src = X + k * s_k + mn0 + 4 * cc;
-                if constexpr (RAGGED)
-                    r[2 * q + e] = load4_masked<AL>(src, k < K ? ext - (mn0 + 4 * cc) : 0);
-                else
-                    r[2 * q + e] = *reinterpret_cast<const f32x4 *>(src);
-            }
-        }
-    }
+    for (int i = 0; i < R / 64; ++i)
+        load_unit<R, KC, RAGGED, AL>(r[i], i, X, mn0, s_mn, s_k, ext, K, k0, t);
 }
 
-// Registers -> the operand's part of an LDS stage (rows of ROW_F floats, k
-// contiguous); an M/N-contiguous 2 x 4 block is transposed on the way.
 template <int R, bool KC>
 __device__ __forceinline__ void store_operand(const f32x4 (&r)[R / 64], float *s, int t)
 {
-    constexpr int UNITS = R / 64;
-    if constexpr (KC) {
-        const int c = t & 3, row = t >> 2;
 #pragma unroll
-        for (int i = 0; i < UNITS; ++i)
-            *reinterpret_cast<f32x4 *>(s + (row + 64 * i) * ROW_F + 4 * c) = r[i];
-    } else {
-#pragma unroll
-        for (int q = 0; q < UNITS / 2; ++q) {
-            const int b = t + 256 * q;
-            const int kk = 2 * (b % (BK / 2)), cc = b / (BK / 2);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<f32x2 *>(s + (4 * cc + j) * ROW_F + kk) =
-                    f32x2{r[2 * q][j], r[2 * q + 1][j]};
-        }
-    }
+    for (int i = 0; i < R / 64; ++i)
+        store_unit<R, KC>(r, i, s, t);
 }
 
 // TA: A is M-contiguous (stride_am == 1), else K-contiguous.
@@ -176,7 +179,40 @@ __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t gr
     // lane (row/col lane%32, half h = lane/32) reads 16-byte chunk 2u + h of
     // its row for u = 0, 1: k = 8u + 4h + e feeds MFMA step 4u + e.
     const int fr = lane & 31, fh = lane >> 5;
-    auto compute_stage = [&](int stage) __attribute__((always_inline)) {
+    // One chunk's MFMAs from `stage`; with `pipe`, the next chunk (k0 = kn)
+    // is loaded into registers, one 16-byte unit every LS MFMAs, during the
+    // first quarter of them, and written to stage `nxt` the same way from
+    // 5/8 of them on.  (Issued apart from the MFMAs, the loads and stores
+    // took 780 of each chunk's 9565 shader cycles at 256 x 256; interleaved,
+    // the chunk takes 9155.  Stores from 1/2 or 3/4 on: level.)
+    constexpr int UA = BM / 64, UB = BN / 64, NU = UA + UB;
+    constexpr int NM = 2 * 4 * MI * NI;  // MFMAs per chunk
+    constexpr int LS = NM / 4 / NU > 0 ? NM / 4 / NU : 1;
+    constexpr int SQ0 = NM * 5 / 8;
+    auto hook = [&](int q, int64_t kn, int nxt) __attribute__((always_inline)) {
+        if (q % LS == 0 && q / LS < NU) {
+            const int x = q / LS;
+            if (x < UA)
+                load_unit<BM, !TA, RAGGED, AL>(ra[x], x, A, m0, p.sam, p.sak, p.M, p.K, kn, t);
+            else
+                load_unit<BN, TB, RAGGED, AL>(rb[x - UA], x - UA, B, n0, p.sbn, p.sbk, p.N, p.K,
+                                              kn, t);
+        }
+        if (q >= SQ0 && (q - SQ0) % LS == 0 && (q - SQ0) / LS < NU) {
+            const int x = (q - SQ0) / LS;
+            float *sa = lds + nxt * STAGE_F;
+            if (x < UA)
+                store_unit<BM, !TA>(ra, x, sa, t);
+            else
+                store_unit<BN, TB>(rb, x - UA, sa + A_F, t);
+        }
+    };
+    auto is_hook = [&](int q) __attribute__((always_inline)) {
+        return (q % LS == 0 && q / LS < NU) ||
+               (q >= SQ0 && (q - SQ0) % LS == 0 && (q - SQ0) / LS < NU);
+    };
+    auto compute_stage = [&](int stage, bool pipe, int64_t kn, int nxt)
+                             __attribute__((always_inline)) {
         const float *sa = lds + stage * STAGE_F + (wm * WM + fr) * ROW_F;
         const float *sb = lds + stage * STAGE_F + A_F + (wn * WN + fr) * ROW_F;
 #pragma unroll
@@ -193,9 +229,18 @@ __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t gr
 #pragma unroll
                 for (int i = 0; i < MI; ++i)
 #pragma unroll
-                    for (int j = 0; j < NI; ++j)
+                    for (int j = 0; j < NI; ++j) {
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][e], fb[j][e],
                                                                         acc[i][j], 0, 0, 0);
+                        const int q = ((u * 4 + e) * MI + i) * NI + j;
+                        if (pipe && is_hook(q)) {
+                            // kept in place: left alone, the compiler sinks
+                            // the loads behind the last MFMAs
+                            __builtin_amdgcn_sched_barrier(0);
+                            hook(q, kn, nxt);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
         }
     };
 
@@ -206,14 +251,10 @@ __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t gr
     for (int64_t kt = 0; kt + 1 < nk; ++kt) {
         const int cur = static_cast<int>(kt & 1);
         debug_sync();
-        load_tile((kt + 1) * BK);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_stage(cur);
-        __builtin_amdgcn_sched_barrier(0);
-        store_tile(cur ^ 1);
+        compute_stage(cur, true, (kt + 1) * BK, cur ^ 1);
         __syncthreads();
     }
-    compute_stage(static_cast<int>((nk - 1) & 1));
+    compute_stage(static_cast<int>((nk - 1) & 1), false, 0, 0);
 
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
