@@ -536,27 +536,21 @@ constexpr int64_t FOUR_WAVE_MIN_K = DTM_FOUR_WAVE_MIN_K;
 
 // The wave-K kernel (128 x 128 tiles whose 4 waves split the K loop, each
 // wave holding the whole tile) takes over from the 128-wide pipelined tile
-// when each tile's K loop is long.  Measured side by side (bf16 / fp16 -> fp32,
-// us, wave-K against 4 waves of 64 x 64): K loops of 8192 or more gain 3-15%
-// (2048^2 x 8192 63.9 / 67.5, 2048^2 x 16384 118.7 / 132.1, 1536^2 x 8192
-// 58.8 / 64.5, 8192 x 1024 x 8192 130.1 / 135.4, 1024^2 x 32768 split 4
-// 67.3 / 71.2, 1024 x 2048 x 16384 split 2 67.7 / 73.3); split slices of
-// 4096 are level back to back when the slices fill the 256 CUs (512^2 x
-// 65536 split 16 42.3 / 42.1, with inputs from HBM 58.2 / 67.3; 1024^2 x
-// 16384 split 4 41.4 / 41.2) and lose when they do not (640^2 x 32768 split
-// 8, 200 workgroups, 42.0 / 37.7); shorter loops lose (1024^2 x 8192 split
-// 4 28.5 / 26.2, 2048^3 23.8 / 20.4).
-constexpr int64_t WAVEK_MIN_K = 8192;        // K loop per tile (per slice when split)
-constexpr int64_t WAVEK_MIN_FULL_SLICE_K = 4096;  // split slices that fill the CUs
+// when each tile's K loop (per slice when split) is 4096 or more.  Measured
+// side by side (us, wave-K against 4 waves of 64 x 64, bf16 / fp16 -> fp32
+// pairs): loops of 8192 and more gain 8-17% (2048^2 x 8192 61.4 / 69.3,
+// 2048^2 x 16384 113.3 / 129.1, 1536^2 x 8192 55.6 / 63.7, 8192 x 1024 x
+// 8192 121.6 / 134.6, 1024^2 x 32768 split 4 65.3 / 71.3), loops of 4096 gain
+// 2-10% whether or not the workgroups fill the 256 CUs (512^2 x 65536 split 16
+// 41.7 / 42.3, 1024^2 x 16384 split 4 40.3 / 41.2, 640^2 x 32768 split 8 35.6
+// / 37.7, 896^2 x 16384 split 4 35.4 / 38.1, 1536^2 x 4096 32.9 / 36.3), and
+// loops of 2048 lose 1-8% (1024^2 x 8192 split 4 27.2 / 26.3, 2048^3 24.2 /
+// 22.4, 256^2 x 65536 split 32 25.2 / 24.5).
+constexpr int64_t WAVEK_MIN_K = 4096;  // K loop per tile (per slice when split)
 
 bool prefer_wavek(const Call &c, int layout, int64_t splits)
 {
-    if (!wavek_fits(c, layout, splits))
-        return false;
-    const int64_t k_slice = c.K / splits;
-    const int64_t units = cdiv(c.M, 128) * cdiv(c.N, 128) * splits;
-    return k_slice >= WAVEK_MIN_K ||
-           (splits > 1 && k_slice >= WAVEK_MIN_FULL_SLICE_K && units >= CUS);
+    return wavek_fits(c, layout, splits) && c.K / splits >= WAVEK_MIN_K;
 }
 
 // The plan for a call.  ws_budget: bytes of workspace the call can use;

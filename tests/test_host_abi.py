@@ -131,11 +131,8 @@ def test_selector_measured_workloads():
         st, p = plan(M, N, K, A=1 << 40, B=2 << 40, C=3 << 40, ind=F16, outd=F32)
         assert st == 0 and (p["block_m"], p["split_k"], p["ragged"]) == (128, S, ragged), \
             (M, N, K, p)
-        # split interior tiles: wave-K for slices of 8192 or more, or of 4096
-        # when tiles x slices fill the 256 CUs
-        units = -(-M // 128) * -(-N // 128) * S
-        wk = not ragged and K % (128 * S) == 0 and (
-            K // S >= 8192 or (K // S >= 4096 and units >= 256))
+        # split interior tiles: wave-K for slices of 4096 or more
+        wk = not ragged and K % (128 * S) == 0 and K // S >= 4096
         assert p["kernel_name"] == ("mfma_f16_wavek" if wk else "mfma_f16"), (M, N, K, p)
     # enough tiles: no split
     st, p = plan(4096, 4096, 65536, A=1 << 40, B=2 << 40, C=3 << 40, ind=F16, outd=F32)
@@ -561,15 +558,16 @@ def test_tensor_binding_rejects_host_and_mixed_devices():
 
 def test_wave_k_selector():
     """The selector's 128-wide interior plans take the wave-K kernel when
-    each tile's K loop (per slice when split) is 8192 or more, or 4096 when
-    tiles x slices fill the 256 CUs; everything else keeps the 4-wave form."""
+    each tile's K loop (per slice when split) is 4096 or more; shorter loops
+    keep the 4-wave form."""
     big = dict(A=1 << 40, B=2 << 40, C=3 << 40)
     for M, N, K, kernel in [(2048, 2048, 8192, "mfma_f16_wavek"), (1536, 1536, 8192, "mfma_f16_wavek"),
                             (8192, 1024, 8192, "mfma_f16_wavek"), (1024, 8192, 8192, "mfma_f16_wavek"),
                             (512, 512, 65536, "mfma_f16_wavek"), (1024, 1024, 16384, "mfma_f16_wavek"),
-                            (1024, 1024, 32768, "mfma_f16_wavek"), (640, 640, 32768, "mfma_f16"),
-                            (896, 896, 16384, "mfma_f16"), (1024, 1024, 8192, "mfma_f16"),
-                            (2048, 2048, 2048, "mfma_f16"), (256, 256, 65536, "mfma_f16")]:
+                            (1024, 1024, 32768, "mfma_f16_wavek"), (640, 640, 32768, "mfma_f16_wavek"),
+                            (896, 896, 16384, "mfma_f16_wavek"), (1536, 1536, 4096, "mfma_f16_wavek"),
+                            (1024, 1024, 8192, "mfma_f16"), (2048, 2048, 2048, "mfma_f16"),
+                            (256, 256, 65536, "mfma_f16"), (1024, 1024, 4096, "mfma_f16")]:
         st, p = plan(M, N, K, ind=BF16, outd=BF16, **big)
         assert st == 0 and p["kernel_name"] == kernel and p["block_m"] == 128, (M, N, K, p)
 
