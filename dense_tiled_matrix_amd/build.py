@@ -4,10 +4,12 @@ Every translation unit is compiled separately (in parallel) and linked into
 one shared library next to this file.  Device code is built for gfx950 only,
 with packed-fp32 instruction selection disabled.
 
-    python -m dense_tiled_matrix_amd.build [-v] [--debug-barriers | --all]
+    python -m dense_tiled_matrix_amd.build [-v] [--debug-barriers | --normal-only]
 
---debug-barriers builds libdtm_gemm_debug.so instead (objects in
-_build_debug/), --all both (what __graft_entry__.build() runs): the same sources with DTM_DEBUG_BARRIERS=1, which waits for
+builds both libraries by default (what __graft_entry__.build() runs), so the
+debug build never lags the sources; --normal-only builds only
+libdtm_gemm.so, --debug-barriers only libdtm_gemm_debug.so (objects in
+_build_debug/): the same sources with DTM_DEBUG_BARRIERS=1, which waits for
 all outstanding memory operations and adds a workgroup barrier at the top of
 every K iteration of the LDS-staged kernels.  Its results must be
 bit-identical to the normal library's (an A/B check for missing waits or
@@ -102,7 +104,10 @@ def build_all(verbose: bool = False, jobs: int | None = None) -> tuple[str, str]
 
 
 if __name__ == "__main__":
-    if "--all" in sys.argv:
-        print("\n".join(build_all(verbose="-v" in sys.argv)))
+    v = "-v" in sys.argv
+    if "--normal-only" in sys.argv:
+        print(build(verbose=v))
+    elif "--debug-barriers" in sys.argv:
+        print(build(verbose=v, debug_barriers=True))
     else:
-        print(build(verbose="-v" in sys.argv, debug_barriers="--debug-barriers" in sys.argv))
+        print("\n".join(build_all(verbose=v)))

@@ -67,7 +67,10 @@ def _operand(rows, cols, dtype, transposed, gen):
 def debug():
     if not os.path.exists(dtm.DEBUG_LIB_PATH):
         pytest.skip("libdtm_gemm_debug.so is not built "
-                    "(python -m dense_tiled_matrix_amd.build --debug-barriers)")
+                    "(python -m dense_tiled_matrix_amd.build)")
+    if os.path.getmtime(dtm.DEBUG_LIB_PATH) < os.path.getmtime(dtm.LIB_PATH) - 600:
+        pytest.skip("libdtm_gemm_debug.so is older than libdtm_gemm.so: rebuild both "
+                    "(python -m dense_tiled_matrix_amd.build)")
     return dtm.debug_lib()
 
 
