@@ -24,10 +24,12 @@ WK = dtm.DTM_KERNEL_MFMA_F16_WAVEK
 @pytest.mark.parametrize("ind", ["f16", "bf16"])
 def test_wavek_layouts_exact(ind, layout):
     """1, 2, 3 and many 128-deep regions per slice (the loop's odd and even
-    trip counts), several grids, split-K, padded leading dimensions, every
-    output dtype: value-exact."""
+    trip counts, with and without split-K: the five LDS slots' rotation from
+    its first state), several grids, padded leading dimensions, every output
+    dtype: value-exact."""
     shapes = [(128, 128, 128, 1), (256, 128, 256, 1), (128, 384, 384, 1), (384, 256, 2048, 1),
-              (512, 512, 8192, 4), (256, 256, 4096, 8), (256, 384, 640, 1)]
+              (512, 512, 8192, 4), (256, 256, 4096, 8), (256, 384, 640, 1),
+              (256, 256, 512, 4), (256, 128, 1024, 4), (128, 256, 1536, 4)]
     for n, (M, N, K, S) in enumerate(shapes):
         outd = ["f32", "f16", "bf16"][n % 3]
         p = padded_int_problem(M, N, K, ind, outd, 8 if K <= 512 else 2, seed=900 + n,
