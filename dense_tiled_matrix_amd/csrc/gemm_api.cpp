@@ -517,6 +517,16 @@ bool prefer_f32_256(const Call &c)
     return F32_RATE_256 * fill256 > fill128;
 }
 
+// fp32 chunk depth: 32 at 256 x 256 when K is a multiple of 32 (one barrier
+// and one refill round per 32 k; 4096^3 and 8192^3 about 1% faster, in 144
+// KiB of LDS), else 16 -- a K off 32 would send every chunk through the
+// range-checked loads.  128 x 128 keeps 16 (32 there holds two workgroups
+// per CU instead of three and cost 5% at 3000^3).
+int32_t f32_block_k(const Call &c, int32_t tile)
+{
+    return tile == 256 && c.K % 32 == 0 ? 32 : 16;
+}
+
 // The pipelined kernel's interior form at tile 256 runs with 4 waves of
 // 128 x 128 (one per SIMD) when each tile's K loop is at least this long,
 // else with 8 waves of 128 x 64 (two per SIMD, which cover each other's
@@ -676,7 +686,7 @@ int make_plan(const Call &c, const dtm_tile_config *force, uint64_t ws_budget, d
         if (forced_dims && !dtm::mfma32_has_config(force->block_m, force->block_n, force->block_k))
             return DTM_ERR_CONFIG;
         p.block_m = p.block_n = forced_dims ? force->block_m : (prefer_f32_256(c) ? 256 : 128);
-        p.block_k = 16;
+        p.block_k = forced_dims ? force->block_k : f32_block_k(c, p.block_m);
         p.threads = 256;
         p.layout = layout32;
     } else if (kernel == DTM_KERNEL_GENERIC || kernel == DTM_KERNEL_GENERIC_FP16ACC) {

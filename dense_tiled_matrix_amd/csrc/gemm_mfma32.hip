@@ -14,13 +14,15 @@
 //    (64 x 64 per wave, three workgroups per CU) or 256 x 256 (128 x 128 per
 //    wave in the accumulation registers, one workgroup per CU, half the LDS
 //    reads per MFMA: 4096^3 121 -> 134 TFLOP/s, 8192^3 126 -> 132).
-//  * 16-deep K-chunks, two LDS stages, loaded through registers one chunk
+//  * K-chunks 16 deep (32 deep at 256 x 256 unless a plan names 16: 144 KiB
+//    of LDS, one barrier and one refill round per 32 k; 4096^3 and 8192^3
+//    gained about 1%), two LDS stages, loaded through registers one chunk
 //    ahead.  A K-contiguous operand (A row-major, or B given as the
 //    transpose of an N x K array) goes to LDS as it is; an M- or
 //    N-contiguous one is loaded along its contiguous axis and each thread
 //    transposes its 2 x 4 block on the way, so LDS holds both operands
-//    k-contiguous, rows padded to 80 bytes (16 consecutive rows hit distinct
-//    bank groups).
+//    k-contiguous, rows padded by 16 bytes (80 or 144 bytes: consecutive
+//    rows start in different bank groups).
 //  * Which k a lane feeds at each MFMA step is a fixed permutation shared by
 //    A and B: lane half h at step s = 4t + e uses k = 8t + 4h + e, so one
 //    16-byte LDS read serves four steps.  The sum over k is unchanged.
@@ -37,9 +39,11 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BK = 16;
-constexpr int ROW_F = BK + 4;  // floats per LDS row (64 data bytes + 16 pad)
 constexpr int64_t GROUP_M = 4;
+
+// A chunk is BK k deep (16, or 32 at 256 x 256); an LDS stage row holds BK
+// floats of one row or column plus a 16-byte pad.
+template <int BK> constexpr int row_floats() { return BK + 4; }
 
 // 4 consecutive floats at p[0..3]; positions >= valid are zero, valid <= 0
 // reads nothing.  AL: p is 16-byte aligned (one vector load when all four
@@ -59,25 +63,27 @@ __device__ __forceinline__ f32x4 load4_masked(const float *p, int64_t valid)
 
 // Global -> registers for the R x BK tile of one operand starting at row
 // (or column) mn0 and k0; X addresses element (mn, k) at mn*s_mn + k*s_k and
-// the operand has ext rows.  Each of the 256 threads holds R/64 16-byte
-// units:
-//  K-contiguous (KC): unit i is chunk t%4 (k 4c .. 4c+3) of row t/4 + 64 i;
+// the operand has ext rows.  Each of the 256 threads holds R*BK/1024 16-byte
+// units (units<BK, R>()):
+//  K-contiguous (KC): unit i is chunk t % (BK/4) (k 4c .. 4c+3) of row
+//  t / (BK/4) + (1024/BK) i;
 //  otherwise: units 2q and 2q+1 are k-rows kk and kk+1 of block b = t + 256 q,
 //  kk = 2 (b % (BK/2)), at rows 4 (b / (BK/2)) .. +3 (k-pair fastest:
 //  conflict-free LDS writes, and each load instruction reads 8 k-rows x 128
 //  contiguous bytes).
 // RAGGED: slots outside the view are exact zeros and are never read.  AL:
 // every 4-float unit starts on a 16-byte boundary (else element loads; only
-// with RAGGED).
-// Unit i of the R x BK tile of one operand (layout below).
-template <int R, bool KC, bool RAGGED, bool AL>
+// with RAGGED).  load_unit fetches unit i.
+template <int BK, int R> constexpr int units() { return R * BK / 1024; }
+
+template <int BK, int R, bool KC, bool RAGGED, bool AL>
 __device__ __forceinline__ void load_unit(f32x4 &r, int i, const float *X, int64_t mn0,
                                           int64_t s_mn, int64_t s_k, int64_t ext, int64_t K,
                                           int64_t k0, int t)
 {
     if constexpr (KC) {
-        const int c = t & 3, row = t >> 2;
-        const int64_t mn = mn0 + row + 64 * i;
+        const int c = t % (BK / 4), row = t / (BK / 4);
+        const int64_t mn = mn0 + row + (1024 / BK) * i;
         const float *src = X + mn * s_mn + k0 + 4 * c;
         if constexpr (RAGGED)
             r = load4_masked<AL>(src, mn < ext ? K - (k0 + 4 * c) : 0);
@@ -95,15 +101,17 @@ __device__ __forceinline__ void load_unit(f32x4 &r, int i, const float *X, int64
     }
 }
 
-// Registers -> the operand's part of an LDS stage (rows of ROW_F floats, k
+// Registers -> the operand's part of an LDS stage (rows of BK + 4 floats, k
 // contiguous), unit i; an M/N-contiguous operand's units go in pairs, as a
 // transposed 2 x 4 block, at the even index.
-template <int R, bool KC>
-__device__ __forceinline__ void store_unit(const f32x4 (&r)[R / 64], int i, float *s, int t)
+template <int BK, int R, bool KC>
+__device__ __forceinline__ void store_unit(const f32x4 (&r)[(units<BK, R>())], int i, float *s,
+                                           int t)
 {
+    constexpr int ROW_F = row_floats<BK>();
     if constexpr (KC) {
-        const int c = t & 3, row = t >> 2;
-        *reinterpret_cast<f32x4 *>(s + (row + 64 * i) * ROW_F + 4 * c) = r[i];
+        const int c = t % (BK / 4), row = t / (BK / 4);
+        *reinterpret_cast<f32x4 *>(s + (row + (1024 / BK) * i) * ROW_F + 4 * c) = r[i];
     } else if ((i & 1) == 0) {
         const int b = t + 256 * (i >> 1);
         const int kk = 2 * (b % (BK / 2)), cc = b / (BK / 2);
@@ -113,36 +121,38 @@ __device__ __forceinline__ void store_unit(const f32x4 (&r)[R / 64], int i, floa
     }
 }
 
-template <int R, bool KC, bool RAGGED, bool AL>
-__device__ __forceinline__ void load_operand(f32x4 (&r)[R / 64], const float *X, int64_t mn0,
-                                             int64_t s_mn, int64_t s_k, int64_t ext,
+template <int BK, int R, bool KC, bool RAGGED, bool AL>
+__device__ __forceinline__ void load_operand(f32x4 (&r)[(units<BK, R>())], const float *X,
+                                             int64_t mn0, int64_t s_mn, int64_t s_k, int64_t ext,
                                              int64_t K, int64_t k0, int t)
 {
 #pragma unroll
-    for (int i = 0; i < R / 64; ++i)
-        load_unit<R, KC, RAGGED, AL>(r[i], i, X, mn0, s_mn, s_k, ext, K, k0, t);
+    for (int i = 0; i < units<BK, R>(); ++i)
+        load_unit<BK, R, KC, RAGGED, AL>(r[i], i, X, mn0, s_mn, s_k, ext, K, k0, t);
 }
 
-template <int R, bool KC>
-__device__ __forceinline__ void store_operand(const f32x4 (&r)[R / 64], float *s, int t)
+template <int BK, int R, bool KC>
+__device__ __forceinline__ void store_operand(const f32x4 (&r)[(units<BK, R>())], float *s, int t)
 {
 #pragma unroll
-    for (int i = 0; i < R / 64; ++i)
-        store_unit<R, KC>(r, i, s, t);
+    for (int i = 0; i < units<BK, R>(); ++i)
+        store_unit<BK, R, KC>(r, i, s, t);
 }
 
 // TA: A is M-contiguous (stride_am == 1), else K-contiguous.
 // TB: B is K-contiguous (stride_bk == 1), else N-contiguous.
-template <int OUT, int BM, int BN, bool RAGGED, bool TA, bool TB, bool AL = true>
+template <int OUT, int BM, int BN, int BK, bool RAGGED, bool TA, bool TB, bool AL = true>
 __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t grid_m,
                                                           int64_t grid_n)
 {
     static_assert(AL || RAGGED, "unaligned operands take the range-checked form");
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int MI = WM / 32, NI = WN / 32;
+    constexpr int ROW_F = row_floats<BK>();
     constexpr int A_F = BM * ROW_F;                 // floats of one A stage
     constexpr int STAGE_F = (BM + BN) * ROW_F;
     static_assert(BM % 128 == 0 && BN % 128 == 0, "operand tiles split over 256 threads");
+    static_assert(BK == 16 || BK == 32, "chunks of 16 or 32 k");
 
     __shared__ __attribute__((aligned(16))) float lds[2 * STAGE_F];
 
@@ -156,17 +166,18 @@ __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t gr
     const float *A = static_cast<const float *>(p.A);
     const float *B = static_cast<const float *>(p.B);
 
-    f32x4 ra[BM / 64];
-    f32x4 rb[BN / 64];
+    constexpr int UA = units<BK, BM>(), UB = units<BK, BN>(), NU = UA + UB;
+    f32x4 ra[UA];
+    f32x4 rb[UB];
 
     auto load_tile = [&](int64_t k0) __attribute__((always_inline)) {
-        load_operand<BM, !TA, RAGGED, AL>(ra, A, m0, p.sam, p.sak, p.M, p.K, k0, t);
-        load_operand<BN, TB, RAGGED, AL>(rb, B, n0, p.sbn, p.sbk, p.N, p.K, k0, t);
+        load_operand<BK, BM, !TA, RAGGED, AL>(ra, A, m0, p.sam, p.sak, p.M, p.K, k0, t);
+        load_operand<BK, BN, TB, RAGGED, AL>(rb, B, n0, p.sbn, p.sbk, p.N, p.K, k0, t);
     };
     auto store_tile = [&](int stage) __attribute__((always_inline)) {
         float *sa = lds + stage * STAGE_F;
-        store_operand<BM, !TA>(ra, sa, t);
-        store_operand<BN, TB>(rb, sa + A_F, t);
+        store_operand<BK, BM, !TA>(ra, sa, t);
+        store_operand<BK, BN, TB>(rb, sa + A_F, t);
     };
 
     floatx16 acc[MI][NI];
@@ -177,7 +188,7 @@ __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t gr
             acc[i][j] = floatx16{0.0f};
 
     // lane (row/col lane%32, half h = lane/32) reads 16-byte chunk 2u + h of
-    // its row for u = 0, 1: k = 8u + 4h + e feeds MFMA step 4u + e.
+    // its row for u < BK/8: k = 8u + 4h + e feeds MFMA step 4u + e.
     const int fr = lane & 31, fh = lane >> 5;
     // One chunk's MFMAs from `stage`; with `pipe`, the next chunk (k0 = kn)
     // is loaded into registers, one 16-byte unit every LS MFMAs, during the
@@ -185,26 +196,26 @@ __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t gr
     // 5/8 of them on.  (Issued apart from the MFMAs, the loads and stores
     // took 780 of each chunk's 9565 shader cycles at 256 x 256; interleaved,
     // the chunk takes 9155.  Stores from 1/2 or 3/4 on: level.)
-    constexpr int UA = BM / 64, UB = BN / 64, NU = UA + UB;
-    constexpr int NM = 2 * 4 * MI * NI;  // MFMAs per chunk
+    constexpr int NM = (BK / 8) * 4 * MI * NI;  // MFMAs per chunk
     constexpr int LS = NM / 4 / NU > 0 ? NM / 4 / NU : 1;
     constexpr int SQ0 = NM * 5 / 8;
     auto hook = [&](int q, int64_t kn, int nxt) __attribute__((always_inline)) {
         if (q % LS == 0 && q / LS < NU) {
             const int x = q / LS;
             if (x < UA)
-                load_unit<BM, !TA, RAGGED, AL>(ra[x], x, A, m0, p.sam, p.sak, p.M, p.K, kn, t);
+                load_unit<BK, BM, !TA, RAGGED, AL>(ra[x], x, A, m0, p.sam, p.sak, p.M, p.K, kn,
+                                                   t);
             else
-                load_unit<BN, TB, RAGGED, AL>(rb[x - UA], x - UA, B, n0, p.sbn, p.sbk, p.N, p.K,
-                                              kn, t);
+                load_unit<BK, BN, TB, RAGGED, AL>(rb[x - UA], x - UA, B, n0, p.sbn, p.sbk, p.N,
+                                                  p.K, kn, t);
         }
         if (q >= SQ0 && (q - SQ0) % LS == 0 && (q - SQ0) / LS < NU) {
             const int x = (q - SQ0) / LS;
             float *sa = lds + nxt * STAGE_F;
             if (x < UA)
-                store_unit<BM, !TA>(ra, x, sa, t);
+                store_unit<BK, BM, !TA>(ra, x, sa, t);
             else
-                store_unit<BN, TB>(rb, x - UA, sa + A_F, t);
+                store_unit<BK, BN, TB>(rb, x - UA, sa + A_F, t);
         }
     };
     auto is_hook = [&](int q) __attribute__((always_inline)) {
@@ -216,7 +227,7 @@ __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t gr
         const float *sa = lds + stage * STAGE_F + (wm * WM + fr) * ROW_F;
         const float *sb = lds + stage * STAGE_F + A_F + (wn * WN + fr) * ROW_F;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < BK / 8; ++u) {
             f32x4 fa[MI], fb[NI];
 #pragma unroll
             for (int i = 0; i < MI; ++i)
@@ -271,52 +282,57 @@ __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t gr
     }
 }
 
-template <int OUT, int BM, int BN, bool TA, bool TB>
+template <int OUT, int T, int BK, bool TA, bool TB>
 hipError_t launch_tile(const GemmArgs &a, bool ragged, bool aligned, hipStream_t s)
 {
-    const int64_t gm = cdiv(a.M, BM), gn = cdiv(a.N, BN);
+    const int64_t gm = cdiv(a.M, T), gn = cdiv(a.N, T);
     const int64_t tiles = gm * gn;
     if (tiles > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     if (!aligned)
-        hipLaunchKernelGGL((gemm_mfma32_kernel<OUT, BM, BN, true, TA, TB, false>),
+        hipLaunchKernelGGL((gemm_mfma32_kernel<OUT, T, T, BK, true, TA, TB, false>),
                            dim3((unsigned)tiles), dim3(256), 0, s, a, gm, gn);
     else if (ragged)
-        hipLaunchKernelGGL((gemm_mfma32_kernel<OUT, BM, BN, true, TA, TB>), dim3((unsigned)tiles),
-                           dim3(256), 0, s, a, gm, gn);
+        hipLaunchKernelGGL((gemm_mfma32_kernel<OUT, T, T, BK, true, TA, TB>),
+                           dim3((unsigned)tiles), dim3(256), 0, s, a, gm, gn);
     else
-        hipLaunchKernelGGL((gemm_mfma32_kernel<OUT, BM, BN, false, TA, TB>), dim3((unsigned)tiles),
-                           dim3(256), 0, s, a, gm, gn);
+        hipLaunchKernelGGL((gemm_mfma32_kernel<OUT, T, T, BK, false, TA, TB>),
+                           dim3((unsigned)tiles), dim3(256), 0, s, a, gm, gn);
     return hipGetLastError();
 }
 
-template <int OUT, int T>
+template <int OUT, int T, int BK>
 hipError_t dispatch_layout(const GemmArgs &a, int layout, bool ragged, bool aligned,
                            hipStream_t s)
 {
     switch (layout) {
-    case 0: return launch_tile<OUT, T, T, false, false>(a, ragged, aligned, s);
-    case DTM_LAYOUT_A_M_CONTIG: return launch_tile<OUT, T, T, true, false>(a, ragged, aligned, s);
-    case DTM_LAYOUT_B_K_CONTIG: return launch_tile<OUT, T, T, false, true>(a, ragged, aligned, s);
+    case 0: return launch_tile<OUT, T, BK, false, false>(a, ragged, aligned, s);
+    case DTM_LAYOUT_A_M_CONTIG:
+        return launch_tile<OUT, T, BK, true, false>(a, ragged, aligned, s);
+    case DTM_LAYOUT_B_K_CONTIG:
+        return launch_tile<OUT, T, BK, false, true>(a, ragged, aligned, s);
     case DTM_LAYOUT_A_M_CONTIG | DTM_LAYOUT_B_K_CONTIG:
-        return launch_tile<OUT, T, T, true, true>(a, ragged, aligned, s);
+        return launch_tile<OUT, T, BK, true, true>(a, ragged, aligned, s);
     }
     return hipErrorInvalidValue;
 }
 
+// (tile, chunk depth): (256, 32), (256, 16) or (128, 16).
 template <int OUT>
-hipError_t dispatch_tile(const GemmArgs &a, int tile, int layout, bool ragged, bool aligned,
-                         hipStream_t s)
+hipError_t dispatch_tile(const GemmArgs &a, int tile, int bk, int layout, bool ragged,
+                         bool aligned, hipStream_t s)
 {
-    return tile == 256 ? dispatch_layout<OUT, 256>(a, layout, ragged, aligned, s)
-                       : dispatch_layout<OUT, 128>(a, layout, ragged, aligned, s);
+    if (tile == 256)
+        return bk == 32 ? dispatch_layout<OUT, 256, 32>(a, layout, ragged, aligned, s)
+                        : dispatch_layout<OUT, 256, 16>(a, layout, ragged, aligned, s);
+    return dispatch_layout<OUT, 128, 16>(a, layout, ragged, aligned, s);
 }
 
 }  // namespace
 
 bool mfma32_has_config(int bm, int bn, int bk)
 {
-    return bk == BK && bm == bn && (bm == 128 || bm == 256);
+    return bm == bn && ((bm == 256 && (bk == 16 || bk == 32)) || (bm == 128 && bk == 16));
 }
 
 hipError_t launch_mfma32(const GemmArgs &a, int out, int bm, int bn, int bk, int layout,
@@ -325,9 +341,9 @@ hipError_t launch_mfma32(const GemmArgs &a, int out, int bm, int bn, int bk, int
     if (!mfma32_has_config(bm, bn, bk))
         return hipErrorInvalidConfiguration;
     switch (out) {
-    case DTM_F32: return dispatch_tile<DTM_F32>(a, bm, layout, ragged, aligned, s);
-    case DTM_F16: return dispatch_tile<DTM_F16>(a, bm, layout, ragged, aligned, s);
-    case DTM_BF16: return dispatch_tile<DTM_BF16>(a, bm, layout, ragged, aligned, s);
+    case DTM_F32: return dispatch_tile<DTM_F32>(a, bm, bk, layout, ragged, aligned, s);
+    case DTM_F16: return dispatch_tile<DTM_F16>(a, bm, bk, layout, ragged, aligned, s);
+    case DTM_BF16: return dispatch_tile<DTM_BF16>(a, bm, bk, layout, ragged, aligned, s);
     }
     return hipErrorInvalidValue;
 }

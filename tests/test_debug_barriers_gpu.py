@@ -48,6 +48,10 @@ CASES = [
      dict(kernel=MF16, block_m=128, block_n=128, block_k=64)),
     ("fp32 MFMA 256", 1024, 512, 512, "f32", "f32", "NN",
      dict(kernel=MF32, block_m=256, block_n=256, block_k=16)),
+    ("fp32 MFMA 256 x 32 TT", 768, 512, 1024, "f32", "f32", "TT",
+     dict(kernel=MF32, block_m=256, block_n=256, block_k=32)),
+    ("fp32 MFMA 256 x 32 ragged", 600, 520, 1000, "f32", "f32", "NN",
+     dict(kernel=MF32, block_m=256, block_n=256, block_k=32)),
     ("fp32 MFMA 128 ragged", 300, 260, 200, "f32", "f32", "NT",
      dict(kernel=MF32, block_m=128, block_n=128, block_k=16)),
     ("generic", 200, 136, 300, "f32", "f32", "TN",

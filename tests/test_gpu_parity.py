@@ -732,13 +732,13 @@ def test_mfma_f32_unaligned_exact(layout):
     for n, (M, N, K, extra, off) in enumerate(cases):
         outd = ["f32", "f16", "bf16"][n % 3]
         p = _unaligned_f32_problem(M, N, K, outd, 660 + n, layout[0], layout[1], extra, off)
-        for tile in (128, 256):
+        for tile, bk in ((128, 16), (256, 16), (256, 32)):
             plan = {}
-            c, untouched = run(p, config=dict(kernel=MF32, block_m=tile, block_n=tile, block_k=16),
+            c, untouched = run(p, config=dict(kernel=MF32, block_m=tile, block_n=tile, block_k=bk),
                                c_pad=2 if n % 2 else 0, plan=plan)
             assert plan["status"] == 0 and plan["layout"] == LAYOUT_BITS[layout], plan
-            compare(p, c, exact=True,
-                    label=f"mfma_f32 unaligned {tile} {layout} {M}x{N}x{K}+{extra}@{off}->{outd}")
+            compare(p, c, exact=True, label=f"mfma_f32 unaligned {tile}x{bk} {layout} "
+                    f"{M}x{N}x{K}+{extra}@{off}->{outd}")
             assert untouched
 
 
@@ -757,17 +757,20 @@ def test_mfma_f32_exact_and_random(layout):
         assert plan["layout"] == LAYOUT_BITS[layout], plan
         compare(p, c, exact=True, label=f"mfma_f32 {layout} {M}x{N}x{K}->{outd}")
         assert untouched
-    # the 256-wide tile (the selector's choice for large full rounds), forced
+    # the 256-wide tile (the selector's choice for large full rounds), forced,
+    # with 16- and 32-deep chunks
     for n, (M, N, K) in enumerate([(256, 256, 16), (512, 768, 96), (257, 513, 49),
-                                   (300, 260, 1000)]):
+                                   (300, 260, 1000), (256, 512, 32), (512, 256, 80)]):
         outd = ["f32", "bf16", "f16"][n % 3]
         p = _padded_f32_problem(M, N, K, outd, 640 + n, layout[0], layout[1])
-        plan = {}
-        c, untouched = run(p, config=dict(kernel=MF32, block_m=256, block_n=256, block_k=16),
-                           c_pad=2 if n % 2 else 0, plan=plan)
-        assert plan["block_m"] == 256 and plan["layout"] == LAYOUT_BITS[layout], plan
-        compare(p, c, exact=True, label=f"mfma_f32 256 {layout} {M}x{N}x{K}->{outd}")
-        assert untouched
+        for bk in (16, 32):
+            plan = {}
+            c, untouched = run(p, config=dict(kernel=MF32, block_m=256, block_n=256, block_k=bk),
+                               c_pad=2 if n % 2 else 0, plan=plan)
+            assert (plan["block_m"], plan["block_k"]) == (256, bk), plan
+            assert plan["layout"] == LAYOUT_BITS[layout], plan
+            compare(p, c, exact=True, label=f"mfma_f32 256x{bk} {layout} {M}x{N}x{K}->{outd}")
+            assert untouched
     for n, (M, N, K) in enumerate([(1024, 1024, 1024), (1000, 600, 776)]):
         p = W.random_problem(M, N, K, "f32", "f32", ("normal", 0.0, 1.0), seed=650 + n,
                              a_layout=layout[0], b_layout=layout[1])

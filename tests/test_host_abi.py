@@ -241,10 +241,20 @@ def test_fp32_selector():
         st, p = plan(M, N, K, ind=F32, outd=F32, **big)
         assert st == 0 and p["kernel_name"] == "mfma_f32" and p["block_m"] == tile, (M, N, K, p)
         assert (p["grid_m"], p["grid_n"]) == (-(-M // tile), -(-N // tile))
-    for bm, ok in [(256, True), (128, True), (64, False)]:
+    for bm, bk, ok in [(256, 16, True), (256, 32, True), (128, 16, True), (128, 32, False),
+                       (64, 16, False), (256, 64, False)]:
         st, p = plan(1000, 1000, 1000, ind=F32, config=dict(kernel=dtm.DTM_KERNEL_MFMA_F32,
-                                                            block_m=bm, block_n=bm, block_k=16))
-        assert (st == 0) == ok and (not ok or p["block_m"] == bm), (bm, st, p)
+                                                            block_m=bm, block_n=bm, block_k=bk))
+        assert (st == 0) == ok and (not ok or (p["block_m"], p["block_k"]) == (bm, bk)), \
+            (bm, bk, st, p)
+    # chunk depth: 32 at 256 x 256 when K is a multiple of 32, else 16
+    for M, N, K, tile, bk, ragged in [(4096, 4096, 4096, 256, 32, 0), (8192, 8192, 8192, 256, 32, 0),
+                                      (4096, 4096, 4112, 256, 16, 0), (4096, 4096, 4100, 256, 16, 1),
+                                      (3000, 3000, 3008, 128, 16, 1), (1024, 1024, 1024, 128, 16, 0)]:
+        st, p = plan(M, N, K, ind=F32, outd=F32, **big)
+        assert st == 0 and (p["block_m"], p["block_k"], p["ragged"]) == (tile, bk, ragged), \
+            (M, N, K, p)
+        assert p["k_iters"] == -(-K // bk)
 
 
 def test_fp16acc_control_is_forced_only():
