@@ -501,30 +501,41 @@ int64_t pick_split(const Call &c, int layout, int64_t tiles, int tile, int64_t c
     return 1;
 }
 
-// fp32 on the matrix cores: 256 x 256 tiles (one workgroup per CU) when
-// their round fill, times their measured rate against 128 x 128 tiles (three
-// workgroups per CU; 4096^3 134 against 121 TFLOP/s), beats the 128-wide
-// tiles' fill: 4096^3 and 8192^3 take 256, 3000^3 (144 tiles of 256 for 256
-// CUs) stays on 128.
-constexpr double F32_RATE_256 = 1.11;
+// fp32 on the matrix cores: the tile (256, 192 or 128 wide) whose rounds
+// over the CUs take the least time, each round priced against a round of
+// 256-wide tiles (one workgroup per CU) over the same K.  From timings at
+// 2048^3-8192^3 (the model's times are off by up to 16%, but it picked the
+// fastest of the three tiles at every size tried): a round of 192-wide tiles
+// (one per CU) costs 0.66; the 128-wide tile runs up to three workgroups per CU, and
+// a round with one, two or three of them per CU costs 0.273, 0.548 or 0.877.
+// 4096^3 and 8192^3 take 256, 3000^3 192 (114 against 86 TFLOP/s on 128),
+// 2048^3, 4608^3 and 6000^3 128.
+constexpr double F32_ROUND_192 = 0.66;
+constexpr double F32_ROUND_128[3] = {0.273, 0.548, 0.877};
 
-bool prefer_f32_256(const Call &c)
+int32_t f32_tile(const Call &c)
 {
-    const int64_t t256 = cdiv(c.M, 256) * cdiv(c.N, 256), t128 = cdiv(c.M, 128) * cdiv(c.N, 128);
-    const double fill256 = static_cast<double>(t256) / static_cast<double>(cdiv(t256, CUS) * CUS);
-    const double fill128 =
-        static_cast<double>(t128) / static_cast<double>(cdiv(t128, 3 * CUS) * 3 * CUS);
-    return F32_RATE_256 * fill256 > fill128;
+    const int64_t t256 = cdiv(c.M, 256) * cdiv(c.N, 256), t192 = cdiv(c.M, 192) * cdiv(c.N, 192);
+    const int64_t t128 = cdiv(c.M, 128) * cdiv(c.N, 128);
+    const double cost256 = static_cast<double>(cdiv(t256, CUS));
+    const double cost192 = static_cast<double>(cdiv(t192, CUS)) * F32_ROUND_192;
+    const int64_t rem = t128 % (3 * CUS);
+    const double cost128 = static_cast<double>(t128 / (3 * CUS)) * F32_ROUND_128[2] +
+                           (rem == 0 ? 0.0 : F32_ROUND_128[cdiv(rem, CUS) - 1]);
+    if (cost256 <= cost192 && cost256 <= cost128)
+        return 256;
+    return cost192 < cost128 ? 192 : 128;
 }
 
 // fp32 chunk depth: 32 at 256 x 256 when K is a multiple of 32 (one barrier
 // and one refill round per 32 k; 4096^3 and 8192^3 about 1% faster, in 144
 // KiB of LDS), else 16 -- a K off 32 would send every chunk through the
-// range-checked loads.  128 x 128 keeps 16 (32 there holds two workgroups
-// per CU instead of three and cost 5% at 3000^3).
+// range-checked loads.  192 x 192 always takes 32 (at 16 an operand tile is
+// an odd number of 16-byte units per thread); 128 x 128 keeps 16 (32 there
+// holds two workgroups per CU instead of three and cost 5% at 3000^3).
 int32_t f32_block_k(const Call &c, int32_t tile)
 {
-    return tile == 256 && c.K % 32 == 0 ? 32 : 16;
+    return tile == 192 || (tile == 256 && c.K % 32 == 0) ? 32 : 16;
 }
 
 // The pipelined kernel's interior form at tile 256 runs with 4 waves of
@@ -685,7 +696,7 @@ int make_plan(const Call &c, const dtm_tile_config *force, uint64_t ws_budget, d
             return DTM_ERR_CONFIG;
         if (forced_dims && !dtm::mfma32_has_config(force->block_m, force->block_n, force->block_k))
             return DTM_ERR_CONFIG;
-        p.block_m = p.block_n = forced_dims ? force->block_m : (prefer_f32_256(c) ? 256 : 128);
+        p.block_m = p.block_n = forced_dims ? force->block_m : f32_tile(c);
         p.block_k = forced_dims ? force->block_k : f32_block_k(c, p.block_m);
         p.threads = 256;
         p.layout = layout32;

@@ -11,12 +11,14 @@
 //  * 256 threads = 4 wave64s in 2 x 2; each wave owns (BM/2) x (BN/2) of C
 //    as 32 x 32 tiles of v_mfma_f32_32x32x2_f32 (one fp32 of A and one of B
 //    per lane per instruction, 16 fp32 results per lane).  Tiles of 128 x 128
-//    (64 x 64 per wave, three workgroups per CU) or 256 x 256 (128 x 128 per
-//    wave in the accumulation registers, one workgroup per CU, half the LDS
-//    reads per MFMA: 4096^3 121 -> 134 TFLOP/s, 8192^3 126 -> 132).
-//  * K-chunks 16 deep (32 deep at 256 x 256 unless a plan names 16: 144 KiB
-//    of LDS, one barrier and one refill round per 32 k; 4096^3 and 8192^3
-//    gained about 1%), two LDS stages, loaded through registers one chunk
+//    (64 x 64 per wave, three workgroups per CU), 192 x 192 (96 x 96 per
+//    wave, one per CU: for grids the other two fill poorly, 3000^3 86 -> 114
+//    TFLOP/s) or 256 x 256 (128 x 128 per wave in the accumulation
+//    registers, one workgroup per CU, half the LDS reads per MFMA of the
+//    128-wide tile: 4096^3 121 -> 134 TFLOP/s, 8192^3 126 -> 132).
+//  * K-chunks 16 deep (32 deep at 192 x 192, and at 256 x 256 unless a plan
+//    names 16: 144 KiB of LDS, one barrier and one refill round per 32 k;
+//    4096^3 and 8192^3 gained about 1%), two LDS stages, loaded through registers one chunk
 //    ahead.  A K-contiguous operand (A row-major, or B given as the
 //    transpose of an N x K array) goes to LDS as it is; an M- or
 //    N-contiguous one is loaded along its contiguous axis and each thread
@@ -151,8 +153,10 @@ __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t gr
     constexpr int ROW_F = row_floats<BK>();
     constexpr int A_F = BM * ROW_F;                 // floats of one A stage
     constexpr int STAGE_F = (BM + BN) * ROW_F;
-    static_assert(BM % 128 == 0 && BN % 128 == 0, "operand tiles split over 256 threads");
     static_assert(BK == 16 || BK == 32, "chunks of 16 or 32 k");
+    static_assert(BM % 64 == 0 && BN % 64 == 0 && units<BK, BM>() % 2 == 0 &&
+                      units<BK, BN>() % 2 == 0 && BM * BK % 1024 == 0 && BN * BK % 1024 == 0,
+                  "operand tiles split over 256 threads in pairs of 16-byte units");
 
     __shared__ __attribute__((aligned(16))) float lds[2 * STAGE_F];
 
@@ -346,7 +350,7 @@ hipError_t dispatch_layout(const GemmArgs &a, int layout, bool ragged, bool alig
     return hipErrorInvalidValue;
 }
 
-// (tile, chunk depth): (256, 32), (256, 16) or (128, 16).
+// (tile, chunk depth): (256, 32), (256, 16), (192, 32) or (128, 16).
 template <int OUT>
 hipError_t dispatch_tile(const GemmArgs &a, int tile, int bk, int layout, bool ragged,
                          bool aligned, hipStream_t s)
@@ -354,6 +358,8 @@ hipError_t dispatch_tile(const GemmArgs &a, int tile, int bk, int layout, bool r
     if (tile == 256)
         return bk == 32 ? dispatch_layout<OUT, 256, 32>(a, layout, ragged, aligned, s)
                         : dispatch_layout<OUT, 256, 16>(a, layout, ragged, aligned, s);
+    if (tile == 192)
+        return dispatch_layout<OUT, 192, 32>(a, layout, ragged, aligned, s);
     return dispatch_layout<OUT, 128, 16>(a, layout, ragged, aligned, s);
 }
 
@@ -361,7 +367,8 @@ hipError_t dispatch_tile(const GemmArgs &a, int tile, int bk, int layout, bool r
 
 bool mfma32_has_config(int bm, int bn, int bk)
 {
-    return bm == bn && ((bm == 256 && (bk == 16 || bk == 32)) || (bm == 128 && bk == 16));
+    return bm == bn && ((bm == 256 && (bk == 16 || bk == 32)) || (bm == 192 && bk == 32) ||
+                        (bm == 128 && bk == 16));
 }
 
 hipError_t launch_mfma32(const GemmArgs &a, int out, int bm, int bn, int bk, int layout,

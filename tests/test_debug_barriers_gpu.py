@@ -52,6 +52,8 @@ CASES = [
      dict(kernel=MF32, block_m=256, block_n=256, block_k=32)),
     ("fp32 MFMA 256 x 32 ragged", 600, 520, 1000, "f32", "f32", "NN",
      dict(kernel=MF32, block_m=256, block_n=256, block_k=32)),
+    ("fp32 MFMA 192 ragged", 400, 580, 1000, "f32", "bf16", "NT",
+     dict(kernel=MF32, block_m=192, block_n=192, block_k=32)),
     ("fp32 MFMA 128 ragged", 300, 260, 200, "f32", "f32", "NT",
      dict(kernel=MF32, block_m=128, block_n=128, block_k=16)),
     ("generic", 200, 136, 300, "f32", "f32", "TN",

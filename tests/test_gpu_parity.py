@@ -732,7 +732,7 @@ def test_mfma_f32_unaligned_exact(layout):
     for n, (M, N, K, extra, off) in enumerate(cases):
         outd = ["f32", "f16", "bf16"][n % 3]
         p = _unaligned_f32_problem(M, N, K, outd, 660 + n, layout[0], layout[1], extra, off)
-        for tile, bk in ((128, 16), (256, 16), (256, 32)):
+        for tile, bk in ((128, 16), (192, 32), (256, 16), (256, 32)):
             plan = {}
             c, untouched = run(p, config=dict(kernel=MF32, block_m=tile, block_n=tile, block_k=bk),
                                c_pad=2 if n % 2 else 0, plan=plan)
@@ -758,20 +758,21 @@ def test_mfma_f32_exact_and_random(layout):
         compare(p, c, exact=True, label=f"mfma_f32 {layout} {M}x{N}x{K}->{outd}")
         assert untouched
     # the 256-wide tile (the selector's choice for large full rounds), forced,
-    # with 16- and 32-deep chunks
+    # with 16- and 32-deep chunks, and the 192-wide tile
     for n, (M, N, K) in enumerate([(256, 256, 16), (512, 768, 96), (257, 513, 49),
-                                   (300, 260, 1000), (256, 512, 32), (512, 256, 80)]):
+                                   (300, 260, 1000), (256, 512, 32), (512, 256, 80),
+                                   (384, 576, 64), (385, 193, 40)]):
         outd = ["f32", "bf16", "f16"][n % 3]
         p = _padded_f32_problem(M, N, K, outd, 640 + n, layout[0], layout[1])
-        for bk in (16, 32):
+        for tile, bk in ((256, 16), (256, 32), (192, 32)):
             plan = {}
-            c, untouched = run(p, config=dict(kernel=MF32, block_m=256, block_n=256, block_k=bk),
+            c, untouched = run(p, config=dict(kernel=MF32, block_m=tile, block_n=tile, block_k=bk),
                                c_pad=2 if n % 2 else 0, plan=plan)
-            assert (plan["block_m"], plan["block_k"]) == (256, bk), plan
+            assert (plan["block_m"], plan["block_k"]) == (tile, bk), plan
             assert plan["layout"] == LAYOUT_BITS[layout], plan
-            compare(p, c, exact=True, label=f"mfma_f32 256x{bk} {layout} {M}x{N}x{K}->{outd}")
+            compare(p, c, exact=True, label=f"mfma_f32 {tile}x{bk} {layout} {M}x{N}x{K}->{outd}")
             assert untouched
-    for n, (M, N, K) in enumerate([(1024, 1024, 1024), (1000, 600, 776)]):
+    for n, (M, N, K) in enumerate([(1024, 1024, 1024), (1000, 600, 776), (3000, 2900, 200)]):
         p = W.random_problem(M, N, K, "f32", "f32", ("normal", 0.0, 1.0), seed=650 + n,
                              a_layout=layout[0], b_layout=layout[1])
         plan = {}

@@ -233,24 +233,28 @@ def test_fp32_selector():
     assert st == dtm.DTM_ERR_CONFIG
     st, p = plan(1024, 1024, 1000, ind=F16, config=dict(kernel=dtm.DTM_KERNEL_MFMA_F32))
     assert st == dtm.DTM_ERR_CONFIG
-    # 256-wide tiles (one workgroup per CU) where their round fill, at 1.11x
-    # the rate, beats the 128-wide tiles' (three workgroups per CU)
+    # the tile whose rounds over the 256 CUs cost least: 256 and 192 wide run
+    # one workgroup per CU, 128 wide up to three
     big = dict(A=1 << 40, B=2 << 40, C=3 << 40)
-    for M, N, K, tile in [(4096, 4096, 4096, 256), (8192, 8192, 8192, 256), (3000, 3000, 3000, 128),
-                          (1024, 1024, 1024, 128), (4096, 8192, 2048, 256), (2048, 2048, 8192, 128)]:
+    for M, N, K, tile in [(4096, 4096, 4096, 256), (8192, 8192, 8192, 256), (3000, 3000, 3000, 192),
+                          (1024, 1024, 1024, 128), (4096, 8192, 2048, 256), (2048, 2048, 8192, 128),
+                          (6000, 6000, 6000, 128), (4608, 4608, 4608, 128), (3072, 3072, 512, 192),
+                          (2900, 3000, 1000, 192)]:
         st, p = plan(M, N, K, ind=F32, outd=F32, **big)
         assert st == 0 and p["kernel_name"] == "mfma_f32" and p["block_m"] == tile, (M, N, K, p)
         assert (p["grid_m"], p["grid_n"]) == (-(-M // tile), -(-N // tile))
-    for bm, bk, ok in [(256, 16, True), (256, 32, True), (128, 16, True), (128, 32, False),
-                       (64, 16, False), (256, 64, False)]:
+    for bm, bk, ok in [(256, 16, True), (256, 32, True), (192, 32, True), (192, 16, False),
+                       (128, 16, True), (128, 32, False), (64, 16, False), (256, 64, False)]:
         st, p = plan(1000, 1000, 1000, ind=F32, config=dict(kernel=dtm.DTM_KERNEL_MFMA_F32,
                                                             block_m=bm, block_n=bm, block_k=bk))
         assert (st == 0) == ok and (not ok or (p["block_m"], p["block_k"]) == (bm, bk)), \
             (bm, bk, st, p)
-    # chunk depth: 32 at 256 x 256 when K is a multiple of 32, else 16
+    # chunk depth: 32 at 192 x 192, and at 256 x 256 when K is a multiple of
+    # 32; else 16
     for M, N, K, tile, bk, ragged in [(4096, 4096, 4096, 256, 32, 0), (8192, 8192, 8192, 256, 32, 0),
                                       (4096, 4096, 4112, 256, 16, 0), (4096, 4096, 4100, 256, 16, 1),
-                                      (3000, 3000, 3008, 128, 16, 1), (1024, 1024, 1024, 128, 16, 0)]:
+                                      (3000, 3000, 3008, 192, 32, 1), (3072, 3072, 4112, 192, 32, 1),
+                                      (3072, 3072, 4096, 192, 32, 0), (1024, 1024, 1024, 128, 16, 0)]:
         st, p = plan(M, N, K, ind=F32, outd=F32, **big)
         assert st == 0 and (p["block_m"], p["block_k"], p["ragged"]) == (tile, bk, ragged), \
             (M, N, K, p)
