@@ -506,10 +506,11 @@ int64_t pick_split(const Call &c, int layout, int64_t tiles, int tile, int64_t c
 // 256-wide tiles (one workgroup per CU) over the same K.  From timings at
 // 2048^3-8192^3 (the model's times are off by up to 16%, but it picked the
 // fastest of the three tiles at every size tried): a round of 192-wide tiles
-// (one per CU) costs 0.66; the 128-wide tile runs up to three workgroups per CU, and
-// a round with one, two or three of them per CU costs 0.273, 0.548 or 0.877.
-// 4096^3 and 8192^3 take 256, 3000^3 192 (114 against 86 TFLOP/s on 128),
-// 2048^3, 4608^3 and 6000^3 128.
+// (one per CU) costs 0.66; the interior 128-wide form runs one workgroup per
+// CU at 0.273 a round, the range-checked one up to three, and a round with
+// one, two or three of them per CU costs 0.273, 0.548 or 0.877.  4096^3 and
+// 8192^3 take 256, 3000^3 192 (114 against 86 TFLOP/s on 128), 2048^3,
+// 4608^3 and 6000^3 128.
 constexpr double F32_ROUND_192 = 0.66;
 constexpr double F32_ROUND_128[3] = {0.273, 0.548, 0.877};
 
@@ -519,9 +520,12 @@ int32_t f32_tile(const Call &c)
     const int64_t t128 = cdiv(c.M, 128) * cdiv(c.N, 128);
     const double cost256 = static_cast<double>(cdiv(t256, CUS));
     const double cost192 = static_cast<double>(cdiv(t192, CUS)) * F32_ROUND_192;
+    const bool interior128 = c.M % 128 == 0 && c.N % 128 == 0 && c.K % 16 == 0;
     const int64_t rem = t128 % (3 * CUS);
-    const double cost128 = static_cast<double>(t128 / (3 * CUS)) * F32_ROUND_128[2] +
-                           (rem == 0 ? 0.0 : F32_ROUND_128[cdiv(rem, CUS) - 1]);
+    const double cost128 =
+        interior128 ? static_cast<double>(cdiv(t128, CUS)) * F32_ROUND_128[0]
+                    : static_cast<double>(t128 / (3 * CUS)) * F32_ROUND_128[2] +
+                          (rem == 0 ? 0.0 : F32_ROUND_128[cdiv(rem, CUS) - 1]);
     if (cost256 <= cost192 && cost256 <= cost128)
         return 256;
     return cost192 < cost128 ? 192 : 128;

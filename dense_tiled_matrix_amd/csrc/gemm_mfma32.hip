@@ -158,7 +158,13 @@ __global__ __launch_bounds__(256) void gemm_mfma32_kernel(GemmArgs p, int64_t gr
                       units<BK, BN>() % 2 == 0 && BM * BK % 1024 == 0 && BN * BK % 1024 == 0,
                   "operand tiles split over 256 threads in pairs of 16-byte units");
 
-    __shared__ __attribute__((aligned(16))) float lds[2 * STAGE_F];
+    // The interior 128 x 128 form reserves 88 KiB of LDS so that it runs one
+    // workgroup per CU: three of them per CU ran slower than one (4096^3 on
+    // 128-wide tiles 104 against 135 TFLOP/s, 4608^3 109 against 113), while
+    // the range-checked form gains from three (6000^3 121 against 101).
+    constexpr int LDS_F = BM == 128 && !RAGGED ? 22528 : 2 * STAGE_F;
+    static_assert(LDS_F >= 2 * STAGE_F, "two stages");
+    __shared__ __attribute__((aligned(16))) float lds[LDS_F];
 
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
