@@ -536,7 +536,8 @@ int32_t f32_tile(const Call &c)
 // KiB of LDS), else 16 -- a K off 32 would send every chunk through the
 // range-checked loads.  192 x 192 always takes 32 (at 16 an operand tile is
 // an odd number of 16-byte units per thread); 128 x 128 keeps 16 (32 there
-// holds two workgroups per CU instead of three and cost 5% at 3000^3).
+// leaves the range-checked form two workgroups per CU instead of three and
+// cost it 5% at 3000^3).
 int32_t f32_block_k(const Call &c, int32_t tile)
 {
     return tile == 192 || (tile == 256 && c.K % 32 == 0) ? 32 : 16;
