@@ -279,7 +279,10 @@ uint64_t gemm_workspace_reserved(void *stream);
  * array (no allocation); no call allocates, frees or waits for the GPU.
  * Every call on a GPU uses that GPU's one array: calls that overlap on one
  * GPU (other streams, other threads) race on it and must be serialised by
- * the caller.  Results equal gemm_ex()'s with the same plan.  Returns a
+ * the caller.  Results equal gemm_ex()'s with the same plan.  The HIP
+ * runtime still takes device memory for a kernel's code on that kernel's
+ * first launch in the process (as through any entry point): launch each
+ * plan once beforehand where device memory must not move.  Returns a
  * dtm_status.
  */
 int gemm_ex_noalloc(int64_t M, int64_t N, int64_t K,
