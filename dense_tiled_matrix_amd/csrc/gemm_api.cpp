@@ -258,6 +258,31 @@ int mfma_layout(const Call &c)
 }
 bool is16(const Call &c) { return c.in == DTM_F16 || c.in == DTM_BF16; }
 
+// fp16/bf16 views that mfma_layout() turns away but whose chunks still start
+// on 4-byte boundaries (bases 4-byte aligned, the non-unit stride of each
+// operand even): the register-staged kernel's range-checked form reads them
+// with 16-byte copies at 4-byte alignment.  Returns the layout bits, or -1.
+int mfma16_unaligned_layout(const Call &c)
+{
+    if (!is16(c) || (reinterpret_cast<uintptr_t>(c.A) & 3) ||
+        (reinterpret_cast<uintptr_t>(c.B) & 3))
+        return -1;
+    int layout = 0;
+    if (c.sak == 1 && c.sam % 2 == 0)
+        ;
+    else if (c.sam == 1 && c.sak % 2 == 0)
+        layout |= DTM_LAYOUT_A_M_CONTIG;
+    else
+        return -1;
+    if (c.sbn == 1 && c.sbk % 2 == 0)
+        ;
+    else if (c.sbk == 1 && c.sbn % 2 == 0)
+        layout |= DTM_LAYOUT_B_K_CONTIG;
+    else
+        return -1;
+    return layout;
+}
+
 // The fp32 matrix-core kernel also reads each operand along its unit-stride
 // axis, but its range-checked form takes views off 16-byte boundaries too
 // (element loads), so any fp32 view with a unit stride along one axis of
@@ -601,7 +626,9 @@ int make_plan(const Call &c, const dtm_tile_config *force, uint64_t ws_budget, d
     // Every MFMA kernel reads all four operand layouts.
     const int layout = mfma_layout(c);
     const bool dma = c.K > 0 && dma_any(c, layout, 1);  // the pipelined kernel, either form
-    const bool fast16 = is16(c) && layout >= 0;
+    // views off 16-byte boundaries: the register-staged kernel only
+    const int layout16u = layout < 0 ? mfma16_unaligned_layout(c) : -1;
+    const bool fast16 = is16(c) && (layout >= 0 || layout16u >= 0);
     const int layout32 = c.in == DTM_F32 ? mfma32_layout(c, nullptr) : -1;
     const bool fast32 = layout32 >= 0;
     p.fast_path = fast16 || fast32 ? 1 : 0;
@@ -682,7 +709,7 @@ int make_plan(const Call &c, const dtm_tile_config *force, uint64_t ws_budget, d
             p.dp_rows = r;
         }
         p.threads = 256;  // the pipelined kernel's is settled below
-        p.layout = layout;
+        p.layout = layout >= 0 ? layout : layout16u;
     } else if (kernel == DTM_KERNEL_MFMA_F16_WAVEK) {
         // forced only: 128 x 128 x 32 tiles, 4 waves, the forced split or none
         const int64_t S = forced_split ? forced_split : 1;
@@ -732,6 +759,8 @@ int make_plan(const Call &c, const dtm_tile_config *force, uint64_t ws_budget, d
         return DTM_ERR_CONFIG;
     p.kernel = kernel;
     fill_grid(c, p);
+    if (kernel == DTM_KERNEL_MFMA_F16 && layout < 0)
+        p.ragged = 1;  // views off 16-byte boundaries: the range-checked form
     const bool dma_tile = kernel == DTM_KERNEL_MFMA_F16 && p.block_k == 32;
     if (dma_tile) {
         // which form of the pipelined kernel, and how many waves (with

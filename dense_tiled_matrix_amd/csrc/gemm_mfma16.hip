@@ -58,11 +58,17 @@ __device__ __forceinline__ floatx16 mfma(const u32x4 &a, const u32x4 &b, const f
 }
 
 // 16 bytes = 8 consecutive elements at p[0..7]; elements at positions >= valid
-// are zero.  `valid` <= 0 gives all zeros without touching memory.
+// are zero.  `valid` <= 0 gives all zeros without touching memory.  All
+// eight valid: one 16-byte copy, which the compiler emits as one dwordx4
+// load also where p is only 4-byte aligned (views whose leading dimension is
+// even but off a multiple of 8 elements take this form).
 __device__ __forceinline__ u32x4 load8_masked(const uint16_t *p, int64_t valid)
 {
-    if (valid >= 8)
-        return *reinterpret_cast<const u32x4 *>(p);
+    if (valid >= 8) {
+        u32x4 v;
+        __builtin_memcpy(&v, p, sizeof(v));
+        return v;
+    }
     uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e)

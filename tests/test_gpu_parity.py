@@ -696,10 +696,12 @@ def _padded_f32_problem(M, N, K, outd, seed, a_layout, b_layout):
                      name=f"f32{a_layout}{b_layout}{M}x{N}x{K}")
 
 
-def _unaligned_f32_problem(M, N, K, outd, seed, a_layout, b_layout, ld_extra, offset):
+def _unaligned_f32_problem(M, N, K, outd, seed, a_layout, b_layout, ld_extra, offset,
+                           ind="f32"):
     """As _padded_f32_problem, but leading dimensions of cols + ld_extra
-    elements (off 16-byte boundaries for ld_extra % 4 != 0) and each view
-    starting `offset` elements into its NaN-filled buffer."""
+    elements (off 16-byte boundaries unless ld_extra * item size is a
+    multiple of 16) and each view starting `offset` elements into its
+    NaN-filled buffer; `ind` the operands' dtype."""
     rng = np.random.default_rng(seed)
     a = rng.integers(-16, 17, size=(M, K))
     b = rng.integers(-16, 17, size=(K, N))
@@ -709,14 +711,46 @@ def _unaligned_f32_problem(M, N, K, outd, seed, a_layout, b_layout, ld_extra, of
         if layout == "T":
             x = x.T
         ld = x.shape[1] + ld_extra
+        if ind != "f32":
+            # 16-bit views: an even leading dimension off a multiple of 8
+            ld += ld % 2
+            ld += 2 if ld % 8 == 0 else 0
         buf = np.full(offset + x.shape[0] * ld + 8, np.nan)
         view = buf[offset:offset + x.shape[0] * ld].reshape(x.shape[0], ld)
         view[:, :x.shape[1]] = x
         strides = (ld, 1) if layout == "N" else (1, ld)
-        return W.Operand(W.to_bits(buf, "f32"), "f32", rows, cols, offset, *strides)
+        return W.Operand(W.to_bits(buf, ind), ind, rows, cols, offset, *strides)
 
-    return W.Problem(M, N, K, store(a, a_layout), store(b, b_layout), "f32", outd,
-                     name=f"f32u{a_layout}{b_layout}{M}x{N}x{K}")
+    return W.Problem(M, N, K, store(a, a_layout), store(b, b_layout), ind, outd,
+                     name=f"{ind}u{a_layout}{b_layout}{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])
+def test_mfma16_views_off_16_bytes_exact(layout):
+    """fp16/bf16 views whose chunks start on 4-byte but not 16-byte
+    boundaries (even leading dimensions off a multiple of 8 elements, views
+    starting 0, 2 or 6 elements into their buffers) on the register-staged
+    kernel's range-checked form, 16-byte copies at 4-byte alignment: value-
+    exact on integer-valued inputs, nothing outside the views read (NaN
+    padding), at both tiles and through the selector."""
+    cases = [(128, 128, 64, 2, 2), (257, 129, 200, 6, 2), (300, 260, 1000, 2, 6),
+             (64, 500, 78, 6, 6), (512, 256, 96, 2, 0), (1000, 776, 520, 2, 2)]
+    for n, (M, N, K, extra, off) in enumerate(cases):
+        ind = ["bf16", "f16"][n % 2]
+        outd = ["f32", "bf16", "f16"][n % 3]
+        p = _unaligned_f32_problem(M, N, K, outd, 700 + n, layout[0], layout[1], extra, off,
+                                   ind=ind)
+        for cfg in (dict(kernel=dtm.DTM_KERNEL_MFMA_F16, block_m=128, block_n=128, block_k=64),
+                    dict(kernel=dtm.DTM_KERNEL_MFMA_F16, block_m=256, block_n=256, block_k=64),
+                    None):
+            plan = {}
+            c, untouched = run(p, config=cfg, c_pad=2 if n % 2 else 0, plan=plan)
+            assert plan["status"] == 0 and plan["kernel_name"] == "mfma_f16", plan
+            assert (plan["block_k"], plan["ragged"]) == (64, 1), plan
+            assert plan["layout"] == LAYOUT_BITS[layout], plan
+            compare(p, c, exact=True, label=f"mfma_f16 4-byte views {layout} {M}x{N}x{K}"
+                    f"+{extra}@{off} {ind}->{outd} {cfg and cfg['block_m']}")
+            assert untouched
 
 
 @pytest.mark.parametrize("layout", ["NN", "TN", "NT", "TT"])

@@ -147,10 +147,10 @@ def test_selector_measured_workloads():
 @pytest.mark.parametrize("kw,why", [
     (dict(sak=2), "A not K-contiguous"),
     (dict(sbn=3), "B not N-contiguous"),
-    (dict(A=PA + 2), "A base not 16-byte aligned"),
-    (dict(B=PB + 8), "B base not 16-byte aligned"),
-    (dict(sam=1001), "A leading dimension not a multiple of 8 elements"),
-    (dict(sbk=999), "B leading dimension not a multiple of 8 elements"),
+    (dict(A=PA + 2), "A base not 4-byte aligned"),
+    (dict(B=PB + 6), "B base not 4-byte aligned"),
+    (dict(sam=1001), "A leading dimension odd"),
+    (dict(sbk=999), "B leading dimension odd"),
 ])
 def test_fast_path_predicate_falls_back_to_generic(kw, why):
     st, p = plan(1024, 1024, 1000, **kw)
@@ -159,6 +159,30 @@ def test_fast_path_predicate_falls_back_to_generic(kw, why):
     # forcing the MFMA kernel on such a layout is a configuration error
     st, _ = plan(1024, 1024, 1000, config=dict(kernel=dtm.DTM_KERNEL_MFMA_F16), **kw)
     assert st == dtm.DTM_ERR_CONFIG
+
+
+@pytest.mark.parametrize("kw,bits", [
+    (dict(B=PB + 8), 0), (dict(A=PA + 4), 0), (dict(sam=1002), 0), (dict(sbk=1006), 0),
+    (dict(sam=1, sak=1026), dtm.DTM_LAYOUT_A_M_CONTIG),
+    (dict(sbk=1, sbn=1010), dtm.DTM_LAYOUT_B_K_CONTIG),
+])
+def test_fp16_views_off_16_bytes_take_the_register_staged_kernel(kw, bits):
+    """fp16/bf16 views whose chunks start on 4-byte but not 16-byte
+    boundaries run on the register-staged kernel's range-checked form (never
+    on the pipelined or wave-K kernels, whose loads need 16-byte chunks)."""
+    st, p = plan(1024, 1024, 1000, **kw)
+    assert st == 0 and p["kernel_name"] == "mfma_f16" and p["fast_path"] == 1, (kw, p)
+    assert (p["block_k"], p["ragged"], p["split_k"], p["layout"]) == (64, 1, 1, bits), (kw, p)
+    st, p = plan(1024, 1024, 1024, **kw)
+    assert st == 0 and (p["kernel_name"], p["block_k"], p["ragged"]) == ("mfma_f16", 64, 1)
+    for cfg in [dict(kernel=dtm.DTM_KERNEL_MFMA_F16, block_m=128, block_n=128, block_k=32),
+                dict(kernel=dtm.DTM_KERNEL_MFMA_F16, split_k=4),
+                dict(kernel=dtm.DTM_KERNEL_MFMA_F16_WAVEK)]:
+        st, _ = plan(1024, 1024, 1024, config=cfg, **kw)
+        assert st == dtm.DTM_ERR_CONFIG, (kw, cfg)
+    st, p = plan(1024, 1024, 1024, config=dict(kernel=dtm.DTM_KERNEL_MFMA_F16, block_m=128,
+                                                block_n=128, block_k=64), **kw)
+    assert st == 0 and (p["block_m"], p["ragged"]) == (128, 1), (kw, p)
 
 
 def test_selector_transposed_layouts():
@@ -196,10 +220,16 @@ def test_selector_transposed_layouts():
     # ... unless K % 8 != 0: then the register-staged kernel
     st, p = plan(256, 256, 60, sam=64, sbk=1, sbn=64, ind=F16, outd=F32)
     assert st == 0 and p["layout"] == LB and p["block_k"] == 64 and p["block_m"] == 128
-    # other stride not a 16-byte multiple: fp16/bf16 on the generic kernel,
-    # fp32 on the fp32 matrix cores' range-checked form (element loads)
-    for M, N, K, kw, ind in [(4096, 4096, 4096, dict(sam=1, sak=4100), F16),
-                             (4096, 4096, 4096, dict(sbk=1, sbn=4092), BF16)]:
+    # other stride not a 16-byte multiple: fp16/bf16 on the register-staged
+    # kernel's range-checked form when it is even, else on the generic kernel;
+    # fp32 on the fp32 matrix cores' range-checked form
+    for M, N, K, kw, ind, bits in [(4096, 4096, 4096, dict(sam=1, sak=4100), F16, LA),
+                                   (4096, 4096, 4096, dict(sbk=1, sbn=4092), BF16, LB)]:
+        st, p = plan(M, N, K, ind=ind, **big, **kw)
+        assert st == 0 and p["kernel_name"] == "mfma_f16" and p["layout"] == bits, (M, N, K, kw)
+        assert (p["block_k"], p["ragged"]) == (64, 1), (M, N, K, kw, p)
+    for M, N, K, kw, ind in [(4096, 4096, 4096, dict(sam=1, sak=4099), F16),
+                             (4096, 4096, 4096, dict(sbk=1, sbn=4093), BF16)]:
         st, p = plan(M, N, K, ind=ind, **big, **kw)
         assert st == 0 and p["kernel_name"] == "generic" and p["layout"] == 0, (M, N, K, kw)
     for M, N, K, kw, bits in [(257, 129, 193, dict(sam=1, sak=257), LA),
