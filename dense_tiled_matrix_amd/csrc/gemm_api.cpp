@@ -235,7 +235,8 @@ int validate(const Call &c)
 // 16-byte aligned (the base and the leading dimension in bytes).  The same
 // rule a tensor descriptor imposes ("Triton matmul", "Things that break"),
 // used here to pick a kernel rather than to reject the call.  Returns the
-// dtm_layout bits, or -1 when no MFMA layout fits.
+// dtm_layout bits, or -1 when no aligned MFMA layout fits (fp16/bf16 views on
+// 4-byte boundaries: mfma16_unaligned_layout; fp32: mfma32_layout).
 int mfma_layout(const Call &c)
 {
     if ((reinterpret_cast<uintptr_t>(c.A) & 15) || (reinterpret_cast<uintptr_t>(c.B) & 15))

@@ -118,10 +118,12 @@ typedef enum {
 } dtm_kernel;
 
 /* Operand layouts the MFMA kernels read at full speed (bits of
- * dtm_plan.layout).  Each operand must have one unit stride; for fp16/bf16
- * its other stride (the leading dimension) must be a multiple of 16 bytes and
- * its base 16-byte aligned (fp32 views off those boundaries run on the fp32
- * kernel's range-checked form with element loads).  With neither bit set, A
+ * dtm_plan.layout).  Each operand must have one unit stride; for the
+ * pipelined fp16/bf16 kernels its other stride (the leading dimension) must
+ * be a multiple of 16 bytes and its base 16-byte aligned; fp16/bf16 views
+ * with an even leading dimension and a 4-byte-aligned base run on the
+ * register-staged kernel's range-checked form, and fp32 views off those
+ * boundaries on the fp32 kernel's range-checked form.  With neither bit set, A
  * is K-contiguous (stride_ak == 1) and B is N-contiguous (stride_bn == 1):
  * both row-major.  A transposed view sets a bit.  Any other layout runs on
  * the generic kernel. */
@@ -159,9 +161,10 @@ typedef struct {
     int32_t split_k;          /* K slices (1 = the whole K in one accumulator) */
     int32_t threads;          /* threads per workgroup */
     int32_t fast_path;        /* 1 when a matrix-core kernel's layout predicate holds:
-                                 fp16/bf16 one unit stride per operand on 16-byte
-                                 boundaries (dtm_layout); fp32 one unit stride per
-                                 operand, any alignment */
+                                 fp16/bf16 one unit stride per operand, the other
+                                 stride even and the base 4-byte aligned (16-byte
+                                 boundaries for the pipelined kernels; dtm_layout);
+                                 fp32 one unit stride per operand, any alignment */
     int32_t ragged;           /* 1 when M, N or K is not a multiple of its block */
     int32_t layout;           /* dtm_layout bits of the operands (MFMA kernels; 0 otherwise) */
     uint64_t workspace_bytes; /* device scratch the plan needs (split-K partials) */
